@@ -1,0 +1,81 @@
+"""Named model geometries and seeded workloads of the uniform byte encoder.
+
+Geometry fields (zero or missing means "derive the default"):
+depth N, hidden D, heads H (head width D/H = 64), ffn F (SwiGLU width), vocab,
+context (tokens kept per item), rope_axes (1 text, 2 image, 3 video),
+rope_base, rms_epsilon, patch_side, channels, quantization ("bf16"|"e4m3").
+
+The five workloads follow the encoder's documented shapes: byte rows of text at
+the trainer's row width, 16x16 RGB patches for images, per-frame 16x16 patches
+with a (frame, row, col) grid for video. Sizes are synthetic stand-ins: the
+documentation's evaluation sets and checkpoints are not used.
+"""
+from __future__ import annotations
+
+DEFAULTS = dict(vocab=258, context=1024, rope_axes=1, rope_base=10000.0, rms_epsilon=1e-6,
+                patch_side=16, channels=3, quantization="bf16", modality="text")
+
+GEOMETRIES = {
+    "tiny": dict(depth=2, hidden=128, heads=2, ffn=512, vocab=256, context=1024),
+    "text512": dict(depth=12, hidden=512, heads=8, ffn=1536, vocab=258, context=1024),
+    "image768": dict(depth=12, hidden=768, heads=12, ffn=2304, rope_axes=2, context=1024, modality="image"),
+    "video1024": dict(depth=24, hidden=1024, heads=16, ffn=3072, rope_axes=3, context=2048, modality="video"),
+    "video1024_e4m3": dict(depth=24, hidden=1024, heads=16, ffn=3072, rope_axes=3, context=2048,
+                           modality="video", quantization="e4m3"),
+}
+
+# input recipes (seed 1)
+WORKLOADS = {
+    "tiny": dict(geometry="tiny", input="text", count=8, len_lo=16, len_hi=65, byte_lo=0, byte_hi=256),
+    "ragged": dict(geometry="text512", input="text", count=64, len_lo=1, len_hi=1025, byte_lo=32, byte_hi=127),
+    "ragged_trunc": dict(geometry="text512", input="text", count=64, len_lo=1, len_hi=2049, byte_lo=32,
+                         byte_hi=127),
+    "throughput": dict(geometry="text512", input="text", count=1024, fixed_length=1024, byte_lo=0, byte_hi=256),
+    "image": dict(geometry="image768", input="media", count=128, frames=1, height=256, width=256),
+    "video": dict(geometry="video1024", input="media", count=16, frames=8, height=224, width=224),
+    "video_e4m3": dict(geometry="video1024_e4m3", input="media", count=16, frames=8, height=224, width=224),
+}
+
+
+def complete(geometry: dict) -> dict:
+    g = dict(DEFAULTS)
+    for k, v in geometry.items():
+        if v is None or (k in DEFAULTS and v == 0):
+            continue  # zero means "derive the default" for defaulted fields
+        g[k] = v
+    if "heads" not in g or not g["heads"]:
+        g["heads"] = g["hidden"] // 64
+    if "ffn" not in g or not g["ffn"]:
+        g["ffn"] = 3 * g["hidden"]
+    return g
+
+
+def geometry(name: str) -> dict:
+    return complete(GEOMETRIES[name])
+
+
+def patch_dim(g: dict) -> int:
+    return g["patch_side"] * g["patch_side"] * g["channels"]
+
+
+def block_flops(g: dict, tokens: int, sum_sq_lengths: int) -> float:
+    """Dense multiply-add flops (2 per MAC) of the N blocks over a batch."""
+    D, F, N = g["hidden"], g["ffn"], g["depth"]
+    gemm = 2.0 * tokens * (D * 3 * D + D * D + D * 2 * F + F * D)
+    attn = 2.0 * 2.0 * sum_sq_lengths * D  # q.k and p.v over all heads
+    return N * (gemm + attn)
+
+
+def encode_flops(g: dict, lengths) -> float:
+    """Algorithmic flops of one encode: frontend GEMM (media) + blocks + reassociated pool."""
+    lengths = [int(x) for x in lengths]
+    T = sum(lengths)
+    ssq = sum(x * x for x in lengths)
+    D, H = g["hidden"], g["heads"]
+    total = block_flops(g, T, ssq)
+    if g.get("modality", "text") != "text":
+        total += 2.0 * T * patch_dim(g) * D
+    # pool: scores x.u_h (H dot products of D per token), weighted sum (H x D per token),
+    # then per item the H x (D x 64) value projection.
+    total += 2.0 * T * H * D * 2 + 2.0 * len(lengths) * D * D
+    return total
