@@ -1,0 +1,198 @@
+"""Throughput of the uniform byte encoder's forward pass on one MI355X.
+
+One step = one whole encode (frontend, N blocks, final norm, attention pool) of
+one synthetic batch whose bytes are already resident in HBM. Default workload:
+the depth-12 / hidden-512 text encoder on 1024 rows of exactly 1024 bytes.
+
+Prints one JSON line: encoded bytes/s (whole job), pooled embeddings/s,
+end-to-end MFMA utilisation, the roofline of the dominant kernel (its launch
+durations measured with HIP events on the encode stream during the timed
+steps), and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "encoded bytes/sec + MFMA util, depth-12 h512 encoder, 1024-byte rows"
+PEAK_BF16 = 2.5e15      # MI355X dense bf16 MFMA, flop/s
+PEAK_HBM = 8.0e12       # bytes/s
+
+WORKLOAD_TEXT = {
+    "throughput": "text encoder depth 12, hidden 512, 8 heads x 64, ffn 1536, 1-axis rotary; 1024 rows x 1024 bytes",
+    "ragged": "text encoder depth 12, hidden 512; 64 rows, lengths 1..1024, printable ASCII",
+    "tiny": "tiny encoder depth 2, hidden 128; 8 rows, lengths 16..64",
+    "image": "image encoder depth 12, hidden 768, 12 heads, 2-axis rotary; 128 images 256x256x3 (256 patches)",
+    "video": "video encoder depth 24, hidden 1024, 16 heads, 3-axis rotary; 16 clips 8x224x224x3 (1568 patches)",
+}
+
+
+def kernel_flops_per_launch(kernel, g, T, lengths):
+    D, F, H = g["hidden"], g["ffn"], g["heads"]
+    if kernel == "gemm_gate_up":
+        return 2.0 * T * D * 2 * F
+    if kernel == "gemm_qkv":
+        return 2.0 * T * D * 3 * D
+    if kernel == "gemm_down":
+        return 2.0 * T * F * D
+    if kernel == "gemm_out":
+        return 2.0 * T * D * D
+    if kernel == "attention":
+        return 4.0 * float(np.sum(np.asarray(lengths, np.float64) ** 2)) * D
+    raise ValueError(kernel)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "kernels.h"):
+        h.update(open(os.path.join(ROOT, "multimodal_embeddings_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(f"{kernel}@{workload}")
+    if not rec or rec.get("source_digest") != source_digest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(workload, weights, batch, rows):
+    import oracle
+    from multimodal_embeddings_amd import synth
+    sub = synth.subset(batch, rows)
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    if workload in ("throughput", "ragged", "tiny"):
+        _, stats = oracle.encode_text(weights, sub.data, sub.offsets)
+        units = stats[1]
+    else:
+        _, stats = oracle.encode_media(weights, sub)
+        units = int(sub.data.size)
+    dt = time.perf_counter() - t0
+    return {"value": units / dt, "unit": "bytes/s", "cores": threads, "kind": "oracle",
+            "sample": f"items {list(rows)} of the {workload} batch ({units} bytes, float64 oracle, {dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="throughput", choices=sorted(WORKLOAD_TEXT))
+    ap.add_argument("--kernel", default="gemm_gate_up", help="dominant kernel for the roofline entry")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", default="0,1")
+    ap.add_argument("--per-kernel", action="store_true", help="also time every kernel kind (extra passes)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported in this build "
+              "(items are independent; a multi-GPU run would shard the tape by items)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import multimodal_embeddings_amd as ube
+    from multimodal_embeddings_amd import configs, synth
+
+    wl = configs.WORKLOADS[args.workload]
+    g = configs.geometry(wl["geometry"])
+    weights = synth.make_weights(g)
+    batch = synth.workload_inputs(args.workload)
+    model = ube.Model(weights, 0)
+    arena = ube.Arena(0)
+    batch.data_device = torch.from_numpy(batch.data).to("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        return ube.encode(model, arena, batch, completion=1, stream=stream)
+
+    rows, stats = step()
+    torch.cuda.synchronize()
+    T = stats[1]
+    if g["modality"] == "text":
+        lengths = np.minimum(np.diff(batch.offsets.astype(np.int64)), g["context"])
+        units = T  # encoded bytes
+    else:
+        per = (batch.heights // g["patch_side"]) * (batch.widths // g["patch_side"]) * batch.frames
+        lengths = per.astype(np.int64)
+        units = int(batch.data.size)  # pixel bytes
+    flops = configs.encode_flops(g, lengths)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    ube.kernel_timer_start(args.kernel, args.steps * g["depth"] + 8)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    kms, launches = ube.kernel_timer_stop()
+    ms = start.elapsed_time(end) / args.steps
+
+    per_kernel = {}
+    if args.per_kernel:
+        for kname in ube.KERNELS:
+            ube.kernel_timer_start(kname, 4 * g["depth"] + 8)
+            step()
+            torch.cuda.synchronize()
+            t, n = ube.kernel_timer_stop()
+            if n:
+                per_kernel[kname] = {"ms_per_step": t, "launches": n}
+
+    kflops = kernel_flops_per_launch(args.kernel, g, T, lengths)
+    avg_s = kms / max(launches, 1) / 1e3
+    achieved = kflops / avg_s / 1e12
+    traffic = load_traffic(args.kernel, args.workload)
+    out = {
+        "metric": METRIC,
+        "value": units / (ms / 1e3),
+        "unit": "bytes/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded bytes, random-init bf16 weights N(0, 0.02))",
+        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}", "items": batch.count,
+                   "tokens": int(T), "parallelism": "1 GPU"},
+        "embeddings_per_s": batch.count / (ms / 1e3),
+        "mfma_util": flops / (ms / 1e3) / PEAK_BF16,
+        "flops_per_step": flops,
+        "roofline": {"kernel": args.kernel, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16 / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved / (PEAK_BF16 / 1e12), "traffic": traffic,
+                     "avg_launch_ms": avg_s * 1e3, "launches": launches},
+    }
+    if per_kernel:
+        out["per_kernel_ms"] = per_kernel
+    if not args.no_cpu_baseline:
+        rows_s = [int(r) for r in args.cpu_rows.split(",") if r != ""]
+        out["cpu_baseline"] = cpu_baseline(args.workload, weights, batch, rows_s)
+    else:
+        out["cpu_baseline"] = None
+    arena.close()
+    model.close()
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,267 @@
+/*
+ * ube.h -- C ABI of the MI355X (gfx950) forward pass of the uniform byte encoder.
+ *
+ * What is computed (UForm documentation pages):
+ *   - "UForm" page, "Architecture & Goals": bytes in, N blocks at one fixed width
+ *     (RMSNorm, QKV attention with multi-axis M-RoPE, SwiGLU MLP, residuals),
+ *     an attention-pooled embedding out.
+ *   - "UForm" page, "One Omni Model": byte-gather frontend for text, 16x16 patch
+ *     projection with 2-D (row, col) rotary positions for images, and per-frame
+ *     patches with 3-D (frame, row, col) positions for video.
+ *   - "UForm" page, "Precision by Design": bf16 storage, fp32 accumulation and
+ *     normalisation, fp32 residual stream; E4M3 inference fixed at load by one
+ *     `quantization` argument, blocks in FP8, frontend and pool in bf16.
+ *   - "UForm" page, FAQ "Why attention pooling instead of mean pooling?": the pool
+ *     query is one learned vector of encoder width; per-token outputs are K and V.
+ *
+ * The call shapes follow the pages' C ABI:
+ *   - "Arenas" page: one argument struct per verb with an `outcome` pointer;
+ *     outputs land in a caller-reused arena that rewinds on every call and grows
+ *     only when outgrown; rows views carry data, count, columns, stride, scalar;
+ *     ragged inputs are Arrow tapes with count+1 offsets in host memory.
+ *   - "Rust" and "Python" pages, "Encoding": `text_encode` takes a tape, a byte per
+ *     token; `image_encode_pixels` takes interleaved 8-bit RGB with per-item
+ *     heights and widths; outputs are f32 by default or bf16; stats report the
+ *     truncated items and the encoded tokens.
+ *   - "Python" page, "Errors": the status codes.
+ *
+ * Threading: calls on different arenas may run concurrently; an arena serves one
+ * call at a time (a second concurrent call reports `contended`). All device work
+ * of a call is enqueued on the caller's HIP stream (`stream`, a hipStream_t; NULL
+ * is the null stream).
+ */
+#ifndef UBE_H
+#define UBE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Outcome of a call ("Python" page, "Errors"; subset used by the encoder). */
+typedef enum ube_status_t {
+    ube_status_success_k = 0,
+    ube_status_invalid_argument_k = 1, /* NULL arena or argument, decreasing offsets, inputs inside the arena */
+    ube_status_shape_mismatch_k = 2,   /* image side not a multiple of the patch, patches over the context */
+    ube_status_out_of_memory_k = 3,    /* the GPU could not grow the arena; no host fallback */
+    ube_status_device_k = 4,           /* arena and model on different devices, or a HIP runtime failure */
+    ube_status_contended_k = 5,        /* the arena is serving another call */
+    ube_status_unsupported_k = 6,      /* a geometry or mode this build does not run */
+    ube_status_internal_k = 7,
+} ube_status_t;
+
+/* `message` is a static string, never freed; NULL on success. */
+typedef struct ube_outcome_t {
+    ube_status_t status;
+    char const *message;
+} ube_outcome_t;
+
+typedef enum ube_scalar_t {
+    ube_scalar_unknown_k = 0,
+    ube_scalar_u8_k = 1,
+    ube_scalar_bf16_k = 2,
+    ube_scalar_f32_k = 3,
+    ube_scalar_e4m3_k = 4,
+} ube_scalar_t;
+
+/* Ragged input, Arrow layout ("Arenas" page, "Rows and Tapes"): item i spans
+ * data[offsets[i] .. offsets[i+1]). `offsets` (count+1 entries) is host memory;
+ * `data` may be device memory of the model's GPU (used in place) or host memory
+ * (copied to the device by the call). offsets[0] may be non-zero. */
+typedef struct ube_tape_view_t {
+    void const *data;
+    size_t const *offsets;
+    size_t count;
+} ube_tape_view_t;
+
+/* Output rows, one per item ("Arenas" page, "Rows and Tapes"): row i starts at
+ * (char*)data + i*stride and holds `columns` values of `scalar`. Device memory
+ * inside the arena, valid until the next call naming that arena. */
+typedef struct ube_rows_view_t {
+    void *data;
+    size_t count, columns, stride;
+    ube_scalar_t scalar;
+} ube_rows_view_t;
+
+/* "Python" page, "Encoding": items cut at the context, and tokens encoded. */
+typedef struct ube_encode_stats_t {
+    size_t truncated, tokens;
+} ube_encode_stats_t;
+
+/* Model shape. Zero fields take the default in brackets.
+ * depth N [required], hidden D [required, multiple of 128], heads H [D/64; D/H
+ * must be 64], ffn F [3D; multiple of 64], vocab [258], context [1024; at most
+ * 32767], rope_axes [1; 1 text, 2 image, 3 video], patch_side [16], channels
+ * [3], rope_base [10000], rms_epsilon [1e-6], quantization [bf16; or e4m3]. */
+typedef struct ube_geometry_t {
+    size_t depth, hidden, heads, ffn, vocab, context, rope_axes, patch_side, channels;
+    float rope_base, rms_epsilon;
+    ube_scalar_t quantization;
+} ube_geometry_t;
+
+/* Weights in host memory, canonical layout y = x W with W row-major [in x out].
+ * Matrices are bf16 bit patterns (uint16); gains are float32. Per-block arrays
+ * hold `depth` pointers. The model copies and packs everything at init; the
+ * caller may free these afterwards.
+ *   embed      [vocab x D]          text models (NULL for media)
+ *   patch_proj [p*p*channels x D]   media models (NULL for text)
+ *   w_qkv      [D x 3D] = [W_q | W_k | W_v];  w_o [D x D]
+ *   w_gate, w_up [D x F];  w_down [F x D]
+ *   attn_norm, mlp_norm, final_norm: [D]
+ *   pool_query [D];  pool_wk, pool_wv [D x D] */
+typedef struct ube_weights_t {
+    uint16_t const *embed;
+    uint16_t const *patch_proj;
+    uint16_t const *const *w_qkv;
+    uint16_t const *const *w_o;
+    uint16_t const *const *w_gate;
+    uint16_t const *const *w_up;
+    uint16_t const *const *w_down;
+    float const *const *attn_norm;
+    float const *const *mlp_norm;
+    float const *final_norm;
+    uint16_t const *pool_query;
+    uint16_t const *pool_wk;
+    uint16_t const *pool_wv;
+} ube_weights_t;
+
+typedef struct ube_model_handle_t *ube_model_t;
+typedef struct ube_arena_handle_t *ube_arena_t;
+
+/* Loads a model onto GPU `device`: validates the geometry, packs the weights
+ * for the gfx950 kernels (and quantises the block matrices to E4M3 with one
+ * amax/448 scale per tensor when geometry.quantization is e4m3), and builds
+ * the rotary cos/sin table (double on the host, stored fp32). On failure
+ * *model is NULL. Statuses: invalid_argument (NULL or missing weights),
+ * unsupported (geometry outside the bounds above), out_of_memory, device. */
+typedef struct ube_model_init_t {
+    ube_model_t *model;
+    ube_outcome_t *outcome;
+    int device;
+    ube_geometry_t geometry;
+    ube_weights_t const *weights;
+} ube_model_init_t;
+void ube_model_init(ube_model_init_t *arguments);
+
+typedef struct ube_model_description_t {
+    size_t dimensions, context, depth, heads, ffn, rope_axes;
+    ube_scalar_t quantization;
+    size_t memory_usage; /* device bytes the model holds */
+    int device;
+} ube_model_description_t;
+
+typedef struct ube_model_describe_t {
+    ube_model_t model;
+    ube_outcome_t *outcome;
+    ube_model_description_t *description;
+} ube_model_describe_t;
+void ube_model_describe(ube_model_describe_t *arguments);
+
+/* NULL-safe; cannot fail. Waits for nothing: the caller finishes its streams first. */
+void ube_model_free(ube_model_t model);
+
+/* An empty arena on GPU `device` ("Arenas" page, `uform_arena_init`): nothing
+ * is allocated until a call writes into it. In this build the arena also holds
+ * the call's activations, so an arena is the unit of concurrency. */
+typedef struct ube_arena_init_t {
+    ube_arena_t *arena;
+    ube_outcome_t *outcome;
+    int device;
+} ube_arena_init_t;
+void ube_arena_init(ube_arena_init_t *arguments);
+
+/* NULL-safe; synchronises the device, then frees the arena and its outputs. */
+void ube_arena_free(ube_arena_t arena);
+
+/* Device bytes the arena holds now (its high-water mark). */
+size_t ube_arena_capacity(ube_arena_t arena);
+
+/* Encodes a tape of byte strings, a byte per token ("Rust"/"Python" pages,
+ * `text_encode`). Items longer than the model context keep their first
+ * `context` bytes and count in stats->truncated. Writes one pooled row of D
+ * values per item into the arena as `outputs_scalar` (f32, the default when
+ * unknown, or bf16) and publishes it through *embeddings; an item with no
+ * bytes pools to the zero row; count == 0 succeeds with an empty view.
+ * completion == 0 blocks until the rows are final; 1 returns once the work is
+ * queued on `stream` (a GPU fault then surfaces at the caller's next
+ * synchronisation). On failure *embeddings is all zeros and NULL.
+ * `trace_residual`, when not NULL, is device memory of (depth+1) * T * D
+ * floats that receives the fp32 residual stream after the frontend and after
+ * every block (T = stats->tokens): a diagnostics hook, off the timed path. */
+typedef struct ube_text_encode_t {
+    ube_model_t model;
+    ube_arena_t arena;
+    void *stream;
+    ube_outcome_t *outcome;
+    int completion;
+    ube_tape_view_t texts;
+    ube_scalar_t outputs_scalar;
+    ube_rows_view_t *embeddings;
+    ube_encode_stats_t *stats;
+    float *trace_residual;
+} ube_text_encode_t;
+void ube_text_encode(ube_text_encode_t *arguments);
+
+/* Encodes images of interleaved 8-bit RGB ("Rust"/"Python" pages,
+ * `image_encode_pixels`): item i is heights[i] x widths[i] x channels bytes of
+ * the tape, cut into patch_side^2 patches in row-major grid order, each patch
+ * vector ordered (row in patch, column in patch, channel) and scaled by 1/255,
+ * projected by patch_proj; positions (grid row, grid col) on a 2-axis model.
+ * heights/widths are host arrays of `count`. shape_mismatch when a side is not
+ * a multiple of patch_side, the item's bytes differ from its size, or its patch
+ * count exceeds the context. Otherwise as ube_text_encode. */
+typedef struct ube_image_encode_pixels_t {
+    ube_model_t model;
+    ube_arena_t arena;
+    void *stream;
+    ube_outcome_t *outcome;
+    int completion;
+    ube_tape_view_t pixels;
+    size_t const *heights;
+    size_t const *widths;
+    ube_scalar_t outputs_scalar;
+    ube_rows_view_t *embeddings;
+    ube_encode_stats_t *stats;
+    float *trace_residual;
+} ube_image_encode_pixels_t;
+void ube_image_encode_pixels(ube_image_encode_pixels_t *arguments);
+
+/* Extension (the pages offer video only from files): item i is frame_counts[i]
+ * frames of heights[i] x widths[i] x channels bytes, each frame cut into
+ * patches as for images; token (f, r, c) sits at f*gh*gw + r*gw + c with
+ * positions (frame, row, col) on a 3-axis model. Otherwise as images. */
+typedef struct ube_video_encode_frames_t {
+    ube_model_t model;
+    ube_arena_t arena;
+    void *stream;
+    ube_outcome_t *outcome;
+    int completion;
+    ube_tape_view_t frames;
+    size_t const *frame_counts;
+    size_t const *heights;
+    size_t const *widths;
+    ube_scalar_t outputs_scalar;
+    ube_rows_view_t *embeddings;
+    ube_encode_stats_t *stats;
+    float *trace_residual;
+} ube_video_encode_frames_t;
+void ube_video_encode_frames(ube_video_encode_frames_t *arguments);
+
+/* Host-only tape plan, the bookkeeping every text encode does first (no
+ * device work; usable without a GPU). lengths[count] receives the kept length
+ * of each item, cu[count+1] their prefix sums, *stats the truncated items and
+ * tokens. Returns invalid_argument if an offset decreases or a pointer is NULL
+ * with count > 0. */
+ube_status_t ube_tape_plan(size_t const *offsets, size_t count, size_t context, uint32_t *lengths, uint32_t *cu,
+                           ube_encode_stats_t *stats);
+
+/* Spelling of a status, a static string. */
+char const *ube_status_name(ube_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UBE_H */

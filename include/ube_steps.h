@@ -1,0 +1,85 @@
+/*
+ * ube_steps.h -- per-step entry points and kernel timing of libube.
+ *
+ * Each step entry point launches one kernel of the encode path on device
+ * buffers the caller owns, so every step of the forward pass can be checked
+ * on its own against a CPU reference. They use the library's internal layouts,
+ * stated with each call. All pointers are device memory of the current device
+ * unless noted; `stream` is a hipStream_t (NULL: null stream). Each returns
+ * invalid_argument for NULL pointers or unsupported sizes, device for a HIP
+ * runtime failure, success otherwise; the work is asynchronous on `stream`
+ * unless noted.
+ */
+#ifndef UBE_STEPS_H
+#define UBE_STEPS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "ube.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Projection ("UForm" page, "Architecture & Goals": the block's matrix
+ * products, bf16 in, fp32 accumulate, "Precision by Design"):
+ * y[M x N] = bf16(x[M x K] w^T), w given transposed as [N x K] (the packed
+ * weight layout), all row-major bf16. x must have round_up(M, 256) readable
+ * rows (rows past M are read, their products discarded). N % 128 == 0,
+ * K % 64 == 0. */
+ube_status_t ube_step_gemm(void const *w, void const *x, void *y, size_t M, size_t N, size_t K, void *stream);
+
+/* RMSNorm ("UForm" page, "Architecture & Goals"; fp32 normalisation,
+ * "Precision by Design"): h[t] = bf16(x[t] * gain / sqrt(mean(x[t]^2) + eps)),
+ * x fp32 [T x D], gain fp32 [D], h bf16 [T x D]. */
+ube_status_t ube_step_rmsnorm(float const *x, float const *gain, void *h, size_t T, size_t D, float eps,
+                              void *stream);
+
+/* Bidirectional variable-length attention ("UForm" page, FAQ "Why no cuDNN,
+ * FlashAttention, xformers, or FA3?": ragged attention, each segment on its
+ * own), head width 64: for every item i (tokens cu[i] .. cu[i+1]) and head h,
+ * o_t,h = sum_u softmax_u(q_t,h . k_u,h / 8) v_u,h over u in item i.
+ * q, k: bf16, row t at q + t*ldqk (elements), head h at columns [64h, 64h+64);
+ * vt: bf16 feature-major, element (64h + e, t) at vt[(64h + e)*ldvt + t];
+ * o: bf16, row t at o + t*ldo. cu_host: host, count+1 non-decreasing entries.
+ * q and k need cu[count] + 256 readable rows, vt ldvt >= cu[count] + 256, with
+ * columns cu[count] .. cu[count]+64 finite. Synchronous (allocates and frees
+ * its tile list). */
+ube_status_t ube_step_attention(void const *q, void const *k, size_t ldqk, void const *vt, size_t ldvt, void *o,
+                                size_t ldo, uint32_t const *cu_host, size_t count, size_t heads, void *stream);
+
+/* Kernels of an encode call, for timing. */
+typedef enum ube_kernel_t {
+    ube_kernel_gather_k = 0,
+    ube_kernel_patchify_k = 1,
+    ube_kernel_rmsnorm_k = 2,
+    ube_kernel_gemm_patch_k = 3,
+    ube_kernel_gemm_qkv_k = 4,
+    ube_kernel_attention_k = 5,
+    ube_kernel_gemm_out_k = 6,
+    ube_kernel_gemm_gate_up_k = 7,
+    ube_kernel_gemm_down_k = 8,
+    ube_kernel_final_norm_k = 9,
+    ube_kernel_pool_k = 10,
+    ube_kernel_count_k = 11,
+} ube_kernel_t;
+
+/* Starts timing every launch of `kernel` made by encode calls in this
+ * process: a HIP event pair is recorded around each launch on the call's
+ * stream, for at most `max_launches` launches (further ones go untimed).
+ * Process-wide; one kernel at a time. Allocates the events now, none later. */
+ube_status_t ube_kernel_timer_start(ube_kernel_t kernel, size_t max_launches);
+
+/* Waits for the recorded events, returns the summed duration in milliseconds
+ * and the number of timed launches, and stops timing (events are freed). */
+ube_status_t ube_kernel_timer_stop(double *total_ms, size_t *launches);
+
+/* Spelling of a kernel id, a static string. */
+char const *ube_kernel_name(ube_kernel_t kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* UBE_STEPS_H */

@@ -1,1 +1,393 @@
-"""MI355X-native forward pass of the uniform byte encoder (placeholder; binding follows)."""
+"""MI355X-native forward pass of the uniform byte encoder: a thin ctypes binding over libube.
+
+Every step of the forward pass runs in libube's gfx950 HIP kernels (built in-tree
+by ``multimodal_embeddings_amd.build``); this module only marshals arguments.
+The raw C entry points keep their C names (``ube_text_encode`` ...); ``Model``,
+``Arena`` and ``text_encode`` / ``image_encode_pixels`` / ``video_encode_frames``
+wrap them for numpy / torch callers. There is no CPU fallback: without the built
+library every call raises ``ExtensionMissing``.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+from . import configs
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libube.so")
+
+
+class ExtensionMissing(RuntimeError):
+    pass
+
+
+# ------------------------------------------------------------------ C structs (include/ube.h)
+
+SZ = C.c_size_t
+VP = C.c_void_p
+
+
+class ube_outcome_t(C.Structure):
+    _fields_ = [("status", C.c_int), ("message", C.c_char_p)]
+
+
+class ube_tape_view_t(C.Structure):
+    _fields_ = [("data", VP), ("offsets", C.POINTER(SZ)), ("count", SZ)]
+
+
+class ube_rows_view_t(C.Structure):
+    _fields_ = [("data", VP), ("count", SZ), ("columns", SZ), ("stride", SZ), ("scalar", C.c_int)]
+
+
+class ube_encode_stats_t(C.Structure):
+    _fields_ = [("truncated", SZ), ("tokens", SZ)]
+
+
+class ube_geometry_t(C.Structure):
+    _fields_ = [(n, SZ) for n in ("depth", "hidden", "heads", "ffn", "vocab", "context", "rope_axes", "patch_side",
+                                  "channels")] + [("rope_base", C.c_float), ("rms_epsilon", C.c_float),
+                                                  ("quantization", C.c_int)]
+
+
+class ube_weights_t(C.Structure):
+    _fields_ = [("embed", VP), ("patch_proj", VP)] + [
+        (n, C.POINTER(VP)) for n in ("w_qkv", "w_o", "w_gate", "w_up", "w_down", "attn_norm", "mlp_norm")] + [
+        ("final_norm", VP), ("pool_query", VP), ("pool_wk", VP), ("pool_wv", VP)]
+
+
+class ube_model_init_t(C.Structure):
+    _fields_ = [("model", C.POINTER(VP)), ("outcome", C.POINTER(ube_outcome_t)), ("device", C.c_int),
+                ("geometry", ube_geometry_t), ("weights", C.POINTER(ube_weights_t))]
+
+
+class ube_model_description_t(C.Structure):
+    _fields_ = [(n, SZ) for n in ("dimensions", "context", "depth", "heads", "ffn", "rope_axes")] + [
+        ("quantization", C.c_int), ("memory_usage", SZ), ("device", C.c_int)]
+
+
+class ube_model_describe_t(C.Structure):
+    _fields_ = [("model", VP), ("outcome", C.POINTER(ube_outcome_t)),
+                ("description", C.POINTER(ube_model_description_t))]
+
+
+class ube_arena_init_t(C.Structure):
+    _fields_ = [("arena", C.POINTER(VP)), ("outcome", C.POINTER(ube_outcome_t)), ("device", C.c_int)]
+
+
+_ENCODE_HEAD = [("model", VP), ("arena", VP), ("stream", VP), ("outcome", C.POINTER(ube_outcome_t)),
+                ("completion", C.c_int)]
+_ENCODE_TAIL = [("outputs_scalar", C.c_int), ("embeddings", C.POINTER(ube_rows_view_t)),
+                ("stats", C.POINTER(ube_encode_stats_t)), ("trace_residual", VP)]
+
+
+class ube_text_encode_t(C.Structure):
+    _fields_ = _ENCODE_HEAD + [("texts", ube_tape_view_t)] + _ENCODE_TAIL
+
+
+class ube_image_encode_pixels_t(C.Structure):
+    _fields_ = _ENCODE_HEAD + [("pixels", ube_tape_view_t), ("heights", C.POINTER(SZ)),
+                               ("widths", C.POINTER(SZ))] + _ENCODE_TAIL
+
+
+class ube_video_encode_frames_t(C.Structure):
+    _fields_ = _ENCODE_HEAD + [("frames", ube_tape_view_t), ("frame_counts", C.POINTER(SZ)),
+                               ("heights", C.POINTER(SZ)), ("widths", C.POINTER(SZ))] + _ENCODE_TAIL
+
+
+STATUS = {0: "success", 1: "invalid_argument", 2: "shape_mismatch", 3: "out_of_memory", 4: "device", 5: "contended",
+          6: "unsupported", 7: "internal"}
+SCALAR = {"unknown": 0, "u8": 1, "bf16": 2, "f32": 3, "e4m3": 4}
+KERNELS = ["gather", "patchify", "rmsnorm", "gemm_patch", "gemm_qkv", "attention", "gemm_out", "gemm_gate_up",
+           "gemm_down", "final_norm", "pool"]
+
+# every symbol the headers declare, with ctypes signatures
+_SIGNATURES = {
+    "ube_model_init": ([C.POINTER(ube_model_init_t)], None),
+    "ube_model_describe": ([C.POINTER(ube_model_describe_t)], None),
+    "ube_model_free": ([VP], None),
+    "ube_arena_init": ([C.POINTER(ube_arena_init_t)], None),
+    "ube_arena_free": ([VP], None),
+    "ube_arena_capacity": ([VP], SZ),
+    "ube_text_encode": ([C.POINTER(ube_text_encode_t)], None),
+    "ube_image_encode_pixels": ([C.POINTER(ube_image_encode_pixels_t)], None),
+    "ube_video_encode_frames": ([C.POINTER(ube_video_encode_frames_t)], None),
+    "ube_tape_plan": ([C.POINTER(SZ), SZ, SZ, VP, VP, C.POINTER(ube_encode_stats_t)], C.c_int),
+    "ube_status_name": ([C.c_int], C.c_char_p),
+    "ube_step_gemm": ([VP, VP, VP, SZ, SZ, SZ, VP], C.c_int),
+    "ube_step_rmsnorm": ([VP, VP, VP, SZ, SZ, C.c_float, VP], C.c_int),
+    "ube_step_attention": ([VP, VP, SZ, VP, SZ, VP, SZ, VP, SZ, SZ, VP], C.c_int),
+    "ube_kernel_timer_start": ([C.c_int, SZ], C.c_int),
+    "ube_kernel_timer_stop": ([C.POINTER(C.c_double), C.POINTER(SZ)], C.c_int),
+    "ube_kernel_name": ([C.c_int], C.c_char_p),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libube.so; raises ExtensionMissing when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ExtensionMissing(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                                   "(python -c 'import __graft_entry__ as g; g.build()')")
+        L = C.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGNATURES.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+class UbeError(RuntimeError):
+    def __init__(self, status, message):
+        self.status = STATUS.get(status, str(status))
+        super().__init__(f"{self.status}: {message.decode() if isinstance(message, bytes) else message}")
+
+
+def _check(outcome):
+    if outcome.status != 0:
+        raise UbeError(outcome.status, outcome.message or b"")
+
+
+def _ptr(a):
+    """Device or host address of a torch tensor or numpy array (None -> NULL)."""
+    if a is None:
+        return None
+    if hasattr(a, "data_ptr"):
+        return a.data_ptr()
+    return a.ctypes.data
+
+
+def _stream_handle(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+# ------------------------------------------------------------------ model / arena
+
+
+class Model:
+    """A model on one GPU, built from host weights (``synth.Weights`` or a dict of the same names)."""
+
+    def __init__(self, weights, device: int = 0):
+        g = configs.complete(weights.geometry)
+        self.geometry = g
+        bits, f32 = weights.bits, weights.f32
+        keep = []
+
+        def host(a, dtype):
+            arr = np.ascontiguousarray(a, dtype=dtype)
+            keep.append(arr)
+            return arr.ctypes.data
+
+        def per_layer(name, table, dtype):
+            arr = (VP * max(g["depth"], 1))(*[host(x, dtype) for x in table[name]])
+            keep.append(arr)
+            return arr
+
+        w = ube_weights_t()
+        if g["modality"] == "text":
+            w.embed = host(bits["embed"], np.uint16)
+        else:
+            w.patch_proj = host(bits["patch_proj"], np.uint16)
+        for name in ("w_qkv", "w_o", "w_gate", "w_up", "w_down"):
+            setattr(w, name, per_layer(name, bits, np.uint16))
+        for name in ("attn_norm", "mlp_norm"):
+            setattr(w, name, per_layer(name, f32, np.float32))
+        w.final_norm = host(f32["final_norm"], np.float32)
+        w.pool_query = host(bits["pool_query"], np.uint16)
+        w.pool_wk = host(bits["pool_wk"], np.uint16)
+        w.pool_wv = host(bits["pool_wv"], np.uint16)
+        geo = ube_geometry_t(g["depth"], g["hidden"], g["heads"], g["ffn"], g["vocab"], g["context"], g["rope_axes"],
+                             g["patch_side"], g["channels"], g["rope_base"], g["rms_epsilon"],
+                             SCALAR[g["quantization"]])
+        handle = VP()
+        outcome = ube_outcome_t()
+        args = ube_model_init_t(C.pointer(handle), C.pointer(outcome), device, geo, C.pointer(w))
+        lib().ube_model_init(C.byref(args))
+        _check(outcome)
+        self.handle = handle
+        self.device = device
+
+    def describe(self):
+        d = ube_model_description_t()
+        outcome = ube_outcome_t()
+        lib().ube_model_describe(C.byref(ube_model_describe_t(self.handle, C.pointer(outcome), C.pointer(d))))
+        _check(outcome)
+        return {f: getattr(d, f) for f, _ in ube_model_description_t._fields_}
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().ube_model_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Arena:
+    def __init__(self, device: int = 0):
+        handle = VP()
+        outcome = ube_outcome_t()
+        lib().ube_arena_init(C.byref(ube_arena_init_t(C.pointer(handle), C.pointer(outcome), device)))
+        _check(outcome)
+        self.handle = handle
+        self.device = device
+
+    @property
+    def capacity(self):
+        return lib().ube_arena_capacity(self.handle)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().ube_arena_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class Rows:
+    """A rows view in arena memory (device); ``tensor()`` copies it into a torch tensor."""
+
+    def __init__(self, view: ube_rows_view_t, device: int):
+        self.data = view.data
+        self.count, self.columns, self.stride = view.count, view.columns, view.stride
+        self.scalar = {v: k for k, v in SCALAR.items()}[view.scalar]
+        self.device = device
+
+    @property
+    def __cuda_array_interface__(self):
+        typestr = "<f4" if self.scalar == "f32" else "<u2"
+        item = 4 if self.scalar == "f32" else 2
+        return {"shape": (self.count, self.columns), "typestr": typestr, "data": (self.data or 0, False),
+                "strides": (self.stride, item), "version": 2}
+
+    def tensor(self):
+        import torch
+        if self.count == 0:
+            dt = torch.float32 if self.scalar == "f32" else torch.int16
+            return torch.zeros((0, self.columns), dtype=dt, device=f"cuda:{self.device}")
+        t = torch.as_tensor(self, device=f"cuda:{self.device}").clone()
+        return t if self.scalar == "f32" else t.view(torch.int16).view(torch.bfloat16)
+
+
+def _tape(data, offsets):
+    off = np.ascontiguousarray(offsets, dtype=np.uint64)
+    return ube_tape_view_t(_ptr(data), off.ctypes.data_as(C.POINTER(SZ)), len(off) - 1), off
+
+
+def text_encode(model: Model, arena: Arena, data, offsets, *, stream=None, outputs_scalar="f32", completion=0,
+                trace=None):
+    """-> (Rows, (truncated, tokens)). ``data``: torch uint8 tensor (device) or numpy (host)."""
+    tape, off = _tape(data, offsets)
+    rows, stats, outcome = ube_rows_view_t(), ube_encode_stats_t(), ube_outcome_t()
+    args = ube_text_encode_t(model.handle, arena.handle, _stream_handle(stream), C.pointer(outcome), completion,
+                             tape, SCALAR[outputs_scalar], C.pointer(rows), C.pointer(stats), _ptr(trace))
+    lib().ube_text_encode(C.byref(args))
+    _check(outcome)
+    return Rows(rows, model.device), (stats.truncated, stats.tokens)
+
+
+def image_encode_pixels(model: Model, arena: Arena, data, offsets, heights, widths, *, stream=None,
+                        outputs_scalar="f32", completion=0, trace=None):
+    tape, off = _tape(data, offsets)
+    hh = np.ascontiguousarray(heights, dtype=np.uint64)
+    ww = np.ascontiguousarray(widths, dtype=np.uint64)
+    rows, stats, outcome = ube_rows_view_t(), ube_encode_stats_t(), ube_outcome_t()
+    args = ube_image_encode_pixels_t(model.handle, arena.handle, _stream_handle(stream), C.pointer(outcome),
+                                     completion, tape, hh.ctypes.data_as(C.POINTER(SZ)),
+                                     ww.ctypes.data_as(C.POINTER(SZ)), SCALAR[outputs_scalar], C.pointer(rows),
+                                     C.pointer(stats), _ptr(trace))
+    lib().ube_image_encode_pixels(C.byref(args))
+    _check(outcome)
+    return Rows(rows, model.device), (stats.truncated, stats.tokens)
+
+
+def video_encode_frames(model: Model, arena: Arena, data, offsets, frame_counts, heights, widths, *, stream=None,
+                        outputs_scalar="f32", completion=0, trace=None):
+    tape, off = _tape(data, offsets)
+    ff = np.ascontiguousarray(frame_counts, dtype=np.uint64)
+    hh = np.ascontiguousarray(heights, dtype=np.uint64)
+    ww = np.ascontiguousarray(widths, dtype=np.uint64)
+    rows, stats, outcome = ube_rows_view_t(), ube_encode_stats_t(), ube_outcome_t()
+    args = ube_video_encode_frames_t(model.handle, arena.handle, _stream_handle(stream), C.pointer(outcome),
+                                     completion, tape, ff.ctypes.data_as(C.POINTER(SZ)),
+                                     hh.ctypes.data_as(C.POINTER(SZ)), ww.ctypes.data_as(C.POINTER(SZ)),
+                                     SCALAR[outputs_scalar], C.pointer(rows), C.pointer(stats), _ptr(trace))
+    lib().ube_video_encode_frames(C.byref(args))
+    _check(outcome)
+    return Rows(rows, model.device), (stats.truncated, stats.tokens)
+
+
+def encode(model: Model, arena: Arena, batch, **kw):
+    """Dispatch a synth batch to the verb of the model's modality."""
+    m = model.geometry["modality"]
+    if m == "text":
+        return text_encode(model, arena, batch.data_device if hasattr(batch, "data_device") else batch.data,
+                           batch.offsets, **kw)
+    data = batch.data_device if hasattr(batch, "data_device") else batch.data
+    if m == "image":
+        return image_encode_pixels(model, arena, data, batch.offsets, batch.heights, batch.widths, **kw)
+    return video_encode_frames(model, arena, data, batch.offsets, batch.frames, batch.heights, batch.widths, **kw)
+
+
+def tape_plan(offsets, context):
+    """Host-only bookkeeping through the library -> (lengths, cu, (truncated, tokens))."""
+    off = np.ascontiguousarray(offsets, dtype=np.uint64)
+    count = len(off) - 1
+    lengths = np.zeros(max(count, 1), np.uint32)
+    cu = np.zeros(count + 1, np.uint32)
+    stats = ube_encode_stats_t()
+    st = lib().ube_tape_plan(off.ctypes.data_as(C.POINTER(SZ)), count, context, lengths.ctypes.data,
+                             cu.ctypes.data, C.byref(stats))
+    if st != 0:
+        raise UbeError(st, b"tape plan refused")
+    return lengths[:count], cu, (stats.truncated, stats.tokens)
+
+
+# ------------------------------------------------------------------ steps and timing (include/ube_steps.h)
+
+
+def _step(st):
+    if st != 0:
+        raise UbeError(st, b"step refused")
+
+
+def step_gemm(w, x, y, M, N, K, stream=None):
+    _step(lib().ube_step_gemm(_ptr(w), _ptr(x), _ptr(y), M, N, K, _stream_handle(stream)))
+
+
+def step_rmsnorm(x, gain, h, T, D, eps, stream=None):
+    _step(lib().ube_step_rmsnorm(_ptr(x), _ptr(gain), _ptr(h), T, D, eps, _stream_handle(stream)))
+
+
+def step_attention(q, k, ldqk, vt, ldvt, o, ldo, cu, heads, stream=None):
+    cu = np.ascontiguousarray(cu, dtype=np.uint32)
+    _step(lib().ube_step_attention(_ptr(q), _ptr(k), ldqk, _ptr(vt), ldvt, _ptr(o), ldo, cu.ctypes.data,
+                                   len(cu) - 1, heads, _stream_handle(stream)))
+
+
+def kernel_timer_start(kernel: str, max_launches: int):
+    _step(lib().ube_kernel_timer_start(KERNELS.index(kernel), max_launches))
+
+
+def kernel_timer_stop():
+    ms, n = C.c_double(), SZ()
+    _step(lib().ube_kernel_timer_stop(C.byref(ms), C.byref(n)))
+    return ms.value, n.value

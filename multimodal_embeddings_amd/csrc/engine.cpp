@@ -1,0 +1,851 @@
+// engine.cpp -- host side of libube: model packing, arenas, tape plans, the
+// launch sequence of an encode call, and the C ABI (include/ube.h,
+// include/ube_steps.h).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <vector>
+
+#include "kernels.h"
+#include "ube.h"
+#include "ube_steps.h"
+
+using namespace ube;
+
+namespace {
+
+// ------------------------------------------------------------------ outcome
+
+void set_outcome(ube_outcome_t *outcome, ube_status_t status, char const *message) {
+    if (outcome) {
+        outcome->status = status;
+        outcome->message = status == ube_status_success_k ? nullptr : message;
+    }
+}
+
+struct Failure {
+    ube_status_t status;
+    char const *message;
+};
+
+#define UBE_HIP(call)                                                                         \
+    do {                                                                                      \
+        hipError_t _e = (call);                                                               \
+        if (_e != hipSuccess) {                                                               \
+            if (_e == hipErrorOutOfMemory) throw Failure{ube_status_out_of_memory_k, "GPU out of memory"}; \
+            throw Failure{ube_status_device_k, "HIP runtime error in " #call};                \
+        }                                                                                     \
+    } while (0)
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ------------------------------------------------------------- kernel timer
+
+struct KernelTimer {
+    std::mutex mu;
+    int kernel = -1;
+    std::vector<hipEvent_t> events;  // pairs
+    size_t used = 0;
+};
+KernelTimer g_timer;
+
+// Launch `fn` (returns hipError_t) on `stream`, bracketed by events when `kernel` is being timed.
+template <typename Fn>
+void timed(ube_kernel_t kernel, hipStream_t stream, Fn fn) {
+    hipEvent_t begin = nullptr, end = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_timer.mu);
+        if (g_timer.kernel == (int)kernel && g_timer.used + 2 <= g_timer.events.size()) {
+            begin = g_timer.events[g_timer.used];
+            end = g_timer.events[g_timer.used + 1];
+            g_timer.used += 2;
+        }
+    }
+    if (begin) UBE_HIP(hipEventRecord(begin, stream));
+    UBE_HIP(fn());
+    if (end) UBE_HIP(hipEventRecord(end, stream));
+}
+
+}  // namespace
+
+// ===================================================================== model
+
+struct ube_model_handle_t {
+    int device = 0;
+    ube_geometry_t g{};
+    bool text = true;
+    char *mem = nullptr;
+    size_t bytes = 0;
+    uint16_t *embed = nullptr, *patch_t = nullptr, *wv = nullptr;
+    struct Layer {
+        uint16_t *wqkv, *wo, *wgu, *wd;
+        float *g1, *g2;
+    };
+    std::vector<Layer> layers;
+    float *gf = nullptr, *u = nullptr;
+    float2 *rope = nullptr;
+    int sec0 = 32, sec1 = 0;
+};
+
+namespace {
+
+bool row_width_supported(size_t D) {
+    if (D % 128 != 0 || D == 0) return false;
+    if (D % 512 == 0) return D / 512 <= 4;
+    if (D % 256 == 0) return (D / 256) % 2 == 1 && D / 256 <= 7;
+    return (D / 128) % 2 == 1 && D / 128 <= 7;
+}
+
+ube_geometry_t complete_geometry(ube_geometry_t g) {
+    if (!g.heads && g.hidden) g.heads = g.hidden / 64;
+    if (!g.ffn) g.ffn = 3 * g.hidden;
+    if (!g.vocab) g.vocab = 258;
+    if (!g.context) g.context = 1024;
+    if (!g.rope_axes) g.rope_axes = 1;
+    if (!g.patch_side) g.patch_side = 16;
+    if (!g.channels) g.channels = 3;
+    if (g.rope_base == 0.f) g.rope_base = 10000.f;
+    if (g.rms_epsilon == 0.f) g.rms_epsilon = 1e-6f;
+    if (g.quantization == ube_scalar_unknown_k) g.quantization = ube_scalar_bf16_k;
+    return g;
+}
+
+char const *check_geometry(ube_geometry_t const &g) {
+    if (!g.depth) return "depth must be positive";
+    if (!row_width_supported(g.hidden) || g.hidden > 1024) return "hidden must be a supported multiple of 128, <= 1024";
+    if (g.heads * 64 != g.hidden) return "head width must be 64";
+    if (g.heads > 16) return "at most 16 heads";
+    if (g.ffn % 64 != 0) return "ffn must be a multiple of 64";
+    if (g.context > 32767) return "context must be at most 32767";
+    if (g.rope_axes < 1 || g.rope_axes > 3) return "rope_axes must be 1, 2 or 3";
+    if (g.quantization != ube_scalar_bf16_k) return "only bf16 quantization is built";
+    if (g.vocab > 65535) return "vocab too large";
+    return nullptr;
+}
+
+// dst[c * rows + r] = src[r * cols + c]  (transpose a row-major [rows x cols] matrix)
+void transpose_into(uint16_t *dst, uint16_t const *src, size_t rows, size_t cols) {
+    for (size_t r = 0; r < rows; ++r)
+        for (size_t c = 0; c < cols; ++c) dst[c * rows + r] = src[r * cols + c];
+}
+
+float bf16_value(uint16_t b) {
+    uint32_t w = (uint32_t)b << 16;
+    float f;
+    std::memcpy(&f, &w, 4);
+    return f;
+}
+
+}  // namespace
+
+extern "C" void ube_model_init(ube_model_init_t *a) {
+    if (!a) return;
+    ube_outcome_t *outcome = a->outcome;
+    if (a->model) *a->model = nullptr;
+    ube_model_t m = nullptr;
+    try {
+        if (!a->model || !a->weights) throw Failure{ube_status_invalid_argument_k, "NULL model or weights"};
+        ube_geometry_t g = complete_geometry(a->geometry);
+        if (char const *why = check_geometry(g)) throw Failure{ube_status_unsupported_k, why};
+        ube_weights_t const &w = *a->weights;
+        bool text = w.embed != nullptr;
+        if (text && g.vocab < 256) throw Failure{ube_status_unsupported_k, "a byte vocabulary needs >= 256 rows"};
+        if (!text && !w.patch_proj) throw Failure{ube_status_invalid_argument_k, "neither embed nor patch_proj"};
+        if (!text && (g.patch_side != 16 || g.channels != 3))
+            throw Failure{ube_status_unsupported_k, "media frontends take 16x16 RGB patches"};
+        if (!w.w_qkv || !w.w_o || !w.w_gate || !w.w_up || !w.w_down || !w.attn_norm || !w.mlp_norm || !w.final_norm ||
+            !w.pool_query || !w.pool_wk || !w.pool_wv)
+            throw Failure{ube_status_invalid_argument_k, "missing weights"};
+        for (size_t l = 0; l < g.depth; ++l)
+            if (!w.w_qkv[l] || !w.w_o[l] || !w.w_gate[l] || !w.w_up[l] || !w.w_down[l] || !w.attn_norm[l] ||
+                !w.mlp_norm[l])
+                throw Failure{ube_status_invalid_argument_k, "missing block weights"};
+        int ndev = 0;
+        if (hipGetDeviceCount(&ndev) != hipSuccess || a->device < 0 || a->device >= ndev)
+            throw Failure{ube_status_device_k, "no such GPU"};
+        UBE_HIP(hipSetDevice(a->device));
+
+        const size_t D = g.hidden, F = g.ffn, H = g.heads, N = g.depth;
+        const size_t KP = g.patch_side * g.patch_side * g.channels;
+        // device layout
+        std::vector<size_t> offs;
+        size_t total = 0;
+        auto take = [&](size_t bytes) {
+            size_t o = total;
+            total = align_up(total + bytes, 256);
+            return o;
+        };
+        size_t o_embed = text ? take(g.vocab * D * 2) : 0;
+        size_t o_patch = text ? 0 : take(D * KP * 2);
+        std::vector<size_t> o_l(N * 6);
+        for (size_t l = 0; l < N; ++l) {
+            o_l[l * 6 + 0] = take(3 * D * D * 2);
+            o_l[l * 6 + 1] = take(D * D * 2);
+            o_l[l * 6 + 2] = take(2 * F * D * 2);
+            o_l[l * 6 + 3] = take(F * D * 2);
+            o_l[l * 6 + 4] = take(D * 4);
+            o_l[l * 6 + 5] = take(D * 4);
+        }
+        size_t o_gf = take(D * 4), o_u = take(H * D * 4), o_wv = take(D * D * 2);
+        size_t o_rope = take(g.context * 32 * sizeof(float2));
+
+        std::vector<char> host(total);
+        char *hb = host.data();
+        if (text) std::memcpy(hb + o_embed, w.embed, g.vocab * D * 2);
+        else transpose_into((uint16_t *)(hb + o_patch), w.patch_proj, KP, D);
+        for (size_t l = 0; l < N; ++l) {
+            transpose_into((uint16_t *)(hb + o_l[l * 6 + 0]), w.w_qkv[l], D, 3 * D);
+            transpose_into((uint16_t *)(hb + o_l[l * 6 + 1]), w.w_o[l], D, D);
+            // gate/up interleaved in blocks of 32 output columns: rows 64b + [0,32) gate, 64b + [32,64) up
+            uint16_t *gu = (uint16_t *)(hb + o_l[l * 6 + 2]);
+            for (size_t col = 0; col < F; ++col) {
+                const size_t b = col / 32, r = col % 32;
+                for (size_t k = 0; k < D; ++k) {
+                    gu[(64 * b + r) * D + k] = w.w_gate[l][k * F + col];
+                    gu[(64 * b + 32 + r) * D + k] = w.w_up[l][k * F + col];
+                }
+            }
+            transpose_into((uint16_t *)(hb + o_l[l * 6 + 3]), w.w_down[l], F, D);
+            std::memcpy(hb + o_l[l * 6 + 4], w.attn_norm[l], D * 4);
+            std::memcpy(hb + o_l[l * 6 + 5], w.mlp_norm[l], D * 4);
+        }
+        std::memcpy(hb + o_gf, w.final_norm, D * 4);
+        // pool keys folded into the query: u_h = W_k[:, head h] q_h / sqrt(64)
+        float *u = (float *)(hb + o_u);
+        for (size_t h = 0; h < H; ++h)
+            for (size_t f = 0; f < D; ++f) {
+                double acc = 0.0;
+                for (size_t e = 0; e < 64; ++e)
+                    acc += (double)bf16_value(w.pool_wk[f * D + h * 64 + e]) * (double)bf16_value(w.pool_query[h * 64 + e]);
+                u[h * D + f] = (float)(acc / 8.0);
+            }
+        std::memcpy(hb + o_wv, w.pool_wv, D * D * 2);
+        // rotary table: (cos, sin) of p * base^(-2j/64), double on the host
+        float2 *rope = (float2 *)(hb + o_rope);
+        for (size_t p = 0; p < g.context; ++p)
+            for (size_t j = 0; j < 32; ++j) {
+                double theta = std::pow((double)g.rope_base, -2.0 * (double)j / 64.0);
+                double phi = (double)p * theta;
+                rope[p * 32 + j] = float2{(float)std::cos(phi), (float)std::sin(phi)};
+            }
+
+        m = new ube_model_handle_t();
+        m->device = a->device;
+        m->g = g;
+        m->text = text;
+        m->bytes = total;
+        UBE_HIP(hipMalloc((void **)&m->mem, total));
+        UBE_HIP(hipMemcpy(m->mem, hb, total, hipMemcpyHostToDevice));
+        char *db = m->mem;
+        m->embed = text ? (uint16_t *)(db + o_embed) : nullptr;
+        m->patch_t = text ? nullptr : (uint16_t *)(db + o_patch);
+        m->layers.resize(N);
+        for (size_t l = 0; l < N; ++l)
+            m->layers[l] = {(uint16_t *)(db + o_l[l * 6 + 0]), (uint16_t *)(db + o_l[l * 6 + 1]),
+                            (uint16_t *)(db + o_l[l * 6 + 2]), (uint16_t *)(db + o_l[l * 6 + 3]),
+                            (float *)(db + o_l[l * 6 + 4]),    (float *)(db + o_l[l * 6 + 5])};
+        m->gf = (float *)(db + o_gf);
+        m->u = (float *)(db + o_u);
+        m->wv = (uint16_t *)(db + o_wv);
+        m->rope = (float2 *)(db + o_rope);
+        const int pairs = 32, axes = (int)g.rope_axes, base = pairs / axes, rem = pairs % axes;
+        m->sec0 = base + (0 < rem ? 1 : 0);
+        m->sec1 = axes >= 2 ? base + (1 < rem ? 1 : 0) : 0;
+        *a->model = m;
+        set_outcome(outcome, ube_status_success_k, nullptr);
+    } catch (Failure const &f) {
+        if (m) {
+            if (m->mem) (void)hipFree(m->mem);
+            delete m;
+        }
+        set_outcome(outcome, f.status, f.message);
+    } catch (std::bad_alloc const &) {
+        if (m) {
+            if (m->mem) (void)hipFree(m->mem);
+            delete m;
+        }
+        set_outcome(outcome, ube_status_out_of_memory_k, "host out of memory");
+    }
+}
+
+extern "C" void ube_model_describe(ube_model_describe_t *a) {
+    if (!a) return;
+    if (!a->model || !a->description) {
+        set_outcome(a->outcome, ube_status_invalid_argument_k, "NULL model or description");
+        return;
+    }
+    ube_model_t m = a->model;
+    ube_model_description_t &d = *a->description;
+    d.dimensions = m->g.hidden;
+    d.context = m->g.context;
+    d.depth = m->g.depth;
+    d.heads = m->g.heads;
+    d.ffn = m->g.ffn;
+    d.rope_axes = m->g.rope_axes;
+    d.quantization = m->g.quantization;
+    d.memory_usage = m->bytes;
+    d.device = m->device;
+    set_outcome(a->outcome, ube_status_success_k, nullptr);
+}
+
+extern "C" void ube_model_free(ube_model_t m) {
+    if (!m) return;
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(m->device);
+    (void)hipFree(m->mem);
+    (void)hipSetDevice(prev);
+    delete m;
+}
+
+// ===================================================================== arena
+
+struct ube_arena_handle_t {
+    int device = 0;
+    std::atomic<int> busy{0};
+    char *dev = nullptr;
+    size_t cap = 0;
+    char *pinned = nullptr;
+    size_t pinned_cap = 0;
+    hipEvent_t staged = nullptr;  // recorded after the last copy out of `pinned`
+    bool staged_pending = false;
+};
+
+extern "C" void ube_arena_init(ube_arena_init_t *a) {
+    if (!a) return;
+    if (!a->arena) {
+        set_outcome(a->outcome, ube_status_invalid_argument_k, "NULL arena output");
+        return;
+    }
+    *a->arena = nullptr;
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || a->device < 0 || a->device >= ndev) {
+        set_outcome(a->outcome, ube_status_device_k, "no such GPU");
+        return;
+    }
+    ube_arena_t ar = new (std::nothrow) ube_arena_handle_t();
+    if (!ar) {
+        set_outcome(a->outcome, ube_status_out_of_memory_k, "host out of memory");
+        return;
+    }
+    ar->device = a->device;
+    *a->arena = ar;
+    set_outcome(a->outcome, ube_status_success_k, nullptr);
+}
+
+extern "C" void ube_arena_free(ube_arena_t ar) {
+    if (!ar) return;
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(ar->device);
+    (void)hipDeviceSynchronize();
+    if (ar->dev) (void)hipFree(ar->dev);
+    if (ar->pinned) (void)hipHostFree(ar->pinned);
+    if (ar->staged) (void)hipEventDestroy(ar->staged);
+    (void)hipSetDevice(prev);
+    delete ar;
+}
+
+extern "C" size_t ube_arena_capacity(ube_arena_t ar) { return ar ? ar->cap : 0; }
+
+// ===================================================================== plan
+
+extern "C" ube_status_t ube_tape_plan(size_t const *offsets, size_t count, size_t context, uint32_t *lengths,
+                                      uint32_t *cu, ube_encode_stats_t *stats) {
+    if (!offsets || !cu || (count && !lengths)) return ube_status_invalid_argument_k;
+    size_t truncated = 0, tokens = 0;
+    cu[0] = 0;
+    for (size_t i = 0; i < count; ++i) {
+        if (offsets[i + 1] < offsets[i]) return ube_status_invalid_argument_k;
+        size_t len = offsets[i + 1] - offsets[i];
+        size_t kept = len > context ? context : len;
+        truncated += len > context;
+        lengths[i] = (uint32_t)kept;
+        tokens += kept;
+        if (tokens > 0x7fffffffull - 4096) return ube_status_invalid_argument_k;
+        cu[i + 1] = (uint32_t)tokens;
+    }
+    if (stats) stats->truncated = truncated, stats->tokens = tokens;
+    return ube_status_success_k;
+}
+
+namespace {
+
+struct Plan {
+    size_t count = 0, T = 0, truncated = 0;
+    std::vector<int> cu;            // count + 1
+    std::vector<int64_t> src;       // count: byte offset of each item in the device input
+    std::vector<int2> tiles;        // (item, first token) per 128-token tile
+    std::vector<MediaItem> media;   // media items
+    size_t input_lo = 0, input_hi = 0;  // tape data range the items read
+};
+
+void make_tiles(Plan &p) {
+    p.tiles.clear();
+    for (size_t i = 0; i < p.count; ++i)
+        for (int t = p.cu[i]; t < p.cu[i + 1]; t += kTileTokens) p.tiles.push_back(int2{(int)i, t});
+}
+
+// Device regions of one call.
+struct Layout {
+    size_t Tpad = 0;
+    size_t out, cu, src, tiles, media, input, x, h, a, qk, vt, o, xf, s, pos, patches, total;
+};
+
+Layout carve(ube_geometry_t const &g, Plan const &p, bool media, size_t input_bytes) {
+    Layout L{};
+    const size_t D = g.hidden, F = g.ffn, H = g.heads;
+    L.Tpad = align_up(p.T, 256) + kRowPad;
+    size_t total = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = total;
+        total = align_up(total + bytes, 256);
+        return o;
+    };
+    L.out = take(std::max<size_t>(p.count, 1) * D * 4);
+    L.cu = take((p.count + 1) * 4);
+    L.src = take(std::max<size_t>(p.count, 1) * 8);
+    L.tiles = take(std::max<size_t>(p.tiles.size(), 1) * 8);
+    L.media = take(media ? std::max<size_t>(p.count, 1) * sizeof(MediaItem) : 0);
+    L.input = take(input_bytes);
+    L.x = take(L.Tpad * D * 4);
+    L.h = take(L.Tpad * D * 2);
+    L.a = take(L.Tpad * F * 2);
+    L.qk = take(L.Tpad * 2 * D * 2);
+    L.vt = take(D * L.Tpad * 2);
+    L.o = take(L.Tpad * D * 2);
+    L.xf = take(L.Tpad * D * 2);
+    L.s = take(L.Tpad * H * 4);
+    L.pos = take(L.Tpad * 4 * 2);
+    L.patches = take(media ? L.Tpad * 768 * 2 : 0);
+    L.total = total;
+    return L;
+}
+
+bool pointer_on_device(void const *ptr, int device) {
+    hipPointerAttribute_t attr;
+    if (hipPointerGetAttributes(&attr, ptr) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return attr.type == hipMemoryTypeDevice && attr.device == device;
+}
+
+// Guards an arena for one call.
+struct ArenaLease {
+    ube_arena_t ar;
+    bool held = false;
+    explicit ArenaLease(ube_arena_t a) : ar(a) {
+        int expected = 0;
+        held = ar->busy.compare_exchange_strong(expected, 1);
+    }
+    ~ArenaLease() {
+        if (held) ar->busy.store(0);
+    }
+};
+
+struct EncodeRequest {
+    ube_model_t model;
+    ube_arena_t arena;
+    hipStream_t stream;
+    int completion;
+    ube_scalar_t outputs_scalar;
+    ube_rows_view_t *embeddings;
+    ube_encode_stats_t *stats;
+    float *trace;
+    void const *data;      // tape data
+    size_t const *offsets; // host
+    size_t count;
+};
+
+// Runs the whole encode for a prepared plan. `media` selects the patch frontend.
+void run_encode(EncodeRequest const &r, Plan &p, bool media) {
+    ube_model_t m = r.model;
+    ube_arena_t ar = r.arena;
+    ube_geometry_t const &g = m->g;
+    const int D = (int)g.hidden, F = (int)g.ffn, H = (int)g.heads;
+    const float eps = g.rms_epsilon;
+    hipStream_t st = r.stream;
+
+    // tape data: in place when it already lives on this GPU, else staged through the arena
+    const bool on_device = p.input_hi > p.input_lo ? pointer_on_device(r.data, m->device) : true;
+    const size_t input_bytes = on_device ? 0 : p.input_hi - p.input_lo;
+    if (on_device && ar->dev && p.input_hi > p.input_lo) {
+        char const *lo = (char const *)r.data + p.input_lo, *hi = (char const *)r.data + p.input_hi;
+        if (hi > ar->dev && lo < ar->dev + ar->cap)
+            throw Failure{ube_status_invalid_argument_k, "inputs lie inside the arena"};
+    }
+    Layout L = carve(g, p, media, input_bytes);
+
+    // grow the arena (only when outgrown)
+    if (L.total > ar->cap) {
+        UBE_HIP(hipStreamSynchronize(st));
+        if (ar->dev) UBE_HIP(hipFree(ar->dev));
+        ar->dev = nullptr;
+        ar->cap = 0;
+        size_t want = align_up(L.total, (size_t)1 << 20);
+        UBE_HIP(hipMalloc((void **)&ar->dev, want));
+        ar->cap = want;
+        UBE_HIP(hipMemsetAsync(ar->dev, 0, want, st));
+    }
+    char *db = ar->dev;
+
+    // host staging: cu, src, tiles, media items (+ tape bytes when host-resident)
+    const size_t meta_bytes = L.input - L.cu;
+    const size_t stage_bytes = meta_bytes + input_bytes;
+    if (ar->staged_pending) {
+        UBE_HIP(hipEventSynchronize(ar->staged));
+        ar->staged_pending = false;
+    }
+    if (stage_bytes > ar->pinned_cap) {
+        if (ar->pinned) UBE_HIP(hipHostFree(ar->pinned));
+        ar->pinned = nullptr;
+        ar->pinned_cap = 0;
+        size_t want = align_up(stage_bytes, (size_t)1 << 16);
+        UBE_HIP(hipHostMalloc((void **)&ar->pinned, want, 0));
+        ar->pinned_cap = want;
+    }
+    if (!ar->staged) UBE_HIP(hipEventCreateWithFlags(&ar->staged, hipEventDisableTiming));
+    char *hp = ar->pinned;
+    std::memset(hp, 0, meta_bytes);
+    std::memcpy(hp + (L.cu - L.cu), p.cu.data(), p.cu.size() * 4);
+    for (size_t i = 0; i < p.count; ++i)
+        ((int64_t *)(hp + (L.src - L.cu)))[i] = p.src[i] - (on_device ? 0 : (int64_t)p.input_lo);
+    if (!p.tiles.empty()) std::memcpy(hp + (L.tiles - L.cu), p.tiles.data(), p.tiles.size() * 8);
+    if (media && p.count) {
+        std::vector<MediaItem> items = p.media;
+        for (auto &it : items) it.pixel_offset -= on_device ? 0 : (int64_t)p.input_lo;
+        std::memcpy(hp + (L.media - L.cu), items.data(), items.size() * sizeof(MediaItem));
+    }
+    if (input_bytes) std::memcpy(hp + meta_bytes, (char const *)r.data + p.input_lo, input_bytes);
+    UBE_HIP(hipMemcpyAsync(db + L.cu, hp, stage_bytes, hipMemcpyHostToDevice, st));
+    UBE_HIP(hipEventRecord(ar->staged, st));
+    ar->staged_pending = true;
+
+    const uint8_t *input = on_device ? (const uint8_t *)r.data : (const uint8_t *)(db + L.input);
+    const int *cu = (const int *)(db + L.cu);
+    const int64_t *src = (const int64_t *)(db + L.src);
+    const int2 *tiles = (const int2 *)(db + L.tiles);
+    const int ntiles = (int)p.tiles.size();
+    float *x = (float *)(db + L.x);
+    uint16_t *h = (uint16_t *)(db + L.h), *act = (uint16_t *)(db + L.a), *qk = (uint16_t *)(db + L.qk);
+    uint16_t *vt = (uint16_t *)(db + L.vt), *o = (uint16_t *)(db + L.o), *xf = (uint16_t *)(db + L.xf);
+    float *s = (float *)(db + L.s);
+    int16_t *pos = (int16_t *)(db + L.pos);
+    const int T = (int)p.T, ldvt = (int)L.Tpad;
+
+    if (T > 0) {
+        // keys past the last token are masked; their values must still be finite (p = 0 times v)
+        UBE_HIP(hipMemset2DAsync(vt + T, (size_t)ldvt * 2, 0, 64 * 2, (size_t)D, st));
+        // ---- frontend
+        if (!media) {
+            timed(ube_kernel_gather_k, st, [&] {
+                return launch_gather_text(input, src, cu, tiles, ntiles, m->embed, m->layers[0].g1, x, h, pos, D, eps,
+                                          st);
+            });
+        } else {
+            uint16_t *patches = (uint16_t *)(db + L.patches);
+            timed(ube_kernel_patchify_k, st, [&] {
+                return launch_patchify(input, (const MediaItem *)(db + L.media), cu, tiles, ntiles, patches, pos,
+                                       (int)g.rope_axes, st);
+            });
+            GemmArgs ga{};
+            ga.w = m->patch_t, ga.x = patches, ga.M = T, ga.N = D, ga.K = 768;
+            ga.out_f32 = x, ga.ld_f32 = D, ga.scale = 1.0f / 255.0f;
+            timed(ube_kernel_gemm_patch_k, st, [&] { return launch_gemm(kEpiPatch, ga, st); });
+            timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm(x, m->layers[0].g1, h, T, D, eps, st); });
+        }
+        if (r.trace) UBE_HIP(hipMemcpyAsync(r.trace, x, (size_t)T * D * 4, hipMemcpyDeviceToDevice, st));
+        // ---- blocks
+        for (size_t l = 0; l < g.depth; ++l) {
+            auto const &Wl = m->layers[l];
+            if (l > 0)
+                timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm(x, Wl.g1, h, T, D, eps, st); });
+            GemmArgs qa{};
+            qa.w = Wl.wqkv, qa.x = h, qa.M = T, qa.N = 3 * D, qa.K = D;
+            qa.out_bf16 = qk, qa.ld_out = 2 * D, qa.vt = vt, qa.ld_vt = ldvt, qa.pos = pos, qa.rope = m->rope;
+            qa.D = D, qa.sec0 = m->sec0, qa.sec1 = m->sec1;
+            timed(ube_kernel_gemm_qkv_k, st, [&] { return launch_gemm(kEpiQkv, qa, st); });
+            timed(ube_kernel_attention_k, st, [&] {
+                return launch_attention(qk, qk + D, 2 * D, vt, ldvt, o, D, cu, tiles, ntiles, H, st);
+            });
+            GemmArgs oa{};
+            oa.w = Wl.wo, oa.x = o, oa.M = T, oa.N = D, oa.K = D, oa.out_f32 = x, oa.ld_f32 = D;
+            timed(ube_kernel_gemm_out_k, st, [&] { return launch_gemm(kEpiResid, oa, st); });
+            timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm(x, Wl.g2, h, T, D, eps, st); });
+            GemmArgs ua{};
+            ua.w = Wl.wgu, ua.x = h, ua.M = T, ua.N = 2 * F, ua.K = D, ua.out_bf16 = act, ua.ld_out = F;
+            timed(ube_kernel_gemm_gate_up_k, st, [&] { return launch_gemm(kEpiSwiglu, ua, st); });
+            GemmArgs da{};
+            da.w = Wl.wd, da.x = act, da.M = T, da.N = D, da.K = F, da.out_f32 = x, da.ld_f32 = D;
+            timed(ube_kernel_gemm_down_k, st, [&] { return launch_gemm(kEpiResid, da, st); });
+            if (r.trace)
+                UBE_HIP(hipMemcpyAsync(r.trace + (l + 1) * (size_t)T * D, x, (size_t)T * D * 4,
+                                       hipMemcpyDeviceToDevice, st));
+        }
+        timed(ube_kernel_final_norm_k, st,
+              [&] { return launch_final_norm_scores(x, m->gf, m->u, xf, s, T, D, H, eps, st); });
+    }
+    const bool bf16_out = r.outputs_scalar == ube_scalar_bf16_k;
+    const size_t row_bytes = (size_t)D * (bf16_out ? 2 : 4);
+    if (p.count) {
+        timed(ube_kernel_pool_k, st, [&] {
+            return launch_pool(xf, s, cu, (int)p.count, m->wv, db + L.out, bf16_out ? 1 : 0, row_bytes, D, H, st);
+        });
+    }
+    if (r.completion == 0) UBE_HIP(hipStreamSynchronize(st));
+    UBE_HIP(hipGetLastError());
+    *r.embeddings = ube_rows_view_t{p.count ? db + L.out : db + L.out, p.count, (size_t)D, row_bytes,
+                                    bf16_out ? ube_scalar_bf16_k : ube_scalar_f32_k};
+    if (r.stats) r.stats->truncated = p.truncated, r.stats->tokens = p.T;
+}
+
+void check_common(ube_model_t model, ube_arena_t arena, ube_rows_view_t *embeddings, ube_scalar_t outputs_scalar) {
+    if (!embeddings) throw Failure{ube_status_invalid_argument_k, "NULL embeddings output"};
+    if (!model) throw Failure{ube_status_invalid_argument_k, "NULL model"};
+    if (!arena) throw Failure{ube_status_invalid_argument_k, "NULL arena"};
+    if (outputs_scalar != ube_scalar_unknown_k && outputs_scalar != ube_scalar_f32_k &&
+        outputs_scalar != ube_scalar_bf16_k)
+        throw Failure{ube_status_invalid_argument_k, "outputs_scalar must be f32 or bf16"};
+    if (arena->device != model->device) throw Failure{ube_status_device_k, "arena and model on different GPUs"};
+}
+
+template <typename Body>
+void guarded(ube_outcome_t *outcome, ube_rows_view_t *embeddings, ube_arena_t arena, Body body) {
+    if (embeddings) *embeddings = ube_rows_view_t{nullptr, 0, 0, 0, ube_scalar_unknown_k};
+    try {
+        if (!arena) throw Failure{ube_status_invalid_argument_k, "NULL arena"};
+        ArenaLease lease(arena);
+        if (!lease.held) throw Failure{ube_status_contended_k, "the arena is serving another call"};
+        UBE_HIP(hipSetDevice(arena->device));
+        body();
+        set_outcome(outcome, ube_status_success_k, nullptr);
+    } catch (Failure const &f) {
+        if (embeddings) *embeddings = ube_rows_view_t{nullptr, 0, 0, 0, ube_scalar_unknown_k};
+        set_outcome(outcome, f.status, f.message);
+    } catch (std::bad_alloc const &) {
+        if (embeddings) *embeddings = ube_rows_view_t{nullptr, 0, 0, 0, ube_scalar_unknown_k};
+        set_outcome(outcome, ube_status_out_of_memory_k, "host out of memory");
+    }
+}
+
+}  // namespace
+
+extern "C" void ube_text_encode(ube_text_encode_t *a) {
+    if (!a) return;
+    guarded(a->outcome, a->embeddings, a->arena, [&] {
+        check_common(a->model, a->arena, a->embeddings, a->outputs_scalar);
+        if (!a->model->text) throw Failure{ube_status_unsupported_k, "the model has no byte frontend"};
+        const size_t count = a->texts.count;
+        if (count && (!a->texts.offsets || !a->texts.data))
+            throw Failure{ube_status_invalid_argument_k, "NULL tape"};
+        Plan p;
+        p.count = count;
+        p.cu.resize(count + 1);
+        std::vector<uint32_t> lengths(count), cu(count + 1);
+        ube_encode_stats_t st{};
+        static const size_t zero = 0;
+        if (ube_tape_plan(count ? a->texts.offsets : &zero, count, a->model->g.context, lengths.data(), cu.data(),
+                          &st) != ube_status_success_k)
+            throw Failure{ube_status_invalid_argument_k, "tape offsets decrease"};
+        p.T = st.tokens;
+        p.truncated = st.truncated;
+        p.src.resize(count);
+        for (size_t i = 0; i <= count; ++i) p.cu[i] = (int)cu[i];
+        for (size_t i = 0; i < count; ++i) p.src[i] = (int64_t)a->texts.offsets[i];
+        if (count) {
+            p.input_lo = a->texts.offsets[0];
+            p.input_hi = a->texts.offsets[0];
+            for (size_t i = 0; i < count; ++i)
+                p.input_hi = std::max(p.input_hi, a->texts.offsets[i] + lengths[i]);
+        }
+        make_tiles(p);
+        EncodeRequest r{a->model, a->arena, (hipStream_t)a->stream, a->completion, a->outputs_scalar,
+                        a->embeddings, a->stats, a->trace_residual, a->texts.data, a->texts.offsets, count};
+        run_encode(r, p, false);
+    });
+}
+
+namespace {
+
+void media_encode(ube_model_t model, ube_arena_t arena, void *stream, int completion, ube_tape_view_t tape,
+                  size_t const *frame_counts, size_t const *heights, size_t const *widths, ube_scalar_t scalar,
+                  ube_rows_view_t *embeddings, ube_encode_stats_t *stats, float *trace, int axes_expected) {
+    check_common(model, arena, embeddings, scalar);
+    if (model->text) throw Failure{ube_status_unsupported_k, "the model has no patch frontend"};
+    if ((int)model->g.rope_axes != axes_expected)
+        throw Failure{ube_status_unsupported_k, "the model's rotary axes do not fit this input"};
+    const size_t count = tape.count;
+    if (count && (!tape.offsets || !tape.data || !heights || !widths))
+        throw Failure{ube_status_invalid_argument_k, "NULL tape or sizes"};
+    const size_t ps = model->g.patch_side, ch = model->g.channels;
+    Plan p;
+    p.count = count;
+    p.cu.assign(count + 1, 0);
+    p.src.assign(count, 0);
+    p.media.resize(count);
+    size_t T = 0;
+    for (size_t i = 0; i < count; ++i) {
+        if (tape.offsets[i + 1] < tape.offsets[i]) throw Failure{ube_status_invalid_argument_k, "tape offsets decrease"};
+        const size_t Hh = heights[i], Ww = widths[i], Fr = frame_counts ? frame_counts[i] : 1;
+        if (Hh % ps || Ww % ps || !Hh || !Ww || !Fr)
+            throw Failure{ube_status_shape_mismatch_k, "a side is not a positive multiple of the patch side"};
+        if (tape.offsets[i + 1] - tape.offsets[i] != Fr * Hh * Ww * ch)
+            throw Failure{ube_status_shape_mismatch_k, "item bytes differ from frames x height x width x channels"};
+        const size_t n = Fr * (Hh / ps) * (Ww / ps);
+        if (n > model->g.context) throw Failure{ube_status_shape_mismatch_k, "patch count exceeds the context"};
+        p.media[i] = MediaItem{(int64_t)tape.offsets[i], (int)Fr, (int)(Hh / ps), (int)(Ww / ps), (int)Ww};
+        T += n;
+        if (T > 0x7fffffffull - 4096) throw Failure{ube_status_invalid_argument_k, "too many tokens"};
+        p.cu[i + 1] = (int)T;
+        p.src[i] = (int64_t)tape.offsets[i];
+    }
+    p.T = T;
+    if (count) p.input_lo = tape.offsets[0], p.input_hi = tape.offsets[count];
+    make_tiles(p);
+    EncodeRequest r{model, arena, (hipStream_t)stream, completion, scalar, embeddings, stats, trace, tape.data,
+                    tape.offsets, count};
+    run_encode(r, p, true);
+}
+
+}  // namespace
+
+extern "C" void ube_image_encode_pixels(ube_image_encode_pixels_t *a) {
+    if (!a) return;
+    guarded(a->outcome, a->embeddings, a->arena, [&] {
+        media_encode(a->model, a->arena, a->stream, a->completion, a->pixels, nullptr, a->heights, a->widths,
+                     a->outputs_scalar, a->embeddings, a->stats, a->trace_residual, 2);
+    });
+}
+
+extern "C" void ube_video_encode_frames(ube_video_encode_frames_t *a) {
+    if (!a) return;
+    guarded(a->outcome, a->embeddings, a->arena, [&] {
+        if (a->frames.count && !a->frame_counts) throw Failure{ube_status_invalid_argument_k, "NULL frame counts"};
+        media_encode(a->model, a->arena, a->stream, a->completion, a->frames, a->frame_counts, a->heights, a->widths,
+                     a->outputs_scalar, a->embeddings, a->stats, a->trace_residual, 3);
+    });
+}
+
+extern "C" char const *ube_status_name(ube_status_t s) {
+    switch (s) {
+        case ube_status_success_k: return "success";
+        case ube_status_invalid_argument_k: return "invalid_argument";
+        case ube_status_shape_mismatch_k: return "shape_mismatch";
+        case ube_status_out_of_memory_k: return "out_of_memory";
+        case ube_status_device_k: return "device";
+        case ube_status_contended_k: return "contended";
+        case ube_status_unsupported_k: return "unsupported";
+        case ube_status_internal_k: return "internal";
+    }
+    return "unknown";
+}
+
+// ===================================================================== steps
+
+namespace {
+ube_status_t step_status(hipError_t e) {
+    if (e == hipSuccess) return ube_status_success_k;
+    if (e == hipErrorInvalidValue) return ube_status_invalid_argument_k;
+    return ube_status_device_k;
+}
+}  // namespace
+
+extern "C" ube_status_t ube_step_gemm(void const *w, void const *x, void *y, size_t M, size_t N, size_t K,
+                                      void *stream) {
+    if (!w || !x || !y || N % 128 || K % 64 || !N || !K || M > 0x7fffffff) return ube_status_invalid_argument_k;
+    GemmArgs a{};
+    a.w = (const uint16_t *)w, a.x = (const uint16_t *)x, a.M = (int)M, a.N = (int)N, a.K = (int)K;
+    a.out_bf16 = (uint16_t *)y, a.ld_out = (int)N;
+    return step_status(launch_gemm(kEpiStore, a, (hipStream_t)stream));
+}
+
+extern "C" ube_status_t ube_step_rmsnorm(float const *x, float const *gain, void *h, size_t T, size_t D, float eps,
+                                         void *stream) {
+    if (!x || !gain || !h || !row_width_supported(D) || T > 0x7fffffff) return ube_status_invalid_argument_k;
+    return step_status(launch_rmsnorm(x, gain, (uint16_t *)h, (int)T, (int)D, eps, (hipStream_t)stream));
+}
+
+extern "C" ube_status_t ube_step_attention(void const *q, void const *k, size_t ldqk, void const *vt, size_t ldvt,
+                                           void *o, size_t ldo, uint32_t const *cu_host, size_t count, size_t heads,
+                                           void *stream) {
+    if (!q || !k || !vt || !o || !cu_host || !heads) return ube_status_invalid_argument_k;
+    std::vector<int> cu(count + 1);
+    Plan p;
+    p.count = count;
+    for (size_t i = 0; i <= count; ++i) {
+        if (i && cu_host[i] < cu_host[i - 1]) return ube_status_invalid_argument_k;
+        cu[i] = (int)cu_host[i];
+    }
+    p.cu = cu;
+    make_tiles(p);
+    if (ldvt < (size_t)cu[count] + kRowPad) return ube_status_invalid_argument_k;
+    void *dcu = nullptr, *dtiles = nullptr;
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e = hipMalloc(&dcu, (count + 1) * 4);
+    if (e == hipSuccess) e = hipMalloc(&dtiles, std::max<size_t>(p.tiles.size(), 1) * 8);
+    if (e == hipSuccess) e = hipMemcpyAsync(dcu, cu.data(), (count + 1) * 4, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess && !p.tiles.empty())
+        e = hipMemcpyAsync(dtiles, p.tiles.data(), p.tiles.size() * 8, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess)
+        e = launch_attention((const uint16_t *)q, (const uint16_t *)k, (int)ldqk, (const uint16_t *)vt, (int)ldvt,
+                             (uint16_t *)o, (int)ldo, (const int *)dcu, (const int2 *)dtiles, (int)p.tiles.size(),
+                             (int)heads, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (dcu) (void)hipFree(dcu);
+    if (dtiles) (void)hipFree(dtiles);
+    return step_status(e);
+}
+
+extern "C" ube_status_t ube_kernel_timer_start(ube_kernel_t kernel, size_t max_launches) {
+    if ((int)kernel < 0 || kernel >= ube_kernel_count_k || !max_launches) return ube_status_invalid_argument_k;
+    std::lock_guard<std::mutex> lock(g_timer.mu);
+    for (hipEvent_t e : g_timer.events) (void)hipEventDestroy(e);
+    g_timer.events.clear();
+    g_timer.used = 0;
+    g_timer.kernel = -1;
+    for (size_t i = 0; i < 2 * max_launches; ++i) {
+        hipEvent_t e;
+        if (hipEventCreate(&e) != hipSuccess) {
+            for (hipEvent_t d : g_timer.events) (void)hipEventDestroy(d);
+            g_timer.events.clear();
+            return ube_status_device_k;
+        }
+        g_timer.events.push_back(e);
+    }
+    g_timer.kernel = (int)kernel;
+    return ube_status_success_k;
+}
+
+extern "C" ube_status_t ube_kernel_timer_stop(double *total_ms, size_t *launches) {
+    std::lock_guard<std::mutex> lock(g_timer.mu);
+    double total = 0.0;
+    ube_status_t status = ube_status_success_k;
+    for (size_t i = 0; i + 1 < g_timer.used; i += 2) {
+        float ms = 0.f;
+        if (hipEventSynchronize(g_timer.events[i + 1]) != hipSuccess ||
+            hipEventElapsedTime(&ms, g_timer.events[i], g_timer.events[i + 1]) != hipSuccess) {
+            status = ube_status_device_k;
+            break;
+        }
+        total += ms;
+    }
+    if (total_ms) *total_ms = total;
+    if (launches) *launches = g_timer.used / 2;
+    for (hipEvent_t e : g_timer.events) (void)hipEventDestroy(e);
+    g_timer.events.clear();
+    g_timer.used = 0;
+    g_timer.kernel = -1;
+    return status;
+}
+
+extern "C" char const *ube_kernel_name(ube_kernel_t k) {
+    static char const *names[] = {"gather", "patchify", "rmsnorm", "gemm_patch", "gemm_qkv", "attention",
+                                  "gemm_out", "gemm_gate_up", "gemm_down", "final_norm", "pool"};
+    return ((int)k >= 0 && k < ube_kernel_count_k) ? names[k] : "unknown";
+}

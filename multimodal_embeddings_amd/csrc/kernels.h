@@ -1,0 +1,72 @@
+// kernels.h -- launch interface of the gfx950 kernels of the encoder (internal to libube).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ube {
+
+// Rows of every activation buffer past the last token; reads of a partial
+// tile stay inside the allocation and see finite values.
+constexpr int kRowPad = 256;
+// Tokens per work tile of the gather, patchify and attention kernels.
+constexpr int kTileTokens = 128;
+
+enum Epilogue : int {
+    kEpiStore = 0,   // C = bf16(acc)                                   [M x N], ld
+    kEpiQkv = 1,     // rotary on q, k -> qk [M x 2D]; v -> vt [D x ldvt] (feature-major)
+    kEpiResid = 2,   // x[M x N] += acc (fp32)
+    kEpiSwiglu = 3,  // interleaved gate/up blocks of 32 -> a = bf16(SiLU(g) * u)   [M x N/2]
+    kEpiPatch = 4,   // x = acc * scale (fp32)
+};
+
+struct GemmArgs {
+    const uint16_t *w;  // [N x K] bf16, K contiguous (packed weights)
+    const uint16_t *x;  // [M_alloc x K] bf16 activations, M_alloc >= round_up(M, 256)
+    int M, N, K;
+    uint16_t *out_bf16;
+    int ld_out;
+    float *out_f32;
+    int ld_f32;
+    uint16_t *vt;
+    int ld_vt;
+    const int16_t *pos;   // [M_alloc x 4] rotary coordinates per token
+    const float2 *rope;   // [positions x 32] (cos, sin)
+    int D;                // width of q, k, v (QKV epilogue)
+    int sec0, sec1;       // rotary pair sections: axis 0 for j < sec0, 1 for j < sec0+sec1, else 2
+    float scale;          // patch epilogue scale
+};
+
+hipError_t launch_gemm(int epilogue, const GemmArgs &args, hipStream_t stream);
+
+// Byte gather + RMSNorm (layer-0 attention norm): tiles are (item, first token).
+hipError_t launch_gather_text(const uint8_t *data, const int64_t *src, const int *cu, const int2 *tiles,
+                              int ntiles, const uint16_t *embed, const float *gain, float *x, uint16_t *h,
+                              int16_t *pos, int D, float eps, hipStream_t stream);
+
+// Patch rows (bf16 [T x 768], values 0..255) and rotary coordinates.
+struct MediaItem {
+    int64_t pixel_offset;  // byte offset of the item in the tape data
+    int frames, grid_h, grid_w, width;
+};
+hipError_t launch_patchify(const uint8_t *pixels, const MediaItem *items, const int *cu, const int2 *tiles,
+                           int ntiles, uint16_t *patches, int16_t *pos, int axes, hipStream_t stream);
+
+hipError_t launch_rmsnorm(const float *x, const float *gain, uint16_t *h, int T, int D, float eps,
+                          hipStream_t stream);
+
+hipError_t launch_attention(const uint16_t *q, const uint16_t *k, int ldqk, const uint16_t *vt, int ldvt,
+                            uint16_t *o, int ldo, const int *cu, const int2 *tiles, int ntiles, int heads,
+                            hipStream_t stream);
+
+// Final RMSNorm -> xf (bf16) and pool scores s[t][h] = xf_t . u_h (fp32).
+hipError_t launch_final_norm_scores(const float *x, const float *gain, const float *u, uint16_t *xf, float *s,
+                                    int T, int D, int H, float eps, hipStream_t stream);
+
+// Per item: softmax of the scores over the item's tokens per head,
+// z_h = sum_t p_t,h xf_t, pooled_h = z_h W_v[:, head h]; empty items -> 0.
+hipError_t launch_pool(const uint16_t *xf, const float *s, const int *cu, int count, const uint16_t *wv, void *out,
+                       int out_bf16, size_t out_stride, int D, int H, hipStream_t stream);
+
+}  // namespace ube

@@ -1,0 +1,773 @@
+// kernels.hip -- gfx950 kernels of the uniform byte encoder's forward pass.
+//
+// Steps (UForm documentation, "UForm" page, "Architecture & Goals" and
+// "Precision by Design"): byte gather, RMSNorm, QKV projection with multi-axis
+// rotary positions, bidirectional varlen attention, output projection and
+// residual, RMSNorm, SwiGLU MLP and residual, final RMSNorm, attention pooling
+// ("UForm" page, FAQ "Why attention pooling instead of mean pooling?").
+// Storage is bf16, accumulation and normalisation fp32, the residual stream fp32.
+//
+// MFMA: v_mfma_f32_32x32x16_bf16. Lane l of a wave supplies row (l % 32) of the
+// A operand and column (l % 32) of the B operand, each as 8 consecutive k values
+// of half (l / 32); both operands use the same (half, slot) -> k assignment, so
+// any consistent k permutation gives the same product. The 32x32 fp32 result
+// sits in lane l, register r = 4i + j at row 8i + 4(l / 32) + j, column l % 32.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace ube {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16(float v) {
+    __bf16 b = (__bf16)v;  // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
+    return (uint32_t)__builtin_bit_cast(uint16_t, b);
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) { return f32_to_bf16(a) | (f32_to_bf16(b) << 16); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+    return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+    return v;
+}
+
+// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
+// b % 8). This remap gives every XCD one contiguous range of logical tiles, so
+// tiles that share operands share that XCD's L2.
+__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
+    int xcd = bid & 7, slot = bid >> 3;
+    int q = nblocks >> 3, r = nblocks & 7;
+    return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
+}
+
+// =========================================================== row kernels
+//
+// One wave per token row. Lane l holds features c*64*V + l*V + [0, V) for
+// chunks c < C (D = 64*V*C): coalesced 64*V-float spans per chunk.
+
+template <int V>
+struct RowIO;
+
+template <>
+struct RowIO<2> {
+    __device__ static void load_f32(const float *p, float *v) {
+        f32x2 a = *(const f32x2 *)p;
+        v[0] = a.x, v[1] = a.y;
+    }
+    __device__ static void store_f32(float *p, const float *v) { *(f32x2 *)p = f32x2{v[0], v[1]}; }
+    __device__ static void load_bf16(const uint16_t *p, float *v) {
+        uint32_t a = *(const uint32_t *)p;
+        v[0] = bf16_to_f32(a & 0xffff), v[1] = bf16_to_f32(a >> 16);
+    }
+    __device__ static void store_bf16(uint16_t *p, const float *v) { *(uint32_t *)p = pack2(v[0], v[1]); }
+};
+
+template <>
+struct RowIO<4> {
+    __device__ static void load_f32(const float *p, float *v) {
+        f32x4 a = *(const f32x4 *)p;
+        v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w;
+    }
+    __device__ static void store_f32(float *p, const float *v) { *(f32x4 *)p = f32x4{v[0], v[1], v[2], v[3]}; }
+    __device__ static void load_bf16(const uint16_t *p, float *v) {
+        u32x2 a = *(const u32x2 *)p;
+        v[0] = bf16_to_f32(a.x & 0xffff), v[1] = bf16_to_f32(a.x >> 16);
+        v[2] = bf16_to_f32(a.y & 0xffff), v[3] = bf16_to_f32(a.y >> 16);
+    }
+    __device__ static void store_bf16(uint16_t *p, const float *v) {
+        *(u32x2 *)p = u32x2{pack2(v[0], v[1]), pack2(v[2], v[3])};
+    }
+};
+
+template <>
+struct RowIO<8> {
+    __device__ static void load_f32(const float *p, float *v) {
+        RowIO<4>::load_f32(p, v);
+        RowIO<4>::load_f32(p + 4, v + 4);
+    }
+    __device__ static void store_f32(float *p, const float *v) {
+        RowIO<4>::store_f32(p, v);
+        RowIO<4>::store_f32(p + 4, v + 4);
+    }
+    __device__ static void load_bf16(const uint16_t *p, float *v) {
+        u32x4 a = *(const u32x4 *)p;
+        uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[2 * i] = bf16_to_f32(w[i] & 0xffff), v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+    __device__ static void store_bf16(uint16_t *p, const float *v) {
+        *(u32x4 *)p = u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+    }
+};
+
+// x row (fp32, in registers) -> h = bf16(x * g / sqrt(mean(x^2) + eps)).
+template <int V, int C>
+__device__ __forceinline__ void norm_store(float (&v)[C][V], const float *gain, uint16_t *hrow, int D, float eps,
+                                           int lane) {
+    float ss = 0.f;
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int i = 0; i < V; ++i) ss += v[c][i] * v[c][i];
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+        const int f = c * 64 * V + lane * V;
+        float g[V], o[V];
+        if constexpr (V == 2) {
+            f32x2 gg = *(const f32x2 *)(gain + f);
+            g[0] = gg.x, g[1] = gg.y;
+        } else {
+#pragma unroll
+            for (int i = 0; i < V; i += 4) {
+                f32x4 gg = *(const f32x4 *)(gain + f + i);
+                g[i] = gg.x, g[i + 1] = gg.y, g[i + 2] = gg.z, g[i + 3] = gg.w;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < V; ++i) o[i] = v[c][i] * inv * g[i];
+        RowIO<V>::store_bf16(hrow + f, o);
+    }
+}
+
+template <int V, int C>
+__global__ __launch_bounds__(256) void k_gather_text(const uint8_t *__restrict__ data, const int64_t *__restrict__ src,
+                                                     const int *__restrict__ cu, const int2 *__restrict__ tiles,
+                                                     const uint16_t *__restrict__ embed,
+                                                     const float *__restrict__ gain, float *__restrict__ x,
+                                                     uint16_t *__restrict__ h, int16_t *__restrict__ pos, int D,
+                                                     float eps) {
+    const int2 tile = tiles[blockIdx.x];
+    const int item = tile.x, start = cu[item], end = min(tile.y + kTileTokens, cu[item + 1]);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int t = tile.y + wave; t < end; t += 4) {
+        const int local = t - start;
+        const uint32_t byte = data[src[item] + local];
+        float v[C][V];
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int f = c * 64 * V + lane * V;
+            RowIO<V>::load_bf16(embed + (size_t)byte * D + f, v[c]);
+            RowIO<V>::store_f32(x + (size_t)t * D + f, v[c]);
+        }
+        norm_store<V, C>(v, gain, h + (size_t)t * D, D, eps, lane);
+        if (lane == 0) *(u32x2 *)(pos + (size_t)t * 4) = u32x2{(uint32_t)(local & 0xffff), 0u};
+    }
+}
+
+template <int V, int C>
+__global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, const float *__restrict__ gain,
+                                                 uint16_t *__restrict__ h, int T, int D, float eps) {
+    const int lane = threadIdx.x & 63;
+    const int waves = gridDim.x * 4;
+    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += waves) {
+        float v[C][V];
+#pragma unroll
+        for (int c = 0; c < C; ++c) RowIO<V>::load_f32(x + (size_t)t * D + c * 64 * V + lane * V, v[c]);
+        norm_store<V, C>(v, gain, h + (size_t)t * D, D, eps, lane);
+    }
+}
+
+template <int V, int C>
+__global__ __launch_bounds__(256) void k_final_norm_scores(const float *__restrict__ x, const float *__restrict__ gain,
+                                                           const float *__restrict__ u, uint16_t *__restrict__ xf,
+                                                           float *__restrict__ s, int T, int D, int H, float eps) {
+    extern __shared__ float su[];  // u [H x D]
+    for (int i = threadIdx.x; i < H * D; i += 256) su[i] = u[i];
+    __syncthreads();
+    const int lane = threadIdx.x & 63;
+    const int waves = gridDim.x * 4;
+    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += waves) {
+        float v[C][V];
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            RowIO<V>::load_f32(x + (size_t)t * D + c * 64 * V + lane * V, v[c]);
+#pragma unroll
+            for (int i = 0; i < V; ++i) ss += v[c][i] * v[c][i];
+        }
+        ss = wave_sum(ss);
+        const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int f = c * 64 * V + lane * V;
+#pragma unroll
+            for (int i = 0; i < V; ++i) v[c][i] = v[c][i] * inv * gain[f + i];
+            RowIO<V>::store_bf16(xf + (size_t)t * D + f, v[c]);
+        }
+        for (int hd = 0; hd < H; ++hd) {
+            float dot = 0.f;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const int f = c * 64 * V + lane * V;
+#pragma unroll
+                for (int i = 0; i < V; ++i) dot += v[c][i] * su[hd * D + f + i];
+            }
+            dot = wave_sum(dot);
+            if (lane == 0) s[(size_t)t * H + hd] = dot;
+        }
+    }
+}
+
+// (V, C) with D = 64*V*C, C <= 8.
+#define UBE_ROW_DISPATCH(D, ...)                         \
+    do {                                                         \
+        const int _n = (D) / 128;                                \
+        if ((D) % 512 == 0 && (D) / 512 <= 8) {                  \
+            switch ((D) / 512) {                                 \
+                case 1: { constexpr int V = 8, C = 1; __VA_ARGS__; } break; \
+                case 2: { constexpr int V = 8, C = 2; __VA_ARGS__; } break; \
+                case 3: { constexpr int V = 8, C = 3; __VA_ARGS__; } break; \
+                case 4: { constexpr int V = 8, C = 4; __VA_ARGS__; } break; \
+                default: return hipErrorInvalidValue;            \
+            }                                                    \
+        } else if ((D) % 256 == 0) {                             \
+            switch ((D) / 256) {                                 \
+                case 1: { constexpr int V = 4, C = 1; __VA_ARGS__; } break; \
+                case 3: { constexpr int V = 4, C = 3; __VA_ARGS__; } break; \
+                case 5: { constexpr int V = 4, C = 5; __VA_ARGS__; } break; \
+                case 7: { constexpr int V = 4, C = 7; __VA_ARGS__; } break; \
+                default: return hipErrorInvalidValue;            \
+            }                                                    \
+        } else {                                                 \
+            switch (_n) {                                        \
+                case 1: { constexpr int V = 2, C = 1; __VA_ARGS__; } break; \
+                case 3: { constexpr int V = 2, C = 3; __VA_ARGS__; } break; \
+                case 5: { constexpr int V = 2, C = 5; __VA_ARGS__; } break; \
+                case 7: { constexpr int V = 2, C = 7; __VA_ARGS__; } break; \
+                default: return hipErrorInvalidValue;            \
+            }                                                    \
+        }                                                        \
+    } while (0)
+
+hipError_t launch_gather_text(const uint8_t *data, const int64_t *src, const int *cu, const int2 *tiles,
+                              int ntiles, const uint16_t *embed, const float *gain, float *x, uint16_t *h,
+                              int16_t *pos, int D, float eps, hipStream_t stream) {
+    if (ntiles == 0) return hipSuccess;
+    UBE_ROW_DISPATCH(D, (k_gather_text<V, C><<<ntiles, 256, 0, stream>>>(data, src, cu, tiles, embed, gain, x, h,
+                                                                           pos, D, eps)));
+    return hipGetLastError();
+}
+
+static int row_grid(int T) {
+    int blocks = (T + 3) / 4;
+    return blocks < 8192 ? blocks : 8192;
+}
+
+hipError_t launch_rmsnorm(const float *x, const float *gain, uint16_t *h, int T, int D, float eps,
+                          hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    UBE_ROW_DISPATCH(D, (k_rmsnorm<V, C><<<row_grid(T), 256, 0, stream>>>(x, gain, h, T, D, eps)));
+    return hipGetLastError();
+}
+
+hipError_t launch_final_norm_scores(const float *x, const float *gain, const float *u, uint16_t *xf, float *s,
+                                    int T, int D, int H, float eps, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    const size_t lds = (size_t)H * D * sizeof(float);
+    UBE_ROW_DISPATCH(D, {
+        if (lds > 65536) {
+            hipError_t e = hipFuncSetAttribute((const void *)k_final_norm_scores<V, C>,
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
+        k_final_norm_scores<V, C><<<row_grid(T), 256, lds, stream>>>(x, gain, u, xf, s, T, D, H, eps);
+    });
+    return hipGetLastError();
+}
+
+// =========================================================== patchify
+//
+// Token (f, r, c) of an item: the 16x16x3 patch at grid (r, c) of frame f,
+// element k = (py*16 + px)*3 + ch = pixel(16r + py, 16c + px, ch). One wave per
+// token; lane l writes elements [12 l, 12 l + 12): py = l / 4, px = 4 (l % 4) + [0, 4).
+__global__ __launch_bounds__(256) void k_patchify(const uint8_t *__restrict__ pixels,
+                                                  const MediaItem *__restrict__ items, const int *__restrict__ cu,
+                                                  const int2 *__restrict__ tiles, uint16_t *__restrict__ patches,
+                                                  int16_t *__restrict__ pos, int axes) {
+    const int2 tile = tiles[blockIdx.x];
+    const MediaItem it = items[tile.x];
+    const int start = cu[tile.x], end = min(tile.y + kTileTokens, cu[tile.x + 1]);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int per_frame = it.grid_h * it.grid_w;
+    const size_t frame_bytes = (size_t)per_frame * 256 * 3;
+    for (int t = tile.y + wave; t < end; t += 4) {
+        const int local = t - start;
+        const int f = local / per_frame, rem = local % per_frame;
+        const int r = rem / it.grid_w, c = rem % it.grid_w;
+        const int py = lane >> 2, px = (lane & 3) * 4;
+        const uint8_t *p = pixels + it.pixel_offset + (size_t)f * frame_bytes +
+                           ((size_t)(16 * r + py) * it.width + 16 * c + px) * 3;
+        uint32_t w[6];
+        // bf16 of a byte value is exact; two per word
+#pragma unroll
+        for (int i = 0; i < 6; ++i) {
+            const float a = (float)p[2 * i], b = (float)p[2 * i + 1];
+            w[i] = pack2(a, b);
+        }
+        uint16_t *out = patches + (size_t)t * 768 + lane * 12;
+        *(u32x2 *)(out + 0) = u32x2{w[0], w[1]};
+        *(u32x2 *)(out + 4) = u32x2{w[2], w[3]};
+        *(u32x2 *)(out + 8) = u32x2{w[4], w[5]};
+        if (lane == 0) {
+            const int p0 = axes == 3 ? f : r, p1 = axes == 3 ? r : c, p2 = axes == 3 ? c : 0;
+            *(u32x2 *)(pos + (size_t)t * 4) =
+                u32x2{(uint32_t)(p0 & 0xffff) | ((uint32_t)(p1 & 0xffff) << 16), (uint32_t)(p2 & 0xffff)};
+        }
+    }
+}
+
+hipError_t launch_patchify(const uint8_t *pixels, const MediaItem *items, const int *cu, const int2 *tiles,
+                           int ntiles, uint16_t *patches, int16_t *pos, int axes, hipStream_t stream) {
+    if (ntiles == 0) return hipSuccess;
+    k_patchify<<<ntiles, 256, 0, stream>>>(pixels, items, cu, tiles, patches, pos, axes);
+    return hipGetLastError();
+}
+
+// =========================================================== GEMM
+//
+// C^T tile = W_tile (A operand: rows are output features) x X_tile^T (B
+// operand: columns are tokens). Workgroup: BM tokens x BN features, 4 waves in
+// 2 x 2, each wave (BM/2) x (BN/2) as (BN/64) x (BM/64) MFMA tiles of 32 x 32.
+// K advances in steps of 64 through LDS (one buffer; the next step's global
+// loads are in flight in registers while the current step computes). LDS rows
+// are 128 bytes; 16-byte chunk c of row r is stored at chunk c ^ (r & 7), so the
+// 8 lanes of one ds_read_b128 phase (8 consecutive rows, same chunk) hit 8
+// distinct bank groups.
+
+template <int BM, int BN, int EPI>
+__global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
+    constexpr int BK = 64;
+    constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 32, TN = WN / 32;
+    constexpr int WCH = BN * 8 / 256, XCH = BM * 8 / 256;
+    __shared__ __attribute__((aligned(16))) u32x4 smem[(BM + BN) * 8];
+    u32x4 *sW = smem, *sX = smem + BN * 8;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int NT = a.N / BN;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int mt = logical / NT, nt = logical % NT;
+    const int m0 = mt * BM, n0 = nt * BN;
+    const int K = a.K;
+
+    u32x4 rw[WCH], rx[XCH];
+    auto gload = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < WCH; ++i) {
+            const int idx = tid + 256 * i, row = idx >> 3, ch = idx & 7;
+            rw[i] = *(const u32x4 *)(a.w + (size_t)(n0 + row) * K + k0 + ch * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) {
+            const int idx = tid + 256 * i, row = idx >> 3, ch = idx & 7;
+            rx[i] = *(const u32x4 *)(a.x + (size_t)(m0 + row) * K + k0 + ch * 8);
+        }
+    };
+    auto sstore = [&]() {
+#pragma unroll
+        for (int i = 0; i < WCH; ++i) {
+            const int idx = tid + 256 * i, row = idx >> 3, ch = idx & 7;
+            sW[row * 8 + (ch ^ (row & 7))] = rw[i];
+        }
+#pragma unroll
+        for (int i = 0; i < XCH; ++i) {
+            const int idx = tid + 256 * i, row = idx >> 3, ch = idx & 7;
+            sX[row * 8 + (ch ^ (row & 7))] = rx[i];
+        }
+    };
+
+    f32x16 acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
+
+    gload(0);
+    for (int k0 = 0; k0 < K; k0 += BK) {
+        sstore();
+        __syncthreads();
+        if (k0 + BK < K) gload(k0 + BK);
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int ch = ks * 2 + hh;
+            bf16x8 af[TN], bfr[TM];
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                const int row = wn * WN + tn * 32 + l32;
+                af[tn] = __builtin_bit_cast(bf16x8, sW[row * 8 + (ch ^ (row & 7))]);
+            }
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                const int row = wm * WM + tm * 32 + l32;
+                bfr[tm] = __builtin_bit_cast(bf16x8, sX[row * 8 + (ch ^ (row & 7))]);
+            }
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+                    acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tn], bfr[tm], acc[tn][tm], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    // ---------------------------------------------------------- epilogues
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+        const int m = m0 + wm * WM + tm * 32 + l32;
+        if (m >= a.M) continue;
+        if constexpr (EPI == kEpiSwiglu) {
+#pragma unroll
+            for (int p = 0; p < TN / 2; ++p) {
+                const int col0 = (n0 + wn * WN) / 2 + p * 32;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const float g = acc[2 * p][tm][i * 4 + j], u = acc[2 * p + 1][tm][i * 4 + j];
+                        o[j] = g / (1.0f + __expf(-g)) * u;
+                    }
+                    const int col = col0 + i * 8 + hh * 4;
+                    *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + col) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+                }
+            }
+        } else {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                const int nbase = n0 + wn * WN + tn * 32;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int n = nbase + i * 8 + hh * 4;
+                    float o[4] = {acc[tn][tm][i * 4 + 0], acc[tn][tm][i * 4 + 1], acc[tn][tm][i * 4 + 2],
+                                  acc[tn][tm][i * 4 + 3]};
+                    if constexpr (EPI == kEpiStore) {
+                        *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+                    } else if constexpr (EPI == kEpiResid) {
+                        f32x4 *px = (f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n);
+                        f32x4 xv = *px;
+                        *px = f32x4{xv.x + o[0], xv.y + o[1], xv.z + o[2], xv.w + o[3]};
+                    } else if constexpr (EPI == kEpiPatch) {
+                        *(f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n) =
+                            f32x4{o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale};
+                    } else if constexpr (EPI == kEpiQkv) {
+                        if (nbase < 2 * a.D) {
+                            // rotary: pairs (e, e+1) and (e+2, e+3), e = n % 64 even
+                            const u32x2 pw = *(const u32x2 *)(a.pos + (size_t)m * 4);
+                            const int p0 = (int)(int16_t)(pw.x & 0xffff), p1 = (int)(int16_t)(pw.x >> 16),
+                                      p2 = (int)(int16_t)(pw.y & 0xffff);
+#pragma unroll
+                            for (int q = 0; q < 2; ++q) {
+                                const int pair = ((n & 63) >> 1) + q;
+                                const int pv = pair < a.sec0 ? p0 : (pair < a.sec0 + a.sec1 ? p1 : p2);
+                                const float2 cs = a.rope[pv * 32 + pair];
+                                const float x0 = o[2 * q], x1 = o[2 * q + 1];
+                                o[2 * q] = x0 * cs.x - x1 * cs.y;
+                                o[2 * q + 1] = x0 * cs.y + x1 * cs.x;
+                            }
+                            *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n) =
+                                u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+                        } else {
+                            const int e = n - 2 * a.D;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j)
+                                a.vt[(size_t)(e + j) * a.ld_vt + m] = (uint16_t)f32_to_bf16(o[j]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int BM, int BN>
+static hipError_t gemm_dispatch(int epi, const GemmArgs &a, hipStream_t stream) {
+    const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN);
+    switch (epi) {
+        case kEpiStore: k_gemm<BM, BN, kEpiStore><<<tiles, 256, 0, stream>>>(a); break;
+        case kEpiQkv: k_gemm<BM, BN, kEpiQkv><<<tiles, 256, 0, stream>>>(a); break;
+        case kEpiResid: k_gemm<BM, BN, kEpiResid><<<tiles, 256, 0, stream>>>(a); break;
+        case kEpiSwiglu: k_gemm<BM, BN, kEpiSwiglu><<<tiles, 256, 0, stream>>>(a); break;
+        case kEpiPatch: k_gemm<BM, BN, kEpiPatch><<<tiles, 256, 0, stream>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_gemm(int epi, const GemmArgs &a, hipStream_t stream) {
+    if (a.M == 0) return hipSuccess;
+    if (a.N % 128 != 0 || a.K % 64 != 0) return hipErrorInvalidValue;
+    return gemm_dispatch<256, 128>(epi, a, stream);
+}
+
+// =========================================================== attention
+//
+// Bidirectional attention inside each item (varlen, tiles from the tape's
+// prefix sums). Workgroup = (query tile of 128 tokens of one item, head); wave
+// w owns queries q0 + 32w + [0, 32). Per key tile of 64:
+//   S^T (keys x queries) = K Q^T   -- lane keeps one query, 32 of its scores
+//   online softmax in fp32 (exp2 of pre-scaled logits; one cross-half exchange)
+//   O^T (d x queries) += V^T P^T   -- P^T taken straight from the S^T registers:
+//     for PV step s, slot k of half h <-> key 32(s/2) + 8 i + 4h + (k % 4) with
+//     i = 2(s % 2) + k / 4, the same assignment on the V^T operand.
+// V arrives feature-major (vt [D x ldvt]) so V^T rows are key-contiguous.
+
+__global__ __launch_bounds__(256) void k_attention(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                   int ldqk, const uint16_t *__restrict__ vt, int ldvt,
+                                                   uint16_t *__restrict__ o, int ldo, const int *__restrict__ cu,
+                                                   const int2 *__restrict__ tiles, int ntiles) {
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int head = logical / ntiles, ti = logical % ntiles;
+    const int2 tile = tiles[ti];
+    const int k0 = cu[tile.x], k1 = cu[tile.x + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l32 = lane & 31, hh = lane >> 5;
+
+    __shared__ __attribute__((aligned(16))) u32x4 sK[64 * 8];
+    __shared__ __attribute__((aligned(16))) u32x2 sV[64 * 16];
+
+    const int qrow = tile.y + wave * 32 + l32;
+    bf16x8 qf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(q + (size_t)qrow * ldqk + head * 64 + ks * 16 + hh * 8));
+
+    f32x16 O[2] = {f32x16{}, f32x16{}};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float c = 0.18033688011112042f;  // log2(e) / sqrt(64)
+
+    for (int kt = k0; kt < k1; kt += 64) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + 256 * i, key = idx >> 3, ch = idx & 7;
+            sK[key * 8 + (ch ^ (key & 7))] = *(const u32x4 *)(k + (size_t)(kt + key) * ldqk + head * 64 + ch * 8);
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int idx = tid + 256 * i, dd = idx >> 3, ch = idx & 7;
+            const u32x4 v = *(const u32x4 *)(vt + (size_t)(head * 64 + dd) * ldvt + kt + ch * 8);
+            const int sw = dd & 15;
+            sV[dd * 16 + ((2 * ch) ^ sw)] = u32x2{v.x, v.y};
+            sV[dd * 16 + ((2 * ch + 1) ^ sw)] = u32x2{v.z, v.w};
+        }
+        __syncthreads();
+
+        f32x16 S[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            S[kk] = f32x16{};
+            const int key = kk * 32 + l32;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int ch = ks * 2 + hh;
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, sK[key * 8 + (ch ^ (key & 7))]);
+                S[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[kk], 0, 0, 0);
+            }
+        }
+        if (kt + 64 > k1) {
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kt + kk * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+                    if (key >= k1) S[kk][r] = -INFINITY;
+                }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kk][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = exp2f((m_run - m_new) * c);
+        const float mc = m_new * c;
+        float rs = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = exp2f(fmaf(S[kk][r], c, -mc));
+                S[kk][r] = p;
+                rs += p;
+            }
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) O[dt] *= alpha;
+
+        bf16x8 pf[4];
+#pragma unroll
+        for (int s2 = 0; s2 < 4; ++s2) {
+            const int kk = s2 >> 1, i0 = (s2 & 1) * 2, i1 = i0 + 1;
+            const u32x4 w = u32x4{pack2(S[kk][i0 * 4 + 0], S[kk][i0 * 4 + 1]), pack2(S[kk][i0 * 4 + 2], S[kk][i0 * 4 + 3]),
+                                  pack2(S[kk][i1 * 4 + 0], S[kk][i1 * 4 + 1]), pack2(S[kk][i1 * 4 + 2], S[kk][i1 * 4 + 3])};
+            pf[s2] = __builtin_bit_cast(bf16x8, w);
+        }
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt) {
+            const int dd = dt * 32 + l32, sw = dd & 15;
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+                const int kk = s2 >> 1, i0 = (s2 & 1) * 2, i1 = i0 + 1;
+                const u32x2 va = sV[dd * 16 + ((kk * 8 + i0 * 2 + hh) ^ sw)];
+                const u32x2 vb = sV[dd * 16 + ((kk * 8 + i1 * 2 + hh) ^ sw)];
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{va.x, va.y, vb.x, vb.y});
+                O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s2], O[dt], 0, 0, 0);
+            }
+        }
+        __syncthreads();
+    }
+
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    if (qrow < k1) {
+        const float inv = 1.0f / l_tot;
+#pragma unroll
+        for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int d = dt * 32 + i * 8 + hh * 4;
+                *(u32x2 *)(o + (size_t)qrow * ldo + head * 64 + d) =
+                    u32x2{pack2(O[dt][i * 4 + 0] * inv, O[dt][i * 4 + 1] * inv),
+                          pack2(O[dt][i * 4 + 2] * inv, O[dt][i * 4 + 3] * inv)};
+            }
+    }
+}
+
+hipError_t launch_attention(const uint16_t *q, const uint16_t *k, int ldqk, const uint16_t *vt, int ldvt,
+                            uint16_t *o, int ldo, const int *cu, const int2 *tiles, int ntiles, int heads,
+                            hipStream_t stream) {
+    if (ntiles == 0) return hipSuccess;
+    k_attention<<<ntiles * heads, 256, 0, stream>>>(q, k, ldqk, vt, ldvt, o, ldo, cu, tiles, ntiles);
+    return hipGetLastError();
+}
+
+// =========================================================== pool
+//
+// One workgroup per item. Scores s[t][h] = xf_t . u_h with u_h = W_k,h q_h / 8
+// (the reassociated form of q_h . (xf_t W_k)_h / sqrt(64)) come from the final
+// norm kernel. Here: per head softmax over the item's tokens (written back as
+// probabilities), z_h = sum_t p_t,h xf_t, then pooled_h = z_h W_v[:, h].
+
+__device__ float block_reduce(float v, float *scratch, bool is_max) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    v = is_max ? wave_max(v) : wave_sum(v);
+    __syncthreads();
+    if (lane == 0) scratch[wave] = v;
+    __syncthreads();
+    float r = scratch[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w) r = is_max ? fmaxf(r, scratch[w]) : r + scratch[w];
+    return r;
+}
+
+template <int HMAX, int CMAX>
+__global__ __launch_bounds__(256) void k_pool(const uint16_t *__restrict__ xf, const float *__restrict__ s,
+                                              const int *__restrict__ cu, const uint16_t *__restrict__ wv,
+                                              void *__restrict__ out, int out_bf16, size_t out_stride, int D, int H) {
+    // LDS: z [H x D] | p chunk [256 x H] | per-head max and 1/sum [2 x H] | 4 floats of reduction scratch
+    extern __shared__ float smem[];
+    float *z = smem, *pc = z + H * D, *mh = pc + 256 * H, *ih = mh + H, *scratch = ih + H;
+    const int item = blockIdx.x, t0 = cu[item], t1 = cu[item + 1];
+    const int tid = threadIdx.x;
+    char *orow = (char *)out + (size_t)item * out_stride;
+    if (t1 == t0) {
+        for (int col = tid; col < D; col += 256) {
+            if (out_bf16) ((uint16_t *)orow)[col] = 0;
+            else ((float *)orow)[col] = 0.f;
+        }
+        return;
+    }
+    for (int hd = 0; hd < H; ++hd) {
+        float m = -INFINITY;
+        for (int t = t0 + tid; t < t1; t += 256) m = fmaxf(m, s[(size_t)t * H + hd]);
+        m = block_reduce(m, scratch, true);
+        float sum = 0.f;
+        for (int t = t0 + tid; t < t1; t += 256) sum += __expf(s[(size_t)t * H + hd] - m);
+        sum = block_reduce(sum, scratch, false);
+        if (tid == 0) mh[hd] = m, ih[hd] = 1.0f / sum;
+    }
+    float zacc[CMAX][HMAX];
+#pragma unroll
+    for (int c = 0; c < CMAX; ++c)
+#pragma unroll
+        for (int hd = 0; hd < HMAX; ++hd) zacc[c][hd] = 0.f;
+    for (int cs = t0; cs < t1; cs += 256) {
+        __syncthreads();
+        if (cs + tid < t1)
+            for (int hd = 0; hd < H; ++hd)
+                pc[tid * H + hd] = __expf(s[(size_t)(cs + tid) * H + hd] - mh[hd]) * ih[hd];
+        __syncthreads();
+        const int n = min(256, t1 - cs);
+        for (int tt = 0; tt < n; ++tt) {
+            float p[HMAX];
+#pragma unroll
+            for (int hd = 0; hd < HMAX; ++hd) p[hd] = hd < H ? pc[tt * H + hd] : 0.f;
+#pragma unroll
+            for (int c = 0; c < CMAX; ++c) {
+                const int f = tid + 256 * c;
+                if (f < D) {
+                    const float xv = bf16_to_f32(xf[(size_t)(cs + tt) * D + f]);
+#pragma unroll
+                    for (int hd = 0; hd < HMAX; ++hd) zacc[c][hd] += p[hd] * xv;
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < CMAX; ++c) {
+        const int f = tid + 256 * c;
+        if (f < D)
+#pragma unroll
+            for (int hd = 0; hd < HMAX; ++hd)
+                if (hd < H) z[hd * D + f] = zacc[c][hd];
+    }
+    __syncthreads();
+    for (int col = tid; col < D; col += 256) {
+        const float *zh = z + (col >> 6) * D;
+        float accv = 0.f;
+        for (int f = 0; f < D; ++f) accv += zh[f] * bf16_to_f32(wv[(size_t)f * D + col]);
+        if (out_bf16) ((uint16_t *)orow)[col] = (uint16_t)f32_to_bf16(accv);
+        else ((float *)orow)[col] = accv;
+    }
+}
+
+hipError_t launch_pool(const uint16_t *xf, const float *s, const int *cu, int count, const uint16_t *wv, void *out,
+                       int out_bf16, size_t out_stride, int D, int H, hipStream_t stream) {
+    if (count == 0) return hipSuccess;
+    const size_t lds = ((size_t)H * D + 256 * (size_t)H + 2 * (size_t)H + 4) * sizeof(float);
+    const int C = (D + 255) / 256;
+    auto go = [&](auto kernel) -> hipError_t {
+        if (lds > 65536) {
+            hipError_t e = hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            if (e != hipSuccess) return e;
+        }
+        kernel<<<count, 256, lds, stream>>>(xf, s, cu, wv, out, out_bf16, out_stride, D, H);
+        return hipGetLastError();
+    };
+    if (H <= 2 && C <= 1) return go(k_pool<2, 1>);
+    if (H <= 8 && C <= 2) return go(k_pool<8, 2>);
+    if (H <= 16 && C <= 4) return go(k_pool<16, 4>);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ube

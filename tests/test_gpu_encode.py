@@ -1,0 +1,205 @@
+"""Whole-encoder parity of the HIP path against the CPU oracle, through the C ABI.
+
+Bar (per pooled row): cosine >= 0.999 and max |difference| <= 2e-2 against the
+float64 oracle; bookkeeping (stats, rows-view metadata) and batch invariance /
+run-to-run determinism are bit-exact.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from multimodal_embeddings_amd import configs, synth
+from tests.gpu_util import check_pooled, device_bytes, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ube():
+    import multimodal_embeddings_amd as m
+    return m
+
+
+_MODELS = {}
+
+
+def _model(ube, name, **kw):
+    key = (name, tuple(sorted(kw.items())))
+    if key not in _MODELS:
+        w = synth.make_weights(configs.geometry(name), **kw)
+        _MODELS[key] = (w, ube.Model(w, 0), ube.Arena(0))
+    return _MODELS[key]
+
+
+def _pooled(rows):
+    return rows.tensor().double().cpu().numpy()
+
+
+# ------------------------------------------------------------------ tiny
+
+
+def test_tiny_matches_oracle_all_rows(ube):
+    import torch
+    w, model, arena = _model(ube, "tiny", gain_jitter=0.2)
+    batch = synth.workload_inputs("tiny")
+    g = w.geometry
+    T = int(batch.offsets[-1])
+    trace = torch.zeros(((g["depth"] + 1) * T * g["hidden"],), dtype=torch.float32, device="cuda:0")
+    rows, stats = ube.text_encode(model, arena, device_bytes(batch.data), batch.offsets, trace=trace)
+    want, ostats = oracle.encode_text(w, batch.data, batch.offsets)
+    assert stats == ostats
+    assert (rows.count, rows.columns, rows.stride, rows.scalar) == (8, 128, 512, "f32")
+    check_pooled(_pooled(rows), want, "tiny")
+    # frontend rows are the embedding rows, exactly
+    tr = trace.cpu().numpy().reshape(g["depth"] + 1, T, g["hidden"])
+    x0 = w.f32["embed"][batch.data.astype(np.int64)]
+    np.testing.assert_array_equal(tr[0], x0)
+    # residual stream after every block against the oracle run to that depth
+    lengths, cu, _ = oracle.tape_plan(batch.offsets, g["context"])
+    x0o, pos = oracle.embed_text(batch.data, batch.offsets, lengths, cu, w.f32["embed"])
+    for depth in range(1, g["depth"] + 1):
+        wd = synth.Weights(dict(g, depth=depth))
+        wd.f32 = {k: (v[:depth] if isinstance(v, list) else v) for k, v in w.f32.items()}
+        x_ref, _ = oracle.forward_states(wd, x0o, pos, cu)
+        rel = np.linalg.norm(tr[depth] - x_ref) / np.linalg.norm(x_ref)
+        say(f"  residual after block {depth}: relative error {rel:.2e}")
+        assert rel < 1e-2
+
+
+def test_tiny_bf16_outputs_and_host_tape(ube):
+    w, model, arena = _model(ube, "tiny", gain_jitter=0.2)
+    batch = synth.workload_inputs("tiny")
+    rows32, _ = ube.text_encode(model, arena, device_bytes(batch.data), batch.offsets)
+    f32 = _pooled(rows32)
+    rows16, _ = ube.text_encode(model, arena, device_bytes(batch.data), batch.offsets, outputs_scalar="bf16")
+    assert rows16.scalar == "bf16" and rows16.stride == 256
+    b16 = _pooled(rows16)
+    import torch
+    np.testing.assert_array_equal(b16, torch.from_numpy(f32).float().to(torch.bfloat16).double().numpy())
+    # a host-resident tape is copied in and gives the same rows
+    rows_h, _ = ube.text_encode(model, arena, batch.data, batch.offsets)
+    np.testing.assert_array_equal(_pooled(rows_h), f32)
+
+
+def test_tiny_empty_items_and_empty_batch(ube):
+    w, model, arena = _model(ube, "tiny", gain_jitter=0.2)
+    data = np.arange(40, dtype=np.uint8)
+    offsets = np.array([0, 10, 10, 40, 40], np.uint64)
+    rows, stats = ube.text_encode(model, arena, device_bytes(data), offsets)
+    got = _pooled(rows)
+    want, ostats = oracle.encode_text(w, data, offsets)
+    assert stats == ostats == (0, 40)
+    assert not got[1].any() and not got[3].any()
+    check_pooled(got, want, "tiny-empty-items")
+    rows, stats = ube.text_encode(model, arena, device_bytes(np.zeros(1, np.uint8)), np.array([0], np.uint64))
+    assert rows.count == 0 and stats == (0, 0)
+
+
+def test_inputs_inside_the_arena_are_refused(ube):
+    w, model, arena = _model(ube, "tiny", gain_jitter=0.2)
+    batch = synth.workload_inputs("tiny")
+    rows, _ = ube.text_encode(model, arena, device_bytes(batch.data), batch.offsets)
+
+    class Inside:
+        def data_ptr(self):
+            return rows.data
+
+    with pytest.raises(ube.UbeError) as e:
+        ube.text_encode(model, arena, Inside(), np.array([0, 16], np.uint64))
+    assert e.value.status == "invalid_argument"
+    with pytest.raises(ube.UbeError) as e:
+        ube.text_encode(model, arena, device_bytes(batch.data), np.array([0, 9, 4], np.uint64))
+    assert e.value.status == "invalid_argument"
+
+
+# ------------------------------------------------------------------ text, depth 12 / hidden 512
+
+
+def test_ragged_rows_match_oracle(ube):
+    w, model, arena = _model(ube, "text512")
+    batch = synth.workload_inputs("ragged")
+    rows, stats = ube.text_encode(model, arena, device_bytes(batch.data), batch.offsets)
+    got = _pooled(rows)
+    assert stats == oracle.tape_plan(batch.offsets, 1024)[2]
+    pick = [0, 5, 17, 33, 63]
+    sub = synth.subset(batch, pick)
+    want, _ = oracle.encode_text(w, sub.data, sub.offsets)
+    say(f"  sampled lengths {np.diff(sub.offsets.astype(np.int64)).tolist()}")
+    check_pooled(got[pick], want, "ragged")
+
+
+def test_ragged_truncation_bookkeeping_and_prefix(ube):
+    w, model, arena = _model(ube, "text512")
+    batch = synth.workload_inputs("ragged_trunc")
+    rows, stats = ube.text_encode(model, arena, device_bytes(batch.data), batch.offsets)
+    assert stats == oracle.tape_plan(batch.offsets, 1024)[2]
+    assert stats[0] > 0
+    got = _pooled(rows)
+    lens = np.diff(batch.offsets.astype(np.int64))
+    i = int(np.argmax(lens))
+    # an item past the context pools exactly like its first 1024 bytes
+    prefix = batch.data[int(batch.offsets[i]):int(batch.offsets[i]) + 1024]
+    rows_p, st = ube.text_encode(model, arena, device_bytes(prefix), np.array([0, 1024], np.uint64))
+    assert st == (0, 1024)
+    np.testing.assert_array_equal(_pooled(rows_p)[0], got[i])
+
+
+def test_throughput_batch_sampled_parity_invariance_determinism(ube):
+    w, model, arena = _model(ube, "text512")
+    batch = synth.workload_inputs("throughput")
+    data = device_bytes(batch.data)
+    rows, stats = ube.text_encode(model, arena, data, batch.offsets)
+    assert stats == (0, 1024 * 1024)
+    full = _pooled(rows)
+    rows2, _ = ube.text_encode(model, arena, data, batch.offsets)
+    np.testing.assert_array_equal(_pooled(rows2), full)  # run to run
+    pick = [517, 3, 900]
+    sub = synth.subset(batch, pick)
+    rows_s, _ = ube.text_encode(model, arena, device_bytes(sub.data), sub.offsets)
+    np.testing.assert_array_equal(_pooled(rows_s), full[pick])  # batch invariance
+    sample = synth.subset(batch, [0, 517])
+    want, _ = oracle.encode_text(w, sample.data, sample.offsets)
+    check_pooled(full[[0, 517]], want, "throughput")
+
+
+# ------------------------------------------------------------------ media
+
+
+def test_image_batch_sampled_parity(ube):
+    w, model, arena = _model(ube, "image768")
+    batch = synth.workload_inputs("image")
+    rows, stats = ube.encode(model, arena, _dev(batch))
+    assert stats == (0, 128 * 256) and rows.count == 128
+    full = _pooled(rows)
+    pick = [0, 77]
+    sub = synth.subset(batch, pick)
+    want, _ = oracle.encode_media(w, sub)
+    check_pooled(full[pick], want, "image")
+    rows_s, _ = ube.encode(model, arena, _dev(sub))
+    np.testing.assert_array_equal(_pooled(rows_s), full[pick])
+
+
+def test_image_shape_refusals(ube):
+    w, model, arena = _model(ube, "image768")
+    px = np.zeros(40 * 48 * 3, np.uint8)
+    with pytest.raises(ube.UbeError) as e:
+        ube.image_encode_pixels(model, arena, device_bytes(px), [0, px.size], [40], [48])
+    assert e.value.status == "shape_mismatch"
+    big = np.zeros(528 * 528 * 3, np.uint8)  # 33 x 33 = 1089 patches > 1024
+    with pytest.raises(ube.UbeError) as e:
+        ube.image_encode_pixels(model, arena, device_bytes(big), [0, big.size], [528], [528])
+    assert e.value.status == "shape_mismatch"
+
+
+def test_video_small_clips_match_oracle(ube):
+    w, model, arena = _model(ube, "video1024")
+    batch = synth.media_batch(3, 2, 64, 48, seed=4)  # 2 x 4 x 3 = 24 tokens per clip
+    rows, stats = ube.encode(model, arena, _dev(batch))
+    assert stats == (0, 72)
+    want, _ = oracle.encode_media(w, batch)
+    check_pooled(_pooled(rows), want, "video-small")
+
+
+def _dev(batch):
+    batch.data_device = device_bytes(batch.data)
+    return batch
