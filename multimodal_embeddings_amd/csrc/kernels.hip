@@ -353,6 +353,10 @@ hipError_t launch_patchify(const uint8_t *pixels, const MediaItem *items, const 
 // 8 lanes of one ds_read_b128 phase (8 consecutive rows, same chunk) hit 8
 // distinct bank groups.
 
+template <int EPI, int TM, int TN>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x16 (&acc)[TN][TM], int mw, int nw, int l32,
+                                              int hh);
+
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     constexpr int BK = 64;
@@ -430,15 +434,23 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
         __syncthreads();
     }
 
-    // ---------------------------------------------------------- epilogues
+    gemm_epilogue<EPI, TM, TN>(a, acc, m0 + wm * WM, n0 + wn * WN, l32, hh);
+}
+
+// Epilogue of one wave's (TN x TM) grid of 32 x 32 accumulator tiles. The wave's
+// features start at nw, its tokens at mw; accumulator register 4i + j of tile
+// (tn, tm) is feature nw + 32 tn + 8 i + 4 (lane / 32) + j, token mw + 32 tm + lane % 32.
+template <int EPI, int TM, int TN>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x16 (&acc)[TN][TM], int mw, int nw, int l32,
+                                              int hh) {
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
-        const int m = m0 + wm * WM + tm * 32 + l32;
+        const int m = mw + tm * 32 + l32;
         if (m >= a.M) continue;
         if constexpr (EPI == kEpiSwiglu) {
 #pragma unroll
             for (int p = 0; p < TN / 2; ++p) {
-                const int col0 = (n0 + wn * WN) / 2 + p * 32;
+                const int col0 = nw / 2 + p * 32;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     float o[4];
@@ -454,7 +466,7 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
         } else {
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
-                const int nbase = n0 + wn * WN + tn * 32;
+                const int nbase = nw + tn * 32;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int n = nbase + i * 8 + hh * 4;
@@ -499,6 +511,113 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
     }
 }
 
+// 256 x 256 tiles for N % 256 == 0: 8 waves (2 token rows x 4 feature columns
+// of 128 x 64), two LDS stages of 64 KB filled by global_load_lds_dwordx4
+// (16 bytes per lane straight into LDS, no register staging). Lane i of a load
+// instruction lands at LDS chunk (base + i); the global chunk it fetches is the
+// logical chunk that the XOR swizzle assigns to that LDS slot.
+__device__ __forceinline__ void lds_dma16(const void *gptr, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+template <int EPI>
+__global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
+    constexpr int BM = 256, BN = 256, BK = 64;
+    constexpr int WM = 128, WN = 64, TM = WM / 32, TN = WN / 32;
+    constexpr int STAGE = (BM + BN) * 8;  // 16-byte chunks per stage
+    __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int NT = a.N / BN;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int mt = logical / NT, nt = logical % NT;
+    const int m0 = mt * BM, n0 = nt * BN;
+    const int K = a.K;
+
+    // global source of this lane for load round r (0..3 weights, 4..7 activations)
+    // chunk slot p = 512 r' + 64 wave + lane within the operand tile: row p / 8, LDS chunk p % 8
+    const int prow = (wave * 64 + lane) >> 3;           // + 64 r'
+    const int pch = lane & 7;
+    auto issue = [&](int k0, int buf) {
+        u32x4 *dst = smem + buf * STAGE;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = r * 64 + prow;
+            const int ch = pch ^ (row & 7);
+            lds_dma16(a.w + (size_t)(n0 + row) * K + k0 + ch * 8, dst + r * 512 + wave * 64);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = r * 64 + prow;
+            const int ch = pch ^ (row & 7);
+            lds_dma16(a.x + (size_t)(m0 + row) * K + k0 + ch * 8, dst + BN * 8 + r * 512 + wave * 64);
+        }
+    };
+
+    f32x16 acc[TN][TM];
+#pragma unroll
+    for (int i = 0; i < TN; ++i)
+#pragma unroll
+        for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
+
+    // One stage: wait for this wave's DMA of the stage (the next stage's 8 loads
+    // may stay in flight), barrier so every wave's DMA is visible, compute, then
+    // drain LDS reads and barrier again before the buffer is refilled. Plain
+    // s_barrier: a __syncthreads() fence would also wait for the next stage.
+    auto compute = [&](const u32x4 *sW) {
+        const u32x4 *sX = sW + BN * 8;
+#pragma unroll
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int ch = ks * 2 + hh;
+            bf16x8 af[TN], bfr[TM];
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                const int row = wn * WN + tn * 32 + l32;
+                af[tn] = __builtin_bit_cast(bf16x8, sW[row * 8 + (ch ^ (row & 7))]);
+            }
+#pragma unroll
+            for (int tm = 0; tm < TM; ++tm) {
+                const int row = wm * WM + tm * 32 + l32;
+                bfr[tm] = __builtin_bit_cast(bf16x8, sX[row * 8 + (ch ^ (row & 7))]);
+            }
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm)
+                    acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tn], bfr[tm], acc[tn][tm], 0, 0, 0);
+        }
+    };
+    const int nk = K / BK;
+    issue(0, 0);
+    for (int kt = 0; kt < nk; kt += 2) {
+        if (kt + 1 < nk) {
+            issue((kt + 1) * BK, 1);
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        __builtin_amdgcn_s_barrier();
+        compute(smem);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        __builtin_amdgcn_s_barrier();
+        if (kt + 1 < nk) {
+            if (kt + 2 < nk) {
+                issue((kt + 2) * BK, 0);
+                asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            __builtin_amdgcn_s_barrier();
+            compute(smem + STAGE);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            __builtin_amdgcn_s_barrier();
+        }
+    }
+    gemm_epilogue<EPI, TM, TN>(a, acc, m0 + wm * WM, n0 + wn * WN, l32, hh);
+}
+
 template <int BM, int BN>
 static hipError_t gemm_dispatch(int epi, const GemmArgs &a, hipStream_t stream) {
     const int tiles = ((a.M + BM - 1) / BM) * (a.N / BN);
@@ -513,9 +632,23 @@ static hipError_t gemm_dispatch(int epi, const GemmArgs &a, hipStream_t stream) 
     return hipGetLastError();
 }
 
+static hipError_t gemm256_dispatch(int epi, const GemmArgs &a, hipStream_t stream) {
+    const int tiles = ((a.M + 255) / 256) * (a.N / 256);
+    switch (epi) {
+        case kEpiStore: k_gemm256<kEpiStore><<<tiles, 512, 0, stream>>>(a); break;
+        case kEpiQkv: k_gemm256<kEpiQkv><<<tiles, 512, 0, stream>>>(a); break;
+        case kEpiResid: k_gemm256<kEpiResid><<<tiles, 512, 0, stream>>>(a); break;
+        case kEpiSwiglu: k_gemm256<kEpiSwiglu><<<tiles, 512, 0, stream>>>(a); break;
+        case kEpiPatch: k_gemm256<kEpiPatch><<<tiles, 512, 0, stream>>>(a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_gemm(int epi, const GemmArgs &a, hipStream_t stream) {
     if (a.M == 0) return hipSuccess;
     if (a.N % 128 != 0 || a.K % 64 != 0) return hipErrorInvalidValue;
+    if (a.N % 256 == 0) return gemm256_dispatch(epi, a, stream);
     return gemm_dispatch<256, 128>(epi, a, stream);
 }
 
