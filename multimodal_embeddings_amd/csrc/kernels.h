@@ -11,7 +11,7 @@ namespace ube {
 // tile stay inside the allocation and see finite values.
 constexpr int kRowPad = 256;
 // Tokens per work tile of the gather, patchify and attention kernels.
-constexpr int kTileTokens = 128;
+constexpr int kTileTokens = 256;
 
 enum Epilogue : int {
     kEpiStore = 0,   // C = bf16(acc)                                   [M x N], ld

@@ -34,7 +34,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float v) {
     return (uint32_t)__builtin_bit_cast(uint16_t, b);
 }
 
-__device__ __forceinline__ uint32_t pack2(float a, float b) { return f32_to_bf16(a) | (f32_to_bf16(b) << 16); }
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
@@ -520,6 +525,13 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, void *lds_base) {
     __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
+// Workgroup barrier without a memory fence (the DMA of the next stage stays in
+// flight); the empty asm keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
     constexpr int BM = 256, BN = 256, BK = 64;
@@ -598,10 +610,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
         } else {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
-        __builtin_amdgcn_s_barrier();
+        lds_barrier();
         compute(smem);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        __builtin_amdgcn_s_barrier();
+        lds_barrier();
         if (kt + 1 < nk) {
             if (kt + 2 < nk) {
                 issue((kt + 2) * BK, 0);
@@ -609,10 +621,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
             } else {
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
-            __builtin_amdgcn_s_barrier();
+            lds_barrier();
             compute(smem + STAGE);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            __builtin_amdgcn_s_barrier();
+            lds_barrier();
         }
     }
     gemm_epilogue<EPI, TM, TN>(a, acc, m0 + wm * WM, n0 + wn * WN, l32, hh);
@@ -655,65 +667,84 @@ hipError_t launch_gemm(int epi, const GemmArgs &a, hipStream_t stream) {
 // =========================================================== attention
 //
 // Bidirectional attention inside each item (varlen, tiles from the tape's
-// prefix sums). Workgroup = (query tile of 128 tokens of one item, head); wave
-// w owns queries q0 + 32w + [0, 32). Per key tile of 64:
-//   S^T (keys x queries) = K Q^T   -- lane keeps one query, 32 of its scores
-//   online softmax in fp32 (exp2 of pre-scaled logits; one cross-half exchange)
-//   O^T (d x queries) += V^T P^T   -- P^T taken straight from the S^T registers:
-//     for PV step s, slot k of half h <-> key 32(s/2) + 8 i + 4h + (k % 4) with
-//     i = 2(s % 2) + k / 4, the same assignment on the V^T operand.
-// V arrives feature-major (vt [D x ldvt]) so V^T rows are key-contiguous.
+// prefix sums). Workgroup = (query tile of 256 tokens of one item, head), 4
+// waves of 64 queries (two 32-query subtiles). Per key tile of 64 keys, staged
+// in LDS by DMA (two stages, the next tile in flight):
+//   S^T (keys x queries) = K Q^T   -- each lane keeps one query and 32 scores
+//                                      per subtile; the row max needs one
+//                                      exchange between the two lane halves
+//   online softmax in fp32 on exp2 of pre-scaled logits; the output is only
+//   rescaled when some query's running max grew
+//   O^T (d x queries) += V^T P^T   -- P^T comes straight from the S^T registers.
+// Within each 32-key subtile, LDS row r of K holds key perm32(r), chosen so that
+// the 8 scores a lane feeds to one PV step belong to 8 consecutive keys; V^T rows
+// (feature-major vt) are then read as one 16-byte chunk, like K. Both operands
+// use 16-byte chunks XOR-swizzled by (row & 7): conflict-free ds_read_b128.
 
-__global__ __launch_bounds__(256) void k_attention(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
-                                                   int ldqk, const uint16_t *__restrict__ vt, int ldvt,
-                                                   uint16_t *__restrict__ o, int ldo, const int *__restrict__ cu,
-                                                   const int2 *__restrict__ tiles, int ntiles) {
+__device__ __forceinline__ int perm32(int r) {  // r = 8 i + 4 h + j
+    const int i = r >> 3, h = (r >> 2) & 1, j = r & 3;
+    return (i >> 1) * 16 + h * 8 + (i & 1) * 4 + j;
+}
+
+__global__ __launch_bounds__(256, 2) void k_attention(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+                                                      int ldqk, const uint16_t *__restrict__ vt, int ldvt,
+                                                      uint16_t *__restrict__ o, int ldo, const int *__restrict__ cu,
+                                                      const int2 *__restrict__ tiles, int ntiles) {
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int head = logical / ntiles, ti = logical % ntiles;
     const int2 tile = tiles[ti];
     const int k0 = cu[tile.x], k1 = cu[tile.x + 1];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
+    constexpr int STAGE = 1024;  // 16-byte chunks: K tile 512 | V^T tile 512
+    __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * STAGE];
 
-    __shared__ __attribute__((aligned(16))) u32x4 sK[64 * 8];
-    __shared__ __attribute__((aligned(16))) u32x2 sV[64 * 16];
-
-    const int qrow = tile.y + wave * 32 + l32;
-    bf16x8 qf[4];
+    const int qbase = tile.y + wave * 64;
+    const bool active = qbase < k1;
+    bf16x8 qf[2][4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        qf[ks] = __builtin_bit_cast(bf16x8, *(const u32x4 *)(q + (size_t)qrow * ldqk + head * 64 + ks * 16 + hh * 8));
+    for (int qs = 0; qs < 2; ++qs)
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            qf[qs][ks] = __builtin_bit_cast(
+                bf16x8, *(const u32x4 *)(q + (size_t)(qbase + qs * 32 + l32) * ldqk + head * 64 + ks * 16 + hh * 8));
 
-    f32x16 O[2] = {f32x16{}, f32x16{}};
-    float m_run = -INFINITY, l_run = 0.f;
+    // DMA: chunk slot p = 256 rd + tid of each operand tile; row p / 8, stored chunk p % 8
+    auto issue = [&](int kt, u32x4 *dst) {
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+            const int p = rd * 256 + tid, row = p >> 3, c = (p & 7) ^ (row & 7);
+            const int key = kt + (row & 32) + perm32(row & 31);
+            lds_dma16(k + (size_t)key * ldqk + head * 64 + c * 8, dst + rd * 256 + wave * 64);
+        }
+#pragma unroll
+        for (int rd = 0; rd < 2; ++rd) {
+            const int p = rd * 256 + tid, row = p >> 3, c = (p & 7) ^ (row & 7);
+            lds_dma16(vt + (size_t)(head * 64 + row) * ldvt + kt + c * 8, dst + 512 + rd * 256 + wave * 64);
+        }
+    };
+
+    f32x16 O[2][2];
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) O[qs][0] = f32x16{}, O[qs][1] = f32x16{};
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
     const float c = 0.18033688011112042f;  // log2(e) / sqrt(64)
 
-    for (int kt = k0; kt < k1; kt += 64) {
+    auto compute = [&](const u32x4 *sK, int kt) {
+        const u32x4 *sV = sK + 512;
+        f32x16 S[2][2];
+        u32x4 P[2][2][2];  // bf16 pairs of p per query subtile, key subtile, PV step (one MFMA operand each)
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i, key = idx >> 3, ch = idx & 7;
-            sK[key * 8 + (ch ^ (key & 7))] = *(const u32x4 *)(k + (size_t)(kt + key) * ldqk + head * 64 + ch * 8);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int idx = tid + 256 * i, dd = idx >> 3, ch = idx & 7;
-            const u32x4 v = *(const u32x4 *)(vt + (size_t)(head * 64 + dd) * ldvt + kt + ch * 8);
-            const int sw = dd & 15;
-            sV[dd * 16 + ((2 * ch) ^ sw)] = u32x2{v.x, v.y};
-            sV[dd * 16 + ((2 * ch + 1) ^ sw)] = u32x2{v.z, v.w};
-        }
-        __syncthreads();
-
-        f32x16 S[2];
+        for (int qs = 0; qs < 2; ++qs) S[qs][0] = f32x16{}, S[qs][1] = f32x16{};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            S[kk] = f32x16{};
-            const int key = kk * 32 + l32;
+            const int row = kk * 32 + l32;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const int ch = ks * 2 + hh;
-                const bf16x8 kf = __builtin_bit_cast(bf16x8, sK[key * 8 + (ch ^ (key & 7))]);
-                S[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[kk], 0, 0, 0);
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, sK[row * 8 + ((ks * 2 + hh) ^ (row & 7))]);
+#pragma unroll
+                for (int qs = 0; qs < 2; ++qs)
+                    S[qs][kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qs][ks], S[qs][kk], 0, 0, 0);
             }
         }
         if (kt + 64 > k1) {
@@ -721,68 +752,105 @@ __global__ __launch_bounds__(256) void k_attention(const uint16_t *__restrict__ 
             for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int key = kt + kk * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-                    if (key >= k1) S[kk][r] = -INFINITY;
+                    const int key = kt + kk * 32 + perm32((r >> 2) * 8 + hh * 4 + (r & 3));
+                    if (key >= k1) S[0][kk][r] = -INFINITY, S[1][kk][r] = -INFINITY;
                 }
         }
-        float mx = -INFINITY;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int qs = 0; qs < 2; ++qs) {
+            float mx = -INFINITY;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kk][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = exp2f((m_run - m_new) * c);
-        const float mc = m_new * c;
-        float rs = 0.f;
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float p = exp2f(fmaf(S[kk][r], c, -mc));
-                S[kk][r] = p;
-                rs += p;
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[qs][kk][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float m_new = fmaxf(m_run[qs], mx);
+            if (__any(m_new > m_run[qs])) {
+                const float alpha = __builtin_amdgcn_exp2f((m_run[qs] - m_new) * c);
+                l_run[qs] *= alpha;
+                O[qs][0] *= alpha;
+                O[qs][1] *= alpha;
             }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
+            m_run[qs] = m_new;
+            const float mc = m_new * c;
+            // p = 2^(c s - c m) on the raw v_exp_f32 (weights below 2^-126 flush to 0);
+            // packed to bf16 at once, and the row sum taken over those same bf16 values
+            float rs = 0.f;
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) O[dt] *= alpha;
-
-        bf16x8 pf[4];
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int r = 0; r < 8; ++r) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[qs][kk][2 * r], c, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[qs][kk][2 * r + 1], c, -mc));
+                    const bf16x2 pb = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+                    P[qs][kk][r >> 2][r & 3] = __builtin_bit_cast(uint32_t, pb);
+                    rs = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rs, false);
+                }
+            l_run[qs] += rs;
+        }
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-            const int kk = s2 >> 1, i0 = (s2 & 1) * 2, i1 = i0 + 1;
-            const u32x4 w = u32x4{pack2(S[kk][i0 * 4 + 0], S[kk][i0 * 4 + 1]), pack2(S[kk][i0 * 4 + 2], S[kk][i0 * 4 + 3]),
-                                  pack2(S[kk][i1 * 4 + 0], S[kk][i1 * 4 + 1]), pack2(S[kk][i1 * 4 + 2], S[kk][i1 * 4 + 3])};
-            pf[s2] = __builtin_bit_cast(bf16x8, w);
-        }
+            const int kk = s2 >> 1, ip = s2 & 1;
+            bf16x8 pf[2];
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt) {
-            const int dd = dt * 32 + l32, sw = dd & 15;
+            for (int qs = 0; qs < 2; ++qs)
+                pf[qs] = __builtin_bit_cast(bf16x8, P[qs][kk][ip]);
 #pragma unroll
-            for (int s2 = 0; s2 < 4; ++s2) {
-                const int kk = s2 >> 1, i0 = (s2 & 1) * 2, i1 = i0 + 1;
-                const u32x2 va = sV[dd * 16 + ((kk * 8 + i0 * 2 + hh) ^ sw)];
-                const u32x2 vb = sV[dd * 16 + ((kk * 8 + i1 * 2 + hh) ^ sw)];
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, u32x4{va.x, va.y, vb.x, vb.y});
-                O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[s2], O[dt], 0, 0, 0);
+            for (int dt = 0; dt < 2; ++dt) {
+                const int row = dt * 32 + l32;
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, sV[row * 8 + ((kk * 4 + ip * 2 + hh) ^ (row & 7))]);
+#pragma unroll
+                for (int qs = 0; qs < 2; ++qs)
+                    O[qs][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qs], O[qs][dt], 0, 0, 0);
             }
         }
-        __syncthreads();
+    };
+
+    const int ntile = (k1 - k0 + 63) >> 6;
+    issue(k0, smem);
+    for (int t = 0; t < ntile; t += 2) {
+        const int kt = k0 + t * 64;
+        if (t + 1 < ntile) {
+            issue(kt + 64, smem + STAGE);
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+        lds_barrier();
+        if (active) compute(smem, kt);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (t + 1 < ntile) {
+            if (t + 2 < ntile) {
+                issue(kt + 128, smem);
+                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+            } else {
+                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            }
+            lds_barrier();
+            if (active) compute(smem + STAGE, kt + 64);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            lds_barrier();
+        }
     }
 
-    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
-    if (qrow < k1) {
-        const float inv = 1.0f / l_tot;
 #pragma unroll
-        for (int dt = 0; dt < 2; ++dt)
+    for (int qs = 0; qs < 2; ++qs) {
+        const float l_tot = l_run[qs] + __shfl_xor(l_run[qs], 32, 64);
+        const int qrow = qbase + qs * 32 + l32;
+        if (qrow < k1) {
+            const float inv = 1.0f / l_tot;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int d = dt * 32 + i * 8 + hh * 4;
-                *(u32x2 *)(o + (size_t)qrow * ldo + head * 64 + d) =
-                    u32x2{pack2(O[dt][i * 4 + 0] * inv, O[dt][i * 4 + 1] * inv),
-                          pack2(O[dt][i * 4 + 2] * inv, O[dt][i * 4 + 3] * inv)};
-            }
+            for (int dt = 0; dt < 2; ++dt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int d = dt * 32 + i * 8 + hh * 4;
+                    *(u32x2 *)(o + (size_t)qrow * ldo + head * 64 + d) =
+                        u32x2{pack2(O[qs][dt][i * 4 + 0] * inv, O[qs][dt][i * 4 + 1] * inv),
+                              pack2(O[qs][dt][i * 4 + 2] * inv, O[qs][dt][i * 4 + 3] * inv)};
+                }
+        }
     }
 }
 
