@@ -49,6 +49,18 @@ ube_status_t ube_step_rmsnorm(float const *x, float const *gain, void *h, size_t
 ube_status_t ube_step_attention(void const *q, void const *k, size_t ldqk, void const *vt, size_t ldvt, void *o,
                                 size_t ldo, uint32_t const *cu_host, size_t count, size_t heads, void *stream);
 
+/* E4M3 activation rows ("UForm" page, "Precision by Design": an e4m3 model runs
+ * its blocks in Float8): in bf16 [T x W] -> codes [T x W] (OCP E4M3FN bytes) and
+ * scales[T] = amax_row / 448, code = nearest-even E4M3 of value * (448 / amax_row)
+ * computed in fp32; an all-zero row gets scale 0 and zero codes. W % 8 == 0. */
+ube_status_t ube_step_quantize_e4m3(void const *in, void *codes, float *scales, size_t T, size_t W, void *stream);
+
+/* E4M3 projection: y[M x N] = bf16(sum_k (x[m,k] x_scale[m]) (w[n,k] w_scale)),
+ * w codes [N x K], x codes with round_up(M, 256) readable rows and x_scale
+ * entries. N % 256 == 0, K % 128 == 0. */
+ube_status_t ube_step_gemm_e4m3(void const *w, float w_scale, void const *x, float const *x_scale, void *y, size_t M,
+                                size_t N, size_t K, void *stream);
+
 /* Kernels of an encode call, for timing. */
 typedef enum ube_kernel_t {
     ube_kernel_gather_k = 0,
@@ -62,7 +74,8 @@ typedef enum ube_kernel_t {
     ube_kernel_gemm_down_k = 8,
     ube_kernel_final_norm_k = 9,
     ube_kernel_pool_k = 10,
-    ube_kernel_count_k = 11,
+    ube_kernel_quantize_k = 11,
+    ube_kernel_count_k = 12,
 } ube_kernel_t;
 
 /* Starts timing every launch of `kernel` made by encode calls in this

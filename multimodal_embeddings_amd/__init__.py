@@ -101,7 +101,7 @@ STATUS = {0: "success", 1: "invalid_argument", 2: "shape_mismatch", 3: "out_of_m
           6: "unsupported", 7: "internal"}
 SCALAR = {"unknown": 0, "u8": 1, "bf16": 2, "f32": 3, "e4m3": 4}
 KERNELS = ["gather", "patchify", "rmsnorm", "gemm_patch", "gemm_qkv", "attention", "gemm_out", "gemm_gate_up",
-           "gemm_down", "final_norm", "pool"]
+           "gemm_down", "final_norm", "pool", "quantize"]
 
 # every symbol the headers declare, with ctypes signatures
 _SIGNATURES = {
@@ -119,6 +119,8 @@ _SIGNATURES = {
     "ube_step_gemm": ([VP, VP, VP, SZ, SZ, SZ, VP], C.c_int),
     "ube_step_rmsnorm": ([VP, VP, VP, SZ, SZ, C.c_float, VP], C.c_int),
     "ube_step_attention": ([VP, VP, SZ, VP, SZ, VP, SZ, VP, SZ, SZ, VP], C.c_int),
+    "ube_step_quantize_e4m3": ([VP, VP, VP, SZ, SZ, VP], C.c_int),
+    "ube_step_gemm_e4m3": ([VP, C.c_float, VP, VP, VP, SZ, SZ, SZ, VP], C.c_int),
     "ube_kernel_timer_start": ([C.c_int, SZ], C.c_int),
     "ube_kernel_timer_stop": ([C.POINTER(C.c_double), C.POINTER(SZ)], C.c_int),
     "ube_kernel_name": ([C.c_int], C.c_char_p),
@@ -381,6 +383,15 @@ def step_attention(q, k, ldqk, vt, ldvt, o, ldo, cu, heads, stream=None):
     cu = np.ascontiguousarray(cu, dtype=np.uint32)
     _step(lib().ube_step_attention(_ptr(q), _ptr(k), ldqk, _ptr(vt), ldvt, _ptr(o), ldo, cu.ctypes.data,
                                    len(cu) - 1, heads, _stream_handle(stream)))
+
+
+def step_quantize_e4m3(x, codes, scales, T, W, stream=None):
+    _step(lib().ube_step_quantize_e4m3(_ptr(x), _ptr(codes), _ptr(scales), T, W, _stream_handle(stream)))
+
+
+def step_gemm_e4m3(w, w_scale, x, x_scale, y, M, N, K, stream=None):
+    _step(lib().ube_step_gemm_e4m3(_ptr(w), w_scale, _ptr(x), _ptr(x_scale), _ptr(y), M, N, K,
+                                   _stream_handle(stream)))
 
 
 def kernel_timer_start(kernel: str, max_launches: int):

@@ -83,9 +83,11 @@ struct ube_model_handle_t {
     size_t bytes = 0;
     uint16_t *embed = nullptr, *patch_t = nullptr, *wv = nullptr;
     struct Layer {
-        uint16_t *wqkv, *wo, *wgu, *wd;
+        uint16_t *wqkv, *wo, *wgu, *wd;  // packed [out x in]; E4M3 codes (bytes) when e4m3
         float *g1, *g2;
+        float s_qkv = 1.f, s_o = 1.f, s_gate = 1.f, s_up = 1.f, s_down = 1.f;  // E4M3 tensor scales
     };
+    bool e4m3 = false;
     std::vector<Layer> layers;
     float *gf = nullptr, *u = nullptr;
     float2 *rope = nullptr;
@@ -123,7 +125,10 @@ char const *check_geometry(ube_geometry_t const &g) {
     if (g.ffn % 64 != 0) return "ffn must be a multiple of 64";
     if (g.context > 32767) return "context must be at most 32767";
     if (g.rope_axes < 1 || g.rope_axes > 3) return "rope_axes must be 1, 2 or 3";
-    if (g.quantization != ube_scalar_bf16_k) return "only bf16 quantization is built";
+    if (g.quantization != ube_scalar_bf16_k && g.quantization != ube_scalar_e4m3_k)
+        return "quantization must be bf16 or e4m3";
+    if (g.quantization == ube_scalar_e4m3_k && (g.hidden % 256 != 0 || g.ffn % 128 != 0))
+        return "e4m3 blocks need hidden % 256 == 0 and ffn % 128 == 0";
     if (g.vocab > 65535) return "vocab too large";
     return nullptr;
 }
@@ -140,6 +145,38 @@ float bf16_value(uint16_t b) {
     std::memcpy(&f, &w, 4);
     return f;
 }
+
+// OCP E4M3FN code of v: 1 sign, 4 exponent (bias 7) and 3 mantissa bits, no
+// infinities; nearest value, ties to even; magnitudes past 448 saturate to 448.
+uint8_t e4m3_code(double v) {
+    const uint8_t sign = std::signbit(v) ? 0x80 : 0;
+    const double a = std::fabs(v);
+    if (a < 0x1p-6) {  // subnormals k * 2^-9
+        const int k = (int)std::nearbyint(a * 512.0);
+        return sign | (uint8_t)(k == 8 ? 0x08 : k);
+    }
+    int e2 = 0;
+    std::frexp(a, &e2);
+    int be = e2 - 1;  // a in [2^be, 2^(be+1))
+    int mant = (int)std::nearbyint(std::ldexp(a, 3 - be));  // 8 .. 16
+    if (mant == 16) be += 1, mant = 8;
+    if (be > 8 || (be == 8 && mant > 14)) be = 8, mant = 14;
+    return sign | (uint8_t)((be + 7) << 3) | (uint8_t)(mant - 8);
+}
+
+// Per-tensor E4M3: scale = amax / 448; codes of value / scale.
+double e4m3_scale(uint16_t const *w, size_t n) {
+    double amax = 0.0;
+    for (size_t i = 0; i < n; ++i) amax = std::max(amax, std::fabs((double)bf16_value(w[i])));
+    return amax > 0.0 ? amax / 448.0 : 0.0;
+}
+
+void e4m3_encode(uint8_t *dst, uint16_t const *packed, size_t n, double scale) {
+    for (size_t i = 0; i < n; ++i) dst[i] = scale > 0.0 ? e4m3_code((double)bf16_value(packed[i]) / scale) : 0;
+}
+
+// interleaved gate/up rows [2F x D]: 64b + [0,32) gate column 32b + r, 64b + [32,64) up
+size_t gate_up_row(size_t col, bool up) { return 64 * (col / 32) + (up ? 32 : 0) + col % 32; }
 
 }  // namespace
 
@@ -182,12 +219,14 @@ extern "C" void ube_model_init(ube_model_init_t *a) {
         };
         size_t o_embed = text ? take(g.vocab * D * 2) : 0;
         size_t o_patch = text ? 0 : take(D * KP * 2);
+        const bool e4m3 = g.quantization == ube_scalar_e4m3_k;
+        const size_t ES = e4m3 ? 1 : 2;  // bytes per block-matrix element
         std::vector<size_t> o_l(N * 6);
         for (size_t l = 0; l < N; ++l) {
-            o_l[l * 6 + 0] = take(3 * D * D * 2);
-            o_l[l * 6 + 1] = take(D * D * 2);
-            o_l[l * 6 + 2] = take(2 * F * D * 2);
-            o_l[l * 6 + 3] = take(F * D * 2);
+            o_l[l * 6 + 0] = take(3 * D * D * ES);
+            o_l[l * 6 + 1] = take(D * D * ES);
+            o_l[l * 6 + 2] = take(2 * F * D * ES);
+            o_l[l * 6 + 3] = take(F * D * ES);
             o_l[l * 6 + 4] = take(D * 4);
             o_l[l * 6 + 5] = take(D * 4);
         }
@@ -198,19 +237,48 @@ extern "C" void ube_model_init(ube_model_init_t *a) {
         char *hb = host.data();
         if (text) std::memcpy(hb + o_embed, w.embed, g.vocab * D * 2);
         else transpose_into((uint16_t *)(hb + o_patch), w.patch_proj, KP, D);
+        std::vector<ube_model_handle_t::Layer> scales(N);
+        std::vector<uint16_t> tmp;
+        // packed bf16 matrix -> its slot (as is, or as E4M3 codes of value / scale)
+        auto place = [&](size_t off, std::vector<uint16_t> const &packed, double scale) {
+            if (e4m3) e4m3_encode((uint8_t *)(hb + off), packed.data(), packed.size(), scale);
+            else std::memcpy(hb + off, packed.data(), packed.size() * 2);
+        };
         for (size_t l = 0; l < N; ++l) {
-            transpose_into((uint16_t *)(hb + o_l[l * 6 + 0]), w.w_qkv[l], D, 3 * D);
-            transpose_into((uint16_t *)(hb + o_l[l * 6 + 1]), w.w_o[l], D, D);
-            // gate/up interleaved in blocks of 32 output columns: rows 64b + [0,32) gate, 64b + [32,64) up
-            uint16_t *gu = (uint16_t *)(hb + o_l[l * 6 + 2]);
-            for (size_t col = 0; col < F; ++col) {
-                const size_t b = col / 32, r = col % 32;
-                for (size_t k = 0; k < D; ++k) {
-                    gu[(64 * b + r) * D + k] = w.w_gate[l][k * F + col];
-                    gu[(64 * b + 32 + r) * D + k] = w.w_up[l][k * F + col];
-                }
+            auto &sc = scales[l];
+            if (e4m3) {
+                sc.s_qkv = (float)e4m3_scale(w.w_qkv[l], D * 3 * D);
+                sc.s_o = (float)e4m3_scale(w.w_o[l], D * D);
+                sc.s_gate = (float)e4m3_scale(w.w_gate[l], D * F);
+                sc.s_up = (float)e4m3_scale(w.w_up[l], D * F);
+                sc.s_down = (float)e4m3_scale(w.w_down[l], F * D);
             }
-            transpose_into((uint16_t *)(hb + o_l[l * 6 + 3]), w.w_down[l], F, D);
+            tmp.assign(3 * D * D, 0);
+            transpose_into(tmp.data(), w.w_qkv[l], D, 3 * D);
+            place(o_l[l * 6 + 0], tmp, e4m3 ? e4m3_scale(w.w_qkv[l], D * 3 * D) : 0.0);
+            tmp.assign(D * D, 0);
+            transpose_into(tmp.data(), w.w_o[l], D, D);
+            place(o_l[l * 6 + 1], tmp, e4m3 ? e4m3_scale(w.w_o[l], D * D) : 0.0);
+            // gate/up interleaved in blocks of 32 output columns; E4M3 keeps one scale per tensor
+            tmp.assign(2 * F * D, 0);
+            for (size_t col = 0; col < F; ++col)
+                for (size_t k = 0; k < D; ++k) {
+                    tmp[gate_up_row(col, false) * D + k] = w.w_gate[l][k * F + col];
+                    tmp[gate_up_row(col, true) * D + k] = w.w_up[l][k * F + col];
+                }
+            if (e4m3) {
+                const double sg = e4m3_scale(w.w_gate[l], D * F), su = e4m3_scale(w.w_up[l], D * F);
+                uint8_t *dst = (uint8_t *)(hb + o_l[l * 6 + 2]);
+                for (size_t r = 0; r < 2 * F; ++r) {
+                    const double sr = ((r / 32) & 1) ? su : sg;
+                    e4m3_encode(dst + r * D, tmp.data() + r * D, D, sr);
+                }
+            } else {
+                place(o_l[l * 6 + 2], tmp, 0.0);
+            }
+            tmp.assign(F * D, 0);
+            transpose_into(tmp.data(), w.w_down[l], F, D);
+            place(o_l[l * 6 + 3], tmp, e4m3 ? e4m3_scale(w.w_down[l], F * D) : 0.0);
             std::memcpy(hb + o_l[l * 6 + 4], w.attn_norm[l], D * 4);
             std::memcpy(hb + o_l[l * 6 + 5], w.mlp_norm[l], D * 4);
         }
@@ -245,10 +313,16 @@ extern "C" void ube_model_init(ube_model_init_t *a) {
         m->embed = text ? (uint16_t *)(db + o_embed) : nullptr;
         m->patch_t = text ? nullptr : (uint16_t *)(db + o_patch);
         m->layers.resize(N);
-        for (size_t l = 0; l < N; ++l)
-            m->layers[l] = {(uint16_t *)(db + o_l[l * 6 + 0]), (uint16_t *)(db + o_l[l * 6 + 1]),
-                            (uint16_t *)(db + o_l[l * 6 + 2]), (uint16_t *)(db + o_l[l * 6 + 3]),
-                            (float *)(db + o_l[l * 6 + 4]),    (float *)(db + o_l[l * 6 + 5])};
+        m->e4m3 = e4m3;
+        for (size_t l = 0; l < N; ++l) {
+            m->layers[l] = scales[l];
+            m->layers[l].wqkv = (uint16_t *)(db + o_l[l * 6 + 0]);
+            m->layers[l].wo = (uint16_t *)(db + o_l[l * 6 + 1]);
+            m->layers[l].wgu = (uint16_t *)(db + o_l[l * 6 + 2]);
+            m->layers[l].wd = (uint16_t *)(db + o_l[l * 6 + 3]);
+            m->layers[l].g1 = (float *)(db + o_l[l * 6 + 4]);
+            m->layers[l].g2 = (float *)(db + o_l[l * 6 + 5]);
+        }
         m->gf = (float *)(db + o_gf);
         m->u = (float *)(db + o_u);
         m->wv = (uint16_t *)(db + o_wv);
@@ -394,10 +468,10 @@ void make_tiles(Plan &p) {
 // Device regions of one call.
 struct Layout {
     size_t Tpad = 0;
-    size_t out, cu, src, tiles, media, input, x, h, a, qk, vt, o, xf, s, pos, patches, total;
+    size_t out, cu, src, tiles, media, input, x, h, a, qk, vt, o, xf, s, pos, patches, q8, qs, total;
 };
 
-Layout carve(ube_geometry_t const &g, Plan const &p, bool media, size_t input_bytes) {
+Layout carve(ube_geometry_t const &g, Plan const &p, bool media, size_t input_bytes, bool e4m3) {
     Layout L{};
     const size_t D = g.hidden, F = g.ffn, H = g.heads;
     L.Tpad = align_up(p.T, 256) + kRowPad;
@@ -423,6 +497,8 @@ Layout carve(ube_geometry_t const &g, Plan const &p, bool media, size_t input_by
     L.s = take(L.Tpad * H * 4);
     L.pos = take(L.Tpad * 4 * 2);
     L.patches = take(media ? L.Tpad * 768 * 2 : 0);
+    L.q8 = take(e4m3 ? L.Tpad * std::max(D, F) : 0);  // E4M3 GEMM input rows
+    L.qs = take(e4m3 ? L.Tpad * 4 : 0);               // their per-row scales
     L.total = total;
     return L;
 }
@@ -480,7 +556,7 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
         if (hi > ar->dev && lo < ar->dev + ar->cap)
             throw Failure{ube_status_invalid_argument_k, "inputs lie inside the arena"};
     }
-    Layout L = carve(g, p, media, input_bytes);
+    Layout L = carve(g, p, media, input_bytes, m->e4m3);
 
     // grow the arena (only when outgrown)
     if (L.total > ar->cap) {
@@ -558,32 +634,55 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
             ga.w = m->patch_t, ga.x = patches, ga.M = T, ga.N = D, ga.K = 768;
             ga.out_f32 = x, ga.ld_f32 = D, ga.scale = 1.0f / 255.0f;
             timed(ube_kernel_gemm_patch_k, st, [&] { return launch_gemm(kEpiPatch, ga, st); });
-            timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm(x, m->layers[0].g1, h, T, D, eps, st); });
+            if (!m->e4m3)
+                timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm(x, m->layers[0].g1, h, T, D, eps, st); });
         }
         if (r.trace) UBE_HIP(hipMemcpyAsync(r.trace, x, (size_t)T * D * 4, hipMemcpyDeviceToDevice, st));
         // ---- blocks
+        uint8_t *q8 = (uint8_t *)(db + L.q8);
+        float *qs = (float *)(db + L.qs);
+        // one projection: bf16 operands, or E4M3 rows (codes + per-row scales) against E4M3 weights
+        auto project = [&](ube_kernel_t kind, int epi, GemmArgs ga, float w_scale, float w_scale2) {
+            if (m->e4m3) {
+                ga.x = (const uint16_t *)q8, ga.x_scale = qs, ga.w_scale = w_scale, ga.w_scale2 = w_scale2;
+                timed(kind, st, [&] { return launch_gemm_e4m3(epi, ga, st); });
+            } else {
+                timed(kind, st, [&] { return launch_gemm(epi, ga, st); });
+            }
+        };
+        // RMSNorm into the next projection's input (bf16 h, or E4M3 rows)
+        auto norm = [&](const float *gain) {
+            if (m->e4m3)
+                timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm_e4m3(x, gain, q8, qs, T, D, eps, st); });
+            else
+                timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm(x, gain, h, T, D, eps, st); });
+        };
+        auto quantize = [&](const uint16_t *rows, int width) {
+            timed(ube_kernel_quantize_k, st, [&] { return launch_quantize_rows(rows, q8, qs, T, width, st); });
+        };
         for (size_t l = 0; l < g.depth; ++l) {
             auto const &Wl = m->layers[l];
-            if (l > 0)
-                timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm(x, Wl.g1, h, T, D, eps, st); });
+            if (l > 0 || m->e4m3) norm(Wl.g1);
             GemmArgs qa{};
             qa.w = Wl.wqkv, qa.x = h, qa.M = T, qa.N = 3 * D, qa.K = D;
             qa.out_bf16 = qk, qa.ld_out = 2 * D, qa.vt = vt, qa.ld_vt = ldvt, qa.pos = pos, qa.rope = m->rope;
             qa.D = D, qa.sec0 = m->sec0, qa.sec1 = m->sec1;
-            timed(ube_kernel_gemm_qkv_k, st, [&] { return launch_gemm(kEpiQkv, qa, st); });
+            project(ube_kernel_gemm_qkv_k, kEpiQkv, qa, Wl.s_qkv, 0.f);
             timed(ube_kernel_attention_k, st, [&] {
                 return launch_attention(qk, qk + D, 2 * D, vt, ldvt, o, D, cu, tiles, ntiles, H, st);
             });
+            if (m->e4m3) quantize(o, D);
             GemmArgs oa{};
             oa.w = Wl.wo, oa.x = o, oa.M = T, oa.N = D, oa.K = D, oa.out_f32 = x, oa.ld_f32 = D;
-            timed(ube_kernel_gemm_out_k, st, [&] { return launch_gemm(kEpiResid, oa, st); });
-            timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm(x, Wl.g2, h, T, D, eps, st); });
+            project(ube_kernel_gemm_out_k, kEpiResid, oa, Wl.s_o, 0.f);
+            norm(Wl.g2);
             GemmArgs ua{};
             ua.w = Wl.wgu, ua.x = h, ua.M = T, ua.N = 2 * F, ua.K = D, ua.out_bf16 = act, ua.ld_out = F;
-            timed(ube_kernel_gemm_gate_up_k, st, [&] { return launch_gemm(kEpiSwiglu, ua, st); });
+            project(ube_kernel_gemm_gate_up_k, kEpiSwiglu, ua, Wl.s_gate, Wl.s_up);
+            if (m->e4m3) quantize(act, F);
             GemmArgs da{};
             da.w = Wl.wd, da.x = act, da.M = T, da.N = D, da.K = F, da.out_f32 = x, da.ld_f32 = D;
-            timed(ube_kernel_gemm_down_k, st, [&] { return launch_gemm(kEpiResid, da, st); });
+            project(ube_kernel_gemm_down_k, kEpiResid, da, Wl.s_down, 0.f);
             if (r.trace)
                 UBE_HIP(hipMemcpyAsync(r.trace + (l + 1) * (size_t)T * D, x, (size_t)T * D * 4,
                                        hipMemcpyDeviceToDevice, st));
@@ -765,6 +864,23 @@ extern "C" ube_status_t ube_step_gemm(void const *w, void const *x, void *y, siz
     return step_status(launch_gemm(kEpiStore, a, (hipStream_t)stream));
 }
 
+extern "C" ube_status_t ube_step_quantize_e4m3(void const *in, void *codes, float *scales, size_t T, size_t W,
+                                               void *stream) {
+    if (!in || !codes || !scales || W % 8 || !W || T > 0x7fffffff || W > 0x7fffffff) return ube_status_invalid_argument_k;
+    return step_status(launch_quantize_rows((const uint16_t *)in, (uint8_t *)codes, scales, (int)T, (int)W,
+                                            (hipStream_t)stream));
+}
+
+extern "C" ube_status_t ube_step_gemm_e4m3(void const *w, float w_scale, void const *x, float const *x_scale, void *y,
+                                           size_t M, size_t N, size_t K, void *stream) {
+    if (!w || !x || !x_scale || !y || N % 256 || K % 128 || !N || !K || M > 0x7fffffff)
+        return ube_status_invalid_argument_k;
+    GemmArgs a{};
+    a.w = (const uint16_t *)w, a.x = (const uint16_t *)x, a.M = (int)M, a.N = (int)N, a.K = (int)K;
+    a.out_bf16 = (uint16_t *)y, a.ld_out = (int)N, a.x_scale = x_scale, a.w_scale = w_scale;
+    return step_status(launch_gemm_e4m3(kEpiStore, a, (hipStream_t)stream));
+}
+
 extern "C" ube_status_t ube_step_rmsnorm(float const *x, float const *gain, void *h, size_t T, size_t D, float eps,
                                          void *stream) {
     if (!x || !gain || !h || !row_width_supported(D) || T > 0x7fffffff) return ube_status_invalid_argument_k;
@@ -845,7 +961,7 @@ extern "C" ube_status_t ube_kernel_timer_stop(double *total_ms, size_t *launches
 }
 
 extern "C" char const *ube_kernel_name(ube_kernel_t k) {
-    static char const *names[] = {"gather", "patchify", "rmsnorm", "gemm_patch", "gemm_qkv", "attention",
-                                  "gemm_out", "gemm_gate_up", "gemm_down", "final_norm", "pool"};
+    static char const *names[] = {"gather",       "patchify",  "rmsnorm",    "gemm_patch", "gemm_qkv", "attention",
+                                  "gemm_out",     "gemm_gate_up", "gemm_down", "final_norm", "pool",     "quantize"};
     return ((int)k >= 0 && k < ube_kernel_count_k) ? names[k] : "unknown";
 }

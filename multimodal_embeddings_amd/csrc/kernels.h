@@ -36,9 +36,15 @@ struct GemmArgs {
     int D;                // width of q, k, v (QKV epilogue)
     int sec0, sec1;       // rotary pair sections: axis 0 for j < sec0, 1 for j < sec0+sec1, else 2
     float scale;          // patch epilogue scale
+    const float *x_scale; // E4M3: per-token activation scale [M_alloc]
+    float w_scale;        // E4M3: weight tensor scale (gate tensor for SwiGLU)
+    float w_scale2;       // E4M3: up tensor scale (SwiGLU)
 };
 
 hipError_t launch_gemm(int epilogue, const GemmArgs &args, hipStream_t stream);
+// E4M3 operands (w, x are bytes; K counts elements, K % 128 == 0, N % 256 == 0);
+// the accumulator is multiplied by x_scale[token] * w_scale before the epilogue.
+hipError_t launch_gemm_e4m3(int epilogue, const GemmArgs &args, hipStream_t stream);
 
 // Byte gather + RMSNorm (layer-0 attention norm): tiles are (item, first token).
 hipError_t launch_gather_text(const uint8_t *data, const int64_t *src, const int *cu, const int2 *tiles,
@@ -52,6 +58,11 @@ struct MediaItem {
 };
 hipError_t launch_patchify(const uint8_t *pixels, const MediaItem *items, const int *cu, const int2 *tiles,
                            int ntiles, uint16_t *patches, int16_t *pos, int axes, hipStream_t stream);
+
+// E4M3 activations: codes + per-row scale amax/448 (value = code * scale).
+hipError_t launch_rmsnorm_e4m3(const float *x, const float *gain, uint8_t *h8, float *hs, int T, int D, float eps,
+                               hipStream_t stream);
+hipError_t launch_quantize_rows(const uint16_t *in, uint8_t *out, float *scale, int T, int W, hipStream_t stream);
 
 hipError_t launch_rmsnorm(const float *x, const float *gain, uint16_t *h, int T, int D, float eps,
                           hipStream_t stream);

@@ -232,6 +232,89 @@ __global__ __launch_bounds__(256) void k_final_norm_scores(const float *__restri
     }
 }
 
+// ------------------------------------------------------------- E4M3 rows
+//
+// Per-row activation quantisation for the E4M3 GEMMs: scale = amax / 448, code
+// = OCP E4M3 of value * 448 / amax (v_cvt_pk_fp8_f32: nearest even; |values| stay
+// within 448). An all-zero row gets scale 0 and zero codes.
+
+__device__ __forceinline__ uint32_t pack4_e4m3(float a, float b, float c, float d) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);  // bytes 0, 1
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(c, d, w, true);       // bytes 2, 3
+    return (uint32_t)w;
+}
+
+// RMSNorm straight to E4M3 codes and a per-row scale.
+template <int V, int C>
+__global__ __launch_bounds__(256) void k_rmsnorm_e4m3(const float *__restrict__ x, const float *__restrict__ gain,
+                                                      uint8_t *__restrict__ h8, float *__restrict__ hs, int T, int D,
+                                                      float eps) {
+    static_assert(V % 4 == 0 || V == 2, "");
+    const int lane = threadIdx.x & 63;
+    const int waves = gridDim.x * 4;
+    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += waves) {
+        float v[C][V];
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            RowIO<V>::load_f32(x + (size_t)t * D + c * 64 * V + lane * V, v[c]);
+#pragma unroll
+            for (int i = 0; i < V; ++i) ss += v[c][i] * v[c][i];
+        }
+        ss = wave_sum(ss);
+        const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c)
+#pragma unroll
+            for (int i = 0; i < V; ++i) {
+                v[c][i] = v[c][i] * inv * gain[c * 64 * V + lane * V + i];
+                amax = fmaxf(amax, fabsf(v[c][i]));
+            }
+        amax = wave_max(amax);
+        const float q = amax > 0.f ? 448.0f / amax : 0.f;
+        if (lane == 0) hs[t] = amax / 448.0f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            uint8_t *dst = h8 + (size_t)t * D + c * 64 * V + lane * V;
+            if constexpr (V == 2) {
+                const uint32_t w = pack4_e4m3(v[c][0] * q, v[c][1] * q, 0.f, 0.f);
+                *(uint16_t *)dst = (uint16_t)(w & 0xffff);
+            } else {
+#pragma unroll
+                for (int i = 0; i < V; i += 4)
+                    *(uint32_t *)(dst + i) = pack4_e4m3(v[c][i] * q, v[c][i + 1] * q, v[c][i + 2] * q, v[c][i + 3] * q);
+            }
+        }
+    }
+}
+
+// bf16 rows [T x W] -> E4M3 codes + per-row scales; one wave per row, W % 8 == 0.
+__global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restrict__ in, uint8_t *__restrict__ out,
+                                                       float *__restrict__ scale, int T, int W) {
+    const int lane = threadIdx.x & 63;
+    const int waves = gridDim.x * 4;
+    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += waves) {
+        const uint16_t *row = in + (size_t)t * W;
+        float amax = 0.f;
+        for (int e = lane * 8; e < W; e += 512) {
+            float v[8];
+            RowIO<8>::load_bf16(row + e, v);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        }
+        amax = wave_max(amax);
+        const float q = amax > 0.f ? 448.0f / amax : 0.f;
+        if (lane == 0) scale[t] = amax / 448.0f;
+        for (int e = lane * 8; e < W; e += 512) {
+            float v[8];
+            RowIO<8>::load_bf16(row + e, v);
+            *(u32x2 *)(out + (size_t)t * W + e) =
+                u32x2{pack4_e4m3(v[0] * q, v[1] * q, v[2] * q, v[3] * q), pack4_e4m3(v[4] * q, v[5] * q, v[6] * q, v[7] * q)};
+        }
+    }
+}
+
 // (V, C) with D = 64*V*C, C <= 8.
 #define UBE_ROW_DISPATCH(D, ...)                         \
     do {                                                         \
@@ -275,6 +358,20 @@ hipError_t launch_gather_text(const uint8_t *data, const int64_t *src, const int
 static int row_grid(int T) {
     int blocks = (T + 3) / 4;
     return blocks < 8192 ? blocks : 8192;
+}
+
+hipError_t launch_rmsnorm_e4m3(const float *x, const float *gain, uint8_t *h8, float *hs, int T, int D, float eps,
+                               hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    UBE_ROW_DISPATCH(D, (k_rmsnorm_e4m3<V, C><<<row_grid(T), 256, 0, stream>>>(x, gain, h8, hs, T, D, eps)));
+    return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows(const uint16_t *in, uint8_t *out, float *scale, int T, int W, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    if (W % 8) return hipErrorInvalidValue;
+    k_quantize_rows<<<row_grid(T), 256, 0, stream>>>(in, out, scale, T, W);
+    return hipGetLastError();
 }
 
 hipError_t launch_rmsnorm(const float *x, const float *gain, uint16_t *h, int T, int D, float eps,
@@ -532,9 +629,12 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int EPI>
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+template <int EPI, bool FP8>
 __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
-    constexpr int BM = 256, BN = 256, BK = 64;
+    // Both operand tiles have 128-byte LDS rows: 64 bf16 or 128 E4M3 values of K per stage.
+    constexpr int BM = 256, BN = 256, ES = FP8 ? 1 : 2, BK = 128 / ES;
     constexpr int WM = 128, WN = 64, TM = WM / 32, TN = WN / 32;
     constexpr int STAGE = (BM + BN) * 8;  // 16-byte chunks per stage
     __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * STAGE];
@@ -546,25 +646,27 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int mt = logical / NT, nt = logical % NT;
     const int m0 = mt * BM, n0 = nt * BN;
-    const int K = a.K;
+    const size_t row_bytes = (size_t)a.K * ES;
+    const uint8_t *wb = (const uint8_t *)a.w, *xb = (const uint8_t *)a.x;
 
-    // global source of this lane for load round r (0..3 weights, 4..7 activations)
-    // chunk slot p = 512 r' + 64 wave + lane within the operand tile: row p / 8, LDS chunk p % 8
-    const int prow = (wave * 64 + lane) >> 3;           // + 64 r'
+    // global source of this lane for load round r (0..3 weights, 4..7 activations):
+    // chunk slot p = 512 r + 64 wave + lane of the operand tile, row p / 8, LDS chunk p % 8
+    const int prow = (wave * 64 + lane) >> 3;
     const int pch = lane & 7;
     auto issue = [&](int k0, int buf) {
         u32x4 *dst = smem + buf * STAGE;
+        const size_t kb = (size_t)k0 * ES;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = r * 64 + prow;
             const int ch = pch ^ (row & 7);
-            lds_dma16(a.w + (size_t)(n0 + row) * K + k0 + ch * 8, dst + r * 512 + wave * 64);
+            lds_dma16(wb + (size_t)(n0 + row) * row_bytes + kb + ch * 16, dst + r * 512 + wave * 64);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = r * 64 + prow;
             const int ch = pch ^ (row & 7);
-            lds_dma16(a.x + (size_t)(m0 + row) * K + k0 + ch * 8, dst + BN * 8 + r * 512 + wave * 64);
+            lds_dma16(xb + (size_t)(m0 + row) * row_bytes + kb + ch * 16, dst + BN * 8 + r * 512 + wave * 64);
         }
     };
 
@@ -580,28 +682,56 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
     // s_barrier: a __syncthreads() fence would also wait for the next stage.
     auto compute = [&](const u32x4 *sW) {
         const u32x4 *sX = sW + BN * 8;
+        if constexpr (!FP8) {
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int ch = ks * 2 + hh;
-            bf16x8 af[TN], bfr[TM];
+            for (int ks = 0; ks < 4; ++ks) {
+                const int ch = ks * 2 + hh;
+                bf16x8 af[TN], bfr[TM];
 #pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                const int row = wn * WN + tn * 32 + l32;
-                af[tn] = __builtin_bit_cast(bf16x8, sW[row * 8 + (ch ^ (row & 7))]);
+                for (int tn = 0; tn < TN; ++tn) {
+                    const int row = wn * WN + tn * 32 + l32;
+                    af[tn] = __builtin_bit_cast(bf16x8, sW[row * 8 + (ch ^ (row & 7))]);
+                }
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    const int row = wm * WM + tm * 32 + l32;
+                    bfr[tm] = __builtin_bit_cast(bf16x8, sX[row * 8 + (ch ^ (row & 7))]);
+                }
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                    for (int tm = 0; tm < TM; ++tm)
+                        acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tn], bfr[tm], acc[tn][tm], 0, 0, 0);
             }
+        } else {
+            // v_mfma_scale_f32_32x32x64_f8f6f4, both operands OCP E4M3 (format 0), unit
+            // E8M0 block scales (127): lane half hh supplies 32 consecutive k bytes.
 #pragma unroll
-            for (int tm = 0; tm < TM; ++tm) {
-                const int row = wm * WM + tm * 32 + l32;
-                bfr[tm] = __builtin_bit_cast(bf16x8, sX[row * 8 + (ch ^ (row & 7))]);
+            for (int ks = 0; ks < 2; ++ks) {
+                const int ch = ks * 4 + hh * 2;
+                i32x8 af[TN], bfr[TM];
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn) {
+                    const int row = wn * WN + tn * 32 + l32;
+                    const u32x4 lo = sW[row * 8 + (ch ^ (row & 7))], hi = sW[row * 8 + ((ch + 1) ^ (row & 7))];
+                    af[tn] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                }
+#pragma unroll
+                for (int tm = 0; tm < TM; ++tm) {
+                    const int row = wm * WM + tm * 32 + l32;
+                    const u32x4 lo = sX[row * 8 + (ch ^ (row & 7))], hi = sX[row * 8 + ((ch + 1) ^ (row & 7))];
+                    bfr[tm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+                }
+#pragma unroll
+                for (int tn = 0; tn < TN; ++tn)
+#pragma unroll
+                    for (int tm = 0; tm < TM; ++tm)
+                        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[tn], bfr[tm], acc[tn][tm], 0, 0,
+                                                                                      0, 127, 0, 127);
             }
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn)
-#pragma unroll
-                for (int tm = 0; tm < TM; ++tm)
-                    acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tn], bfr[tm], acc[tn][tm], 0, 0, 0);
         }
     };
-    const int nk = K / BK;
+    const int nk = a.K / BK;
     issue(0, 0);
     for (int kt = 0; kt < nk; kt += 2) {
         if (kt + 1 < nk) {
@@ -627,6 +757,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
             lds_barrier();
         }
     }
+    if constexpr (FP8) {
+        // dequantise: per-token activation scale times the weight tensor's scale
+        // (the SwiGLU matrix holds two tensors: gate blocks even, up blocks odd)
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+            const float sa = a.x_scale[m0 + wm * WM + tm * 32 + l32];
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) {
+                const float sw = (EPI == kEpiSwiglu && (tn & 1)) ? a.w_scale2 : a.w_scale;
+                acc[tn][tm] *= sa * sw;
+            }
+        }
+    }
     gemm_epilogue<EPI, TM, TN>(a, acc, m0 + wm * WM, n0 + wn * WN, l32, hh);
 }
 
@@ -644,14 +787,15 @@ static hipError_t gemm_dispatch(int epi, const GemmArgs &a, hipStream_t stream) 
     return hipGetLastError();
 }
 
+template <bool FP8>
 static hipError_t gemm256_dispatch(int epi, const GemmArgs &a, hipStream_t stream) {
     const int tiles = ((a.M + 255) / 256) * (a.N / 256);
     switch (epi) {
-        case kEpiStore: k_gemm256<kEpiStore><<<tiles, 512, 0, stream>>>(a); break;
-        case kEpiQkv: k_gemm256<kEpiQkv><<<tiles, 512, 0, stream>>>(a); break;
-        case kEpiResid: k_gemm256<kEpiResid><<<tiles, 512, 0, stream>>>(a); break;
-        case kEpiSwiglu: k_gemm256<kEpiSwiglu><<<tiles, 512, 0, stream>>>(a); break;
-        case kEpiPatch: k_gemm256<kEpiPatch><<<tiles, 512, 0, stream>>>(a); break;
+        case kEpiStore: k_gemm256<kEpiStore, FP8><<<tiles, 512, 0, stream>>>(a); break;
+        case kEpiQkv: k_gemm256<kEpiQkv, FP8><<<tiles, 512, 0, stream>>>(a); break;
+        case kEpiResid: k_gemm256<kEpiResid, FP8><<<tiles, 512, 0, stream>>>(a); break;
+        case kEpiSwiglu: k_gemm256<kEpiSwiglu, FP8><<<tiles, 512, 0, stream>>>(a); break;
+        case kEpiPatch: k_gemm256<kEpiPatch, FP8><<<tiles, 512, 0, stream>>>(a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
@@ -660,8 +804,14 @@ static hipError_t gemm256_dispatch(int epi, const GemmArgs &a, hipStream_t strea
 hipError_t launch_gemm(int epi, const GemmArgs &a, hipStream_t stream) {
     if (a.M == 0) return hipSuccess;
     if (a.N % 128 != 0 || a.K % 64 != 0) return hipErrorInvalidValue;
-    if (a.N % 256 == 0) return gemm256_dispatch(epi, a, stream);
+    if (a.N % 256 == 0) return gemm256_dispatch<false>(epi, a, stream);
     return gemm_dispatch<256, 128>(epi, a, stream);
+}
+
+hipError_t launch_gemm_e4m3(int epi, const GemmArgs &a, hipStream_t stream) {
+    if (a.M == 0) return hipSuccess;
+    if (a.N % 256 != 0 || a.K % 128 != 0 || !a.x_scale) return hipErrorInvalidValue;
+    return gemm256_dispatch<true>(epi, a, stream);
 }
 
 // =========================================================== attention

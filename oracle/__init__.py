@@ -62,6 +62,8 @@ def _declare(L):
     L.oracle_e4m3_round.argtypes = [C.c_double]
     L.oracle_e4m3_round.restype = C.c_double
     L.oracle_e4m3_qdq.argtypes = [P, P, SZ]
+    L.oracle_bf16_round.argtypes = [C.c_double]
+    L.oracle_bf16_round.restype = C.c_double
     L.oracle_rmsnorm.argtypes = [P, P, SZ, SZ, C.c_double, P]
     L.oracle_rope_axis_of.argtypes = [SZ, SZ, C.c_int]
     L.oracle_rope_axis_of.restype = C.c_int
@@ -134,6 +136,10 @@ def embed_patches(pixels, frames, height, width, channels, patch, patch_proj, ax
 
 def e4m3_round(v: float) -> float:
     return lib().oracle_e4m3_round(float(v))
+
+
+def bf16_round(v: float) -> float:
+    return lib().oracle_bf16_round(float(v))
 
 
 def e4m3_qdq(a):

@@ -172,6 +172,25 @@ static void e4m3_qdq(const double *in, double *out, size_t n) {
 
 void oracle_e4m3_qdq(const double *in, double *out, size_t n) { e4m3_qdq(in, out, n); }
 
+/* Nearest bfloat16 value of v, as stored by a GPU that holds activations in
+ * bf16 ("UForm" page, "Precision by Design": store and compute in BF16,
+ * accumulate in Float32): v is first rounded to float32, then to bf16 with ties
+ * to even (the fp32 accumulator -> bf16 storage path). */
+double oracle_bf16_round(double v) {
+    float f = (float)v;
+    uint32_t u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7f800000u) == 0x7f800000u) return v; /* inf / nan unchanged */
+    u += 0x7fffu + ((u >> 16) & 1u);
+    u &= 0xffff0000u;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+static void bf16_round_all(double *a, size_t n) {
+    for (size_t i = 0; i < n; ++i) a[i] = oracle_bf16_round(a[i]);
+}
+
 /* ------------------------------------------------------------- the blocks */
 
 /* y[T x N] = x[T x K] W[K x N]. With `e4m3`, every row of x is first
@@ -322,7 +341,10 @@ static double *widen(const float *w, size_t n, int e4m3) {
  * Design"). Readings: x += Attn(RMSNorm1(x)); x += MLP(RMSNorm2(x)); fused
  * W_qkv = [W_q | W_k | W_v] with no biases; MLP = (SiLU(h W_gate) * (h W_up))
  * W_down. In E4M3 mode every block matrix is quantised per tensor and every
- * GEMM input row per row. x is [T x D], updated in place. */
+ * GEMM input row per row, and the activations the pages store in bf16 are
+ * rounded to bf16 where they are stored: q and k after the rotation, v, the
+ * attention output o and the SwiGLU output a (the normalised rows h are
+ * quantised straight from their fp32 values). x is [T x D], updated in place. */
 void oracle_block(const oracle_geometry_t *g, const oracle_block_t *w, double *x, const int32_t *pos,
                   const uint64_t *cu, size_t count, size_t T) {
     size_t D = g->hidden, H = g->heads, F = g->ffn, d = D / H;
@@ -350,7 +372,13 @@ void oracle_block(const oracle_geometry_t *g, const oracle_block_t *w, double *x
         }
     oracle_rope(q, pos, T, H, d, g->rope_axes, g->rope_base);
     oracle_rope(k, pos, T, H, d, g->rope_axes, g->rope_base);
+    if (g->e4m3) {
+        bf16_round_all(q, T * D);
+        bf16_round_all(k, T * D);
+        bf16_round_all(v, T * D);
+    }
     oracle_attention(q, k, v, cu, count, H, d, o);
+    if (g->e4m3) bf16_round_all(o, T * D);
     matmul(o, T, D, Wo, D, y, g->e4m3);
     for (size_t i = 0; i < T * D; ++i) x[i] += y[i];
 
@@ -359,6 +387,7 @@ void oracle_block(const oracle_geometry_t *g, const oracle_block_t *w, double *x
     matmul(h, T, D, Wg, F, gt, g->e4m3);
     matmul(h, T, D, Wu, F, up, g->e4m3);
     for (size_t i = 0; i < T * F; ++i) gt[i] = silu(gt[i]) * up[i];
+    if (g->e4m3) bf16_round_all(gt, T * F);
     matmul(gt, T, F, Wd, D, y, g->e4m3);
     for (size_t i = 0; i < T * D; ++i) x[i] += y[i];
 

@@ -203,3 +203,45 @@ def test_video_small_clips_match_oracle(ube):
 def _dev(batch):
     batch.data_device = device_bytes(batch.data)
     return batch
+
+
+def test_video_e4m3_small_clips_match_oracle_e4m3_mode(ube):
+    w, model, arena = _model(ube, "video1024_e4m3")
+    assert model.describe()["quantization"] == 4
+    batch = synth.media_batch(3, 4, 112, 112, seed=4)  # 4 x 7 x 7 = 196 tokens per clip
+    rows, stats = ube.encode(model, arena, _dev(batch))
+    got = _pooled(rows)
+    want, _ = oracle.encode_media(w, batch)  # the oracle's E4M3 mode (weights and GEMM rows quantised)
+    check_pooled(got, want, "video-small-e4m3", e4m3=True)
+    # for information: the same clips through the bf16 model of the same weights
+    wb, mb, ab = _model(ube, "video1024")
+    rows_b, _ = ube.encode(mb, ab, _dev(batch))
+    from tests.gpu_util import row_cos
+    say(f"  e4m3 vs bf16 pooled cosine: min {row_cos(got, _pooled(rows_b)).min():.5f}")
+
+
+def _video_full(ube, name):
+    w, model, arena = _model(ube, name)
+    batch = synth.workload_inputs("video")
+    rows, stats = ube.encode(model, arena, _dev(batch))
+    assert stats == (0, 16 * 1568) and rows.count == 16
+    return w, batch, _pooled(rows)
+
+
+def test_video_full_batch_sampled_parity(ube):
+    w, batch, full = _video_full(ube, "video1024")
+    sub = synth.subset(batch, [0])
+    want, _ = oracle.encode_media(w, sub)
+    check_pooled(full[[0]], want, "video")
+
+
+def test_video_e4m3_full_batch_sampled_parity(ube):
+    w, batch, full = _video_full(ube, "video1024_e4m3")
+    sub = synth.subset(batch, [0])
+    want, _ = oracle.encode_media(w, sub)
+    from tests.gpu_util import row_cos
+    say(f"  e4m3 clip 0: cos {row_cos(full[[0]], want)[0]:.6f}, max |diff| {np.abs(full[0] - want[0]).max():.3e}, "
+        f"pooled rms {np.sqrt((want ** 2).mean()):.3e}")
+    _, _, full_bf16 = _video_full(ube, "video1024")
+    say(f"  e4m3 vs bf16 run, all clips: min cos {row_cos(full, full_bf16).min():.5f}")
+    check_pooled(full[[0]], want, "video-e4m3", e4m3=True)

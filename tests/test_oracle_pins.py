@@ -506,3 +506,14 @@ def test_e4m3_saturates_and_qdq_scale():
     assert all(round(float(abs(x)), 9) in {round(v, 9) for v in vals} for x in q[:50])
     assert np.all(np.abs(r - a) <= np.abs(a) * 2 ** -4 + s * 2 ** -10)
     assert not oracle.e4m3_qdq(np.zeros(8)).any()
+
+
+def test_bf16_round_matches_library_cast():
+    vals = np.concatenate([RNG.standard_normal(2000) * np.exp(RNG.uniform(-20, 20, 2000)),
+                           [0.0, -0.0, 1.0, 1.00390625, 1.0078125, 1.01171875, 3.0e38, -1e-39]])
+    f32 = vals.astype(np.float32)
+    want = torch.from_numpy(f32).to(torch.bfloat16).double().numpy()
+    got = np.array([oracle.bf16_round(float(v)) for v in f32])
+    np.testing.assert_array_equal(got, want)
+    # ties go to even: 1 + 2^-8 sits halfway between 1 and 1 + 2^-7
+    assert oracle.bf16_round(1.0 + 2 ** -8) == 1.0 and oracle.bf16_round(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6
