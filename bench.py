@@ -33,6 +33,7 @@ WORKLOAD_TEXT = {
     "tiny": "tiny encoder depth 2, hidden 128; 8 rows, lengths 16..64",
     "image": "image encoder depth 12, hidden 768, 12 heads, 2-axis rotary; 128 images 256x256x3 (256 patches)",
     "video": "video encoder depth 24, hidden 1024, 16 heads, 3-axis rotary; 16 clips 8x224x224x3 (1568 patches)",
+    "video_e4m3": "video encoder as above with E4M3 blocks (per-tensor weight scales, per-row activation scales)",
 }
 
 
@@ -94,7 +95,10 @@ def main():
     ap.add_argument("--workload", default="throughput", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--kernel", default="gemm_gate_up", help="dominant kernel for the roofline entry")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", default="0,1")
+    ap.add_argument("--cpu-rows", default=",".join(str(i) for i in range(24)))
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="first copy MIB MiB device-to-device 3 times (a plain copy kernel of known size, "
+                         "for calibrating HBM byte counters)")
     ap.add_argument("--per-kernel", action="store_true", help="also time every kernel kind (extra passes)")
     args = ap.parse_args()
 
@@ -106,6 +110,16 @@ def main():
     import torch
     import multimodal_embeddings_amd as ube
     from multimodal_embeddings_amd import configs, synth
+
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy probe: 3 copies of {n} bytes (read {n}, write {n} each)", file=sys.stderr, flush=True)
+        del src, dst
 
     wl = configs.WORKLOADS[args.workload]
     g = configs.geometry(wl["geometry"])
@@ -171,7 +185,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "e4m3" if g["quantization"] == "e4m3" else "bf16",
         "data": "synthetic (seeded bytes, random-init bf16 weights N(0, 0.02))",
         "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}", "items": batch.count,
                    "tokens": int(T), "parallelism": "1 GPU"},
