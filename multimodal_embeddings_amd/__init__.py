@@ -17,7 +17,8 @@ import numpy as np
 from . import configs
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libube.so")
+# UBE_LIBRARY may name another build of libube.so (A/B comparisons of kernel versions)
+LIB_PATH = os.environ.get("UBE_LIBRARY") or os.path.join(HERE, "libube.so")
 
 
 class ExtensionMissing(RuntimeError):

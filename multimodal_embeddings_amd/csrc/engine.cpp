@@ -146,6 +146,14 @@ float bf16_value(uint16_t b) {
     return f;
 }
 
+// float -> bf16 bits, round to nearest even (finite inputs)
+uint16_t bf16_bits(float f) {
+    uint32_t u;
+    std::memcpy(&u, &f, 4);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
 // OCP E4M3FN code of v: 1 sign, 4 exponent (bias 7) and 3 mantissa bits, no
 // infinities; nearest value, ties to even; magnitudes past 448 saturate to 448.
 uint8_t e4m3_code(double v) {
@@ -253,8 +261,17 @@ extern "C" void ube_model_init(ube_model_init_t *a) {
                 sc.s_up = (float)e4m3_scale(w.w_up[l], D * F);
                 sc.s_down = (float)e4m3_scale(w.w_down[l], F * D);
             }
+            // bf16 blocks: each RMSNorm gain folds into the projection that reads the
+            // normalised rows, W'[n][k] = g[k] W[k][n] (the kernels apply 1/rms(x) to the
+            // accumulator). E4M3 blocks keep W and quantise the normalised rows.
+            auto fold = [&](std::vector<uint16_t> &packed, size_t K, float const *gain) {
+                if (e4m3) return;
+                for (size_t i = 0; i < packed.size(); ++i)
+                    packed[i] = bf16_bits(bf16_value(packed[i]) * gain[i % K]);
+            };
             tmp.assign(3 * D * D, 0);
             transpose_into(tmp.data(), w.w_qkv[l], D, 3 * D);
+            fold(tmp, D, w.attn_norm[l]);
             place(o_l[l * 6 + 0], tmp, e4m3 ? e4m3_scale(w.w_qkv[l], D * 3 * D) : 0.0);
             tmp.assign(D * D, 0);
             transpose_into(tmp.data(), w.w_o[l], D, D);
@@ -266,6 +283,7 @@ extern "C" void ube_model_init(ube_model_init_t *a) {
                     tmp[gate_up_row(col, false) * D + k] = w.w_gate[l][k * F + col];
                     tmp[gate_up_row(col, true) * D + k] = w.w_up[l][k * F + col];
                 }
+            fold(tmp, D, w.mlp_norm[l]);
             if (e4m3) {
                 const double sg = e4m3_scale(w.w_gate[l], D * F), su = e4m3_scale(w.w_up[l], D * F);
                 uint8_t *dst = (uint8_t *)(hb + o_l[l * 6 + 2]);
@@ -468,7 +486,7 @@ void make_tiles(Plan &p) {
 // Device regions of one call.
 struct Layout {
     size_t Tpad = 0;
-    size_t out, cu, src, tiles, media, input, x, h, a, qk, vt, o, xf, s, pos, patches, q8, qs, total;
+    size_t out, cu, src, tiles, media, input, x, h, a, qk, vt, o, xf, s, pos, patches, q8, qs, ss, total;
 };
 
 Layout carve(ube_geometry_t const &g, Plan const &p, bool media, size_t input_bytes, bool e4m3) {
@@ -499,6 +517,7 @@ Layout carve(ube_geometry_t const &g, Plan const &p, bool media, size_t input_by
     L.patches = take(media ? L.Tpad * 768 * 2 : 0);
     L.q8 = take(e4m3 ? L.Tpad * std::max(D, F) : 0);  // E4M3 GEMM input rows
     L.qs = take(e4m3 ? L.Tpad * 4 : 0);               // their per-row scales
+    L.ss = take(L.Tpad * kSsParts * 4);               // partial sums of squares of x
     L.total = total;
     return L;
 }
@@ -613,6 +632,7 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
     uint16_t *vt = (uint16_t *)(db + L.vt), *o = (uint16_t *)(db + L.o), *xf = (uint16_t *)(db + L.xf);
     float *s = (float *)(db + L.s);
     int16_t *pos = (int16_t *)(db + L.pos);
+    float *ssq = (float *)(db + L.ss);
     const int T = (int)p.T, ldvt = (int)L.Tpad;
 
     if (T > 0) {
@@ -621,8 +641,7 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
         // ---- frontend
         if (!media) {
             timed(ube_kernel_gather_k, st, [&] {
-                return launch_gather_text(input, src, cu, tiles, ntiles, m->embed, m->layers[0].g1, x, h, pos, D, eps,
-                                          st);
+                return launch_gather_text(input, src, cu, tiles, ntiles, m->embed, x, h, ssq, pos, D, st);
             });
         } else {
             uint16_t *patches = (uint16_t *)(db + L.patches);
@@ -633,9 +652,8 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
             GemmArgs ga{};
             ga.w = m->patch_t, ga.x = patches, ga.M = T, ga.N = D, ga.K = 768;
             ga.out_f32 = x, ga.ld_f32 = D, ga.scale = 1.0f / 255.0f;
+            ga.out_bf16 = h, ga.ld_out = D, ga.ss_out = ssq;
             timed(ube_kernel_gemm_patch_k, st, [&] { return launch_gemm(kEpiPatch, ga, st); });
-            if (!m->e4m3)
-                timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm(x, m->layers[0].g1, h, T, D, eps, st); });
         }
         if (r.trace) UBE_HIP(hipMemcpyAsync(r.trace, x, (size_t)T * D * 4, hipMemcpyDeviceToDevice, st));
         // ---- blocks
@@ -660,11 +678,22 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
         auto quantize = [&](const uint16_t *rows, int width) {
             timed(ube_kernel_quantize_k, st, [&] { return launch_quantize_rows(rows, q8, qs, T, width, st); });
         };
+        // bf16: the normalisation of the rows a projection reads is folded into it
+        // (x's bf16 copy h in, gain in the weights, 1/rms from the partial sums)
+        auto folded_norm = [&](GemmArgs &ga) {
+            // producers of x (residual and patch GEMMs, N = D) write one partial per
+            // 256 features from the 256-wide kernel, else one per 64 (gather: part 0)
+            if (!m->e4m3) ga.ss_in = ssq, ga.ss_parts = D % 256 == 0 ? D / 256 : D / 64, ga.eps = eps;
+        };
+        auto residual_out = [&](GemmArgs &ga) {
+            if (!m->e4m3) ga.out_bf16 = h, ga.ld_out = D, ga.ss_out = ssq;
+        };
         for (size_t l = 0; l < g.depth; ++l) {
             auto const &Wl = m->layers[l];
-            if (l > 0 || m->e4m3) norm(Wl.g1);
+            if (m->e4m3) norm(Wl.g1);
             GemmArgs qa{};
             qa.w = Wl.wqkv, qa.x = h, qa.M = T, qa.N = 3 * D, qa.K = D;
+            folded_norm(qa);
             qa.out_bf16 = qk, qa.ld_out = 2 * D, qa.vt = vt, qa.ld_vt = ldvt, qa.pos = pos, qa.rope = m->rope;
             qa.D = D, qa.sec0 = m->sec0, qa.sec1 = m->sec1;
             project(ube_kernel_gemm_qkv_k, kEpiQkv, qa, Wl.s_qkv, 0.f);
@@ -674,14 +703,17 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
             if (m->e4m3) quantize(o, D);
             GemmArgs oa{};
             oa.w = Wl.wo, oa.x = o, oa.M = T, oa.N = D, oa.K = D, oa.out_f32 = x, oa.ld_f32 = D;
+            residual_out(oa);
             project(ube_kernel_gemm_out_k, kEpiResid, oa, Wl.s_o, 0.f);
-            norm(Wl.g2);
+            if (m->e4m3) norm(Wl.g2);
             GemmArgs ua{};
             ua.w = Wl.wgu, ua.x = h, ua.M = T, ua.N = 2 * F, ua.K = D, ua.out_bf16 = act, ua.ld_out = F;
+            folded_norm(ua);
             project(ube_kernel_gemm_gate_up_k, kEpiSwiglu, ua, Wl.s_gate, Wl.s_up);
             if (m->e4m3) quantize(act, F);
             GemmArgs da{};
             da.w = Wl.wd, da.x = act, da.M = T, da.N = D, da.K = F, da.out_f32 = x, da.ld_f32 = D;
+            residual_out(da);
             project(ube_kernel_gemm_down_k, kEpiResid, da, Wl.s_down, 0.f);
             if (r.trace)
                 UBE_HIP(hipMemcpyAsync(r.trace + (l + 1) * (size_t)T * D, x, (size_t)T * D * 4,

@@ -12,6 +12,8 @@ namespace ube {
 constexpr int kRowPad = 256;
 // Tokens per work tile of the gather, patchify and attention kernels.
 constexpr int kTileTokens = 256;
+// Partial sums of squares kept per token row (one per 64 features; D <= 1024).
+constexpr int kSsParts = 16;
 
 enum Epilogue : int {
     kEpiStore = 0,   // C = bf16(acc)                                   [M x N], ld
@@ -39,6 +41,12 @@ struct GemmArgs {
     const float *x_scale; // E4M3: per-token activation scale [M_alloc]
     float w_scale;        // E4M3: weight tensor scale (gate tensor for SwiGLU)
     float w_scale2;       // E4M3: up tensor scale (SwiGLU)
+    float *ss_out;        // residual / patch: partial sums of squares of the new x [M_alloc x kSsParts], one
+                          // per 256 features (N % 256 == 0 kernel) or per 64 (otherwise), and x's bf16 copy
+                          // into out_bf16 (ld_out), when not NULL
+    const float *ss_in;   // QKV / gate-up: scale rows by 1/sqrt(sum(ss_in[m][0..ss_parts)) / K + eps)
+    int ss_parts;
+    float eps;
 };
 
 hipError_t launch_gemm(int epilogue, const GemmArgs &args, hipStream_t stream);
@@ -46,10 +54,11 @@ hipError_t launch_gemm(int epilogue, const GemmArgs &args, hipStream_t stream);
 // the accumulator is multiplied by x_scale[token] * w_scale before the epilogue.
 hipError_t launch_gemm_e4m3(int epilogue, const GemmArgs &args, hipStream_t stream);
 
-// Byte gather + RMSNorm (layer-0 attention norm): tiles are (item, first token).
+// Byte gather: x (fp32), its bf16 copy xb, the row's sum of squares (part 0 of
+// kSsParts; the rest 0) and text positions. Tiles are (item, first token).
 hipError_t launch_gather_text(const uint8_t *data, const int64_t *src, const int *cu, const int2 *tiles,
-                              int ntiles, const uint16_t *embed, const float *gain, float *x, uint16_t *h,
-                              int16_t *pos, int D, float eps, hipStream_t stream);
+                              int ntiles, const uint16_t *embed, float *x, uint16_t *xb, float *ss, int16_t *pos,
+                              int D, hipStream_t stream);
 
 // Patch rows (bf16 [T x 768], values 0..255) and rotary coordinates.
 struct MediaItem {

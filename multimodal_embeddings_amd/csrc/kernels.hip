@@ -156,24 +156,28 @@ __device__ __forceinline__ void norm_store(float (&v)[C][V], const float *gain, 
 template <int V, int C>
 __global__ __launch_bounds__(256) void k_gather_text(const uint8_t *__restrict__ data, const int64_t *__restrict__ src,
                                                      const int *__restrict__ cu, const int2 *__restrict__ tiles,
-                                                     const uint16_t *__restrict__ embed,
-                                                     const float *__restrict__ gain, float *__restrict__ x,
-                                                     uint16_t *__restrict__ h, int16_t *__restrict__ pos, int D,
-                                                     float eps) {
+                                                     const uint16_t *__restrict__ embed, float *__restrict__ x,
+                                                     uint16_t *__restrict__ xb, float *__restrict__ ss,
+                                                     int16_t *__restrict__ pos, int D) {
     const int2 tile = tiles[blockIdx.x];
     const int item = tile.x, start = cu[item], end = min(tile.y + kTileTokens, cu[item + 1]);
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     for (int t = tile.y + wave; t < end; t += 4) {
         const int local = t - start;
         const uint32_t byte = data[src[item] + local];
-        float v[C][V];
+        float v[V];
+        float sq = 0.f;
 #pragma unroll
         for (int c = 0; c < C; ++c) {
             const int f = c * 64 * V + lane * V;
-            RowIO<V>::load_bf16(embed + (size_t)byte * D + f, v[c]);
-            RowIO<V>::store_f32(x + (size_t)t * D + f, v[c]);
+            RowIO<V>::load_bf16(embed + (size_t)byte * D + f, v);
+            RowIO<V>::store_f32(x + (size_t)t * D + f, v);
+            RowIO<V>::store_bf16(xb + (size_t)t * D + f, v);  // exact: embedding rows are bf16
+#pragma unroll
+            for (int i = 0; i < V; ++i) sq += v[i] * v[i];
         }
-        norm_store<V, C>(v, gain, h + (size_t)t * D, D, eps, lane);
+        sq = wave_sum(sq);
+        if (lane < kSsParts) ss[(size_t)t * kSsParts + lane] = lane == 0 ? sq : 0.f;
         if (lane == 0) *(u32x2 *)(pos + (size_t)t * 4) = u32x2{(uint32_t)(local & 0xffff), 0u};
     }
 }
@@ -347,11 +351,11 @@ __global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restric
     } while (0)
 
 hipError_t launch_gather_text(const uint8_t *data, const int64_t *src, const int *cu, const int2 *tiles,
-                              int ntiles, const uint16_t *embed, const float *gain, float *x, uint16_t *h,
-                              int16_t *pos, int D, float eps, hipStream_t stream) {
+                              int ntiles, const uint16_t *embed, float *x, uint16_t *xb, float *ss, int16_t *pos,
+                              int D, hipStream_t stream) {
     if (ntiles == 0) return hipSuccess;
-    UBE_ROW_DISPATCH(D, (k_gather_text<V, C><<<ntiles, 256, 0, stream>>>(data, src, cu, tiles, embed, gain, x, h,
-                                                                           pos, D, eps)));
+    UBE_ROW_DISPATCH(D, (k_gather_text<V, C><<<ntiles, 256, 0, stream>>>(data, src, cu, tiles, embed, x, xb, ss, pos,
+                                                                           D)));
     return hipGetLastError();
 }
 
@@ -457,7 +461,17 @@ hipError_t launch_patchify(const uint8_t *pixels, const MediaItem *items, const 
 
 template <int EPI, int TM, int TN>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x16 (&acc)[TN][TM], int mw, int nw, int l32,
-                                              int hh);
+                                              int hh, const float (&inv)[TM]);
+
+// 1/rms of the folded RMSNorm for token m (1 when the projection reads plain rows):
+// the partial sums of squares the row's producer wrote, summed in a fixed order.
+__device__ __forceinline__ float folded_inv_rms(const GemmArgs &a, int m) {
+    if (!a.ss_in) return 1.f;
+    const float *pp = a.ss_in + (size_t)m * kSsParts;
+    float ss = 0.f;
+    for (int i = 0; i < a.ss_parts; ++i) ss += pp[i];
+    return 1.0f / sqrtf(ss / (float)a.K + a.eps);
+}
 
 template <int BM, int BN, int EPI>
 __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
@@ -536,19 +550,33 @@ __global__ __launch_bounds__(256) void k_gemm(GemmArgs a) {
         __syncthreads();
     }
 
-    gemm_epilogue<EPI, TM, TN>(a, acc, m0 + wm * WM, n0 + wn * WN, l32, hh);
+    float inv[TM];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+        inv[tm] = (EPI == kEpiQkv || EPI == kEpiSwiglu) ? folded_inv_rms(a, m0 + wm * WM + tm * 32 + l32) : 1.f;
+    gemm_epilogue<EPI, TM, TN>(a, acc, m0 + wm * WM, n0 + wn * WN, l32, hh, inv);
 }
 
 // Epilogue of one wave's (TN x TM) grid of 32 x 32 accumulator tiles. The wave's
-// features start at nw, its tokens at mw; accumulator register 4i + j of tile
-// (tn, tm) is feature nw + 32 tn + 8 i + 4 (lane / 32) + j, token mw + 32 tm + lane % 32.
+// features start at nw (a multiple of 64; the wave covers 64 of them), its tokens
+// at mw; accumulator register 4i + j of tile (tn, tm) is feature
+// nw + 32 tn + 8 i + 4 (lane / 32) + j, token mw + 32 tm + lane % 32.
+//
+// Folded RMSNorm: a consumer of normalised rows (QKV, gate/up) reads x's bf16 copy
+// with the gain already in its weights, and scales its accumulator by 1/rms(x),
+// rms from the partial sums of squares the row's producer wrote (one per 64
+// features, summed here in a fixed order).
 template <int EPI, int TM, int TN>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x16 (&acc)[TN][TM], int mw, int nw, int l32,
-                                              int hh) {
+                                              int hh, const float (&inv)[TM]) {
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) {
         const int m = mw + tm * 32 + l32;
         if (m >= a.M) continue;
+        if constexpr (EPI == kEpiQkv || EPI == kEpiSwiglu) {
+#pragma unroll
+            for (int tn = 0; tn < TN; ++tn) acc[tn][tm] *= inv[tm];
+        }
         if constexpr (EPI == kEpiSwiglu) {
 #pragma unroll
             for (int p = 0; p < TN / 2; ++p) {
@@ -566,6 +594,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x16 (&acc)[T
                 }
             }
         } else {
+            float ssp = 0.f;  // sum of squares of this wave's 64 output features (residual / patch)
 #pragma unroll
             for (int tn = 0; tn < TN; ++tn) {
                 const int nbase = nw + tn * 32;
@@ -576,13 +605,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x16 (&acc)[T
                                   acc[tn][tm][i * 4 + 3]};
                     if constexpr (EPI == kEpiStore) {
                         *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
-                    } else if constexpr (EPI == kEpiResid) {
+                    } else if constexpr (EPI == kEpiResid || EPI == kEpiPatch) {
                         f32x4 *px = (f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n);
-                        f32x4 xv = *px;
-                        *px = f32x4{xv.x + o[0], xv.y + o[1], xv.z + o[2], xv.w + o[3]};
-                    } else if constexpr (EPI == kEpiPatch) {
-                        *(f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n) =
-                            f32x4{o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale};
+                        f32x4 xv;
+                        if constexpr (EPI == kEpiResid) {
+                            xv = *px;
+                            xv = f32x4{xv.x + o[0], xv.y + o[1], xv.z + o[2], xv.w + o[3]};
+                        } else {
+                            xv = f32x4{o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale};
+                        }
+                        *px = xv;
+                        if (a.ss_out) {
+                            ssp += xv.x * xv.x + xv.y * xv.y + xv.z * xv.z + xv.w * xv.w;
+                            *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n) = u32x2{pack2(xv.x, xv.y), pack2(xv.z, xv.w)};
+                        }
                     } else if constexpr (EPI == kEpiQkv) {
                         if (nbase < 2 * a.D) {
                             // rotary: pairs (e, e+1) and (e+2, e+3), e = n % 64 even
@@ -609,6 +645,12 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x16 (&acc)[T
                     }
                 }
             }
+            if constexpr (EPI == kEpiResid || EPI == kEpiPatch) {
+                if (a.ss_out) {
+                    ssp += __shfl_xor(ssp, 32, 64);  // lanes l and l ^ 32 hold the same token
+                    if (hh == 0) a.ss_out[(size_t)m * kSsParts + (nw >> 6)] = ssp;
+                }
+            }
         }
     }
 }
@@ -627,6 +669,120 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, void *lds_base) {
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+
+// Epilogue of the 256 x 256 kernel, staged through LDS in four slices of 64
+// tokens: LDS row r = 32 wm + l32 holds token m0 + 128 wm + 32 tm + l32 as 256
+// fp32 values (rows padded to 260 floats: the 16-byte writes down a column hit
+// distinct banks). Every global access of a wave instruction then covers whole
+// row segments: one 1 KB fp32 row (residual, patch), one 512 B bf16 row (q, k,
+// plain store), two 256 B rows (SwiGLU output) or 16-byte token runs of
+// feature-major v.
+template <int EPI>
+__device__ __forceinline__ void gemm256_epilogue(const GemmArgs &a, f32x16 (&acc)[2][4], float *lds, int m0, int n0,
+                                                 int wm, int wn, int l32, int hh, int tid, const float (&inv)[4],
+                                                 const u32x2 (&pw)[4]) {
+    constexpr int LD = 260;
+    const int wave = tid >> 6, lane = tid & 63;
+    auto token = [&](int r, int tm) { return m0 + (r >> 5) * 128 + tm * 32 + (r & 31); };
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm) {
+        // ---- registers -> LDS (row r = 32 wm + l32)
+        float *row = lds + (wm * 32 + l32) * LD;
+        if constexpr (EPI == kEpiSwiglu) {
+            // gate (tn 0) and up (tn 1) of 32 outputs: cols 32 wn + 8 i + 4 hh + j
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float g = acc[0][tm][i * 4 + j] * inv[tm], u = acc[1][tm][i * 4 + j] * inv[tm];
+                    o[j] = g / (1.0f + __expf(-g)) * u;
+                }
+                *(f32x4 *)(row + wn * 32 + i * 8 + hh * 4) = f32x4{o[0], o[1], o[2], o[3]};
+            }
+        } else {
+            const bool rotate = EPI == kEpiQkv && n0 < 2 * a.D;
+            const int p0 = (int)(int16_t)(pw[tm].x & 0xffff), p1 = (int)(int16_t)(pw[tm].x >> 16),
+                      p2 = (int)(int16_t)(pw[tm].y & 0xffff);
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = wn * 64 + tn * 32 + i * 8 + hh * 4;  // column in the tile
+                    float o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[j] = acc[tn][tm][i * 4 + j] * inv[tm];
+                    if (rotate) {
+                        // rotary pairs (e, e+1), (e+2, e+3) with e = feature % 64 even
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const int pair = (((n0 + c) & 63) >> 1) + q;
+                            const int pv = pair < a.sec0 ? p0 : (pair < a.sec0 + a.sec1 ? p1 : p2);
+                            const float2 cs = a.rope[pv * 32 + pair];
+                            const float x0 = o[2 * q], x1 = o[2 * q + 1];
+                            o[2 * q] = x0 * cs.x - x1 * cs.y;
+                            o[2 * q + 1] = x0 * cs.y + x1 * cs.x;
+                        }
+                    }
+                    *(f32x4 *)(row + c) = f32x4{o[0], o[1], o[2], o[3]};
+                }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+        // ---- LDS -> global, wave w handles LDS rows 8w .. 8w + 7
+        if constexpr (EPI == kEpiSwiglu) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int r = wave * 8 + k * 2 + (lane >> 5), m = token(r, tm);
+                if (m < a.M) {
+                    const f32x4 v = *(const f32x4 *)(lds + r * LD + (lane & 31) * 4);
+                    *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 / 2 + (lane & 31) * 4) =
+                        u32x2{pack2(v.x, v.y), pack2(v.z, v.w)};
+                }
+            }
+        } else if (EPI == kEpiQkv && n0 >= 2 * a.D) {
+            // v, feature-major: thread -> feature f, 8-token runs
+            const int f = tid & 255, half = tid >> 8;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int r0 = half * 32 + k * 8, m = token(r0, tm);
+                float v[8];
+#pragma unroll
+                for (int t = 0; t < 8; ++t) v[t] = m + t < a.M ? lds[(r0 + t) * LD + f] : 0.f;
+                if (m < a.M)
+                    *(u32x4 *)(a.vt + (size_t)(n0 - 2 * a.D + f) * a.ld_vt + m) =
+                        u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int r = wave * 8 + k, m = token(r, tm);
+                if (m >= a.M) continue;
+                const int n = n0 + lane * 4;
+                f32x4 v = *(const f32x4 *)(lds + r * LD + lane * 4);
+                if constexpr (EPI == kEpiStore || EPI == kEpiQkv) {
+                    *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n) = u32x2{pack2(v.x, v.y), pack2(v.z, v.w)};
+                } else {
+                    f32x4 *px = (f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n);
+                    if constexpr (EPI == kEpiResid) {
+                        const f32x4 xo = *px;
+                        v = f32x4{xo.x + v.x, xo.y + v.y, xo.z + v.z, xo.w + v.w};
+                    } else {
+                        v = f32x4{v.x * a.scale, v.y * a.scale, v.z * a.scale, v.w * a.scale};
+                    }
+                    *px = v;
+                    if (a.ss_out) {
+                        *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n) = u32x2{pack2(v.x, v.y), pack2(v.z, v.w)};
+                        const float sq = wave_sum(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
+                        if (lane == 0) a.ss_out[(size_t)m * kSsParts + (n0 >> 8)] = sq;
+                    }
+                }
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+    }
 }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -648,6 +804,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
     const int m0 = mt * BM, n0 = nt * BN;
     const size_t row_bytes = (size_t)a.K * ES;
     const uint8_t *wb = (const uint8_t *)a.w, *xb = (const uint8_t *)a.x;
+
+    // per-token epilogue inputs, loaded before the K loop so their latency hides
+    // behind it (and only used after it): the partial sums of squares of the
+    // folded RMSNorm (up to 4 parts here; more are read in the epilogue) and the
+    // rotary coordinates
+    constexpr bool kNorm = EPI == kEpiQkv || EPI == kEpiSwiglu;
+    const bool ss_early = kNorm && a.ss_in && a.ss_parts <= 4;
+    f32x4 ssv[4] = {};
+    u32x2 pw[4] = {};
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm) {
+        const int m = m0 + wm * 128 + tm * 32 + l32;
+        if (ss_early) ssv[tm] = *(const f32x4 *)(a.ss_in + (size_t)m * kSsParts);
+        if (EPI == kEpiQkv) pw[tm] = *(const u32x2 *)(a.pos + (size_t)m * 4);
+    }
 
     // global source of this lane for load round r (0..3 weights, 4..7 activations):
     // chunk slot p = 512 r + 64 wave + lane of the operand tile, row p / 8, LDS chunk p % 8
@@ -770,7 +941,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
             }
         }
     }
-    gemm_epilogue<EPI, TM, TN>(a, acc, m0 + wm * WM, n0 + wn * WN, l32, hh);
+    float inv[4] = {1.f, 1.f, 1.f, 1.f};
+    if (kNorm && a.ss_in) {
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            if (ss_early) {
+                // fixed order: part 0, 1, 2, 3 (parts past ss_parts are skipped)
+                float ss = ssv[tm].x;
+                if (a.ss_parts > 1) ss += ssv[tm].y;
+                if (a.ss_parts > 2) ss += ssv[tm].z;
+                if (a.ss_parts > 3) ss += ssv[tm].w;
+                inv[tm] = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+            } else {
+                inv[tm] = folded_inv_rms(a, m0 + wm * 128 + tm * 32 + l32);
+            }
+        }
+    }
+    // residual and patch outputs (fp32 x read-modify-write plus its bf16 copy) go
+    // through LDS for row-contiguous accesses; the others store from registers
+    if constexpr (EPI == kEpiResid || EPI == kEpiPatch)
+        gemm256_epilogue<EPI>(a, acc, (float *)smem, m0, n0, wm, wn, l32, hh, tid, inv, pw);
+    else
+        gemm_epilogue<EPI, TM, TN>(a, acc, m0 + wm * WM, n0 + wn * WN, l32, hh, inv);
 }
 
 template <int BM, int BN>
