@@ -659,7 +659,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x16 (&acc)[T
 // of 128 x 64), two LDS stages of 64 KB filled by global_load_lds_dwordx4
 // (16 bytes per lane straight into LDS, no register staging). Lane i of a load
 // instruction lands at LDS chunk (base + i); the global chunk it fetches is the
-// logical chunk that the XOR swizzle assigns to that LDS slot.
+// logical chunk that the swizzle assigns to that LDS slot.
 __device__ __forceinline__ void lds_dma16(const void *gptr, void *lds_base) {
     __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
@@ -671,237 +671,120 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-// Epilogue of the 256 x 256 kernel, staged through LDS in four slices of 64
-// tokens: LDS row r = 32 wm + l32 holds token m0 + 128 wm + 32 tm + l32 as 256
-// fp32 values (rows padded to 260 floats: the 16-byte writes down a column hit
-// distinct banks). Every global access of a wave instruction then covers whole
-// row segments: one 1 KB fp32 row (residual, patch), one 512 B bf16 row (q, k,
-// plain store), two 256 B rows (SwiGLU output) or 16-byte token runs of
-// feature-major v.
-template <int EPI>
-__device__ __forceinline__ void gemm256_epilogue(const GemmArgs &a, f32x16 (&acc)[2][4], float *lds, int m0, int n0,
-                                                 int wm, int wn, int l32, int hh, int tid, const float (&inv)[4],
-                                                 const u32x2 (&pw)[4]) {
-    constexpr int LD = 260;
-    const int wave = tid >> 6, lane = tid & 63;
-    auto token = [&](int r, int tm) { return m0 + (r >> 5) * 128 + tm * 32 + (r & 31); };
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-        // ---- registers -> LDS (row r = 32 wm + l32)
-        float *row = lds + (wm * 32 + l32) * LD;
-        if constexpr (EPI == kEpiSwiglu) {
-            // gate (tn 0) and up (tn 1) of 32 outputs: cols 32 wn + 8 i + 4 hh + j
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float o[4];
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const float g = acc[0][tm][i * 4 + j] * inv[tm], u = acc[1][tm][i * 4 + j] * inv[tm];
-                    o[j] = g / (1.0f + __expf(-g)) * u;
-                }
-                *(f32x4 *)(row + wn * 32 + i * 8 + hh * 4) = f32x4{o[0], o[1], o[2], o[3]};
-            }
-        } else {
-            const bool rotate = EPI == kEpiQkv && n0 < 2 * a.D;
-            const int p0 = (int)(int16_t)(pw[tm].x & 0xffff), p1 = (int)(int16_t)(pw[tm].x >> 16),
-                      p2 = (int)(int16_t)(pw[tm].y & 0xffff);
-#pragma unroll
-            for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int c = wn * 64 + tn * 32 + i * 8 + hh * 4;  // column in the tile
-                    float o[4];
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) o[j] = acc[tn][tm][i * 4 + j] * inv[tm];
-                    if (rotate) {
-                        // rotary pairs (e, e+1), (e+2, e+3) with e = feature % 64 even
-#pragma unroll
-                        for (int q = 0; q < 2; ++q) {
-                            const int pair = (((n0 + c) & 63) >> 1) + q;
-                            const int pv = pair < a.sec0 ? p0 : (pair < a.sec0 + a.sec1 ? p1 : p2);
-                            const float2 cs = a.rope[pv * 32 + pair];
-                            const float x0 = o[2 * q], x1 = o[2 * q + 1];
-                            o[2 * q] = x0 * cs.x - x1 * cs.y;
-                            o[2 * q + 1] = x0 * cs.y + x1 * cs.x;
-                        }
-                    }
-                    *(f32x4 *)(row + c) = f32x4{o[0], o[1], o[2], o[3]};
-                }
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        lds_barrier();
-        // ---- LDS -> global, wave w handles LDS rows 8w .. 8w + 7
-        if constexpr (EPI == kEpiSwiglu) {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int r = wave * 8 + k * 2 + (lane >> 5), m = token(r, tm);
-                if (m < a.M) {
-                    const f32x4 v = *(const f32x4 *)(lds + r * LD + (lane & 31) * 4);
-                    *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 / 2 + (lane & 31) * 4) =
-                        u32x2{pack2(v.x, v.y), pack2(v.z, v.w)};
-                }
-            }
-        } else if (EPI == kEpiQkv && n0 >= 2 * a.D) {
-            // v, feature-major: thread -> feature f, 8-token runs
-            const int f = tid & 255, half = tid >> 8;
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int r0 = half * 32 + k * 8, m = token(r0, tm);
-                float v[8];
-#pragma unroll
-                for (int t = 0; t < 8; ++t) v[t] = m + t < a.M ? lds[(r0 + t) * LD + f] : 0.f;
-                if (m < a.M)
-                    *(u32x4 *)(a.vt + (size_t)(n0 - 2 * a.D + f) * a.ld_vt + m) =
-                        u32x4{pack2(v[0], v[1]), pack2(v[2], v[3]), pack2(v[4], v[5]), pack2(v[6], v[7])};
-            }
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; ++k) {
-                const int r = wave * 8 + k, m = token(r, tm);
-                if (m >= a.M) continue;
-                const int n = n0 + lane * 4;
-                f32x4 v = *(const f32x4 *)(lds + r * LD + lane * 4);
-                if constexpr (EPI == kEpiStore || EPI == kEpiQkv) {
-                    *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n) = u32x2{pack2(v.x, v.y), pack2(v.z, v.w)};
-                } else {
-                    f32x4 *px = (f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n);
-                    if constexpr (EPI == kEpiResid) {
-                        const f32x4 xo = *px;
-                        v = f32x4{xo.x + v.x, xo.y + v.y, xo.z + v.z, xo.w + v.w};
-                    } else {
-                        v = f32x4{v.x * a.scale, v.y * a.scale, v.z * a.scale, v.w * a.scale};
-                    }
-                    *px = v;
-                    if (a.ss_out) {
-                        *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n) = u32x2{pack2(v.x, v.y), pack2(v.z, v.w)};
-                        const float sq = wave_sum(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
-                        if (lane == 0) a.ss_out[(size_t)m * kSsParts + (n0 >> 8)] = sq;
-                    }
-                }
-            }
-        }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        lds_barrier();
-    }
-}
+// Operand rows are 128 bytes (8 chunks of 16). gfx950's LDS has 64 banks (256
+// bytes per cycle) and serves a 16-byte read for 16 lanes at a time: lanes
+// reading rows r .. r+15 at the same logical chunk hit 16 distinct 16-byte bank
+// groups when the chunk is XOR-ed with (row / 2) % 8 (row parity picks the
+// 128-byte half of the 256-byte bank window).
+__device__ __forceinline__ int swz(int row, int ch) { return ch ^ ((row >> 1) & 7); }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-template <int EPI, bool FP8>
-__global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
-    // Both operand tiles have 128-byte LDS rows: 64 bf16 or 128 E4M3 values of K per stage.
-    constexpr int BM = 256, BN = 256, ES = FP8 ? 1 : 2, BK = 128 / ES;
-    constexpr int WM = 128, WN = 64, TM = WM / 32, TN = WN / 32;
-    constexpr int STAGE = (BM + BN) * 8;  // 16-byte chunks per stage
-    __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * STAGE];
+// LDS of the 256 x 256 kernel (bytes): the two operand stages [0, 128 KB) during
+// the K loop; afterwards the epilogue's staging area [0, kStageBytes) and, past
+// it, one float per tile token (row scale of the feature-major v tiles).
+constexpr int kQkPitch = 528;                 // bf16 rows of 256 values + 16 B
+constexpr int kGluPitch = 272;                // bf16 rows of 128 values + 16 B
+constexpr int kResPitch = 1040;               // fp32 rows of 256 values + 16 B
+constexpr int kResSlice = 64 * kResPitch;     // 64 tokens
+constexpr int kStageBytes = 256 * kQkPitch;   // 135,168 >= 2 * kResSlice
+constexpr int kSmemBytes = kStageBytes + 256 * 4;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave & 1, wn = wave >> 1;
-    const int l32 = lane & 31, hh = lane >> 5;
-    const int NT = a.N / BN;
-    const int logical = xcd_remap(blockIdx.x, gridDim.x);
-    const int mt = logical / NT, nt = logical % NT;
-    const int m0 = mt * BM, n0 = nt * BN;
+// K loop of one tile. SWAP = false: MFMA A operand = weight rows, B = token
+// rows, so lane (l32, hh) holds features 8 i + 4 hh + j of token l32 in register
+// 4 i + j. SWAP = true (feature-major v tiles): A = token rows, so the lane holds
+// tokens 8 i + 4 hh + j of feature l32.
+template <bool FP8, bool SWAP>
+__device__ __forceinline__ void gemm256_kloop(const GemmArgs &a, u32x4 *smem, f32x16 (&acc)[2][4], int m0, int n0,
+                                              int wave, int lane) {
+    constexpr int BM = 256, BN = 256, ES = FP8 ? 1 : 2, BK = 128 / ES;
+    constexpr int STAGE = (BM + BN) * 8;  // 16-byte chunks per stage
+    const int wm = wave & 1, wn = wave >> 1, l32 = lane & 31, hh = lane >> 5;
     const size_t row_bytes = (size_t)a.K * ES;
     const uint8_t *wb = (const uint8_t *)a.w, *xb = (const uint8_t *)a.x;
-
-    // per-token epilogue inputs, loaded before the K loop so their latency hides
-    // behind it (and only used after it): the partial sums of squares of the
-    // folded RMSNorm (up to 4 parts here; more are read in the epilogue) and the
-    // rotary coordinates
-    constexpr bool kNorm = EPI == kEpiQkv || EPI == kEpiSwiglu;
-    const bool ss_early = kNorm && a.ss_in && a.ss_parts <= 4;
-    f32x4 ssv[4] = {};
-    u32x2 pw[4] = {};
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-        const int m = m0 + wm * 128 + tm * 32 + l32;
-        if (ss_early) ssv[tm] = *(const f32x4 *)(a.ss_in + (size_t)m * kSsParts);
-        if (EPI == kEpiQkv) pw[tm] = *(const u32x2 *)(a.pos + (size_t)m * 4);
-    }
-
-    // global source of this lane for load round r (0..3 weights, 4..7 activations):
-    // chunk slot p = 512 r + 64 wave + lane of the operand tile, row p / 8, LDS chunk p % 8
-    const int prow = (wave * 64 + lane) >> 3;
-    const int pch = lane & 7;
+    // load round r (0..3 weights, 4..7 activations): chunk slot 512 r + 64 wave + lane
+    // of the operand tile, row (64 r + slot / 8), LDS chunk slot % 8
+    const int prow = (wave * 64 + lane) >> 3, pch = lane & 7;
     auto issue = [&](int k0, int buf) {
         u32x4 *dst = smem + buf * STAGE;
         const size_t kb = (size_t)k0 * ES;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = r * 64 + prow;
-            const int ch = pch ^ (row & 7);
-            lds_dma16(wb + (size_t)(n0 + row) * row_bytes + kb + ch * 16, dst + r * 512 + wave * 64);
+            lds_dma16(wb + (size_t)(n0 + row) * row_bytes + kb + swz(row, pch) * 16, dst + r * 512 + wave * 64);
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = r * 64 + prow;
-            const int ch = pch ^ (row & 7);
-            lds_dma16(xb + (size_t)(m0 + row) * row_bytes + kb + ch * 16, dst + BN * 8 + r * 512 + wave * 64);
+            lds_dma16(xb + (size_t)(m0 + row) * row_bytes + kb + swz(row, pch) * 16,
+                      dst + BN * 8 + r * 512 + wave * 64);
         }
     };
-
-    f32x16 acc[TN][TM];
-#pragma unroll
-    for (int i = 0; i < TN; ++i)
-#pragma unroll
-        for (int j = 0; j < TM; ++j) acc[i][j] = f32x16{};
-
-    // One stage: wait for this wave's DMA of the stage (the next stage's 8 loads
-    // may stay in flight), barrier so every wave's DMA is visible, compute, then
-    // drain LDS reads and barrier again before the buffer is refilled. Plain
-    // s_barrier: a __syncthreads() fence would also wait for the next stage.
+    auto mfma = [&](const auto &w_op, const auto &x_op, f32x16 &c) {
+        if constexpr (FP8) {
+            // v_mfma_scale_f32_32x32x64_f8f6f4, both operands OCP E4M3 (format 0),
+            // unit E8M0 block scales (127)
+            if constexpr (SWAP)
+                c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(x_op, w_op, c, 0, 0, 0, 127, 0, 127);
+            else
+                c = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(w_op, x_op, c, 0, 0, 0, 127, 0, 127);
+        } else {
+            if constexpr (SWAP)
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x_op, w_op, c, 0, 0, 0);
+            else
+                c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(w_op, x_op, c, 0, 0, 0);
+        }
+    };
     auto compute = [&](const u32x4 *sW) {
         const u32x4 *sX = sW + BN * 8;
         if constexpr (!FP8) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const int ch = ks * 2 + hh;
-                bf16x8 af[TN], bfr[TM];
+                const int ch = ks * 2 + hh;  // lane half hh supplies 8 consecutive k
+                bf16x8 af[2], bfr[4];
 #pragma unroll
-                for (int tn = 0; tn < TN; ++tn) {
-                    const int row = wn * WN + tn * 32 + l32;
-                    af[tn] = __builtin_bit_cast(bf16x8, sW[row * 8 + (ch ^ (row & 7))]);
+                for (int tn = 0; tn < 2; ++tn) {
+                    const int row = wn * 64 + tn * 32 + l32;
+                    af[tn] = __builtin_bit_cast(bf16x8, sW[row * 8 + swz(row, ch)]);
                 }
 #pragma unroll
-                for (int tm = 0; tm < TM; ++tm) {
-                    const int row = wm * WM + tm * 32 + l32;
-                    bfr[tm] = __builtin_bit_cast(bf16x8, sX[row * 8 + (ch ^ (row & 7))]);
+                for (int tm = 0; tm < 4; ++tm) {
+                    const int row = wm * 128 + tm * 32 + l32;
+                    bfr[tm] = __builtin_bit_cast(bf16x8, sX[row * 8 + swz(row, ch)]);
                 }
 #pragma unroll
-                for (int tn = 0; tn < TN; ++tn)
+                for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
-                    for (int tm = 0; tm < TM; ++tm)
-                        acc[tn][tm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[tn], bfr[tm], acc[tn][tm], 0, 0, 0);
+                    for (int tm = 0; tm < 4; ++tm) mfma(af[tn], bfr[tm], acc[tn][tm]);
             }
         } else {
-            // v_mfma_scale_f32_32x32x64_f8f6f4, both operands OCP E4M3 (format 0), unit
-            // E8M0 block scales (127): lane half hh supplies 32 consecutive k bytes.
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks) {
-                const int ch = ks * 4 + hh * 2;
-                i32x8 af[TN], bfr[TM];
+                const int ch = ks * 4 + hh * 2;  // lane half hh supplies 32 consecutive k bytes
+                i32x8 af[2], bfr[4];
 #pragma unroll
-                for (int tn = 0; tn < TN; ++tn) {
-                    const int row = wn * WN + tn * 32 + l32;
-                    const u32x4 lo = sW[row * 8 + (ch ^ (row & 7))], hi = sW[row * 8 + ((ch + 1) ^ (row & 7))];
+                for (int tn = 0; tn < 2; ++tn) {
+                    const int row = wn * 64 + tn * 32 + l32;
+                    const u32x4 lo = sW[row * 8 + swz(row, ch)], hi = sW[row * 8 + swz(row, ch + 1)];
                     af[tn] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 }
 #pragma unroll
-                for (int tm = 0; tm < TM; ++tm) {
-                    const int row = wm * WM + tm * 32 + l32;
-                    const u32x4 lo = sX[row * 8 + (ch ^ (row & 7))], hi = sX[row * 8 + ((ch + 1) ^ (row & 7))];
+                for (int tm = 0; tm < 4; ++tm) {
+                    const int row = wm * 128 + tm * 32 + l32;
+                    const u32x4 lo = sX[row * 8 + swz(row, ch)], hi = sX[row * 8 + swz(row, ch + 1)];
                     bfr[tm] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
                 }
 #pragma unroll
-                for (int tn = 0; tn < TN; ++tn)
+                for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
-                    for (int tm = 0; tm < TM; ++tm)
-                        acc[tn][tm] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[tn], bfr[tm], acc[tn][tm], 0, 0,
-                                                                                      0, 127, 0, 127);
+                    for (int tm = 0; tm < 4; ++tm) mfma(af[tn], bfr[tm], acc[tn][tm]);
             }
         }
     };
+    // One stage: wait for this wave's DMA of the stage (the next stage's 8 loads
+    // may stay in flight), barrier so every wave's DMA is visible, compute, then
+    // drain LDS reads and barrier again before the buffer is refilled. Plain
+    // s_barrier: a __syncthreads() fence would also wait for the next stage.
     const int nk = a.K / BK;
     issue(0, 0);
     for (int kt = 0; kt < nk; kt += 2) {
@@ -928,41 +811,260 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
             lds_barrier();
         }
     }
-    if constexpr (FP8) {
-        // dequantise: per-token activation scale times the weight tensor's scale
-        // (the SwiGLU matrix holds two tensors: gate blocks even, up blocks odd)
+}
+
+// Rotary on four consecutive features (pairs (e, e+1), (e+2, e+3), e = feature
+// % 64 even) of one token: cs holds the two (cos, sin) entries.
+__device__ __forceinline__ void rotate4(float (&o)[4], const float2 (&cs)[2]) {
 #pragma unroll
-        for (int tm = 0; tm < TM; ++tm) {
-            const float sa = a.x_scale[m0 + wm * WM + tm * 32 + l32];
-#pragma unroll
-            for (int tn = 0; tn < TN; ++tn) {
-                const float sw = (EPI == kEpiSwiglu && (tn & 1)) ? a.w_scale2 : a.w_scale;
-                acc[tn][tm] *= sa * sw;
-            }
-        }
+    for (int q = 0; q < 2; ++q) {
+        const float x0 = o[2 * q], x1 = o[2 * q + 1];
+        o[2 * q] = x0 * cs[q].x - x1 * cs[q].y;
+        o[2 * q + 1] = x0 * cs[q].y + x1 * cs[q].x;
     }
-    float inv[4] = {1.f, 1.f, 1.f, 1.f};
-    if (kNorm && a.ss_in) {
+}
+
+// Epilogues of the 256 x 256 kernel, all staged through LDS so that every global
+// access of a wave instruction covers whole rows with 16 bytes per lane: 512 B
+// bf16 rows (q, k, plain store, feature-major v), 256 B rows (SwiGLU output) or
+// 1 KB fp32 rows (residual and patch, with the bf16 copy and the row's sum of
+// squares over the tile's 256 features).
+template <int EPI, bool FP8>
+__global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
+    __shared__ __attribute__((aligned(1024))) u32x4 smem[kSmemBytes / 16];
+    uint8_t *L = (uint8_t *)smem;
+    float *row_scale = (float *)(L + kStageBytes);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave & 1, wn = wave >> 1;
+    const int l32 = lane & 31, hh = lane >> 5;
+    const int NT = a.N / 256;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int m0 = (logical / NT) * 256, n0 = (logical % NT) * 256;
+    const bool vtile = EPI == kEpiQkv && n0 >= 2 * a.D;
+
+    // per-token epilogue inputs, loaded before the K loop so their latency hides
+    // behind it (and only used after it): the partial sums of squares of the
+    // folded RMSNorm (up to 4 parts here; more are read in the epilogue) and the
+    // rotary coordinates
+    constexpr bool kNorm = EPI == kEpiQkv || EPI == kEpiSwiglu;
+    const bool ss_early = kNorm && a.ss_in && a.ss_parts <= 4;
+    f32x4 ssv[4] = {};
+    u32x2 pw[4] = {};
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) {
+    for (int tm = 0; tm < 4; ++tm) {
+        const int m = m0 + wm * 128 + tm * 32 + l32;
+        if (ss_early) ssv[tm] = *(const f32x4 *)(a.ss_in + (size_t)m * kSsParts);
+        if (EPI == kEpiQkv) pw[tm] = *(const u32x2 *)(a.pos + (size_t)m * 4);
+    }
+
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    if (vtile)
+        gemm256_kloop<FP8, true>(a, smem, acc, m0, n0, wave, lane);
+    else
+        gemm256_kloop<FP8, false>(a, smem, acc, m0, n0, wave, lane);
+
+    // per-token row factor of lane token (m0 + 128 wm + 32 tm + l32): folded
+    // RMSNorm 1/rms (fixed summation order: part 0, 1, 2, ...) times the E4M3
+    // activation scale
+    float fac[4] = {1.f, 1.f, 1.f, 1.f};
+#pragma unroll
+    for (int tm = 0; tm < 4; ++tm) {
+        const int m = m0 + wm * 128 + tm * 32 + l32;
+        if (kNorm && a.ss_in) {
             if (ss_early) {
-                // fixed order: part 0, 1, 2, 3 (parts past ss_parts are skipped)
                 float ss = ssv[tm].x;
                 if (a.ss_parts > 1) ss += ssv[tm].y;
                 if (a.ss_parts > 2) ss += ssv[tm].z;
                 if (a.ss_parts > 3) ss += ssv[tm].w;
-                inv[tm] = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+                fac[tm] = 1.0f / sqrtf(ss / (float)a.K + a.eps);
             } else {
-                inv[tm] = folded_inv_rms(a, m0 + wm * 128 + tm * 32 + l32);
+                fac[tm] = folded_inv_rms(a, m);
+            }
+        }
+        if constexpr (FP8) fac[tm] *= a.x_scale[m];
+    }
+
+    if constexpr (EPI == kEpiQkv) {
+        if (vtile) {
+            // ---- feature-major v: rows = 256 features of the tile, 512 B of tokens each
+            if (wn == 0 && hh == 0) {
+#pragma unroll
+                for (int tm = 0; tm < 4; ++tm) row_scale[wm * 128 + tm * 32 + l32] = fac[tm];
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            lds_barrier();
+            const float wsc = FP8 ? a.w_scale : 1.0f;
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn) {
+                    const int f = wn * 64 + tn * 32 + l32;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int t = wm * 128 + tm * 32 + i * 8 + hh * 4;
+                        const f32x4 s = *(const f32x4 *)(row_scale + t);
+                        const float v[4] = {acc[tn][tm][i * 4], acc[tn][tm][i * 4 + 1], acc[tn][tm][i * 4 + 2],
+                                            acc[tn][tm][i * 4 + 3]};
+                        *(u32x2 *)(L + f * kQkPitch + t * 2) =
+                            u32x2{pack2(v[0] * s.x * wsc, v[1] * s.y * wsc), pack2(v[2] * s.z * wsc, v[3] * s.w * wsc)};
+                    }
+                }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            lds_barrier();
+            // tokens past M are written as zeros (masked keys must hold finite values)
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+                const int f = it * 16 + wave * 2 + hh, t0 = l32 * 8;
+                u32x4 v = *(const u32x4 *)(L + f * kQkPitch + t0 * 2);
+                const int valid = a.M - (m0 + t0);
+                if (valid < 8) {
+                    uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t lo = 2 * e < valid ? 0xffffu : 0u, hi = 2 * e + 1 < valid ? 0xffff0000u : 0u;
+                        w4[e] &= lo | hi;
+                    }
+                    v = u32x4{w4[0], w4[1], w4[2], w4[3]};
+                }
+                *(u32x4 *)(a.vt + (size_t)(n0 - 2 * a.D + f) * a.ld_vt + m0 + t0) = v;
+            }
+            return;
+        }
+    }
+
+    if constexpr (EPI == kEpiStore || EPI == kEpiQkv) {
+        // ---- token-major bf16 rows of 256 features (q and k rotated)
+        const float wsc = FP8 ? a.w_scale : 1.0f;
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            const int t = wm * 128 + tm * 32 + l32;
+            int p[3] = {0, 0, 0};
+            if constexpr (EPI == kEpiQkv) {
+                p[0] = (int)(int16_t)(pw[tm].x & 0xffff);
+                p[1] = (int)(int16_t)(pw[tm].x >> 16);
+                p[2] = (int)(int16_t)(pw[tm].y & 0xffff);
+            }
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int c = wn * 64 + tn * 32 + i * 8 + hh * 4;
+                    float o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[j] = acc[tn][tm][i * 4 + j] * fac[tm] * wsc;
+                    if constexpr (EPI == kEpiQkv) {
+                        float2 cs[2];
+#pragma unroll
+                        for (int q = 0; q < 2; ++q) {
+                            const int pair = ((c & 63) >> 1) + q;
+                            const int pv = pair < a.sec0 ? p[0] : (pair < a.sec0 + a.sec1 ? p[1] : p[2]);
+                            cs[q] = a.rope[pv * 32 + pair];
+                        }
+                        rotate4(o, cs);
+                    }
+                    *(u32x2 *)(L + t * kQkPitch + c * 2) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+                }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int t = it * 16 + wave * 2 + hh, m = m0 + t;
+            const u32x4 v = *(const u32x4 *)(L + t * kQkPitch + l32 * 16);
+            if (m < a.M) *(u32x4 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 + l32 * 8) = v;
+        }
+    } else if constexpr (EPI == kEpiSwiglu) {
+        // ---- gate (tn 0) and up (tn 1) of 32 outputs per wave: output column
+        // 32 wn + 8 i + 4 hh + j of the tile's 128; rows of 256 B
+        const float sg = FP8 ? a.w_scale : 1.0f, su = FP8 ? a.w_scale2 : 1.0f;
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            const int t = wm * 128 + tm * 32 + l32;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                float o[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const float g = acc[0][tm][i * 4 + j] * fac[tm] * sg, u = acc[1][tm][i * 4 + j] * fac[tm] * su;
+                    o[j] = g / (1.0f + __expf(-g)) * u;
+                }
+                *(u32x2 *)(L + t * kGluPitch + (wn * 32 + i * 8 + hh * 4) * 2) =
+                    u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int t = it * 32 + wave * 4 + (lane >> 4), m = m0 + t, ch = lane & 15;
+            const u32x4 v = *(const u32x4 *)(L + t * kGluPitch + ch * 16);
+            if (m < a.M) *(u32x4 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 / 2 + ch * 8) = v;
+        }
+    } else {
+        // ---- residual / patch: four slices of 64 tokens (slice s = tile tokens
+        // [64 s, 64 s + 64), held by the waves with wm = s / 2 at tm = 2 (s % 2) +
+        // 0, 1), double-buffered in LDS; wave w finishes rows 8 w .. 8 w + 7 of a
+        // slice: x (fp32, read one slice ahead) += acc, its bf16 copy, and the sum
+        // of squares of the row's 256 new values
+        const float wsc = FP8 ? a.w_scale : 1.0f;
+        f32x4 xin[2][8];
+        auto load_x = [&](int s, f32x4 (&dst)[8]) {
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int m = m0 + s * 64 + wave * 8 + k;
+                dst[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (EPI == kEpiResid && m < a.M)
+                    dst[k] = *(const f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n0 + lane * 4);
+            }
+        };
+        load_x(0, xin[0]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float *S = (float *)(L + (s & 1) * kResSlice);
+            if (wm == (s >> 1)) {
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int tm = 2 * (s & 1) + q, r = q * 32 + l32;
+#pragma unroll
+                    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int c = wn * 64 + tn * 32 + i * 8 + hh * 4;
+                            const float v[4] = {acc[tn][tm][i * 4], acc[tn][tm][i * 4 + 1], acc[tn][tm][i * 4 + 2],
+                                                acc[tn][tm][i * 4 + 3]};
+                            const float k = fac[tm] * wsc;
+                            *(f32x4 *)((uint8_t *)S + r * kResPitch + c * 4) = f32x4{v[0] * k, v[1] * k, v[2] * k, v[3] * k};
+                        }
+                }
+            }
+            if (s + 1 < 4) load_x(s + 1, xin[(s + 1) & 1]);
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            lds_barrier();
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+                const int r = wave * 8 + k, m = m0 + s * 64 + r;
+                if (m >= a.M) continue;
+                const f32x4 d = *(const f32x4 *)((const uint8_t *)S + r * kResPitch + lane * 16);
+                const f32x4 xo = xin[s & 1][k];
+                f32x4 v;
+                if constexpr (EPI == kEpiResid)
+                    v = f32x4{xo.x + d.x, xo.y + d.y, xo.z + d.z, xo.w + d.w};
+                else
+                    v = f32x4{d.x * a.scale, d.y * a.scale, d.z * a.scale, d.w * a.scale};
+                *(f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n0 + lane * 4) = v;
+                if (a.ss_out) {
+                    *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 + lane * 4) = u32x2{pack2(v.x, v.y), pack2(v.z, v.w)};
+                    const float sq = wave_sum(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
+                    if (lane == 0) a.ss_out[(size_t)m * kSsParts + (n0 >> 8)] = sq;
+                }
             }
         }
     }
-    // residual and patch outputs (fp32 x read-modify-write plus its bf16 copy) go
-    // through LDS for row-contiguous accesses; the others store from registers
-    if constexpr (EPI == kEpiResid || EPI == kEpiPatch)
-        gemm256_epilogue<EPI>(a, acc, (float *)smem, m0, n0, wm, wn, l32, hh, tid, inv, pw);
-    else
-        gemm_epilogue<EPI, TM, TN>(a, acc, m0 + wm * WM, n0 + wn * WN, l32, hh, inv);
 }
 
 template <int BM, int BN>
