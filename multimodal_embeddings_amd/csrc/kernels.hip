@@ -872,6 +872,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
     // RMSNorm 1/rms (fixed summation order: part 0, 1, 2, ...) times the E4M3
     // activation scale
     float fac[4] = {1.f, 1.f, 1.f, 1.f};
+    const float inv_k = 1.0f / (float)a.K;
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm) {
         const int m = m0 + wm * 128 + tm * 32 + l32;
@@ -881,7 +882,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
                 if (a.ss_parts > 1) ss += ssv[tm].y;
                 if (a.ss_parts > 2) ss += ssv[tm].z;
                 if (a.ss_parts > 3) ss += ssv[tm].w;
-                fac[tm] = 1.0f / sqrtf(ss / (float)a.K + a.eps);
+                fac[tm] = __builtin_amdgcn_rsqf(ss * inv_k + a.eps);
             } else {
                 fac[tm] = folded_inv_rms(a, m);
             }
@@ -908,10 +909,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
                     for (int i = 0; i < 4; ++i) {
                         const int t = wm * 128 + tm * 32 + i * 8 + hh * 4;
                         const f32x4 s = *(const f32x4 *)(row_scale + t);
-                        const float v[4] = {acc[tn][tm][i * 4], acc[tn][tm][i * 4 + 1], acc[tn][tm][i * 4 + 2],
-                                            acc[tn][tm][i * 4 + 3]};
-                        *(u32x2 *)(L + f * kQkPitch + t * 2) =
-                            u32x2{pack2(v[0] * s.x * wsc, v[1] * s.y * wsc), pack2(v[2] * s.z * wsc, v[3] * s.w * wsc)};
+                        f32x4 v = {acc[tn][tm][i * 4], acc[tn][tm][i * 4 + 1], acc[tn][tm][i * 4 + 2],
+                                   acc[tn][tm][i * 4 + 3]};
+                        v *= s;
+                        if constexpr (FP8) v *= wsc;
+                        *(u32x2 *)(L + f * kQkPitch + t * 2) = u32x2{pack2(v.x, v.y), pack2(v.z, v.w)};
                     }
                 }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -943,11 +945,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) {
             const int t = wm * 128 + tm * 32 + l32;
-            int p[3] = {0, 0, 0};
+            const float k = fac[tm] * wsc;
+            // rotary table row of each axis for this token, offset by the lane half's
+            // first pair (hh * 2): pair 4 i + 16 tn + q + 2 hh is then rb[axis][4 i + 16 tn + q]
+            const float2 *rb[3] = {a.rope, a.rope, a.rope};
             if constexpr (EPI == kEpiQkv) {
-                p[0] = (int)(int16_t)(pw[tm].x & 0xffff);
-                p[1] = (int)(int16_t)(pw[tm].x >> 16);
-                p[2] = (int)(int16_t)(pw[tm].y & 0xffff);
+                rb[0] = a.rope + (int)(int16_t)(pw[tm].x & 0xffff) * 32 + hh * 2;
+                rb[1] = a.rope + (int)(int16_t)(pw[tm].x >> 16) * 32 + hh * 2;
+                rb[2] = a.rope + (int)(int16_t)(pw[tm].y & 0xffff) * 32 + hh * 2;
             }
 #pragma unroll
             for (int tn = 0; tn < 2; ++tn)
@@ -956,14 +961,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
                     const int c = wn * 64 + tn * 32 + i * 8 + hh * 4;
                     float o[4];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) o[j] = acc[tn][tm][i * 4 + j] * fac[tm] * wsc;
+                    for (int j = 0; j < 4; ++j) o[j] = acc[tn][tm][i * 4 + j] * k;
                     if constexpr (EPI == kEpiQkv) {
                         float2 cs[2];
 #pragma unroll
                         for (int q = 0; q < 2; ++q) {
-                            const int pair = ((c & 63) >> 1) + q;
-                            const int pv = pair < a.sec0 ? p[0] : (pair < a.sec0 + a.sec1 ? p[1] : p[2]);
-                            cs[q] = a.rope[pv * 32 + pair];
+                            const int jp = tn * 16 + i * 4 + q, pair = jp + hh * 2;
+                            const float2 *b = pair < a.sec0 ? rb[0] : (pair < a.sec0 + a.sec1 ? rb[1] : rb[2]);
+                            cs[q] = b[jp];
                         }
                         rotate4(o, cs);
                     }
@@ -985,13 +990,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) {
             const int t = wm * 128 + tm * 32 + l32;
+            // g = ag kg, u = au ku: SiLU(g) u = ag au (kg ku) / (1 + 2^(ag (-kg log2 e)))
+            const float kg = fac[tm] * sg, ke = kg * -1.4426950408889634f, kgu = kg * fac[tm] * su;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float o[4];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const float g = acc[0][tm][i * 4 + j] * fac[tm] * sg, u = acc[1][tm][i * 4 + j] * fac[tm] * su;
-                    o[j] = g / (1.0f + __expf(-g)) * u;
+                    const float ag = acc[0][tm][i * 4 + j], au = acc[1][tm][i * 4 + j];
+                    const float e = __builtin_amdgcn_exp2f(ag * ke);
+                    o[j] = ag * au * kgu * __builtin_amdgcn_rcpf(1.0f + e);
                 }
                 *(u32x2 *)(L + t * kGluPitch + (wn * 32 + i * 8 + hh * 4) * 2) =
                     u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
@@ -1035,33 +1043,48 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
 #pragma unroll
                         for (int i = 0; i < 4; ++i) {
                             const int c = wn * 64 + tn * 32 + i * 8 + hh * 4;
-                            const float v[4] = {acc[tn][tm][i * 4], acc[tn][tm][i * 4 + 1], acc[tn][tm][i * 4 + 2],
-                                                acc[tn][tm][i * 4 + 3]};
-                            const float k = fac[tm] * wsc;
-                            *(f32x4 *)((uint8_t *)S + r * kResPitch + c * 4) = f32x4{v[0] * k, v[1] * k, v[2] * k, v[3] * k};
+                            f32x4 v = {acc[tn][tm][i * 4], acc[tn][tm][i * 4 + 1], acc[tn][tm][i * 4 + 2],
+                                       acc[tn][tm][i * 4 + 3]};
+                            if constexpr (FP8) v *= fac[tm] * wsc;
+                            *(f32x4 *)((uint8_t *)S + r * kResPitch + c * 4) = v;
                         }
                 }
             }
             if (s + 1 < 4) load_x(s + 1, xin[(s + 1) & 1]);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             lds_barrier();
+            float sq[8];
 #pragma unroll
             for (int k = 0; k < 8; ++k) {
                 const int r = wave * 8 + k, m = m0 + s * 64 + r;
-                if (m >= a.M) continue;
                 const f32x4 d = *(const f32x4 *)((const uint8_t *)S + r * kResPitch + lane * 16);
-                const f32x4 xo = xin[s & 1][k];
-                f32x4 v;
-                if constexpr (EPI == kEpiResid)
-                    v = f32x4{xo.x + d.x, xo.y + d.y, xo.z + d.z, xo.w + d.w};
-                else
-                    v = f32x4{d.x * a.scale, d.y * a.scale, d.z * a.scale, d.w * a.scale};
-                *(f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n0 + lane * 4) = v;
-                if (a.ss_out) {
-                    *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 + lane * 4) = u32x2{pack2(v.x, v.y), pack2(v.z, v.w)};
-                    const float sq = wave_sum(v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w);
-                    if (lane == 0) a.ss_out[(size_t)m * kSsParts + (n0 >> 8)] = sq;
+                const f32x4 v = EPI == kEpiResid ? xin[s & 1][k] + d : d * a.scale;
+                sq[k] = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+                if (m < a.M) {
+                    *(f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n0 + lane * 4) = v;
+                    if (a.ss_out)
+                        *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 + lane * 4) =
+                            u32x2{pack2(v.x, v.y), pack2(v.z, v.w)};
                 }
+            }
+            if (a.ss_out) {
+                // row sums over the 64 lanes for all 8 rows at once: each exchange step
+                // halves the rows a lane keeps (lane bits 5, 4, 3 pick them), the last
+                // three finish the sum; lane 8 b then holds row b
+                const bool b5 = lane & 32, b4 = lane & 16, b3 = lane & 8;
+                float s4[4], s2[2];
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    s4[j] = (b5 ? sq[4 + j] : sq[j]) + __shfl_xor(b5 ? sq[j] : sq[4 + j], 32, 64);
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    s2[j] = (b4 ? s4[2 + j] : s4[j]) + __shfl_xor(b4 ? s4[j] : s4[2 + j], 16, 64);
+                float s1 = (b3 ? s2[1] : s2[0]) + __shfl_xor(b3 ? s2[0] : s2[1], 8, 64);
+                s1 += __shfl_xor(s1, 4, 64);
+                s1 += __shfl_xor(s1, 2, 64);
+                s1 += __shfl_xor(s1, 1, 64);
+                const int m = m0 + s * 64 + wave * 8 + (lane >> 3);
+                if ((lane & 7) == 0 && m < a.M) a.ss_out[(size_t)m * kSsParts + (n0 >> 8)] = s1;
             }
         }
     }
