@@ -919,12 +919,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             lds_barrier();
             // tokens past M are written as zeros (masked keys must hold finite values)
+            const bool full = m0 + 256 <= a.M;
 #pragma unroll
             for (int it = 0; it < 16; ++it) {
                 const int f = it * 16 + wave * 2 + hh, t0 = l32 * 8;
                 u32x4 v = *(const u32x4 *)(L + f * kQkPitch + t0 * 2);
                 const int valid = a.M - (m0 + t0);
-                if (valid < 8) {
+                if (!full && valid < 8) {
                     uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
@@ -942,6 +943,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
     if constexpr (EPI == kEpiStore || EPI == kEpiQkv) {
         // ---- token-major bf16 rows of 256 features (q and k rotated)
         const float wsc = FP8 ? a.w_scale : 1.0f;
+        const bool one_axis = a.sec0 >= 32;
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) {
             const int t = wm * 128 + tm * 32 + l32;
@@ -964,11 +966,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
                     for (int j = 0; j < 4; ++j) o[j] = acc[tn][tm][i * 4 + j] * k;
                     if constexpr (EPI == kEpiQkv) {
                         float2 cs[2];
+                        if (one_axis) {
+                            // one rotary axis (text): both (cos, sin) entries in one 16-byte load
+                            const f32x4 e = *(const f32x4 *)(rb[0] + tn * 16 + i * 4);
+                            cs[0] = float2{e.x, e.y};
+                            cs[1] = float2{e.z, e.w};
+                        } else {
 #pragma unroll
-                        for (int q = 0; q < 2; ++q) {
-                            const int jp = tn * 16 + i * 4 + q, pair = jp + hh * 2;
-                            const float2 *b = pair < a.sec0 ? rb[0] : (pair < a.sec0 + a.sec1 ? rb[1] : rb[2]);
-                            cs[q] = b[jp];
+                            for (int q = 0; q < 2; ++q) {
+                                const int jp = tn * 16 + i * 4 + q, pair = jp + hh * 2;
+                                const float2 *b = pair < a.sec0 ? rb[0] : (pair < a.sec0 + a.sec1 ? rb[1] : rb[2]);
+                                cs[q] = b[jp];
+                            }
                         }
                         rotate4(o, cs);
                     }
