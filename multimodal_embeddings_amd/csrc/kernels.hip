@@ -1143,29 +1143,34 @@ hipError_t launch_gemm_e4m3(int epi, const GemmArgs &a, hipStream_t stream) {
 // =========================================================== attention
 //
 // Bidirectional attention inside each item (varlen, tiles from the tape's
-// prefix sums). Workgroup = (query tile of 256 tokens of one item, head), 4
-// waves of 64 queries (two 32-query subtiles). Per key tile of 64 keys, staged
-// in LDS by DMA (two stages, the next tile in flight):
-//   S^T (keys x queries) = K Q^T   -- each lane keeps one query and 32 scores
-//                                      per subtile; the row max needs one
-//                                      exchange between the two lane halves
+// prefix sums). Workgroup = (query tile of 256 tokens of one item, head), 8
+// waves of 32 queries; key tiles of 64 keys staged in LDS by DMA, four stages
+// (three in flight), one barrier per tile. Per key tile:
+//   S^T (keys x queries) = K Q^T   -- each lane keeps one query and 32 of its
+//                                      scores; the row max needs one exchange
+//                                      between the two lane halves
 //   online softmax in fp32 on exp2 of pre-scaled logits; the output is only
 //   rescaled when some query's running max grew
 //   O^T (d x queries) += V^T P^T   -- P^T comes straight from the S^T registers.
+// Small waves (under 128 registers) let four waves share each SIMD, so the
+// softmax of some waves runs on the vector ALUs while others keep the matrix
+// cores busy.
 // Within each 32-key subtile, LDS row r of K holds key perm32(r), chosen so that
 // the 8 scores a lane feeds to one PV step belong to 8 consecutive keys; V^T rows
 // (feature-major vt) are then read as one 16-byte chunk, like K. Both operands
-// use 16-byte chunks XOR-swizzled by (row & 7): conflict-free ds_read_b128.
+// use 16-byte chunks XOR-swizzled by (row / 2) % 8: conflict-free ds_read_b128
+// on 64 banks.
 
 __device__ __forceinline__ int perm32(int r) {  // r = 8 i + 4 h + j
     const int i = r >> 3, h = (r >> 2) & 1, j = r & 3;
     return (i >> 1) * 16 + h * 8 + (i & 1) * 4 + j;
 }
 
-__global__ __launch_bounds__(256, 2) void k_attention(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
+__global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                       int ldqk, const uint16_t *__restrict__ vt, int ldvt,
                                                       uint16_t *__restrict__ o, int ldo, const int *__restrict__ cu,
                                                       const int2 *__restrict__ tiles, int ntiles) {
+    constexpr int NS = 4;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int head = logical / ntiles, ti = logical % ntiles;
     const int2 tile = tiles[ti];
@@ -1173,54 +1178,41 @@ __global__ __launch_bounds__(256, 2) void k_attention(const uint16_t *__restrict
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l32 = lane & 31, hh = lane >> 5;
     constexpr int STAGE = 1024;  // 16-byte chunks: K tile 512 | V^T tile 512
-    __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * STAGE];
+    __shared__ __attribute__((aligned(1024))) u32x4 smem[NS * STAGE];
 
-    const int qbase = tile.y + wave * 64;
+    const int qbase = tile.y + wave * 32;
     const bool active = qbase < k1;
-    bf16x8 qf[2][4];
+    bf16x8 qf[4];
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs)
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            qf[qs][ks] = __builtin_bit_cast(
-                bf16x8, *(const u32x4 *)(q + (size_t)(qbase + qs * 32 + l32) * ldqk + head * 64 + ks * 16 + hh * 8));
+    for (int ks = 0; ks < 4; ++ks)
+        qf[ks] = __builtin_bit_cast(bf16x8,
+                                    *(const u32x4 *)(q + (size_t)(qbase + l32) * ldqk + head * 64 + ks * 16 + hh * 8));
 
-    // DMA: chunk slot p = 256 rd + tid of each operand tile; row p / 8, stored chunk p % 8
-    auto issue = [&](int kt, u32x4 *dst) {
-#pragma unroll
-        for (int rd = 0; rd < 2; ++rd) {
-            const int p = rd * 256 + tid, row = p >> 3, c = (p & 7) ^ (row & 7);
-            const int key = kt + (row & 32) + perm32(row & 31);
-            lds_dma16(k + (size_t)key * ldqk + head * 64 + c * 8, dst + rd * 256 + wave * 64);
-        }
-#pragma unroll
-        for (int rd = 0; rd < 2; ++rd) {
-            const int p = rd * 256 + tid, row = p >> 3, c = (p & 7) ^ (row & 7);
-            lds_dma16(vt + (size_t)(head * 64 + row) * ldvt + kt + c * 8, dst + 512 + rd * 256 + wave * 64);
-        }
+    // DMA of stage t into buffer t % NS: thread tid moves K chunk slot tid and V^T
+    // chunk slot tid (row slot / 8, stored chunk slot % 8)
+    const int prow = tid >> 3, pc = swz(prow, tid & 7);
+    const int pkey = (prow & 32) + perm32(prow & 31);
+    auto issue = [&](int t) {
+        const int kt = k0 + t * 64;
+        u32x4 *dst = smem + (t % NS) * STAGE;
+        lds_dma16(k + (size_t)(kt + pkey) * ldqk + head * 64 + pc * 8, dst + wave * 64);
+        lds_dma16(vt + (size_t)(head * 64 + prow) * ldvt + kt + pc * 8, dst + 512 + wave * 64);
     };
 
-    f32x16 O[2][2];
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) O[qs][0] = f32x16{}, O[qs][1] = f32x16{};
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+    f32x16 O[2] = {f32x16{}, f32x16{}};
+    float m_run = -INFINITY, l_run = 0.f;
     const float c = 0.18033688011112042f;  // log2(e) / sqrt(64)
 
     auto compute = [&](const u32x4 *sK, int kt) {
         const u32x4 *sV = sK + 512;
-        f32x16 S[2][2];
-        u32x4 P[2][2][2];  // bf16 pairs of p per query subtile, key subtile, PV step (one MFMA operand each)
-#pragma unroll
-        for (int qs = 0; qs < 2; ++qs) S[qs][0] = f32x16{}, S[qs][1] = f32x16{};
+        f32x16 S[2] = {f32x16{}, f32x16{}};
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int row = kk * 32 + l32;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const bf16x8 kf = __builtin_bit_cast(bf16x8, sK[row * 8 + ((ks * 2 + hh) ^ (row & 7))]);
-#pragma unroll
-                for (int qs = 0; qs < 2; ++qs)
-                    S[qs][kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qs][ks], S[qs][kk], 0, 0, 0);
+                const bf16x8 kf = __builtin_bit_cast(bf16x8, sK[row * 8 + swz(row, ks * 2 + hh)]);
+                S[kk] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], S[kk], 0, 0, 0);
             }
         }
         if (kt + 64 > k1) {
@@ -1229,104 +1221,89 @@ __global__ __launch_bounds__(256, 2) void k_attention(const uint16_t *__restrict
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = kt + kk * 32 + perm32((r >> 2) * 8 + hh * 4 + (r & 3));
-                    if (key >= k1) S[0][kk][r] = -INFINITY, S[1][kk][r] = -INFINITY;
+                    if (key >= k1) S[kk][r] = -INFINITY;
                 }
         }
+        float mx = -INFINITY;
 #pragma unroll
-        for (int qs = 0; qs < 2; ++qs) {
-            float mx = -INFINITY;
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kk][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float m_new = fmaxf(m_run, mx);
+        if (__any(m_new > m_run)) {
+            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
+            l_run *= alpha;
+            O[0] *= alpha;
+            O[1] *= alpha;
+        }
+        m_run = m_new;
+        const float mc = m_new * c;
+        // p = 2^(c s - c m) on the raw v_exp_f32 (weights below 2^-126 flush to 0);
+        // packed to bf16 at once, and the row sum taken over those same bf16 values
+        u32x4 P[2][2];
+        float rs = 0.f;
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[qs][kk][r]);
-            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-            const float m_new = fmaxf(m_run[qs], mx);
-            if (__any(m_new > m_run[qs])) {
-                const float alpha = __builtin_amdgcn_exp2f((m_run[qs] - m_new) * c);
-                l_run[qs] *= alpha;
-                O[qs][0] *= alpha;
-                O[qs][1] *= alpha;
-            }
-            m_run[qs] = m_new;
-            const float mc = m_new * c;
-            // p = 2^(c s - c m) on the raw v_exp_f32 (weights below 2^-126 flush to 0);
-            // packed to bf16 at once, and the row sum taken over those same bf16 values
-            float rs = 0.f;
-            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
+            for (int ip = 0; ip < 2; ++ip) {
+                uint32_t w[4];
 #pragma unroll
-                for (int r = 0; r < 8; ++r) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[qs][kk][2 * r], c, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[qs][kk][2 * r + 1], c, -mc));
+                for (int e = 0; e < 4; ++e) {
+                    const int r = ip * 4 + e;
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kk][2 * r], c, -mc));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kk][2 * r + 1], c, -mc));
                     const bf16x2 pb = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-                    P[qs][kk][r >> 2][r & 3] = __builtin_bit_cast(uint32_t, pb);
+                    w[e] = __builtin_bit_cast(uint32_t, pb);
                     rs = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rs, false);
                 }
-            l_run[qs] += rs;
-        }
+                P[kk][ip] = u32x4{w[0], w[1], w[2], w[3]};
+            }
+        l_run += rs;
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
             const int kk = s2 >> 1, ip = s2 & 1;
-            bf16x8 pf[2];
-#pragma unroll
-            for (int qs = 0; qs < 2; ++qs)
-                pf[qs] = __builtin_bit_cast(bf16x8, P[qs][kk][ip]);
+            const bf16x8 pf = __builtin_bit_cast(bf16x8, P[kk][ip]);
 #pragma unroll
             for (int dt = 0; dt < 2; ++dt) {
                 const int row = dt * 32 + l32;
-                const bf16x8 vf = __builtin_bit_cast(bf16x8, sV[row * 8 + ((kk * 4 + ip * 2 + hh) ^ (row & 7))]);
-#pragma unroll
-                for (int qs = 0; qs < 2; ++qs)
-                    O[qs][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qs], O[qs][dt], 0, 0, 0);
+                const bf16x8 vf = __builtin_bit_cast(bf16x8, sV[row * 8 + swz(row, kk * 4 + ip * 2 + hh)]);
+                O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, O[dt], 0, 0, 0);
             }
         }
     };
 
     const int ntile = (k1 - k0 + 63) >> 6;
-    issue(k0, smem);
-    for (int t = 0; t < ntile; t += 2) {
-        const int kt = k0 + t * 64;
-        if (t + 1 < ntile) {
-            issue(kt + 64, smem + STAGE);
-            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        }
-        lds_barrier();
-        if (active) compute(smem, kt);
+#pragma unroll
+    for (int s = 0; s < NS - 1; ++s)
+        if (s < ntile) issue(s);
+    for (int t = 0; t < ntile; ++t) {
+        // stage t landed for every wave, and every wave is done with stage t-1,
+        // whose buffer receives stage t + NS - 1
+        const int after = min(ntile - 1, t + NS - 2) - t;  // stages in flight behind t
+        if (after >= 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else if (after == 1) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         lds_barrier();
-        if (t + 1 < ntile) {
-            if (t + 2 < ntile) {
-                issue(kt + 128, smem);
-                asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-            } else {
-                asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-            }
-            lds_barrier();
-            if (active) compute(smem + STAGE, kt + 64);
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            lds_barrier();
-        }
+        if (t + NS - 1 < ntile) issue(t + NS - 1);
+        if (active) compute(smem + (t % NS) * STAGE, k0 + t * 64);
     }
 
+    const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
+    const int qrow = qbase + l32;
+    if (active && qrow < k1) {
+        const float inv = 1.0f / l_tot;
 #pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-        const float l_tot = l_run[qs] + __shfl_xor(l_run[qs], 32, 64);
-        const int qrow = qbase + qs * 32 + l32;
-        if (qrow < k1) {
-            const float inv = 1.0f / l_tot;
+        for (int dt = 0; dt < 2; ++dt)
 #pragma unroll
-            for (int dt = 0; dt < 2; ++dt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int d = dt * 32 + i * 8 + hh * 4;
-                    *(u32x2 *)(o + (size_t)qrow * ldo + head * 64 + d) =
-                        u32x2{pack2(O[qs][dt][i * 4 + 0] * inv, O[qs][dt][i * 4 + 1] * inv),
-                              pack2(O[qs][dt][i * 4 + 2] * inv, O[qs][dt][i * 4 + 3] * inv)};
-                }
-        }
+            for (int i = 0; i < 4; ++i) {
+                const int d = dt * 32 + i * 8 + hh * 4;
+                *(u32x2 *)(o + (size_t)qrow * ldo + head * 64 + d) =
+                    u32x2{pack2(O[dt][i * 4 + 0] * inv, O[dt][i * 4 + 1] * inv),
+                          pack2(O[dt][i * 4 + 2] * inv, O[dt][i * 4 + 3] * inv)};
+            }
     }
 }
 
@@ -1334,7 +1311,7 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, int ldqk, cons
                             uint16_t *o, int ldo, const int *cu, const int2 *tiles, int ntiles, int heads,
                             hipStream_t stream) {
     if (ntiles == 0) return hipSuccess;
-    k_attention<<<ntiles * heads, 256, 0, stream>>>(q, k, ldqk, vt, ldvt, o, ldo, cu, tiles, ntiles);
+    k_attention<<<ntiles * heads, 512, 0, stream>>>(q, k, ldqk, vt, ldvt, o, ldo, cu, tiles, ntiles);
     return hipGetLastError();
 }
 
