@@ -24,6 +24,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -1149,8 +1150,9 @@ hipError_t launch_gemm_e4m3(int epi, const GemmArgs &a, hipStream_t stream) {
 //   S^T (keys x queries) = K Q^T   -- each lane keeps one query and 32 of its
 //                                      scores; the row max needs one exchange
 //                                      between the two lane halves
-//   online softmax in fp32 on exp2 of pre-scaled logits; the output is only
-//   rescaled when some query's running max grew
+//   online softmax in fp32 on exp2 of pre-scaled logits: the score accumulators
+//   start at minus the running max, so a weight costs one exponential; the
+//   output is only rescaled when some query's running max grew
 //   O^T (d x queries) += V^T P^T   -- P^T comes straight from the S^T registers.
 // Small waves (under 128 registers) let four waves share each SIMD, so the
 // softmax of some waves runs on the vector ALUs while others keep the matrix
@@ -1182,11 +1184,16 @@ __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict
 
     const int qbase = tile.y + wave * 32;
     const bool active = qbase < k1;
+    // queries pre-scaled by c = log2(e) / sqrt(64): scores come out of the MFMAs in
+    // base-2 logit units
+    const float c = 0.18033688011112042f;
     bf16x8 qf[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-        qf[ks] = __builtin_bit_cast(bf16x8,
-                                    *(const u32x4 *)(q + (size_t)(qbase + l32) * ldqk + head * 64 + ks * 16 + hh * 8));
+    for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 raw = __builtin_bit_cast(
+            bf16x8, *(const u32x4 *)(q + (size_t)(qbase + l32) * ldqk + head * 64 + ks * 16 + hh * 8));
+        qf[ks] = __builtin_convertvector(__builtin_convertvector(raw, f32x8) * c, bf16x8);
+    }
 
     // DMA of stage t into buffer t % NS: thread tid moves K chunk slot tid and V^T
     // chunk slot tid (row slot / 8, stored chunk slot % 8)
@@ -1200,12 +1207,16 @@ __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict
     };
 
     f32x16 O[2] = {f32x16{}, f32x16{}};
-    float m_run = -INFINITY, l_run = 0.f;
-    const float c = 0.18033688011112042f;  // log2(e) / sqrt(64)
+    float m_run = 0.f, l_run = 0.f;  // running max of the scaled scores, sum of weights
 
-    auto compute = [&](const u32x4 *sK, int kt) {
+    auto compute = [&](const u32x4 *sK, int kt, bool first) {
         const u32x4 *sV = sK + 512;
-        f32x16 S[2] = {f32x16{}, f32x16{}};
+        // the accumulators start at -m_run: the MFMAs return scores relative to the
+        // running max, ready for the exponential
+        const float init = first ? 0.f : -m_run;
+        f32x16 S[2];
+        S[0] = init;
+        S[1] = init;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int row = kk * 32 + l32;
@@ -1230,17 +1241,22 @@ __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kk][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        const float m_new = fmaxf(m_run, mx);
-        if (__any(m_new > m_run)) {
-            const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);
-            l_run *= alpha;
-            O[0] *= alpha;
-            O[1] *= alpha;
+        // the first tile sets the running max; later ones move it only where some
+        // score exceeds it (then the output and the row sum are rescaled)
+        const float d = first ? mx : fmaxf(mx, 0.f);
+        if (first || __any(d > 0.f)) {
+            m_run += d;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) S[kk] -= d;
+            if (!first) {
+                const float alpha = __builtin_amdgcn_exp2f(-d);
+                l_run *= alpha;
+                O[0] *= alpha;
+                O[1] *= alpha;
+            }
         }
-        m_run = m_new;
-        const float mc = m_new * c;
-        // p = 2^(c s - c m) on the raw v_exp_f32 (weights below 2^-126 flush to 0);
-        // packed to bf16 at once, and the row sum taken over those same bf16 values
+        // p = 2^(relative score) on the raw v_exp_f32 (weights below 2^-126 flush to
+        // 0); packed to bf16 at once, and the row sum taken over those same bf16 values
         u32x4 P[2][2];
         float rs = 0.f;
         const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -1252,8 +1268,8 @@ __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int r = ip * 4 + e;
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(S[kk][2 * r], c, -mc));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(S[kk][2 * r + 1], c, -mc));
+                    const float p0 = __builtin_amdgcn_exp2f(S[kk][2 * r]);
+                    const float p1 = __builtin_amdgcn_exp2f(S[kk][2 * r + 1]);
                     const bf16x2 pb = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
                     w[e] = __builtin_bit_cast(uint32_t, pb);
                     rs = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rs, false);
@@ -1288,7 +1304,7 @@ __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         lds_barrier();
         if (t + NS - 1 < ntile) issue(t + NS - 1);
-        if (active) compute(smem + (t % NS) * STAGE, k0 + t * 64);
+        if (active) compute(smem + (t % NS) * STAGE, k0 + t * 64, t == 0);
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
