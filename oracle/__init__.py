@@ -74,6 +74,8 @@ def _declare(L):
     L.oracle_pool.argtypes = [P, P, SZ, SZ, SZ, P, P, P, P]
     L.oracle_forward.argtypes = [C.POINTER(Geometry), P, P, P, P, P, P, P, P, SZ, P]
     L.oracle_forward_states.argtypes = [C.POINTER(Geometry), P, P, P, P, P, SZ, P, P]
+    L.oracle_token_vectors.argtypes = [P, SZ, SZ, P, SZ, P]
+    L.oracle_maxsim.argtypes = [P, P, SZ, P, P, SZ, SZ, SZ, SZ, P]
 
 
 def _p(a):
@@ -303,3 +305,36 @@ def media_frontend(weights, batch):
 def encode_media(weights, batch):
     x0, pos, cu = media_frontend(weights, batch)
     return forward(weights, x0, pos, cu), (0, int(cu[-1]))
+
+
+# ------------------------------------------------------- per-token outputs
+
+
+def token_vectors(xf, w):
+    """Unit rows of xf W (token head) -> [T x width] float64."""
+    xf = _f64(xf)
+    T, D = xf.shape
+    w = _f32(w)
+    width = w.shape[1]
+    out = np.zeros((max(T, 1), width), np.float64)
+    if T:
+        lib().oracle_token_vectors(_p(xf), T, D, _p(w), width, _p(out))
+    return out[:T]
+
+
+def maxsim(q, q_offsets, d, d_offsets, prefix=0, span=64):
+    """Hard MaxSim scores [len(q_offsets)-1 x len(d_offsets)-1] float64."""
+    q, d = _f64(q), _f64(d)
+    qo = np.ascontiguousarray(q_offsets, dtype=np.uint64)
+    do = np.ascontiguousarray(d_offsets, dtype=np.uint64)
+    nq, nd = len(qo) - 1, len(do) - 1
+    width = q.shape[1] if q.ndim == 2 else d.shape[1]
+    if q.size == 0:
+        q = np.zeros((1, width), np.float64)
+    if d.size == 0:
+        d = np.zeros((1, width), np.float64)
+    out = np.zeros((max(nq, 1), max(nd, 1)), np.float64)
+    if nq and nd:
+        lib().oracle_maxsim(_p(q), _p(qo), nq, _p(d), _p(do), nd, width, prefix, span, _p(out))
+    return out[:nq, :nd]
+

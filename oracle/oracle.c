@@ -480,3 +480,60 @@ void oracle_forward_states(const oracle_geometry_t *g, const oracle_block_t *blo
     for (size_t l = 0; l < g->depth; ++l) oracle_block(g, &blocks[l], x_out, pos, cu, count, T);
     oracle_rmsnorm(x_out, final_norm, T, D, g->rms_epsilon, xf_out);
 }
+
+/* ------------------------------------------------------- per-token outputs */
+
+/* Token head ("UForm" page, the reranker paragraph of its losses: the per-byte
+ * encoder output refined through a per-byte projection head into unit vectors;
+ * "Rust" and "Python" pages, "Encoding": TOKEN_VECTORS are the head's unit
+ * rows, one per state, token_width wide). Readings: a bias-free linear map of
+ * the final-norm states, y = xf W with W [D x width] (bf16-exact), then every
+ * row divided by its Euclidean norm; a zero row stays zero. out is [T x width]. */
+void oracle_token_vectors(const double *xf, size_t T, size_t D, const float *w, size_t width, double *out) {
+    double *W = widen(w, D * width, 0);
+    matmul(xf, T, D, W, width, out, 0);
+    for (size_t t = 0; t < T; ++t) {
+        double ss = 0.0;
+        for (size_t e = 0; e < width; ++e) ss += out[t * width + e] * out[t * width + e];
+        if (ss > 0.0) {
+            double norm = sqrt(ss);
+            for (size_t e = 0; e < width; ++e) out[t * width + e] /= norm;
+        }
+    }
+    free(W);
+}
+
+/* Hard MaxSim ("UForm" page, same paragraph): the score of query i against
+ * document j is the mean, over the query's rows t, of the largest inner product
+ * <q_t, d_s> over the document's rows s. q and d are row-major [rows x width];
+ * query i owns rows qoff[i] .. qoff[i+1], document j rows doff[j] .. doff[j+1].
+ * Readings: the query's rows start past its first `prefix` rows and at most
+ * `span` of them count (the trainer's max_query_span, "Training" page,
+ * uform_late_interaction_t); a query with no counted rows, or a document with
+ * no rows, scores 0. scores is [nq x nd]. */
+void oracle_maxsim(const double *q, const uint64_t *qoff, size_t nq, const double *d, const uint64_t *doff,
+                   size_t nd, size_t width, size_t prefix, size_t span, double *scores) {
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (size_t i = 0; i < nq; ++i) {
+        for (size_t j = 0; j < nd; ++j) {
+            uint64_t qa = qoff[i] + prefix, qb = qoff[i + 1];
+            if (qa > qb) qa = qb;
+            if (qb - qa > span) qb = qa + span;
+            uint64_t da = doff[j], db = doff[j + 1];
+            double total = 0.0;
+            if (qb > qa && db > da) {
+                for (uint64_t t = qa; t < qb; ++t) {
+                    double best = -INFINITY;
+                    for (uint64_t s = da; s < db; ++s) {
+                        double dot = 0.0;
+                        for (size_t e = 0; e < width; ++e) dot += q[t * width + e] * d[s * width + e];
+                        if (dot > best) best = dot;
+                    }
+                    total += best;
+                }
+                total /= (double)(qb - qa);
+            }
+            scores[i * nd + j] = total;
+        }
+    }
+}

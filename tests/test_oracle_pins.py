@@ -517,3 +517,82 @@ def test_bf16_round_matches_library_cast():
     np.testing.assert_array_equal(got, want)
     # ties go to even: 1 + 2^-8 sits halfway between 1 and 1 + 2^-7
     assert oracle.bf16_round(1.0 + 2 ** -8) == 1.0 and oracle.bf16_round(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6
+
+
+# ------------------------------------------------------- per-token outputs
+
+
+def _unit_rows(n, width, rng):
+    v = rng.standard_normal((n, width))
+    return v / np.linalg.norm(v, axis=1, keepdims=True)
+
+
+def test_token_vectors_are_unit_rows_of_the_projection():
+    xf = RNG.standard_normal((9, 16))
+    w = synth.bf16_bits_to_f32(synth.to_bf16_bits(RNG.standard_normal((16, 8)).astype(np.float32)))
+    v = oracle.token_vectors(xf, w)
+    assert np.allclose(np.linalg.norm(v, axis=1), 1.0, atol=1e-12)
+    # direction: parallel to xf W (cosine 1 against a plain matmul of the same operands)
+    y = xf @ w.astype(np.float64)
+    assert np.allclose((v * y).sum(1), np.linalg.norm(y, axis=1), rtol=1e-12)
+    # identity head: the unit states themselves; positive scaling of W changes nothing; negation flips
+    eye = np.eye(16, dtype=np.float32)
+    assert np.allclose(oracle.token_vectors(xf, eye), xf / np.linalg.norm(xf, axis=1, keepdims=True), atol=1e-12)
+    assert np.allclose(oracle.token_vectors(xf, 4 * w), v, atol=1e-12)
+    assert np.allclose(oracle.token_vectors(xf, -w), -v, atol=1e-12)
+    # a zero state stays zero (reading) and does not disturb the other rows
+    xz = xf.copy()
+    xz[3] = 0
+    vz = oracle.token_vectors(xz, w)
+    assert np.all(vz[3] == 0) and np.allclose(np.delete(vz, 3, 0), np.delete(v, 3, 0))
+
+
+def test_maxsim_closed_forms():
+    e = np.eye(6)
+    # one row each: the inner product
+    a, b = _unit_rows(1, 6, RNG), _unit_rows(1, 6, RNG)
+    assert np.isclose(oracle.maxsim(a, [0, 1], b, [0, 1])[0, 0], float(a[0] @ b[0]), atol=1e-15)
+    # orthonormal rows: query {e0, e1} against document {e1, e2} keeps 0 and 1 -> mean 0.5
+    assert oracle.maxsim(e[[0, 1]], [0, 2], e[[1, 2]], [0, 2])[0, 0] == 0.5
+    # antipodal document: every best match is -1
+    q = _unit_rows(5, 6, RNG)
+    assert np.isclose(oracle.maxsim(q, [0, 5], -q[:1], [0, 1])[0, 0], -float((q @ q[0]).mean()), atol=1e-15)
+    # a document holding every query row scores 1 (the largest inner product of unit rows)
+    d = np.concatenate([_unit_rows(7, 6, RNG), q])
+    assert np.isclose(oracle.maxsim(q, [0, 5], d, [0, 12])[0, 0], 1.0, atol=1e-12)
+
+
+def test_maxsim_is_a_mean_of_per_row_maxima():
+    # brute force on a tiny case through a different route: sort each query row's
+    # products and take the last one
+    q, d = _unit_rows(7, 8, RNG), _unit_rows(11, 8, RNG)
+    qo, do = [0, 3, 7], [0, 5, 5, 11]
+    s = oracle.maxsim(q, qo, d, do)
+    for i in range(2):
+        for j in range(3):
+            rows = d[do[j]:do[j + 1]]
+            if len(rows) == 0:
+                assert s[i, j] == 0.0  # empty document (reading)
+                continue
+            best = [sorted(float(np.dot(qt, r)) for r in rows)[-1] for qt in q[qo[i]:qo[i + 1]]]
+            assert np.isclose(s[i, j], sum(best) / len(best), atol=1e-14)
+
+
+def test_maxsim_invariances_and_query_span():
+    q, d = _unit_rows(20, 8, RNG), _unit_rows(30, 8, RNG)
+    base = oracle.maxsim(q, [0, 20], d, [0, 30], prefix=0, span=64)[0, 0]
+    # document rows in any order
+    perm = RNG.permutation(30)
+    assert np.isclose(oracle.maxsim(q, [0, 20], d[perm], [0, 30])[0, 0], base, atol=1e-14)
+    # more document rows never lower a score
+    more = np.concatenate([d, _unit_rows(9, 8, RNG)])
+    assert oracle.maxsim(q, [0, 20], more, [0, 39])[0, 0] >= base - 1e-14
+    # prefix and span select query rows [prefix, prefix + span): the same as slicing them out
+    s = oracle.maxsim(q, [0, 20], d, [0, 30], prefix=3, span=5)[0, 0]
+    assert np.isclose(s, oracle.maxsim(q[3:8], [0, 5], d, [0, 30], prefix=0, span=64)[0, 0], atol=1e-14)
+    # a query with no rows past its prefix scores 0 (reading)
+    assert oracle.maxsim(q, [0, 20], d, [0, 30], prefix=20, span=64)[0, 0] == 0.0
+    # span caps the counted rows
+    s64 = oracle.maxsim(q, [0, 20], d, [0, 30], prefix=0, span=64)[0, 0]
+    s20 = oracle.maxsim(q, [0, 20], d, [0, 30], prefix=0, span=20)[0, 0]
+    assert s64 == s20
