@@ -85,6 +85,28 @@ typedef struct ube_rows_view_t {
     ube_scalar_t scalar;
 } ube_rows_view_t;
 
+/* Ragged output rows ("Arenas" page, "Rows and Tapes": packed rows and one
+ * more offset than items): item i owns rows offsets[i] .. offsets[i+1]; row r
+ * starts at (char*)data + r*stride and holds `columns` values of `scalar`;
+ * `rows` = offsets[count]. Written by an encode, data and offsets are device
+ * memory inside the arena, valid until the next call naming that arena. */
+typedef struct ube_rows_tape_view_t {
+    void *data;
+    size_t const *offsets;
+    size_t count, rows, columns, stride;
+    ube_scalar_t scalar;
+} ube_rows_tape_view_t;
+
+/* Surfaces an encode writes ("Rust" and "Python" pages, "Encoding": Outputs);
+ * OR-ed together, 0 meaning embeddings alone. States are the final-norm rows,
+ * one per token; token vectors are the token head's unit rows on the same
+ * offsets. A surface left out costs nothing past the final norm. */
+typedef enum ube_outputs_t {
+    ube_outputs_embeddings_k = 1,
+    ube_outputs_states_k = 2,
+    ube_outputs_token_vectors_k = 4,
+} ube_outputs_t;
+
 /* "Python" page, "Encoding": items cut at the context, and tokens encoded. */
 typedef struct ube_encode_stats_t {
     size_t truncated, tokens;
@@ -94,11 +116,14 @@ typedef struct ube_encode_stats_t {
  * depth N [required], hidden D [required, multiple of 128], heads H [D/64; D/H
  * must be 64], ffn F [3D; multiple of 64], vocab [258], context [1024; at most
  * 32767], rope_axes [1; 1 text, 2 image, 3 video], patch_side [16], channels
- * [3], rope_base [10000], rms_epsilon [1e-6], quantization [bf16; or e4m3]. */
+ * [3], rope_base [10000], rms_epsilon [1e-6], quantization [bf16; or e4m3],
+ * token_width [0 = no token head; a multiple of 128 up to 1024 here, where the
+ * pages allow multiples of 8; "Training" page, uform_late_interaction_t]. */
 typedef struct ube_geometry_t {
     size_t depth, hidden, heads, ffn, vocab, context, rope_axes, patch_side, channels;
     float rope_base, rms_epsilon;
     ube_scalar_t quantization;
+    size_t token_width;
 } ube_geometry_t;
 
 /* Weights in host memory, canonical layout y = x W with W row-major [in x out].
@@ -110,7 +135,9 @@ typedef struct ube_geometry_t {
  *   w_qkv      [D x 3D] = [W_q | W_k | W_v];  w_o [D x D]
  *   w_gate, w_up [D x F];  w_down [F x D]
  *   attn_norm, mlp_norm, final_norm: [D]
- *   pool_query [D];  pool_wk, pool_wv [D x D] */
+ *   pool_query [D];  pool_wk, pool_wv [D x D]
+ *   token_head [D x token_width] (NULL when token_width is 0): the per-token
+ *   projection whose rows, divided by their norms, are the token vectors */
 typedef struct ube_weights_t {
     uint16_t const *embed;
     uint16_t const *patch_proj;
@@ -125,6 +152,7 @@ typedef struct ube_weights_t {
     uint16_t const *pool_query;
     uint16_t const *pool_wk;
     uint16_t const *pool_wv;
+    uint16_t const *token_head;
 } ube_weights_t;
 
 typedef struct ube_model_handle_t *ube_model_t;
@@ -150,6 +178,7 @@ typedef struct ube_model_description_t {
     ube_scalar_t quantization;
     size_t memory_usage; /* device bytes the model holds */
     int device;
+    size_t token_width;  /* 0: the model has no token head */
 } ube_model_description_t;
 
 typedef struct ube_model_describe_t {
@@ -189,7 +218,13 @@ size_t ube_arena_capacity(ube_arena_t arena);
  * synchronisation). On failure *embeddings is all zeros and NULL.
  * `trace_residual`, when not NULL, is device memory of (depth+1) * T * D
  * floats that receives the fp32 residual stream after the frontend and after
- * every block (T = stats->tokens): a diagnostics hook, off the timed path. */
+ * every block (T = stats->tokens): a diagnostics hook, off the timed path.
+ * `outputs` (ube_outputs_t bits, 0 = embeddings) picks the surfaces: with
+ * states, *states receives the final-norm rows [T x D]; with token vectors,
+ * *token_vectors receives the unit rows [T x token_width] (unsupported when the
+ * model has no token head); both on the offsets of the kept tokens, as
+ * `outputs_scalar`. A surface not asked for is published empty; its pointer
+ * may then be NULL. */
 typedef struct ube_text_encode_t {
     ube_model_t model;
     ube_arena_t arena;
@@ -201,6 +236,9 @@ typedef struct ube_text_encode_t {
     ube_rows_view_t *embeddings;
     ube_encode_stats_t *stats;
     float *trace_residual;
+    unsigned outputs;
+    ube_rows_tape_view_t *states;
+    ube_rows_tape_view_t *token_vectors;
 } ube_text_encode_t;
 void ube_text_encode(ube_text_encode_t *arguments);
 
@@ -225,6 +263,9 @@ typedef struct ube_image_encode_pixels_t {
     ube_rows_view_t *embeddings;
     ube_encode_stats_t *stats;
     float *trace_residual;
+    unsigned outputs;
+    ube_rows_tape_view_t *states;
+    ube_rows_tape_view_t *token_vectors;
 } ube_image_encode_pixels_t;
 void ube_image_encode_pixels(ube_image_encode_pixels_t *arguments);
 
@@ -246,8 +287,36 @@ typedef struct ube_video_encode_frames_t {
     ube_rows_view_t *embeddings;
     ube_encode_stats_t *stats;
     float *trace_residual;
+    unsigned outputs;
+    ube_rows_tape_view_t *states;
+    ube_rows_tape_view_t *token_vectors;
 } ube_video_encode_frames_t;
 void ube_video_encode_frames(ube_video_encode_frames_t *arguments);
+
+/* Hard MaxSim scores ("UForm" page, the reranker paragraph of its losses: each
+ * query token keeps its best inner product over the candidate's tokens,
+ * averaged over the query). scores[i * scores_stride + j] = mean over query i's
+ * rows t in [prefix, prefix + span) (clipped to the item) of max over document
+ * j's rows s of <q_t, d_s>; a query with no counted rows, or an empty document,
+ * scores 0. query_span 0 means 64, the pages' max_query_span ("Training" page,
+ * uform_late_interaction_t). Both tapes are bf16 rows of the same `columns`
+ * (a multiple of 16, at most 1024) in device memory of `device`, offsets
+ * included (as an encode's token vectors are); offsets past `rows` are clamped
+ * to it. `scores` is device memory, scores_stride 0 meaning documents.count.
+ * completion == 0 blocks until the scores are final. invalid_argument on NULL
+ * or mismatched inputs; unsupported for other scalars or widths. */
+typedef struct ube_maxsim_t {
+    void *stream;
+    ube_outcome_t *outcome;
+    int device;
+    int completion;
+    ube_rows_tape_view_t queries;
+    ube_rows_tape_view_t documents;
+    size_t query_prefix, query_span;
+    float *scores;
+    size_t scores_stride;
+} ube_maxsim_t;
+void ube_maxsim(ube_maxsim_t *arguments);
 
 /* Host-only tape plan, the bookkeeping every text encode does first (no
  * device work; usable without a GPU). lengths[count] receives the kept length

@@ -43,6 +43,11 @@ class ube_rows_view_t(C.Structure):
     _fields_ = [("data", VP), ("count", SZ), ("columns", SZ), ("stride", SZ), ("scalar", C.c_int)]
 
 
+class ube_rows_tape_view_t(C.Structure):
+    _fields_ = [("data", VP), ("offsets", VP), ("count", SZ), ("rows", SZ), ("columns", SZ), ("stride", SZ),
+                ("scalar", C.c_int)]
+
+
 class ube_encode_stats_t(C.Structure):
     _fields_ = [("truncated", SZ), ("tokens", SZ)]
 
@@ -50,13 +55,13 @@ class ube_encode_stats_t(C.Structure):
 class ube_geometry_t(C.Structure):
     _fields_ = [(n, SZ) for n in ("depth", "hidden", "heads", "ffn", "vocab", "context", "rope_axes", "patch_side",
                                   "channels")] + [("rope_base", C.c_float), ("rms_epsilon", C.c_float),
-                                                  ("quantization", C.c_int)]
+                                                  ("quantization", C.c_int), ("token_width", SZ)]
 
 
 class ube_weights_t(C.Structure):
     _fields_ = [("embed", VP), ("patch_proj", VP)] + [
         (n, C.POINTER(VP)) for n in ("w_qkv", "w_o", "w_gate", "w_up", "w_down", "attn_norm", "mlp_norm")] + [
-        ("final_norm", VP), ("pool_query", VP), ("pool_wk", VP), ("pool_wv", VP)]
+        ("final_norm", VP), ("pool_query", VP), ("pool_wk", VP), ("pool_wv", VP), ("token_head", VP)]
 
 
 class ube_model_init_t(C.Structure):
@@ -66,7 +71,7 @@ class ube_model_init_t(C.Structure):
 
 class ube_model_description_t(C.Structure):
     _fields_ = [(n, SZ) for n in ("dimensions", "context", "depth", "heads", "ffn", "rope_axes")] + [
-        ("quantization", C.c_int), ("memory_usage", SZ), ("device", C.c_int)]
+        ("quantization", C.c_int), ("memory_usage", SZ), ("device", C.c_int), ("token_width", SZ)]
 
 
 class ube_model_describe_t(C.Structure):
@@ -81,7 +86,8 @@ class ube_arena_init_t(C.Structure):
 _ENCODE_HEAD = [("model", VP), ("arena", VP), ("stream", VP), ("outcome", C.POINTER(ube_outcome_t)),
                 ("completion", C.c_int)]
 _ENCODE_TAIL = [("outputs_scalar", C.c_int), ("embeddings", C.POINTER(ube_rows_view_t)),
-                ("stats", C.POINTER(ube_encode_stats_t)), ("trace_residual", VP)]
+                ("stats", C.POINTER(ube_encode_stats_t)), ("trace_residual", VP), ("outputs", C.c_uint),
+                ("states", C.POINTER(ube_rows_tape_view_t)), ("token_vectors", C.POINTER(ube_rows_tape_view_t))]
 
 
 class ube_text_encode_t(C.Structure):
@@ -96,6 +102,12 @@ class ube_image_encode_pixels_t(C.Structure):
 class ube_video_encode_frames_t(C.Structure):
     _fields_ = _ENCODE_HEAD + [("frames", ube_tape_view_t), ("frame_counts", C.POINTER(SZ)),
                                ("heights", C.POINTER(SZ)), ("widths", C.POINTER(SZ))] + _ENCODE_TAIL
+
+
+class ube_maxsim_t(C.Structure):
+    _fields_ = [("stream", VP), ("outcome", C.POINTER(ube_outcome_t)), ("device", C.c_int), ("completion", C.c_int),
+                ("queries", ube_rows_tape_view_t), ("documents", ube_rows_tape_view_t), ("query_prefix", SZ),
+                ("query_span", SZ), ("scores", VP), ("scores_stride", SZ)]
 
 
 STATUS = {0: "success", 1: "invalid_argument", 2: "shape_mismatch", 3: "out_of_memory", 4: "device", 5: "contended",
@@ -115,6 +127,7 @@ _SIGNATURES = {
     "ube_text_encode": ([C.POINTER(ube_text_encode_t)], None),
     "ube_image_encode_pixels": ([C.POINTER(ube_image_encode_pixels_t)], None),
     "ube_video_encode_frames": ([C.POINTER(ube_video_encode_frames_t)], None),
+    "ube_maxsim": ([C.POINTER(ube_maxsim_t)], None),
     "ube_tape_plan": ([C.POINTER(SZ), SZ, SZ, VP, VP, C.POINTER(ube_encode_stats_t)], C.c_int),
     "ube_status_name": ([C.c_int], C.c_char_p),
     "ube_step_gemm": ([VP, VP, VP, SZ, SZ, SZ, VP], C.c_int),
@@ -210,9 +223,11 @@ class Model:
         w.pool_query = host(bits["pool_query"], np.uint16)
         w.pool_wk = host(bits["pool_wk"], np.uint16)
         w.pool_wv = host(bits["pool_wv"], np.uint16)
+        if g.get("token_width"):
+            w.token_head = host(bits["token_head"], np.uint16)
         geo = ube_geometry_t(g["depth"], g["hidden"], g["heads"], g["ffn"], g["vocab"], g["context"], g["rope_axes"],
                              g["patch_side"], g["channels"], g["rope_base"], g["rms_epsilon"],
-                             SCALAR[g["quantization"]])
+                             SCALAR[g["quantization"]], g.get("token_width", 0))
         handle = VP()
         outcome = ube_outcome_t()
         args = ube_model_init_t(C.pointer(handle), C.pointer(outcome), device, geo, C.pointer(w))
@@ -290,52 +305,134 @@ class Rows:
         return t if self.scalar == "f32" else t.view(torch.int16).view(torch.bfloat16)
 
 
+class RowsTape:
+    """A rows tape in device memory: item i owns rows offsets[i] .. offsets[i+1] of a [rows x columns] matrix."""
+
+    def __init__(self, view: ube_rows_tape_view_t, device: int, keep=None):
+        self.view = view
+        self.data, self.offsets_ptr = view.data, view.offsets
+        self.count, self.rows, self.columns, self.stride = view.count, view.rows, view.columns, view.stride
+        self.scalar = {v: k for k, v in SCALAR.items()}[view.scalar]
+        self.device = device
+        self._keep = keep
+
+    def tensor(self):
+        """A torch copy of the rows, [rows x columns] (float32 or bfloat16)."""
+        import torch
+        item = 4 if self.scalar == "f32" else 2
+        if self.rows == 0:
+            dt = torch.float32 if self.scalar == "f32" else torch.bfloat16
+            return torch.zeros((0, self.columns), dtype=dt, device=f"cuda:{self.device}")
+        holder = type("_Cai", (), {"__cuda_array_interface__": {
+            "shape": (self.rows, self.columns), "typestr": "<f4" if item == 4 else "<u2",
+            "data": (self.data, False), "strides": (self.stride, item), "version": 2}})()
+        t = torch.as_tensor(holder, device=f"cuda:{self.device}").clone()
+        return t if item == 4 else t.view(torch.int16).view(torch.bfloat16)
+
+    def offsets(self):
+        """The count+1 offsets, copied to the host."""
+        import torch
+        holder = type("_Cai", (), {"__cuda_array_interface__": {
+            "shape": (self.count + 1,), "typestr": "<u8", "data": (self.offsets_ptr, False), "version": 2}})()
+        return torch.as_tensor(holder, device=f"cuda:{self.device}").cpu().numpy().copy()
+
+
+def rows_tape(rows, offsets, device: int = 0):
+    """A RowsTape over a torch bfloat16/float32 [rows x columns] tensor and a device uint64 offsets tensor."""
+    import torch
+    scalar = SCALAR["bf16"] if rows.dtype == torch.bfloat16 else SCALAR["f32"]
+    view = ube_rows_tape_view_t(rows.data_ptr(), offsets.data_ptr(), offsets.numel() - 1, rows.shape[0],
+                                rows.shape[1], rows.stride(0) * rows.element_size(), scalar)
+    return RowsTape(view, device, keep=(rows, offsets))
+
+
+OUTPUTS = {"embeddings": 1, "states": 2, "token_vectors": 4}
+
+
+def _outputs_bits(outputs):
+    if outputs is None:
+        return 0
+    if isinstance(outputs, int):
+        return outputs
+    bits = 0
+    for name in outputs:
+        bits |= OUTPUTS[name]
+    return bits
+
+
+def _finish(model, rows, states, vectors, stats, bits):
+    if bits == 0:
+        return Rows(rows, model.device), (stats.truncated, stats.tokens)
+    emb = Rows(rows, model.device) if bits & 1 else None
+    st = RowsTape(states, model.device) if bits & 2 else None
+    tv = RowsTape(vectors, model.device) if bits & 4 else None
+    return emb, st, tv, (stats.truncated, stats.tokens)
+
+
+def maxsim(queries: RowsTape, documents: RowsTape, scores, *, prefix=0, span=0, stream=None, completion=0,
+           device: int = 0):
+    """Hard MaxSim scores of every (query, document) pair into ``scores`` (device float32 [nq x >= nd])."""
+    outcome = ube_outcome_t()
+    args = ube_maxsim_t(_stream_handle(stream), C.pointer(outcome), device, completion, queries.view,
+                        documents.view, prefix, span, _ptr(scores), scores.stride(0) if scores.dim() == 2 else 0)
+    lib().ube_maxsim(C.byref(args))
+    _check(outcome)
+    return scores
+
+
 def _tape(data, offsets):
     off = np.ascontiguousarray(offsets, dtype=np.uint64)
     return ube_tape_view_t(_ptr(data), off.ctypes.data_as(C.POINTER(SZ)), len(off) - 1), off
 
 
 def text_encode(model: Model, arena: Arena, data, offsets, *, stream=None, outputs_scalar="f32", completion=0,
-                trace=None):
-    """-> (Rows, (truncated, tokens)). ``data``: torch uint8 tensor (device) or numpy (host)."""
+                trace=None, outputs=None):
+    """-> (Rows, (truncated, tokens)); with ``outputs`` (names or bits) -> (embeddings Rows | None,
+    states RowsTape | None, token vectors RowsTape | None, (truncated, tokens)).
+    ``data``: torch uint8 tensor (device) or numpy (host)."""
     tape, off = _tape(data, offsets)
     rows, stats, outcome = ube_rows_view_t(), ube_encode_stats_t(), ube_outcome_t()
+    states, vectors, bits = ube_rows_tape_view_t(), ube_rows_tape_view_t(), _outputs_bits(outputs)
     args = ube_text_encode_t(model.handle, arena.handle, _stream_handle(stream), C.pointer(outcome), completion,
-                             tape, SCALAR[outputs_scalar], C.pointer(rows), C.pointer(stats), _ptr(trace))
+                             tape, SCALAR[outputs_scalar], C.pointer(rows), C.pointer(stats), _ptr(trace), bits,
+                             C.pointer(states), C.pointer(vectors))
     lib().ube_text_encode(C.byref(args))
     _check(outcome)
-    return Rows(rows, model.device), (stats.truncated, stats.tokens)
+    return _finish(model, rows, states, vectors, stats, bits)
 
 
 def image_encode_pixels(model: Model, arena: Arena, data, offsets, heights, widths, *, stream=None,
-                        outputs_scalar="f32", completion=0, trace=None):
+                        outputs_scalar="f32", completion=0, trace=None, outputs=None):
     tape, off = _tape(data, offsets)
     hh = np.ascontiguousarray(heights, dtype=np.uint64)
     ww = np.ascontiguousarray(widths, dtype=np.uint64)
     rows, stats, outcome = ube_rows_view_t(), ube_encode_stats_t(), ube_outcome_t()
+    states, vectors, bits = ube_rows_tape_view_t(), ube_rows_tape_view_t(), _outputs_bits(outputs)
     args = ube_image_encode_pixels_t(model.handle, arena.handle, _stream_handle(stream), C.pointer(outcome),
                                      completion, tape, hh.ctypes.data_as(C.POINTER(SZ)),
                                      ww.ctypes.data_as(C.POINTER(SZ)), SCALAR[outputs_scalar], C.pointer(rows),
-                                     C.pointer(stats), _ptr(trace))
+                                     C.pointer(stats), _ptr(trace), bits, C.pointer(states), C.pointer(vectors))
     lib().ube_image_encode_pixels(C.byref(args))
     _check(outcome)
-    return Rows(rows, model.device), (stats.truncated, stats.tokens)
+    return _finish(model, rows, states, vectors, stats, bits)
 
 
 def video_encode_frames(model: Model, arena: Arena, data, offsets, frame_counts, heights, widths, *, stream=None,
-                        outputs_scalar="f32", completion=0, trace=None):
+                        outputs_scalar="f32", completion=0, trace=None, outputs=None):
     tape, off = _tape(data, offsets)
     ff = np.ascontiguousarray(frame_counts, dtype=np.uint64)
     hh = np.ascontiguousarray(heights, dtype=np.uint64)
     ww = np.ascontiguousarray(widths, dtype=np.uint64)
     rows, stats, outcome = ube_rows_view_t(), ube_encode_stats_t(), ube_outcome_t()
+    states, vectors, bits = ube_rows_tape_view_t(), ube_rows_tape_view_t(), _outputs_bits(outputs)
     args = ube_video_encode_frames_t(model.handle, arena.handle, _stream_handle(stream), C.pointer(outcome),
                                      completion, tape, ff.ctypes.data_as(C.POINTER(SZ)),
                                      hh.ctypes.data_as(C.POINTER(SZ)), ww.ctypes.data_as(C.POINTER(SZ)),
-                                     SCALAR[outputs_scalar], C.pointer(rows), C.pointer(stats), _ptr(trace))
+                                     SCALAR[outputs_scalar], C.pointer(rows), C.pointer(stats), _ptr(trace), bits,
+                                     C.pointer(states), C.pointer(vectors))
     lib().ube_video_encode_frames(C.byref(args))
     _check(outcome)
-    return Rows(rows, model.device), (stats.truncated, stats.tokens)
+    return _finish(model, rows, states, vectors, stats, bits)
 
 
 def encode(model: Model, arena: Arena, batch, **kw):

@@ -13,11 +13,11 @@ documentation's evaluation sets and checkpoints are not used.
 from __future__ import annotations
 
 DEFAULTS = dict(vocab=258, context=1024, rope_axes=1, rope_base=10000.0, rms_epsilon=1e-6,
-                patch_side=16, channels=3, quantization="bf16", modality="text")
+                patch_side=16, channels=3, quantization="bf16", modality="text", token_width=0)
 
 GEOMETRIES = {
-    "tiny": dict(depth=2, hidden=128, heads=2, ffn=512, vocab=256, context=1024),
-    "text512": dict(depth=12, hidden=512, heads=8, ffn=1536, vocab=258, context=1024),
+    "tiny": dict(depth=2, hidden=128, heads=2, ffn=512, vocab=256, context=1024, token_width=128),
+    "text512": dict(depth=12, hidden=512, heads=8, ffn=1536, vocab=258, context=1024, token_width=128),
     "image768": dict(depth=12, hidden=768, heads=12, ffn=2304, rope_axes=2, context=1024, modality="image"),
     "video1024": dict(depth=24, hidden=1024, heads=16, ffn=3072, rope_axes=3, context=2048, modality="video"),
     "video1024_e4m3": dict(depth=24, hidden=1024, heads=16, ffn=3072, rope_axes=3, context=2048,

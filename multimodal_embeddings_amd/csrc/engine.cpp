@@ -91,6 +91,7 @@ struct ube_model_handle_t {
     std::vector<Layer> layers;
     float *gf = nullptr, *u = nullptr;
     float2 *rope = nullptr;
+    uint16_t *tok = nullptr;  // token head, packed [token_width x D]
     int sec0 = 32, sec1 = 0;
 };
 
@@ -130,6 +131,8 @@ char const *check_geometry(ube_geometry_t const &g) {
     if (g.quantization == ube_scalar_e4m3_k && (g.hidden % 256 != 0 || g.ffn % 128 != 0))
         return "e4m3 blocks need hidden % 256 == 0 and ffn % 128 == 0";
     if (g.vocab > 65535) return "vocab too large";
+    if (g.token_width && (!row_width_supported(g.token_width) || g.token_width > 1024))
+        return "token_width must be a supported multiple of 128, <= 1024";
     return nullptr;
 }
 
@@ -210,6 +213,7 @@ extern "C" void ube_model_init(ube_model_init_t *a) {
             if (!w.w_qkv[l] || !w.w_o[l] || !w.w_gate[l] || !w.w_up[l] || !w.w_down[l] || !w.attn_norm[l] ||
                 !w.mlp_norm[l])
                 throw Failure{ube_status_invalid_argument_k, "missing block weights"};
+        if (g.token_width && !w.token_head) throw Failure{ube_status_invalid_argument_k, "missing token head"};
         int ndev = 0;
         if (hipGetDeviceCount(&ndev) != hipSuccess || a->device < 0 || a->device >= ndev)
             throw Failure{ube_status_device_k, "no such GPU"};
@@ -240,6 +244,7 @@ extern "C" void ube_model_init(ube_model_init_t *a) {
         }
         size_t o_gf = take(D * 4), o_u = take(H * D * 4), o_wv = take(D * D * 2);
         size_t o_rope = take(g.context * 32 * sizeof(float2));
+        size_t o_tok = g.token_width ? take(g.token_width * D * 2) : 0;
 
         std::vector<char> host(total);
         char *hb = host.data();
@@ -311,6 +316,7 @@ extern "C" void ube_model_init(ube_model_init_t *a) {
                 u[h * D + f] = (float)(acc / 8.0);
             }
         std::memcpy(hb + o_wv, w.pool_wv, D * D * 2);
+        if (g.token_width) transpose_into((uint16_t *)(hb + o_tok), w.token_head, D, g.token_width);
         // rotary table: (cos, sin) of p * base^(-2j/64), double on the host
         float2 *rope = (float2 *)(hb + o_rope);
         for (size_t p = 0; p < g.context; ++p)
@@ -345,6 +351,7 @@ extern "C" void ube_model_init(ube_model_init_t *a) {
         m->u = (float *)(db + o_u);
         m->wv = (uint16_t *)(db + o_wv);
         m->rope = (float2 *)(db + o_rope);
+        m->tok = g.token_width ? (uint16_t *)(db + o_tok) : nullptr;
         const int pairs = 32, axes = (int)g.rope_axes, base = pairs / axes, rem = pairs % axes;
         m->sec0 = base + (0 < rem ? 1 : 0);
         m->sec1 = axes >= 2 ? base + (1 < rem ? 1 : 0) : 0;
@@ -382,6 +389,7 @@ extern "C" void ube_model_describe(ube_model_describe_t *a) {
     d.quantization = m->g.quantization;
     d.memory_usage = m->bytes;
     d.device = m->device;
+    d.token_width = m->g.token_width;
     set_outcome(a->outcome, ube_status_success_k, nullptr);
 }
 
@@ -486,10 +494,19 @@ void make_tiles(Plan &p) {
 // Device regions of one call.
 struct Layout {
     size_t Tpad = 0;
-    size_t out, cu, src, tiles, media, input, x, h, a, qk, vt, o, xf, s, pos, patches, q8, qs, ss, total;
+    size_t out, cu, offs, src, tiles, media, input, x, h, a, qk, vt, o, xf, s, pos, patches, q8, qs, ss, st, tvf, tv,
+        total;
 };
 
-Layout carve(ube_geometry_t const &g, Plan const &p, bool media, size_t input_bytes, bool e4m3) {
+// Per-token surfaces of one call: fp32 states (bf16 states are the final-norm
+// rows themselves), token vectors.
+struct TokenOutputs {
+    bool states_f32 = false, vectors = false;
+    size_t width = 0, vector_bytes = 2;
+};
+
+Layout carve(ube_geometry_t const &g, Plan const &p, bool media, size_t input_bytes, bool e4m3,
+             TokenOutputs const &tok) {
     Layout L{};
     const size_t D = g.hidden, F = g.ffn, H = g.heads;
     L.Tpad = align_up(p.T, 256) + kRowPad;
@@ -501,6 +518,7 @@ Layout carve(ube_geometry_t const &g, Plan const &p, bool media, size_t input_by
     };
     L.out = take(std::max<size_t>(p.count, 1) * D * 4);
     L.cu = take((p.count + 1) * 4);
+    L.offs = take((p.count + 1) * 8);  // the token offsets as size_t, for rows tapes
     L.src = take(std::max<size_t>(p.count, 1) * 8);
     L.tiles = take(std::max<size_t>(p.tiles.size(), 1) * 8);
     L.media = take(media ? std::max<size_t>(p.count, 1) * sizeof(MediaItem) : 0);
@@ -518,6 +536,9 @@ Layout carve(ube_geometry_t const &g, Plan const &p, bool media, size_t input_by
     L.q8 = take(e4m3 ? L.Tpad * std::max(D, F) : 0);  // E4M3 GEMM input rows
     L.qs = take(e4m3 ? L.Tpad * 4 : 0);               // their per-row scales
     L.ss = take(L.Tpad * kSsParts * 4);               // partial sums of squares of x
+    L.st = take(tok.states_f32 ? L.Tpad * D * 4 : 0);
+    L.tvf = take(tok.vectors ? L.Tpad * tok.width * 4 : 0);  // token head output before normalisation
+    L.tv = take(tok.vectors ? L.Tpad * tok.width * tok.vector_bytes : 0);
     L.total = total;
     return L;
 }
@@ -556,7 +577,12 @@ struct EncodeRequest {
     void const *data;      // tape data
     size_t const *offsets; // host
     size_t count;
+    unsigned outputs;
+    ube_rows_tape_view_t *states;
+    ube_rows_tape_view_t *token_vectors;
 };
+
+bool wants(unsigned outputs, ube_outputs_t o) { return (outputs ? outputs : ube_outputs_embeddings_k) & o; }
 
 // Runs the whole encode for a prepared plan. `media` selects the patch frontend.
 void run_encode(EncodeRequest const &r, Plan &p, bool media) {
@@ -575,7 +601,13 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
         if (hi > ar->dev && lo < ar->dev + ar->cap)
             throw Failure{ube_status_invalid_argument_k, "inputs lie inside the arena"};
     }
-    Layout L = carve(g, p, media, input_bytes, m->e4m3);
+    const bool bf16_out = r.outputs_scalar == ube_scalar_bf16_k;
+    TokenOutputs tok;
+    tok.states_f32 = wants(r.outputs, ube_outputs_states_k) && !bf16_out;
+    tok.vectors = wants(r.outputs, ube_outputs_token_vectors_k);
+    tok.width = g.token_width;
+    tok.vector_bytes = bf16_out ? 2 : 4;
+    Layout L = carve(g, p, media, input_bytes, m->e4m3, tok);
 
     // grow the arena (only when outgrown)
     if (L.total > ar->cap) {
@@ -609,6 +641,7 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
     char *hp = ar->pinned;
     std::memset(hp, 0, meta_bytes);
     std::memcpy(hp + (L.cu - L.cu), p.cu.data(), p.cu.size() * 4);
+    for (size_t i = 0; i <= p.count; ++i) ((uint64_t *)(hp + (L.offs - L.cu)))[i] = (uint64_t)p.cu[i];
     for (size_t i = 0; i < p.count; ++i)
         ((int64_t *)(hp + (L.src - L.cu)))[i] = p.src[i] - (on_device ? 0 : (int64_t)p.input_lo);
     if (!p.tiles.empty()) std::memcpy(hp + (L.tiles - L.cu), p.tiles.data(), p.tiles.size() * 8);
@@ -719,36 +752,75 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
                 UBE_HIP(hipMemcpyAsync(r.trace + (l + 1) * (size_t)T * D, x, (size_t)T * D * 4,
                                        hipMemcpyDeviceToDevice, st));
         }
+        float *states = tok.states_f32 ? (float *)(db + L.st) : nullptr;
         timed(ube_kernel_final_norm_k, st,
-              [&] { return launch_final_norm_scores(x, m->gf, m->u, xf, s, T, D, H, eps, st); });
+              [&] { return launch_final_norm_scores(x, m->gf, m->u, xf, s, states, T, D, H, eps, st); });
+        if (tok.vectors) {
+            // token head (bf16 operands, fp32 rows), then unit rows
+            GemmArgs ta{};
+            ta.w = m->tok, ta.x = xf, ta.M = T, ta.N = (int)tok.width, ta.K = D;
+            ta.out_f32 = (float *)(db + L.tvf), ta.ld_f32 = (int)tok.width, ta.scale = 1.0f;
+            UBE_HIP(launch_gemm(kEpiPatch, ta, st));
+            UBE_HIP(launch_unit_rows((const float *)(db + L.tvf), db + L.tv, bf16_out ? 1 : 0, T, (int)tok.width, st));
+        }
     }
-    const bool bf16_out = r.outputs_scalar == ube_scalar_bf16_k;
     const size_t row_bytes = (size_t)D * (bf16_out ? 2 : 4);
-    if (p.count) {
+    const bool embeddings = wants(r.outputs, ube_outputs_embeddings_k);
+    if (p.count && embeddings) {
         timed(ube_kernel_pool_k, st, [&] {
             return launch_pool(xf, s, cu, (int)p.count, m->wv, db + L.out, bf16_out ? 1 : 0, row_bytes, D, H, st);
         });
     }
     if (r.completion == 0) UBE_HIP(hipStreamSynchronize(st));
     UBE_HIP(hipGetLastError());
-    *r.embeddings = ube_rows_view_t{p.count ? db + L.out : db + L.out, p.count, (size_t)D, row_bytes,
-                                    bf16_out ? ube_scalar_bf16_k : ube_scalar_f32_k};
+    const ube_scalar_t scalar = bf16_out ? ube_scalar_bf16_k : ube_scalar_f32_k;
+    if (r.embeddings) {
+        *r.embeddings = embeddings ? ube_rows_view_t{db + L.out, p.count, (size_t)D, row_bytes, scalar}
+                                   : ube_rows_view_t{nullptr, 0, 0, 0, ube_scalar_unknown_k};
+    }
+    size_t const *offs = (size_t const *)(db + L.offs);
+    if (r.states) {
+        *r.states = wants(r.outputs, ube_outputs_states_k)
+                        ? ube_rows_tape_view_t{bf16_out ? (void *)(db + L.xf) : (void *)(db + L.st), offs, p.count,
+                                               p.T, (size_t)D, row_bytes, scalar}
+                        : ube_rows_tape_view_t{nullptr, nullptr, 0, 0, 0, 0, ube_scalar_unknown_k};
+    }
+    if (r.token_vectors) {
+        *r.token_vectors = tok.vectors ? ube_rows_tape_view_t{db + L.tv, offs, p.count, p.T, tok.width,
+                                                              tok.width * tok.vector_bytes, scalar}
+                                       : ube_rows_tape_view_t{nullptr, nullptr, 0, 0, 0, 0, ube_scalar_unknown_k};
+    }
     if (r.stats) r.stats->truncated = p.truncated, r.stats->tokens = p.T;
 }
 
-void check_common(ube_model_t model, ube_arena_t arena, ube_rows_view_t *embeddings, ube_scalar_t outputs_scalar) {
-    if (!embeddings) throw Failure{ube_status_invalid_argument_k, "NULL embeddings output"};
+void check_common(ube_model_t model, ube_arena_t arena, ube_rows_view_t *embeddings, ube_scalar_t outputs_scalar,
+                  unsigned outputs, ube_rows_tape_view_t *states, ube_rows_tape_view_t *token_vectors) {
+    if (outputs & ~7u) throw Failure{ube_status_invalid_argument_k, "unknown output surface"};
+    if (!embeddings && wants(outputs, ube_outputs_embeddings_k))
+        throw Failure{ube_status_invalid_argument_k, "NULL embeddings output"};
+    if (!states && wants(outputs, ube_outputs_states_k))
+        throw Failure{ube_status_invalid_argument_k, "NULL states output"};
+    if (!token_vectors && wants(outputs, ube_outputs_token_vectors_k))
+        throw Failure{ube_status_invalid_argument_k, "NULL token vectors output"};
     if (!model) throw Failure{ube_status_invalid_argument_k, "NULL model"};
     if (!arena) throw Failure{ube_status_invalid_argument_k, "NULL arena"};
     if (outputs_scalar != ube_scalar_unknown_k && outputs_scalar != ube_scalar_f32_k &&
         outputs_scalar != ube_scalar_bf16_k)
         throw Failure{ube_status_invalid_argument_k, "outputs_scalar must be f32 or bf16"};
     if (arena->device != model->device) throw Failure{ube_status_device_k, "arena and model on different GPUs"};
+    if (wants(outputs, ube_outputs_token_vectors_k) && !model->g.token_width)
+        throw Failure{ube_status_unsupported_k, "the model has no token head"};
 }
 
 template <typename Body>
-void guarded(ube_outcome_t *outcome, ube_rows_view_t *embeddings, ube_arena_t arena, Body body) {
-    if (embeddings) *embeddings = ube_rows_view_t{nullptr, 0, 0, 0, ube_scalar_unknown_k};
+void guarded(ube_outcome_t *outcome, ube_rows_view_t *embeddings, ube_rows_tape_view_t *states,
+             ube_rows_tape_view_t *token_vectors, ube_arena_t arena, Body body) {
+    auto clear = [&] {
+        if (embeddings) *embeddings = ube_rows_view_t{nullptr, 0, 0, 0, ube_scalar_unknown_k};
+        if (states) *states = ube_rows_tape_view_t{nullptr, nullptr, 0, 0, 0, 0, ube_scalar_unknown_k};
+        if (token_vectors) *token_vectors = ube_rows_tape_view_t{nullptr, nullptr, 0, 0, 0, 0, ube_scalar_unknown_k};
+    };
+    clear();
     try {
         if (!arena) throw Failure{ube_status_invalid_argument_k, "NULL arena"};
         ArenaLease lease(arena);
@@ -757,10 +829,10 @@ void guarded(ube_outcome_t *outcome, ube_rows_view_t *embeddings, ube_arena_t ar
         body();
         set_outcome(outcome, ube_status_success_k, nullptr);
     } catch (Failure const &f) {
-        if (embeddings) *embeddings = ube_rows_view_t{nullptr, 0, 0, 0, ube_scalar_unknown_k};
+        clear();
         set_outcome(outcome, f.status, f.message);
     } catch (std::bad_alloc const &) {
-        if (embeddings) *embeddings = ube_rows_view_t{nullptr, 0, 0, 0, ube_scalar_unknown_k};
+        clear();
         set_outcome(outcome, ube_status_out_of_memory_k, "host out of memory");
     }
 }
@@ -769,8 +841,8 @@ void guarded(ube_outcome_t *outcome, ube_rows_view_t *embeddings, ube_arena_t ar
 
 extern "C" void ube_text_encode(ube_text_encode_t *a) {
     if (!a) return;
-    guarded(a->outcome, a->embeddings, a->arena, [&] {
-        check_common(a->model, a->arena, a->embeddings, a->outputs_scalar);
+    guarded(a->outcome, a->embeddings, a->states, a->token_vectors, a->arena, [&] {
+        check_common(a->model, a->arena, a->embeddings, a->outputs_scalar, a->outputs, a->states, a->token_vectors);
         if (!a->model->text) throw Failure{ube_status_unsupported_k, "the model has no byte frontend"};
         const size_t count = a->texts.count;
         if (count && (!a->texts.offsets || !a->texts.data))
@@ -797,7 +869,8 @@ extern "C" void ube_text_encode(ube_text_encode_t *a) {
         }
         make_tiles(p);
         EncodeRequest r{a->model, a->arena, (hipStream_t)a->stream, a->completion, a->outputs_scalar,
-                        a->embeddings, a->stats, a->trace_residual, a->texts.data, a->texts.offsets, count};
+                        a->embeddings, a->stats, a->trace_residual, a->texts.data, a->texts.offsets, count,
+                        a->outputs, a->states, a->token_vectors};
         run_encode(r, p, false);
     });
 }
@@ -806,8 +879,9 @@ namespace {
 
 void media_encode(ube_model_t model, ube_arena_t arena, void *stream, int completion, ube_tape_view_t tape,
                   size_t const *frame_counts, size_t const *heights, size_t const *widths, ube_scalar_t scalar,
-                  ube_rows_view_t *embeddings, ube_encode_stats_t *stats, float *trace, int axes_expected) {
-    check_common(model, arena, embeddings, scalar);
+                  ube_rows_view_t *embeddings, ube_encode_stats_t *stats, float *trace, int axes_expected,
+                  unsigned outputs, ube_rows_tape_view_t *states, ube_rows_tape_view_t *token_vectors) {
+    check_common(model, arena, embeddings, scalar, outputs, states, token_vectors);
     if (model->text) throw Failure{ube_status_unsupported_k, "the model has no patch frontend"};
     if ((int)model->g.rope_axes != axes_expected)
         throw Failure{ube_status_unsupported_k, "the model's rotary axes do not fit this input"};
@@ -840,7 +914,7 @@ void media_encode(ube_model_t model, ube_arena_t arena, void *stream, int comple
     if (count) p.input_lo = tape.offsets[0], p.input_hi = tape.offsets[count];
     make_tiles(p);
     EncodeRequest r{model, arena, (hipStream_t)stream, completion, scalar, embeddings, stats, trace, tape.data,
-                    tape.offsets, count};
+                    tape.offsets, count, outputs, states, token_vectors};
     run_encode(r, p, true);
 }
 
@@ -848,19 +922,55 @@ void media_encode(ube_model_t model, ube_arena_t arena, void *stream, int comple
 
 extern "C" void ube_image_encode_pixels(ube_image_encode_pixels_t *a) {
     if (!a) return;
-    guarded(a->outcome, a->embeddings, a->arena, [&] {
+    guarded(a->outcome, a->embeddings, a->states, a->token_vectors, a->arena, [&] {
         media_encode(a->model, a->arena, a->stream, a->completion, a->pixels, nullptr, a->heights, a->widths,
-                     a->outputs_scalar, a->embeddings, a->stats, a->trace_residual, 2);
+                     a->outputs_scalar, a->embeddings, a->stats, a->trace_residual, 2, a->outputs, a->states,
+                     a->token_vectors);
     });
 }
 
 extern "C" void ube_video_encode_frames(ube_video_encode_frames_t *a) {
     if (!a) return;
-    guarded(a->outcome, a->embeddings, a->arena, [&] {
+    guarded(a->outcome, a->embeddings, a->states, a->token_vectors, a->arena, [&] {
         if (a->frames.count && !a->frame_counts) throw Failure{ube_status_invalid_argument_k, "NULL frame counts"};
         media_encode(a->model, a->arena, a->stream, a->completion, a->frames, a->frame_counts, a->heights, a->widths,
-                     a->outputs_scalar, a->embeddings, a->stats, a->trace_residual, 3);
+                     a->outputs_scalar, a->embeddings, a->stats, a->trace_residual, 3, a->outputs, a->states,
+                     a->token_vectors);
     });
+}
+
+extern "C" void ube_maxsim(ube_maxsim_t *a) {
+    if (!a) return;
+    try {
+        auto const &q = a->queries, &d = a->documents;
+        if (!a->scores) throw Failure{ube_status_invalid_argument_k, "NULL scores"};
+        if ((q.count && (!q.offsets || (q.rows && !q.data))) || (d.count && (!d.offsets || (d.rows && !d.data))))
+            throw Failure{ube_status_invalid_argument_k, "NULL rows tape"};
+        if (q.columns != d.columns) throw Failure{ube_status_invalid_argument_k, "queries and documents differ in width"};
+        if (q.scalar != ube_scalar_bf16_k || d.scalar != ube_scalar_bf16_k)
+            throw Failure{ube_status_unsupported_k, "MaxSim takes bf16 rows"};
+        if (q.columns != 128 && q.columns != 256) throw Failure{ube_status_unsupported_k, "MaxSim width must be 128 or 256"};
+        if (q.stride % 16 || d.stride % 16 || q.stride < q.columns * 2 || d.stride < d.columns * 2 ||
+            ((uintptr_t)q.data % 16) || ((uintptr_t)d.data % 16))
+            throw Failure{ube_status_invalid_argument_k, "rows must be 16-byte aligned and hold `columns` values"};
+        if (q.count > 0x7fffffff || d.count > 0x7fffffff || q.count * d.count > ((size_t)1 << 40))
+            throw Failure{ube_status_invalid_argument_k, "too many pairs"};
+        const size_t ld = a->scores_stride ? a->scores_stride : d.count;
+        if (ld < d.count) throw Failure{ube_status_invalid_argument_k, "scores_stride below the document count"};
+        int ndev = 0;
+        if (hipGetDeviceCount(&ndev) != hipSuccess || a->device < 0 || a->device >= ndev)
+            throw Failure{ube_status_device_k, "no such GPU"};
+        UBE_HIP(hipSetDevice(a->device));
+        hipStream_t st = (hipStream_t)a->stream;
+        const size_t span = a->query_span ? a->query_span : 64;
+        UBE_HIP(launch_maxsim((const uint16_t *)q.data, q.offsets, q.rows, q.stride / 2, (int)q.count,
+                              (const uint16_t *)d.data, d.offsets, d.rows, d.stride / 2, (int)d.count, (int)q.columns,
+                              a->query_prefix, span, a->scores, ld, st));
+        if (a->completion == 0) UBE_HIP(hipStreamSynchronize(st));
+        set_outcome(a->outcome, ube_status_success_k, nullptr);
+    } catch (Failure const &f) {
+        set_outcome(a->outcome, f.status, f.message);
+    }
 }
 
 extern "C" char const *ube_status_name(ube_status_t s) {

@@ -82,7 +82,13 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, int ldqk, cons
 
 // Final RMSNorm -> xf (bf16) and pool scores s[t][h] = xf_t . u_h (fp32).
 hipError_t launch_final_norm_scores(const float *x, const float *gain, const float *u, uint16_t *xf, float *s,
-                                    int T, int D, int H, float eps, hipStream_t stream);
+                                    float *states, int T, int D, int H, float eps, hipStream_t stream);
+// rows of `in` [T x W] divided by their norms, into out as f32 or bf16
+hipError_t launch_unit_rows(const float *in, void *out, int out_bf16, int T, int W, hipStream_t stream);
+// hard MaxSim of every (query item, document item) pair; columns 128 or 256
+hipError_t launch_maxsim(const uint16_t *q, const size_t *qoff, size_t qrows, size_t qld, int nq, const uint16_t *d,
+                         const size_t *doff, size_t drows, size_t dld, int nd, int columns, size_t prefix, size_t span,
+                         float *scores, size_t ld, hipStream_t stream);
 
 // Per item: softmax of the scores over the item's tokens per head,
 // z_h = sum_t p_t,h xf_t, pooled_h = z_h W_v[:, head h]; empty items -> 0.

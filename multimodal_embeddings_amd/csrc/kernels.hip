@@ -199,7 +199,8 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, co
 template <int V, int C>
 __global__ __launch_bounds__(256) void k_final_norm_scores(const float *__restrict__ x, const float *__restrict__ gain,
                                                            const float *__restrict__ u, uint16_t *__restrict__ xf,
-                                                           float *__restrict__ s, int T, int D, int H, float eps) {
+                                                           float *__restrict__ s, float *__restrict__ states, int T,
+                                                           int D, int H, float eps) {
     extern __shared__ float su[];  // u [H x D]
     for (int i = threadIdx.x; i < H * D; i += 256) su[i] = u[i];
     __syncthreads();
@@ -222,6 +223,7 @@ __global__ __launch_bounds__(256) void k_final_norm_scores(const float *__restri
 #pragma unroll
             for (int i = 0; i < V; ++i) v[c][i] = v[c][i] * inv * gain[f + i];
             RowIO<V>::store_bf16(xf + (size_t)t * D + f, v[c]);
+            if (states) RowIO<V>::store_f32(states + (size_t)t * D + f, v[c]);
         }
         for (int hd = 0; hd < H; ++hd) {
             float dot = 0.f;
@@ -387,7 +389,7 @@ hipError_t launch_rmsnorm(const float *x, const float *gain, uint16_t *h, int T,
 }
 
 hipError_t launch_final_norm_scores(const float *x, const float *gain, const float *u, uint16_t *xf, float *s,
-                                    int T, int D, int H, float eps, hipStream_t stream) {
+                                    float *states, int T, int D, int H, float eps, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const size_t lds = (size_t)H * D * sizeof(float);
     UBE_ROW_DISPATCH(D, {
@@ -396,8 +398,45 @@ hipError_t launch_final_norm_scores(const float *x, const float *gain, const flo
                                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
         }
-        k_final_norm_scores<V, C><<<row_grid(T), 256, lds, stream>>>(x, gain, u, xf, s, T, D, H, eps);
+        k_final_norm_scores<V, C><<<row_grid(T), 256, lds, stream>>>(x, gain, u, xf, s, states, T, D, H, eps);
     });
+    return hipGetLastError();
+}
+
+// Token vectors: every fp32 row divided by its Euclidean norm (a zero row stays
+// zero), written as f32 or bf16.
+template <int V, int C>
+__global__ __launch_bounds__(256) void k_unit_rows(const float *__restrict__ in, void *__restrict__ out, int out_bf16,
+                                                   int T, int W) {
+    const int lane = threadIdx.x & 63;
+    const int waves = gridDim.x * 4;
+    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += waves) {
+        float v[C][V];
+        float ss = 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            RowIO<V>::load_f32(in + (size_t)t * W + c * 64 * V + lane * V, v[c]);
+#pragma unroll
+            for (int i = 0; i < V; ++i) ss += v[c][i] * v[c][i];
+        }
+        ss = wave_sum(ss);
+        const float inv = ss > 0.f ? 1.0f / sqrtf(ss) : 0.f;
+#pragma unroll
+        for (int c = 0; c < C; ++c) {
+            const int f = c * 64 * V + lane * V;
+#pragma unroll
+            for (int i = 0; i < V; ++i) v[c][i] *= inv;
+            if (out_bf16)
+                RowIO<V>::store_bf16((uint16_t *)out + (size_t)t * W + f, v[c]);
+            else
+                RowIO<V>::store_f32((float *)out + (size_t)t * W + f, v[c]);
+        }
+    }
+}
+
+hipError_t launch_unit_rows(const float *in, void *out, int out_bf16, int T, int W, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    UBE_ROW_DISPATCH(W, (k_unit_rows<V, C><<<row_grid(T), 256, 0, stream>>>(in, out, out_bf16, T, W)));
     return hipGetLastError();
 }
 
@@ -1328,6 +1367,83 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, int ldqk, cons
                             hipStream_t stream) {
     if (ntiles == 0) return hipSuccess;
     k_attention<<<ntiles * heads, 512, 0, stream>>>(q, k, ldqk, vt, ldvt, o, ldo, cu, tiles, ntiles);
+    return hipGetLastError();
+}
+
+// =========================================================== MaxSim
+//
+// Hard MaxSim of every (query item, document item) pair: one wave per pair.
+// The query's counted rows (64 per pass, zero past the end) are the MFMA B
+// operand, held in registers for the pass; the document's rows stream through
+// as the A operand in tiles of 32, straight from memory (16 bytes per lane: row
+// l32, k half hh). Output S^T: a lane holds 16 document rows of one query row,
+// so the running max stays in registers; the two lane halves are merged at the
+// end of the pass and the row maxima of the counted rows summed over the wave.
+template <int KS>  // columns / 16
+__global__ __launch_bounds__(256) void k_maxsim(const uint16_t *__restrict__ q, const size_t *__restrict__ qoff,
+                                                size_t qrows, size_t qld, int nq, const uint16_t *__restrict__ d,
+                                                const size_t *__restrict__ doff, size_t drows, size_t dld, int nd,
+                                                size_t prefix, size_t span, float *__restrict__ scores, size_t ld) {
+    const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
+    const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (pair >= (long)nq * nd) return;
+    const int i = (int)(pair / nd), j = (int)(pair % nd);
+    size_t q0 = min(qoff[i], qrows), q1 = min(qoff[i + 1], qrows);
+    size_t d0 = min(doff[j], drows), d1 = min(doff[j + 1], drows);
+    q1 = max(q0, q1), d1 = max(d0, d1);
+    const size_t qa = min(q0 + prefix, q1), qb = min(q1, qa + span);
+    float total = 0.f;
+    if (qb > qa && d1 > d0) {
+        for (size_t c0 = qa; c0 < qb; c0 += 64) {
+            bf16x8 qf[2][KS];
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const size_t r = c0 + b * 32 + l32;
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks)
+                    qf[b][ks] = r < qb ? __builtin_bit_cast(bf16x8, *(const u32x4 *)(q + r * qld + ks * 16 + hh * 8))
+                                       : bf16x8{};
+            }
+            float best[2] = {-INFINITY, -INFINITY};
+            for (size_t t0 = d0; t0 < d1; t0 += 32) {
+                const size_t r = min(t0 + l32, d1 - 1);  // rows past the end repeat the last one
+                f32x16 S[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const bf16x8 df = __builtin_bit_cast(bf16x8, *(const u32x4 *)(d + r * dld + ks * 16 + hh * 8));
+#pragma unroll
+                    for (int b = 0; b < 2; ++b)
+                        S[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(df, qf[b][ks], S[b], 0, 0, 0);
+                }
+#pragma unroll
+                for (int b = 0; b < 2; ++b)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) best[b] = fmaxf(best[b], S[b][e]);
+            }
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+                const float m = fmaxf(best[b], __shfl_xor(best[b], 32, 64));
+                const size_t r = c0 + b * 32 + l32;
+                total += (hh == 0 && r < qb) ? m : 0.f;
+            }
+        }
+        total = wave_sum(total) / (float)(qb - qa);
+    }
+    if (lane == 0) scores[(size_t)i * ld + j] = total;
+}
+
+hipError_t launch_maxsim(const uint16_t *q, const size_t *qoff, size_t qrows, size_t qld, int nq, const uint16_t *d,
+                         const size_t *doff, size_t drows, size_t dld, int nd, int columns, size_t prefix, size_t span,
+                         float *scores, size_t ld, hipStream_t stream) {
+    if (nq == 0 || nd == 0) return hipSuccess;
+    const long pairs = (long)nq * nd;
+    const int blocks = (int)((pairs + 3) / 4);
+    if (columns == 128)
+        k_maxsim<8><<<blocks, 256, 0, stream>>>(q, qoff, qrows, qld, nq, d, doff, drows, dld, nd, prefix, span, scores, ld);
+    else if (columns == 256)
+        k_maxsim<16><<<blocks, 256, 0, stream>>>(q, qoff, qrows, qld, nq, d, doff, drows, dld, nd, prefix, span, scores, ld);
+    else
+        return hipErrorInvalidValue;
     return hipGetLastError();
 }
 

@@ -97,6 +97,8 @@ def make_weights(geometry: dict, seed: int = 0, std: float = 0.02,
     put("pool_query", (D,))
     put("pool_wk", (D, D))
     put("pool_wv", (D, D))
+    if g.get("token_width"):
+        put("token_head", (D, g["token_width"]))
 
     grng = np.random.default_rng(gain_seed)
 
