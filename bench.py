@@ -34,7 +34,10 @@ WORKLOAD_TEXT = {
     "image": "image encoder depth 12, hidden 768, 12 heads, 2-axis rotary; 128 images 256x256x3 (256 patches)",
     "video": "video encoder depth 24, hidden 1024, 16 heads, 3-axis rotary; 16 clips 8x224x224x3 (1568 patches)",
     "video_e4m3": "video encoder as above with E4M3 blocks (per-tensor weight scales, per-row activation scales)",
+    "maxsim": "hard MaxSim of a 256 x 256 band: token vectors (width 128, bf16) of the first 256 rows of the "
+              "1024-byte text batch, queries the first 64 tokens of each row, documents all 1024",
 }
+MAXSIM_ITEMS = 256
 
 
 def kernel_flops_per_launch(kernel, g, T, lengths):
@@ -87,6 +90,66 @@ def cpu_baseline(workload, weights, batch, rows):
             "sample": f"items {list(rows)} of the {workload} batch ({units} bytes, float64 oracle, {dt:.1f} s)"}
 
 
+def bench_maxsim(args):
+    """Times the MaxSim scorer on token vectors the encoder produced (outside the timed region)."""
+    import torch
+    import multimodal_embeddings_amd as ube
+    from multimodal_embeddings_amd import configs, synth
+    g = configs.geometry("text512")
+    weights = synth.make_weights(g)
+    batch = synth.subset(synth.workload_inputs("throughput"), list(range(MAXSIM_ITEMS)))
+    model, arena = ube.Model(weights, 0), ube.Arena(0)
+    _, _, vecs, _ = ube.text_encode(model, arena, torch.from_numpy(batch.data).to("cuda:0"), batch.offsets,
+                                    outputs_scalar="bf16", outputs=("token_vectors",))
+    v = vecs.tensor()
+    off_h = vecs.offsets()
+    off = torch.from_numpy(off_h.astype(np.int64)).to("cuda:0")
+    tape = ube.rows_tape(v, off)
+    n = MAXSIM_ITEMS
+    scores = torch.empty((n, n), dtype=torch.float32, device="cuda:0")
+    stream = torch.cuda.current_stream()
+    span = 64
+    qrows = np.minimum(np.diff(off_h.astype(np.int64)), span)
+    drows = np.diff(off_h.astype(np.int64))
+    flops = 2.0 * float(qrows.sum()) * float(drows.sum()) * g["token_width"]
+    for _ in range(args.warmup):
+        ube.maxsim(tape, tape, scores, span=span, completion=1, stream=stream)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        ube.maxsim(tape, tape, scores, span=span, completion=1, stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    achieved = flops / (ms / 1e3) / 1e12
+    out = {
+        "metric": "MaxSim query-document pairs/sec (256 x 256 band, 64 query tokens x 1024 document tokens, width 128)",
+        "value": n * n / (ms / 1e3), "unit": "pairs/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (token vectors of the seeded 1024-byte text batch, random-init weights)",
+        "config": {"workload": f"maxsim: {WORKLOAD_TEXT['maxsim']}", "pairs": n * n, "parallelism": "1 GPU"},
+        "roofline": {"kernel": "maxsim", "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16 / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved / (PEAK_BF16 / 1e12), "traffic": None,
+                     "avg_launch_ms": ms, "launches": args.steps},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        host = v.float().cpu().numpy().astype(np.float64)
+        nq = 64
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        oracle.maxsim(host, off_h[:nq + 1], host, off_h, prefix=0, span=span)
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": nq * n / dt, "unit": "pairs/s", "cores": threads, "kind": "oracle",
+                               "sample": f"queries 0-{nq - 1} against all {n} documents (float64 oracle, {dt:.1f} s)"}
+    else:
+        out["cpu_baseline"] = None
+    arena.close()
+    model.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -106,6 +169,9 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported in this build "
               "(items are independent; a multi-GPU run would shard the tape by items)", file=sys.stderr)
         sys.exit(2)
+
+    if args.workload == "maxsim":
+        return bench_maxsim(args)
 
     import torch
     import multimodal_embeddings_amd as ube
