@@ -1372,29 +1372,58 @@ hipError_t launch_attention(const uint16_t *q, const uint16_t *k, int ldqk, cons
 
 // =========================================================== MaxSim
 //
-// Hard MaxSim of every (query item, document item) pair: one wave per pair.
-// The query's counted rows (64 per pass, zero past the end) are the MFMA B
-// operand, held in registers for the pass; the document's rows stream through
-// as the A operand in tiles of 32, straight from memory (16 bytes per lane: row
-// l32, k half hh). Output S^T: a lane holds 16 document rows of one query row,
-// so the running max stays in registers; the two lane halves are merged at the
-// end of the pass and the row maxima of the counted rows summed over the wave.
+// Hard MaxSim of every (query item, document item) pair. Workgroup = one
+// document and four queries (one per wave): the document's rows pass through
+// LDS once, in double-buffered tiles of 32 rows filled by DMA, and all four
+// waves score them. Each wave holds its query's counted rows (64 per pass, zero
+// past the end) as the MFMA B operand in registers and reads the document tile
+// as the A operand (16-byte chunks XOR-swizzled by row % 16: conflict-free).
+// Output S^T: a lane holds 16 document rows of one query row, so the running max
+// stays in registers; the two lane halves are merged at the end of a pass and
+// the wave sums the counted rows. Document rows past the end repeat the last
+// row, which cannot change a maximum.
 template <int KS>  // columns / 16
 __global__ __launch_bounds__(256) void k_maxsim(const uint16_t *__restrict__ q, const size_t *__restrict__ qoff,
                                                 size_t qrows, size_t qld, int nq, const uint16_t *__restrict__ d,
                                                 const size_t *__restrict__ doff, size_t drows, size_t dld, int nd,
                                                 size_t prefix, size_t span, float *__restrict__ scores, size_t ld) {
-    const int lane = threadIdx.x & 63, l32 = lane & 31, hh = lane >> 5;
-    const long pair = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (pair >= (long)nq * nd) return;
-    const int i = (int)(pair / nd), j = (int)(pair % nd);
-    size_t q0 = min(qoff[i], qrows), q1 = min(qoff[i + 1], qrows);
-    size_t d0 = min(doff[j], drows), d1 = min(doff[j + 1], drows);
-    q1 = max(q0, q1), d1 = max(d0, d1);
-    const size_t qa = min(q0 + prefix, q1), qb = min(q1, qa + span);
+    constexpr int CH = 2 * KS;        // 16-byte chunks per row
+    constexpr int TILE = 32 * CH;     // chunks per tile of 32 rows
+    constexpr int LPT = TILE / 256;   // DMA loads per thread per tile
+    __shared__ __attribute__((aligned(1024))) u32x4 sD[2 * TILE];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+    const int groups = (nq + 3) / 4;
+    const int j = blockIdx.x / groups, grp = blockIdx.x % groups;
+    // counted rows [qa, qb) of query grp*4 + w; empty past nq
+    auto query_rows = [&](int w, size_t &qa, size_t &qb) {
+        const int i = grp * 4 + w;
+        qa = qb = 0;
+        if (i >= nq) return;
+        size_t q0 = min(qoff[i], qrows), q1 = max(q0, min(qoff[i + 1], qrows));
+        qa = min(q0 + prefix, q1), qb = min(q1, qa + span);
+    };
+    size_t qa, qb;
+    query_rows(wave, qa, qb);
+    int passes = 0;  // uniform over the workgroup
+    for (int w = 0; w < 4; ++w) {
+        size_t a, b;
+        query_rows(w, a, b);
+        passes = max(passes, (int)((b - a + 63) / 64));
+    }
+    const size_t d0 = min(doff[j], drows), d1 = max(d0, min(doff[j + 1], drows));
+    const int ntiles = (int)((d1 - d0 + 31) / 32);
     float total = 0.f;
-    if (qb > qa && d1 > d0) {
-        for (size_t c0 = qa; c0 < qb; c0 += 64) {
+    if (ntiles > 0) {
+        auto issue = [&](int t, int buf) {
+#pragma unroll
+            for (int r = 0; r < LPT; ++r) {
+                const int p = r * 256 + tid, row = p / CH, c = (p % CH) ^ (row & 15);
+                const size_t src = min(d0 + (size_t)t * 32 + row, d1 - 1);
+                lds_dma16(d + src * dld + c * 8, sD + buf * TILE + r * 256 + wave * 64);
+            }
+        };
+        for (int pass = 0; pass < passes; ++pass) {
+            const size_t c0 = qa + (size_t)pass * 64;
             bf16x8 qf[2][KS];
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
@@ -1405,12 +1434,21 @@ __global__ __launch_bounds__(256) void k_maxsim(const uint16_t *__restrict__ q, 
                                        : bf16x8{};
             }
             float best[2] = {-INFINITY, -INFINITY};
-            for (size_t t0 = d0; t0 < d1; t0 += 32) {
-                const size_t r = min(t0 + l32, d1 - 1);  // rows past the end repeat the last one
+            issue(0, 0);
+            for (int t = 0; t < ntiles; ++t) {
+                if (t + 1 < ntiles) {
+                    issue(t + 1, (t + 1) & 1);
+                    if constexpr (LPT == 2) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+                    else asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+                } else {
+                    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+                }
+                lds_barrier();
+                const u32x4 *tile = sD + (t & 1) * TILE;
                 f32x16 S[2] = {f32x16{}, f32x16{}};
 #pragma unroll
                 for (int ks = 0; ks < KS; ++ks) {
-                    const bf16x8 df = __builtin_bit_cast(bf16x8, *(const u32x4 *)(d + r * dld + ks * 16 + hh * 8));
+                    const bf16x8 df = __builtin_bit_cast(bf16x8, tile[l32 * CH + ((ks * 2 + hh) ^ (l32 & 15))]);
 #pragma unroll
                     for (int b = 0; b < 2; ++b)
                         S[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(df, qf[b][ks], S[b], 0, 0, 0);
@@ -1419,6 +1457,8 @@ __global__ __launch_bounds__(256) void k_maxsim(const uint16_t *__restrict__ q, 
                 for (int b = 0; b < 2; ++b)
 #pragma unroll
                     for (int e = 0; e < 16; ++e) best[b] = fmaxf(best[b], S[b][e]);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                lds_barrier();
             }
 #pragma unroll
             for (int b = 0; b < 2; ++b) {
@@ -1427,17 +1467,19 @@ __global__ __launch_bounds__(256) void k_maxsim(const uint16_t *__restrict__ q, 
                 total += (hh == 0 && r < qb) ? m : 0.f;
             }
         }
-        total = wave_sum(total) / (float)(qb - qa);
+        total = qb > qa ? wave_sum(total) / (float)(qb - qa) : 0.f;
     }
-    if (lane == 0) scores[(size_t)i * ld + j] = total;
+    const int i = grp * 4 + wave;
+    if (i < nq && lane == 0) scores[(size_t)i * ld + j] = total;
 }
 
 hipError_t launch_maxsim(const uint16_t *q, const size_t *qoff, size_t qrows, size_t qld, int nq, const uint16_t *d,
                          const size_t *doff, size_t drows, size_t dld, int nd, int columns, size_t prefix, size_t span,
                          float *scores, size_t ld, hipStream_t stream) {
     if (nq == 0 || nd == 0) return hipSuccess;
-    const long pairs = (long)nq * nd;
-    const int blocks = (int)((pairs + 3) / 4);
+    const long blocks_l = (long)((nq + 3) / 4) * nd;
+    if (blocks_l > 0x7fffffffL) return hipErrorInvalidValue;
+    const int blocks = (int)blocks_l;
     if (columns == 128)
         k_maxsim<8><<<blocks, 256, 0, stream>>>(q, qoff, qrows, qld, nq, d, doff, drows, dld, nd, prefix, span, scores, ld);
     else if (columns == 256)
