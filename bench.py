@@ -30,6 +30,8 @@ PEAK_HBM = 8.0e12       # bytes/s
 WORKLOAD_TEXT = {
     "throughput": "text encoder depth 12, hidden 512, 8 heads x 64, ffn 1536, 1-axis rotary; 1024 rows x 1024 bytes",
     "ragged": "text encoder depth 12, hidden 512; 64 rows, lengths 1..1024, printable ASCII",
+    "long": "text encoder depth 12, hidden 512, context 4096; 256 rows x 4096 bytes",
+    "packed": "text encoder depth 12, hidden 512; 4096 segments, lengths 32..512, printable ASCII",
     "tiny": "tiny encoder depth 2, hidden 128; 8 rows, lengths 16..64",
     "image": "image encoder depth 12, hidden 768, 12 heads, 2-axis rotary; 128 images 256x256x3 (256 patches)",
     "video": "video encoder depth 24, hidden 1024, 16 heads, 3-axis rotary; 16 clips 8x224x224x3 (1568 patches)",
@@ -79,7 +81,7 @@ def cpu_baseline(workload, weights, batch, rows):
     sub = synth.subset(batch, rows)
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    if workload in ("throughput", "ragged", "tiny"):
+    if workload in ("throughput", "ragged", "tiny", "long", "packed"):
         _, stats = oracle.encode_text(weights, sub.data, sub.offsets)
         units = stats[1]
     else:
@@ -158,7 +160,7 @@ def main():
     ap.add_argument("--workload", default="throughput", choices=sorted(WORKLOAD_TEXT))
     ap.add_argument("--kernel", default="gemm_gate_up", help="dominant kernel for the roofline entry")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", default=",".join(str(i) for i in range(24)))
+    ap.add_argument("--cpu-rows", default=None, help="items the CPU oracle encodes (default: ~10-30 s of work)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="first copy MIB MiB device-to-device 3 times (a plain copy kernel of known size, "
                          "for calibrating HBM byte counters)")
@@ -265,7 +267,9 @@ def main():
     if per_kernel:
         out["per_kernel_ms"] = per_kernel
     if not args.no_cpu_baseline:
-        rows_s = [int(r) for r in args.cpu_rows.split(",") if r != ""]
+        default_rows = {"long": 1, "packed": 96, "image": 8, "video": 1, "video_e4m3": 1}.get(args.workload, 24)
+        rows_s = ([int(r) for r in args.cpu_rows.split(",") if r != ""] if args.cpu_rows is not None
+                  else list(range(min(default_rows, batch.count))))
         out["cpu_baseline"] = cpu_baseline(args.workload, weights, batch, rows_s)
     else:
         out["cpu_baseline"] = None

@@ -18,6 +18,7 @@ DEFAULTS = dict(vocab=258, context=1024, rope_axes=1, rope_base=10000.0, rms_eps
 GEOMETRIES = {
     "tiny": dict(depth=2, hidden=128, heads=2, ffn=512, vocab=256, context=1024, token_width=128),
     "text512": dict(depth=12, hidden=512, heads=8, ffn=1536, vocab=258, context=1024, token_width=128),
+    "text512_4k": dict(depth=12, hidden=512, heads=8, ffn=1536, vocab=258, context=4096, token_width=128),
     "image768": dict(depth=12, hidden=768, heads=12, ffn=2304, rope_axes=2, context=1024, modality="image"),
     "video1024": dict(depth=24, hidden=1024, heads=16, ffn=3072, rope_axes=3, context=2048, modality="video"),
     "video1024_e4m3": dict(depth=24, hidden=1024, heads=16, ffn=3072, rope_axes=3, context=2048,
@@ -31,6 +32,10 @@ WORKLOADS = {
     "ragged_trunc": dict(geometry="text512", input="text", count=64, len_lo=1, len_hi=2049, byte_lo=32,
                          byte_hi=127),
     "throughput": dict(geometry="text512", input="text", count=1024, fixed_length=1024, byte_lo=0, byte_hi=256),
+    # the pages' text-only row width: 4096-byte rows, attention about half the flops
+    "long": dict(geometry="text512_4k", input="text", count=256, fixed_length=4096, byte_lo=0, byte_hi=256),
+    # many short segments (the pages pack sentences of a few hundred bytes), about the throughput token budget
+    "packed": dict(geometry="text512", input="text", count=4096, len_lo=32, len_hi=513, byte_lo=32, byte_hi=127),
     "image": dict(geometry="image768", input="media", count=128, frames=1, height=256, width=256),
     "video": dict(geometry="video1024", input="media", count=16, frames=8, height=224, width=224),
     "video_e4m3": dict(geometry="video1024_e4m3", input="media", count=16, frames=8, height=224, width=224),

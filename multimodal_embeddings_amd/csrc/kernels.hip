@@ -895,7 +895,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
     for (int tm = 0; tm < 4; ++tm) {
         const int m = m0 + wm * 128 + tm * 32 + l32;
         if (ss_early) ssv[tm] = *(const f32x4 *)(a.ss_in + (size_t)m * kSsParts);
-        if (EPI == kEpiQkv) pw[tm] = *(const u32x2 *)(a.pos + (size_t)m * 4);
+        // rows past M hold whatever an earlier call left in the arena: their
+        // positions must not index the rotary table
+        if (EPI == kEpiQkv && m < a.M) pw[tm] = *(const u32x2 *)(a.pos + (size_t)m * 4);
     }
 
     f32x16 acc[2][4];

@@ -245,3 +245,50 @@ def test_video_e4m3_full_batch_sampled_parity(ube):
     _, _, full_bf16 = _video_full(ube, "video1024")
     say(f"  e4m3 vs bf16 run, all clips: min cos {row_cos(full, full_bf16).min():.5f}")
     check_pooled(full[[0]], want, "video-e4m3", e4m3=True)
+
+
+# ------------------------------------------------------------------ 4096-byte rows, packed segments
+
+
+def test_long_rows_at_depth_2_all_rows(ube):
+    """Context 4096 (the pages' text row width): full, partial and truncated rows."""
+    g = dict(configs.geometry("text512_4k"))
+    g["depth"] = 2
+    w = synth.make_weights(g)
+    model, arena = ube.Model(w, 0), ube.Arena(0)
+    rng = np.random.default_rng(11)
+    lengths = [4096, 2500, 5000, 1]
+    data = rng.integers(0, 256, sum(lengths), dtype=np.uint8)
+    offsets = np.zeros(len(lengths) + 1, np.uint64)
+    offsets[1:] = np.cumsum(lengths)
+    rows, stats = ube.text_encode(model, arena, device_bytes(data), offsets)
+    want, ostats = oracle.encode_text(w, data, offsets)
+    assert stats == ostats == (1, 4096 + 2500 + 4096 + 1)
+    check_pooled(_pooled(rows), want, "long depth 2")
+    arena.close()
+    model.close()
+
+
+def test_long_rows_sampled(ube):
+    w, model, arena = _model(ube, "text512_4k")
+    batch = synth.workload_inputs("long")
+    rows, stats = ube.text_encode(model, arena, device_bytes(batch.data), batch.offsets)
+    assert stats == (0, 256 * 4096)
+    got = _pooled(rows)
+    sub = synth.subset(batch, [0])
+    want, _ = oracle.encode_text(w, sub.data, sub.offsets)
+    check_pooled(got[[0]], want, "long")
+
+
+def test_packed_segments_sampled_and_batch_invariant(ube):
+    w, model, arena = _model(ube, "text512")
+    batch = synth.workload_inputs("packed")
+    rows, stats = ube.text_encode(model, arena, device_bytes(batch.data), batch.offsets)
+    got = _pooled(rows)
+    pick = [0, 1, 1000, 2047, 4095]
+    sub = synth.subset(batch, pick)
+    want, _ = oracle.encode_text(w, sub.data, sub.offsets)
+    check_pooled(got[pick], want, "packed")
+    # the same segments encoded alone give the same rows, bit for bit
+    alone, _ = ube.text_encode(model, arena, device_bytes(sub.data), sub.offsets)
+    np.testing.assert_array_equal(_pooled(alone), got[pick])
