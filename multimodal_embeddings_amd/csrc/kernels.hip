@@ -196,6 +196,27 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, co
     }
 }
 
+// Sums HP per-lane values over the 64 lanes of a wave at once: each exchange
+// step halves the values a lane keeps (lane bits 5, 4, ... pick the half), the
+// remaining steps finish the sums. Lane L then holds the total of value
+// L / (64 / HP).
+template <int HP>
+__device__ __forceinline__ float lanes_reduce(const float (&p)[HP], int lane) {
+    float cur[HP];
+#pragma unroll
+    for (int j = 0; j < HP; ++j) cur[j] = p[j];
+    int m = 32;
+#pragma unroll
+    for (int n = HP; n > 1; n >>= 1, m >>= 1) {
+        const bool up = lane & m;
+#pragma unroll
+        for (int j = 0; j < n / 2; ++j)
+            cur[j] = (up ? cur[n / 2 + j] : cur[j]) + __shfl_xor(up ? cur[j] : cur[n / 2 + j], m, 64);
+    }
+    for (; m >= 1; m >>= 1) cur[0] += __shfl_xor(cur[0], m, 64);
+    return cur[0];
+}
+
 template <int V, int C>
 __global__ __launch_bounds__(256) void k_final_norm_scores(const float *__restrict__ x, const float *__restrict__ gain,
                                                            const float *__restrict__ u, uint16_t *__restrict__ xf,
@@ -225,16 +246,30 @@ __global__ __launch_bounds__(256) void k_final_norm_scores(const float *__restri
             RowIO<V>::store_bf16(xf + (size_t)t * D + f, v[c]);
             if (states) RowIO<V>::store_f32(states + (size_t)t * D + f, v[c]);
         }
-        for (int hd = 0; hd < H; ++hd) {
+        // pool scores of up to 16 heads reduced together (lanes_reduce)
+        float dots[16];
+#pragma unroll
+        for (int hd = 0; hd < 16; ++hd) {
             float dot = 0.f;
+            if (hd < H) {
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
-                const int f = c * 64 * V + lane * V;
+                for (int c = 0; c < C; ++c) {
+                    const int f = c * 64 * V + lane * V;
 #pragma unroll
-                for (int i = 0; i < V; ++i) dot += v[c][i] * su[hd * D + f + i];
+                    for (int i = 0; i < V; ++i) dot += v[c][i] * su[hd * D + f + i];
+                }
             }
-            dot = wave_sum(dot);
-            if (lane == 0) s[(size_t)t * H + hd] = dot;
+            dots[hd] = dot;
+        }
+        if (H <= 8) {
+            float d8[8];
+#pragma unroll
+            for (int hd = 0; hd < 8; ++hd) d8[hd] = dots[hd];
+            const float tot = lanes_reduce<8>(d8, lane);
+            if ((lane & 7) == 0 && (lane >> 3) < H) s[(size_t)t * H + (lane >> 3)] = tot;
+        } else {
+            const float tot = lanes_reduce<16>(dots, lane);
+            if ((lane & 3) == 0 && (lane >> 2) < H) s[(size_t)t * H + (lane >> 2)] = tot;
         }
     }
 }
