@@ -84,3 +84,31 @@ def encode_flops(g: dict, lengths) -> float:
     # then per item the H x (D x 64) value projection.
     total += 2.0 * T * H * D * 2 + 2.0 * len(lengths) * D * D
     return total
+
+
+# Contrastive (SigLIP-form, Matryoshka) loss over pooled embeddings: one device's anchors scored against
+# every item of the step. ``items`` embeddings of width ``columns``; anchors are items
+# [anchor_begin, anchor_begin + anchors); the positives pair item 2k with 2k + 1, and every anchor also
+# carries ``hard`` named repel edges and ``ignored`` ignore edges. Starting temperature and bias as the
+# pages derive them for the sigmoid form (10 and -10).
+SIGLIP_WORKLOADS = {
+    "siglip_tiny": dict(items=40, columns=128, anchor_begin=0, anchors=40, widths=(64, 128), hard=1, ignored=1),
+    "siglip_small": dict(items=300, columns=256, anchor_begin=0, anchors=300, widths=(64, 128, 256), hard=2,
+                         ignored=1),
+    "siglip_offset": dict(items=520, columns=256, anchor_begin=130, anchors=200, widths=(64, 192), hard=2,
+                          ignored=2),
+    # the encoder's own pooled width over a packed step of 4096 segments, every item an anchor
+    "siglip_pooled": dict(items=4096, columns=512, anchor_begin=0, anchors=4096, widths=(64, 128, 256, 512),
+                          hard=2, ignored=1),
+    # one device's band of a 72-device domain: 1024 anchors against 72 x 1024 gathered 1024-d embeddings
+    "siglip_band": dict(items=73728, columns=1024, anchor_begin=0, anchors=1024, widths=(64, 128, 256, 512, 1024),
+                        hard=2, ignored=1),
+}
+SIGLIP_TEMPERATURE = 10.0
+SIGLIP_BIAS = -10.0
+
+
+def siglip_flops(items: int, anchors: int, columns: int) -> float:
+    """Algorithmic MFMA flops of one loss + gradient pass: the anchor-by-item products at full width,
+    then the two gradient contractions (rows and columns), each 2 * anchors * items * columns."""
+    return 3.0 * 2.0 * anchors * items * columns

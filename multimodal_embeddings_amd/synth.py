@@ -206,3 +206,89 @@ def subset(batch, rows):
     if isinstance(batch, TextBatch):
         return TextBatch(data, offsets)
     return MediaBatch(data, offsets, batch.heights[rows], batch.widths[rows], batch.frames[rows])
+
+
+# --------------------------------------------------------------------------- contrastive loss inputs
+
+
+class Edges:
+    """One edge set in compressed-row form over the anchors: ``offsets`` (anchors + 1, uint64),
+    ``ids`` (uint32 item indices, ascending and unique within each run) and optional float32 ``weights``."""
+
+    def __init__(self, offsets, ids, weights=None):
+        self.offsets = np.ascontiguousarray(offsets, dtype=np.uint64)
+        self.ids = np.ascontiguousarray(ids, dtype=np.uint32)
+        self.weights = None if weights is None else np.ascontiguousarray(weights, dtype=np.float32)
+
+    @staticmethod
+    def from_lists(lists, weights=None):
+        offsets = np.zeros(len(lists) + 1, dtype=np.uint64)
+        offsets[1:] = np.cumsum([len(x) for x in lists]).astype(np.uint64) if lists else []
+        ids = np.concatenate([np.asarray(x, dtype=np.uint32) for x in lists]) if lists else np.zeros(0, np.uint32)
+        w = None
+        if weights is not None:
+            w = np.concatenate([np.asarray(x, dtype=np.float32) for x in weights]) if weights else \
+                np.zeros(0, np.float32)
+        return Edges(offsets, ids, w)
+
+    def runs(self):
+        off = self.offsets.astype(np.int64)
+        for p in range(len(off) - 1):
+            ids = self.ids[off[p]:off[p + 1]]
+            w = self.weights[off[p]:off[p + 1]] if self.weights is not None else np.ones(len(ids), np.float32)
+            yield p, ids, w
+
+
+class SiglipBatch:
+    """Pooled embeddings (bf16 bits and their exact float32 values) plus the relations of one step."""
+
+    def __init__(self, emb_bits, anchor_begin, anchors, attract, repel, ignore):
+        self.emb_bits = np.ascontiguousarray(emb_bits, dtype=np.uint16)
+        self.emb = bf16_bits_to_f32(self.emb_bits)
+        self.anchor_begin = int(anchor_begin)
+        self.anchors = int(anchors)
+        self.attract, self.repel, self.ignore = attract, repel, ignore
+
+    @property
+    def items(self):
+        return self.emb_bits.shape[0]
+
+    @property
+    def columns(self):
+        return self.emb_bits.shape[1]
+
+
+def siglip_batch(items, columns, anchor_begin, anchors, hard=2, ignored=1, seed=1, weighted=True):
+    """Seeded contrastive step: items 2k and 2k + 1 are views of one latent (cosine about 0.8), row norms
+    spread over [0.5, 2]; anchor p attracts its partner (and, one time in four, a second random positive),
+    repels ``hard`` random items with weights in [0.5, 2] and ignores ``ignored`` random items (which may
+    coincide with named edges, so precedence is exercised)."""
+    rng = np.random.default_rng(seed)
+    latent = rng.standard_normal(size=((items + 1) // 2, columns), dtype=np.float32)
+    view = rng.standard_normal(size=(items, columns), dtype=np.float32)
+    emb = latent[np.arange(items) // 2] + np.float32(0.5) * view
+    emb /= np.linalg.norm(emb, axis=1, keepdims=True) / np.float32(np.sqrt(columns))
+    emb *= rng.uniform(0.5, 2.0, size=(items, 1)).astype(np.float32) / np.float32(np.sqrt(columns))
+    bits = to_bf16_bits(emb)
+    att, att_w, rep, rep_w, ign = [], [], [], [], []
+    for p in range(anchors):
+        i = anchor_begin + p
+        pos = {i ^ 1} if (i ^ 1) < items else set()
+        if rng.random() < 0.25:
+            pos.add(int(rng.integers(0, items)))
+        neg = set(int(x) for x in rng.integers(0, items, size=hard))
+        skip = set(int(x) for x in rng.integers(0, items, size=ignored))
+        a, r, s = sorted(pos), sorted(neg), sorted(skip)
+        att.append(a)
+        rep.append(r)
+        ign.append(s)
+        att_w.append(rng.uniform(0.5, 2.0, size=len(a)) if weighted else np.ones(len(a)))
+        rep_w.append(rng.uniform(0.5, 2.0, size=len(r)) if weighted else np.ones(len(r)))
+    return SiglipBatch(bits.reshape(items, columns), anchor_begin, anchors,
+                       Edges.from_lists(att, att_w), Edges.from_lists(rep, rep_w), Edges.from_lists(ign))
+
+
+def siglip_workload(name: str, seed: int = 1) -> SiglipBatch:
+    wl = configs.SIGLIP_WORKLOADS[name]
+    return siglip_batch(wl["items"], wl["columns"], wl["anchor_begin"], wl["anchors"], wl["hard"], wl["ignored"],
+                        seed=seed)
