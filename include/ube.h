@@ -318,6 +318,81 @@ typedef struct ube_maxsim_t {
 } ube_maxsim_t;
 void ube_maxsim(ube_maxsim_t *arguments);
 
+/* Which pairs the contrastive loss pushes apart ("Training" page, uform_negatives_t): ambient repels
+ * every pair no edge names at `ambient_repulsion_weight` (and the named repel edges); named repels the
+ * repel edges alone. */
+typedef enum ube_negatives_t {
+    ube_negatives_ambient_k = 0,
+    ube_negatives_named_k = 1,
+} ube_negatives_t;
+
+/* How a row of scores turns into forces ("Training" page, uform_pair_loss_form_t). This library runs
+ * the sigmoid form (SigLIP's, the pooled embeddings' own); balanced and ranked report unsupported. */
+typedef enum ube_pair_loss_form_t {
+    ube_pair_loss_form_derived_k = 0,
+    ube_pair_loss_form_balanced_k = 1,
+    ube_pair_loss_form_ranked_k = 2,
+    ube_pair_loss_form_sigmoid_k = 3,
+} ube_pair_loss_form_t;
+
+/* One edge set over the anchors in compressed rows ("Training" page, uform_edges_view_t): anchor p
+ * links to items ids[offsets[p] .. offsets[p+1]), strictly ascending within each run; `weights`, when
+ * not NULL, pairs a weight with each id (else every edge weighs 1; ignore edges read none). Host
+ * memory; offsets NULL names no edges, otherwise it has anchor_count + 1 entries. */
+typedef struct ube_edges_view_t {
+    size_t const *offsets;
+    uint32_t const *ids;
+    float const *weights;
+} ube_edges_view_t;
+
+/* The contrastive targets ("Training" page, uform_relations_view_t), resolved per pair in the pages'
+ * order: ignore skips, attract pulls, repel pushes, every other pair follows `negatives`. */
+typedef struct ube_relations_view_t {
+    ube_edges_view_t attract, repel, ignore;
+} ube_relations_view_t;
+
+/* Matryoshka sigmoid contrastive loss over pooled embeddings, forward and backward ("UForm" page,
+ * "Matryoshka-Like Multi-Scale Embedders": every nested prefix width scored under SigLIP's per-cell
+ * sigmoid loss; "Training" page, uform_contrastive_t for the widths, inverse temperature, bias and
+ * ambient weight). The step's `count` items are bf16 rows of `columns` (a multiple of 64, at most 4096)
+ * in device memory of the arena's GPU; anchors are items [anchor_begin, anchor_begin + anchor_count) (one
+ * device's share of a gathered band), every item is a candidate, and an item paired with itself is
+ * skipped. For each width m: cosine s of the length-m prefixes (a zero prefix has cosine 0), logit
+ * z = inverse_temperature * s + bias, cell loss -w log sigma(z) for an attract edge of weight w and
+ * -w log(1 - sigma(z)) for a repelled pair; the width's loss sums the cells of an anchor's row and
+ * averages over anchors, and the loss is the mean over widths.
+ * `matryoshka_dimensions`: host array of strictly ascending widths, each a multiple of 8 up to `columns`,
+ * at most 8 (NULL: `columns` alone); this library runs multiples of 64 and reports others unsupported.
+ * Outputs (device memory): `scalars` receives 3 + widths floats: the loss, d loss / d inverse_temperature,
+ * d loss / d bias, then each width's loss (the loss entries are NaN when `want_loss` is 0, which skips
+ * their per-pair logarithms). `gradient`, when not NULL, receives d loss / d embedding as fp32 rows of
+ * `columns` at `gradient_stride` bytes (16-byte aligned); columns past the widest width get 0.
+ * The arena is the call's workspace (it grows to about 2 * widths * anchors * count bytes plus small
+ * buffers and invalidates earlier views into it); the embeddings must not lie in it. completion == 0
+ * blocks until the outputs are final. Statuses: invalid_argument (NULL or misaligned pointers, anchors
+ * outside the items, bad widths or edges), unsupported (non-bf16 rows, other widths or loss forms),
+ * contended, device, out_of_memory. */
+typedef struct ube_contrastive_t {
+    ube_arena_t arena;
+    void *stream;
+    ube_outcome_t *outcome;
+    int completion;
+    ube_rows_view_t embeddings;
+    size_t anchor_begin, anchor_count;
+    size_t const *matryoshka_dimensions;
+    size_t matryoshka_dimensions_count;
+    float inverse_temperature, bias;
+    ube_negatives_t negatives;
+    float ambient_repulsion_weight;
+    ube_pair_loss_form_t pair_loss;
+    ube_relations_view_t relations;
+    int want_loss;
+    float *scalars;
+    float *gradient;
+    size_t gradient_stride;
+} ube_contrastive_t;
+void ube_contrastive(ube_contrastive_t *arguments);
+
 /* Host-only tape plan, the bookkeeping every text encode does first (no
  * device work; usable without a GPU). lengths[count] receives the kept length
  * of each item, cu[count+1] their prefix sums, *stats the truncated items and

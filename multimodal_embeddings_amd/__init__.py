@@ -110,11 +110,31 @@ class ube_maxsim_t(C.Structure):
                 ("query_span", SZ), ("scores", VP), ("scores_stride", SZ)]
 
 
+class ube_edges_view_t(C.Structure):
+    _fields_ = [("offsets", C.POINTER(SZ)), ("ids", C.POINTER(C.c_uint32)), ("weights", C.POINTER(C.c_float))]
+
+
+class ube_relations_view_t(C.Structure):
+    _fields_ = [("attract", ube_edges_view_t), ("repel", ube_edges_view_t), ("ignore", ube_edges_view_t)]
+
+
+class ube_contrastive_t(C.Structure):
+    _fields_ = [("arena", VP), ("stream", VP), ("outcome", C.POINTER(ube_outcome_t)), ("completion", C.c_int),
+                ("embeddings", ube_rows_view_t), ("anchor_begin", SZ), ("anchor_count", SZ),
+                ("matryoshka_dimensions", C.POINTER(SZ)), ("matryoshka_dimensions_count", SZ),
+                ("inverse_temperature", C.c_float), ("bias", C.c_float), ("negatives", C.c_int),
+                ("ambient_repulsion_weight", C.c_float), ("pair_loss", C.c_int), ("relations", ube_relations_view_t),
+                ("want_loss", C.c_int), ("scalars", VP), ("gradient", VP), ("gradient_stride", SZ)]
+
+
 STATUS = {0: "success", 1: "invalid_argument", 2: "shape_mismatch", 3: "out_of_memory", 4: "device", 5: "contended",
           6: "unsupported", 7: "internal"}
 SCALAR = {"unknown": 0, "u8": 1, "bf16": 2, "f32": 3, "e4m3": 4}
 KERNELS = ["gather", "patchify", "rmsnorm", "gemm_patch", "gemm_qkv", "attention", "gemm_out", "gemm_gate_up",
-           "gemm_down", "final_norm", "pool", "quantize"]
+           "gemm_down", "final_norm", "pool", "quantize", "contrastive_cells", "contrastive_rows",
+           "contrastive_cols"]
+NEGATIVES = {"ambient": 0, "named": 1}
+PAIR_LOSS = {"derived": 0, "balanced": 1, "ranked": 2, "sigmoid": 3}
 
 # every symbol the headers declare, with ctypes signatures
 _SIGNATURES = {
@@ -128,6 +148,7 @@ _SIGNATURES = {
     "ube_image_encode_pixels": ([C.POINTER(ube_image_encode_pixels_t)], None),
     "ube_video_encode_frames": ([C.POINTER(ube_video_encode_frames_t)], None),
     "ube_maxsim": ([C.POINTER(ube_maxsim_t)], None),
+    "ube_contrastive": ([C.POINTER(ube_contrastive_t)], None),
     "ube_tape_plan": ([C.POINTER(SZ), SZ, SZ, VP, VP, C.POINTER(ube_encode_stats_t)], C.c_int),
     "ube_status_name": ([C.c_int], C.c_char_p),
     "ube_step_gemm": ([VP, VP, VP, SZ, SZ, SZ, VP], C.c_int),
@@ -378,6 +399,55 @@ def maxsim(queries: RowsTape, documents: RowsTape, scores, *, prefix=0, span=0, 
     lib().ube_maxsim(C.byref(args))
     _check(outcome)
     return scores
+
+
+def _edges(edges, keep):
+    """ube_edges_view_t over a (offsets, ids, weights-or-None) triple or an object with those attributes."""
+    if edges is None:
+        return ube_edges_view_t()
+    if isinstance(edges, tuple):
+        off, ids, w = edges
+    else:
+        off, ids, w = edges.offsets, edges.ids, edges.weights
+    off = np.ascontiguousarray(off, dtype=np.uint64)
+    ids = np.ascontiguousarray(ids, dtype=np.uint32)
+    keep += [off, ids]
+    wp = None
+    if w is not None:
+        w = np.ascontiguousarray(w, dtype=np.float32)
+        keep.append(w)
+        wp = w.ctypes.data_as(C.POINTER(C.c_float))
+    return ube_edges_view_t(off.ctypes.data_as(C.POINTER(SZ)), ids.ctypes.data_as(C.POINTER(C.c_uint32)), wp)
+
+
+def contrastive(arena: Arena, embeddings, scalars, *, anchor_begin=0, anchor_count=None, widths=None,
+                inverse_temperature=10.0, bias=-10.0, negatives="ambient", ambient_weight=1.0, pair_loss="sigmoid",
+                attract=None, repel=None, ignore=None, want_loss=True, gradient=None, stream=None, completion=0):
+    """Matryoshka sigmoid contrastive loss over bf16 device rows ``embeddings`` [count x columns] (a torch
+    bfloat16 tensor). ``scalars``: device float32 of at least 3 + widths entries (loss, d/dt, d/db, width
+    losses); ``gradient``: optional device float32 [count x columns] receiving d loss / d embeddings.
+    Edge sets are (offsets, ids, weights) triples over the anchors (host arrays)."""
+    import torch
+    count, columns = embeddings.shape
+    if embeddings.dtype != torch.bfloat16:
+        raise TypeError("embeddings must be bfloat16")
+    anchor_count = count - anchor_begin if anchor_count is None else anchor_count
+    keep = []
+    wd = None
+    if widths is not None:
+        wd = np.ascontiguousarray(widths, dtype=np.uint64)
+        keep.append(wd)
+    view = ube_rows_view_t(_ptr(embeddings), count, columns, embeddings.stride(0) * 2, SCALAR["bf16"])
+    rel = ube_relations_view_t(_edges(attract, keep), _edges(repel, keep), _edges(ignore, keep))
+    outcome = ube_outcome_t()
+    args = ube_contrastive_t(arena.handle, _stream_handle(stream), C.pointer(outcome), completion, view, anchor_begin,
+                             anchor_count, wd.ctypes.data_as(C.POINTER(SZ)) if wd is not None else None,
+                             len(wd) if wd is not None else 0, inverse_temperature, bias, NEGATIVES[negatives],
+                             ambient_weight, PAIR_LOSS[pair_loss], rel, 1 if want_loss else 0, _ptr(scalars),
+                             _ptr(gradient), gradient.stride(0) * 4 if gradient is not None else 0)
+    lib().ube_contrastive(C.byref(args))
+    _check(outcome)
+    return scalars, gradient
 
 
 def _tape(data, offsets):

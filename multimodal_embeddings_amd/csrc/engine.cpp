@@ -11,6 +11,7 @@
 #include <new>
 #include <vector>
 
+#include "contrastive.h"
 #include "kernels.h"
 #include "ube.h"
 #include "ube_steps.h"
@@ -973,6 +974,276 @@ extern "C" void ube_maxsim(ube_maxsim_t *a) {
     }
 }
 
+// ============================================================== contrastive loss
+
+namespace {
+
+struct ResolvedEdges {
+    std::vector<ContrastiveEdge> edges;     // sorted by (anchor, item)
+    std::vector<uint32_t> row_edges;        // [R + 1]
+    std::vector<uint32_t> col_offsets;      // [n + 1]
+    std::vector<uint32_t> col_edges;        // [E]
+    std::vector<uint32_t> touched;          // items with edges, ascending
+};
+
+// Reads one edge run; ids must be strictly ascending and name items.
+void edge_run(ube_edges_view_t const &ev, size_t p, size_t n, size_t &lo, size_t &hi) {
+    lo = hi = 0;
+    if (!ev.offsets) return;
+    lo = ev.offsets[p];
+    hi = ev.offsets[p + 1];
+    if (hi < lo) throw Failure{ube_status_invalid_argument_k, "edge offsets decrease"};
+    if (hi > lo && !ev.ids) throw Failure{ube_status_invalid_argument_k, "NULL edge ids"};
+    for (size_t e = lo; e < hi; ++e) {
+        if (ev.ids[e] >= n) throw Failure{ube_status_invalid_argument_k, "edge names an item past the step"};
+        if (e > lo && ev.ids[e] <= ev.ids[e - 1])
+            throw Failure{ube_status_invalid_argument_k, "edge ids must ascend strictly within a run"};
+    }
+}
+
+// Resolves the three edge sets per anchor in the pages' precedence (ignore, attract, repel), drops the
+// item paired with itself, and drops ignore edges when no dense pass runs (they change nothing then).
+ResolvedEdges resolve_edges(ube_relations_view_t const &rel, size_t r0, size_t R, size_t n, bool dense) {
+    ResolvedEdges out;
+    out.row_edges.assign(R + 1, 0);
+    ube_edges_view_t const *sets[3] = {&rel.ignore, &rel.attract, &rel.repel};  // highest precedence first
+    const int labels[3] = {0, 1, -1};
+    for (size_t p = 0; p < R; ++p) {
+        size_t lo[3], hi[3], at[3];
+        for (int k = 0; k < 3; ++k) {
+            edge_run(*sets[k], p, n, lo[k], hi[k]);
+            at[k] = lo[k];
+        }
+        for (;;) {
+            uint32_t j = UINT32_MAX;
+            for (int k = 0; k < 3; ++k)
+                if (at[k] < hi[k]) j = std::min(j, sets[k]->ids[at[k]]);
+            if (j == UINT32_MAX) break;
+            int label = 2;
+            float w = 1.f;
+            for (int k = 0; k < 3; ++k) {
+                if (at[k] < hi[k] && sets[k]->ids[at[k]] == j) {
+                    if (label == 2) {
+                        label = labels[k];
+                        if (labels[k] != 0 && sets[k]->weights) w = sets[k]->weights[at[k]];
+                    }
+                    ++at[k];
+                }
+            }
+            if ((size_t)j == r0 + p) continue;
+            if (label == 0 && !dense) continue;
+            out.edges.push_back(ContrastiveEdge{(int)p, (int)j, label, w});
+        }
+        out.row_edges[p + 1] = (uint32_t)out.edges.size();
+    }
+    const size_t E = out.edges.size();
+    if (!E) return out;
+    out.col_offsets.assign(n + 1, 0);
+    for (auto const &e : out.edges) ++out.col_offsets[e.j + 1];
+    for (size_t j = 0; j < n; ++j) out.col_offsets[j + 1] += out.col_offsets[j];
+    out.col_edges.resize(E);
+    std::vector<uint32_t> fill(out.col_offsets.begin(), out.col_offsets.end() - 1);
+    for (size_t e = 0; e < E; ++e) out.col_edges[fill[out.edges[e].j]++] = (uint32_t)e;
+    std::vector<char> mark(n, 0);
+    for (auto const &e : out.edges) mark[r0 + e.p] = mark[e.j] = 1;
+    for (size_t i = 0; i < n; ++i)
+        if (mark[i]) out.touched.push_back((uint32_t)i);
+    return out;
+}
+
+}  // namespace
+
+extern "C" void ube_contrastive(ube_contrastive_t *a) {
+    if (!a) return;
+    try {
+        if (!a->arena) throw Failure{ube_status_invalid_argument_k, "NULL arena"};
+        ArenaLease lease(a->arena);
+        if (!lease.held) throw Failure{ube_status_contended_k, "arena busy"};
+        ube_arena_t ar = a->arena;
+        auto const &ev = a->embeddings;
+        const size_t n = ev.count, D = ev.columns, R = a->anchor_count, r0 = a->anchor_begin;
+        if (!a->scalars) throw Failure{ube_status_invalid_argument_k, "NULL scalars"};
+        if (n && !ev.data) throw Failure{ube_status_invalid_argument_k, "NULL embeddings"};
+        if (ev.scalar != ube_scalar_bf16_k) throw Failure{ube_status_unsupported_k, "contrastive loss takes bf16 rows"};
+        if (D == 0 || D % 64 || D > 4096)
+            throw Failure{ube_status_unsupported_k, "embedding width must be a multiple of 64 up to 4096"};
+        if (ev.stride % 16 || ev.stride < D * 2 || ((uintptr_t)ev.data % 16))
+            throw Failure{ube_status_invalid_argument_k, "rows must be 16-byte aligned and hold `columns` values"};
+        if (n > ((size_t)1 << 30)) throw Failure{ube_status_invalid_argument_k, "too many items"};
+        if (r0 > n || R > n - r0) throw Failure{ube_status_invalid_argument_k, "anchors outside the items"};
+        if (a->negatives != ube_negatives_ambient_k && a->negatives != ube_negatives_named_k)
+            throw Failure{ube_status_invalid_argument_k, "unknown negatives rule"};
+        if (a->pair_loss != ube_pair_loss_form_derived_k && a->pair_loss != ube_pair_loss_form_sigmoid_k)
+            throw Failure{ube_status_unsupported_k, "only the sigmoid pair loss runs here"};
+        // widths
+        std::vector<int> widths;
+        if (!a->matryoshka_dimensions) {
+            if (a->matryoshka_dimensions_count) throw Failure{ube_status_invalid_argument_k, "NULL widths"};
+            widths.push_back((int)D);
+        } else {
+            if (a->matryoshka_dimensions_count == 0 || a->matryoshka_dimensions_count > (size_t)kMaxWidths)
+                throw Failure{ube_status_invalid_argument_k, "between 1 and 8 widths"};
+            for (size_t w = 0; w < a->matryoshka_dimensions_count; ++w) {
+                const size_t m = a->matryoshka_dimensions[w];
+                if (m == 0 || m % 8 || m > D || (w && m <= (size_t)widths.back()))
+                    throw Failure{ube_status_invalid_argument_k,
+                                  "widths must ascend strictly, be multiples of 8 and fit the rows"};
+                widths.push_back((int)m);
+            }
+            for (int m : widths)
+                if (m % 64) throw Failure{ube_status_unsupported_k, "widths must be multiples of 64 here"};
+        }
+        const int K = (int)widths.size();
+        if (a->gradient && (a->gradient_stride % 16 || a->gradient_stride < D * 4 || ((uintptr_t)a->gradient % 16)))
+            throw Failure{ube_status_invalid_argument_k, "gradient rows must be 16-byte aligned and hold `columns` floats"};
+        if (n && !pointer_on_device(ev.data, ar->device))
+            throw Failure{ube_status_device_k, "embeddings are not device memory of the arena's GPU"};
+        if (n && ar->dev) {
+            char const *lo = (char const *)ev.data, *hi = lo + (n - 1) * ev.stride + D * 2;
+            if (hi > ar->dev && lo < ar->dev + ar->cap) throw Failure{ube_status_invalid_argument_k, "inputs lie inside the arena"};
+        }
+        UBE_HIP(hipSetDevice(ar->device));
+        hipStream_t st = (hipStream_t)a->stream;
+        const bool grad = a->gradient != nullptr;
+        const bool dense = a->negatives == ube_negatives_ambient_k && a->ambient_repulsion_weight != 0.f;
+
+        ContrastiveArgs ca{};
+        ca.emb = (const uint16_t *)ev.data;
+        ca.ld = ev.stride / 2;
+        ca.n = (int)n;
+        ca.R = (int)R;
+        ca.r0 = (int)r0;
+        ca.D = (int)D;
+        ca.K = K;
+        for (int w = 0; w < kMaxWidths; ++w) ca.widths[w] = w < K ? widths[w] : widths[K - 1];
+        ca.t = a->inverse_temperature;
+        ca.b = a->bias;
+        ca.wa = a->ambient_repulsion_weight;
+        ca.c = R ? 1.0f / (float)((double)K * (double)R) : 0.f;
+        ca.dense = dense;
+        ca.scalars = a->scalars;
+        ca.want_loss = a->want_loss != 0;
+        ca.grad = a->gradient;
+        ca.gld = a->gradient_stride / 4;
+        if (R == 0) {
+            UBE_HIP(launch_contrastive_empty(ca, st));
+            if (a->completion == 0) UBE_HIP(hipStreamSynchronize(st));
+            set_outcome(a->outcome, ube_status_success_k, nullptr);
+            return;
+        }
+        ResolvedEdges re = resolve_edges(a->relations, r0, R, n, dense);
+        const size_t E = re.edges.size(), T = re.touched.size();
+        const size_t R_pad = align_up(R, 256), n_pad = align_up(n, 256);
+        ca.R_pad = (int)R_pad;
+        ca.n_pad = (int)n_pad;
+        ca.E = (int)E;
+        ca.T = (int)T;
+        // split of the items for the rows contraction: about 512 workgroups
+        const size_t per_split = (R_pad / 256) * (size_t)(widths[K - 1] / 64);
+        size_t splits = std::max<size_t>(1, std::min<size_t>(n_pad / 64, (512 + per_split - 1) / per_split));
+        const size_t chunk = align_up((n_pad + splits - 1) / splits, 64);
+        splits = (n_pad + chunk - 1) / chunk;
+        ca.splits = (int)splits;
+        ca.chunk = (int)chunk;
+
+        // workspace layout (256-byte aligned pieces)
+        size_t off = 0;
+        auto take = [&](size_t bytes) {
+            size_t at = off;
+            off += align_up(bytes, 256);
+            return at;
+        };
+        const size_t JT = n_pad / 128, PT = R_pad / 128;
+        const size_t o_inv = take((size_t)K * n * 4);
+        const size_t o_h = take(grad && dense ? (size_t)K * R_pad * n_pad * 2 : 0);
+        const size_t o_rowpart = take(dense ? JT * K * R_pad * 4 : 0);
+        const size_t o_colpart = take(grad && dense ? PT * K * n_pad * 4 : 0);
+        const size_t o_wg = take(dense ? PT * JT * K * 2 * 4 : 0);
+        const size_t o_rho = take((size_t)K * R_pad * 4);
+        const size_t o_kappa = take(grad ? (size_t)K * n_pad * 4 : 0);
+        const size_t o_dt = take(R_pad * 4);
+        const size_t o_rpart = take(grad && dense ? splits * R_pad * D * 4 : 0);
+        const size_t o_rfinal = take(grad && dense ? R_pad * D * 4 : 0);
+        const size_t o_eout = take(E * 4 * K * 4);
+        const size_t meta_begin = off;
+        const size_t o_edges = take(E * sizeof(ContrastiveEdge));
+        const size_t o_rowe = take(E ? (R + 1) * 4 : 0);
+        const size_t o_colo = take(E ? (n + 1) * 4 : 0);
+        const size_t o_cole = take(E * 4);
+        const size_t o_touch = take(T * 4);
+        const size_t total = off;
+        if (total > ar->cap) {
+            UBE_HIP(hipStreamSynchronize(st));
+            if (ar->dev) UBE_HIP(hipFree(ar->dev));
+            ar->dev = nullptr;
+            ar->cap = 0;
+            const size_t want = align_up(total, (size_t)1 << 20);
+            UBE_HIP(hipMalloc((void **)&ar->dev, want));
+            ar->cap = want;
+        }
+        char *db = ar->dev;
+        ca.inv = (float *)(db + o_inv);
+        ca.H = (uint16_t *)(db + o_h);
+        ca.rowpart = (float *)(db + o_rowpart);
+        ca.colpart = (float *)(db + o_colpart);
+        ca.wgpart = (float *)(db + o_wg);
+        ca.rho_blk = (float *)(db + o_rho);
+        ca.kappa_blk = (float *)(db + o_kappa);
+        ca.dtrow = (float *)(db + o_dt);
+        ca.rows_partial = (float *)(db + o_rpart);
+        ca.rows_final = (float *)(db + o_rfinal);
+        ca.edge_out = (float *)(db + o_eout);
+        ca.edges = (const ContrastiveEdge *)(db + o_edges);
+        ca.row_edges = (const uint32_t *)(db + o_rowe);
+        ca.col_offsets = (const uint32_t *)(db + o_colo);
+        ca.col_edges = (const uint32_t *)(db + o_cole);
+        ca.touched = (const uint32_t *)(db + o_touch);
+
+        // stage the resolved edges through the arena's pinned buffer
+        const size_t meta_bytes = total - meta_begin;
+        if (E) {
+            if (ar->staged_pending) {
+                UBE_HIP(hipEventSynchronize(ar->staged));
+                ar->staged_pending = false;
+            }
+            if (meta_bytes > ar->pinned_cap) {
+                if (ar->pinned) UBE_HIP(hipHostFree(ar->pinned));
+                ar->pinned = nullptr;
+                ar->pinned_cap = 0;
+                const size_t want = align_up(meta_bytes, (size_t)1 << 16);
+                UBE_HIP(hipHostMalloc((void **)&ar->pinned, want, 0));
+                ar->pinned_cap = want;
+            }
+            if (!ar->staged) UBE_HIP(hipEventCreateWithFlags(&ar->staged, hipEventDisableTiming));
+            char *hp = ar->pinned;
+            std::memcpy(hp + (o_edges - meta_begin), re.edges.data(), E * sizeof(ContrastiveEdge));
+            std::memcpy(hp + (o_rowe - meta_begin), re.row_edges.data(), (R + 1) * 4);
+            std::memcpy(hp + (o_colo - meta_begin), re.col_offsets.data(), (n + 1) * 4);
+            std::memcpy(hp + (o_cole - meta_begin), re.col_edges.data(), E * 4);
+            std::memcpy(hp + (o_touch - meta_begin), re.touched.data(), T * 4);
+            UBE_HIP(hipMemcpyAsync(db + meta_begin, hp, meta_bytes, hipMemcpyHostToDevice, st));
+            UBE_HIP(hipEventRecord(ar->staged, st));
+            ar->staged_pending = true;
+        }
+
+        UBE_HIP(launch_prefix_inv_norms(ca, st));
+        UBE_HIP(launch_contrastive_edges(ca, st));
+        timed(ube_kernel_contrastive_cells_k, st, [&] { return launch_contrastive_cells(ca, grad, st); });
+        UBE_HIP(launch_contrastive_reduce(ca, grad, st));
+        if (grad) {
+            timed(ube_kernel_contrastive_rows_k, st, [&] { return launch_contrastive_grad_rows(ca, st); });
+            timed(ube_kernel_contrastive_cols_k, st, [&] { return launch_contrastive_grad_cols(ca, st); });
+            UBE_HIP(launch_contrastive_sparse(ca, st));
+        }
+        if (a->completion == 0) UBE_HIP(hipStreamSynchronize(st));
+        set_outcome(a->outcome, ube_status_success_k, nullptr);
+    } catch (Failure const &f) {
+        set_outcome(a->outcome, f.status, f.message);
+    } catch (std::bad_alloc const &) {
+        set_outcome(a->outcome, ube_status_out_of_memory_k, "host out of memory");
+    }
+}
+
 extern "C" char const *ube_status_name(ube_status_t s) {
     switch (s) {
         case ube_status_success_k: return "success";
@@ -1104,6 +1375,7 @@ extern "C" ube_status_t ube_kernel_timer_stop(double *total_ms, size_t *launches
 
 extern "C" char const *ube_kernel_name(ube_kernel_t k) {
     static char const *names[] = {"gather",       "patchify",  "rmsnorm",    "gemm_patch", "gemm_qkv", "attention",
-                                  "gemm_out",     "gemm_gate_up", "gemm_down", "final_norm", "pool",     "quantize"};
+                                  "gemm_out",     "gemm_gate_up", "gemm_down", "final_norm", "pool",     "quantize",
+                                  "contrastive_cells", "contrastive_rows", "contrastive_cols"};
     return ((int)k >= 0 && k < ube_kernel_count_k) ? names[k] : "unknown";
 }

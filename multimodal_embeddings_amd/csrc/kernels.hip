@@ -16,52 +16,11 @@
 #include <math.h>
 #include <stdint.h>
 
+#include "device.h"
 #include "kernels.h"
 
 namespace ube {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
-
-__device__ __forceinline__ uint32_t f32_to_bf16(float v) {
-    __bf16 b = (__bf16)v;  // round to nearest even (v_cvt_pk_bf16_f32 on gfx950)
-    return (uint32_t)__builtin_bit_cast(uint16_t, b);
-}
-
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-
-// two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
-    return v;
-}
-
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
-    return v;
-}
-
-// Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
-// b % 8). This remap gives every XCD one contiguous range of logical tiles, so
-// tiles that share operands share that XCD's L2.
-__device__ __forceinline__ int xcd_remap(int bid, int nblocks) {
-    int xcd = bid & 7, slot = bid >> 3;
-    int q = nblocks >> 3, r = nblocks & 7;
-    return (xcd < r) ? xcd * (q + 1) + slot : r * (q + 1) + (xcd - r) * q + slot;
-}
 
 // =========================================================== row kernels
 //
@@ -735,23 +694,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x16 (&acc)[T
 // (16 bytes per lane straight into LDS, no register staging). Lane i of a load
 // instruction lands at LDS chunk (base + i); the global chunk it fetches is the
 // logical chunk that the swizzle assigns to that LDS slot.
-__device__ __forceinline__ void lds_dma16(const void *gptr, void *lds_base) {
-    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
-}
-
-// Workgroup barrier without a memory fence (the DMA of the next stage stays in
-// flight); the empty asm keeps the compiler from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// Operand rows are 128 bytes (8 chunks of 16). gfx950's LDS has 64 banks (256
-// bytes per cycle) and serves a 16-byte read for 16 lanes at a time: lanes
-// reading rows r .. r+15 at the same logical chunk hit 16 distinct 16-byte bank
-// groups when the chunk is XOR-ed with (row / 2) % 8 (row parity picks the
-// 128-byte half of the 256-byte bank window).
-__device__ __forceinline__ int swz(int row, int ch) { return ch ^ ((row >> 1) & 7); }
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
