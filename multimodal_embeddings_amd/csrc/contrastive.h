@@ -48,9 +48,9 @@ struct ContrastiveArgs {
     const uint32_t *col_edges;   // [E] edge indices grouped by item, ascending anchor within an item
     float *edge_out;             // [E][4][K]: delta gamma s, delta gamma, delta loss, delta H (per block)
     // reductions
-    float *rho_blk;    // [K][R_pad]
-    float *kappa_blk;  // [K][n_pad]
-    float *dtrow;      // [R_pad]
+    float *rho;        // [K][R_pad]: rho of each width
+    float *rsum;       // [K][R_pad]: sum over the anchor's row of gamma s, per width
+    float *kappa_blk;  // [K][n_pad]: block coefficients of kappa (sums over widths w >= k)
     float *scalars;    // [3 + K]: loss, d/dt, d/db, width losses
     bool want_loss;
     // gradient

@@ -102,19 +102,27 @@ __global__ __launch_bounds__(256) void k_prefix_inv_norms(ContrastiveArgs a) {
     float bins[kMaxWidths];
 #pragma unroll
     for (int w = 0; w < kMaxWidths; ++w) bins[w] = 0.f;
-    for (int c = lane; c * 8 < mK; c += 64) {
-        const u32x4 v = *(const u32x4 *)(row + c * 8);
-        const uint32_t x[4] = {v.x, v.y, v.z, v.w};
-        float ss = 0.f;
+    for (int c0 = lane; c0 * 8 < mK; c0 += 128) {
+        u32x4 v[2];
 #pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            const float lo = bf16_to_f32(x[h] & 0xffff), hi = bf16_to_f32(x[h] >> 16);
-            ss += lo * lo + hi * hi;
+        for (int u = 0; u < 2; ++u) {
+            const int c = c0 + 64 * u;
+            v[u] = c * 8 < mK ? *(const u32x4 *)(row + c * 8) : u32x4{0u, 0u, 0u, 0u};
         }
-        const int k = block_of(a, c * 8);
 #pragma unroll
-        for (int w = 0; w < kMaxWidths; ++w)
-            if (w == k) bins[w] += ss;
+        for (int u = 0; u < 2; ++u) {
+            const uint32_t x[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            float ss = 0.f;
+#pragma unroll
+            for (int h = 0; h < 4; ++h) {
+                const float lo = bf16_to_f32(x[h] & 0xffff), hi = bf16_to_f32(x[h] >> 16);
+                ss += lo * lo + hi * hi;
+            }
+            const int k = block_of(a, (c0 + 64 * u) * 8);
+#pragma unroll
+            for (int w = 0; w < kMaxWidths; ++w)
+                if (w == k) bins[w] += ss;
+        }
     }
     float cum = 0.f;
 #pragma unroll
@@ -232,8 +240,16 @@ __device__ __forceinline__ void score_width(const ContrastiveArgs &a, const f32x
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const float sp = acc[tj][4 * i + jj] * ijv[jj];
-                const float z2 = fmaf(sp, cpl, bl);
-                float sig = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-z2));
+                const float z2 = fmaf(sp, cpl, bl);  // z log2(e)
+                // u = 2^z2 (clamped: sigma is 1 to fp32 precision long before), sigma = u / (1 + u); the loss
+                // reuses 1 + u: log2(1 + e^z) = log2(1 + u) (z2 itself past 24; u log2(e) below 2^-12)
+                const float u = __builtin_amdgcn_exp2f(fminf(z2, 64.f));
+                const float d = 1.f + u;
+                float sig = u * __builtin_amdgcn_rcpf(d), l2 = 0.f;
+                if constexpr (LOSS) {
+                    l2 = u < 0x1p-12f ? u * kLog2e : __builtin_amdgcn_logf(d);
+                    l2 = z2 > 24.f ? z2 : l2;
+                }
                 bool valid = true;
                 if constexpr (MASK) {
                     const int j = jbase + 32 * tj + 8 * i + 4 * hh + jj;
@@ -244,12 +260,7 @@ __device__ __forceinline__ void score_width(const ContrastiveArgs &a, const f32x
                 gsum += sig;
                 rowacc += v;
                 col[4 * i + jj] = v;
-                if constexpr (LOSS) {
-                    const float u = __builtin_amdgcn_exp2f(z2);
-                    float l2 = u < 0x1p-12f ? u * kLog2e : __builtin_amdgcn_logf(1.f + u);
-                    l2 = z2 > 24.f ? z2 : l2;
-                    lsum += valid ? l2 : 0.f;
-                }
+                if constexpr (LOSS) lsum += valid ? l2 : 0.f;
                 if constexpr (GRAD) qv[jj] = sig * ijv[jj] * fq;
             }
             if constexpr (GRAD) {
@@ -263,7 +274,7 @@ __device__ __forceinline__ void score_width(const ContrastiveArgs &a, const f32x
 
 template <bool LOSS, bool GRAD>
 __global__ __launch_bounds__(512, 1) void k_contrastive_cells(ContrastiveArgs a) {
-    __shared__ __attribute__((aligned(1024))) u32x4 smem[4096];  // 2 stages x 256 rows x 8 chunks
+    __shared__ __attribute__((aligned(1024))) u32x4 smem[4352];  // 2 stages x 256 rows x 8 chunks; H staging
     __shared__ __attribute__((aligned(16))) float sInvJ[kMaxWidths][128];
     __shared__ __attribute__((aligned(16))) float sInvP[kMaxWidths][128];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -352,25 +363,43 @@ __global__ __launch_bounds__(512, 1) void k_contrastive_cells(ContrastiveArgs a)
     }
 
     if constexpr (GRAD) {
+        // H_k = Q_k + H_{k+1}, widest first; each block goes through LDS (rows of 128 items, 272-byte pitch)
+        // so that every global store writes 16 bytes of a contiguous 256-byte row segment
+        constexpr int kPitch = 272;
+        uint8_t *stg = (uint8_t *)smem;
         const size_t hstride = (size_t)a.R_pad * a.n_pad;
-        uint16_t *hrow = a.H + (size_t)(p0 + p_local) * a.n_pad + jbase + 4 * hh;
+        float h[2][4][4];
 #pragma unroll
         for (int tj = 0; tj < 2; ++tj)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float h[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-                for (int w = kMaxWidths - 1; w >= 0; --w) {
-                    if (w < a.K) {
+                for (int jj = 0; jj < 4; ++jj) h[tj][i][jj] = 0.f;
+#pragma unroll
+        for (int w = kMaxWidths - 1; w >= 0; --w) {
+            if (w < a.K) {
+#pragma unroll
+                for (int tj = 0; tj < 2; ++tj)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
                         const uint32_t x0 = q[w][tj * 8 + 2 * i], x1 = q[w][tj * 8 + 2 * i + 1];
-                        h[0] += bf16_to_f32(x0 & 0xffff);
-                        h[1] += bf16_to_f32(x0 >> 16);
-                        h[2] += bf16_to_f32(x1 & 0xffff);
-                        h[3] += bf16_to_f32(x1 >> 16);
-                        *(u32x2 *)(hrow + w * hstride + 32 * tj + 8 * i) = u32x2{pack2(h[0], h[1]), pack2(h[2], h[3])};
+                        h[tj][i][0] += bf16_to_f32(x0 & 0xffff);
+                        h[tj][i][1] += bf16_to_f32(x0 >> 16);
+                        h[tj][i][2] += bf16_to_f32(x1 & 0xffff);
+                        h[tj][i][3] += bf16_to_f32(x1 >> 16);
+                        *(u32x2 *)(stg + p_local * kPitch + (64 * wj + 32 * tj + 8 * i + 4 * hh) * 2) =
+                            u32x2{pack2(h[tj][i][0], h[tj][i][1]), pack2(h[tj][i][2], h[tj][i][3])};
                     }
+                __syncthreads();
+                uint16_t *hw = a.H + (size_t)w * hstride + (size_t)p0 * a.n_pad + j0;
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const int c = tid + 512 * x, row = c >> 4, ch = c & 15;
+                    *(u32x4 *)(hw + (size_t)row * a.n_pad + ch * 8) = *(const u32x4 *)(stg + row * kPitch + ch * 16);
                 }
+                __syncthreads();
             }
+        }
     }
 
     // fixed-order reductions through LDS (the operand stages are free after the loop's last barrier)
@@ -419,50 +448,52 @@ __global__ __launch_bounds__(512, 1) void k_contrastive_cells(ContrastiveArgs a)
 
 // -------------------------------------------------------------------------------------- reductions
 
-// Per anchor: rho of every width from the item-tile partials plus the anchor's edges (in order), then
-// the per-block coefficients and the anchor's share of d loss / d t. 8 waves split the item tiles into
-// eight fixed ranges; 64 anchors per workgroup.
+// Per anchor and width: rho from the item-tile partials plus the anchor's edges (in order), and the raw
+// sum of gamma s (the anchor's share of d loss / d t). Workgroup = 64 anchors x one width; its 8 waves
+// split the item tiles into eight fixed ranges.
 __global__ __launch_bounds__(512) void k_contrastive_rows(ContrastiveArgs a) {
-    __shared__ float part[kMaxWidths][8][64];
+    __shared__ float part[8][64];
     const int tid = threadIdx.x, pl = tid & 63, sl = tid >> 6;
-    const int p = blockIdx.x * 64 + pl;
+    const int p = blockIdx.x * 64 + pl, w = blockIdx.y;
     const int JT = a.n_pad >> 7;
     const int lo = (int)((long)JT * sl / 8), hi = (int)((long)JT * (sl + 1) / 8);
-#pragma unroll
-    for (int w = 0; w < kMaxWidths; ++w) {
-        if (w < a.K) {
-            float s = 0.f;
-            if (a.dense)
-                for (int jt = lo; jt < hi; ++jt) s += a.rowpart[((size_t)jt * a.K + w) * a.R_pad + p];
-            part[w][sl][pl] = s;
+    float s = 0.f;
+    if (a.dense) {
+        const float *src = a.rowpart + (size_t)w * a.R_pad + p;
+        const size_t step = (size_t)a.K * a.R_pad;
+        int jt = lo;
+        float s1 = 0.f, s2 = 0.f, s3 = 0.f;
+        for (; jt + 4 <= hi; jt += 4) {
+            s += src[(size_t)jt * step];
+            s1 += src[(size_t)(jt + 1) * step];
+            s2 += src[(size_t)(jt + 2) * step];
+            s3 += src[(size_t)(jt + 3) * step];
         }
+        for (; jt < hi; ++jt) s += src[(size_t)jt * step];
+        s = (s + s1) + (s2 + s3);
     }
+    part[sl][pl] = s;
     __syncthreads();
     if (sl != 0) return;
-    float rho[kMaxWidths], dt = 0.f;
-#pragma unroll
-    for (int w = 0; w < kMaxWidths; ++w) {
-        rho[w] = 0.f;
-        if (w < a.K && p < a.R) {
-            float s = 0.f;
-            for (int v = 0; v < 8; ++v) s += part[w][v][pl];
-            if (a.E)
-                for (uint32_t e = a.row_edges[p]; e < a.row_edges[p + 1]; ++e)
-                    s += a.edge_out[((size_t)e * 4) * a.K + w];
-            dt += s;
-            const float ip = a.inv[(size_t)w * a.n + a.r0 + p];
-            rho[w] = a.t * ip * ip * s;
-        }
+    float tot = 0.f, rho = 0.f;
+    if (p < a.R) {
+        for (int v = 0; v < 8; ++v) tot += part[v][pl];
+        if (a.E)
+            for (uint32_t e = a.row_edges[p]; e < a.row_edges[p + 1]; ++e) tot += a.edge_out[((size_t)e * 4) * a.K + w];
+        const float ip = a.inv[(size_t)w * a.n + a.r0 + p];
+        rho = a.t * ip * ip * tot;
     }
+    a.rho[(size_t)w * a.R_pad + p] = rho;
+    a.rsum[(size_t)w * a.R_pad + p] = tot;
+}
+
+// Block coefficient of rho for anchor p and column block k: the sum over widths w >= k.
+__device__ __forceinline__ float rho_block(const ContrastiveArgs &a, int k, int p) {
     float h = 0.f;
 #pragma unroll
-    for (int w = kMaxWidths - 1; w >= 0; --w) {
-        if (w < a.K) {
-            h += rho[w];
-            a.rho_blk[(size_t)w * a.R_pad + p] = h;
-        }
-    }
-    a.dtrow[p] = dt;
+    for (int w = kMaxWidths - 1; w >= 0; --w)
+        if (w < a.K && w >= k) h += a.rho[(size_t)w * a.R_pad + p];
+    return h;
 }
 
 // Per item: kappa of every width from the anchor-tile partials plus the item's incoming edges.
@@ -495,47 +526,66 @@ __global__ __launch_bounds__(256) void k_contrastive_cols(ContrastiveArgs a) {
     }
 }
 
-// The scalars: width losses, d loss / d t, d loss / d b; every sum in a fixed order.
-__global__ __launch_bounds__(256) void k_contrastive_scalars(ContrastiveArgs a) {
-    __shared__ float red[256];
-    const int tid = threadIdx.x;
+// The scalars: width losses, d loss / d t, d loss / d b; every sum in a fixed order (a fixed share per
+// thread, then wave sums, then the 16 waves in order).
+__global__ __launch_bounds__(1024) void k_contrastive_scalars(ContrastiveArgs a) {
+    __shared__ float red[16][2 * kMaxWidths + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int tiles = a.dense ? (a.R_pad >> 7) * (a.n_pad >> 7) : 0;
-    auto block_sum = [&](float v) {
-        red[tid] = v;
-        __syncthreads();
-        for (int s = 128; s > 0; s >>= 1) {
-            if (tid < s) red[tid] += red[tid + s];
-            __syncthreads();
+    float g[kMaxWidths], l[kMaxWidths], dt = 0.f;
+#pragma unroll
+    for (int w = 0; w < kMaxWidths; ++w) g[w] = l[w] = 0.f;
+    for (int x = tid; x < tiles; x += 1024) {
+#pragma unroll
+        for (int w = 0; w < kMaxWidths; ++w) {
+            if (w < a.K) {
+                const float2 v = *(const float2 *)(a.wgpart + ((size_t)x * a.K + w) * 2);
+                g[w] += v.x;
+                l[w] += v.y;
+            }
         }
-        const float r = red[0];
-        __syncthreads();
-        return r;
-    };
-    float loss_sum = 0.f, db = 0.f;
+    }
+    for (int e = tid; e < a.E; e += 1024) {
+#pragma unroll
+        for (int w = 0; w < kMaxWidths; ++w) {
+            if (w < a.K) {
+                g[w] += a.edge_out[((size_t)e * 4 + 1) * a.K + w];
+                l[w] += a.edge_out[((size_t)e * 4 + 2) * a.K + w];
+            }
+        }
+    }
+    for (int idx = tid; idx < a.K * a.R_pad; idx += 1024)
+        if (idx % a.R_pad < a.R) dt += a.rsum[idx];
+#pragma unroll
+    for (int w = 0; w < kMaxWidths; ++w) {
+        if (w < a.K) {
+            const float gs = wave_sum(g[w]), ls = wave_sum(l[w]);
+            if (lane == 0) {
+                red[wave][2 * w] = gs;
+                red[wave][2 * w + 1] = ls;
+            }
+        }
+    }
+    dt = wave_sum(dt);
+    if (lane == 0) red[wave][2 * kMaxWidths] = dt;
+    __syncthreads();
+    if (tid != 0) return;
+    float db = 0.f, loss = 0.f, dts = 0.f;
+    for (int v = 0; v < 16; ++v) dts += red[v][2 * kMaxWidths];
     for (int w = 0; w < a.K; ++w) {
-        float g = 0.f, l = 0.f;
-        for (int x = tid; x < tiles; x += 256) {
-            g += a.wgpart[((size_t)x * a.K + w) * 2];
-            l += a.wgpart[((size_t)x * a.K + w) * 2 + 1];
+        float gw = 0.f, lw = 0.f;
+        for (int v = 0; v < 16; ++v) {
+            gw += red[v][2 * w];
+            lw += red[v][2 * w + 1];
         }
-        for (int e = tid; e < a.E; e += 256) {
-            g += a.edge_out[((size_t)e * 4 + 1) * a.K + w];
-            l += a.edge_out[((size_t)e * 4 + 2) * a.K + w];
-        }
-        g = block_sum(g);
-        l = block_sum(l) / (float)a.R;
-        db += g;
-        loss_sum += l;
-        if (tid == 0) a.scalars[3 + w] = a.want_loss ? l : __builtin_nanf("");
+        lw /= (float)a.R;
+        db += gw;
+        loss += lw;
+        a.scalars[3 + w] = a.want_loss ? lw : __builtin_nanf("");
     }
-    float dt = 0.f;
-    for (int p = tid; p < a.R; p += 256) dt += a.dtrow[p];
-    dt = block_sum(dt);
-    if (tid == 0) {
-        a.scalars[0] = a.want_loss ? loss_sum / (float)a.K : __builtin_nanf("");
-        a.scalars[1] = dt;
-        a.scalars[2] = db;
-    }
+    a.scalars[0] = a.want_loss ? loss / (float)a.K : __builtin_nanf("");
+    a.scalars[1] = dts;
+    a.scalars[2] = db;
 }
 
 // ------------------------------------------------------------------------------------ contractions
@@ -632,7 +682,7 @@ __global__ __launch_bounds__(256) void k_contrastive_rows_finish(ContrastiveArgs
     f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
     if (d < a.widths[a.K - 1]) {
         for (int sp = 0; sp < a.splits; ++sp) s += *(const f32x4 *)(a.rows_partial + ((size_t)sp * a.R_pad + p) * a.D + d);
-        const float rho = a.rho_blk[(size_t)block_of(a, d) * a.R_pad + p];
+        const float rho = rho_block(a, block_of(a, d), p);
         const u32x2 e = *(const u32x2 *)(a.emb + (size_t)(a.r0 + p) * a.ld + d);
         s.x -= rho * bf16_to_f32(e.x & 0xffff);
         s.y -= rho * bf16_to_f32(e.x >> 16);
@@ -744,7 +794,7 @@ __global__ __launch_bounds__(256) void k_contrastive_diag(ContrastiveArgs a) {
     if (d < a.widths[a.K - 1]) {
         const int k = block_of(a, d);
         float c = a.kappa_blk[(size_t)k * a.n_pad + j];
-        if (j >= a.r0 && j < a.r0 + a.R) c += a.rho_blk[(size_t)k * a.R_pad + (j - a.r0)];
+        if (j >= a.r0 && j < a.r0 + a.R) c += rho_block(a, k, j - a.r0);
         const u32x2 e = *(const u32x2 *)(a.emb + (size_t)j * a.ld + d);
         o = f32x4{-c * bf16_to_f32(e.x & 0xffff), -c * bf16_to_f32(e.x >> 16), -c * bf16_to_f32(e.y & 0xffff),
                   -c * bf16_to_f32(e.y >> 16)};
@@ -813,14 +863,14 @@ hipError_t launch_contrastive_cells(const ContrastiveArgs &a, bool grad, hipStre
 }
 
 hipError_t launch_contrastive_reduce(const ContrastiveArgs &a, bool grad, hipStream_t stream) {
-    k_contrastive_rows<<<a.R_pad / 64, 512, 0, stream>>>(a);
+    k_contrastive_rows<<<dim3(a.R_pad / 64, a.K), 512, 0, stream>>>(a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     if (grad) {
         k_contrastive_cols<<<a.n_pad / 256, 256, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    k_contrastive_scalars<<<1, 256, 0, stream>>>(a);
+    k_contrastive_scalars<<<1, 1024, 0, stream>>>(a);
     return hipGetLastError();
 }
 

@@ -1161,7 +1161,7 @@ extern "C" void ube_contrastive(ube_contrastive_t *a) {
         const size_t o_wg = take(dense ? PT * JT * K * 2 * 4 : 0);
         const size_t o_rho = take((size_t)K * R_pad * 4);
         const size_t o_kappa = take(grad ? (size_t)K * n_pad * 4 : 0);
-        const size_t o_dt = take(R_pad * 4);
+        const size_t o_rsum = take((size_t)K * R_pad * 4);
         const size_t o_rpart = take(grad && dense ? splits * R_pad * D * 4 : 0);
         const size_t o_rfinal = take(grad && dense ? R_pad * D * 4 : 0);
         const size_t o_eout = take(E * 4 * K * 4);
@@ -1187,9 +1187,9 @@ extern "C" void ube_contrastive(ube_contrastive_t *a) {
         ca.rowpart = (float *)(db + o_rowpart);
         ca.colpart = (float *)(db + o_colpart);
         ca.wgpart = (float *)(db + o_wg);
-        ca.rho_blk = (float *)(db + o_rho);
+        ca.rho = (float *)(db + o_rho);
         ca.kappa_blk = (float *)(db + o_kappa);
-        ca.dtrow = (float *)(db + o_dt);
+        ca.rsum = (float *)(db + o_rsum);
         ca.rows_partial = (float *)(db + o_rpart);
         ca.rows_final = (float *)(db + o_rfinal);
         ca.edge_out = (float *)(db + o_eout);
