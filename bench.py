@@ -40,6 +40,20 @@ WORKLOAD_TEXT = {
               "1024-byte text batch, queries the first 64 tokens of each row, documents all 1024",
 }
 MAXSIM_ITEMS = 256
+WORKLOAD_TEXT.update({
+    "siglip_band": "Matryoshka sigmoid contrastive loss + gradient: 1024 anchors (one device's share) against "
+                   "73,728 gathered 1024-d bf16 pooled embeddings, widths 64/128/256/512/1024, t 10, b -10, "
+                   "ambient negatives, 1-2 positives, 2 hard negatives and 1 ignore edge per anchor",
+    "siglip_pooled": "Matryoshka sigmoid contrastive loss + gradient over a 4096-segment step of 512-d pooled "
+                     "embeddings, every item an anchor, widths 64/128/256/512",
+})
+# Contrastive cells: the per-(anchor, item, width) work the method needs at the least -- logit from the
+# prefix dot (2 fp32 ops), sigmoid (exp and reciprocal: 2 transcendental + 2 ops), loss (log: 1
+# transcendental + 1 op), gradient coefficient (1 op), the row, column and bias sums (4 ops): 10 VALU
+# slots plus 3 transcendental ops at a quarter of the VALU rate (12 slots). MI355X issues 64 fp32 lane
+# ops per clock per CU (4 SIMDs x 16 lanes), 256 CUs at 2.4 GHz: 3.93e13 slots/s / 22 slots.
+CELL_SLOTS = 22
+PEAK_CELLS = 256 * 64 * 2.4e9 / CELL_SLOTS
 
 
 def kernel_flops_per_launch(kernel, g, T, lengths):
@@ -57,9 +71,10 @@ def kernel_flops_per_launch(kernel, g, T, lengths):
     raise ValueError(kernel)
 
 
-def source_digest():
+def source_digest(kernel="gemm"):
     h = hashlib.sha256()
-    for f in ("kernels.hip", "kernels.h"):
+    files = ("contrastive.hip", "contrastive.h") if kernel.startswith("contrastive") else ("kernels.hip", "kernels.h")
+    for f in files:
         h.update(open(os.path.join(ROOT, "multimodal_embeddings_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -70,7 +85,7 @@ def load_traffic(kernel, workload):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path)).get(f"{kernel}@{workload}")
-    if not rec or rec.get("source_digest") != source_digest():
+    if not rec or rec.get("source_digest") != source_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -152,6 +167,98 @@ def bench_maxsim(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_siglip(args):
+    """Times whole contrastive calls (loss and gradient) on resident bf16 embeddings."""
+    import torch
+    import multimodal_embeddings_amd as ube
+    from multimodal_embeddings_amd import configs, synth
+    wl = configs.SIGLIP_WORKLOADS[args.workload]
+    batch = synth.siglip_workload(args.workload)
+    emb = torch.from_numpy(batch.emb_bits.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    widths = wl["widths"]
+    K, R, n, D = len(widths), batch.anchors, batch.items, batch.columns
+    scalars = torch.zeros(3 + K, dtype=torch.float32, device="cuda:0")
+    grad = torch.empty((n, D), dtype=torch.float32, device="cuda:0")
+    arena = ube.Arena(0)
+    stream = torch.cuda.current_stream()
+    rel = dict(attract=(batch.attract.offsets, batch.attract.ids, batch.attract.weights),
+               repel=(batch.repel.offsets, batch.repel.ids, batch.repel.weights),
+               ignore=(batch.ignore.offsets, batch.ignore.ids, None))
+
+    def step():
+        ube.contrastive(arena, emb, scalars, anchor_begin=batch.anchor_begin, anchor_count=R, widths=widths,
+                        inverse_temperature=configs.SIGLIP_TEMPERATURE, bias=configs.SIGLIP_BIAS, gradient=grad,
+                        completion=1, stream=stream, **rel)
+
+    kernel = args.kernel if args.kernel.startswith("contrastive") else "contrastive_cells"
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    ube.kernel_timer_start(kernel, args.steps + 4)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    kms, launches = ube.kernel_timer_stop()
+    ms = start.elapsed_time(end) / args.steps
+    per_kernel = {}
+    if args.per_kernel:
+        for kname in ("contrastive_cells", "contrastive_rows", "contrastive_cols"):
+            ube.kernel_timer_start(kname, 8)
+            step()
+            torch.cuda.synchronize()
+            t, nl = ube.kernel_timer_stop()
+            per_kernel[kname] = {"ms_per_step": t, "launches": nl}
+    avg_s = kms / max(launches, 1) / 1e3
+    pairs = R * n
+    flops = configs.siglip_flops(n, R, D)
+    if kernel == "contrastive_cells":
+        achieved = pairs * K / avg_s
+        roof = {"kernel": kernel, "bound": "alu", "achieved": achieved / 1e9, "peak": PEAK_CELLS / 1e9,
+                "unit": "G cell-widths/s", "frac": achieved / PEAK_CELLS}
+    else:
+        achieved = 2.0 * R * n * D / avg_s / 1e12
+        roof = {"kernel": kernel, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16 / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / (PEAK_BF16 / 1e12)}
+    roof.update({"traffic": load_traffic(kernel, args.workload), "avg_launch_ms": avg_s * 1e3, "launches": launches})
+    out = {
+        "metric": "contrastive band pairs/sec (Matryoshka sigmoid loss + gradient over pooled embeddings)",
+        "value": pairs / (ms / 1e3), "unit": "pairs/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded paired views of shared latents, bf16 rows, seeded edges)",
+        "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}", "anchors": R, "items": n,
+                   "columns": D, "widths": list(widths), "parallelism": "1 GPU"},
+        "mfma_util": flops / (ms / 1e3) / PEAK_BF16,
+        "flops_per_step": flops,
+        "roofline": roof,
+    }
+    if per_kernel:
+        out["per_kernel_ms"] = per_kernel
+    if not args.no_cpu_baseline:
+        from oracle import siglip as S
+        A = int(args.cpu_rows) if args.cpu_rows else {"siglip_band": 256}.get(args.workload, 1024)
+        A = min(A, R)
+
+        def head(e, weighted=True):
+            off = e.offsets[:A + 1]
+            return (off, e.ids, e.weights if weighted else None)
+
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        S.siglip(batch.emb, batch.anchor_begin, A, widths, configs.SIGLIP_TEMPERATURE, configs.SIGLIP_BIAS,
+                 head(batch.attract), head(batch.repel), head(batch.ignore, False))
+        dt = time.perf_counter() - t0
+        out["cpu_baseline"] = {"value": A * n / dt, "unit": "pairs/s", "cores": threads, "kind": "oracle",
+                               "sample": f"anchors 0-{A - 1} against all {n} items, loss and gradient "
+                                         f"(float64 oracle, {dt:.1f} s)"}
+    else:
+        out["cpu_baseline"] = None
+    arena.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,6 +281,8 @@ def main():
 
     if args.workload == "maxsim":
         return bench_maxsim(args)
+    if args.workload.startswith("siglip"):
+        return bench_siglip(args)
 
     import torch
     import multimodal_embeddings_amd as ube

@@ -127,3 +127,54 @@ def siglip_batch(batch, widths, t, b, negatives=AMBIENT, ambient_weight=1.0):
         return (x.offsets, x.ids, x.weights)
     return siglip(batch.emb, batch.anchor_begin, batch.anchors, widths, t, b, edges(batch.attract),
                   edges(batch.repel), (batch.ignore.offsets, batch.ignore.ids, None), negatives, ambient_weight)
+
+
+def siglip_sampled(emb, anchor_begin, anchors, widths, t, b, attract=None, repel=None, ignore=None,
+                   negatives=AMBIENT, ambient_weight=1.0, sample=(), block=256):
+    """``siglip`` for steps too large for dense [anchors x items] matrices: the loss, width losses, d/dt
+    and d/db over every cell, and the gradient rows of the items in ``sample`` only. The same steps in
+    the same order, taken over blocks of ``block`` anchors; returns (loss, width_losses, {item: row}, dt, db).
+    """
+    e = np.asarray(emb, dtype=np.float64)
+    items, columns = e.shape
+    widths = [columns] if widths is None else [int(m) for m in widths]
+    K = len(widths)
+    sample = sorted(set(int(i) for i in sample))
+    grads = {i: np.zeros(columns) for i in sample}
+    width_losses = np.zeros(K)
+    dt = db = 0.0
+    if anchors == 0:
+        return 0.0, width_losses, grads, 0.0, 0.0
+    idx = np.asarray(sample, dtype=np.int64)
+
+    def rows_of(edges, lo, hi):
+        if edges is None:
+            return None
+        off, ids, wts = edges
+        return (np.asarray(off)[lo:hi + 1], ids, wts)
+
+    for k, m in enumerate(widths):
+        xhat, inv = _normalise(e[:, :m])
+        d_cols = np.zeros((len(sample), m))
+        d_rows = {}
+        for lo in range(0, anchors, block):
+            hi = min(anchors, lo + block)
+            y, w = resolve_cells(items, anchor_begin + lo, hi - lo, rows_of(attract, lo, hi), rows_of(repel, lo, hi),
+                                 rows_of(ignore, lo, hi), negatives, ambient_weight)
+            rows = slice(anchor_begin + lo, anchor_begin + hi)
+            s = xhat[rows] @ xhat.T
+            z = t * s + b
+            width_losses[k] += (w * _softplus(-y * z)).sum() / anchors
+            g = w * (_sigmoid(z) - (y == 1)) / (K * anchors)
+            db += g.sum()
+            dt += (g * s).sum()
+            ds = t * g
+            if len(idx):
+                d_cols += ds[:, idx].T @ xhat[rows]
+            for i in sample:
+                if anchor_begin + lo <= i < anchor_begin + hi:
+                    d_rows[i] = ds[i - anchor_begin - lo] @ xhat
+        for n_, i in enumerate(sample):
+            dx = d_cols[n_] + d_rows.get(i, 0.0)
+            grads[i][:m] += _normalise_backward(xhat[i:i + 1], inv[i:i + 1], dx[None, :])[0]
+    return float(width_losses.mean()), width_losses, grads, float(dt), float(db)

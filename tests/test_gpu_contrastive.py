@@ -156,3 +156,37 @@ def test_refusals(ube, arena):
     with pytest.raises(ube.UbeError) as e:
         ube.contrastive(arena, emb.float().to(torch.bfloat16)[:, :96].contiguous(), sc)
     assert e.value.status == "unsupported"
+
+
+def test_band_full_size_sampled(ube, arena):
+    """One device's band at full size (1024 anchors x 73,728 items x 1024 columns, five widths): the loss,
+    d/dt and d/db over every cell and sampled gradient rows against the blocked oracle; the radial part of
+    every gradient row (zero in exact arithmetic: the loss ignores each item's scale) stays small."""
+    import time
+    name = "siglip_band"
+    wl = configs.SIGLIP_WORKLOADS[name]
+    batch = synth.siglip_workload(name)
+    sc, g = _gpu(ube, arena, batch, wl["widths"])
+    off = batch.attract.offsets.astype(np.int64)
+    named = set(int(x) for x in batch.attract.ids[off[0]:off[2]]) | set(int(x) for x in batch.repel.ids[:4])
+    sample = sorted({0, 1, 511, 1023, 1024, 40000, 73727} | named)
+    t0 = time.time()
+    loss, wls, rows, dt, db = S.siglip_sampled(batch.emb, batch.anchor_begin, batch.anchors, wl["widths"], T, B,
+                                               _edges(batch.attract), _edges(batch.repel),
+                                               _edges(batch.ignore, False), sample=sample)
+    say(f"[band] oracle {time.time() - t0:.1f} s; loss {sc[0]:.8g} vs {loss:.8g}; dt {sc[1]:.6g} vs {dt:.6g}; "
+        f"db {sc[2]:.6g} vs {db:.6g}")
+    assert abs(sc[0] - loss) <= 1e-4 * abs(loss)
+    assert np.allclose(sc[3:3 + len(wls)], wls, rtol=1e-4)
+    assert abs(sc[1] - dt) <= 2e-3 * abs(dt) + 1e-6 and abs(sc[2] - db) <= 2e-3 * abs(db) + 1e-6
+    want = np.stack([rows[i] for i in sample])
+    got = g[sample]
+    cos = row_cos(got, want)
+    err = np.abs(got - want).max()
+    scale = np.abs(want).max()
+    say(f"[band] sampled rows {sample}: min cos {cos.min():.6f}, max |diff| {err:.3e} ({err / scale:.2e} of max)")
+    assert cos.min() >= COS_MIN and err <= 2e-2 * scale
+    e = batch.emb.astype(np.float64)
+    radial = np.abs((g * e).sum(1)) / np.maximum(np.linalg.norm(g, axis=1) * np.linalg.norm(e, axis=1), 1e-30)
+    say(f"[band] largest radial cosine over {len(g)} rows: {radial.max():.2e}")
+    assert radial.max() <= 2e-2

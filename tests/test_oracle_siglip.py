@@ -250,3 +250,22 @@ def test_anchor_ranges_add_up():
     assert 40 * full[0] == pytest.approx(13 * a[0] + 27 * b[0], rel=1e-12)
     assert np.allclose(40 * full[2], 13 * a[2] + 27 * b[2], rtol=1e-9, atol=1e-15)
     assert 40 * full[4] == pytest.approx(13 * a[4] + 27 * b[4], rel=1e-9)
+
+
+def test_sampled_form_equals_dense_form():
+    # the blocked, sampled form used at full size against the dense form on steps both can run
+    batch = synth.siglip_batch(90, 64, 17, 50, seed=13)
+    edges = dict(attract=(batch.attract.offsets, batch.attract.ids, batch.attract.weights),
+                 repel=(batch.repel.offsets, batch.repel.ids, batch.repel.weights),
+                 ignore=(batch.ignore.offsets, batch.ignore.ids, None))
+    for negatives, wa in ((S.AMBIENT, 1.0), (S.NAMED, 1.0), (S.AMBIENT, 0.4)):
+        dense = S.siglip(batch.emb, 17, 50, (16, 48, 64), T, B, negatives=negatives, ambient_weight=wa, **edges)
+        sample = [0, 16, 17, 18, 40, 66, 67, 89]
+        samp = S.siglip_sampled(batch.emb, 17, 50, (16, 48, 64), T, B, negatives=negatives, ambient_weight=wa,
+                                sample=sample, block=7, **edges)
+        assert samp[0] == pytest.approx(dense[0], rel=1e-12)
+        assert np.allclose(samp[1], dense[1], rtol=1e-12)
+        assert samp[3] == pytest.approx(dense[3], rel=1e-10, abs=1e-15)
+        assert samp[4] == pytest.approx(dense[4], rel=1e-10, abs=1e-15)
+        for i in sample:
+            assert np.allclose(samp[2][i], dense[2][i], rtol=1e-9, atol=1e-16), i
