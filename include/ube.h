@@ -393,6 +393,71 @@ typedef struct ube_contrastive_t {
 } ube_contrastive_t;
 void ube_contrastive(ube_contrastive_t *arguments);
 
+/* Training of a text model ("UForm" page, "Precision by Design" and "Adafactor Optimizer"; "Training"
+ * page, uform_trainer_t and uform_trainer_step: forward, loss, backward, update). One device; the loss is
+ * the caller's (for example ube_contrastive over the pooled rows), handed in as its gradient with respect
+ * to the pooled embeddings.
+ *
+ * A trainer keeps bf16 master weights (fp32 for the norm gains) in the canonical layout of ube_weights_t,
+ * their fp32 gradients and the Adafactor state, and refreshes the model's forward weights after every
+ * step (so encodes on the model see the updated weights). Text models in bf16 with 1-axis rotary and
+ * hidden <= 1024 (unsupported otherwise). Adafactor: beta1 [0.9], decay_rate [-0.8] (beta2_t = 1 -
+ * t^decay_rate), epsilon1 [1e-30], clip_threshold [1]; zero fields take the defaults in brackets. */
+typedef struct ube_trainer_handle_t *ube_trainer_t;
+
+typedef struct ube_trainer_init_t {
+    ube_trainer_t *trainer;
+    ube_outcome_t *outcome;
+    ube_model_t model;               /* borrowed until the trainer is freed */
+    ube_weights_t const *weights;    /* the model's weights in host memory (copied) */
+    float beta1, decay_rate, epsilon1, clip_threshold;
+} ube_trainer_init_t;
+void ube_trainer_init(ube_trainer_init_t *arguments);
+
+/* Backward pass over a byte tape: replays the forward with every block's fp32 input kept, then walks
+ * the blocks from last to first, each replaying its forward from that input ("activation recomputation
+ * is always on") before its backward. d_embeddings: device fp32 rows [count x hidden] (packed; stride 0
+ * or hidden * 4 bytes), d loss / d pooled embedding. Writes d loss / d every parameter into the trainer's
+ * fp32 gradient buffers (overwritten, not accumulated); the arena serves the replayed forward. */
+typedef struct ube_trainer_backward_t {
+    ube_trainer_t trainer;
+    ube_arena_t arena;
+    void *stream;
+    ube_outcome_t *outcome;
+    int completion;
+    ube_tape_view_t texts;
+    float const *d_embeddings;
+    size_t d_embeddings_stride;
+    ube_encode_stats_t *stats;
+} ube_trainer_backward_t;
+void ube_trainer_backward(ube_trainer_backward_t *arguments);
+
+/* One Adafactor update of every tensor with the gradients of the last backward, at `learning_rate`
+ * (the caller's schedule); then the model's forward weights are rebuilt from the masters. */
+typedef struct ube_trainer_step_t {
+    ube_trainer_t trainer;
+    void *stream;
+    ube_outcome_t *outcome;
+    int completion;
+    float learning_rate;
+} ube_trainer_step_t;
+void ube_trainer_step(ube_trainer_step_t *arguments);
+
+/* Device views of the trainer's tensors, in a fixed order (embed; per block attn_norm, w_qkv, w_o,
+ * mlp_norm, w_gate, w_up, w_down; final_norm, pool_query, pool_wk, pool_wv): canonical layout, `cols` 0
+ * for vectors; master bf16 or f32; gradient fp32. Returns the tensor count; fills at most `capacity`. */
+typedef struct ube_trainer_tensor_t {
+    char const *name;
+    size_t layer, rows, cols;
+    void *master;
+    ube_scalar_t master_scalar;
+    float *gradient;
+} ube_trainer_tensor_t;
+size_t ube_trainer_tensors(ube_trainer_t trainer, ube_trainer_tensor_t *tensors, size_t capacity);
+
+/* NULL-safe; synchronises the device, then frees the trainer's memory. */
+void ube_trainer_free(ube_trainer_t trainer);
+
 /* Host-only tape plan, the bookkeeping every text encode does first (no
  * device work; usable without a GPU). lengths[count] receives the kept length
  * of each item, cu[count+1] their prefix sums, *stats the truncated items and

@@ -127,6 +127,28 @@ class ube_contrastive_t(C.Structure):
                 ("want_loss", C.c_int), ("scalars", VP), ("gradient", VP), ("gradient_stride", SZ)]
 
 
+class ube_trainer_init_t(C.Structure):
+    _fields_ = [("trainer", C.POINTER(VP)), ("outcome", C.POINTER(ube_outcome_t)), ("model", VP),
+                ("weights", C.POINTER(ube_weights_t)), ("beta1", C.c_float), ("decay_rate", C.c_float),
+                ("epsilon1", C.c_float), ("clip_threshold", C.c_float)]
+
+
+class ube_trainer_backward_t(C.Structure):
+    _fields_ = [("trainer", VP), ("arena", VP), ("stream", VP), ("outcome", C.POINTER(ube_outcome_t)),
+                ("completion", C.c_int), ("texts", ube_tape_view_t), ("d_embeddings", VP),
+                ("d_embeddings_stride", SZ), ("stats", C.POINTER(ube_encode_stats_t))]
+
+
+class ube_trainer_step_t(C.Structure):
+    _fields_ = [("trainer", VP), ("stream", VP), ("outcome", C.POINTER(ube_outcome_t)), ("completion", C.c_int),
+                ("learning_rate", C.c_float)]
+
+
+class ube_trainer_tensor_t(C.Structure):
+    _fields_ = [("name", C.c_char_p), ("layer", SZ), ("rows", SZ), ("cols", SZ), ("master", VP),
+                ("master_scalar", C.c_int), ("gradient", VP)]
+
+
 STATUS = {0: "success", 1: "invalid_argument", 2: "shape_mismatch", 3: "out_of_memory", 4: "device", 5: "contended",
           6: "unsupported", 7: "internal"}
 SCALAR = {"unknown": 0, "u8": 1, "bf16": 2, "f32": 3, "e4m3": 4}
@@ -149,6 +171,11 @@ _SIGNATURES = {
     "ube_video_encode_frames": ([C.POINTER(ube_video_encode_frames_t)], None),
     "ube_maxsim": ([C.POINTER(ube_maxsim_t)], None),
     "ube_contrastive": ([C.POINTER(ube_contrastive_t)], None),
+    "ube_trainer_init": ([C.POINTER(ube_trainer_init_t)], None),
+    "ube_trainer_backward": ([C.POINTER(ube_trainer_backward_t)], None),
+    "ube_trainer_step": ([C.POINTER(ube_trainer_step_t)], None),
+    "ube_trainer_tensors": ([VP, C.POINTER(ube_trainer_tensor_t), SZ], SZ),
+    "ube_trainer_free": ([VP], None),
     "ube_tape_plan": ([C.POINTER(SZ), SZ, SZ, VP, VP, C.POINTER(ube_encode_stats_t)], C.c_int),
     "ube_status_name": ([C.c_int], C.c_char_p),
     "ube_step_gemm": ([VP, VP, VP, SZ, SZ, SZ, VP], C.c_int),
@@ -212,40 +239,47 @@ def _stream_handle(stream):
 # ------------------------------------------------------------------ model / arena
 
 
+def _weights_struct(weights, g):
+    """ube_weights_t over host copies of ``weights`` (bf16 bits and fp32 gains); returns it with the arrays
+    that must outlive the call."""
+    bits, f32 = weights.bits, weights.f32
+    keep = []
+
+    def host(a, dtype):
+        arr = np.ascontiguousarray(a, dtype=dtype)
+        keep.append(arr)
+        return arr.ctypes.data
+
+    def per_layer(name, table, dtype):
+        arr = (VP * max(g["depth"], 1))(*[host(x, dtype) for x in table[name]])
+        keep.append(arr)
+        return arr
+
+    w = ube_weights_t()
+    if g["modality"] == "text":
+        w.embed = host(bits["embed"], np.uint16)
+    else:
+        w.patch_proj = host(bits["patch_proj"], np.uint16)
+    for name in ("w_qkv", "w_o", "w_gate", "w_up", "w_down"):
+        setattr(w, name, per_layer(name, bits, np.uint16))
+    for name in ("attn_norm", "mlp_norm"):
+        setattr(w, name, per_layer(name, f32, np.float32))
+    w.final_norm = host(f32["final_norm"], np.float32)
+    w.pool_query = host(bits["pool_query"], np.uint16)
+    w.pool_wk = host(bits["pool_wk"], np.uint16)
+    w.pool_wv = host(bits["pool_wv"], np.uint16)
+    if g.get("token_width"):
+        w.token_head = host(bits["token_head"], np.uint16)
+    return w, keep
+
+
 class Model:
     """A model on one GPU, built from host weights (``synth.Weights`` or a dict of the same names)."""
 
     def __init__(self, weights, device: int = 0):
         g = configs.complete(weights.geometry)
         self.geometry = g
-        bits, f32 = weights.bits, weights.f32
-        keep = []
-
-        def host(a, dtype):
-            arr = np.ascontiguousarray(a, dtype=dtype)
-            keep.append(arr)
-            return arr.ctypes.data
-
-        def per_layer(name, table, dtype):
-            arr = (VP * max(g["depth"], 1))(*[host(x, dtype) for x in table[name]])
-            keep.append(arr)
-            return arr
-
-        w = ube_weights_t()
-        if g["modality"] == "text":
-            w.embed = host(bits["embed"], np.uint16)
-        else:
-            w.patch_proj = host(bits["patch_proj"], np.uint16)
-        for name in ("w_qkv", "w_o", "w_gate", "w_up", "w_down"):
-            setattr(w, name, per_layer(name, bits, np.uint16))
-        for name in ("attn_norm", "mlp_norm"):
-            setattr(w, name, per_layer(name, f32, np.float32))
-        w.final_norm = host(f32["final_norm"], np.float32)
-        w.pool_query = host(bits["pool_query"], np.uint16)
-        w.pool_wk = host(bits["pool_wk"], np.uint16)
-        w.pool_wv = host(bits["pool_wv"], np.uint16)
-        if g.get("token_width"):
-            w.token_head = host(bits["token_head"], np.uint16)
+        w, keep = _weights_struct(weights, g)
         geo = ube_geometry_t(g["depth"], g["hidden"], g["heads"], g["ffn"], g["vocab"], g["context"], g["rope_axes"],
                              g["patch_side"], g["channels"], g["rope_base"], g["rms_epsilon"],
                              SCALAR[g["quantization"]], g.get("token_width", 0))
@@ -256,6 +290,7 @@ class Model:
         _check(outcome)
         self.handle = handle
         self.device = device
+        del keep
 
     def describe(self):
         d = ube_model_description_t()
@@ -448,6 +483,75 @@ def contrastive(arena: Arena, embeddings, scalars, *, anchor_begin=0, anchor_cou
     lib().ube_contrastive(C.byref(args))
     _check(outcome)
     return scalars, gradient
+
+
+class _DeviceArray:
+    """__cuda_array_interface__ over raw device memory (torch.as_tensor turns it into a view)."""
+
+    def __init__(self, ptr, shape, typestr):
+        self.__cuda_array_interface__ = {"shape": tuple(shape), "typestr": typestr, "data": (ptr or 0, False),
+                                         "version": 2}
+
+
+class Trainer:
+    """Training state of a text model on its GPU: bf16 masters (fp32 gains), fp32 gradients, Adafactor."""
+
+    def __init__(self, model: Model, weights, *, beta1=0.0, decay_rate=0.0, epsilon1=0.0, clip_threshold=0.0):
+        w, keep = _weights_struct(weights, model.geometry)
+        handle = VP()
+        outcome = ube_outcome_t()
+        args = ube_trainer_init_t(C.pointer(handle), C.pointer(outcome), model.handle, C.pointer(w), beta1,
+                                  decay_rate, epsilon1, clip_threshold)
+        lib().ube_trainer_init(C.byref(args))
+        _check(outcome)
+        del keep
+        self.handle = handle
+        self.model = model
+
+    def tensors(self):
+        """[(name, layer, master view, gradient view)] as torch tensors over the trainer's device memory."""
+        import torch
+        n = lib().ube_trainer_tensors(self.handle, None, 0)
+        arr = (ube_trainer_tensor_t * n)()
+        lib().ube_trainer_tensors(self.handle, arr, n)
+        out = []
+        for t in arr:
+            shape = (t.rows, t.cols) if t.cols else (t.rows,)
+            if t.master_scalar == SCALAR["bf16"]:
+                master = torch.as_tensor(_DeviceArray(t.master, shape, "<i2"), device="cuda").view(torch.bfloat16)
+            else:
+                master = torch.as_tensor(_DeviceArray(t.master, shape, "<f4"), device="cuda")
+            grad = torch.as_tensor(_DeviceArray(t.gradient, shape, "<f4"), device="cuda")
+            out.append((t.name.decode(), t.layer, master, grad))
+        return out
+
+    def backward(self, arena: Arena, data, offsets, d_embeddings, *, stream=None, completion=0):
+        off = np.ascontiguousarray(offsets, dtype=np.uint64)
+        tape = ube_tape_view_t(_ptr(data), off.ctypes.data_as(C.POINTER(SZ)), len(off) - 1)
+        outcome = ube_outcome_t()
+        stats = ube_encode_stats_t()
+        args = ube_trainer_backward_t(self.handle, arena.handle, _stream_handle(stream), C.pointer(outcome), completion,
+                                      tape, _ptr(d_embeddings), 0, C.pointer(stats))
+        lib().ube_trainer_backward(C.byref(args))
+        _check(outcome)
+        return stats.truncated, stats.tokens
+
+    def step(self, learning_rate, *, stream=None, completion=0):
+        outcome = ube_outcome_t()
+        args = ube_trainer_step_t(self.handle, _stream_handle(stream), C.pointer(outcome), completion, learning_rate)
+        lib().ube_trainer_step(C.byref(args))
+        _check(outcome)
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().ube_trainer_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def _tape(data, offsets):

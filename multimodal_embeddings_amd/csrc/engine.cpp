@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <atomic>
 #include <cmath>
 #include <cstring>
@@ -13,6 +14,7 @@
 
 #include "contrastive.h"
 #include "kernels.h"
+#include "train.h"
 #include "ube.h"
 #include "ube_steps.h"
 
@@ -581,6 +583,7 @@ struct EncodeRequest {
     unsigned outputs;
     ube_rows_tape_view_t *states;
     ube_rows_tape_view_t *token_vectors;
+    Layout *layout = nullptr;  // when set, receives the call's arena layout (the trainer reads cu, tiles, xf)
 };
 
 bool wants(unsigned outputs, ube_outputs_t o) { return (outputs ? outputs : ube_outputs_embeddings_k) & o; }
@@ -609,6 +612,7 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
     tok.width = g.token_width;
     tok.vector_bytes = bf16_out ? 2 : 4;
     Layout L = carve(g, p, media, input_bytes, m->e4m3, tok);
+    if (r.layout) *r.layout = L;
 
     // grow the arena (only when outgrown)
     if (L.total > ar->cap) {
@@ -840,35 +844,44 @@ void guarded(ube_outcome_t *outcome, ube_rows_view_t *embeddings, ube_rows_tape_
 
 }  // namespace
 
+namespace {
+
+// The plan of a byte tape: kept lengths, token prefix sums, item sources and tiles.
+Plan text_plan(ube_model_t model, ube_tape_view_t const &texts) {
+    const size_t count = texts.count;
+    if (count && (!texts.offsets || !texts.data)) throw Failure{ube_status_invalid_argument_k, "NULL tape"};
+    Plan p;
+    p.count = count;
+    p.cu.resize(count + 1);
+    std::vector<uint32_t> lengths(count), cu(count + 1);
+    ube_encode_stats_t st{};
+    static const size_t zero = 0;
+    if (ube_tape_plan(count ? texts.offsets : &zero, count, model->g.context, lengths.data(), cu.data(), &st) !=
+        ube_status_success_k)
+        throw Failure{ube_status_invalid_argument_k, "tape offsets decrease"};
+    p.T = st.tokens;
+    p.truncated = st.truncated;
+    p.src.resize(count);
+    for (size_t i = 0; i <= count; ++i) p.cu[i] = (int)cu[i];
+    for (size_t i = 0; i < count; ++i) p.src[i] = (int64_t)texts.offsets[i];
+    if (count) {
+        p.input_lo = texts.offsets[0];
+        p.input_hi = texts.offsets[0];
+        for (size_t i = 0; i < count; ++i) p.input_hi = std::max(p.input_hi, texts.offsets[i] + lengths[i]);
+    }
+    make_tiles(p);
+    return p;
+}
+
+}  // namespace
+
 extern "C" void ube_text_encode(ube_text_encode_t *a) {
     if (!a) return;
     guarded(a->outcome, a->embeddings, a->states, a->token_vectors, a->arena, [&] {
         check_common(a->model, a->arena, a->embeddings, a->outputs_scalar, a->outputs, a->states, a->token_vectors);
         if (!a->model->text) throw Failure{ube_status_unsupported_k, "the model has no byte frontend"};
         const size_t count = a->texts.count;
-        if (count && (!a->texts.offsets || !a->texts.data))
-            throw Failure{ube_status_invalid_argument_k, "NULL tape"};
-        Plan p;
-        p.count = count;
-        p.cu.resize(count + 1);
-        std::vector<uint32_t> lengths(count), cu(count + 1);
-        ube_encode_stats_t st{};
-        static const size_t zero = 0;
-        if (ube_tape_plan(count ? a->texts.offsets : &zero, count, a->model->g.context, lengths.data(), cu.data(),
-                          &st) != ube_status_success_k)
-            throw Failure{ube_status_invalid_argument_k, "tape offsets decrease"};
-        p.T = st.tokens;
-        p.truncated = st.truncated;
-        p.src.resize(count);
-        for (size_t i = 0; i <= count; ++i) p.cu[i] = (int)cu[i];
-        for (size_t i = 0; i < count; ++i) p.src[i] = (int64_t)a->texts.offsets[i];
-        if (count) {
-            p.input_lo = a->texts.offsets[0];
-            p.input_hi = a->texts.offsets[0];
-            for (size_t i = 0; i < count; ++i)
-                p.input_hi = std::max(p.input_hi, a->texts.offsets[i] + lengths[i]);
-        }
-        make_tiles(p);
+        Plan p = text_plan(a->model, a->texts);
         EncodeRequest r{a->model, a->arena, (hipStream_t)a->stream, a->completion, a->outputs_scalar,
                         a->embeddings, a->stats, a->trace_residual, a->texts.data, a->texts.offsets, count,
                         a->outputs, a->states, a->token_vectors};
@@ -1256,6 +1269,474 @@ extern "C" char const *ube_status_name(ube_status_t s) {
         case ube_status_internal_k: return "internal";
     }
     return "unknown";
+}
+
+// ===================================================================== trainer
+
+struct ube_trainer_handle_t {
+    ube_model_t model = nullptr;
+    int device = 0;
+    float beta1 = 0.9f, decay = -0.8f, eps1 = 1e-30f, clip = 1.0f;
+    size_t step = 0;
+    char *mem = nullptr;  // masters, derived packings, gradients, optimizer state
+    size_t bytes = 0;
+    struct Tensor {
+        char const *name;
+        size_t layer, rows, cols;  // cols == 0: a vector of `rows`
+        uint16_t *w16 = nullptr;   // bf16 master (matrices, the pool query)
+        float *w32 = nullptr;      // fp32 master (norm gains)
+        float *grad = nullptr, *r = nullptr, *c = nullptr, *v = nullptr, *m = nullptr;
+    };
+    std::vector<Tensor> tensors;
+    struct Block {  // indices into tensors, and packings derived from the masters
+        size_t qkv, o, gate, up, down, g1, g2;
+        uint16_t *qkvT, *oT, *guT, *dT, *gu_cols;
+    };
+    std::vector<Block> blocks;
+    size_t t_embed = 0, t_gf = 0, t_query = 0, t_wk = 0, t_wv = 0;
+    float *ada_work = nullptr;
+    // per-call workspace (grows)
+    char *ws = nullptr;
+    size_t ws_cap = 0;
+};
+
+namespace {
+
+// Workspace of one backward call for T tokens.
+struct TrainLayout {
+    size_t stash, h1, qk, vt, v, o, lse, delta, x1, h2, gu, dx, dxb, da, dgu, act, dh, dx1, dx1b, dout, dq, dk, dv,
+        dqkv, gpart, xty, dz, pd, z, du, dxf, tok_off, tok, total;
+    size_t Tpad, xty_splits, xty_chunk, rows_per_block;
+};
+
+TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count) {
+    TrainLayout L{};
+    const size_t D = g.hidden, F = g.ffn, H = g.heads, N = g.depth;
+    L.Tpad = align_up(T, 256) + kRowPad;
+    const size_t Tp = L.Tpad;
+    size_t total = 0;
+    auto take = [&](size_t bytes) {
+        size_t o = total;
+        total = align_up(total + bytes, 256);
+        return o;
+    };
+    L.stash = take((N + 1) * std::max<size_t>(T, 1) * D * 4);
+    L.h1 = take(Tp * D * 2);
+    L.qk = take(Tp * 2 * D * 2);
+    L.vt = take(D * Tp * 2);
+    L.v = take(Tp * D * 2);
+    L.o = take(Tp * D * 2);
+    L.lse = take(H * Tp * 4);
+    L.delta = take(H * Tp * 4);
+    L.x1 = take(Tp * D * 4);
+    L.h2 = take(Tp * D * 2);
+    L.gu = take(Tp * 2 * F * 2);
+    L.dx = take(Tp * D * 4);
+    L.dxb = take(Tp * D * 2);
+    L.da = take(Tp * F * 2);
+    L.dgu = take(Tp * 2 * F * 2);
+    L.act = take(Tp * F * 2);
+    L.dh = take(Tp * D * 4);
+    L.dx1 = take(Tp * D * 4);
+    L.dx1b = take(Tp * D * 2);
+    L.dout = take(Tp * D * 2);
+    L.dq = take(Tp * D * 2);
+    L.dk = take(Tp * D * 2);
+    L.dv = take(Tp * D * 2);
+    L.dqkv = take(Tp * 3 * D * 2);
+    L.rows_per_block = 64;
+    L.gpart = take((size_t)rmsnorm_bwd_blocks((int)std::max<size_t>(T, 1), (int)L.rows_per_block) * D * 4);
+    // weight gradients: about 8 ranges of tokens, each a multiple of 64
+    L.xty_chunk = align_up(std::max<size_t>((T + 7) / 8, 64), 64);
+    L.xty_splits = std::max<size_t>(1, (T + L.xty_chunk - 1) / L.xty_chunk);
+    L.xty = take(L.xty_splits * std::max(D * 3 * D, std::max(D * 2 * F, F * D)) * 4);
+    L.dz = take(std::max<size_t>(count, 1) * H * D * 4);
+    L.pd = take(Tp * H * 2 * 4);
+    L.z = take(std::max<size_t>(count, 1) * H * D * 4);
+    L.du = take(std::max<size_t>(count, 1) * H * D * 4);
+    L.dxf = take(Tp * D * 4);
+    L.tok_off = take((g.vocab + 1) * 4);
+    L.tok = take(std::max<size_t>(T, 1) * 4);
+    L.total = total;
+    return L;
+}
+
+// GEMM y = x W with W given as [N x K] K-contiguous (the kernels' packed layout)
+void gemm(int epi, const uint16_t *w, const uint16_t *x, int M, int N, int K, uint16_t *out_bf16, int ld_out,
+          float *out_f32, int ld_f32, hipStream_t st) {
+    GemmArgs ga{};
+    ga.w = w, ga.x = x, ga.M = M, ga.N = N, ga.K = K;
+    ga.out_bf16 = out_bf16, ga.ld_out = ld_out, ga.out_f32 = out_f32, ga.ld_f32 = ld_f32, ga.scale = 1.0f;
+    UBE_HIP(launch_gemm(epi, ga, st));
+}
+
+// Derived packings after the masters change: the trainer's unfolded [out x in] copies and interleaved
+// canonical gate/up columns, and the model's forward weights (gains folded, pool keys refolded).
+void repack(ube_trainer_t tr, hipStream_t st) {
+    ube_model_t m = tr->model;
+    const ube_geometry_t &g = m->g;
+    const int D = (int)g.hidden, F = (int)g.ffn, H = (int)g.heads;
+    auto &T = tr->tensors;
+    for (size_t l = 0; l < g.depth; ++l) {
+        auto const &b = tr->blocks[l];
+        auto &ml = m->layers[l];
+        UBE_HIP(launch_pack_transpose(T[b.qkv].w16, nullptr, nullptr, b.qkvT, D, 3 * D, false, st));
+        UBE_HIP(launch_pack_transpose(T[b.o].w16, nullptr, nullptr, b.oT, D, D, false, st));
+        UBE_HIP(launch_pack_transpose(T[b.gate].w16, T[b.up].w16, nullptr, b.guT, D, F, true, st));
+        UBE_HIP(launch_pack_transpose(T[b.down].w16, nullptr, nullptr, b.dT, F, D, false, st));
+        UBE_HIP(launch_interleave_cols(T[b.gate].w16, T[b.up].w16, b.gu_cols, D, F, st));
+        UBE_HIP(launch_pack_transpose(T[b.qkv].w16, nullptr, T[b.g1].w32, ml.wqkv, D, 3 * D, false, st));
+        UBE_HIP(launch_pack_transpose(T[b.o].w16, nullptr, nullptr, ml.wo, D, D, false, st));
+        UBE_HIP(launch_pack_transpose(T[b.gate].w16, T[b.up].w16, T[b.g2].w32, ml.wgu, D, F, true, st));
+        UBE_HIP(launch_pack_transpose(T[b.down].w16, nullptr, nullptr, ml.wd, F, D, false, st));
+        UBE_HIP(hipMemcpyAsync(ml.g1, T[b.g1].w32, D * 4, hipMemcpyDeviceToDevice, st));
+        UBE_HIP(hipMemcpyAsync(ml.g2, T[b.g2].w32, D * 4, hipMemcpyDeviceToDevice, st));
+    }
+    UBE_HIP(hipMemcpyAsync(m->embed, T[tr->t_embed].w16, g.vocab * D * 2, hipMemcpyDeviceToDevice, st));
+    UBE_HIP(hipMemcpyAsync(m->gf, T[tr->t_gf].w32, D * 4, hipMemcpyDeviceToDevice, st));
+    UBE_HIP(hipMemcpyAsync(m->wv, T[tr->t_wv].w16, (size_t)D * D * 2, hipMemcpyDeviceToDevice, st));
+    UBE_HIP(launch_pool_u(T[tr->t_wk].w16, T[tr->t_query].w16, m->u, D, H, st));
+}
+
+}  // namespace
+
+extern "C" void ube_trainer_init(ube_trainer_init_t *a) {
+    if (!a) return;
+    if (a->trainer) *a->trainer = nullptr;
+    ube_trainer_t tr = nullptr;
+    try {
+        if (!a->trainer || !a->model || !a->weights) throw Failure{ube_status_invalid_argument_k, "NULL trainer, model or weights"};
+        ube_model_t m = a->model;
+        const ube_geometry_t &g = m->g;
+        if (!m->text) throw Failure{ube_status_unsupported_k, "training runs text models"};
+        if (m->e4m3) throw Failure{ube_status_unsupported_k, "training runs bf16 models (E4M3 is inference-only)"};
+        if (g.rope_axes != 1) throw Failure{ube_status_unsupported_k, "training runs 1-axis rotary"};
+        if (g.hidden > 1024 || g.heads > 16) throw Failure{ube_status_unsupported_k, "training runs hidden <= 1024"};
+        ube_weights_t const &w = *a->weights;
+        if (!w.embed || !w.w_qkv || !w.w_o || !w.w_gate || !w.w_up || !w.w_down || !w.attn_norm || !w.mlp_norm ||
+            !w.final_norm || !w.pool_query || !w.pool_wk || !w.pool_wv)
+            throw Failure{ube_status_invalid_argument_k, "missing weights"};
+        UBE_HIP(hipSetDevice(m->device));
+        const size_t D = g.hidden, F = g.ffn, N = g.depth, V = g.vocab;
+        tr = new ube_trainer_handle_t();
+        tr->model = m;
+        tr->device = m->device;
+        if (a->beta1 > 0.f) tr->beta1 = a->beta1;
+        if (a->decay_rate < 0.f) tr->decay = a->decay_rate;
+        if (a->epsilon1 > 0.f) tr->eps1 = a->epsilon1;
+        if (a->clip_threshold > 0.f) tr->clip = a->clip_threshold;
+        // tensors in a fixed order: embed, blocks, final gain, pool query, W_k, W_v
+        auto add = [&](char const *name, size_t layer, size_t rows, size_t cols) {
+            tr->tensors.push_back(ube_trainer_handle_t::Tensor{name, layer, rows, cols});
+            return tr->tensors.size() - 1;
+        };
+        tr->t_embed = add("embed", 0, V, D);
+        tr->blocks.resize(N);
+        for (size_t l = 0; l < N; ++l) {
+            auto &b = tr->blocks[l];
+            b.g1 = add("attn_norm", l, D, 0);
+            b.qkv = add("w_qkv", l, D, 3 * D);
+            b.o = add("w_o", l, D, D);
+            b.g2 = add("mlp_norm", l, D, 0);
+            b.gate = add("w_gate", l, D, F);
+            b.up = add("w_up", l, D, F);
+            b.down = add("w_down", l, F, D);
+        }
+        tr->t_gf = add("final_norm", 0, D, 0);
+        tr->t_query = add("pool_query", 0, D, 0);
+        tr->t_wk = add("pool_wk", 0, D, D);
+        tr->t_wv = add("pool_wv", 0, D, D);
+        // device memory
+        size_t total = 0;
+        auto take = [&](size_t bytes) {
+            size_t o = total;
+            total = align_up(total + bytes, 256);
+            return o;
+        };
+        std::vector<std::array<size_t, 6>> offs(tr->tensors.size());
+        for (size_t i = 0; i < tr->tensors.size(); ++i) {
+            auto const &t = tr->tensors[i];
+            const size_t n = t.rows * (t.cols ? t.cols : 1);
+            const bool fp32_master = t.cols == 0 && std::strcmp(t.name, "pool_query") != 0;
+            offs[i][0] = take(n * (fp32_master ? 4 : 2));
+            offs[i][1] = take(n * 4);                    // gradient
+            offs[i][2] = take(t.cols ? t.rows * 4 : 0);  // r
+            offs[i][3] = take(t.cols ? t.cols * 4 : 0);  // c
+            offs[i][4] = take(t.cols ? 0 : n * 4);       // v
+            offs[i][5] = take(n * 4);                    // m
+        }
+        std::vector<std::array<size_t, 5>> boffs(N);
+        for (size_t l = 0; l < N; ++l)
+            boffs[l] = {take(3 * D * D * 2), take(D * D * 2), take(2 * F * D * 2), take(F * D * 2), take(2 * F * D * 2)};
+        const size_t o_work = take(kAdafactorWork * 4);
+        UBE_HIP(hipMalloc((void **)&tr->mem, total));
+        tr->bytes = total;
+        UBE_HIP(hipMemset(tr->mem, 0, total));
+        char *db = tr->mem;
+        for (size_t i = 0; i < tr->tensors.size(); ++i) {
+            auto &t = tr->tensors[i];
+            const bool fp32_master = t.cols == 0 && std::strcmp(t.name, "pool_query") != 0;
+            if (fp32_master) t.w32 = (float *)(db + offs[i][0]);
+            else t.w16 = (uint16_t *)(db + offs[i][0]);
+            t.grad = (float *)(db + offs[i][1]);
+            t.r = t.cols ? (float *)(db + offs[i][2]) : nullptr;
+            t.c = t.cols ? (float *)(db + offs[i][3]) : nullptr;
+            t.v = t.cols ? nullptr : (float *)(db + offs[i][4]);
+            t.m = (float *)(db + offs[i][5]);
+        }
+        for (size_t l = 0; l < N; ++l) {
+            auto &b = tr->blocks[l];
+            b.qkvT = (uint16_t *)(db + boffs[l][0]);
+            b.oT = (uint16_t *)(db + boffs[l][1]);
+            b.guT = (uint16_t *)(db + boffs[l][2]);
+            b.dT = (uint16_t *)(db + boffs[l][3]);
+            b.gu_cols = (uint16_t *)(db + boffs[l][4]);
+        }
+        tr->ada_work = (float *)(db + o_work);
+        // masters from the caller's canonical weights
+        auto up16 = [&](size_t i, uint16_t const *src) {
+            auto const &t = tr->tensors[i];
+            UBE_HIP(hipMemcpy(t.w16, src, t.rows * (t.cols ? t.cols : 1) * 2, hipMemcpyHostToDevice));
+        };
+        auto up32 = [&](size_t i, float const *src) {
+            UBE_HIP(hipMemcpy(tr->tensors[i].w32, src, tr->tensors[i].rows * 4, hipMemcpyHostToDevice));
+        };
+        up16(tr->t_embed, w.embed);
+        for (size_t l = 0; l < N; ++l) {
+            auto const &b = tr->blocks[l];
+            up32(b.g1, w.attn_norm[l]);
+            up16(b.qkv, w.w_qkv[l]);
+            up16(b.o, w.w_o[l]);
+            up32(b.g2, w.mlp_norm[l]);
+            up16(b.gate, w.w_gate[l]);
+            up16(b.up, w.w_up[l]);
+            up16(b.down, w.w_down[l]);
+        }
+        up32(tr->t_gf, w.final_norm);
+        up16(tr->t_query, w.pool_query);
+        up16(tr->t_wk, w.pool_wk);
+        up16(tr->t_wv, w.pool_wv);
+        repack(tr, nullptr);
+        UBE_HIP(hipDeviceSynchronize());
+        *a->trainer = tr;
+        set_outcome(a->outcome, ube_status_success_k, nullptr);
+    } catch (Failure const &f) {
+        if (tr) {
+            if (tr->mem) (void)hipFree(tr->mem);
+            delete tr;
+        }
+        set_outcome(a->outcome, f.status, f.message);
+    } catch (std::bad_alloc const &) {
+        if (tr) {
+            if (tr->mem) (void)hipFree(tr->mem);
+            delete tr;
+        }
+        set_outcome(a->outcome, ube_status_out_of_memory_k, "host out of memory");
+    }
+}
+
+extern "C" void ube_trainer_free(ube_trainer_t tr) {
+    if (!tr) return;
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    (void)hipSetDevice(tr->device);
+    (void)hipDeviceSynchronize();
+    if (tr->mem) (void)hipFree(tr->mem);
+    if (tr->ws) (void)hipFree(tr->ws);
+    (void)hipSetDevice(prev);
+    delete tr;
+}
+
+extern "C" size_t ube_trainer_tensors(ube_trainer_t tr, ube_trainer_tensor_t *out, size_t capacity) {
+    if (!tr) return 0;
+    for (size_t i = 0; i < tr->tensors.size() && i < capacity && out; ++i) {
+        auto const &t = tr->tensors[i];
+        out[i] = ube_trainer_tensor_t{t.name, t.layer, t.rows, t.cols, t.w16 ? (void *)t.w16 : (void *)t.w32,
+                                      t.w16 ? ube_scalar_bf16_k : ube_scalar_f32_k, t.grad};
+    }
+    return tr->tensors.size();
+}
+
+extern "C" void ube_trainer_backward(ube_trainer_backward_t *a) {
+    if (!a) return;
+    try {
+        if (!a->trainer || !a->arena) throw Failure{ube_status_invalid_argument_k, "NULL trainer or arena"};
+        ube_trainer_t tr = a->trainer;
+        ube_model_t m = tr->model;
+        const ube_geometry_t &g = m->g;
+        if (a->arena->device != tr->device) throw Failure{ube_status_device_k, "arena and trainer on different GPUs"};
+        const size_t D = g.hidden, F = g.ffn, H = g.heads, N = g.depth, V = g.vocab;
+        const float eps = g.rms_epsilon;
+        const size_t count = a->texts.count;
+        if (count && !a->d_embeddings) throw Failure{ube_status_invalid_argument_k, "NULL embedding gradient"};
+        if (count && a->d_embeddings_stride && a->d_embeddings_stride != D * 4)
+            throw Failure{ube_status_unsupported_k, "embedding gradient rows must be packed"};
+        ArenaLease lease(a->arena);  // the replayed forward's rows (xf, scores, tiles) stay in the arena
+        if (!lease.held) throw Failure{ube_status_contended_k, "the arena is serving another call"};
+        Plan p = text_plan(m, a->texts);
+        const size_t T = p.T;
+        UBE_HIP(hipSetDevice(tr->device));
+        hipStream_t st = (hipStream_t)a->stream;
+        // byte of every kept token, grouped by value in token order (the embedding gradient's fixed order)
+        std::vector<uint8_t> bytes(p.input_hi - p.input_lo);
+        if (!bytes.empty()) {
+            const bool dev = pointer_on_device(a->texts.data, tr->device);
+            const char *src = (const char *)a->texts.data + p.input_lo;
+            if (dev) UBE_HIP(hipMemcpy(bytes.data(), src, bytes.size(), hipMemcpyDeviceToHost));
+            else std::memcpy(bytes.data(), src, bytes.size());
+        }
+        std::vector<uint32_t> tok_off(V + 1, 0), tok(std::max<size_t>(T, 1));
+        for (size_t i = 0; i < count; ++i)
+            for (int t = p.cu[i]; t < p.cu[i + 1]; ++t) ++tok_off[bytes[p.src[i] - p.input_lo + (t - p.cu[i])] + 1];
+        for (size_t v = 0; v < V; ++v) tok_off[v + 1] += tok_off[v];
+        {
+            std::vector<uint32_t> fill(tok_off.begin(), tok_off.end() - 1);
+            for (size_t i = 0; i < count; ++i)
+                for (int t = p.cu[i]; t < p.cu[i + 1]; ++t)
+                    tok[fill[bytes[p.src[i] - p.input_lo + (t - p.cu[i])]]++] = (uint32_t)t;
+        }
+        // workspace
+        TrainLayout L = train_carve(g, T, count);
+        if (L.total > tr->ws_cap) {
+            UBE_HIP(hipStreamSynchronize(st));
+            if (tr->ws) UBE_HIP(hipFree(tr->ws));
+            tr->ws = nullptr;
+            tr->ws_cap = 0;
+            const size_t want = align_up(L.total, (size_t)1 << 20);
+            UBE_HIP(hipMalloc((void **)&tr->ws, want));
+            tr->ws_cap = want;
+            UBE_HIP(hipMemsetAsync(tr->ws, 0, want, st));
+        }
+        char *wb = tr->ws;
+        auto F32 = [&](size_t o) { return (float *)(wb + o); };
+        auto B16 = [&](size_t o) { return (uint16_t *)(wb + o); };
+        UBE_HIP(hipMemcpyAsync(wb + L.tok_off, tok_off.data(), (V + 1) * 4, hipMemcpyHostToDevice, st));
+        UBE_HIP(hipMemcpyAsync(wb + L.tok, tok.data(), tok.size() * 4, hipMemcpyHostToDevice, st));
+        // forward with the block inputs stashed (fp32), leaving xf, scores, cu, tiles and positions in the arena
+        Layout EL{};
+        ube_rows_view_t rows{};
+        {
+            EncodeRequest r{m, a->arena, st, 1, ube_scalar_f32_k, &rows, a->stats, F32(L.stash), a->texts.data,
+                            a->texts.offsets, count, 0, nullptr, nullptr, &EL};
+            run_encode(r, p, false);
+        }
+        if (T == 0) {
+            for (auto const &t : tr->tensors)
+                UBE_HIP(hipMemsetAsync(t.grad, 0, t.rows * (t.cols ? t.cols : 1) * 4, st));
+            if (a->completion == 0) UBE_HIP(hipStreamSynchronize(st));
+            set_outcome(a->outcome, ube_status_success_k, nullptr);
+            return;
+        }
+        char *ab = a->arena->dev;
+        const int *cu = (const int *)(ab + EL.cu);
+        const int2 *tiles = (const int2 *)(ab + EL.tiles);
+        const int ntiles = (int)p.tiles.size();
+        const int16_t *pos = (const int16_t *)(ab + EL.pos);
+        const uint16_t *xf = (const uint16_t *)(ab + EL.xf);
+        const float *sc = (const float *)(ab + EL.s);
+        auto &TT = tr->tensors;
+        const int Ti = (int)T, Di = (int)D, Fi = (int)F, Hi = (int)H;
+        const int ldvt = (int)L.Tpad, ldl = (int)L.Tpad;
+        const int blocks = rmsnorm_bwd_blocks(Ti, (int)L.rows_per_block);
+        auto xty = [&](const uint16_t *x, int M, const uint16_t *y, int Nn, float *out, float *out2, bool di) {
+            UBE_HIP(launch_xty(x, M, y, Nn, Ti, M, Nn, F32(L.xty), (int)L.xty_splits, (int)L.xty_chunk, out, out2, di, st));
+        };
+        // ---- pool and final norm
+        PoolBwdArgs pa{};
+        pa.xf = xf, pa.s = sc, pa.cu = cu, pa.count = (int)count, pa.D = Di, pa.H = Hi, pa.u = m->u;
+        pa.wv = TT[tr->t_wv].w16, pa.wk = TT[tr->t_wk].w16, pa.query = TT[tr->t_query].w16;
+        pa.dpooled = a->d_embeddings;
+        pa.dxf = F32(L.dxf), pa.z = F32(L.z), pa.du = F32(L.du);
+        pa.dwv = TT[tr->t_wv].grad, pa.dwk = TT[tr->t_wk].grad, pa.dquery = TT[tr->t_query].grad;
+        UBE_HIP(launch_pool_bwd(pa, F32(L.dz), F32(L.pd), st));
+        UBE_HIP(launch_rmsnorm_bwd(F32(L.stash) + N * T * D, TT[tr->t_gf].w32, F32(L.dxf), nullptr, F32(L.dx), B16(L.dxb),
+                                   F32(L.gpart), (int)L.rows_per_block, Ti, Di, eps, st));
+        UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[tr->t_gf].grad, st));
+        // ---- blocks, last to first: replay the forward from the stashed input, then its backward
+        for (size_t li = N; li-- > 0;) {
+            auto const &b = tr->blocks[li];
+            const float *x_in = F32(L.stash) + li * T * D;
+            uint16_t *h1 = B16(L.h1), *qk = B16(L.qk), *vt = B16(L.vt), *v = B16(L.v), *o = B16(L.o);
+            float *lse = F32(L.lse), *delta = F32(L.delta), *x1 = F32(L.x1);
+            uint16_t *h2 = B16(L.h2), *gu = B16(L.gu);
+            // replay
+            UBE_HIP(launch_rmsnorm(x_in, TT[b.g1].w32, h1, Ti, Di, eps, st));
+            UBE_HIP(hipMemset2DAsync(vt + T, (size_t)ldvt * 2, 0, 64 * 2, D, st));
+            GemmArgs qa{};
+            qa.w = b.qkvT, qa.x = h1, qa.M = Ti, qa.N = 3 * Di, qa.K = Di;
+            qa.out_bf16 = qk, qa.ld_out = 2 * Di, qa.vt = vt, qa.ld_vt = ldvt, qa.pos = pos, qa.rope = m->rope;
+            qa.D = Di, qa.sec0 = m->sec0, qa.sec1 = m->sec1;
+            UBE_HIP(launch_gemm(kEpiQkv, qa, st));
+            UBE_HIP(launch_attention(qk, qk + D, 2 * Di, vt, ldvt, o, Di, cu, tiles, ntiles, Hi, st, lse, ldl));
+            UBE_HIP(launch_vt_rows(vt, ldvt, v, Ti, Di, st));
+            UBE_HIP(hipMemcpyAsync(x1, x_in, T * D * 4, hipMemcpyDeviceToDevice, st));
+            gemm(kEpiResid, b.oT, o, Ti, Di, Di, nullptr, 0, x1, Di, st);
+            UBE_HIP(launch_rmsnorm(x1, TT[b.g2].w32, h2, Ti, Di, eps, st));
+            gemm(kEpiStore, b.guT, h2, Ti, 2 * Fi, Di, gu, 2 * Fi, nullptr, 0, st);
+            // MLP half
+            float *dx = F32(L.dx), *dh = F32(L.dh), *dx1 = F32(L.dx1);
+            uint16_t *dxb = B16(L.dxb), *da = B16(L.da), *dgu = B16(L.dgu), *act = B16(L.act), *dx1b = B16(L.dx1b);
+            gemm(kEpiStore, TT[b.down].w16, dxb, Ti, Fi, Di, da, Fi, nullptr, 0, st);
+            UBE_HIP(launch_swiglu_bwd(gu, da, dgu, act, Ti, Fi, st));
+            xty(act, Fi, dxb, Di, TT[b.down].grad, nullptr, false);
+            gemm(kEpiPatch, b.gu_cols, dgu, Ti, Di, 2 * Fi, nullptr, 0, dh, Di, st);
+            xty(h2, Di, dgu, 2 * Fi, TT[b.gate].grad, TT[b.up].grad, true);
+            UBE_HIP(launch_rmsnorm_bwd(x1, TT[b.g2].w32, dh, dx, dx1, dx1b, F32(L.gpart), (int)L.rows_per_block, Ti, Di,
+                                       eps, st));
+            UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[b.g2].grad, st));
+            // attention half
+            uint16_t *dout = B16(L.dout), *dq = B16(L.dq), *dk = B16(L.dk), *dv = B16(L.dv), *dqkv = B16(L.dqkv);
+            gemm(kEpiStore, TT[b.o].w16, dx1b, Ti, Di, Di, dout, Di, nullptr, 0, st);
+            xty(o, Di, dx1b, Di, TT[b.o].grad, nullptr, false);
+            UBE_HIP(launch_attention_delta(dout, o, Di, delta, ldl, Ti, Hi, st));
+            AttnBwdArgs ab2{};
+            ab2.q = qk, ab2.k = qk + D, ab2.ldqk = 2 * Di, ab2.v = v, ab2.ldv = Di, ab2.dout = dout, ab2.lddo = Di;
+            ab2.lse = lse, ab2.delta = delta, ab2.ldl = ldl, ab2.dq = dq, ab2.dk = dk, ab2.dv = dv, ab2.ldd = Di;
+            ab2.cu = cu, ab2.tiles = tiles, ab2.ntiles = ntiles, ab2.heads = Hi;
+            UBE_HIP(launch_attention_bwd(ab2, st));
+            UBE_HIP(launch_rope_bwd(dq, dk, dv, Di, pos, m->rope, dqkv, Ti, Di, st));
+            gemm(kEpiPatch, TT[b.qkv].w16, dqkv, Ti, Di, 3 * Di, nullptr, 0, dh, Di, st);
+            xty(h1, Di, dqkv, 3 * Di, TT[b.qkv].grad, nullptr, false);
+            UBE_HIP(launch_rmsnorm_bwd(x_in, TT[b.g1].w32, dh, dx1, dx, dxb, F32(L.gpart), (int)L.rows_per_block, Ti, Di,
+                                       eps, st));
+            UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[b.g1].grad, st));
+        }
+        UBE_HIP(launch_embed_bwd(F32(L.dx), (const uint32_t *)(wb + L.tok_off), (const uint32_t *)(wb + L.tok), (int)V,
+                                 Di, TT[tr->t_embed].grad, st));
+        if (a->completion == 0) UBE_HIP(hipStreamSynchronize(st));
+        set_outcome(a->outcome, ube_status_success_k, nullptr);
+    } catch (Failure const &f) {
+        set_outcome(a->outcome, f.status, f.message);
+    } catch (std::bad_alloc const &) {
+        set_outcome(a->outcome, ube_status_out_of_memory_k, "host out of memory");
+    }
+}
+
+extern "C" void ube_trainer_step(ube_trainer_step_t *a) {
+    if (!a) return;
+    try {
+        if (!a->trainer) throw Failure{ube_status_invalid_argument_k, "NULL trainer"};
+        ube_trainer_t tr = a->trainer;
+        UBE_HIP(hipSetDevice(tr->device));
+        hipStream_t st = (hipStream_t)a->stream;
+        tr->step += 1;
+        const double t = (double)tr->step;
+        const float beta2 = (float)(1.0 - std::pow(t, (double)tr->decay));
+        const float bc = (float)(1.0 - std::pow((double)tr->beta1, t));
+        for (auto const &ts : tr->tensors) {
+            AdafactorArgs ad{};
+            ad.g = ts.grad, ad.w16 = ts.w16, ad.w32 = ts.w32, ad.r = ts.r, ad.c = ts.c, ad.v = ts.v, ad.m = ts.m;
+            ad.work = tr->ada_work, ad.rows = (int)ts.rows, ad.cols = (int)ts.cols;
+            ad.lr = a->learning_rate, ad.beta1 = tr->beta1, ad.beta2 = beta2, ad.eps1 = tr->eps1, ad.clip = tr->clip;
+            ad.bias_correction = bc;
+            UBE_HIP(launch_adafactor(ad, st));
+        }
+        repack(tr, st);
+        if (a->completion == 0) UBE_HIP(hipStreamSynchronize(st));
+        set_outcome(a->outcome, ube_status_success_k, nullptr);
+    } catch (Failure const &f) {
+        set_outcome(a->outcome, f.status, f.message);
+    }
 }
 
 // ===================================================================== steps

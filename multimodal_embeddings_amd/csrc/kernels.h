@@ -76,9 +76,11 @@ hipError_t launch_quantize_rows(const uint16_t *in, uint8_t *out, float *scale, 
 hipError_t launch_rmsnorm(const float *x, const float *gain, uint16_t *h, int T, int D, float eps,
                           hipStream_t stream);
 
+// lse (optional, head-major [heads x ldl]): log2 of each query's softmax denominator in units of
+// log2(e) q.k / 8, for the backward pass
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, int ldqk, const uint16_t *vt, int ldvt,
                             uint16_t *o, int ldo, const int *cu, const int2 *tiles, int ntiles, int heads,
-                            hipStream_t stream);
+                            hipStream_t stream, float *lse = nullptr, int ldl = 0);
 
 // Final RMSNorm -> xf (bf16) and pool scores s[t][h] = xf_t . u_h (fp32).
 hipError_t launch_final_norm_scores(const float *x, const float *gain, const float *u, uint16_t *xf, float *s,

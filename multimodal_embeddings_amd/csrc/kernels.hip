@@ -1189,7 +1189,8 @@ __device__ __forceinline__ int perm32(int r) {  // r = 8 i + 4 h + j
 __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                       int ldqk, const uint16_t *__restrict__ vt, int ldvt,
                                                       uint16_t *__restrict__ o, int ldo, const int *__restrict__ cu,
-                                                      const int2 *__restrict__ tiles, int ntiles) {
+                                                      const int2 *__restrict__ tiles, int ntiles,
+                                                      float *__restrict__ lse, int ldl) {
     constexpr int NS = 4;
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int head = logical / ntiles, ti = logical % ntiles;
@@ -1338,14 +1339,17 @@ __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict
                     u32x2{pack2(O[dt][i * 4 + 0] * inv, O[dt][i * 4 + 1] * inv),
                           pack2(O[dt][i * 4 + 2] * inv, O[dt][i * 4 + 3] * inv)};
             }
+        // log2 of the softmax denominator in the pre-scaled (base-2) logit units, head-major; the
+        // backward pass rebuilds the weights from it
+        if (lse && hh == 0) lse[(size_t)head * ldl + qrow] = m_run + __log2f(l_tot);
     }
 }
 
 hipError_t launch_attention(const uint16_t *q, const uint16_t *k, int ldqk, const uint16_t *vt, int ldvt,
                             uint16_t *o, int ldo, const int *cu, const int2 *tiles, int ntiles, int heads,
-                            hipStream_t stream) {
+                            hipStream_t stream, float *lse, int ldl) {
     if (ntiles == 0) return hipSuccess;
-    k_attention<<<ntiles * heads, 512, 0, stream>>>(q, k, ldqk, vt, ldvt, o, ldo, cu, tiles, ntiles);
+    k_attention<<<ntiles * heads, 512, 0, stream>>>(q, k, ldqk, vt, ldvt, o, ldo, cu, tiles, ntiles, lse, ldl);
     return hipGetLastError();
 }
 

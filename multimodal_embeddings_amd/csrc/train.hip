@@ -1,0 +1,893 @@
+// train.hip -- gfx950 kernels of the text encoder's backward pass and of the Adafactor update.
+//
+// What is computed: "UForm" page, "Precision by Design" (bf16 storage and matrix products with fp32
+// accumulation; gradients accumulated in fp32; every block's backward replays its forward from the
+// block's fp32 input) and "Adafactor Optimizer" (factored second moment, clipped update, first moment
+// with Adam's bias correction; bf16 master weights, fp32 norm gains).
+//
+// The products of the backward pass reuse the forward's GEMM kernel (activation gradients: dY W^T reads
+// the canonical [in x out] weights, which are K-contiguous for that product). This file adds the weight
+// gradients X^T Y (both operands token-major: read through the LDS transpose load), attention backward,
+// and the row kernels (RMSNorm, SwiGLU and rotary backward, the pool and the byte embedding).
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "device.h"
+#include "train.h"
+
+namespace ube {
+
+namespace {
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ s16x4 tr16(const uint8_t *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
+}
+
+__device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
+    const s16x8 v = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// MFMA A operand whose k runs down the rows of an LDS tile [rows][64 bf16] (128-byte rows, 16-byte chunks
+// swizzled by swz): lane l receives column c0 + l % 32 at the 8 k slots of half hh = l / 32, slot q being
+// row kb + 4 hh + (q % 4) + 8 (q / 4) -- the order in which a 32x32 MFMA result holds its rows in
+// registers 8s .. 8s + 7 (kb = 16 s), so such an accumulator, packed to bf16, is the matching B operand.
+// ds_read_b64_tr_b16: lane i = 4a + b of a 16-lane group receives element b of the 8 bytes read by lanes
+// 4e + a of the group, as its element e.
+__device__ __forceinline__ bf16x8 tr_rows_frag(const uint8_t *tile, int kb, int c0, int lane) {
+    const int g = lane >> 4, i = lane & 15, hh = g >> 1;
+    const int col = c0 + 16 * (g & 1) + 4 * (i & 3);
+    const int chunk = col >> 3, half = (col >> 2) & 1;
+    const int r0 = kb + 4 * hh + (i >> 2), r1 = r0 + 8;
+    const uint8_t *p0 = tile + r0 * 128 + (swz(r0, chunk) << 4) + (half << 3);
+    const uint8_t *p1 = tile + r1 * 128 + (swz(r1, chunk) << 4) + (half << 3);
+    return join(tr16(p0), tr16(p1));
+}
+
+// MFMA operand whose k runs down the rows of an LDS tile of PITCH-byte rows in plain k order (rows kb + 8 hh
+// + 0..7), chunks XOR-swizzled by 4 ((r / 2) % 2) (128-byte rows) or 4 (r % 4) (256 bytes and more).
+template <int PITCH>
+__device__ __forceinline__ int kmajor_swz(int r) {
+    return PITCH == 128 ? 4 * ((r >> 1) & 1) : 4 * (r & 3);
+}
+
+template <int PITCH>
+__device__ __forceinline__ bf16x8 tr_frag(const uint8_t *tile, int kb, int c0, int lane) {
+    const int g = lane >> 4, i = lane & 15;
+    const int col = c0 + 16 * (g & 1) + 4 * (i & 3);
+    const int chunk = col >> 3, half = (col >> 2) & 1;
+    const int r0 = kb + 8 * (g >> 1) + (i >> 2), r1 = r0 + 4;
+    const uint8_t *p0 = tile + r0 * PITCH + ((chunk ^ kmajor_swz<PITCH>(r0)) << 4) + (half << 3);
+    const uint8_t *p1 = tile + r1 * PITCH + ((chunk ^ kmajor_swz<PITCH>(r1)) << 4) + (half << 3);
+    return join(tr16(p0), tr16(p1));
+}
+
+__device__ __forceinline__ bf16x8 pack8(const f32x16 &v, int s) {
+    const u32x4 w = {pack2(v[8 * s], v[8 * s + 1]), pack2(v[8 * s + 2], v[8 * s + 3]), pack2(v[8 * s + 4], v[8 * s + 5]),
+                     pack2(v[8 * s + 6], v[8 * s + 7])};
+    return __builtin_bit_cast(bf16x8, w);
+}
+
+__device__ __forceinline__ u32x4 load16(const uint16_t *p) { return *(const u32x4 *)p; }
+
+// ----------------------------------------------------------------------------------- attention backward
+//
+// Notation per head: s = q.k / 8 (natural units), P = softmax over the item's keys, rebuilt as
+// 2^(log2(e) s - lse) from the forward's base-2 log denominators; dP = dO V^T; dS = P (dP - delta) with
+// delta = rowsum(dO O); dQ = dS K / 8, dK = dS^T Q / 8, dV = P^T dO.
+// Two kernels, 8 waves x 32 rows per workgroup (one 256-token tile of one item and head), 64-row tiles of
+// the other side double-buffered in LDS by DMA (16-byte chunks swizzled by swz):
+//   dQ: S^T = K Q^T and dP^T = V dO^T (a lane holds one query and 16 keys), dQ^T += K^T dS^T;
+//   dK, dV: S = Q K^T and dP = dO V^T (a lane holds one key and 16 queries), dV^T += dO^T P,
+//           dK^T += Q^T dS.
+// The second product of each pair reads its A operand through the transpose load in the row order of the
+// accumulator, so the accumulators feed it as B operands without leaving registers.
+
+constexpr float kScale2 = 0.18033688011112042f;  // log2(e) / 8
+
+__global__ __launch_bounds__(512, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * 1024];  // stage: K tile 512 | V tile 512 chunks
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int head = logical / a.ntiles, ti = logical % a.ntiles;
+    const int2 tile = a.tiles[ti];
+    const int k0 = a.cu[tile.x], k1 = a.cu[tile.x + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+    const int qbase = tile.y + wave * 32;
+    const bool active = qbase < k1;
+    const bool qvalid = qbase + l32 < k1;
+    const int t = min(qbase + l32, k1 - 1);
+    bf16x8 qf[4], dof[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        qf[ks] = __builtin_bit_cast(bf16x8, load16(a.q + (size_t)t * a.ldqk + head * 64 + ks * 16 + hh * 8));
+        dof[ks] = __builtin_bit_cast(bf16x8, load16(a.dout + (size_t)t * a.lddo + head * 64 + ks * 16 + hh * 8));
+    }
+    const float lse2 = a.lse[(size_t)head * a.ldl + t], dlt = a.delta[(size_t)head * a.ldl + t];
+    const int prow = tid >> 3, pc = swz(prow, tid & 7);
+    auto issue = [&](int tt, int buf) {
+        const int row = min(k0 + tt * 64 + prow, k1 - 1);
+        u32x4 *dst = smem + buf * 1024;
+        lds_dma16(a.k + (size_t)row * a.ldqk + head * 64 + pc * 8, dst + wave * 64);
+        lds_dma16(a.v + (size_t)row * a.ldv + head * 64 + pc * 8, dst + 512 + wave * 64);
+    };
+    f32x16 dQ[2] = {f32x16{}, f32x16{}};
+    const int ntile = (k1 - k0 + 63) >> 6;
+    issue(0, 0);
+    for (int tt = 0; tt < ntile; ++tt) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();  // tile tt landed for every wave; every wave is done with tile tt - 1
+        if (tt + 1 < ntile) issue(tt + 1, (tt + 1) & 1);
+        if (!active) continue;
+        const u32x4 *sK = smem + (tt & 1) * 1024, *sV = sK + 512;
+        const int kt = k0 + tt * 64;
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            f32x16 S = f32x16{}, dP = f32x16{};
+            const int row = kk * 32 + l32;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int ch = swz(row, ks * 2 + hh);
+                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sK[row * 8 + ch]), qf[ks], S, 0, 0, 0);
+                dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sV[row * 8 + ch]), dof[ks], dP, 0, 0,
+                                                             0);
+            }
+            f32x16 dS;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int u = kt + kk * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const float p = (u < k1 && qvalid) ? __builtin_amdgcn_exp2f(S[r] * kScale2 - lse2) : 0.f;
+                dS[r] = p * (dP[r] - dlt);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const bf16x8 b = pack8(dS, s);
+#pragma unroll
+                for (int te = 0; te < 2; ++te)
+                    dQ[te] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        tr_rows_frag((const uint8_t *)sK, kk * 32 + 16 * s, 32 * te, lane), b, dQ[te], 0, 0, 0);
+            }
+        }
+    }
+    if (active && qvalid) {
+#pragma unroll
+        for (int te = 0; te < 2; ++te)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 32 * te + 8 * i + 4 * hh;
+                *(u32x2 *)(a.dq + (size_t)t * a.ldd + head * 64 + e) =
+                    u32x2{pack2(dQ[te][4 * i] * 0.125f, dQ[te][4 * i + 1] * 0.125f),
+                          pack2(dQ[te][4 * i + 2] * 0.125f, dQ[te][4 * i + 3] * 0.125f)};
+            }
+    }
+}
+
+__global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
+    __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * 1024];  // stage: Q tile 512 | dO tile 512 chunks
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int head = logical / a.ntiles, ti = logical % a.ntiles;
+    const int2 tile = a.tiles[ti];
+    const int k0 = a.cu[tile.x], k1 = a.cu[tile.x + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+    const int kbase = tile.y + wave * 32;
+    const bool active = kbase < k1;
+    const bool kvalid = kbase + l32 < k1;
+    const int u = min(kbase + l32, k1 - 1);
+    bf16x8 kf[4], vf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        kf[ks] = __builtin_bit_cast(bf16x8, load16(a.k + (size_t)u * a.ldqk + head * 64 + ks * 16 + hh * 8));
+        vf[ks] = __builtin_bit_cast(bf16x8, load16(a.v + (size_t)u * a.ldv + head * 64 + ks * 16 + hh * 8));
+    }
+    const int prow = tid >> 3, pc = swz(prow, tid & 7);
+    auto issue = [&](int tt, int buf) {
+        const int row = min(k0 + tt * 64 + prow, k1 - 1);
+        u32x4 *dst = smem + buf * 1024;
+        lds_dma16(a.q + (size_t)row * a.ldqk + head * 64 + pc * 8, dst + wave * 64);
+        lds_dma16(a.dout + (size_t)row * a.lddo + head * 64 + pc * 8, dst + 512 + wave * 64);
+    };
+    f32x16 dK[2] = {f32x16{}, f32x16{}}, dV[2] = {f32x16{}, f32x16{}};
+    const float *lse = a.lse + (size_t)head * a.ldl, *dl = a.delta + (size_t)head * a.ldl;
+    const int ntile = (k1 - k0 + 63) >> 6;
+    issue(0, 0);
+    for (int tt = 0; tt < ntile; ++tt) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (tt + 1 < ntile) issue(tt + 1, (tt + 1) & 1);
+        if (!active) continue;
+        const u32x4 *sQ = smem + (tt & 1) * 1024, *sO = sQ + 512;
+        const int tq = k0 + tt * 64;
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+            f32x16 S = f32x16{}, dP = f32x16{};
+            const int row = qq * 32 + l32;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int ch = swz(row, ks * 2 + hh);
+                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sQ[row * 8 + ch]), kf[ks], S, 0, 0, 0);
+                dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sO[row * 8 + ch]), vf[ks], dP, 0, 0,
+                                                             0);
+            }
+            f32x16 P, dS;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int tq_r = tq + qq * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
+                const bool ok = tq_r < k1;
+                const int tr = ok ? tq_r : k0;
+                const float p = ok ? __builtin_amdgcn_exp2f(S[r] * kScale2 - lse[tr]) : 0.f;
+                P[r] = p;
+                dS[r] = p * (dP[r] - dl[tr]);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const bf16x8 bp = pack8(P, s), bs = pack8(dS, s);
+#pragma unroll
+                for (int te = 0; te < 2; ++te) {
+                    dV[te] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        tr_rows_frag((const uint8_t *)sO, qq * 32 + 16 * s, 32 * te, lane), bp, dV[te], 0, 0, 0);
+                    dK[te] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        tr_rows_frag((const uint8_t *)sQ, qq * 32 + 16 * s, 32 * te, lane), bs, dK[te], 0, 0, 0);
+                }
+            }
+        }
+    }
+    if (active && kvalid) {
+#pragma unroll
+        for (int te = 0; te < 2; ++te)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int e = 32 * te + 8 * i + 4 * hh;
+                *(u32x2 *)(a.dk + (size_t)u * a.ldd + head * 64 + e) =
+                    u32x2{pack2(dK[te][4 * i] * 0.125f, dK[te][4 * i + 1] * 0.125f),
+                          pack2(dK[te][4 * i + 2] * 0.125f, dK[te][4 * i + 3] * 0.125f)};
+                *(u32x2 *)(a.dv + (size_t)u * a.ldd + head * 64 + e) =
+                    u32x2{pack2(dV[te][4 * i], dV[te][4 * i + 1]), pack2(dV[te][4 * i + 2], dV[te][4 * i + 3])};
+            }
+    }
+}
+
+// one thread per (token, head)
+__global__ __launch_bounds__(256) void k_attn_delta(const uint16_t *dout, const uint16_t *o, int ld, float *delta,
+                                                    int ldl, int T, int heads) {
+    const int idx = blockIdx.x * 256 + threadIdx.x;
+    if (idx >= T * heads) return;
+    const int t = idx / heads, h = idx % heads;
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const u32x4 x = load16(dout + (size_t)t * ld + h * 64 + c * 8), y = load16(o + (size_t)t * ld + h * 64 + c * 8);
+        const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            s += bf16_to_f32(xs[q] & 0xffff) * bf16_to_f32(ys[q] & 0xffff) + bf16_to_f32(xs[q] >> 16) * bf16_to_f32(ys[q] >> 16);
+    }
+    delta[(size_t)h * ldl + t] = s;
+}
+
+// 64 x 64 tiles through LDS
+__global__ __launch_bounds__(256) void k_vt_rows(const uint16_t *vt, int ldvt, uint16_t *v, int T, int D) {
+    __shared__ uint16_t tile[64][66];
+    const int f0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
+    for (int x = threadIdx.x; x < 64 * 64; x += 256) {
+        const int f = x >> 6, t = x & 63;
+        tile[f][t] = (t0 + t < T) ? vt[(size_t)(f0 + f) * ldvt + t0 + t] : 0;
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < 64 * 64; x += 256) {
+        const int t = x >> 6, f = x & 63;
+        if (t0 + t < T) v[(size_t)(t0 + t) * D + f0 + f] = tile[f][t];
+    }
+}
+
+// one thread per (token, pair of one head of q or k): the transpose of the rotation, then v copied
+__global__ __launch_bounds__(256) void k_rope_bwd(const uint16_t *dq, const uint16_t *dk, const uint16_t *dv, int ld,
+                                                  const int16_t *pos, const float2 *rope, uint16_t *dqkv, int T, int D) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const int pairs = D / 2;
+    if (idx >= (size_t)T * pairs * 3) return;
+    const int t = (int)(idx / (pairs * 3)), r = (int)(idx % (pairs * 3));
+    const int part = r / pairs, pr = r % pairs;
+    uint16_t *out = dqkv + (size_t)t * 3 * D + part * D + 2 * pr;
+    if (part == 2) {
+        *(uint32_t *)out = *(const uint32_t *)(dv + (size_t)t * ld + 2 * pr);
+        return;
+    }
+    const uint16_t *src = (part == 0 ? dq : dk) + (size_t)t * ld + 2 * pr;
+    const uint32_t x = *(const uint32_t *)src;
+    const float x0 = bf16_to_f32(x & 0xffff), x1 = bf16_to_f32(x >> 16);
+    const float2 cs = rope[(size_t)pos[(size_t)t * 4] * 32 + (pr & 31)];
+    *(uint32_t *)out = pack2(cs.x * x0 + cs.y * x1, -cs.y * x0 + cs.x * x1);
+}
+
+// one thread per (token, 2 features)
+__global__ __launch_bounds__(256) void k_swiglu_bwd(const uint16_t *gu, const uint16_t *da, uint16_t *dgu, uint16_t *a,
+                                                    int T, int F) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)T * (F / 2)) return;
+    const int t = (int)(idx / (F / 2)), f = (int)(idx % (F / 2)) * 2;
+    const int blk = f >> 5, w = f & 31;
+    const size_t gi = (size_t)t * 2 * F + blk * 64 + w, ui = gi + 32;
+    const uint32_t gg = *(const uint32_t *)(gu + gi), uu = *(const uint32_t *)(gu + ui);
+    const uint32_t dd = *(const uint32_t *)(da + (size_t)t * F + f);
+    float g[2] = {bf16_to_f32(gg & 0xffff), bf16_to_f32(gg >> 16)}, up[2] = {bf16_to_f32(uu & 0xffff), bf16_to_f32(uu >> 16)};
+    float d[2] = {bf16_to_f32(dd & 0xffff), bf16_to_f32(dd >> 16)};
+    float dg[2], du[2], av[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const float sg = 1.f / (1.f + expf(-g[j]));
+        const float silu = g[j] * sg;
+        av[j] = silu * up[j];
+        du[j] = d[j] * silu;
+        dg[j] = d[j] * up[j] * sg * (1.f + g[j] * (1.f - sg));
+    }
+    *(uint32_t *)(dgu + gi) = pack2(dg[0], dg[1]);
+    *(uint32_t *)(dgu + ui) = pack2(du[0], du[1]);
+    *(uint32_t *)(a + (size_t)t * F + f) = pack2(av[0], av[1]);
+}
+
+// One wave per row; workgroup (4 waves) = rows_per_block consecutive rows, so the gain partial of the
+// block is summed in a fixed order.
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd(const float *x, const float *gain, const float *dh,
+                                                     const float *dres, float *dx, uint16_t *dxb, float *gpart,
+                                                     int rows_per_block, int T, int D, float eps) {
+    __shared__ float sg[4][1024];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int per = D / 64;  // columns per lane (D <= 1024)
+    float gacc[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c) gacc[c] = 0.f;
+    const int r0 = blockIdx.x * rows_per_block, r1 = min(T, r0 + rows_per_block);
+    for (int t = r0 + wave; t < r1; t += 4) {
+        float xv[16], hv[16], gv[16];
+        float ss = 0.f, sd = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            if (c < per) {
+                const int i = c * 64 + lane;
+                xv[c] = x[(size_t)t * D + i];
+                hv[c] = dh[(size_t)t * D + i];
+                gv[c] = gain[i];
+                ss += xv[c] * xv[c];
+                sd += hv[c] * gv[c] * xv[c];
+            }
+        }
+        ss = wave_sum(ss);
+        sd = wave_sum(sd);
+        const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+        const float k = inv * inv * inv * sd / (float)D;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) {
+            if (c < per) {
+                const int i = c * 64 + lane;
+                float v = inv * gv[c] * hv[c] - xv[c] * k;
+                if (dres) v += dres[(size_t)t * D + i];
+                dx[(size_t)t * D + i] = v;
+                if (dxb) dxb[(size_t)t * D + i] = (uint16_t)f32_to_bf16(v);
+                gacc[c] += hv[c] * xv[c] * inv;
+            }
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+        if (c < per) sg[wave][c * 64 + lane] = gacc[c];
+    __syncthreads();
+    for (int i = threadIdx.x; i < D; i += 256) gpart[(size_t)blockIdx.x * D + i] = ((sg[0][i] + sg[1][i]) + sg[2][i]) + sg[3][i];
+}
+
+__global__ __launch_bounds__(256) void k_sum_rows(const float *part, int blocks, int D, float *out) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= D) return;
+    float s = 0.f;
+    for (int b = 0; b < blocks; ++b) s += part[(size_t)b * D + i];
+    out[i] = s;
+}
+
+// ------------------------------------------------------------------------------------ weight gradients
+//
+// out[m][n] = sum over t of X[t][m] Y[t][n]. Workgroup tile 64 n x 128 m, 4 waves (32 m each, two 32x32
+// MFMA tiles along n): C = Y^T X, A operand = Y^T (rows n) and B = X (columns m), both read k-major (k = t)
+// through the transpose load from LDS tiles of 64 tokens; a lane ends with 4 consecutive n of one m, so the
+// fp32 partials are stored as rows of out. Split over t into `splits` ranges of `chunk` tokens (a multiple
+// of 64); the last range's rows past T are zeroed in LDS.
+constexpr int kXtyStage = 512 + 1024;  // chunks: Y tile [64 t][64 n] | X tile [64 t][128 m]
+
+__global__ __launch_bounds__(256, 2) void k_xty(const uint16_t *x, int ldx, const uint16_t *y, int ldy, int T, int M,
+                                                int N, float *partial, int chunk) {
+    __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * kXtyStage];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+    const int MT = M / 128, NT = N / 64;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int s = logical / (MT * NT), rest = logical % (MT * NT);
+    const int mt = rest / NT, nt = rest % NT;  // consecutive tiles share their X columns
+    const int m0 = mt * 128, n0 = nt * 64;
+    const int tb = s * chunk, te = min(T, tb + chunk);
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+    const int yrow = tid >> 3, ych = tid & 7;    // Y tile: 64 rows x 8 chunks, 2 rounds of 32 rows
+    const int xrow = tid >> 4, xch = tid & 15;   // X tile: 64 rows x 16 chunks, 4 rounds of 16 rows
+    auto issue = [&](int t0, int buf) {
+        u32x4 *st = smem + buf * kXtyStage;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int row = 32 * r + yrow, src = min(t0 + row, T - 1);
+            lds_dma16(y + (size_t)src * ldy + n0 + ((ych ^ kmajor_swz<128>(row)) << 3), st + r * 256 + wave * 64);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * r + xrow, src = min(t0 + row, T - 1);
+            lds_dma16(x + (size_t)src * ldx + m0 + ((xch ^ kmajor_swz<256>(row)) << 3), st + 512 + r * 256 + wave * 64);
+        }
+    };
+    const int nk = te > tb ? (te - tb + 63) >> 6 : 0;
+    if (nk) issue(tb, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1, t0 = tb + kt * 64;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (t0 + 64 > te) {  // rows past the range read as zero
+            u32x4 *st = smem + buf * kXtyStage;
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+                if (t0 + 32 * r + yrow >= te) st[r * 256 + tid] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (t0 + 16 * r + xrow >= te) st[512 + r * 256 + tid] = u32x4{0u, 0u, 0u, 0u};
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (kt + 1 < nk) issue(t0 + 64, buf ^ 1);
+        const uint8_t *sY = (const uint8_t *)(smem + buf * kXtyStage), *sX = sY + 512 * 16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 b = tr_frag<256>(sX, 16 * ks, 32 * wave, lane);
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn)
+                acc[tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<128>(sY, 16 * ks, 32 * tn, lane), b, acc[tn], 0, 0, 0);
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+    }
+    const int m = m0 + 32 * wave + l32;
+    float *out = partial + ((size_t)s * M + m) * N + n0 + 4 * hh;
+#pragma unroll
+    for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            *(f32x4 *)(out + 32 * tn + 8 * i) = f32x4{acc[tn][4 * i], acc[tn][4 * i + 1], acc[tn][4 * i + 2], acc[tn][4 * i + 3]};
+}
+
+__global__ __launch_bounds__(256) void k_xty_reduce(const float *partial, int splits, int M, int N, float *out,
+                                                    float *out2, int deinterleave) {
+    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (idx >= (size_t)M * N) return;
+    float s = 0.f;
+    for (int sp = 0; sp < splits; ++sp) s += partial[(size_t)sp * M * N + idx];
+    if (!deinterleave) {
+        out[idx] = s;
+        return;
+    }
+    const int m = (int)(idx / N), n = (int)(idx % N);
+    const int blk = n >> 6, w = n & 63, half = N / 2;
+    if (w < 32) out[(size_t)m * half + blk * 32 + w] = s;
+    else out2[(size_t)m * half + blk * 32 + w - 32] = s;
+}
+
+// -------------------------------------------------------------------------------- embedding and pool
+
+// one workgroup per byte value: its tokens' gradient rows summed in token order
+__global__ __launch_bounds__(256) void k_embed_bwd(const float *dx, const uint32_t *tok_off, const uint32_t *tok, int D,
+                                                   float *dE) {
+    const int v = blockIdx.x;
+    for (int i = threadIdx.x; i < D; i += 256) {
+        float s = 0.f;
+        for (uint32_t p = tok_off[v]; p < tok_off[v + 1]; ++p) s += dx[(size_t)tok[p] * D + i];
+        dE[(size_t)v * D + i] = s;
+    }
+}
+
+// Pool backward. With p = softmax over an item's tokens of s_t,h, z_h = sum_t p_t,h xf_t and
+// pooled_h = z_h W_v,h (W_v,h = columns 64h .. 64h + 63 of W_v):
+//   dz_h = W_v,h dpooled_h;  a_t,h = xf_t . dz_h;  ds_t,h = p_t,h (a_t,h - sum_t p a);
+//   dxf_t = sum_h (p_t,h dz_h + ds_t,h u_h);  du_h = sum over items and tokens of ds_t,h xf_t;
+//   dW_v[:, 64h + e] = sum over items of z_h dpooled_h[e];  u_h = W_k,h q_h / 8 gives
+//   dW_k[:, 64h + e] = du_h q_h[e] / 8 and dq_h[e] = W_k[:, 64h + e] . du_h / 8.
+// Every sum runs in a fixed order (tokens ascending, items ascending).
+
+// dz[item][h][i], one thread per (h, i)
+__global__ __launch_bounds__(256) void k_pool_bwd_dz(PoolBwdArgs a, float *dz) {
+    const int item = blockIdx.y, x = blockIdx.x * 256 + threadIdx.x;
+    if (x >= a.H * a.D) return;
+    const int h = x / a.D, i = x % a.D;
+    float s = 0.f;
+    for (int e = 0; e < 64; ++e) s += bf16_to_f32(a.wv[(size_t)i * a.D + 64 * h + e]) * a.dpooled[(size_t)item * a.D + 64 * h + e];
+    dz[((size_t)item * a.H + h) * a.D + i] = s;
+}
+
+// per item: p and ds of every (token, head) into pd[t][h][2]; one workgroup (4 waves) per item
+__global__ __launch_bounds__(256) void k_pool_bwd_tokens(PoolBwdArgs a, const float *dz, float *pd) {
+    __shared__ float stat[16][3];
+    const int item = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int D = a.D, H = a.H, t0 = a.cu[item], t1 = a.cu[item + 1];
+    if (t1 == t0) return;
+    if (tid < H) {  // softmax statistics of head tid, tokens in order
+        float mx = -INFINITY, se = 0.f;
+        for (int t = t0; t < t1; ++t) mx = fmaxf(mx, a.s[(size_t)t * H + tid]);
+        for (int t = t0; t < t1; ++t) se += expf(a.s[(size_t)t * H + tid] - mx);
+        stat[tid][0] = mx;
+        stat[tid][1] = se;
+    }
+    __syncthreads();
+    for (int t = t0 + wave; t < t1; t += 4) {  // a_t,h by one wave per token
+        for (int h = 0; h < H; ++h) {
+            const float *dzh = dz + ((size_t)item * H + h) * D;
+            float dot = 0.f;
+            for (int i = lane; i < D; i += 64) dot += bf16_to_f32(a.xf[(size_t)t * D + i]) * dzh[i];
+            dot = wave_sum(dot);
+            if (lane == 0) {
+                pd[((size_t)t * H + h) * 2] = expf(a.s[(size_t)t * H + h] - stat[h][0]) / stat[h][1];
+                pd[((size_t)t * H + h) * 2 + 1] = dot;
+            }
+        }
+    }
+    __syncthreads();
+    if (tid < H) {
+        float spa = 0.f;
+        for (int t = t0; t < t1; ++t) spa += pd[((size_t)t * H + tid) * 2] * pd[((size_t)t * H + tid) * 2 + 1];
+        stat[tid][2] = spa;
+    }
+    __syncthreads();
+    for (int x = tid; x < (t1 - t0) * H; x += 256) {
+        const int t = t0 + x / H, h = x % H;
+        float *q = pd + ((size_t)t * H + h) * 2;
+        q[1] = q[0] * (q[1] - stat[h][2]);
+    }
+}
+
+// per item, one thread per column: z, du and dxf
+__global__ __launch_bounds__(256) void k_pool_bwd_cols(PoolBwdArgs a, const float *dz, const float *pd) {
+    const int item = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
+    const int D = a.D, H = a.H, t0 = a.cu[item], t1 = a.cu[item + 1];
+    if (i >= D) return;
+    float zv[16], duv[16], dzv[16], uv[16];
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+        zv[h] = duv[h] = 0.f;
+        dzv[h] = h < H ? dz[((size_t)item * H + h) * D + i] : 0.f;
+        uv[h] = h < H ? a.u[(size_t)h * D + i] : 0.f;
+    }
+    for (int t = t0; t < t1; ++t) {
+        const float xv = bf16_to_f32(a.xf[(size_t)t * D + i]);
+        float g = 0.f;
+#pragma unroll
+        for (int h = 0; h < 16; ++h) {
+            if (h < H) {
+                const float p = pd[((size_t)t * H + h) * 2], ds = pd[((size_t)t * H + h) * 2 + 1];
+                zv[h] += p * xv;
+                duv[h] += ds * xv;
+                g += p * dzv[h] + ds * uv[h];
+            }
+        }
+        a.dxf[(size_t)t * D + i] = g;
+    }
+#pragma unroll
+    for (int h = 0; h < 16; ++h) {
+        if (h < H) {
+            a.z[((size_t)item * H + h) * D + i] = zv[h];
+            a.du[((size_t)item * H + h) * D + i] = duv[h];
+        }
+    }
+}
+
+// weight gradients: one thread per (i, column c = 64h + e) of dW_v and dW_k; threads of the first row also
+// give dq
+__global__ __launch_bounds__(256) void k_pool_bwd_weights(PoolBwdArgs a) {
+    const int D = a.D, H = a.H;
+    const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= (size_t)D * D) return;
+    const int i = (int)(x / D), c = (int)(x % D), h = c / 64;
+    float wv = 0.f, du = 0.f;
+    for (int item = 0; item < a.count; ++item) {
+        wv += a.z[((size_t)item * H + h) * D + i] * a.dpooled[(size_t)item * D + c];
+        du += a.du[((size_t)item * H + h) * D + i];
+    }
+    a.dwv[x] = wv;
+    a.dwk[x] = du * bf16_to_f32(a.query[c]) * 0.125f;
+    if (i == 0) {
+        float dq = 0.f;
+        for (int r = 0; r < D; ++r) {
+            float dur = 0.f;
+            for (int item = 0; item < a.count; ++item) dur += a.du[((size_t)item * H + h) * D + r];
+            dq += bf16_to_f32(a.wk[(size_t)r * D + c]) * dur;
+        }
+        a.dquery[c] = dq * 0.125f;
+    }
+}
+
+// ------------------------------------------------------------------------------------------ Adafactor
+//
+// Shazeer and Stern's update with the first moment the pages add: for a matrix, row and column means of
+// g^2 + eps1 decayed by beta2 (r, c), v = r c^T / mean(r); for a vector, v decayed elementwise;
+// u = g / sqrt(v), clipped to RMS(u) <= clip; m = beta1 m + (1 - beta1) u; w -= lr m / (1 - beta1^t).
+// Sums run over fixed ranges in a fixed order.
+
+constexpr int kAdaParts = 128;
+
+__global__ __launch_bounds__(256) void k_ada_rows(AdafactorArgs a) {
+    if (a.cols == 0) {  // vector: one thread per element
+        const int i = blockIdx.x * 256 + threadIdx.x;
+        if (i < a.rows) a.v[i] = a.beta2 * a.v[i] + (1.f - a.beta2) * (a.g[i] * a.g[i] + a.eps1);
+        return;
+    }
+    const int lane = threadIdx.x & 63, row = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= a.rows) return;
+    float s = 0.f;
+    for (int j = lane; j < a.cols; j += 64) {
+        const float g = a.g[(size_t)row * a.cols + j];
+        s += g * g + a.eps1;
+    }
+    s = wave_sum(s);
+    if (lane == 0) a.r[row] = a.beta2 * a.r[row] + (1.f - a.beta2) * s / (float)a.cols;
+}
+
+__global__ __launch_bounds__(256) void k_ada_cols(AdafactorArgs a) {
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= a.cols) return;
+    float s = 0.f;
+    for (int i = 0; i < a.rows; ++i) {
+        const float g = a.g[(size_t)i * a.cols + j];
+        s += g * g + a.eps1;
+    }
+    a.c[j] = a.beta2 * a.c[j] + (1.f - a.beta2) * s / (float)a.rows;
+}
+
+__device__ __forceinline__ float block_sum256(float v, float *red) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    return ((red[0] + red[1]) + red[2]) + red[3];
+}
+
+// work[0] = mean(r) (matrices)
+__global__ __launch_bounds__(256) void k_ada_mean(AdafactorArgs a) {
+    __shared__ float red[4];
+    float s = 0.f;
+    for (int i = threadIdx.x; i < a.rows; i += 256) s += a.r[i];
+    s = block_sum256(s, red);
+    if (threadIdx.x == 0) a.work[0] = s / (float)a.rows;
+}
+
+__device__ __forceinline__ float ada_u(const AdafactorArgs &a, size_t idx) {
+    const float g = a.g[idx];
+    if (a.cols == 0) return g * rsqrtf(a.v[idx]);
+    const int i = (int)(idx / a.cols), j = (int)(idx % a.cols);
+    return g * rsqrtf(a.r[i] * a.c[j] / a.work[0]);
+}
+
+// work[2 + b] = sum of u^2 over part b (kAdaParts equal ranges)
+__global__ __launch_bounds__(256) void k_ada_rms_parts(AdafactorArgs a) {
+    __shared__ float red[4];
+    const size_t n = (size_t)a.rows * (a.cols ? a.cols : 1);
+    const size_t per = (n + kAdaParts - 1) / kAdaParts, b0 = blockIdx.x * per, b1 = min(n, b0 + per);
+    float s = 0.f;
+    for (size_t x = b0 + threadIdx.x; x < b1; x += 256) {
+        const float u = ada_u(a, x);
+        s += u * u;
+    }
+    s = block_sum256(s, red);
+    if (threadIdx.x == 0) a.work[2 + blockIdx.x] = s;
+}
+
+// work[1] = 1 / max(1, RMS(u) / clip)
+__global__ __launch_bounds__(64) void k_ada_clip(AdafactorArgs a) {
+    if (threadIdx.x) return;
+    const size_t n = (size_t)a.rows * (a.cols ? a.cols : 1);
+    float s = 0.f;
+    for (int b = 0; b < kAdaParts; ++b) s += a.work[2 + b];
+    const float rms = sqrtf(s / (float)n);
+    a.work[1] = 1.f / fmaxf(1.f, rms / a.clip);
+}
+
+__global__ __launch_bounds__(256) void k_ada_update(AdafactorArgs a) {
+    const size_t n = (size_t)a.rows * (a.cols ? a.cols : 1);
+    const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= n) return;
+    const float u = ada_u(a, x) * a.work[1];
+    const float m = a.beta1 * a.m[x] + (1.f - a.beta1) * u;
+    a.m[x] = m;
+    const float step = a.lr * m / a.bias_correction;
+    if (a.w16) a.w16[x] = (uint16_t)f32_to_bf16(bf16_to_f32(a.w16[x]) - step);
+    else a.w32[x] = a.w32[x] - step;
+}
+
+// -------------------------------------------------------------------------------------------- packing
+
+// out[n][k] = bf16(W[k][n] * gain[k]) through 64 x 64 LDS tiles; interleaved: out row n takes column
+// 32 (n / 64) + n % 32 of W (n % 64 < 32) or W2
+__global__ __launch_bounds__(256) void k_pack_transpose(const uint16_t *w, const uint16_t *w2, const float *gain,
+                                                        uint16_t *out, int K, int N, int interleave) {
+    __shared__ float tile[64][65];
+    const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
+    const int NO = interleave ? 2 * N : N;
+    for (int x = threadIdx.x; x < 64 * 64; x += 256) {
+        const int kk = x >> 6, nn = x & 63, n = n0 + nn;
+        const uint16_t *src = w;
+        int col = n;
+        if (interleave) {
+            src = (n & 63) < 32 ? w : w2;
+            col = (n >> 6) * 32 + (n & 31);
+        }
+        const float g = gain ? gain[k0 + kk] : 1.f;
+        tile[kk][nn] = (n < NO && k0 + kk < K) ? bf16_to_f32(src[(size_t)(k0 + kk) * N + col]) * g : 0.f;
+    }
+    __syncthreads();
+    for (int x = threadIdx.x; x < 64 * 64; x += 256) {
+        const int nn = x >> 6, kk = x & 63;
+        if (n0 + nn < NO && k0 + kk < K) out[(size_t)(n0 + nn) * K + k0 + kk] = (uint16_t)f32_to_bf16(tile[kk][nn]);
+    }
+}
+
+// out[k][32 b + ...]: rows of W and W2 interleaved in blocks of 32 columns ([W 32 | W2 32] per 64)
+__global__ __launch_bounds__(256) void k_interleave_cols(const uint16_t *w, const uint16_t *w2, uint16_t *out, int K,
+                                                         int N) {
+    const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (x >= (size_t)K * 2 * N) return;
+    const int k = (int)(x / (2 * N)), n = (int)(x % (2 * N));
+    const uint16_t *src = (n & 63) < 32 ? w : w2;
+    out[x] = src[(size_t)k * N + (n >> 6) * 32 + (n & 31)];
+}
+
+// u_h = W_k[:, 64h .. 64h + 63] q_h / 8, one thread per (h, i)
+__global__ __launch_bounds__(256) void k_pool_u(const uint16_t *wk, const uint16_t *query, float *u, int D, int H) {
+    const int x = blockIdx.x * 256 + threadIdx.x;
+    if (x >= H * D) return;
+    const int h = x / D, i = x % D;
+    float s = 0.f;
+    for (int e = 0; e < 64; ++e) s += bf16_to_f32(wk[(size_t)i * D + 64 * h + e]) * bf16_to_f32(query[64 * h + e]);
+    u[x] = s * 0.125f;
+}
+
+}  // namespace
+
+// (launchers follow)
+
+hipError_t launch_attention_bwd(const AttnBwdArgs &a, hipStream_t stream) {
+    if (a.ntiles == 0) return hipSuccess;
+    k_attn_bwd_dq<<<a.ntiles * a.heads, 512, 0, stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_attn_bwd_dkv<<<a.ntiles * a.heads, 512, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attention_delta(const uint16_t *dout, const uint16_t *o, int ld, float *delta, int ldl, int T,
+                                  int heads, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    k_attn_delta<<<(T * heads + 255) / 256, 256, 0, stream>>>(dout, o, ld, delta, ldl, T, heads);
+    return hipGetLastError();
+}
+
+hipError_t launch_vt_rows(const uint16_t *vt, int ldvt, uint16_t *v, int T, int D, hipStream_t stream) {
+    if (T == 0) return hipSuccess;
+    k_vt_rows<<<dim3(D / 64, (T + 63) / 64), 256, 0, stream>>>(vt, ldvt, v, T, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_rope_bwd(const uint16_t *dq, const uint16_t *dk, const uint16_t *dv, int ld, const int16_t *pos,
+                           const float2 *rope, uint16_t *dqkv, int T, int D, hipStream_t stream) {
+    const size_t n = (size_t)T * (D / 2) * 3;
+    if (!n) return hipSuccess;
+    k_rope_bwd<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(dq, dk, dv, ld, pos, rope, dqkv, T, D);
+    return hipGetLastError();
+}
+
+hipError_t launch_swiglu_bwd(const uint16_t *gu, const uint16_t *da, uint16_t *dgu, uint16_t *a, int T, int F,
+                             hipStream_t stream) {
+    const size_t n = (size_t)T * (F / 2);
+    if (!n) return hipSuccess;
+    k_swiglu_bwd<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(gu, da, dgu, a, T, F);
+    return hipGetLastError();
+}
+
+int rmsnorm_bwd_blocks(int T, int rows_per_block) { return (T + rows_per_block - 1) / rows_per_block; }
+
+hipError_t launch_rmsnorm_bwd(const float *x, const float *gain, const float *dh, const float *dres, float *dx,
+                              uint16_t *dxb, float *gpart, int rows_per_block, int T, int D, float eps,
+                              hipStream_t stream) {
+    if (D % 64 || D > 1024) return hipErrorInvalidValue;
+    const int blocks = rmsnorm_bwd_blocks(T, rows_per_block);
+    if (!blocks) return hipSuccess;
+    k_rmsnorm_bwd<<<blocks, 256, 0, stream>>>(x, gain, dh, dres, dx, dxb, gpart, rows_per_block, T, D, eps);
+    return hipGetLastError();
+}
+
+hipError_t launch_sum_rows(const float *part, int blocks, int D, float *out, hipStream_t stream) {
+    k_sum_rows<<<(D + 255) / 256, 256, 0, stream>>>(part, blocks, D, out);
+    return hipGetLastError();
+}
+
+hipError_t launch_xty(const uint16_t *x, int ldx, const uint16_t *y, int ldy, int T, int M, int N, float *partial,
+                      int splits, int chunk, float *out, float *out2, bool deinterleave, hipStream_t stream) {
+    if (M % 128 || N % 64 || chunk % 64 || T <= 0) return hipErrorInvalidValue;
+    k_xty<<<splits * (M / 128) * (N / 64), 256, 0, stream>>>(x, ldx, y, ldy, T, M, N, partial, chunk);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const size_t n = (size_t)M * N;
+    k_xty_reduce<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(partial, splits, M, N, out, out2, deinterleave ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_embed_bwd(const float *dx, const uint32_t *tok_off, const uint32_t *tok, int V, int D, float *dE,
+                            hipStream_t stream) {
+    k_embed_bwd<<<V, 256, 0, stream>>>(dx, tok_off, tok, D, dE);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_bwd(const PoolBwdArgs &a, float *dz, float *pd, hipStream_t stream) {
+    if (a.H > 16 || a.D > 1024) return hipErrorInvalidValue;
+    hipError_t e;
+    if (a.count > 0) {
+        k_pool_bwd_dz<<<dim3((a.H * a.D + 255) / 256, a.count), 256, 0, stream>>>(a, dz);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        k_pool_bwd_tokens<<<a.count, 256, 0, stream>>>(a, dz, pd);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        k_pool_bwd_cols<<<dim3((a.D + 255) / 256, a.count), 256, 0, stream>>>(a, dz, pd);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const size_t n = (size_t)a.D * a.D;
+    k_pool_bwd_weights<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace ube
+
+namespace ube {
+
+hipError_t launch_adafactor(const AdafactorArgs &a, hipStream_t stream) {
+    const size_t n = (size_t)a.rows * (a.cols ? a.cols : 1);
+    if (!n) return hipSuccess;
+    hipError_t e;
+    if (a.cols == 0) {
+        k_ada_rows<<<(a.rows + 255) / 256, 256, 0, stream>>>(a);
+    } else {
+        k_ada_rows<<<(a.rows + 3) / 4, 256, 0, stream>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        k_ada_cols<<<(a.cols + 255) / 256, 256, 0, stream>>>(a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        k_ada_mean<<<1, 256, 0, stream>>>(a);
+    }
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_ada_rms_parts<<<kAdaParts, 256, 0, stream>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_ada_clip<<<1, 64, 0, stream>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    k_ada_update<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_transpose(const uint16_t *w, const uint16_t *w2, const float *gain, uint16_t *out, int K, int N,
+                                 bool interleave, hipStream_t stream) {
+    const int NO = interleave ? 2 * N : N;
+    k_pack_transpose<<<dim3((NO + 63) / 64, (K + 63) / 64), 256, 0, stream>>>(w, w2, gain, out, K, N, interleave ? 1 : 0);
+    return hipGetLastError();
+}
+
+hipError_t launch_pool_u(const uint16_t *wk, const uint16_t *query, float *u, int D, int H, hipStream_t stream) {
+    k_pool_u<<<(H * D + 255) / 256, 256, 0, stream>>>(wk, query, u, D, H);
+    return hipGetLastError();
+}
+
+hipError_t launch_interleave_cols(const uint16_t *w, const uint16_t *w2, uint16_t *out, int K, int N,
+                                  hipStream_t stream) {
+    const size_t n = (size_t)K * 2 * N;
+    k_interleave_cols<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(w, w2, out, K, N);
+    return hipGetLastError();
+}
+
+}  // namespace ube
