@@ -41,6 +41,9 @@ WORKLOAD_TEXT = {
 }
 MAXSIM_ITEMS = 256
 WORKLOAD_TEXT.update({
+    "train": "training step of the depth-12 hidden-512 text encoder on 64 rows x 1024 bytes: encode, Matryoshka "
+             "sigmoid contrastive loss over the 64 pooled rows (pairs 2k/2k+1, widths 64..512), backward with "
+             "per-block recomputation from each block's fp32 input, Adafactor update of every tensor",
     "siglip_band": "Matryoshka sigmoid contrastive loss + gradient: 1024 anchors (one device's share) against "
                    "73,728 gathered 1024-d bf16 pooled embeddings, widths 64/128/256/512/1024, t 10, b -10, "
                    "ambient negatives, 1-2 positives, 2 hard negatives and 1 ignore edge per anchor",
@@ -259,13 +262,122 @@ def bench_siglip(args):
     print(json.dumps(out), flush=True)
 
 
+def train_flops(g, T, lengths):
+    """MFMA flops of one training step: the caller's encode, the backward's forward with the stash, every
+    block replayed once more, and the backward (twice the forward's flops: activation and weight gradients;
+    attention backward counted as 2.5 times its forward)."""
+    from multimodal_embeddings_amd import configs
+    fwd = configs.encode_flops(g, lengths)
+    attn = 4.0 * float(np.sum(np.asarray(lengths, np.float64) ** 2)) * g["hidden"] * g["depth"]
+    bwd = 2.0 * (fwd - attn) + 2.5 * attn
+    return 3.0 * fwd + bwd
+
+
+def bench_train(args):
+    """Times whole training steps (encode, contrastive loss, backward, Adafactor) on resident bytes."""
+    import torch
+    import multimodal_embeddings_amd as ube
+    from multimodal_embeddings_amd import configs, synth
+    wl = configs.WORKLOADS["train"]
+    g = configs.geometry(wl["geometry"])
+    weights = synth.make_weights(g)
+    batch = synth.workload_inputs("train")
+    model, arena, arena2 = ube.Model(weights, 0), ube.Arena(0), ube.Arena(0)
+    trainer = ube.Trainer(model, weights)
+    data = torch.from_numpy(batch.data).to("cuda:0")
+    stream = torch.cuda.current_stream()
+    n = batch.count
+    pairs = synth.Edges.from_lists([[i ^ 1] for i in range(n)])
+    widths = (64, 128, 256, 512)
+    scalars = torch.zeros(3 + len(widths), device="cuda:0")
+    gemb = torch.zeros((n, g["hidden"]), device="cuda:0")
+
+    def step():
+        rows, _ = ube.text_encode(model, arena, data, batch.offsets, completion=1, stream=stream)
+        emb = torch.as_tensor(rows, device="cuda:0").to(torch.bfloat16)
+        ube.contrastive(arena2, emb, scalars, widths=widths, attract=(pairs.offsets, pairs.ids, None),
+                        gradient=gemb, completion=1, stream=stream)
+        trainer.backward(arena, data, batch.offsets, gemb, completion=1, stream=stream)
+        trainer.step(1e-4, completion=1, stream=stream)
+
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    kernel = args.kernel
+    ube.kernel_timer_start(kernel, args.steps * g["depth"] * 8 + 8)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    kms, launches = ube.kernel_timer_stop()
+    ms = start.elapsed_time(end) / args.steps
+    per_kernel = {}
+    if args.per_kernel:
+        for kname in ube.KERNELS:
+            ube.kernel_timer_start(kname, 16 * g["depth"] + 8)
+            step()
+            torch.cuda.synchronize()
+            t, nl = ube.kernel_timer_stop()
+            if nl:
+                per_kernel[kname] = {"ms_per_step": t, "launches": nl}
+    lengths = np.diff(batch.offsets.astype(np.int64))
+    T = int(lengths.sum())
+    flops = train_flops(g, T, lengths)
+    D = g["hidden"]
+    if kernel == "attention_bwd":
+        kflops = 2.5 * 4.0 * float(np.sum(lengths.astype(np.float64) ** 2)) * D  # one layer's launch pair
+    elif kernel == "weight_grad":
+        kflops = None
+    else:
+        kflops = kernel_flops_per_launch(kernel, g, T, lengths) if kernel in ("gemm_qkv", "gemm_out", "gemm_gate_up",
+                                                                               "gemm_down", "attention") else None
+    avg_s = kms / max(launches, 1) / 1e3
+    roof = None
+    if kflops:
+        achieved = kflops / avg_s / 1e12
+        roof = {"kernel": kernel, "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                "frac": achieved / (PEAK_BF16 / 1e12), "traffic": load_traffic(kernel, "train"),
+                "avg_launch_ms": avg_s * 1e3, "launches": launches}
+    out = {
+        "metric": "training tokens/sec (one device's step: encode, contrastive loss, backward, Adafactor)",
+        "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded bytes, random-init bf16 weights N(0, 0.02))",
+        "config": {"workload": f"train: {WORKLOAD_TEXT['train']}", "items": n, "tokens": T, "parallelism": "1 GPU"},
+        "mfma_util": flops / (ms / 1e3) / PEAK_BF16, "flops_per_step": flops, "roofline": roof,
+    }
+    if per_kernel:
+        out["per_kernel_ms"] = per_kernel
+    if not args.no_cpu_baseline:
+        from oracle import train as TR
+        rows_s = 2
+        sub = synth.subset(batch, list(range(rows_s)))
+        threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+        t0 = time.perf_counter()
+        TR.text_backward(weights, sub.data, sub.offsets, np.ones((rows_s, D)))
+        dt = time.perf_counter() - t0
+        toks = int(sub.offsets[-1])
+        out["cpu_baseline"] = {"value": toks / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"rows 0-{rows_s - 1} ({toks} bytes): float64 forward and autograd backward "
+                                         f"({dt:.1f} s; the Adafactor update not included)"}
+    else:
+        out["cpu_baseline"] = None
+    trainer.close()
+    arena.close()
+    arena2.close()
+    model.close()
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="throughput", choices=sorted(WORKLOAD_TEXT))
-    ap.add_argument("--kernel", default="gemm_gate_up", help="dominant kernel for the roofline entry")
+    ap.add_argument("--kernel", default=None, help="kernel of the roofline entry (default: the workload's dominant one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", default=None, help="items the CPU oracle encodes (default: ~10-30 s of work)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -279,10 +391,15 @@ def main():
               "(items are independent; a multi-GPU run would shard the tape by items)", file=sys.stderr)
         sys.exit(2)
 
+    if args.kernel is None:
+        args.kernel = {"train": "attention_bwd"}.get(args.workload, "contrastive_cells" if args.workload.startswith(
+            "siglip") else "gemm_gate_up")
     if args.workload == "maxsim":
         return bench_maxsim(args)
     if args.workload.startswith("siglip"):
         return bench_siglip(args)
+    if args.workload == "train":
+        return bench_train(args)
 
     import torch
     import multimodal_embeddings_amd as ube

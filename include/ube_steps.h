@@ -61,7 +61,7 @@ ube_status_t ube_step_quantize_e4m3(void const *in, void *codes, float *scales, 
 ube_status_t ube_step_gemm_e4m3(void const *w, float w_scale, void const *x, float const *x_scale, void *y, size_t M,
                                 size_t N, size_t K, void *stream);
 
-/* Kernels of an encode or contrastive call, for timing. */
+/* Kernels of an encode, contrastive or trainer call, for timing. */
 typedef enum ube_kernel_t {
     ube_kernel_gather_k = 0,
     ube_kernel_patchify_k = 1,
@@ -78,7 +78,9 @@ typedef enum ube_kernel_t {
     ube_kernel_contrastive_cells_k = 12, /* contrastive loss: dense cells */
     ube_kernel_contrastive_rows_k = 13,  /* contrastive loss: rows contraction */
     ube_kernel_contrastive_cols_k = 14,  /* contrastive loss: columns contraction */
-    ube_kernel_count_k = 15,
+    ube_kernel_attention_bwd_k = 15,     /* trainer: attention backward (dQ, then dK and dV) */
+    ube_kernel_weight_grad_k = 16,       /* trainer: weight gradients X^T Y */
+    ube_kernel_count_k = 17,
 } ube_kernel_t;
 
 /* Starts timing every launch of `kernel` made by encode calls in this

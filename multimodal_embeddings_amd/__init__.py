@@ -154,7 +154,7 @@ STATUS = {0: "success", 1: "invalid_argument", 2: "shape_mismatch", 3: "out_of_m
 SCALAR = {"unknown": 0, "u8": 1, "bf16": 2, "f32": 3, "e4m3": 4}
 KERNELS = ["gather", "patchify", "rmsnorm", "gemm_patch", "gemm_qkv", "attention", "gemm_out", "gemm_gate_up",
            "gemm_down", "final_norm", "pool", "quantize", "contrastive_cells", "contrastive_rows",
-           "contrastive_cols"]
+           "contrastive_cols", "attention_bwd", "weight_grad"]
 NEGATIVES = {"ambient": 0, "named": 1}
 PAIR_LOSS = {"derived": 0, "balanced": 1, "ranked": 2, "sigmoid": 3}
 

@@ -36,6 +36,8 @@ WORKLOADS = {
     "long": dict(geometry="text512_4k", input="text", count=256, fixed_length=4096, byte_lo=0, byte_hi=256),
     # many short segments (the pages pack sentences of a few hundred bytes), about the throughput token budget
     "packed": dict(geometry="text512", input="text", count=4096, len_lo=32, len_hi=513, byte_lo=32, byte_hi=127),
+    # one device's training step as the pages' trainer example sizes it: 64 rows of 1024 bytes
+    "train": dict(geometry="text512", input="text", count=64, fixed_length=1024, byte_lo=0, byte_hi=256),
     "image": dict(geometry="image768", input="media", count=128, frames=1, height=256, width=256),
     "video": dict(geometry="video1024", input="media", count=16, frames=8, height=224, width=224),
     "video_e4m3": dict(geometry="video1024_e4m3", input="media", count=16, frames=8, height=224, width=224),

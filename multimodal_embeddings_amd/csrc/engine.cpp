@@ -1305,7 +1305,7 @@ namespace {
 // Workspace of one backward call for T tokens.
 struct TrainLayout {
     size_t stash, h1, qk, vt, v, o, lse, delta, x1, h2, gu, dx, dxb, da, dgu, act, dh, dx1, dx1b, dout, dq, dk, dv,
-        dqkv, gpart, xty, dz, pd, z, du, dxf, tok_off, tok, total;
+        dqkv, gpart, gsum, xty, dz, pd, z, du, dxf, tok_off, tok, total;
     size_t Tpad, xty_splits, xty_chunk, rows_per_block;
 };
 
@@ -1345,7 +1345,9 @@ TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count) {
     L.dv = take(Tp * D * 2);
     L.dqkv = take(Tp * 3 * D * 2);
     L.rows_per_block = 64;
-    L.gpart = take((size_t)rmsnorm_bwd_blocks((int)std::max<size_t>(T, 1), (int)L.rows_per_block) * D * 4);
+    const size_t gblocks = (size_t)rmsnorm_bwd_blocks((int)std::max<size_t>(T, 1), (int)L.rows_per_block);
+    L.gpart = take(gblocks * D * 4);
+    L.gsum = take((gblocks + 31) / 32 * D * 4);
     // weight gradients: about 8 ranges of tokens, each a multiple of 64
     L.xty_chunk = align_up(std::max<size_t>((T + 7) / 8, 64), 64);
     L.xty_splits = std::max<size_t>(1, (T + L.xty_chunk - 1) / L.xty_chunk);
@@ -1468,7 +1470,7 @@ extern "C" void ube_trainer_init(ube_trainer_init_t *a) {
         std::vector<std::array<size_t, 5>> boffs(N);
         for (size_t l = 0; l < N; ++l)
             boffs[l] = {take(3 * D * D * 2), take(D * D * 2), take(2 * F * D * 2), take(F * D * 2), take(2 * F * D * 2)};
-        const size_t o_work = take(kAdafactorWork * 4);
+        const size_t o_work = take((kAdafactorWork + kAdafactorColParts) * 4);
         UBE_HIP(hipMalloc((void **)&tr->mem, total));
         tr->bytes = total;
         UBE_HIP(hipMemset(tr->mem, 0, total));
@@ -1639,7 +1641,10 @@ extern "C" void ube_trainer_backward(ube_trainer_backward_t *a) {
         const int ldvt = (int)L.Tpad, ldl = (int)L.Tpad;
         const int blocks = rmsnorm_bwd_blocks(Ti, (int)L.rows_per_block);
         auto xty = [&](const uint16_t *x, int M, const uint16_t *y, int Nn, float *out, float *out2, bool di) {
-            UBE_HIP(launch_xty(x, M, y, Nn, Ti, M, Nn, F32(L.xty), (int)L.xty_splits, (int)L.xty_chunk, out, out2, di, st));
+            timed(ube_kernel_weight_grad_k, st, [&] {
+                return launch_xty(x, M, y, Nn, Ti, M, Nn, F32(L.xty), (int)L.xty_splits, (int)L.xty_chunk, out, out2, di,
+                                  st);
+            });
         };
         // ---- pool and final norm
         PoolBwdArgs pa{};
@@ -1651,7 +1656,7 @@ extern "C" void ube_trainer_backward(ube_trainer_backward_t *a) {
         UBE_HIP(launch_pool_bwd(pa, F32(L.dz), F32(L.pd), st));
         UBE_HIP(launch_rmsnorm_bwd(F32(L.stash) + N * T * D, TT[tr->t_gf].w32, F32(L.dxf), nullptr, F32(L.dx), B16(L.dxb),
                                    F32(L.gpart), (int)L.rows_per_block, Ti, Di, eps, st));
-        UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[tr->t_gf].grad, st));
+        UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[tr->t_gf].grad, F32(L.gsum), st));
         // ---- blocks, last to first: replay the forward from the stashed input, then its backward
         for (size_t li = N; li-- > 0;) {
             auto const &b = tr->blocks[li];
@@ -1683,7 +1688,7 @@ extern "C" void ube_trainer_backward(ube_trainer_backward_t *a) {
             xty(h2, Di, dgu, 2 * Fi, TT[b.gate].grad, TT[b.up].grad, true);
             UBE_HIP(launch_rmsnorm_bwd(x1, TT[b.g2].w32, dh, dx, dx1, dx1b, F32(L.gpart), (int)L.rows_per_block, Ti, Di,
                                        eps, st));
-            UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[b.g2].grad, st));
+            UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[b.g2].grad, F32(L.gsum), st));
             // attention half
             uint16_t *dout = B16(L.dout), *dq = B16(L.dq), *dk = B16(L.dk), *dv = B16(L.dv), *dqkv = B16(L.dqkv);
             gemm(kEpiStore, TT[b.o].w16, dx1b, Ti, Di, Di, dout, Di, nullptr, 0, st);
@@ -1693,13 +1698,13 @@ extern "C" void ube_trainer_backward(ube_trainer_backward_t *a) {
             ab2.q = qk, ab2.k = qk + D, ab2.ldqk = 2 * Di, ab2.v = v, ab2.ldv = Di, ab2.dout = dout, ab2.lddo = Di;
             ab2.lse = lse, ab2.delta = delta, ab2.ldl = ldl, ab2.dq = dq, ab2.dk = dk, ab2.dv = dv, ab2.ldd = Di;
             ab2.cu = cu, ab2.tiles = tiles, ab2.ntiles = ntiles, ab2.heads = Hi;
-            UBE_HIP(launch_attention_bwd(ab2, st));
+            timed(ube_kernel_attention_bwd_k, st, [&] { return launch_attention_bwd(ab2, st); });
             UBE_HIP(launch_rope_bwd(dq, dk, dv, Di, pos, m->rope, dqkv, Ti, Di, st));
             gemm(kEpiPatch, TT[b.qkv].w16, dqkv, Ti, Di, 3 * Di, nullptr, 0, dh, Di, st);
             xty(h1, Di, dqkv, 3 * Di, TT[b.qkv].grad, nullptr, false);
             UBE_HIP(launch_rmsnorm_bwd(x_in, TT[b.g1].w32, dh, dx1, dx, dxb, F32(L.gpart), (int)L.rows_per_block, Ti, Di,
                                        eps, st));
-            UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[b.g1].grad, st));
+            UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[b.g1].grad, F32(L.gsum), st));
         }
         UBE_HIP(launch_embed_bwd(F32(L.dx), (const uint32_t *)(wb + L.tok_off), (const uint32_t *)(wb + L.tok), (int)V,
                                  Di, TT[tr->t_embed].grad, st));
@@ -1857,6 +1862,7 @@ extern "C" ube_status_t ube_kernel_timer_stop(double *total_ms, size_t *launches
 extern "C" char const *ube_kernel_name(ube_kernel_t k) {
     static char const *names[] = {"gather",       "patchify",  "rmsnorm",    "gemm_patch", "gemm_qkv", "attention",
                                   "gemm_out",     "gemm_gate_up", "gemm_down", "final_norm", "pool",     "quantize",
-                                  "contrastive_cells", "contrastive_rows", "contrastive_cols"};
+                                  "contrastive_cells", "contrastive_rows", "contrastive_cols", "attention_bwd",
+                                  "weight_grad"};
     return ((int)k >= 0 && k < ube_kernel_count_k) ? names[k] : "unknown";
 }

@@ -52,7 +52,8 @@ int rmsnorm_bwd_blocks(int T, int rows_per_block);
 hipError_t launch_xty(const uint16_t *x, int ldx, const uint16_t *y, int ldy, int T, int M, int N, float *partial,
                       int splits, int chunk, float *out, float *out2, bool deinterleave, hipStream_t stream);
 // columns sums of fixed blocks: out[d] = sum over b < blocks of part[b][d]
-hipError_t launch_sum_rows(const float *part, int blocks, int D, float *out, hipStream_t stream);
+// work: at least ceil(blocks / 32) * D floats
+hipError_t launch_sum_rows(const float *part, int blocks, int D, float *out, float *work, hipStream_t stream);
 // Embedding gradient: dE[v] = sum over tokens of byte v (host-sorted lists) of dx[t]
 hipError_t launch_embed_bwd(const float *dx, const uint32_t *tok_off, const uint32_t *tok, int V, int D, float *dE,
                             hipStream_t stream);
@@ -76,8 +77,8 @@ struct PoolBwdArgs {
 hipError_t launch_pool_bwd(const PoolBwdArgs &a, float *dz, float *pd, hipStream_t stream);
 
 // Adafactor on one tensor: rows x cols (cols == 0: a vector of `rows`); g fp32; master bf16 (w16) or fp32
-// (w32); state r [rows], c [cols] (matrices) or v [rows] (vectors), m [rows x cols]; work: kAdafactorWork
-// floats. lr, beta2 and the bias correction 1 - beta1^t come from the host.
+// (w32); state r [rows], c [cols] (matrices) or v [rows] (vectors), m [rows x cols]; work: kAdafactorWork +
+// kAdafactorColParts floats. lr, beta2 and the bias correction 1 - beta1^t come from the host.
 struct AdafactorArgs {
     const float *g;
     uint16_t *w16;
@@ -98,6 +99,7 @@ hipError_t launch_interleave_cols(const uint16_t *w, const uint16_t *w2, uint16_
                                   hipStream_t stream);
 // the pool's folded keys u_h = W_k[:, head h] q_h / 8 ([H x D] fp32)
 hipError_t launch_pool_u(const uint16_t *wk, const uint16_t *query, float *u, int D, int H, hipStream_t stream);
-constexpr int kAdafactorWork = 2 + 128;  // floats of AdafactorArgs::work
+constexpr int kAdafactorWork = 2 + 128;           // floats of AdafactorArgs::work before the column partials
+constexpr size_t kAdafactorColParts = 1 << 18;   // column partials (ceil(rows / 32) x cols floats) after them
 
 }  // namespace ube

@@ -170,6 +170,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
 
 __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
     __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * 1024];  // stage: Q tile 512 | dO tile 512 chunks
+    __shared__ __attribute__((aligned(16))) float sld[2][2][64];     // stage: lse, delta of the tile's queries
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int head = logical / a.ntiles, ti = logical % a.ntiles;
     const int2 tile = a.tiles[ti];
@@ -186,14 +187,19 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
         vf[ks] = __builtin_bit_cast(bf16x8, load16(a.v + (size_t)u * a.ldv + head * 64 + ks * 16 + hh * 8));
     }
     const int prow = tid >> 3, pc = swz(prow, tid & 7);
+    const float *lse = a.lse + (size_t)head * a.ldl, *dl = a.delta + (size_t)head * a.ldl;
     auto issue = [&](int tt, int buf) {
         const int row = min(k0 + tt * 64 + prow, k1 - 1);
         u32x4 *dst = smem + buf * 1024;
         lds_dma16(a.q + (size_t)row * a.ldqk + head * 64 + pc * 8, dst + wave * 64);
         lds_dma16(a.dout + (size_t)row * a.lddo + head * 64 + pc * 8, dst + 512 + wave * 64);
+        if (tid < 128) {  // queries past the item get lse = +inf (weight 0) and delta 0
+            const int r = tid & 63, t = k0 + tt * 64 + r;
+            const bool ok = t < k1;
+            sld[buf][tid >> 6][r] = (tid < 64) ? (ok ? lse[t] : INFINITY) : (ok ? dl[t] : 0.f);
+        }
     };
     f32x16 dK[2] = {f32x16{}, f32x16{}}, dV[2] = {f32x16{}, f32x16{}};
-    const float *lse = a.lse + (size_t)head * a.ldl, *dl = a.delta + (size_t)head * a.ldl;
     const int ntile = (k1 - k0 + 63) >> 6;
     issue(0, 0);
     for (int tt = 0; tt < ntile; ++tt) {
@@ -217,13 +223,17 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
             }
             f32x16 P, dS;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int tq_r = tq + qq * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const bool ok = tq_r < k1;
-                const int tr = ok ? tq_r : k0;
-                const float p = ok ? __builtin_amdgcn_exp2f(S[r] * kScale2 - lse[tr]) : 0.f;
-                P[r] = p;
-                dS[r] = p * (dP[r] - dl[tr]);
+            for (int i = 0; i < 4; ++i) {
+                const int r0 = qq * 32 + 8 * i + 4 * hh;
+                const f32x4 l4 = *(const f32x4 *)&sld[tt & 1][0][r0], d4 = *(const f32x4 *)&sld[tt & 1][1][r0];
+                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int r = 4 * i + jj;
+                    const float p = __builtin_amdgcn_exp2f(S[r] * kScale2 - lv[jj]);
+                    P[r] = p;
+                    dS[r] = p * (dP[r] - dv4[jj]);
+                }
             }
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -381,6 +391,23 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const float *x, const float
     for (int i = threadIdx.x; i < D; i += 256) gpart[(size_t)blockIdx.x * D + i] = ((sg[0][i] + sg[1][i]) + sg[2][i]) + sg[3][i];
 }
 
+// Column sums in two fixed-order levels: slices of kColSlice rows into partials (one thread per column and
+// slice), then the partials of a column in slice order. `square`: sum g^2 + eps1 instead of g.
+constexpr int kColSlice = 32;
+
+__global__ __launch_bounds__(256) void k_col_parts(const float *src, int rows, int cols, float *parts, int square,
+                                                   float eps1) {
+    const int j = blockIdx.x * 256 + threadIdx.x, sl = blockIdx.y;
+    if (j >= cols) return;
+    const int r0 = sl * kColSlice, r1 = min(rows, r0 + kColSlice);
+    float s = 0.f;
+    for (int i = r0; i < r1; ++i) {
+        const float v = src[(size_t)i * cols + j];
+        s += square ? v * v + eps1 : v;
+    }
+    parts[(size_t)sl * cols + j] = s;
+}
+
 __global__ __launch_bounds__(256) void k_sum_rows(const float *part, int blocks, int D, float *out) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i >= D) return;
@@ -508,43 +535,47 @@ __global__ __launch_bounds__(256) void k_pool_bwd_dz(PoolBwdArgs a, float *dz) {
     dz[((size_t)item * a.H + h) * a.D + i] = s;
 }
 
-// per item: p and ds of every (token, head) into pd[t][h][2]; one workgroup (4 waves) per item
+// p and ds of every (token, head) into pd[t][h][2]; one workgroup (4 waves) per (item, head): softmax
+// statistics by a fixed tree, a_t,h by one wave per token, sum p a in token order
 __global__ __launch_bounds__(256) void k_pool_bwd_tokens(PoolBwdArgs a, const float *dz, float *pd) {
-    __shared__ float stat[16][3];
-    const int item = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    __shared__ float red[4];
+    __shared__ float stat[3];
+    const int item = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int D = a.D, H = a.H, t0 = a.cu[item], t1 = a.cu[item + 1];
     if (t1 == t0) return;
-    if (tid < H) {  // softmax statistics of head tid, tokens in order
-        float mx = -INFINITY, se = 0.f;
-        for (int t = t0; t < t1; ++t) mx = fmaxf(mx, a.s[(size_t)t * H + tid]);
-        for (int t = t0; t < t1; ++t) se += expf(a.s[(size_t)t * H + tid] - mx);
-        stat[tid][0] = mx;
-        stat[tid][1] = se;
-    }
+    float mx = -INFINITY;
+    for (int t = t0 + tid; t < t1; t += 256) mx = fmaxf(mx, a.s[(size_t)t * H + h]);
+    mx = wave_max(mx);
+    if (lane == 0) red[wave] = mx;
     __syncthreads();
-    for (int t = t0 + wave; t < t1; t += 4) {  // a_t,h by one wave per token
-        for (int h = 0; h < H; ++h) {
-            const float *dzh = dz + ((size_t)item * H + h) * D;
-            float dot = 0.f;
-            for (int i = lane; i < D; i += 64) dot += bf16_to_f32(a.xf[(size_t)t * D + i]) * dzh[i];
-            dot = wave_sum(dot);
-            if (lane == 0) {
-                pd[((size_t)t * H + h) * 2] = expf(a.s[(size_t)t * H + h] - stat[h][0]) / stat[h][1];
-                pd[((size_t)t * H + h) * 2 + 1] = dot;
-            }
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    __syncthreads();
+    float se = 0.f;
+    for (int t = t0 + tid; t < t1; t += 256) se += expf(a.s[(size_t)t * H + h] - mx);
+    se = wave_sum(se);
+    if (lane == 0) red[wave] = se;
+    __syncthreads();
+    se = ((red[0] + red[1]) + red[2]) + red[3];
+    const float *dzh = dz + ((size_t)item * H + h) * D;
+    for (int t = t0 + wave; t < t1; t += 4) {
+        float dot = 0.f;
+        for (int i = lane; i < D; i += 64) dot += bf16_to_f32(a.xf[(size_t)t * D + i]) * dzh[i];
+        dot = wave_sum(dot);
+        if (lane == 0) {
+            pd[((size_t)t * H + h) * 2] = expf(a.s[(size_t)t * H + h] - mx) / se;
+            pd[((size_t)t * H + h) * 2 + 1] = dot;
         }
     }
     __syncthreads();
-    if (tid < H) {
+    if (tid == 0) {
         float spa = 0.f;
-        for (int t = t0; t < t1; ++t) spa += pd[((size_t)t * H + tid) * 2] * pd[((size_t)t * H + tid) * 2 + 1];
-        stat[tid][2] = spa;
+        for (int t = t0; t < t1; ++t) spa += pd[((size_t)t * H + h) * 2] * pd[((size_t)t * H + h) * 2 + 1];
+        stat[0] = spa;
     }
     __syncthreads();
-    for (int x = tid; x < (t1 - t0) * H; x += 256) {
-        const int t = t0 + x / H, h = x % H;
+    for (int t = t0 + tid; t < t1; t += 256) {
         float *q = pd + ((size_t)t * H + h) * 2;
-        q[1] = q[0] * (q[1] - stat[h][2]);
+        q[1] = q[0] * (q[1] - stat[0]);
     }
 }
 
@@ -583,27 +614,30 @@ __global__ __launch_bounds__(256) void k_pool_bwd_cols(PoolBwdArgs a, const floa
     }
 }
 
-// weight gradients: one thread per (i, column c = 64h + e) of dW_v and dW_k; threads of the first row also
-// give dq
-__global__ __launch_bounds__(256) void k_pool_bwd_weights(PoolBwdArgs a) {
+// du totals over items (items ascending), one thread per (h, i)
+__global__ __launch_bounds__(256) void k_pool_bwd_du(PoolBwdArgs a, float *du_tot) {
+    const int x = blockIdx.x * 256 + threadIdx.x;
+    if (x >= a.H * a.D) return;
+    float s = 0.f;
+    for (int item = 0; item < a.count; ++item) s += a.du[(size_t)item * a.H * a.D + x];
+    du_tot[x] = s;
+}
+
+// weight gradients, one thread per (i, column c = 64h + e) of dW_v and dW_k; one thread per c of dq
+__global__ __launch_bounds__(256) void k_pool_bwd_weights(PoolBwdArgs a, const float *du_tot) {
     const int D = a.D, H = a.H;
     const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (x >= (size_t)D * D) return;
-    const int i = (int)(x / D), c = (int)(x % D), h = c / 64;
-    float wv = 0.f, du = 0.f;
-    for (int item = 0; item < a.count; ++item) {
-        wv += a.z[((size_t)item * H + h) * D + i] * a.dpooled[(size_t)item * D + c];
-        du += a.du[((size_t)item * H + h) * D + i];
-    }
-    a.dwv[x] = wv;
-    a.dwk[x] = du * bf16_to_f32(a.query[c]) * 0.125f;
-    if (i == 0) {
+    if (x < (size_t)D * D) {
+        const int i = (int)(x / D), c = (int)(x % D), h = c / 64;
+        float wv = 0.f;
+        for (int item = 0; item < a.count; ++item)
+            wv += a.z[((size_t)item * H + h) * D + i] * a.dpooled[(size_t)item * D + c];
+        a.dwv[x] = wv;
+        a.dwk[x] = du_tot[(size_t)h * D + i] * bf16_to_f32(a.query[c]) * 0.125f;
+    } else if (x < (size_t)D * D + D) {
+        const int c = (int)(x - (size_t)D * D), h = c / 64;
         float dq = 0.f;
-        for (int r = 0; r < D; ++r) {
-            float dur = 0.f;
-            for (int item = 0; item < a.count; ++item) dur += a.du[((size_t)item * H + h) * D + r];
-            dq += bf16_to_f32(a.wk[(size_t)r * D + c]) * dur;
-        }
+        for (int r = 0; r < D; ++r) dq += bf16_to_f32(a.wk[(size_t)r * D + c]) * du_tot[(size_t)h * D + r];
         a.dquery[c] = dq * 0.125f;
     }
 }
@@ -634,14 +668,12 @@ __global__ __launch_bounds__(256) void k_ada_rows(AdafactorArgs a) {
     if (lane == 0) a.r[row] = a.beta2 * a.r[row] + (1.f - a.beta2) * s / (float)a.cols;
 }
 
-__global__ __launch_bounds__(256) void k_ada_cols(AdafactorArgs a) {
+// column means from the slice partials (k_col_parts over g^2 + eps1), in slice order
+__global__ __launch_bounds__(256) void k_ada_cols(AdafactorArgs a, const float *parts, int slices) {
     const int j = blockIdx.x * 256 + threadIdx.x;
     if (j >= a.cols) return;
     float s = 0.f;
-    for (int i = 0; i < a.rows; ++i) {
-        const float g = a.g[(size_t)i * a.cols + j];
-        s += g * g + a.eps1;
-    }
+    for (int b = 0; b < slices; ++b) s += parts[(size_t)b * a.cols + j];
     a.c[j] = a.beta2 * a.c[j] + (1.f - a.beta2) * s / (float)a.rows;
 }
 
@@ -807,8 +839,12 @@ hipError_t launch_rmsnorm_bwd(const float *x, const float *gain, const float *dh
     return hipGetLastError();
 }
 
-hipError_t launch_sum_rows(const float *part, int blocks, int D, float *out, hipStream_t stream) {
-    k_sum_rows<<<(D + 255) / 256, 256, 0, stream>>>(part, blocks, D, out);
+hipError_t launch_sum_rows(const float *part, int blocks, int D, float *out, float *work, hipStream_t stream) {
+    const int slices = (blocks + kColSlice - 1) / kColSlice;
+    k_col_parts<<<dim3((D + 255) / 256, slices), 256, 0, stream>>>(part, blocks, D, work, 0, 0.f);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_sum_rows<<<(D + 255) / 256, 256, 0, stream>>>(work, slices, D, out);
     return hipGetLastError();
 }
 
@@ -835,13 +871,16 @@ hipError_t launch_pool_bwd(const PoolBwdArgs &a, float *dz, float *pd, hipStream
     if (a.count > 0) {
         k_pool_bwd_dz<<<dim3((a.H * a.D + 255) / 256, a.count), 256, 0, stream>>>(a, dz);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_pool_bwd_tokens<<<a.count, 256, 0, stream>>>(a, dz, pd);
+        k_pool_bwd_tokens<<<dim3(a.count, a.H), 256, 0, stream>>>(a, dz, pd);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         k_pool_bwd_cols<<<dim3((a.D + 255) / 256, a.count), 256, 0, stream>>>(a, dz, pd);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    const size_t n = (size_t)a.D * a.D;
-    k_pool_bwd_weights<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a);
+    float *du_tot = dz;  // dz is free once the columns pass ran
+    k_pool_bwd_du<<<(a.H * a.D + 255) / 256, 256, 0, stream>>>(a, du_tot);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t n = (size_t)a.D * a.D + a.D;
+    k_pool_bwd_weights<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a, du_tot);
     return hipGetLastError();
 }
 
@@ -858,7 +897,12 @@ hipError_t launch_adafactor(const AdafactorArgs &a, hipStream_t stream) {
     } else {
         k_ada_rows<<<(a.rows + 3) / 4, 256, 0, stream>>>(a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_ada_cols<<<(a.cols + 255) / 256, 256, 0, stream>>>(a);
+        const int slices = (a.rows + kColSlice - 1) / kColSlice;
+        if ((size_t)slices * a.cols > kAdafactorColParts) return hipErrorInvalidValue;
+        k_col_parts<<<dim3((a.cols + 255) / 256, slices), 256, 0, stream>>>(a.g, a.rows, a.cols, a.work + kAdafactorWork,
+                                                                           1, a.eps1);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        k_ada_cols<<<(a.cols + 255) / 256, 256, 0, stream>>>(a, a.work + kAdafactorWork, slices);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         k_ada_mean<<<1, 256, 0, stream>>>(a);
     }
