@@ -42,8 +42,9 @@ WORKLOAD_TEXT = {
 MAXSIM_ITEMS = 256
 WORKLOAD_TEXT.update({
     "train": "training step of the depth-12 hidden-512 text encoder on 64 rows x 1024 bytes: encode, Matryoshka "
-             "sigmoid contrastive loss over the 64 pooled rows (pairs 2k/2k+1, widths 64..512), backward with "
-             "per-block recomputation from each block's fp32 input, Adafactor update of every tensor",
+             "sigmoid contrastive loss over the 64 pooled rows (pairs 2k/2k+1, widths 64..512), backward over "
+             "the forward's kept activations (norm outputs and gate/up pre-activations rebuilt per block), "
+             "Adafactor update of every tensor",
     "siglip_band": "Matryoshka sigmoid contrastive loss + gradient: 1024 anchors (one device's share) against "
                    "73,728 gathered 1024-d bf16 pooled embeddings, widths 64/128/256/512/1024, t 10, b -10, "
                    "ambient negatives, 1-2 positives, 2 hard negatives and 1 ignore edge per anchor",
@@ -263,14 +264,14 @@ def bench_siglip(args):
 
 
 def train_flops(g, T, lengths):
-    """MFMA flops of one training step: the caller's encode, the backward's forward with the stash, every
-    block replayed once more, and the backward (twice the forward's flops: activation and weight gradients;
-    attention backward counted as 2.5 times its forward)."""
+    """Model flops of one training step (MFMA work, 2 per multiply-add): the forward once and the backward
+    (twice the forward's projections: activation and weight gradients; attention backward counted as 2.5
+    times its forward). The rebuilt gate/up projection is recomputation and not counted."""
     from multimodal_embeddings_amd import configs
     fwd = configs.encode_flops(g, lengths)
     attn = 4.0 * float(np.sum(np.asarray(lengths, np.float64) ** 2)) * g["hidden"] * g["depth"]
     bwd = 2.0 * (fwd - attn) + 2.5 * attn
-    return 3.0 * fwd + bwd
+    return fwd + bwd
 
 
 def bench_train(args):
@@ -293,11 +294,11 @@ def bench_train(args):
     gemb = torch.zeros((n, g["hidden"]), device="cuda:0")
 
     def step():
-        rows, _ = ube.text_encode(model, arena, data, batch.offsets, completion=1, stream=stream)
+        rows, _ = trainer.forward(arena, data, batch.offsets, completion=1, stream=stream)
         emb = torch.as_tensor(rows, device="cuda:0").to(torch.bfloat16)
         ube.contrastive(arena2, emb, scalars, widths=widths, attract=(pairs.offsets, pairs.ids, None),
                         gradient=gemb, completion=1, stream=stream)
-        trainer.backward(arena, data, batch.offsets, gemb, completion=1, stream=stream)
+        trainer.backward(None, None, None, gemb, completion=1, stream=stream, after_forward=True)
         trainer.step(1e-4, completion=1, stream=stream)
 
     for _ in range(max(args.warmup, 1)):

@@ -414,11 +414,31 @@ typedef struct ube_trainer_init_t {
 } ube_trainer_init_t;
 void ube_trainer_init(ube_trainer_init_t *arguments);
 
-/* Backward pass over a byte tape: replays the forward with every block's fp32 input kept, then walks
- * the blocks from last to first, each replaying its forward from that input ("activation recomputation
- * is always on") before its backward. d_embeddings: device fp32 rows [count x hidden] (packed; stride 0
- * or hidden * 4 bytes), d loss / d pooled embedding. Writes d loss / d every parameter into the trainer's
- * fp32 gradient buffers (overwritten, not accumulated); the arena serves the replayed forward. */
+/* Training forward over a byte tape: the model's forward, with the activations its backward reads kept in
+ * the trainer's device memory (per block: the fp32 input and the fp32 rows after the attention half, the
+ * rotated q|k rows, v, the attention output and its softmax denominators; about 16 * hidden bytes per
+ * token and block). *embeddings receives the pooled fp32 rows [count x hidden] in the arena, valid until
+ * the arena's next call. The kept activations serve the next ube_trainer_backward with after_forward set,
+ * until a step changes the weights. */
+typedef struct ube_trainer_forward_t {
+    ube_trainer_t trainer;
+    ube_arena_t arena;
+    void *stream;
+    ube_outcome_t *outcome;
+    int completion;
+    ube_tape_view_t texts;
+    ube_rows_view_t *embeddings;
+    ube_encode_stats_t *stats;
+} ube_trainer_forward_t;
+void ube_trainer_forward(ube_trainer_forward_t *arguments);
+
+/* Backward pass: walks the blocks from last to first over the kept activations, rebuilding only each
+ * block's two RMSNorm outputs, v's rows and the gate/up pre-activations from them. after_forward != 0:
+ * differentiates the rows of the last ube_trainer_forward (arena, texts and stats unused; an error if a
+ * step came in between); after_forward == 0: runs that forward over `texts` on `arena` first.
+ * d_embeddings: device fp32 rows [count x hidden] (packed; stride 0 or hidden * 4 bytes), d loss / d
+ * pooled embedding. Writes d loss / d every parameter into the trainer's fp32 gradient buffers
+ * (overwritten, not accumulated). */
 typedef struct ube_trainer_backward_t {
     ube_trainer_t trainer;
     ube_arena_t arena;
@@ -429,6 +449,7 @@ typedef struct ube_trainer_backward_t {
     float const *d_embeddings;
     size_t d_embeddings_stride;
     ube_encode_stats_t *stats;
+    int after_forward;
 } ube_trainer_backward_t;
 void ube_trainer_backward(ube_trainer_backward_t *arguments);
 

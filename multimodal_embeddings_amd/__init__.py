@@ -133,10 +133,16 @@ class ube_trainer_init_t(C.Structure):
                 ("epsilon1", C.c_float), ("clip_threshold", C.c_float)]
 
 
+class ube_trainer_forward_t(C.Structure):
+    _fields_ = [("trainer", VP), ("arena", VP), ("stream", VP), ("outcome", C.POINTER(ube_outcome_t)),
+                ("completion", C.c_int), ("texts", ube_tape_view_t), ("embeddings", C.POINTER(ube_rows_view_t)),
+                ("stats", C.POINTER(ube_encode_stats_t))]
+
+
 class ube_trainer_backward_t(C.Structure):
     _fields_ = [("trainer", VP), ("arena", VP), ("stream", VP), ("outcome", C.POINTER(ube_outcome_t)),
                 ("completion", C.c_int), ("texts", ube_tape_view_t), ("d_embeddings", VP),
-                ("d_embeddings_stride", SZ), ("stats", C.POINTER(ube_encode_stats_t))]
+                ("d_embeddings_stride", SZ), ("stats", C.POINTER(ube_encode_stats_t)), ("after_forward", C.c_int)]
 
 
 class ube_trainer_step_t(C.Structure):
@@ -172,6 +178,7 @@ _SIGNATURES = {
     "ube_maxsim": ([C.POINTER(ube_maxsim_t)], None),
     "ube_contrastive": ([C.POINTER(ube_contrastive_t)], None),
     "ube_trainer_init": ([C.POINTER(ube_trainer_init_t)], None),
+    "ube_trainer_forward": ([C.POINTER(ube_trainer_forward_t)], None),
     "ube_trainer_backward": ([C.POINTER(ube_trainer_backward_t)], None),
     "ube_trainer_step": ([C.POINTER(ube_trainer_step_t)], None),
     "ube_trainer_tensors": ([VP, C.POINTER(ube_trainer_tensor_t), SZ], SZ),
@@ -525,13 +532,30 @@ class Trainer:
             out.append((t.name.decode(), t.layer, master, grad))
         return out
 
-    def backward(self, arena: Arena, data, offsets, d_embeddings, *, stream=None, completion=0):
+    def forward(self, arena: Arena, data, offsets, *, stream=None, completion=0):
+        """-> (Rows of fp32 pooled embeddings in the arena, (truncated, tokens)); keeps the activations that
+        ``backward(..., after_forward=True)`` differentiates."""
         off = np.ascontiguousarray(offsets, dtype=np.uint64)
         tape = ube_tape_view_t(_ptr(data), off.ctypes.data_as(C.POINTER(SZ)), len(off) - 1)
+        outcome, stats, rows = ube_outcome_t(), ube_encode_stats_t(), ube_rows_view_t()
+        args = ube_trainer_forward_t(self.handle, arena.handle, _stream_handle(stream), C.pointer(outcome), completion,
+                                     tape, C.pointer(rows), C.pointer(stats))
+        lib().ube_trainer_forward(C.byref(args))
+        _check(outcome)
+        return Rows(rows, self.model.device), (stats.truncated, stats.tokens)
+
+    def backward(self, arena, data, offsets, d_embeddings, *, stream=None, completion=0, after_forward=False):
+        """Gradients of every parameter from d loss / d pooled rows: over the last ``forward`` with
+        ``after_forward`` (arena, data and offsets unused), else after running that forward here."""
+        if after_forward:
+            tape, handle = ube_tape_view_t(None, None, 0), None
+        else:
+            off = np.ascontiguousarray(offsets, dtype=np.uint64)
+            tape, handle = ube_tape_view_t(_ptr(data), off.ctypes.data_as(C.POINTER(SZ)), len(off) - 1), arena.handle
         outcome = ube_outcome_t()
         stats = ube_encode_stats_t()
-        args = ube_trainer_backward_t(self.handle, arena.handle, _stream_handle(stream), C.pointer(outcome), completion,
-                                      tape, _ptr(d_embeddings), 0, C.pointer(stats))
+        args = ube_trainer_backward_t(self.handle, handle, _stream_handle(stream), C.pointer(outcome), completion,
+                                      tape, _ptr(d_embeddings), 0, C.pointer(stats), 1 if after_forward else 0)
         lib().ube_trainer_backward(C.byref(args))
         _check(outcome)
         return stats.truncated, stats.tokens

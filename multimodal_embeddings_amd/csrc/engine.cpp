@@ -568,6 +568,22 @@ struct ArenaLease {
     }
 };
 
+// Where a training forward leaves the activations its backward reads (device memory outside the arena):
+// every block's fp32 input (and the final norm's, at block N), the fp32 rows after each block's attention
+// half, each block's rotated q|k rows, feature-major v, attention output and softmax log2 denominators,
+// and the final-norm rows and pool scores.
+struct Keep {
+    float *x;         // [(N + 1) x T x D]
+    float *x1;        // [N x T x D]
+    uint16_t *qk;     // [N][Tpad x 2D]
+    uint16_t *vt;     // [N][D x ldvt]
+    uint16_t *o;      // [N][Tpad x D]
+    float *lse;       // [N][H x ldl]
+    uint16_t *xf;     // [Tpad x D]
+    float *s;         // [Tpad x H]
+    size_t Tpad, ldvt, ldl;
+};
+
 struct EncodeRequest {
     ube_model_t model;
     ube_arena_t arena;
@@ -583,8 +599,10 @@ struct EncodeRequest {
     unsigned outputs;
     ube_rows_tape_view_t *states;
     ube_rows_tape_view_t *token_vectors;
-    Layout *layout = nullptr;  // when set, receives the call's arena layout (the trainer reads cu, tiles, xf)
+    Layout *layout = nullptr;  // when set, receives the call's arena layout (the trainer reads cu, tiles)
+    Keep const *keep = nullptr;  // training forward: where the backward's activations go
 };
+
 
 bool wants(unsigned outputs, ube_outputs_t o) { return (outputs ? outputs : ube_outputs_embeddings_k) & o; }
 
@@ -694,6 +712,8 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
             timed(ube_kernel_gemm_patch_k, st, [&] { return launch_gemm(kEpiPatch, ga, st); });
         }
         if (r.trace) UBE_HIP(hipMemcpyAsync(r.trace, x, (size_t)T * D * 4, hipMemcpyDeviceToDevice, st));
+        Keep const *kp = r.keep;
+        const size_t TD = (size_t)T * D;
         // ---- blocks
         uint8_t *q8 = (uint8_t *)(db + L.q8);
         float *qs = (float *)(db + L.qs);
@@ -728,21 +748,33 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
         };
         for (size_t l = 0; l < g.depth; ++l) {
             auto const &Wl = m->layers[l];
+            // this block's q|k, v and attention rows: the arena's scratch, or the training forward's own
+            uint16_t *qk_l = qk, *vt_l = vt, *o_l = o;
+            int ldvt_l = ldvt;
+            float *lse_l = nullptr;
+            if (kp) {
+                UBE_HIP(hipMemcpyAsync(kp->x + l * TD, x, TD * 4, hipMemcpyDeviceToDevice, st));
+                qk_l = kp->qk + l * kp->Tpad * 2 * D, vt_l = kp->vt + l * D * kp->ldvt, o_l = kp->o + l * kp->Tpad * D;
+                ldvt_l = (int)kp->ldvt, lse_l = kp->lse + l * H * kp->ldl;
+                UBE_HIP(hipMemset2DAsync(vt_l + T, kp->ldvt * 2, 0, 64 * 2, (size_t)D, st));
+            }
             if (m->e4m3) norm(Wl.g1);
             GemmArgs qa{};
             qa.w = Wl.wqkv, qa.x = h, qa.M = T, qa.N = 3 * D, qa.K = D;
             folded_norm(qa);
-            qa.out_bf16 = qk, qa.ld_out = 2 * D, qa.vt = vt, qa.ld_vt = ldvt, qa.pos = pos, qa.rope = m->rope;
+            qa.out_bf16 = qk_l, qa.ld_out = 2 * D, qa.vt = vt_l, qa.ld_vt = ldvt_l, qa.pos = pos, qa.rope = m->rope;
             qa.D = D, qa.sec0 = m->sec0, qa.sec1 = m->sec1;
             project(ube_kernel_gemm_qkv_k, kEpiQkv, qa, Wl.s_qkv, 0.f);
             timed(ube_kernel_attention_k, st, [&] {
-                return launch_attention(qk, qk + D, 2 * D, vt, ldvt, o, D, cu, tiles, ntiles, H, st);
+                return launch_attention(qk_l, qk_l + D, 2 * D, vt_l, ldvt_l, o_l, D, cu, tiles, ntiles, H, st, lse_l,
+                                        kp ? (int)kp->ldl : 0);
             });
-            if (m->e4m3) quantize(o, D);
+            if (m->e4m3) quantize(o_l, D);
             GemmArgs oa{};
-            oa.w = Wl.wo, oa.x = o, oa.M = T, oa.N = D, oa.K = D, oa.out_f32 = x, oa.ld_f32 = D;
+            oa.w = Wl.wo, oa.x = o_l, oa.M = T, oa.N = D, oa.K = D, oa.out_f32 = x, oa.ld_f32 = D;
             residual_out(oa);
             project(ube_kernel_gemm_out_k, kEpiResid, oa, Wl.s_o, 0.f);
+            if (kp) UBE_HIP(hipMemcpyAsync(kp->x1 + l * TD, x, TD * 4, hipMemcpyDeviceToDevice, st));
             if (m->e4m3) norm(Wl.g2);
             GemmArgs ua{};
             ua.w = Wl.wgu, ua.x = h, ua.M = T, ua.N = 2 * F, ua.K = D, ua.out_bf16 = act, ua.ld_out = F;
@@ -756,6 +788,10 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
             if (r.trace)
                 UBE_HIP(hipMemcpyAsync(r.trace + (l + 1) * (size_t)T * D, x, (size_t)T * D * 4,
                                        hipMemcpyDeviceToDevice, st));
+        }
+        if (kp) {
+            UBE_HIP(hipMemcpyAsync(kp->x + g.depth * TD, x, TD * 4, hipMemcpyDeviceToDevice, st));
+            xf = kp->xf, s = kp->s;
         }
         float *states = tok.states_f32 ? (float *)(db + L.st) : nullptr;
         timed(ube_kernel_final_norm_k, st,
@@ -1273,6 +1309,17 @@ extern "C" char const *ube_status_name(ube_status_t s) {
 
 // ===================================================================== trainer
 
+namespace {
+// Workspace of one training forward and backward over T tokens: the activations the forward keeps (k*),
+// host-built tables (cu, tiles, positions, byte -> token lists), then the backward's scratch.
+struct TrainLayout {
+    size_t kx, kx1, kqk, kvt, ko, klse, kxf, ks, kcu, ktiles, kpos, tok_off, tok;
+    size_t h1, v, h2, gu, dx, dxb, da, dgu, act, dh, dx1, dx1b, dout, dq, dk, dv, dqkv, gpart, gsum, xty, dz, pd, z,
+        du, dxf, delta, total;
+    size_t Tpad, xty_splits, xty_chunk, rows_per_block;
+};
+}  // namespace
+
 struct ube_trainer_handle_t {
     ube_model_t model = nullptr;
     int device = 0;
@@ -1295,6 +1342,10 @@ struct ube_trainer_handle_t {
     std::vector<Block> blocks;
     size_t t_embed = 0, t_gf = 0, t_query = 0, t_wk = 0, t_wv = 0;
     float *ada_work = nullptr;
+    // the last training forward, whose activations the workspace holds until a step changes the weights
+    bool fw_valid = false;
+    size_t fw_T = 0, fw_count = 0, fw_ntiles = 0;
+    TrainLayout fw_L{};
     // per-call workspace (grows)
     char *ws = nullptr;
     size_t ws_cap = 0;
@@ -1302,33 +1353,34 @@ struct ube_trainer_handle_t {
 
 namespace {
 
-// Workspace of one backward call for T tokens.
-struct TrainLayout {
-    size_t stash, h1, qk, vt, v, o, lse, delta, x1, h2, gu, dx, dxb, da, dgu, act, dh, dx1, dx1b, dout, dq, dk, dv,
-        dqkv, gpart, gsum, xty, dz, pd, z, du, dxf, tok_off, tok, total;
-    size_t Tpad, xty_splits, xty_chunk, rows_per_block;
-};
-
-TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count) {
+TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count, size_t ntiles) {
     TrainLayout L{};
     const size_t D = g.hidden, F = g.ffn, H = g.heads, N = g.depth;
     L.Tpad = align_up(T, 256) + kRowPad;
-    const size_t Tp = L.Tpad;
+    const size_t Tp = L.Tpad, T1 = std::max<size_t>(T, 1);
     size_t total = 0;
     auto take = [&](size_t bytes) {
         size_t o = total;
         total = align_up(total + bytes, 256);
         return o;
     };
-    L.stash = take((N + 1) * std::max<size_t>(T, 1) * D * 4);
+    // kept by the forward
+    L.kx = take((N + 1) * T1 * D * 4);
+    L.kx1 = take(N * T1 * D * 4);
+    L.kqk = take(N * Tp * 2 * D * 2);
+    L.kvt = take(N * D * Tp * 2);
+    L.ko = take(N * Tp * D * 2);
+    L.klse = take(N * H * Tp * 4);
+    L.kxf = take(Tp * D * 2);
+    L.ks = take(Tp * H * 4);
+    L.kcu = take((count + 1) * 4);
+    L.ktiles = take(std::max<size_t>(ntiles, 1) * 8);
+    L.kpos = take(Tp * 4 * 2);
+    L.tok_off = take((g.vocab + 1) * 4);
+    L.tok = take(T1 * 4);
+    // backward scratch
     L.h1 = take(Tp * D * 2);
-    L.qk = take(Tp * 2 * D * 2);
-    L.vt = take(D * Tp * 2);
     L.v = take(Tp * D * 2);
-    L.o = take(Tp * D * 2);
-    L.lse = take(H * Tp * 4);
-    L.delta = take(H * Tp * 4);
-    L.x1 = take(Tp * D * 4);
     L.h2 = take(Tp * D * 2);
     L.gu = take(Tp * 2 * F * 2);
     L.dx = take(Tp * D * 4);
@@ -1344,8 +1396,9 @@ TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count) {
     L.dk = take(Tp * D * 2);
     L.dv = take(Tp * D * 2);
     L.dqkv = take(Tp * 3 * D * 2);
+    L.delta = take(H * Tp * 4);
     L.rows_per_block = 64;
-    const size_t gblocks = (size_t)rmsnorm_bwd_blocks((int)std::max<size_t>(T, 1), (int)L.rows_per_block);
+    const size_t gblocks = (size_t)rmsnorm_bwd_blocks((int)T1, (int)L.rows_per_block);
     L.gpart = take(gblocks * D * 4);
     L.gsum = take((gblocks + 31) / 32 * D * 4);
     // weight gradients: about 8 ranges of tokens, each a multiple of 64
@@ -1357,8 +1410,6 @@ TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count) {
     L.z = take(std::max<size_t>(count, 1) * H * D * 4);
     L.du = take(std::max<size_t>(count, 1) * H * D * 4);
     L.dxf = take(Tp * D * 4);
-    L.tok_off = take((g.vocab + 1) * 4);
-    L.tok = take(std::max<size_t>(T, 1) * 4);
     L.total = total;
     return L;
 }
@@ -1559,155 +1610,206 @@ extern "C" size_t ube_trainer_tensors(ube_trainer_t tr, ube_trainer_tensor_t *ou
     return tr->tensors.size();
 }
 
+namespace {
+
+// The training forward over a byte tape: the model's forward (pooled fp32 rows into the arena) with the
+// activations of the backward kept in the trainer's workspace, plus the tables the backward reads
+// (item bounds, tiles, positions, and the tokens of every byte value in token order).
+void train_forward(ube_trainer_t tr, ube_arena_t arena, hipStream_t st, ube_tape_view_t const &texts,
+                   ube_encode_stats_t *stats, ube_rows_view_t *rows) {
+    ube_model_t m = tr->model;
+    const ube_geometry_t &g = m->g;
+    if (arena->device != tr->device) throw Failure{ube_status_device_k, "arena and trainer on different GPUs"};
+    const size_t V = g.vocab;
+    tr->fw_valid = false;
+    Plan p = text_plan(m, texts);
+    const size_t T = p.T, count = texts.count;
+    UBE_HIP(hipSetDevice(tr->device));
+    // byte of every kept token, grouped by value in token order (the embedding gradient's fixed order)
+    std::vector<uint8_t> bytes(p.input_hi - p.input_lo);
+    if (!bytes.empty()) {
+        const bool dev = pointer_on_device(texts.data, tr->device);
+        const char *src = (const char *)texts.data + p.input_lo;
+        if (dev) UBE_HIP(hipMemcpy(bytes.data(), src, bytes.size(), hipMemcpyDeviceToHost));
+        else std::memcpy(bytes.data(), src, bytes.size());
+    }
+    std::vector<uint32_t> tok_off(V + 1, 0), tok(std::max<size_t>(T, 1));
+    for (size_t i = 0; i < count; ++i)
+        for (int t = p.cu[i]; t < p.cu[i + 1]; ++t) ++tok_off[bytes[p.src[i] - p.input_lo + (t - p.cu[i])] + 1];
+    for (size_t v = 0; v < V; ++v) tok_off[v + 1] += tok_off[v];
+    {
+        std::vector<uint32_t> fill(tok_off.begin(), tok_off.end() - 1);
+        for (size_t i = 0; i < count; ++i)
+            for (int t = p.cu[i]; t < p.cu[i + 1]; ++t)
+                tok[fill[bytes[p.src[i] - p.input_lo + (t - p.cu[i])]]++] = (uint32_t)t;
+    }
+    TrainLayout L = train_carve(g, T, count, p.tiles.size());
+    if (L.total > tr->ws_cap) {
+        UBE_HIP(hipStreamSynchronize(st));
+        if (tr->ws) UBE_HIP(hipFree(tr->ws));
+        tr->ws = nullptr;
+        tr->ws_cap = 0;
+        const size_t want = align_up(L.total, (size_t)1 << 20);
+        UBE_HIP(hipMalloc((void **)&tr->ws, want));
+        tr->ws_cap = want;
+        UBE_HIP(hipMemsetAsync(tr->ws, 0, want, st));
+    }
+    char *wb = tr->ws;
+    UBE_HIP(hipMemcpyAsync(wb + L.tok_off, tok_off.data(), (V + 1) * 4, hipMemcpyHostToDevice, st));
+    UBE_HIP(hipMemcpyAsync(wb + L.tok, tok.data(), tok.size() * 4, hipMemcpyHostToDevice, st));
+    Keep k{};
+    k.x = (float *)(wb + L.kx), k.x1 = (float *)(wb + L.kx1);
+    k.qk = (uint16_t *)(wb + L.kqk), k.vt = (uint16_t *)(wb + L.kvt), k.o = (uint16_t *)(wb + L.ko);
+    k.lse = (float *)(wb + L.klse), k.xf = (uint16_t *)(wb + L.kxf), k.s = (float *)(wb + L.ks);
+    k.Tpad = L.Tpad, k.ldvt = L.Tpad, k.ldl = L.Tpad;
+    Layout EL{};
+    EncodeRequest r{m, arena, st, 1, ube_scalar_f32_k, rows, stats, nullptr, texts.data, texts.offsets, count, 0,
+                    nullptr, nullptr, &EL, &k};
+    run_encode(r, p, false);
+    char *ab = arena->dev;
+    if (T) {
+        UBE_HIP(hipMemcpyAsync(wb + L.kcu, ab + EL.cu, (count + 1) * 4, hipMemcpyDeviceToDevice, st));
+        UBE_HIP(hipMemcpyAsync(wb + L.ktiles, ab + EL.tiles, p.tiles.size() * 8, hipMemcpyDeviceToDevice, st));
+        UBE_HIP(hipMemcpyAsync(wb + L.kpos, ab + EL.pos, L.Tpad * 4 * 2, hipMemcpyDeviceToDevice, st));
+    }
+    tr->fw_T = T, tr->fw_count = count, tr->fw_ntiles = p.tiles.size(), tr->fw_L = L;
+    tr->fw_valid = true;
+}
+
+// The backward over the last training forward's activations: d loss / d every parameter from d loss /
+// d pooled rows. Per block (last to first) the few inputs that were not kept are rebuilt from the kept
+// rows (the two RMSNorm outputs, v's rows, the gate/up pre-activations), then the block's backward runs.
+void train_backward(ube_trainer_t tr, hipStream_t st, float const *d_embeddings) {
+    ube_model_t m = tr->model;
+    const ube_geometry_t &g = m->g;
+    const size_t D = g.hidden, F = g.ffn, H = g.heads, N = g.depth, V = g.vocab;
+    const float eps = g.rms_epsilon;
+    const TrainLayout &L = tr->fw_L;
+    const size_t T = tr->fw_T, count = tr->fw_count;
+    UBE_HIP(hipSetDevice(tr->device));
+    if (T == 0) {
+        for (auto const &t : tr->tensors) UBE_HIP(hipMemsetAsync(t.grad, 0, t.rows * (t.cols ? t.cols : 1) * 4, st));
+        return;
+    }
+    char *wb = tr->ws;
+    auto F32 = [&](size_t o) { return (float *)(wb + o); };
+    auto B16 = [&](size_t o) { return (uint16_t *)(wb + o); };
+    const int *cu = (const int *)(wb + L.kcu);
+    const int2 *tiles = (const int2 *)(wb + L.ktiles);
+    const int ntiles = (int)tr->fw_ntiles;
+    const int16_t *pos = (const int16_t *)(wb + L.kpos);
+    auto &TT = tr->tensors;
+    const int Ti = (int)T, Di = (int)D, Fi = (int)F, Hi = (int)H;
+    const size_t Tp = L.Tpad, TD = T * D;
+    const int ldvt = (int)Tp, ldl = (int)Tp;
+    const int blocks = rmsnorm_bwd_blocks(Ti, (int)L.rows_per_block);
+    auto xty = [&](const uint16_t *x, int M, const uint16_t *y, int Nn, float *out, float *out2, bool di) {
+        timed(ube_kernel_weight_grad_k, st, [&] {
+            return launch_xty(x, M, y, Nn, Ti, M, Nn, F32(L.xty), (int)L.xty_splits, (int)L.xty_chunk, out, out2, di,
+                              st);
+        });
+    };
+    // ---- pool and final norm
+    PoolBwdArgs pa{};
+    pa.xf = B16(L.kxf), pa.s = F32(L.ks), pa.cu = cu, pa.count = (int)count, pa.D = Di, pa.H = Hi, pa.u = m->u;
+    pa.wv = TT[tr->t_wv].w16, pa.wk = TT[tr->t_wk].w16, pa.query = TT[tr->t_query].w16;
+    pa.dpooled = d_embeddings;
+    pa.dxf = F32(L.dxf), pa.z = F32(L.z), pa.du = F32(L.du);
+    pa.dwv = TT[tr->t_wv].grad, pa.dwk = TT[tr->t_wk].grad, pa.dquery = TT[tr->t_query].grad;
+    UBE_HIP(launch_pool_bwd(pa, F32(L.dz), F32(L.pd), st));
+    UBE_HIP(launch_rmsnorm_bwd(F32(L.kx) + N * TD, TT[tr->t_gf].w32, F32(L.dxf), nullptr, F32(L.dx), B16(L.dxb),
+                               F32(L.gpart), (int)L.rows_per_block, Ti, Di, eps, st));
+    UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[tr->t_gf].grad, F32(L.gsum), st));
+    // ---- blocks, last to first
+    for (size_t li = N; li-- > 0;) {
+        auto const &b = tr->blocks[li];
+        const float *x_in = F32(L.kx) + li * TD, *x1 = F32(L.kx1) + li * TD;
+        const uint16_t *qk = B16(L.kqk) + li * Tp * 2 * D, *vt = B16(L.kvt) + li * D * Tp, *o = B16(L.ko) + li * Tp * D;
+        const float *lse = F32(L.klse) + li * H * Tp;
+        uint16_t *h1 = B16(L.h1), *v = B16(L.v), *h2 = B16(L.h2), *gu = B16(L.gu);
+        float *delta = F32(L.delta);
+        // the block's inputs that were not kept
+        UBE_HIP(launch_rmsnorm(x_in, TT[b.g1].w32, h1, Ti, Di, eps, st));
+        UBE_HIP(launch_vt_rows(vt, ldvt, v, Ti, Di, st));
+        UBE_HIP(launch_rmsnorm(x1, TT[b.g2].w32, h2, Ti, Di, eps, st));
+        gemm(kEpiStore, b.guT, h2, Ti, 2 * Fi, Di, gu, 2 * Fi, nullptr, 0, st);
+        // MLP half
+        float *dx = F32(L.dx), *dh = F32(L.dh), *dx1 = F32(L.dx1);
+        uint16_t *dxb = B16(L.dxb), *da = B16(L.da), *dgu = B16(L.dgu), *act = B16(L.act), *dx1b = B16(L.dx1b);
+        gemm(kEpiStore, TT[b.down].w16, dxb, Ti, Fi, Di, da, Fi, nullptr, 0, st);
+        UBE_HIP(launch_swiglu_bwd(gu, da, dgu, act, Ti, Fi, st));
+        xty(act, Fi, dxb, Di, TT[b.down].grad, nullptr, false);
+        gemm(kEpiPatch, b.gu_cols, dgu, Ti, Di, 2 * Fi, nullptr, 0, dh, Di, st);
+        xty(h2, Di, dgu, 2 * Fi, TT[b.gate].grad, TT[b.up].grad, true);
+        UBE_HIP(launch_rmsnorm_bwd(x1, TT[b.g2].w32, dh, dx, dx1, dx1b, F32(L.gpart), (int)L.rows_per_block, Ti, Di,
+                                   eps, st));
+        UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[b.g2].grad, F32(L.gsum), st));
+        // attention half
+        uint16_t *dout = B16(L.dout), *dq = B16(L.dq), *dk = B16(L.dk), *dv = B16(L.dv), *dqkv = B16(L.dqkv);
+        gemm(kEpiStore, TT[b.o].w16, dx1b, Ti, Di, Di, dout, Di, nullptr, 0, st);
+        xty(o, Di, dx1b, Di, TT[b.o].grad, nullptr, false);
+        UBE_HIP(launch_attention_delta(dout, o, Di, delta, ldl, Ti, Hi, st));
+        AttnBwdArgs ab2{};
+        ab2.q = qk, ab2.k = qk + D, ab2.ldqk = 2 * Di, ab2.v = v, ab2.ldv = Di, ab2.dout = dout, ab2.lddo = Di;
+        ab2.lse = lse, ab2.delta = delta, ab2.ldl = ldl, ab2.dq = dq, ab2.dk = dk, ab2.dv = dv, ab2.ldd = Di;
+        ab2.cu = cu, ab2.tiles = tiles, ab2.ntiles = ntiles, ab2.heads = Hi;
+        timed(ube_kernel_attention_bwd_k, st, [&] { return launch_attention_bwd(ab2, st); });
+        UBE_HIP(launch_rope_bwd(dq, dk, dv, Di, pos, m->rope, dqkv, Ti, Di, st));
+        gemm(kEpiPatch, TT[b.qkv].w16, dqkv, Ti, Di, 3 * Di, nullptr, 0, dh, Di, st);
+        xty(h1, Di, dqkv, 3 * Di, TT[b.qkv].grad, nullptr, false);
+        UBE_HIP(launch_rmsnorm_bwd(x_in, TT[b.g1].w32, dh, dx1, dx, dxb, F32(L.gpart), (int)L.rows_per_block, Ti, Di,
+                                   eps, st));
+        UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[b.g1].grad, F32(L.gsum), st));
+    }
+    UBE_HIP(launch_embed_bwd(F32(L.dx), (const uint32_t *)(wb + L.tok_off), (const uint32_t *)(wb + L.tok), (int)V, Di,
+                             TT[tr->t_embed].grad, st));
+}
+
+}  // namespace
+
+extern "C" void ube_trainer_forward(ube_trainer_forward_t *a) {
+    if (!a) return;
+    if (a->embeddings) *a->embeddings = ube_rows_view_t{nullptr, 0, 0, 0, ube_scalar_unknown_k};
+    try {
+        if (!a->trainer || !a->arena) throw Failure{ube_status_invalid_argument_k, "NULL trainer or arena"};
+        if (!a->embeddings) throw Failure{ube_status_invalid_argument_k, "NULL embeddings output"};
+        ArenaLease lease(a->arena);
+        if (!lease.held) throw Failure{ube_status_contended_k, "the arena is serving another call"};
+        hipStream_t st = (hipStream_t)a->stream;
+        train_forward(a->trainer, a->arena, st, a->texts, a->stats, a->embeddings);
+        if (a->completion == 0) UBE_HIP(hipStreamSynchronize(st));
+        set_outcome(a->outcome, ube_status_success_k, nullptr);
+    } catch (Failure const &f) {
+        if (a->trainer) a->trainer->fw_valid = false;
+        if (a->embeddings) *a->embeddings = ube_rows_view_t{nullptr, 0, 0, 0, ube_scalar_unknown_k};
+        set_outcome(a->outcome, f.status, f.message);
+    } catch (std::bad_alloc const &) {
+        if (a->trainer) a->trainer->fw_valid = false;
+        set_outcome(a->outcome, ube_status_out_of_memory_k, "host out of memory");
+    }
+}
+
 extern "C" void ube_trainer_backward(ube_trainer_backward_t *a) {
     if (!a) return;
     try {
-        if (!a->trainer || !a->arena) throw Failure{ube_status_invalid_argument_k, "NULL trainer or arena"};
+        if (!a->trainer) throw Failure{ube_status_invalid_argument_k, "NULL trainer"};
         ube_trainer_t tr = a->trainer;
-        ube_model_t m = tr->model;
-        const ube_geometry_t &g = m->g;
-        if (a->arena->device != tr->device) throw Failure{ube_status_device_k, "arena and trainer on different GPUs"};
-        const size_t D = g.hidden, F = g.ffn, H = g.heads, N = g.depth, V = g.vocab;
-        const float eps = g.rms_epsilon;
-        const size_t count = a->texts.count;
-        if (count && !a->d_embeddings) throw Failure{ube_status_invalid_argument_k, "NULL embedding gradient"};
-        if (count && a->d_embeddings_stride && a->d_embeddings_stride != D * 4)
-            throw Failure{ube_status_unsupported_k, "embedding gradient rows must be packed"};
-        ArenaLease lease(a->arena);  // the replayed forward's rows (xf, scores, tiles) stay in the arena
-        if (!lease.held) throw Failure{ube_status_contended_k, "the arena is serving another call"};
-        Plan p = text_plan(m, a->texts);
-        const size_t T = p.T;
-        UBE_HIP(hipSetDevice(tr->device));
+        const size_t D = tr->model->g.hidden;
         hipStream_t st = (hipStream_t)a->stream;
-        // byte of every kept token, grouped by value in token order (the embedding gradient's fixed order)
-        std::vector<uint8_t> bytes(p.input_hi - p.input_lo);
-        if (!bytes.empty()) {
-            const bool dev = pointer_on_device(a->texts.data, tr->device);
-            const char *src = (const char *)a->texts.data + p.input_lo;
-            if (dev) UBE_HIP(hipMemcpy(bytes.data(), src, bytes.size(), hipMemcpyDeviceToHost));
-            else std::memcpy(bytes.data(), src, bytes.size());
+        if (a->after_forward) {
+            if (!tr->fw_valid)
+                throw Failure{ube_status_invalid_argument_k, "no training forward since the last step"};
+        } else {
+            if (!a->arena) throw Failure{ube_status_invalid_argument_k, "NULL arena"};
+            ArenaLease lease(a->arena);
+            if (!lease.held) throw Failure{ube_status_contended_k, "the arena is serving another call"};
+            ube_rows_view_t rows{};
+            train_forward(tr, a->arena, st, a->texts, a->stats, &rows);
         }
-        std::vector<uint32_t> tok_off(V + 1, 0), tok(std::max<size_t>(T, 1));
-        for (size_t i = 0; i < count; ++i)
-            for (int t = p.cu[i]; t < p.cu[i + 1]; ++t) ++tok_off[bytes[p.src[i] - p.input_lo + (t - p.cu[i])] + 1];
-        for (size_t v = 0; v < V; ++v) tok_off[v + 1] += tok_off[v];
-        {
-            std::vector<uint32_t> fill(tok_off.begin(), tok_off.end() - 1);
-            for (size_t i = 0; i < count; ++i)
-                for (int t = p.cu[i]; t < p.cu[i + 1]; ++t)
-                    tok[fill[bytes[p.src[i] - p.input_lo + (t - p.cu[i])]]++] = (uint32_t)t;
-        }
-        // workspace
-        TrainLayout L = train_carve(g, T, count);
-        if (L.total > tr->ws_cap) {
-            UBE_HIP(hipStreamSynchronize(st));
-            if (tr->ws) UBE_HIP(hipFree(tr->ws));
-            tr->ws = nullptr;
-            tr->ws_cap = 0;
-            const size_t want = align_up(L.total, (size_t)1 << 20);
-            UBE_HIP(hipMalloc((void **)&tr->ws, want));
-            tr->ws_cap = want;
-            UBE_HIP(hipMemsetAsync(tr->ws, 0, want, st));
-        }
-        char *wb = tr->ws;
-        auto F32 = [&](size_t o) { return (float *)(wb + o); };
-        auto B16 = [&](size_t o) { return (uint16_t *)(wb + o); };
-        UBE_HIP(hipMemcpyAsync(wb + L.tok_off, tok_off.data(), (V + 1) * 4, hipMemcpyHostToDevice, st));
-        UBE_HIP(hipMemcpyAsync(wb + L.tok, tok.data(), tok.size() * 4, hipMemcpyHostToDevice, st));
-        // forward with the block inputs stashed (fp32), leaving xf, scores, cu, tiles and positions in the arena
-        Layout EL{};
-        ube_rows_view_t rows{};
-        {
-            EncodeRequest r{m, a->arena, st, 1, ube_scalar_f32_k, &rows, a->stats, F32(L.stash), a->texts.data,
-                            a->texts.offsets, count, 0, nullptr, nullptr, &EL};
-            run_encode(r, p, false);
-        }
-        if (T == 0) {
-            for (auto const &t : tr->tensors)
-                UBE_HIP(hipMemsetAsync(t.grad, 0, t.rows * (t.cols ? t.cols : 1) * 4, st));
-            if (a->completion == 0) UBE_HIP(hipStreamSynchronize(st));
-            set_outcome(a->outcome, ube_status_success_k, nullptr);
-            return;
-        }
-        char *ab = a->arena->dev;
-        const int *cu = (const int *)(ab + EL.cu);
-        const int2 *tiles = (const int2 *)(ab + EL.tiles);
-        const int ntiles = (int)p.tiles.size();
-        const int16_t *pos = (const int16_t *)(ab + EL.pos);
-        const uint16_t *xf = (const uint16_t *)(ab + EL.xf);
-        const float *sc = (const float *)(ab + EL.s);
-        auto &TT = tr->tensors;
-        const int Ti = (int)T, Di = (int)D, Fi = (int)F, Hi = (int)H;
-        const int ldvt = (int)L.Tpad, ldl = (int)L.Tpad;
-        const int blocks = rmsnorm_bwd_blocks(Ti, (int)L.rows_per_block);
-        auto xty = [&](const uint16_t *x, int M, const uint16_t *y, int Nn, float *out, float *out2, bool di) {
-            timed(ube_kernel_weight_grad_k, st, [&] {
-                return launch_xty(x, M, y, Nn, Ti, M, Nn, F32(L.xty), (int)L.xty_splits, (int)L.xty_chunk, out, out2, di,
-                                  st);
-            });
-        };
-        // ---- pool and final norm
-        PoolBwdArgs pa{};
-        pa.xf = xf, pa.s = sc, pa.cu = cu, pa.count = (int)count, pa.D = Di, pa.H = Hi, pa.u = m->u;
-        pa.wv = TT[tr->t_wv].w16, pa.wk = TT[tr->t_wk].w16, pa.query = TT[tr->t_query].w16;
-        pa.dpooled = a->d_embeddings;
-        pa.dxf = F32(L.dxf), pa.z = F32(L.z), pa.du = F32(L.du);
-        pa.dwv = TT[tr->t_wv].grad, pa.dwk = TT[tr->t_wk].grad, pa.dquery = TT[tr->t_query].grad;
-        UBE_HIP(launch_pool_bwd(pa, F32(L.dz), F32(L.pd), st));
-        UBE_HIP(launch_rmsnorm_bwd(F32(L.stash) + N * T * D, TT[tr->t_gf].w32, F32(L.dxf), nullptr, F32(L.dx), B16(L.dxb),
-                                   F32(L.gpart), (int)L.rows_per_block, Ti, Di, eps, st));
-        UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[tr->t_gf].grad, F32(L.gsum), st));
-        // ---- blocks, last to first: replay the forward from the stashed input, then its backward
-        for (size_t li = N; li-- > 0;) {
-            auto const &b = tr->blocks[li];
-            const float *x_in = F32(L.stash) + li * T * D;
-            uint16_t *h1 = B16(L.h1), *qk = B16(L.qk), *vt = B16(L.vt), *v = B16(L.v), *o = B16(L.o);
-            float *lse = F32(L.lse), *delta = F32(L.delta), *x1 = F32(L.x1);
-            uint16_t *h2 = B16(L.h2), *gu = B16(L.gu);
-            // replay
-            UBE_HIP(launch_rmsnorm(x_in, TT[b.g1].w32, h1, Ti, Di, eps, st));
-            UBE_HIP(hipMemset2DAsync(vt + T, (size_t)ldvt * 2, 0, 64 * 2, D, st));
-            GemmArgs qa{};
-            qa.w = b.qkvT, qa.x = h1, qa.M = Ti, qa.N = 3 * Di, qa.K = Di;
-            qa.out_bf16 = qk, qa.ld_out = 2 * Di, qa.vt = vt, qa.ld_vt = ldvt, qa.pos = pos, qa.rope = m->rope;
-            qa.D = Di, qa.sec0 = m->sec0, qa.sec1 = m->sec1;
-            UBE_HIP(launch_gemm(kEpiQkv, qa, st));
-            UBE_HIP(launch_attention(qk, qk + D, 2 * Di, vt, ldvt, o, Di, cu, tiles, ntiles, Hi, st, lse, ldl));
-            UBE_HIP(launch_vt_rows(vt, ldvt, v, Ti, Di, st));
-            UBE_HIP(hipMemcpyAsync(x1, x_in, T * D * 4, hipMemcpyDeviceToDevice, st));
-            gemm(kEpiResid, b.oT, o, Ti, Di, Di, nullptr, 0, x1, Di, st);
-            UBE_HIP(launch_rmsnorm(x1, TT[b.g2].w32, h2, Ti, Di, eps, st));
-            gemm(kEpiStore, b.guT, h2, Ti, 2 * Fi, Di, gu, 2 * Fi, nullptr, 0, st);
-            // MLP half
-            float *dx = F32(L.dx), *dh = F32(L.dh), *dx1 = F32(L.dx1);
-            uint16_t *dxb = B16(L.dxb), *da = B16(L.da), *dgu = B16(L.dgu), *act = B16(L.act), *dx1b = B16(L.dx1b);
-            gemm(kEpiStore, TT[b.down].w16, dxb, Ti, Fi, Di, da, Fi, nullptr, 0, st);
-            UBE_HIP(launch_swiglu_bwd(gu, da, dgu, act, Ti, Fi, st));
-            xty(act, Fi, dxb, Di, TT[b.down].grad, nullptr, false);
-            gemm(kEpiPatch, b.gu_cols, dgu, Ti, Di, 2 * Fi, nullptr, 0, dh, Di, st);
-            xty(h2, Di, dgu, 2 * Fi, TT[b.gate].grad, TT[b.up].grad, true);
-            UBE_HIP(launch_rmsnorm_bwd(x1, TT[b.g2].w32, dh, dx, dx1, dx1b, F32(L.gpart), (int)L.rows_per_block, Ti, Di,
-                                       eps, st));
-            UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[b.g2].grad, F32(L.gsum), st));
-            // attention half
-            uint16_t *dout = B16(L.dout), *dq = B16(L.dq), *dk = B16(L.dk), *dv = B16(L.dv), *dqkv = B16(L.dqkv);
-            gemm(kEpiStore, TT[b.o].w16, dx1b, Ti, Di, Di, dout, Di, nullptr, 0, st);
-            xty(o, Di, dx1b, Di, TT[b.o].grad, nullptr, false);
-            UBE_HIP(launch_attention_delta(dout, o, Di, delta, ldl, Ti, Hi, st));
-            AttnBwdArgs ab2{};
-            ab2.q = qk, ab2.k = qk + D, ab2.ldqk = 2 * Di, ab2.v = v, ab2.ldv = Di, ab2.dout = dout, ab2.lddo = Di;
-            ab2.lse = lse, ab2.delta = delta, ab2.ldl = ldl, ab2.dq = dq, ab2.dk = dk, ab2.dv = dv, ab2.ldd = Di;
-            ab2.cu = cu, ab2.tiles = tiles, ab2.ntiles = ntiles, ab2.heads = Hi;
-            timed(ube_kernel_attention_bwd_k, st, [&] { return launch_attention_bwd(ab2, st); });
-            UBE_HIP(launch_rope_bwd(dq, dk, dv, Di, pos, m->rope, dqkv, Ti, Di, st));
-            gemm(kEpiPatch, TT[b.qkv].w16, dqkv, Ti, Di, 3 * Di, nullptr, 0, dh, Di, st);
-            xty(h1, Di, dqkv, 3 * Di, TT[b.qkv].grad, nullptr, false);
-            UBE_HIP(launch_rmsnorm_bwd(x_in, TT[b.g1].w32, dh, dx1, dx, dxb, F32(L.gpart), (int)L.rows_per_block, Ti, Di,
-                                       eps, st));
-            UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[b.g1].grad, F32(L.gsum), st));
-        }
-        UBE_HIP(launch_embed_bwd(F32(L.dx), (const uint32_t *)(wb + L.tok_off), (const uint32_t *)(wb + L.tok), (int)V,
-                                 Di, TT[tr->t_embed].grad, st));
+        if (tr->fw_count && !a->d_embeddings) throw Failure{ube_status_invalid_argument_k, "NULL embedding gradient"};
+        if (tr->fw_count && a->d_embeddings_stride && a->d_embeddings_stride != D * 4)
+            throw Failure{ube_status_unsupported_k, "embedding gradient rows must be packed"};
+        train_backward(tr, st, a->d_embeddings);
         if (a->completion == 0) UBE_HIP(hipStreamSynchronize(st));
         set_outcome(a->outcome, ube_status_success_k, nullptr);
     } catch (Failure const &f) {
@@ -1725,6 +1827,7 @@ extern "C" void ube_trainer_step(ube_trainer_step_t *a) {
         UBE_HIP(hipSetDevice(tr->device));
         hipStream_t st = (hipStream_t)a->stream;
         tr->step += 1;
+        tr->fw_valid = false;  // the kept activations belong to the weights before this update
         const double t = (double)tr->step;
         const float beta2 = (float)(1.0 - std::pow(t, (double)tr->decay));
         const float bc = (float)(1.0 - std::pow((double)tr->beta1, t));

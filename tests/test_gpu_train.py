@@ -125,6 +125,32 @@ def test_adafactor_step_and_refreshed_forward(ube):
     assert cos.min() >= COS_MIN and err <= 2e-2
 
 
+def test_forward_then_backward(ube):
+    """The training forward returns the encode's rows bit for bit, and a backward over its kept activations
+    equals the self-contained backward bit for bit; after a step the kept activations are refused."""
+    import torch
+    g, w, batch, model, trainer, arena = _setup(ube, "tiny", 6, seed=4)
+    data = device_bytes(batch.data)
+    d = torch.from_numpy(np.random.default_rng(11).standard_normal((batch.count, g["hidden"])).astype(np.float32)).cuda()
+    rows, (_, tokens) = trainer.forward(arena, data, batch.offsets)
+    got = rows.tensor()
+    enc, _ = ube.text_encode(model, arena, data, batch.offsets)
+    assert tokens == int(np.diff(batch.offsets).sum()) and torch.equal(got, enc.tensor())
+    trainer.backward(None, None, None, d, after_forward=True)
+    torch.cuda.synchronize()
+    kept = [gr.clone() for _, _, _, gr in trainer.tensors()]
+    trainer.backward(arena, data, batch.offsets, d)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(kept, [gr for _, _, _, gr in trainer.tensors()]))
+    # the self-contained backward leaves its own forward kept: a second pass over it agrees too
+    trainer.backward(None, None, None, d, after_forward=True)
+    torch.cuda.synchronize()
+    assert all(torch.equal(a, b) for a, b in zip(kept, [gr for _, _, _, gr in trainer.tensors()]))
+    trainer.step(1e-3)
+    with pytest.raises(ube.UbeError):
+        trainer.backward(None, None, None, d, after_forward=True)
+
+
 def test_depth12_backward_matches_oracle(ube):
     """The depth-12, hidden-512 encoder on a few ragged rows (cosine and max-difference bars as above)."""
     import torch
