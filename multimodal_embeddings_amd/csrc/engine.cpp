@@ -1337,11 +1337,15 @@ struct ube_trainer_handle_t {
     std::vector<Tensor> tensors;
     struct Block {  // indices into tensors, and packings derived from the masters
         size_t qkv, o, gate, up, down, g1, g2;
-        uint16_t *qkvT, *oT, *guT, *dT, *gu_cols;
+        uint16_t *guT, *gu_cols;
     };
     std::vector<Block> blocks;
     size_t t_embed = 0, t_gf = 0, t_query = 0, t_wk = 0, t_wv = 0;
-    float *ada_work = nullptr;
+    // device tables of the multi-tensor update and of the repacking, with their grid sizes
+    ube::AdaTensor *ada_table = nullptr;
+    int ada_stats = 0, ada_cols = 0, ada_upd = 0;
+    ube::PackJob *pack_table = nullptr;
+    int pack_jobs = 0, pack_wgs = 0;
     // the last training forward, whose activations the workspace holds until a step changes the weights
     bool fw_valid = false;
     size_t fw_T = 0, fw_count = 0, fw_ntiles = 0;
@@ -1423,32 +1427,10 @@ void gemm(int epi, const uint16_t *w, const uint16_t *x, int M, int N, int K, ui
     UBE_HIP(launch_gemm(epi, ga, st));
 }
 
-// Derived packings after the masters change: the trainer's unfolded [out x in] copies and interleaved
-// canonical gate/up columns, and the model's forward weights (gains folded, pool keys refolded).
+// Derived packings after the masters change (one launch over the job table): the trainer's unfolded
+// gate/up copies, the model's forward weights (gains folded, pool keys refolded) and its plain copies.
 void repack(ube_trainer_t tr, hipStream_t st) {
-    ube_model_t m = tr->model;
-    const ube_geometry_t &g = m->g;
-    const int D = (int)g.hidden, F = (int)g.ffn, H = (int)g.heads;
-    auto &T = tr->tensors;
-    for (size_t l = 0; l < g.depth; ++l) {
-        auto const &b = tr->blocks[l];
-        auto &ml = m->layers[l];
-        UBE_HIP(launch_pack_transpose(T[b.qkv].w16, nullptr, nullptr, b.qkvT, D, 3 * D, false, st));
-        UBE_HIP(launch_pack_transpose(T[b.o].w16, nullptr, nullptr, b.oT, D, D, false, st));
-        UBE_HIP(launch_pack_transpose(T[b.gate].w16, T[b.up].w16, nullptr, b.guT, D, F, true, st));
-        UBE_HIP(launch_pack_transpose(T[b.down].w16, nullptr, nullptr, b.dT, F, D, false, st));
-        UBE_HIP(launch_interleave_cols(T[b.gate].w16, T[b.up].w16, b.gu_cols, D, F, st));
-        UBE_HIP(launch_pack_transpose(T[b.qkv].w16, nullptr, T[b.g1].w32, ml.wqkv, D, 3 * D, false, st));
-        UBE_HIP(launch_pack_transpose(T[b.o].w16, nullptr, nullptr, ml.wo, D, D, false, st));
-        UBE_HIP(launch_pack_transpose(T[b.gate].w16, T[b.up].w16, T[b.g2].w32, ml.wgu, D, F, true, st));
-        UBE_HIP(launch_pack_transpose(T[b.down].w16, nullptr, nullptr, ml.wd, F, D, false, st));
-        UBE_HIP(hipMemcpyAsync(ml.g1, T[b.g1].w32, D * 4, hipMemcpyDeviceToDevice, st));
-        UBE_HIP(hipMemcpyAsync(ml.g2, T[b.g2].w32, D * 4, hipMemcpyDeviceToDevice, st));
-    }
-    UBE_HIP(hipMemcpyAsync(m->embed, T[tr->t_embed].w16, g.vocab * D * 2, hipMemcpyDeviceToDevice, st));
-    UBE_HIP(hipMemcpyAsync(m->gf, T[tr->t_gf].w32, D * 4, hipMemcpyDeviceToDevice, st));
-    UBE_HIP(hipMemcpyAsync(m->wv, T[tr->t_wv].w16, (size_t)D * D * 2, hipMemcpyDeviceToDevice, st));
-    UBE_HIP(launch_pool_u(T[tr->t_wk].w16, T[tr->t_query].w16, m->u, D, H, st));
+    UBE_HIP(launch_pack(tr->pack_table, tr->pack_jobs, tr->pack_wgs, st));
 }
 
 }  // namespace
@@ -1518,10 +1500,18 @@ extern "C" void ube_trainer_init(ube_trainer_init_t *a) {
             offs[i][4] = take(t.cols ? 0 : n * 4);       // v
             offs[i][5] = take(n * 4);                    // m
         }
-        std::vector<std::array<size_t, 5>> boffs(N);
-        for (size_t l = 0; l < N; ++l)
-            boffs[l] = {take(3 * D * D * 2), take(D * D * 2), take(2 * F * D * 2), take(F * D * 2), take(2 * F * D * 2)};
-        const size_t o_work = take((kAdafactorWork + kAdafactorColParts) * 4);
+        std::vector<std::array<size_t, 3>> aoffs(tr->tensors.size());  // col_parts, rms_parts, mean_r
+        for (size_t i = 0; i < tr->tensors.size(); ++i) {
+            auto const &t = tr->tensors[i];
+            const size_t n = t.rows * (t.cols ? t.cols : 1);
+            aoffs[i] = {take(t.cols ? (t.rows + kAdaSlice - 1) / kAdaSlice * t.cols * 4 : 0),
+                        take((n + kAdaChunk - 1) / kAdaChunk * 4), take(4)};
+        }
+        std::vector<std::array<size_t, 2>> boffs(N);
+        for (size_t l = 0; l < N; ++l) boffs[l] = {take(2 * F * D * 2), take(2 * F * D * 2)};
+        const size_t n_jobs = 8 * N + 4;
+        const size_t o_ada = take(tr->tensors.size() * sizeof(AdaTensor));
+        const size_t o_pack = take(n_jobs * sizeof(PackJob));
         UBE_HIP(hipMalloc((void **)&tr->mem, total));
         tr->bytes = total;
         UBE_HIP(hipMemset(tr->mem, 0, total));
@@ -1539,13 +1529,53 @@ extern "C" void ube_trainer_init(ube_trainer_init_t *a) {
         }
         for (size_t l = 0; l < N; ++l) {
             auto &b = tr->blocks[l];
-            b.qkvT = (uint16_t *)(db + boffs[l][0]);
-            b.oT = (uint16_t *)(db + boffs[l][1]);
-            b.guT = (uint16_t *)(db + boffs[l][2]);
-            b.dT = (uint16_t *)(db + boffs[l][3]);
-            b.gu_cols = (uint16_t *)(db + boffs[l][4]);
+            b.guT = (uint16_t *)(db + boffs[l][0]);
+            b.gu_cols = (uint16_t *)(db + boffs[l][1]);
         }
-        tr->ada_work = (float *)(db + o_work);
+        // the multi-tensor update's table
+        std::vector<AdaTensor> ada(tr->tensors.size());
+        for (size_t i = 0; i < tr->tensors.size(); ++i) {
+            auto const &t = tr->tensors[i];
+            AdaTensor &e = ada[i];
+            e.g = t.grad, e.w16 = t.w16, e.w32 = t.w32, e.r = t.r, e.c = t.c, e.v = t.v, e.m = t.m;
+            e.col_parts = (float *)(db + aoffs[i][0]), e.rms_parts = (float *)(db + aoffs[i][1]);
+            e.mean_r = (float *)(db + aoffs[i][2]);
+            e.rows = (int)t.rows, e.cols = (int)t.cols;
+        }
+        if (adafactor_grids(ada.data(), (int)ada.size(), &tr->ada_stats, &tr->ada_cols, &tr->ada_upd) != 0)
+            throw Failure{ube_status_unsupported_k, "a tensor of 2^31 elements or more"};
+        tr->ada_table = (AdaTensor *)(db + o_ada);
+        UBE_HIP(hipMemcpy(tr->ada_table, ada.data(), ada.size() * sizeof(AdaTensor), hipMemcpyHostToDevice));
+        // the repacking's jobs
+        {
+            auto &T = tr->tensors;
+            const int Di = (int)D, Fi = (int)F, Hi = (int)g.heads;
+            std::vector<PackJob> jobs;
+            auto job = [&](const void *src, const void *src2, const float *gain, void *dst, int K, int Nn, int kind) {
+                jobs.push_back(PackJob{src, src2, gain, dst, K, Nn, kind, 0});
+            };
+            for (size_t l = 0; l < N; ++l) {
+                auto const &b = tr->blocks[l];
+                auto &ml = m->layers[l];
+                job(T[b.gate].w16, T[b.up].w16, nullptr, b.guT, Di, Fi, kPackTransposePair);
+                job(T[b.gate].w16, T[b.up].w16, nullptr, b.gu_cols, Di, Fi, kPackColumnPair);
+                job(T[b.qkv].w16, nullptr, T[b.g1].w32, ml.wqkv, Di, 3 * Di, kPackTranspose);
+                job(T[b.o].w16, nullptr, nullptr, ml.wo, Di, Di, kPackTranspose);
+                job(T[b.gate].w16, T[b.up].w16, T[b.g2].w32, ml.wgu, Di, Fi, kPackTransposePair);
+                job(T[b.down].w16, nullptr, nullptr, ml.wd, Fi, Di, kPackTranspose);
+                job(T[b.g1].w32, nullptr, nullptr, ml.g1, 1, Di, kPackCopy);
+                job(T[b.g2].w32, nullptr, nullptr, ml.g2, 1, Di, kPackCopy);
+            }
+            job(T[tr->t_embed].w16, nullptr, nullptr, m->embed, 1, (int)(V * D / 2), kPackCopy);
+            job(T[tr->t_gf].w32, nullptr, nullptr, m->gf, 1, Di, kPackCopy);
+            job(T[tr->t_wv].w16, nullptr, nullptr, m->wv, 1, Di * Di / 2, kPackCopy);
+            job(T[tr->t_wk].w16, T[tr->t_query].w16, nullptr, m->u, Di, Hi, kPackPoolKeys);
+            if (jobs.size() > n_jobs) throw Failure{ube_status_invalid_argument_k, "packing table overflow"};
+            tr->pack_wgs = pack_workgroups(jobs.data(), (int)jobs.size());
+            tr->pack_jobs = (int)jobs.size();
+            tr->pack_table = (PackJob *)(db + o_pack);
+            UBE_HIP(hipMemcpy(tr->pack_table, jobs.data(), jobs.size() * sizeof(PackJob), hipMemcpyHostToDevice));
+        }
         // masters from the caller's canonical weights
         auto up16 = [&](size_t i, uint16_t const *src) {
             auto const &t = tr->tensors[i];
@@ -1831,14 +1861,9 @@ extern "C" void ube_trainer_step(ube_trainer_step_t *a) {
         const double t = (double)tr->step;
         const float beta2 = (float)(1.0 - std::pow(t, (double)tr->decay));
         const float bc = (float)(1.0 - std::pow((double)tr->beta1, t));
-        for (auto const &ts : tr->tensors) {
-            AdafactorArgs ad{};
-            ad.g = ts.grad, ad.w16 = ts.w16, ad.w32 = ts.w32, ad.r = ts.r, ad.c = ts.c, ad.v = ts.v, ad.m = ts.m;
-            ad.work = tr->ada_work, ad.rows = (int)ts.rows, ad.cols = (int)ts.cols;
-            ad.lr = a->learning_rate, ad.beta1 = tr->beta1, ad.beta2 = beta2, ad.eps1 = tr->eps1, ad.clip = tr->clip;
-            ad.bias_correction = bc;
-            UBE_HIP(launch_adafactor(ad, st));
-        }
+        AdaStep as{a->learning_rate, tr->beta1, beta2, tr->eps1, tr->clip, bc};
+        UBE_HIP(launch_adafactor(tr->ada_table, (int)tr->tensors.size(), tr->ada_stats, tr->ada_cols, tr->ada_upd, as,
+                                 st));
         repack(tr, st);
         if (a->completion == 0) UBE_HIP(hipStreamSynchronize(st));
         set_outcome(a->outcome, ube_status_success_k, nullptr);

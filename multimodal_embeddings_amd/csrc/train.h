@@ -76,30 +76,46 @@ struct PoolBwdArgs {
 // dz [count x H x D] and pd [T x H x 2] are work buffers
 hipError_t launch_pool_bwd(const PoolBwdArgs &a, float *dz, float *pd, hipStream_t stream);
 
-// Adafactor on one tensor: rows x cols (cols == 0: a vector of `rows`); g fp32; master bf16 (w16) or fp32
-// (w32); state r [rows], c [cols] (matrices) or v [rows] (vectors), m [rows x cols]; work: kAdafactorWork +
-// kAdafactorColParts floats. lr, beta2 and the bias correction 1 - beta1^t come from the host.
-struct AdafactorArgs {
+// Adafactor over every tensor of a model in four launches. One table entry per tensor (device memory,
+// built once): gradient g fp32; master bf16 (w16) or fp32 (w32); state r [rows], c [cols] (matrices) or
+// v [rows] (vectors), m [rows x cols]; work: col_parts [ceil(rows / kAdaSlice) x cols], rms_parts
+// [ceil(count / kAdaChunk)], mean_r [1]. adafactor_grids fills the wg_* fields (host copy of the table)
+// and the three grid sizes; -1 for an empty tensor or one of 2^31 elements or more.
+constexpr int kAdaSlice = 32;
+constexpr int kAdaChunk = 4096;
+struct AdaTensor {
     const float *g;
     uint16_t *w16;
     float *w32;
     float *r, *c, *v, *m;
-    float *work;
-    int rows, cols;
+    float *col_parts, *rms_parts, *mean_r;
+    int rows, cols;  // cols == 0: a vector of `rows`
+    int wg_stats, wg_cols, wg_upd;
+};
+struct AdaStep {
     float lr, beta1, beta2, eps1, clip, bias_correction;
 };
-hipError_t launch_adafactor(const AdafactorArgs &a, hipStream_t stream);
+int adafactor_grids(AdaTensor *table, int n, int *stats, int *cols, int *upd);
+hipError_t launch_adafactor(const AdaTensor *table, int n, int stats, int cols, int upd, const AdaStep &step,
+                            hipStream_t stream);
 
-// Packing for the forward: out[n][k] = bf16(W[k][n] * (gain ? gain[k] : 1)) for W [K x N] bf16; with
-// `interleave`, W is the pair (W, W2) [K x N] each and out rows run over [W 32 | W2 32] blocks.
-hipError_t launch_pack_transpose(const uint16_t *w, const uint16_t *w2, const float *gain, uint16_t *out, int K,
-                                 int N, bool interleave, hipStream_t stream);
-// out [K x 2N]: the columns of W and W2 [K x N] interleaved in blocks of 32 ([W 32 | W2 32] per 64)
-hipError_t launch_interleave_cols(const uint16_t *w, const uint16_t *w2, uint16_t *out, int K, int N,
-                                  hipStream_t stream);
-// the pool's folded keys u_h = W_k[:, head h] q_h / 8 ([H x D] fp32)
-hipError_t launch_pool_u(const uint16_t *wk, const uint16_t *query, float *u, int D, int H, hipStream_t stream);
-constexpr int kAdafactorWork = 2 + 128;           // floats of AdafactorArgs::work before the column partials
-constexpr size_t kAdafactorColParts = 1 << 18;   // column partials (ceil(rows / 32) x cols floats) after them
+// The derived copies of the masters in one launch, from a device table of jobs (pack_workgroups fills
+// first_wg on the host copy and returns the grid size):
+//   kPackTranspose:     dst[n][k] = bf16(src[k][n] * (gain ? gain[k] : 1)), src [K x N] bf16
+//   kPackTransposePair: the same over the pair (src, src2) [K x N] each, dst rows running over
+//                       [src 32 | src2 32] column blocks ([2N x K])
+//   kPackColumnPair:    dst [K x 2N], the columns of src and src2 interleaved in blocks of 32
+//   kPackCopy:          K x N 32-bit words
+//   kPackPoolKeys:      dst[h][i] = src[i, 64h .. 64h + 63] . src2[64h ..] / 8 (fp32 [N x K]; K = hidden,
+//                       N = heads; src W_k, src2 the pool query)
+enum PackKind { kPackTranspose = 0, kPackTransposePair = 1, kPackColumnPair = 2, kPackCopy = 3, kPackPoolKeys = 4 };
+struct PackJob {
+    const void *src, *src2;
+    const float *gain;
+    void *dst;
+    int K, N, kind, first_wg;
+};
+int pack_workgroups(PackJob *jobs, int n);
+hipError_t launch_pack(const PackJob *jobs, int n, int workgroups, hipStream_t stream);
 
 }  // namespace ube

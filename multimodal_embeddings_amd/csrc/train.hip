@@ -647,34 +647,25 @@ __global__ __launch_bounds__(256) void k_pool_bwd_weights(PoolBwdArgs a, const f
 // Shazeer and Stern's update with the first moment the pages add: for a matrix, row and column means of
 // g^2 + eps1 decayed by beta2 (r, c), v = r c^T / mean(r); for a vector, v decayed elementwise;
 // u = g / sqrt(v), clipped to RMS(u) <= clip; m = beta1 m + (1 - beta1) u; w -= lr m / (1 - beta1^t).
-// Sums run over fixed ranges in a fixed order.
+// Every tensor of the model in the same four launches (statistics, column means, sums of u^2, update);
+// a workgroup finds its tensor by binary search over the table's first-workgroup fields. Sums run over
+// fixed ranges in a fixed order.
 
-constexpr int kAdaParts = 128;
-
-__global__ __launch_bounds__(256) void k_ada_rows(AdafactorArgs a) {
-    if (a.cols == 0) {  // vector: one thread per element
-        const int i = blockIdx.x * 256 + threadIdx.x;
-        if (i < a.rows) a.v[i] = a.beta2 * a.v[i] + (1.f - a.beta2) * (a.g[i] * a.g[i] + a.eps1);
-        return;
-    }
-    const int lane = threadIdx.x & 63, row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= a.rows) return;
-    float s = 0.f;
-    for (int j = lane; j < a.cols; j += 64) {
-        const float g = a.g[(size_t)row * a.cols + j];
-        s += g * g + a.eps1;
-    }
-    s = wave_sum(s);
-    if (lane == 0) a.r[row] = a.beta2 * a.r[row] + (1.f - a.beta2) * s / (float)a.cols;
+template <int kField>
+__device__ __forceinline__ int ada_first(const AdaTensor &t) {
+    return kField == 0 ? t.wg_stats : (kField == 1 ? t.wg_cols : t.wg_upd);
 }
 
-// column means from the slice partials (k_col_parts over g^2 + eps1), in slice order
-__global__ __launch_bounds__(256) void k_ada_cols(AdafactorArgs a, const float *parts, int slices) {
-    const int j = blockIdx.x * 256 + threadIdx.x;
-    if (j >= a.cols) return;
-    float s = 0.f;
-    for (int b = 0; b < slices; ++b) s += parts[(size_t)b * a.cols + j];
-    a.c[j] = a.beta2 * a.c[j] + (1.f - a.beta2) * s / (float)a.rows;
+// the last tensor whose first workgroup (of grid kField) is <= wg
+template <int kField>
+__device__ int ada_find(const AdaTensor *tab, int n, int wg) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ada_first<kField>(tab[mid]) <= wg) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
 }
 
 __device__ __forceinline__ float block_sum256(float v, float *red) {
@@ -686,103 +677,182 @@ __device__ __forceinline__ float block_sum256(float v, float *red) {
     return ((red[0] + red[1]) + red[2]) + red[3];
 }
 
-// work[0] = mean(r) (matrices)
-__global__ __launch_bounds__(256) void k_ada_mean(AdafactorArgs a) {
-    __shared__ float red[4];
-    float s = 0.f;
-    for (int i = threadIdx.x; i < a.rows; i += 256) s += a.r[i];
-    s = block_sum256(s, red);
-    if (threadIdx.x == 0) a.work[0] = s / (float)a.rows;
+// matrices: one workgroup per slice of kAdaSlice rows (column partials of the slice, then the decayed
+// row means); vectors: 256 elements of v per workgroup
+__global__ __launch_bounds__(256) void k_ada_stats(const AdaTensor *tab, int n, AdaStep st) {
+    const int t = ada_find<0>(tab, n, blockIdx.x);
+    const AdaTensor a = tab[t];
+    const int local = blockIdx.x - a.wg_stats, tid = threadIdx.x;
+    if (a.cols == 0) {
+        const int i = local * 256 + tid;
+        if (i < a.rows) a.v[i] = st.beta2 * a.v[i] + (1.f - st.beta2) * (a.g[i] * a.g[i] + st.eps1);
+        return;
+    }
+    const int r0 = local * kAdaSlice, r1 = min(a.rows, r0 + kAdaSlice);
+    for (int j = tid; j < a.cols; j += 256) {
+        float sum = 0.f;
+        for (int i = r0; i < r1; ++i) {
+            const float g = a.g[(size_t)i * a.cols + j];
+            sum += g * g + st.eps1;
+        }
+        a.col_parts[(size_t)local * a.cols + j] = sum;
+    }
+    const int lane = tid & 63, wave = tid >> 6;
+    for (int k = 0; k < kAdaSlice / 4; ++k) {
+        const int row = r0 + wave * (kAdaSlice / 4) + k;
+        if (row >= r1) break;
+        float sum = 0.f;
+        for (int j = lane; j < a.cols; j += 64) {
+            const float g = a.g[(size_t)row * a.cols + j];
+            sum += g * g + st.eps1;
+        }
+        sum = wave_sum(sum);
+        if (lane == 0) a.r[row] = st.beta2 * a.r[row] + (1.f - st.beta2) * sum / (float)a.cols;
+    }
 }
 
-__device__ __forceinline__ float ada_u(const AdafactorArgs &a, size_t idx) {
+// matrices: decayed column means from the slice partials (slice order), 256 columns per workgroup; the
+// tensor's first workgroup also writes mean(r)
+__global__ __launch_bounds__(256) void k_ada_cols(const AdaTensor *tab, int n, AdaStep st) {
+    __shared__ float red[4];
+    const int t = ada_find<1>(tab, n, blockIdx.x);
+    const AdaTensor a = tab[t];
+    const int local = blockIdx.x - a.wg_cols, tid = threadIdx.x;
+    if (local == 0) {
+        float sum = 0.f;
+        for (int i = tid; i < a.rows; i += 256) sum += a.r[i];
+        sum = block_sum256(sum, red);
+        if (tid == 0) a.mean_r[0] = sum / (float)a.rows;
+    }
+    const int j = local * 256 + tid;
+    if (j >= a.cols) return;
+    const int slices = (a.rows + kAdaSlice - 1) / kAdaSlice;
+    float sum = 0.f;
+    for (int b = 0; b < slices; ++b) sum += a.col_parts[(size_t)b * a.cols + j];
+    a.c[j] = st.beta2 * a.c[j] + (1.f - st.beta2) * sum / (float)a.rows;
+}
+
+__device__ __forceinline__ float ada_u(const AdaTensor &a, int idx, float mean_r) {
     const float g = a.g[idx];
     if (a.cols == 0) return g * rsqrtf(a.v[idx]);
-    const int i = (int)(idx / a.cols), j = (int)(idx % a.cols);
-    return g * rsqrtf(a.r[i] * a.c[j] / a.work[0]);
+    const int i = idx / a.cols, j = idx - i * a.cols;
+    return g * rsqrtf(a.r[i] * a.c[j] / mean_r);
 }
 
-// work[2 + b] = sum of u^2 over part b (kAdaParts equal ranges)
-__global__ __launch_bounds__(256) void k_ada_rms_parts(AdafactorArgs a) {
+// sum of u^2 over each chunk of kAdaChunk elements
+__global__ __launch_bounds__(256) void k_ada_rms(const AdaTensor *tab, int n, AdaStep st) {
     __shared__ float red[4];
-    const size_t n = (size_t)a.rows * (a.cols ? a.cols : 1);
-    const size_t per = (n + kAdaParts - 1) / kAdaParts, b0 = blockIdx.x * per, b1 = min(n, b0 + per);
-    float s = 0.f;
-    for (size_t x = b0 + threadIdx.x; x < b1; x += 256) {
-        const float u = ada_u(a, x);
-        s += u * u;
+    const int t = ada_find<2>(tab, n, blockIdx.x);
+    const AdaTensor a = tab[t];
+    const int local = blockIdx.x - a.wg_upd;
+    const int count = a.rows * (a.cols ? a.cols : 1);
+    const int e0 = local * kAdaChunk, e1 = min(count, e0 + kAdaChunk);
+    const float mean_r = a.cols ? a.mean_r[0] : 1.f;
+    float sum = 0.f;
+    for (int x = e0 + threadIdx.x; x < e1; x += 256) {
+        const float u = ada_u(a, x, mean_r);
+        sum += u * u;
     }
-    s = block_sum256(s, red);
-    if (threadIdx.x == 0) a.work[2 + blockIdx.x] = s;
+    sum = block_sum256(sum, red);
+    if (threadIdx.x == 0) a.rms_parts[local] = sum;
 }
 
-// work[1] = 1 / max(1, RMS(u) / clip)
-__global__ __launch_bounds__(64) void k_ada_clip(AdafactorArgs a) {
-    if (threadIdx.x) return;
-    const size_t n = (size_t)a.rows * (a.cols ? a.cols : 1);
-    float s = 0.f;
-    for (int b = 0; b < kAdaParts; ++b) s += a.work[2 + b];
-    const float rms = sqrtf(s / (float)n);
-    a.work[1] = 1.f / fmaxf(1.f, rms / a.clip);
-}
-
-__global__ __launch_bounds__(256) void k_ada_update(AdafactorArgs a) {
-    const size_t n = (size_t)a.rows * (a.cols ? a.cols : 1);
-    const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (x >= n) return;
-    const float u = ada_u(a, x) * a.work[1];
-    const float m = a.beta1 * a.m[x] + (1.f - a.beta1) * u;
-    a.m[x] = m;
-    const float step = a.lr * m / a.bias_correction;
-    if (a.w16) a.w16[x] = (uint16_t)f32_to_bf16(bf16_to_f32(a.w16[x]) - step);
-    else a.w32[x] = a.w32[x] - step;
+// clip factor from all chunks' sums, then the first moment and the master update of this chunk
+__global__ __launch_bounds__(256) void k_ada_apply(const AdaTensor *tab, int n, AdaStep st) {
+    __shared__ float red[4];
+    const int t = ada_find<2>(tab, n, blockIdx.x);
+    const AdaTensor a = tab[t];
+    const int local = blockIdx.x - a.wg_upd;
+    const int count = a.rows * (a.cols ? a.cols : 1);
+    const int chunks = (count + kAdaChunk - 1) / kAdaChunk;
+    float sum = 0.f;
+    for (int b = threadIdx.x; b < chunks; b += 256) sum += a.rms_parts[b];
+    sum = block_sum256(sum, red);
+    const float rms = sqrtf(sum / (float)count);
+    const float scale = 1.f / fmaxf(1.f, rms / st.clip);
+    const float mean_r = a.cols ? a.mean_r[0] : 1.f;
+    const int e0 = local * kAdaChunk, e1 = min(count, e0 + kAdaChunk);
+    for (int x = e0 + threadIdx.x; x < e1; x += 256) {
+        const float u = ada_u(a, x, mean_r) * scale;
+        const float m = st.beta1 * a.m[x] + (1.f - st.beta1) * u;
+        a.m[x] = m;
+        const float step = st.lr * m / st.bias_correction;
+        if (a.w16) a.w16[x] = (uint16_t)f32_to_bf16(bf16_to_f32(a.w16[x]) - step);
+        else a.w32[x] = a.w32[x] - step;
+    }
 }
 
 // -------------------------------------------------------------------------------------------- packing
+//
+// The forward's and the backward's derived copies of the masters, every one in one launch: a table of
+// jobs, each a range of workgroups (binary search over first_wg).
 
-// out[n][k] = bf16(W[k][n] * gain[k]) through 64 x 64 LDS tiles; interleaved: out row n takes column
-// 32 (n / 64) + n % 32 of W (n % 64 < 32) or W2
-__global__ __launch_bounds__(256) void k_pack_transpose(const uint16_t *w, const uint16_t *w2, const float *gain,
-                                                        uint16_t *out, int K, int N, int interleave) {
+__device__ int pack_find(const PackJob *jobs, int n, int wg) {
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (jobs[mid].first_wg <= wg) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(256) void k_pack(const PackJob *jobs, int n) {
     __shared__ float tile[64][65];
-    const int n0 = blockIdx.x * 64, k0 = blockIdx.y * 64;
-    const int NO = interleave ? 2 * N : N;
-    for (int x = threadIdx.x; x < 64 * 64; x += 256) {
-        const int kk = x >> 6, nn = x & 63, n = n0 + nn;
-        const uint16_t *src = w;
-        int col = n;
-        if (interleave) {
-            src = (n & 63) < 32 ? w : w2;
-            col = (n >> 6) * 32 + (n & 31);
+    const PackJob jb = jobs[pack_find(jobs, n, blockIdx.x)];
+    const int local = blockIdx.x - jb.first_wg, tid = threadIdx.x;
+    const int K = jb.K, N = jb.N;
+    if (jb.kind == kPackTranspose || jb.kind == kPackTransposePair) {
+        // out[n][k] = bf16(W[k][n] * gain[k]) through a 64 x 64 LDS tile; pair: out row n takes column
+        // 32 (n / 64) + n % 32 of W (n % 64 < 32) or of W2
+        const bool pair = jb.kind == kPackTransposePair;
+        const int NO = pair ? 2 * N : N, ntn = (NO + 63) / 64;
+        const int n0 = (local % ntn) * 64, k0 = (local / ntn) * 64;
+        const uint16_t *w = (const uint16_t *)jb.src, *w2 = (const uint16_t *)jb.src2;
+        for (int x = tid; x < 64 * 64; x += 256) {
+            const int kk = x >> 6, nn = x & 63, nx = n0 + nn;
+            const uint16_t *src = w;
+            int col = nx;
+            if (pair) {
+                src = (nx & 63) < 32 ? w : w2;
+                col = (nx >> 6) * 32 + (nx & 31);
+            }
+            const bool in = nx < NO && k0 + kk < K;
+            const float g = jb.gain && in ? jb.gain[k0 + kk] : 1.f;
+            tile[kk][nn] = in ? bf16_to_f32(src[(size_t)(k0 + kk) * N + col]) * g : 0.f;
         }
-        const float g = gain ? gain[k0 + kk] : 1.f;
-        tile[kk][nn] = (n < NO && k0 + kk < K) ? bf16_to_f32(src[(size_t)(k0 + kk) * N + col]) * g : 0.f;
+        __syncthreads();
+        uint16_t *out = (uint16_t *)jb.dst;
+        for (int x = tid; x < 64 * 64; x += 256) {
+            const int nn = x >> 6, kk = x & 63;
+            if (n0 + nn < NO && k0 + kk < K) out[(size_t)(n0 + nn) * K + k0 + kk] = (uint16_t)f32_to_bf16(tile[kk][nn]);
+        }
+    } else if (jb.kind == kPackColumnPair) {
+        // out [K x 2N]: columns of W and W2 interleaved in blocks of 32 ([W 32 | W2 32] per 64)
+        const uint16_t *w = (const uint16_t *)jb.src, *w2 = (const uint16_t *)jb.src2;
+        uint16_t *out = (uint16_t *)jb.dst;
+        const size_t total = (size_t)K * 2 * N;
+        for (size_t x = (size_t)local * 4096 + tid; x < min(total, (size_t)(local + 1) * 4096); x += 256) {
+            const int k = (int)(x / (2 * N)), nx = (int)(x % (2 * N));
+            const uint16_t *src = (nx & 63) < 32 ? w : w2;
+            out[x] = src[(size_t)k * N + (nx >> 6) * 32 + (nx & 31)];
+        }
+    } else if (jb.kind == kPackCopy) {
+        // K x N 32-bit words
+        const uint32_t *src = (const uint32_t *)jb.src;
+        uint32_t *out = (uint32_t *)jb.dst;
+        const size_t total = (size_t)K * N;
+        for (size_t x = (size_t)local * 4096 + tid; x < min(total, (size_t)(local + 1) * 4096); x += 256) out[x] = src[x];
+    } else {
+        // pool keys: u[h][i] = W_k[i, 64h .. 64h + 63] . q_h / 8 (K = D, N = heads; src W_k, src2 the query)
+        const uint16_t *wk = (const uint16_t *)jb.src, *q = (const uint16_t *)jb.src2;
+        const int x = local * 256 + tid;
+        if (x >= N * K) return;
+        const int h = x / K, i = x % K;
+        float sum = 0.f;
+        for (int e = 0; e < 64; ++e) sum += bf16_to_f32(wk[(size_t)i * K + 64 * h + e]) * bf16_to_f32(q[64 * h + e]);
+        ((float *)jb.dst)[x] = sum * 0.125f;
     }
-    __syncthreads();
-    for (int x = threadIdx.x; x < 64 * 64; x += 256) {
-        const int nn = x >> 6, kk = x & 63;
-        if (n0 + nn < NO && k0 + kk < K) out[(size_t)(n0 + nn) * K + k0 + kk] = (uint16_t)f32_to_bf16(tile[kk][nn]);
-    }
-}
-
-// out[k][32 b + ...]: rows of W and W2 interleaved in blocks of 32 columns ([W 32 | W2 32] per 64)
-__global__ __launch_bounds__(256) void k_interleave_cols(const uint16_t *w, const uint16_t *w2, uint16_t *out, int K,
-                                                         int N) {
-    const size_t x = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (x >= (size_t)K * 2 * N) return;
-    const int k = (int)(x / (2 * N)), n = (int)(x % (2 * N));
-    const uint16_t *src = (n & 63) < 32 ? w : w2;
-    out[x] = src[(size_t)k * N + (n >> 6) * 32 + (n & 31)];
-}
-
-// u_h = W_k[:, 64h .. 64h + 63] q_h / 8, one thread per (h, i)
-__global__ __launch_bounds__(256) void k_pool_u(const uint16_t *wk, const uint16_t *query, float *u, int D, int H) {
-    const int x = blockIdx.x * 256 + threadIdx.x;
-    if (x >= H * D) return;
-    const int h = x / D, i = x % D;
-    float s = 0.f;
-    for (int e = 0; e < 64; ++e) s += bf16_to_f32(wk[(size_t)i * D + 64 * h + e]) * bf16_to_f32(query[64 * h + e]);
-    u[x] = s * 0.125f;
 }
 
 }  // namespace
@@ -888,49 +958,57 @@ hipError_t launch_pool_bwd(const PoolBwdArgs &a, float *dz, float *pd, hipStream
 
 namespace ube {
 
-hipError_t launch_adafactor(const AdafactorArgs &a, hipStream_t stream) {
-    const size_t n = (size_t)a.rows * (a.cols ? a.cols : 1);
-    if (!n) return hipSuccess;
-    hipError_t e;
-    if (a.cols == 0) {
-        k_ada_rows<<<(a.rows + 255) / 256, 256, 0, stream>>>(a);
-    } else {
-        k_ada_rows<<<(a.rows + 3) / 4, 256, 0, stream>>>(a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        const int slices = (a.rows + kColSlice - 1) / kColSlice;
-        if ((size_t)slices * a.cols > kAdafactorColParts) return hipErrorInvalidValue;
-        k_col_parts<<<dim3((a.cols + 255) / 256, slices), 256, 0, stream>>>(a.g, a.rows, a.cols, a.work + kAdafactorWork,
-                                                                           1, a.eps1);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_ada_cols<<<(a.cols + 255) / 256, 256, 0, stream>>>(a, a.work + kAdafactorWork, slices);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_ada_mean<<<1, 256, 0, stream>>>(a);
+int adafactor_grids(AdaTensor *tab, int n, int *stats, int *cols, int *upd) {
+    int g0 = 0, g1 = 0, g2 = 0;
+    for (int i = 0; i < n; ++i) {
+        AdaTensor &t = tab[i];
+        const long long count = (long long)t.rows * (t.cols ? t.cols : 1);
+        if (count <= 0 || count > 0x7fffffffLL) return -1;
+        t.wg_stats = g0, t.wg_cols = g1, t.wg_upd = g2;
+        g0 += t.cols ? (t.rows + kAdaSlice - 1) / kAdaSlice : (t.rows + 255) / 256;
+        g1 += t.cols ? (t.cols + 255) / 256 : 0;
+        g2 += (int)((count + kAdaChunk - 1) / kAdaChunk);
     }
+    *stats = g0, *cols = g1, *upd = g2;
+    return 0;
+}
+
+hipError_t launch_adafactor(const AdaTensor *tab, int n, int stats, int cols, int upd, const AdaStep &st,
+                            hipStream_t stream) {
+    if (n <= 0) return hipSuccess;
+    k_ada_stats<<<stats, 256, 0, stream>>>(tab, n, st);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (cols > 0) {
+        k_ada_cols<<<cols, 256, 0, stream>>>(tab, n, st);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    k_ada_rms<<<upd, 256, 0, stream>>>(tab, n, st);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    k_ada_rms_parts<<<kAdaParts, 256, 0, stream>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    k_ada_clip<<<1, 64, 0, stream>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    k_ada_update<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a);
+    k_ada_apply<<<upd, 256, 0, stream>>>(tab, n, st);
     return hipGetLastError();
 }
 
-hipError_t launch_pack_transpose(const uint16_t *w, const uint16_t *w2, const float *gain, uint16_t *out, int K, int N,
-                                 bool interleave, hipStream_t stream) {
-    const int NO = interleave ? 2 * N : N;
-    k_pack_transpose<<<dim3((NO + 63) / 64, (K + 63) / 64), 256, 0, stream>>>(w, w2, gain, out, K, N, interleave ? 1 : 0);
-    return hipGetLastError();
+int pack_workgroups(PackJob *jobs, int n) {
+    int g = 0;
+    for (int i = 0; i < n; ++i) {
+        PackJob &j = jobs[i];
+        j.first_wg = g;
+        const size_t K = (size_t)j.K, N = (size_t)j.N;
+        switch (j.kind) {
+            case kPackTranspose: g += (int)(((N + 63) / 64) * ((K + 63) / 64)); break;
+            case kPackTransposePair: g += (int)(((2 * N + 63) / 64) * ((K + 63) / 64)); break;
+            case kPackColumnPair: g += (int)((K * 2 * N + 4095) / 4096); break;
+            case kPackCopy: g += (int)((K * N + 4095) / 4096); break;
+            default: g += (int)((K * N + 255) / 256); break;
+        }
+    }
+    return g;
 }
 
-hipError_t launch_pool_u(const uint16_t *wk, const uint16_t *query, float *u, int D, int H, hipStream_t stream) {
-    k_pool_u<<<(H * D + 255) / 256, 256, 0, stream>>>(wk, query, u, D, H);
-    return hipGetLastError();
-}
-
-hipError_t launch_interleave_cols(const uint16_t *w, const uint16_t *w2, uint16_t *out, int K, int N,
-                                  hipStream_t stream) {
-    const size_t n = (size_t)K * 2 * N;
-    k_interleave_cols<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(w, w2, out, K, N);
+hipError_t launch_pack(const PackJob *jobs, int n, int workgroups, hipStream_t stream) {
+    if (n <= 0 || workgroups <= 0) return hipSuccess;
+    k_pack<<<workgroups, 256, 0, stream>>>(jobs, n);
     return hipGetLastError();
 }
 
