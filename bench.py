@@ -284,7 +284,7 @@ def bench_train(args):
     weights = synth.make_weights(g)
     batch = synth.workload_inputs("train")
     model, arena, arena2 = ube.Model(weights, 0), ube.Arena(0), ube.Arena(0)
-    trainer = ube.Trainer(model, weights)
+    trainer = ube.Trainer(model, weights, activation_recomputation=args.recompute)
     data = torch.from_numpy(batch.data).to("cuda:0")
     stream = torch.cuda.current_stream()
     n = batch.count
@@ -346,7 +346,8 @@ def bench_train(args):
         "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded bytes, random-init bf16 weights N(0, 0.02))",
-        "config": {"workload": f"train: {WORKLOAD_TEXT['train']}", "items": n, "tokens": T, "parallelism": "1 GPU"},
+        "config": {"workload": f"train: {WORKLOAD_TEXT['train']}", "items": n, "tokens": T, "parallelism": "1 GPU",
+                   "activation_recomputation": bool(args.recompute)},
         "mfma_util": flops / (ms / 1e3) / PEAK_BF16, "flops_per_step": flops, "roofline": roof,
     }
     if per_kernel:
@@ -385,6 +386,8 @@ def main():
                     help="first copy MIB MiB device-to-device 3 times (a plain copy kernel of known size, "
                          "for calibrating HBM byte counters)")
     ap.add_argument("--per-kernel", action="store_true", help="also time every kernel kind (extra passes)")
+    ap.add_argument("--recompute", action="store_true",
+                    help="train: keep only each block's fp32 input and replay the block in the backward")
     args = ap.parse_args()
 
     if args.gpus != 1:

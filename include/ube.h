@@ -402,7 +402,11 @@ void ube_contrastive(ube_contrastive_t *arguments);
  * their fp32 gradients and the Adafactor state, and refreshes the model's forward weights after every
  * step (so encodes on the model see the updated weights). Text models in bf16 with 1-axis rotary and
  * hidden <= 1024 (unsupported otherwise). Adafactor: beta1 [0.9], decay_rate [-0.8] (beta2_t = 1 -
- * t^decay_rate), epsilon1 [1e-30], clip_threshold [1]; zero fields take the defaults in brackets. */
+ * t^decay_rate), epsilon1 [1e-30], clip_threshold [1]; zero fields take the defaults in brackets; the
+ * update reads each fp32 gradient cast to bf16 (nearest even). With activation_recomputation the
+ * training forward keeps only every block's fp32 input and the backward replays each block's attention
+ * half from it (the pages' memory plan: 4 * hidden bytes per token and block); without it the forward
+ * keeps what the backward reads (about 16 * hidden bytes per token and block, no replay). */
 typedef struct ube_trainer_handle_t *ube_trainer_t;
 
 typedef struct ube_trainer_init_t {
@@ -411,13 +415,14 @@ typedef struct ube_trainer_init_t {
     ube_model_t model;               /* borrowed until the trainer is freed */
     ube_weights_t const *weights;    /* the model's weights in host memory (copied) */
     float beta1, decay_rate, epsilon1, clip_threshold;
+    int activation_recomputation;    /* nonzero: keep only each block's fp32 input ("Precision by Design") */
 } ube_trainer_init_t;
 void ube_trainer_init(ube_trainer_init_t *arguments);
 
 /* Training forward over a byte tape: the model's forward, with the activations its backward reads kept in
- * the trainer's device memory (per block: the fp32 input and the fp32 rows after the attention half, the
- * rotated q|k rows, v, the attention output and its softmax denominators; about 16 * hidden bytes per
- * token and block). *embeddings receives the pooled fp32 rows [count x hidden] in the arena, valid until
+ * the trainer's device memory (per block: the fp32 input; without recomputation also the fp32 rows after
+ * the attention half, the rotated q|k rows, v, the attention output and its softmax denominators).
+ * *embeddings receives the pooled fp32 rows [count x hidden] in the arena, valid until
  * the arena's next call. The kept activations serve the next ube_trainer_backward with after_forward set,
  * until a step changes the weights. */
 typedef struct ube_trainer_forward_t {
@@ -432,8 +437,9 @@ typedef struct ube_trainer_forward_t {
 } ube_trainer_forward_t;
 void ube_trainer_forward(ube_trainer_forward_t *arguments);
 
-/* Backward pass: walks the blocks from last to first over the kept activations, rebuilding only each
- * block's two RMSNorm outputs, v's rows and the gate/up pre-activations from them. after_forward != 0:
+/* Backward pass: walks the blocks from last to first over the kept activations (replaying each block's
+ * attention half first under recomputation), rebuilding each block's two RMSNorm outputs, v's rows and
+ * the gate/up pre-activations. after_forward != 0:
  * differentiates the rows of the last ube_trainer_forward (arena, texts and stats unused; an error if a
  * step came in between); after_forward == 0: runs that forward over `texts` on `arena` first.
  * d_embeddings: device fp32 rows [count x hidden] (packed; stride 0 or hidden * 4 bytes), d loss / d

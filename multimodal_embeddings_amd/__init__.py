@@ -130,7 +130,7 @@ class ube_contrastive_t(C.Structure):
 class ube_trainer_init_t(C.Structure):
     _fields_ = [("trainer", C.POINTER(VP)), ("outcome", C.POINTER(ube_outcome_t)), ("model", VP),
                 ("weights", C.POINTER(ube_weights_t)), ("beta1", C.c_float), ("decay_rate", C.c_float),
-                ("epsilon1", C.c_float), ("clip_threshold", C.c_float)]
+                ("epsilon1", C.c_float), ("clip_threshold", C.c_float), ("activation_recomputation", C.c_int)]
 
 
 class ube_trainer_forward_t(C.Structure):
@@ -503,12 +503,13 @@ class _DeviceArray:
 class Trainer:
     """Training state of a text model on its GPU: bf16 masters (fp32 gains), fp32 gradients, Adafactor."""
 
-    def __init__(self, model: Model, weights, *, beta1=0.0, decay_rate=0.0, epsilon1=0.0, clip_threshold=0.0):
+    def __init__(self, model: Model, weights, *, beta1=0.0, decay_rate=0.0, epsilon1=0.0, clip_threshold=0.0,
+                 activation_recomputation=False):
         w, keep = _weights_struct(weights, model.geometry)
         handle = VP()
         outcome = ube_outcome_t()
         args = ube_trainer_init_t(C.pointer(handle), C.pointer(outcome), model.handle, C.pointer(w), beta1,
-                                  decay_rate, epsilon1, clip_threshold)
+                                  decay_rate, epsilon1, clip_threshold, 1 if activation_recomputation else 0)
         lib().ube_trainer_init(C.byref(args))
         _check(outcome)
         del keep

@@ -569,13 +569,13 @@ struct ArenaLease {
 };
 
 // Where a training forward leaves the activations its backward reads (device memory outside the arena):
-// every block's fp32 input (and the final norm's, at block N), the fp32 rows after each block's attention
-// half, each block's rotated q|k rows, feature-major v, attention output and softmax log2 denominators,
-// and the final-norm rows and pool scores.
+// every block's fp32 input (and the final norm's, at block N) and the final-norm rows and pool scores;
+// unless the backward recomputes them (x1 and qk NULL), also the fp32 rows after each block's attention
+// half and each block's rotated q|k rows, feature-major v, attention output and softmax log2 denominators.
 struct Keep {
     float *x;         // [(N + 1) x T x D]
-    float *x1;        // [N x T x D]
-    uint16_t *qk;     // [N][Tpad x 2D]
+    float *x1;        // [N x T x D] or NULL
+    uint16_t *qk;     // [N][Tpad x 2D] or NULL (then vt, o, lse unused)
     uint16_t *vt;     // [N][D x ldvt]
     uint16_t *o;      // [N][Tpad x D]
     float *lse;       // [N][H x ldl]
@@ -752,8 +752,8 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
             uint16_t *qk_l = qk, *vt_l = vt, *o_l = o;
             int ldvt_l = ldvt;
             float *lse_l = nullptr;
-            if (kp) {
-                UBE_HIP(hipMemcpyAsync(kp->x + l * TD, x, TD * 4, hipMemcpyDeviceToDevice, st));
+            if (kp) UBE_HIP(hipMemcpyAsync(kp->x + l * TD, x, TD * 4, hipMemcpyDeviceToDevice, st));
+            if (kp && kp->qk) {
                 qk_l = kp->qk + l * kp->Tpad * 2 * D, vt_l = kp->vt + l * D * kp->ldvt, o_l = kp->o + l * kp->Tpad * D;
                 ldvt_l = (int)kp->ldvt, lse_l = kp->lse + l * H * kp->ldl;
                 UBE_HIP(hipMemset2DAsync(vt_l + T, kp->ldvt * 2, 0, 64 * 2, (size_t)D, st));
@@ -767,14 +767,14 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
             project(ube_kernel_gemm_qkv_k, kEpiQkv, qa, Wl.s_qkv, 0.f);
             timed(ube_kernel_attention_k, st, [&] {
                 return launch_attention(qk_l, qk_l + D, 2 * D, vt_l, ldvt_l, o_l, D, cu, tiles, ntiles, H, st, lse_l,
-                                        kp ? (int)kp->ldl : 0);
+                                        lse_l ? (int)kp->ldl : 0);
             });
             if (m->e4m3) quantize(o_l, D);
             GemmArgs oa{};
             oa.w = Wl.wo, oa.x = o_l, oa.M = T, oa.N = D, oa.K = D, oa.out_f32 = x, oa.ld_f32 = D;
             residual_out(oa);
             project(ube_kernel_gemm_out_k, kEpiResid, oa, Wl.s_o, 0.f);
-            if (kp) UBE_HIP(hipMemcpyAsync(kp->x1 + l * TD, x, TD * 4, hipMemcpyDeviceToDevice, st));
+            if (kp && kp->x1) UBE_HIP(hipMemcpyAsync(kp->x1 + l * TD, x, TD * 4, hipMemcpyDeviceToDevice, st));
             if (m->e4m3) norm(Wl.g2);
             GemmArgs ua{};
             ua.w = Wl.wgu, ua.x = h, ua.M = T, ua.N = 2 * F, ua.K = D, ua.out_bf16 = act, ua.ld_out = F;
@@ -1337,7 +1337,7 @@ struct ube_trainer_handle_t {
     std::vector<Tensor> tensors;
     struct Block {  // indices into tensors, and packings derived from the masters
         size_t qkv, o, gate, up, down, g1, g2;
-        uint16_t *guT, *gu_cols;
+        uint16_t *guT, *gu_cols, *qkvT;  // qkvT: recomputation only
     };
     std::vector<Block> blocks;
     size_t t_embed = 0, t_gf = 0, t_query = 0, t_wk = 0, t_wv = 0;
@@ -1346,6 +1346,9 @@ struct ube_trainer_handle_t {
     int ada_stats = 0, ada_cols = 0, ada_upd = 0;
     ube::PackJob *pack_table = nullptr;
     int pack_jobs = 0, pack_wgs = 0;
+    // activation recomputation: the forward keeps only each block's fp32 input and the backward replays
+    // the block from it (else the forward keeps every activation the backward reads)
+    bool recompute = false;
     // the last training forward, whose activations the workspace holds until a step changes the weights
     bool fw_valid = false;
     size_t fw_T = 0, fw_count = 0, fw_ntiles = 0;
@@ -1357,7 +1360,7 @@ struct ube_trainer_handle_t {
 
 namespace {
 
-TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count, size_t ntiles) {
+TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count, size_t ntiles, bool recompute) {
     TrainLayout L{};
     const size_t D = g.hidden, F = g.ffn, H = g.heads, N = g.depth;
     L.Tpad = align_up(T, 256) + kRowPad;
@@ -1368,13 +1371,14 @@ TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count, size_t 
         total = align_up(total + bytes, 256);
         return o;
     };
-    // kept by the forward
+    // kept by the forward (recomputation: one block's set, refilled by each block's replay)
+    const size_t NB = recompute ? 1 : N;
     L.kx = take((N + 1) * T1 * D * 4);
-    L.kx1 = take(N * T1 * D * 4);
-    L.kqk = take(N * Tp * 2 * D * 2);
-    L.kvt = take(N * D * Tp * 2);
-    L.ko = take(N * Tp * D * 2);
-    L.klse = take(N * H * Tp * 4);
+    L.kx1 = take(NB * T1 * D * 4);
+    L.kqk = take(NB * Tp * 2 * D * 2);
+    L.kvt = take(NB * D * Tp * 2);
+    L.ko = take(NB * Tp * D * 2);
+    L.klse = take(NB * H * Tp * 4);
     L.kxf = take(Tp * D * 2);
     L.ks = take(Tp * H * 4);
     L.kcu = take((count + 1) * 4);
@@ -1460,6 +1464,7 @@ extern "C" void ube_trainer_init(ube_trainer_init_t *a) {
         if (a->decay_rate < 0.f) tr->decay = a->decay_rate;
         if (a->epsilon1 > 0.f) tr->eps1 = a->epsilon1;
         if (a->clip_threshold > 0.f) tr->clip = a->clip_threshold;
+        tr->recompute = a->activation_recomputation != 0;
         // tensors in a fixed order: embed, blocks, final gain, pool query, W_k, W_v
         auto add = [&](char const *name, size_t layer, size_t rows, size_t cols) {
             tr->tensors.push_back(ube_trainer_handle_t::Tensor{name, layer, rows, cols});
@@ -1507,9 +1512,10 @@ extern "C" void ube_trainer_init(ube_trainer_init_t *a) {
             aoffs[i] = {take(t.cols ? (t.rows + kAdaSlice - 1) / kAdaSlice * t.cols * 4 : 0),
                         take((n + kAdaChunk - 1) / kAdaChunk * 4), take(4)};
         }
-        std::vector<std::array<size_t, 2>> boffs(N);
-        for (size_t l = 0; l < N; ++l) boffs[l] = {take(2 * F * D * 2), take(2 * F * D * 2)};
-        const size_t n_jobs = 8 * N + 4;
+        std::vector<std::array<size_t, 3>> boffs(N);
+        for (size_t l = 0; l < N; ++l)
+            boffs[l] = {take(2 * F * D * 2), take(2 * F * D * 2), take(tr->recompute ? 3 * D * D * 2 : 0)};
+        const size_t n_jobs = 9 * N + 4;
         const size_t o_ada = take(tr->tensors.size() * sizeof(AdaTensor));
         const size_t o_pack = take(n_jobs * sizeof(PackJob));
         UBE_HIP(hipMalloc((void **)&tr->mem, total));
@@ -1531,6 +1537,7 @@ extern "C" void ube_trainer_init(ube_trainer_init_t *a) {
             auto &b = tr->blocks[l];
             b.guT = (uint16_t *)(db + boffs[l][0]);
             b.gu_cols = (uint16_t *)(db + boffs[l][1]);
+            b.qkvT = tr->recompute ? (uint16_t *)(db + boffs[l][2]) : nullptr;
         }
         // the multi-tensor update's table
         std::vector<AdaTensor> ada(tr->tensors.size());
@@ -1565,6 +1572,7 @@ extern "C" void ube_trainer_init(ube_trainer_init_t *a) {
                 job(T[b.down].w16, nullptr, nullptr, ml.wd, Fi, Di, kPackTranspose);
                 job(T[b.g1].w32, nullptr, nullptr, ml.g1, 1, Di, kPackCopy);
                 job(T[b.g2].w32, nullptr, nullptr, ml.g2, 1, Di, kPackCopy);
+                if (b.qkvT) job(T[b.qkv].w16, nullptr, nullptr, b.qkvT, Di, 3 * Di, kPackTranspose);
             }
             job(T[tr->t_embed].w16, nullptr, nullptr, m->embed, 1, (int)(V * D / 2), kPackCopy);
             job(T[tr->t_gf].w32, nullptr, nullptr, m->gf, 1, Di, kPackCopy);
@@ -1673,7 +1681,7 @@ void train_forward(ube_trainer_t tr, ube_arena_t arena, hipStream_t st, ube_tape
             for (int t = p.cu[i]; t < p.cu[i + 1]; ++t)
                 tok[fill[bytes[p.src[i] - p.input_lo + (t - p.cu[i])]]++] = (uint32_t)t;
     }
-    TrainLayout L = train_carve(g, T, count, p.tiles.size());
+    TrainLayout L = train_carve(g, T, count, p.tiles.size(), tr->recompute);
     if (L.total > tr->ws_cap) {
         UBE_HIP(hipStreamSynchronize(st));
         if (tr->ws) UBE_HIP(hipFree(tr->ws));
@@ -1688,9 +1696,12 @@ void train_forward(ube_trainer_t tr, ube_arena_t arena, hipStream_t st, ube_tape
     UBE_HIP(hipMemcpyAsync(wb + L.tok_off, tok_off.data(), (V + 1) * 4, hipMemcpyHostToDevice, st));
     UBE_HIP(hipMemcpyAsync(wb + L.tok, tok.data(), tok.size() * 4, hipMemcpyHostToDevice, st));
     Keep k{};
-    k.x = (float *)(wb + L.kx), k.x1 = (float *)(wb + L.kx1);
-    k.qk = (uint16_t *)(wb + L.kqk), k.vt = (uint16_t *)(wb + L.kvt), k.o = (uint16_t *)(wb + L.ko);
-    k.lse = (float *)(wb + L.klse), k.xf = (uint16_t *)(wb + L.kxf), k.s = (float *)(wb + L.ks);
+    k.x = (float *)(wb + L.kx), k.xf = (uint16_t *)(wb + L.kxf), k.s = (float *)(wb + L.ks);
+    if (!tr->recompute) {
+        k.x1 = (float *)(wb + L.kx1);
+        k.qk = (uint16_t *)(wb + L.kqk), k.vt = (uint16_t *)(wb + L.kvt), k.o = (uint16_t *)(wb + L.ko);
+        k.lse = (float *)(wb + L.klse);
+    }
     k.Tpad = L.Tpad, k.ldvt = L.Tpad, k.ldl = L.Tpad;
     Layout EL{};
     EncodeRequest r{m, arena, st, 1, ube_scalar_f32_k, rows, stats, nullptr, texts.data, texts.offsets, count, 0,
@@ -1753,13 +1764,27 @@ void train_backward(ube_trainer_t tr, hipStream_t st, float const *d_embeddings)
     // ---- blocks, last to first
     for (size_t li = N; li-- > 0;) {
         auto const &b = tr->blocks[li];
-        const float *x_in = F32(L.kx) + li * TD, *x1 = F32(L.kx1) + li * TD;
-        const uint16_t *qk = B16(L.kqk) + li * Tp * 2 * D, *vt = B16(L.kvt) + li * D * Tp, *o = B16(L.ko) + li * Tp * D;
-        const float *lse = F32(L.klse) + li * H * Tp;
+        const size_t kb = tr->recompute ? 0 : li;  // which kept set holds this block's activations
+        const float *x_in = F32(L.kx) + li * TD;
+        float *x1 = F32(L.kx1) + kb * TD;
+        uint16_t *qk = B16(L.kqk) + kb * Tp * 2 * D, *vt = B16(L.kvt) + kb * D * Tp, *o = B16(L.ko) + kb * Tp * D;
+        float *lse = F32(L.klse) + kb * H * Tp;
         uint16_t *h1 = B16(L.h1), *v = B16(L.v), *h2 = B16(L.h2), *gu = B16(L.gu);
         float *delta = F32(L.delta);
-        // the block's inputs that were not kept
         UBE_HIP(launch_rmsnorm(x_in, TT[b.g1].w32, h1, Ti, Di, eps, st));
+        if (tr->recompute) {
+            // replay the block's attention half from its fp32 input
+            UBE_HIP(hipMemset2DAsync(vt + T, (size_t)ldvt * 2, 0, 64 * 2, D, st));
+            GemmArgs qa{};
+            qa.w = b.qkvT, qa.x = h1, qa.M = Ti, qa.N = 3 * Di, qa.K = Di;
+            qa.out_bf16 = qk, qa.ld_out = 2 * Di, qa.vt = vt, qa.ld_vt = ldvt, qa.pos = pos, qa.rope = m->rope;
+            qa.D = Di, qa.sec0 = m->sec0, qa.sec1 = m->sec1;
+            UBE_HIP(launch_gemm(kEpiQkv, qa, st));
+            UBE_HIP(launch_attention(qk, qk + D, 2 * Di, vt, ldvt, o, Di, cu, tiles, ntiles, Hi, st, lse, ldl));
+            UBE_HIP(hipMemcpyAsync(x1, x_in, TD * 4, hipMemcpyDeviceToDevice, st));
+            gemm(kEpiResid, m->layers[li].wo, o, Ti, Di, Di, nullptr, 0, x1, Di, st);
+        }
+        // the block's inputs that were not kept
         UBE_HIP(launch_vt_rows(vt, ldvt, v, Ti, Di, st));
         UBE_HIP(launch_rmsnorm(x1, TT[b.g2].w32, h2, Ti, Di, eps, st));
         gemm(kEpiStore, b.guT, h2, Ti, 2 * Fi, Di, gu, 2 * Fi, nullptr, 0, st);

@@ -644,7 +644,7 @@ __global__ __launch_bounds__(256) void k_pool_bwd_weights(PoolBwdArgs a, const f
 
 // ------------------------------------------------------------------------------------------ Adafactor
 //
-// Shazeer and Stern's update with the first moment the pages add: for a matrix, row and column means of
+// Shazeer and Stern's update with the first moment the pages add, over the gradient cast to bf16: for a matrix, row and column means of
 // g^2 + eps1 decayed by beta2 (r, c), v = r c^T / mean(r); for a vector, v decayed elementwise;
 // u = g / sqrt(v), clipped to RMS(u) <= clip; m = beta1 m + (1 - beta1) u; w -= lr m / (1 - beta1^t).
 // Every tensor of the model in the same four launches (statistics, column means, sums of u^2, update);
@@ -677,6 +677,11 @@ __device__ __forceinline__ float block_sum256(float v, float *red) {
     return ((red[0] + red[1]) + red[2]) + red[3];
 }
 
+// the optimizer reads each fp32 gradient cast to bf16 (round to nearest even)
+__device__ __forceinline__ float ada_grad(const AdaTensor &a, size_t idx) {
+    return bf16_to_f32(f32_to_bf16(a.g[idx]));
+}
+
 // matrices: one workgroup per slice of kAdaSlice rows (column partials of the slice, then the decayed
 // row means); vectors: 256 elements of v per workgroup
 __global__ __launch_bounds__(256) void k_ada_stats(const AdaTensor *tab, int n, AdaStep st) {
@@ -685,14 +690,17 @@ __global__ __launch_bounds__(256) void k_ada_stats(const AdaTensor *tab, int n, 
     const int local = blockIdx.x - a.wg_stats, tid = threadIdx.x;
     if (a.cols == 0) {
         const int i = local * 256 + tid;
-        if (i < a.rows) a.v[i] = st.beta2 * a.v[i] + (1.f - st.beta2) * (a.g[i] * a.g[i] + st.eps1);
+        if (i < a.rows) {
+            const float g = ada_grad(a, i);
+            a.v[i] = st.beta2 * a.v[i] + (1.f - st.beta2) * (g * g + st.eps1);
+        }
         return;
     }
     const int r0 = local * kAdaSlice, r1 = min(a.rows, r0 + kAdaSlice);
     for (int j = tid; j < a.cols; j += 256) {
         float sum = 0.f;
         for (int i = r0; i < r1; ++i) {
-            const float g = a.g[(size_t)i * a.cols + j];
+            const float g = ada_grad(a, (size_t)i * a.cols + j);
             sum += g * g + st.eps1;
         }
         a.col_parts[(size_t)local * a.cols + j] = sum;
@@ -703,7 +711,7 @@ __global__ __launch_bounds__(256) void k_ada_stats(const AdaTensor *tab, int n, 
         if (row >= r1) break;
         float sum = 0.f;
         for (int j = lane; j < a.cols; j += 64) {
-            const float g = a.g[(size_t)row * a.cols + j];
+            const float g = ada_grad(a, (size_t)row * a.cols + j);
             sum += g * g + st.eps1;
         }
         sum = wave_sum(sum);
@@ -733,7 +741,7 @@ __global__ __launch_bounds__(256) void k_ada_cols(const AdaTensor *tab, int n, A
 }
 
 __device__ __forceinline__ float ada_u(const AdaTensor &a, int idx, float mean_r) {
-    const float g = a.g[idx];
+    const float g = ada_grad(a, idx);
     if (a.cols == 0) return g * rsqrtf(a.v[idx]);
     const int i = idx / a.cols, j = idx - i * a.cols;
     return g * rsqrtf(a.r[i] * a.c[j] / mean_r);

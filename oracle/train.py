@@ -11,8 +11,8 @@ TEST INFRASTRUCTURE ONLY: imported by the tests, ``__graft_entry__.smoke`` and t
 * ``text_backward``: gradients of <pooled, d_pooled> with respect to every parameter by torch autograd
   over that float64 forward (a library primitive standing for the chain rule; pinned by finite
   differences).
-* ``adafactor``: one Adafactor update ("UForm" page, "Adafactor Optimizer" and "Precision by Design"):
-  factored second moment (row and column means of g^2 + eps1, decayed by beta2_t = 1 - t^decay) for
+* ``adafactor``: one Adafactor update ("UForm" page, "Adafactor Optimizer" and "Precision by Design")
+  of the gradient cast to bf16: factored second moment (row and column means of g^2 + eps1, decayed by beta2_t = 1 - t^decay) for
   matrices, an unfactored one for vectors; update u = g / sqrt(v) clipped to RMS <= d; first moment of
   the clipped update with Adam's bias correction; w -= lr * m_hat. Written from Shazeer and Stern's
   published algorithm (Adafactor, 2018), with the first moment the pages add.
@@ -138,11 +138,18 @@ class AdafactorState:
         self.m = np.zeros(shape)
 
 
-def adafactor(w, g, state, lr, step, beta1=0.9, decay=-0.8, eps1=1e-30, clip=1.0):
+def bf16_round(a):
+    """Float32 values rounded to bfloat16 (nearest even) by the library cast, back in float64."""
+    t = torch.as_tensor(np.asarray(a, dtype=np.float32))
+    return t.to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def adafactor(w, g, state, lr, step, beta1=0.9, decay=-0.8, eps1=1e-30, clip=1.0, grad_bf16=True):
     """One update of tensor w (float64 values) with gradient g at step `step` (counted from 1); returns
-    the new values and updates `state` in place."""
+    the new values and updates `state` in place. With ``grad_bf16`` the float32 gradient is cast to bf16
+    first ("Precision by Design": gradients accumulate in float32 and are cast to BF16 for the step)."""
     w = np.asarray(w, dtype=np.float64)
-    g = np.asarray(g, dtype=np.float64)
+    g = bf16_round(g) if grad_bf16 else np.asarray(g, dtype=np.float64)
     beta2 = 1.0 - step ** decay
     sq = g * g + eps1
     if g.ndim == 2:

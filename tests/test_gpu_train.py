@@ -26,12 +26,12 @@ def ube():
     return m
 
 
-def _setup(ube, name="tiny", count=None, seed=1):
+def _setup(ube, name="tiny", count=None, seed=1, recompute=False):
     g = configs.geometry(name)
     w = synth.make_weights(g, gain_jitter=0.2)
     batch = synth.workload_inputs(name) if count is None else synth.text_batch(count, 16, 200, 0, 256, seed=seed)
     model = ube.Model(w, 0)
-    trainer = ube.Trainer(model, w)
+    trainer = ube.Trainer(model, w, activation_recomputation=recompute)
     arena = ube.Arena(0)
     return g, w, batch, model, trainer, arena
 
@@ -58,9 +58,9 @@ def _compare_grads(label, got, want_grads, depth):
     return worst
 
 
-@pytest.mark.parametrize("name,count", [("tiny", None), ("tiny", 5)])
-def test_backward_matches_oracle(ube, name, count):
-    g, w, batch, model, trainer, arena = _setup(ube, name, count)
+@pytest.mark.parametrize("name,count,recompute", [("tiny", None, False), ("tiny", 5, False), ("tiny", None, True)])
+def test_backward_matches_oracle(ube, name, count, recompute):
+    g, w, batch, model, trainer, arena = _setup(ube, name, count, recompute=recompute)
     rng = np.random.default_rng(7)
     d_pooled = rng.standard_normal((batch.count, g["hidden"])).astype(np.float32)
     say(f"[{name}] items {batch.count}, bytes {int(batch.offsets[-1])}")
@@ -151,14 +151,16 @@ def test_forward_then_backward(ube):
         trainer.backward(None, None, None, d, after_forward=True)
 
 
-def test_depth12_backward_matches_oracle(ube):
-    """The depth-12, hidden-512 encoder on a few ragged rows (cosine and max-difference bars as above)."""
+@pytest.mark.parametrize("recompute", [False, True])
+def test_depth12_backward_matches_oracle(ube, recompute):
+    """The depth-12, hidden-512 encoder on a few ragged rows (cosine and max-difference bars as above), with
+    every activation kept and with each block's attention half replayed from its fp32 input."""
     import torch
     g = configs.geometry("text512")
     w = synth.make_weights(g, gain_jitter=0.2)
     batch = synth.text_batch(4, 100, 400, 0, 256, seed=3)
     model, arena = ube.Model(w, 0), ube.Arena(0)
-    trainer = ube.Trainer(model, w)
+    trainer = ube.Trainer(model, w, activation_recomputation=recompute)
     rng = np.random.default_rng(9)
     d_pooled = rng.standard_normal((batch.count, g["hidden"])).astype(np.float32)
     trainer.backward(arena, device_bytes(batch.data), batch.offsets, device_bytes(d_pooled))

@@ -77,13 +77,13 @@ def test_adafactor_first_step_is_sign_descent():
     # vector: v = g^2, u = sign(g), no clipping at RMS 1, bias-corrected first moment = u
     w, g = rng.standard_normal(7), rng.standard_normal(7)
     st = TR.AdafactorState(w.shape)
-    assert np.allclose(TR.adafactor(w, g, st, 0.01, 1), w - 0.01 * np.sign(g), rtol=0, atol=1e-15)
+    assert np.allclose(TR.adafactor(w, g, st, 0.01, 1, grad_bf16=False), w - 0.01 * np.sign(g), rtol=0, atol=1e-15)
     # matrix with rank-one g^2: the factored second moment is exact
     a, b = rng.standard_normal(5), rng.standard_normal(4)
     G = np.outer(a, b)
     W = rng.standard_normal((5, 4))
     st = TR.AdafactorState(W.shape)
-    assert np.allclose(TR.adafactor(W, G, st, 0.02, 1), W - 0.02 * np.sign(G), rtol=0, atol=1e-12)
+    assert np.allclose(TR.adafactor(W, G, st, 0.02, 1, grad_bf16=False), W - 0.02 * np.sign(G), rtol=0, atol=1e-12)
     assert np.allclose(st.r, (G * G).mean(1) + 1e-30) and np.allclose(st.c, (G * G).mean(0) + 1e-30)
 
 
@@ -91,9 +91,9 @@ def test_adafactor_second_step_clipping_and_bias_correction():
     n = 6
     w = np.zeros(n)
     st = TR.AdafactorState((n,))
-    w1 = TR.adafactor(w, np.full(n, 1e-10), st, 0.5, 1)
+    w1 = TR.adafactor(w, np.full(n, 1e-10), st, 0.5, 1, grad_bf16=False)
     assert np.allclose(w1, -0.5)
-    w2 = TR.adafactor(w1, np.ones(n), st, 0.5, 2)
+    w2 = TR.adafactor(w1, np.ones(n), st, 0.5, 2, grad_bf16=False)
     beta2 = 1 - 2 ** -0.8
     u = 1 / math.sqrt(beta2 * (1e-20 + 1e-30) + (1 - beta2) * (1 + 1e-30))
     assert u > 1.3  # clipped back to RMS 1
@@ -105,6 +105,25 @@ def test_adafactor_is_gradient_scale_free():
     rng = np.random.default_rng(2)
     W, G1, G2 = rng.standard_normal((6, 3)), rng.standard_normal((6, 3)), rng.standard_normal((6, 3))
     s1, s2 = TR.AdafactorState(W.shape), TR.AdafactorState(W.shape)
-    a = TR.adafactor(TR.adafactor(W, G1, s1, 0.1, 1), G2, s1, 0.1, 2)
-    b = TR.adafactor(TR.adafactor(W, 1e3 * G1, s2, 0.1, 1), 1e3 * G2, s2, 0.1, 2)
+    a = TR.adafactor(TR.adafactor(W, G1, s1, 0.1, 1, grad_bf16=False), G2, s1, 0.1, 2, grad_bf16=False)
+    b = TR.adafactor(TR.adafactor(W, 1e3 * G1, s2, 0.1, 1, grad_bf16=False), 1e3 * G2, s2, 0.1, 2, grad_bf16=False)
     assert np.allclose(a, b, rtol=1e-9)
+
+
+def test_adafactor_reads_the_gradient_at_bf16_precision():
+    rng = np.random.default_rng(3)
+    W = rng.standard_normal((5, 7))
+    G = TR.bf16_round(rng.standard_normal((5, 7)))  # bf16 values
+    a = TR.adafactor(W, G, TR.AdafactorState(W.shape), 0.05, 1)
+    # a relative change of 2^-10 is below half a bf16 step: the cast takes it back to G
+    b = TR.adafactor(W, G * (1 + 2.0 ** -10), TR.AdafactorState(W.shape), 0.05, 1)
+    assert np.array_equal(a, b)
+    # one of 2^-7 is a whole step: the update changes, and equals the update of the rounded gradient
+    G2 = G * (1 + 2.0 ** -7)
+    c = TR.adafactor(W, G2, TR.AdafactorState(W.shape), 0.05, 1)
+    assert not np.array_equal(a, c)
+    d = TR.adafactor(W, TR.bf16_round(G2), TR.AdafactorState(W.shape), 0.05, 1, grad_bf16=False)
+    assert np.array_equal(c, d)
+    # the cast is the nearest-even rounding to 8 significant bits
+    x = np.array([1 + 2.0 ** -8, 1 + 3 * 2.0 ** -8, 1 + 2.0 ** -9, -(1 + 2.0 ** -7 + 2.0 ** -9)])
+    assert np.array_equal(TR.bf16_round(x), [1.0, 1 + 2.0 ** -6, 1.0, -(1 + 2.0 ** -7)])
