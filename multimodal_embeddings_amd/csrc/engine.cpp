@@ -1316,7 +1316,7 @@ struct TrainLayout {
     size_t kx, kx1, kqk, kvt, ko, klse, kxf, ks, kcu, ktiles, kpos, tok_off, tok;
     size_t h1, v, h2, gu, dx, dxb, da, dgu, act, dh, dx1, dx1b, dout, dq, dk, dv, dqkv, gpart, gsum, xty, dz, pd, z,
         du, dxf, delta, total;
-    size_t Tpad, xty_splits, xty_chunk, rows_per_block;
+    size_t Tpad, rows_per_block;
 };
 }  // namespace
 
@@ -1409,10 +1409,14 @@ TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count, size_t 
     const size_t gblocks = (size_t)rmsnorm_bwd_blocks((int)T1, (int)L.rows_per_block);
     L.gpart = take(gblocks * D * 4);
     L.gsum = take((gblocks + 31) / 32 * D * 4);
-    // weight gradients: about 8 ranges of tokens, each a multiple of 64
-    L.xty_chunk = align_up(std::max<size_t>((T + 7) / 8, 64), 64);
-    L.xty_splits = std::max<size_t>(1, (T + L.xty_chunk - 1) / L.xty_chunk);
-    L.xty = take(L.xty_splits * std::max(D * 3 * D, std::max(D * 2 * F, F * D)) * 4);
+    // weight-gradient partials: ranges of tokens for each product's shape
+    size_t xty_floats = 0;
+    for (auto mn : {std::array<size_t, 2>{D, 3 * D}, {D, D}, {D, 2 * F}, {F, D}}) {
+        int sp = 0, ch = 0;
+        xty_split((int)T1, (int)mn[0], (int)mn[1], &sp, &ch);
+        xty_floats = std::max(xty_floats, (size_t)sp * mn[0] * mn[1]);
+    }
+    L.xty = take(xty_floats * 4);
     L.dz = take(std::max<size_t>(count, 1) * H * D * 4);
     L.pd = take(Tp * H * 2 * 4);
     L.z = take(std::max<size_t>(count, 1) * H * D * 4);
@@ -1746,7 +1750,7 @@ void train_backward(ube_trainer_t tr, hipStream_t st, float const *d_embeddings)
     const int blocks = rmsnorm_bwd_blocks(Ti, (int)L.rows_per_block);
     auto xty = [&](const uint16_t *x, int M, const uint16_t *y, int Nn, float *out, float *out2, bool di) {
         timed(ube_kernel_weight_grad_k, st, [&] {
-            return launch_xty(x, M, y, Nn, Ti, M, Nn, F32(L.xty), (int)L.xty_splits, (int)L.xty_chunk, out, out2, di,
+            return launch_xty(x, M, y, Nn, Ti, M, Nn, F32(L.xty), out, out2, di,
                               st);
         });
     };

@@ -46,11 +46,13 @@ hipError_t launch_rmsnorm_bwd(const float *x, const float *gain, const float *dh
                               uint16_t *dxb, float *gpart, int rows_per_block, int T, int D, float eps,
                               hipStream_t stream);
 int rmsnorm_bwd_blocks(int T, int rows_per_block);
-// out[m][n] = sum over t of X[t][m] Y[t][n] (bf16 operands, fp32 partials per split of t, then reduced);
-// M % 128 == 0, N % 64 == 0. With `deinterleave`, n runs over [gate 32 | up 32] blocks and out receives
-// the gate columns, out2 the up columns ([M x N/2] each).
+// out[m][n] = sum over t of X[t][m] Y[t][n] (bf16 operands, fp32 partials per range of t, then reduced in
+// range order); M % 128 == 0, N % 64 == 0. With `deinterleave`, n runs over [gate 32 | up 32] blocks and
+// out receives the gate columns, out2 the up columns ([M x N/2] each). xty_split gives the ranges the
+// launch uses: `partial` holds splits * M * N floats.
+void xty_split(int T, int M, int N, int *splits, int *chunk);
 hipError_t launch_xty(const uint16_t *x, int ldx, const uint16_t *y, int ldy, int T, int M, int N, float *partial,
-                      int splits, int chunk, float *out, float *out2, bool deinterleave, hipStream_t stream);
+                      float *out, float *out2, bool deinterleave, hipStream_t stream);
 // columns sums of fixed blocks: out[d] = sum over b < blocks of part[b][d]
 // work: at least ceil(blocks / 32) * D floats
 hipError_t launch_sum_rows(const float *part, int blocks, int D, float *out, float *work, hipStream_t stream);

@@ -11,6 +11,8 @@
 // and the row kernels (RMSNorm, SwiGLU and rotary backward, the pool and the byte embedding).
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "device.h"
@@ -488,6 +490,87 @@ __global__ __launch_bounds__(256, 2) void k_xty(const uint16_t *x, int ldx, cons
             *(f32x4 *)(out + 32 * tn + 8 * i) = f32x4{acc[tn][4 * i], acc[tn][4 * i + 1], acc[tn][4 * i + 2], acc[tn][4 * i + 3]};
 }
 
+// The same product for M % 256 == 0 and N % 256 == 0: a 256 n x 256 m tile per workgroup of 8 waves;
+// wave (wn = wave % 2, wm = wave / 2) holds n rows 128 wn .. + 127 (four 32-row A tiles of Y^T) against m
+// columns 64 wm .. + 63 (two 32-column B tiles of X). LDS stages of 64 tokens hold both tiles as 512-byte
+// rows (chunks swizzled by 4 (t % 4), which keeps the transpose reads of a 16-lane group on distinct banks);
+// two stages, the next one's DMA in flight during the current one's products.
+constexpr int kXtyWideStage = 2 * 2048;  // 16-byte chunks: Y tile [64 t][256 n] | X tile [64 t][256 m]
+
+__global__ __launch_bounds__(512, 1) void k_xty256(const uint16_t *x, int ldx, const uint16_t *y, int ldy, int T,
+                                                   int M, int N, float *partial, int chunk) {
+    __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * kXtyWideStage];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, l32 = lane & 31, hh = lane >> 5;
+    const int wn = wave & 1, wm = wave >> 1;
+    const int MT = M / 256, NT = N / 256;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    const int s = logical / (MT * NT), rest = logical % (MT * NT);
+    const int mt = rest / NT, nt = rest % NT;  // consecutive tiles share their X columns
+    const int m0 = mt * 256, n0 = nt * 256;
+    const int tb = s * chunk, te = min(T, tb + chunk);
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i][0] = acc[i][1] = f32x16{};
+    const int lrow = tid >> 5, lch = tid & 31;  // 16 rows of 32 chunks per round, 4 rounds per tile
+    auto issue = [&](int t0, int buf) {
+        u32x4 *st = smem + buf * kXtyWideStage;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * r + lrow, src = min(t0 + row, T - 1);
+            lds_dma16(y + (size_t)src * ldy + n0 + ((lch ^ kmajor_swz<512>(row)) << 3), st + r * 512 + wave * 64);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int row = 16 * r + lrow, src = min(t0 + row, T - 1);
+            lds_dma16(x + (size_t)src * ldx + m0 + ((lch ^ kmajor_swz<512>(row)) << 3),
+                      st + 2048 + r * 512 + wave * 64);
+        }
+    };
+    const int nk = te > tb ? (te - tb + 63) >> 6 : 0;
+    if (nk) issue(tb, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+        const int buf = kt & 1, t0 = tb + kt * 64;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (t0 + 64 > te) {  // rows past the range read as zero
+            u32x4 *st = smem + buf * kXtyWideStage;
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (t0 + 16 * r + lrow >= te) {
+                    st[r * 512 + tid] = u32x4{0u, 0u, 0u, 0u};
+                    st[2048 + r * 512 + tid] = u32x4{0u, 0u, 0u, 0u};
+                }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (kt + 1 < nk) issue(t0 + 64, buf ^ 1);
+        const uint8_t *sY = (const uint8_t *)(smem + buf * kXtyWideStage), *sX = sY + 2048 * 16;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 b0 = tr_frag<512>(sX, 16 * ks, 64 * wm, lane);
+            const bf16x8 b1 = tr_frag<512>(sX, 16 * ks, 64 * wm + 32, lane);
+#pragma unroll
+            for (int tn = 0; tn < 4; ++tn) {
+                const bf16x8 a = tr_frag<512>(sY, 16 * ks, 128 * wn + 32 * tn, lane);
+                acc[tn][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[tn][0], 0, 0, 0);
+                acc[tn][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[tn][1], 0, 0, 0);
+            }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        lds_barrier();
+    }
+#pragma unroll
+    for (int tm = 0; tm < 2; ++tm) {
+        const int m = m0 + 64 * wm + 32 * tm + l32;
+        float *out = partial + ((size_t)s * M + m) * N + n0 + 128 * wn + 4 * hh;
+#pragma unroll
+        for (int tn = 0; tn < 4; ++tn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *(f32x4 *)(out + 32 * tn + 8 * i) = f32x4{acc[tn][tm][4 * i], acc[tn][tm][4 * i + 1],
+                                                          acc[tn][tm][4 * i + 2], acc[tn][tm][4 * i + 3]};
+    }
+}
+
 __global__ __launch_bounds__(256) void k_xty_reduce(const float *partial, int splits, int M, int N, float *out,
                                                     float *out2, int deinterleave) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
@@ -926,10 +1009,28 @@ hipError_t launch_sum_rows(const float *part, int blocks, int D, float *out, flo
     return hipGetLastError();
 }
 
+void xty_split(int T, int M, int N, int *splits, int *chunk) {
+    const bool wide = M % 256 == 0 && N % 256 == 0;
+    const int tiles = wide ? (M / 256) * (N / 256) : (M / 128) * (N / 64);
+    // as many ranges as fit one round of workgroups on the 256 CUs (one wide or two narrow workgroups per
+    // CU): a partial second round would double the launch's time
+    const int want = std::max(1, (wide ? 256 : 512) / tiles);
+    const int cap = std::max(1, (T + 255) / 256);                  // at least 256 tokens per range
+    int sp = std::max(1, std::min(want, cap));
+    const int ch = ((T + sp - 1) / sp + 63) / 64 * 64;
+    *chunk = std::max(ch, 64);
+    *splits = std::max(1, (T + *chunk - 1) / *chunk);
+}
+
 hipError_t launch_xty(const uint16_t *x, int ldx, const uint16_t *y, int ldy, int T, int M, int N, float *partial,
-                      int splits, int chunk, float *out, float *out2, bool deinterleave, hipStream_t stream) {
-    if (M % 128 || N % 64 || chunk % 64 || T <= 0) return hipErrorInvalidValue;
-    k_xty<<<splits * (M / 128) * (N / 64), 256, 0, stream>>>(x, ldx, y, ldy, T, M, N, partial, chunk);
+                      float *out, float *out2, bool deinterleave, hipStream_t stream) {
+    if (T <= 0 || M % 128 || N % 64) return hipErrorInvalidValue;
+    int splits = 0, chunk = 0;
+    xty_split(T, M, N, &splits, &chunk);
+    if (M % 256 == 0 && N % 256 == 0)
+        k_xty256<<<splits * (M / 256) * (N / 256), 512, 0, stream>>>(x, ldx, y, ldy, T, M, N, partial, chunk);
+    else
+        k_xty<<<splits * (M / 128) * (N / 64), 256, 0, stream>>>(x, ldx, y, ldy, T, M, N, partial, chunk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t n = (size_t)M * N;
