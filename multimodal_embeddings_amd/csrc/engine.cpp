@@ -1314,7 +1314,7 @@ namespace {
 // host-built tables (cu, tiles, positions, byte -> token lists), then the backward's scratch.
 struct TrainLayout {
     size_t kx, kx1, kqk, kvt, ko, klse, kxf, ks, kcu, ktiles, kpos, tok_off, tok;
-    size_t h1, v, h2, gu, dx, dxb, da, dgu, act, dh, dx1, dx1b, dout, dq, dk, dv, dqkv, gpart, gsum, xty, dz, pd, z,
+    size_t h1, v, h2, gu, dx, dxb, da, dgu, act, dh, dx1, dx1b, dout, dqkv, gpart, gsum, xty, dz, pd, z,
         du, dxf, delta, total;
     size_t Tpad, rows_per_block;
 };
@@ -1400,9 +1400,6 @@ TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count, size_t 
     L.dx1 = take(Tp * D * 4);
     L.dx1b = take(Tp * D * 2);
     L.dout = take(Tp * D * 2);
-    L.dq = take(Tp * D * 2);
-    L.dk = take(Tp * D * 2);
-    L.dv = take(Tp * D * 2);
     L.dqkv = take(Tp * 3 * D * 2);
     L.delta = take(H * Tp * 4);
     L.rows_per_block = 64;
@@ -1804,16 +1801,16 @@ void train_backward(ube_trainer_t tr, hipStream_t st, float const *d_embeddings)
                                    eps, st));
         UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[b.g2].grad, F32(L.gsum), st));
         // attention half
-        uint16_t *dout = B16(L.dout), *dq = B16(L.dq), *dk = B16(L.dk), *dv = B16(L.dv), *dqkv = B16(L.dqkv);
+        uint16_t *dout = B16(L.dout), *dqkv = B16(L.dqkv);
         gemm(kEpiStore, TT[b.o].w16, dx1b, Ti, Di, Di, dout, Di, nullptr, 0, st);
         xty(o, Di, dx1b, Di, TT[b.o].grad, nullptr, false);
         UBE_HIP(launch_attention_delta(dout, o, Di, delta, ldl, Ti, Hi, st));
         AttnBwdArgs ab2{};
         ab2.q = qk, ab2.k = qk + D, ab2.ldqk = 2 * Di, ab2.v = v, ab2.ldv = Di, ab2.dout = dout, ab2.lddo = Di;
-        ab2.lse = lse, ab2.delta = delta, ab2.ldl = ldl, ab2.dq = dq, ab2.dk = dk, ab2.dv = dv, ab2.ldd = Di;
-        ab2.cu = cu, ab2.tiles = tiles, ab2.ntiles = ntiles, ab2.heads = Hi;
+        ab2.lse = lse, ab2.delta = delta, ab2.ldl = ldl;
+        ab2.dq = dqkv, ab2.dk = dqkv + D, ab2.dv = dqkv + 2 * D, ab2.ldd = 3 * Di;  // straight into d[q|k|v]
+        ab2.cu = cu, ab2.tiles = tiles, ab2.ntiles = ntiles, ab2.heads = Hi, ab2.pos = pos, ab2.rope = m->rope;
         timed(ube_kernel_attention_bwd_k, st, [&] { return launch_attention_bwd(ab2, st); });
-        UBE_HIP(launch_rope_bwd(dq, dk, dv, Di, pos, m->rope, dqkv, Ti, Di, st));
         gemm(kEpiPatch, TT[b.qkv].w16, dqkv, Ti, Di, 3 * Di, nullptr, 0, dh, Di, st);
         xty(h1, Di, dqkv, 3 * Di, TT[b.qkv].grad, nullptr, false);
         UBE_HIP(launch_rmsnorm_bwd(x_in, TT[b.g1].w32, dh, dx1, dx, dxb, F32(L.gpart), (int)L.rows_per_block, Ti, Di,

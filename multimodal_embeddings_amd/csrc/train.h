@@ -20,12 +20,16 @@ struct AttnBwdArgs {
     int lddo;
     const float *lse, *delta;
     int ldl;
-    uint16_t *dq, *dk, *dv;  // rows [T x D]; dq, dk in the rotated space
+    uint16_t *dq, *dk, *dv;  // rows of ldd elements (e.g. the three parts of one [T x 3D] buffer)
     int ldd;
     const int *cu;
     const int2 *tiles;
     int ntiles;
     int heads;
+    // 1-axis rotary (positions pos[t * 4], table rope[pos * 32 + pair] of (cos, sin)): when set, dq and dk
+    // are written through the transposed rotation, i.e. with respect to q and k before the rotary
+    const int16_t *pos;
+    const float2 *rope;
 };
 hipError_t launch_attention_bwd(const AttnBwdArgs &a, hipStream_t stream);
 // delta[h][t] = sum_e dO[t][64h + e] O[t][64h + e]
@@ -33,9 +37,6 @@ hipError_t launch_attention_delta(const uint16_t *dout, const uint16_t *o, int l
                                   int heads, hipStream_t stream);
 // v rows [T x D] from the feature-major vt [D x ldvt]
 hipError_t launch_vt_rows(const uint16_t *vt, int ldvt, uint16_t *v, int T, int D, hipStream_t stream);
-// Rotary backward (1-axis text positions pos[t * 4]): dqkv [T x 3D] = (R^T dq | R^T dk | dv)
-hipError_t launch_rope_bwd(const uint16_t *dq, const uint16_t *dk, const uint16_t *dv, int ld, const int16_t *pos,
-                           const float2 *rope, uint16_t *dqkv, int T, int D, hipStream_t stream);
 // SwiGLU backward: gu [T x 2F] interleaved in blocks of 32 (gate | up), da [T x F] -> dgu (same interleave)
 // and a = SiLU(g) u [T x F]
 hipError_t launch_swiglu_bwd(const uint16_t *gu, const uint16_t *da, uint16_t *dgu, uint16_t *a, int T, int F,

@@ -93,6 +93,14 @@ __device__ __forceinline__ u32x4 load16(const uint16_t *p) { return *(const u32x
 
 constexpr float kScale2 = 0.18033688011112042f;  // log2(e) / 8
 
+// The transpose of the rotary map on two adjacent pairs (g0, g1), (g2, g3) with cs = (cos, sin) of each:
+// (g0, g1) -> (c g0 + s g1, -s g0 + c g1), the gradient with respect to the values before the rotation.
+__device__ __forceinline__ void unrotate4(float (&g)[4], f32x4 cs) {
+    const float a0 = cs.x * g[0] + cs.y * g[1], a1 = -cs.y * g[0] + cs.x * g[1];
+    const float b0 = cs.z * g[2] + cs.w * g[3], b1 = -cs.w * g[2] + cs.z * g[3];
+    g[0] = a0, g[1] = a1, g[2] = b0, g[3] = b1;
+}
+
 __global__ __launch_bounds__(512, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
     __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * 1024];  // stage: K tile 512 | V tile 512 chunks
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
@@ -158,14 +166,17 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
         }
     }
     if (active && qvalid) {
+        const float2 *rb = a.rope ? a.rope + (int)a.pos[(size_t)t * 4] * 32 : nullptr;
 #pragma unroll
         for (int te = 0; te < 2; ++te)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = 32 * te + 8 * i + 4 * hh;
-                *(u32x2 *)(a.dq + (size_t)t * a.ldd + head * 64 + e) =
-                    u32x2{pack2(dQ[te][4 * i] * 0.125f, dQ[te][4 * i + 1] * 0.125f),
-                          pack2(dQ[te][4 * i + 2] * 0.125f, dQ[te][4 * i + 3] * 0.125f)};
+                float g[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) g[j] = dQ[te][4 * i + j] * 0.125f;
+                if (rb) unrotate4(g, *(const f32x4 *)(rb + e / 2));
+                *(u32x2 *)(a.dq + (size_t)t * a.ldd + head * 64 + e) = u32x2{pack2(g[0], g[1]), pack2(g[2], g[3])};
             }
     }
 }
@@ -251,14 +262,17 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
         }
     }
     if (active && kvalid) {
+        const float2 *rb = a.rope ? a.rope + (int)a.pos[(size_t)u * 4] * 32 : nullptr;
 #pragma unroll
         for (int te = 0; te < 2; ++te)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = 32 * te + 8 * i + 4 * hh;
-                *(u32x2 *)(a.dk + (size_t)u * a.ldd + head * 64 + e) =
-                    u32x2{pack2(dK[te][4 * i] * 0.125f, dK[te][4 * i + 1] * 0.125f),
-                          pack2(dK[te][4 * i + 2] * 0.125f, dK[te][4 * i + 3] * 0.125f)};
+                float g[4];
+#pragma unroll
+                for (int j = 0; j < 4; ++j) g[j] = dK[te][4 * i + j] * 0.125f;
+                if (rb) unrotate4(g, *(const f32x4 *)(rb + e / 2));
+                *(u32x2 *)(a.dk + (size_t)u * a.ldd + head * 64 + e) = u32x2{pack2(g[0], g[1]), pack2(g[2], g[3])};
                 *(u32x2 *)(a.dv + (size_t)u * a.ldd + head * 64 + e) =
                     u32x2{pack2(dV[te][4 * i], dV[te][4 * i + 1]), pack2(dV[te][4 * i + 2], dV[te][4 * i + 3])};
             }
@@ -296,26 +310,6 @@ __global__ __launch_bounds__(256) void k_vt_rows(const uint16_t *vt, int ldvt, u
         const int t = x >> 6, f = x & 63;
         if (t0 + t < T) v[(size_t)(t0 + t) * D + f0 + f] = tile[f][t];
     }
-}
-
-// one thread per (token, pair of one head of q or k): the transpose of the rotation, then v copied
-__global__ __launch_bounds__(256) void k_rope_bwd(const uint16_t *dq, const uint16_t *dk, const uint16_t *dv, int ld,
-                                                  const int16_t *pos, const float2 *rope, uint16_t *dqkv, int T, int D) {
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const int pairs = D / 2;
-    if (idx >= (size_t)T * pairs * 3) return;
-    const int t = (int)(idx / (pairs * 3)), r = (int)(idx % (pairs * 3));
-    const int part = r / pairs, pr = r % pairs;
-    uint16_t *out = dqkv + (size_t)t * 3 * D + part * D + 2 * pr;
-    if (part == 2) {
-        *(uint32_t *)out = *(const uint32_t *)(dv + (size_t)t * ld + 2 * pr);
-        return;
-    }
-    const uint16_t *src = (part == 0 ? dq : dk) + (size_t)t * ld + 2 * pr;
-    const uint32_t x = *(const uint32_t *)src;
-    const float x0 = bf16_to_f32(x & 0xffff), x1 = bf16_to_f32(x >> 16);
-    const float2 cs = rope[(size_t)pos[(size_t)t * 4] * 32 + (pr & 31)];
-    *(uint32_t *)out = pack2(cs.x * x0 + cs.y * x1, -cs.y * x0 + cs.x * x1);
 }
 
 // one thread per (token, 2 features)
@@ -969,14 +963,6 @@ hipError_t launch_attention_delta(const uint16_t *dout, const uint16_t *o, int l
 hipError_t launch_vt_rows(const uint16_t *vt, int ldvt, uint16_t *v, int T, int D, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     k_vt_rows<<<dim3(D / 64, (T + 63) / 64), 256, 0, stream>>>(vt, ldvt, v, T, D);
-    return hipGetLastError();
-}
-
-hipError_t launch_rope_bwd(const uint16_t *dq, const uint16_t *dk, const uint16_t *dv, int ld, const int16_t *pos,
-                           const float2 *rope, uint16_t *dqkv, int T, int D, hipStream_t stream) {
-    const size_t n = (size_t)T * (D / 2) * 3;
-    if (!n) return hipSuccess;
-    k_rope_bwd<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(dq, dk, dv, ld, pos, rope, dqkv, T, D);
     return hipGetLastError();
 }
 
