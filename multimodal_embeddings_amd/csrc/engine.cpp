@@ -692,12 +692,19 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
     const int T = (int)p.T, ldvt = (int)L.Tpad;
 
     if (T > 0) {
+        // the residual stream: in place in the arena, or (training forward) block l's fp32 input kept at
+        // keep->x + l T D and the rows after its attention half at keep->x1 + l T D (the arena's x when
+        // those are recomputed), every residual product writing out of place
+        Keep const *kp = r.keep;
+        const size_t TD = (size_t)T * D;
+        auto xin = [&](size_t l) { return kp ? kp->x + l * TD : x; };
+        auto xmid = [&](size_t l) { return kp && kp->x1 ? kp->x1 + l * TD : x; };
         // keys past the last token are masked; their values must still be finite (p = 0 times v)
         UBE_HIP(hipMemset2DAsync(vt + T, (size_t)ldvt * 2, 0, 64 * 2, (size_t)D, st));
         // ---- frontend
         if (!media) {
             timed(ube_kernel_gather_k, st, [&] {
-                return launch_gather_text(input, src, cu, tiles, ntiles, m->embed, x, h, ssq, pos, D, st);
+                return launch_gather_text(input, src, cu, tiles, ntiles, m->embed, xin(0), h, ssq, pos, D, st);
             });
         } else {
             uint16_t *patches = (uint16_t *)(db + L.patches);
@@ -707,13 +714,11 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
             });
             GemmArgs ga{};
             ga.w = m->patch_t, ga.x = patches, ga.M = T, ga.N = D, ga.K = 768;
-            ga.out_f32 = x, ga.ld_f32 = D, ga.scale = 1.0f / 255.0f;
+            ga.out_f32 = xin(0), ga.ld_f32 = D, ga.scale = 1.0f / 255.0f;
             ga.out_bf16 = h, ga.ld_out = D, ga.ss_out = ssq;
             timed(ube_kernel_gemm_patch_k, st, [&] { return launch_gemm(kEpiPatch, ga, st); });
         }
-        if (r.trace) UBE_HIP(hipMemcpyAsync(r.trace, x, (size_t)T * D * 4, hipMemcpyDeviceToDevice, st));
-        Keep const *kp = r.keep;
-        const size_t TD = (size_t)T * D;
+        if (r.trace) UBE_HIP(hipMemcpyAsync(r.trace, xin(0), TD * 4, hipMemcpyDeviceToDevice, st));
         // ---- blocks
         uint8_t *q8 = (uint8_t *)(db + L.q8);
         float *qs = (float *)(db + L.qs);
@@ -727,11 +732,11 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
             }
         };
         // RMSNorm into the next projection's input (bf16 h, or E4M3 rows)
-        auto norm = [&](const float *gain) {
+        auto norm = [&](const float *xr, const float *gain) {
             if (m->e4m3)
-                timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm_e4m3(x, gain, q8, qs, T, D, eps, st); });
+                timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm_e4m3(xr, gain, q8, qs, T, D, eps, st); });
             else
-                timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm(x, gain, h, T, D, eps, st); });
+                timed(ube_kernel_rmsnorm_k, st, [&] { return launch_rmsnorm(xr, gain, h, T, D, eps, st); });
         };
         auto quantize = [&](const uint16_t *rows, int width) {
             timed(ube_kernel_quantize_k, st, [&] { return launch_quantize_rows(rows, q8, qs, T, width, st); });
@@ -752,13 +757,13 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
             uint16_t *qk_l = qk, *vt_l = vt, *o_l = o;
             int ldvt_l = ldvt;
             float *lse_l = nullptr;
-            if (kp) UBE_HIP(hipMemcpyAsync(kp->x + l * TD, x, TD * 4, hipMemcpyDeviceToDevice, st));
+            float *x_l = xin(l), *x1_l = xmid(l), *x_next = xin(l + 1);
             if (kp && kp->qk) {
                 qk_l = kp->qk + l * kp->Tpad * 2 * D, vt_l = kp->vt + l * D * kp->ldvt, o_l = kp->o + l * kp->Tpad * D;
                 ldvt_l = (int)kp->ldvt, lse_l = kp->lse + l * H * kp->ldl;
                 UBE_HIP(hipMemset2DAsync(vt_l + T, kp->ldvt * 2, 0, 64 * 2, (size_t)D, st));
             }
-            if (m->e4m3) norm(Wl.g1);
+            if (m->e4m3) norm(x_l, Wl.g1);
             GemmArgs qa{};
             qa.w = Wl.wqkv, qa.x = h, qa.M = T, qa.N = 3 * D, qa.K = D;
             folded_norm(qa);
@@ -771,31 +776,27 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
             });
             if (m->e4m3) quantize(o_l, D);
             GemmArgs oa{};
-            oa.w = Wl.wo, oa.x = o_l, oa.M = T, oa.N = D, oa.K = D, oa.out_f32 = x, oa.ld_f32 = D;
+            oa.w = Wl.wo, oa.x = o_l, oa.M = T, oa.N = D, oa.K = D, oa.out_f32 = x1_l, oa.ld_f32 = D;
+            oa.res_in = x1_l == x_l ? nullptr : x_l;
             residual_out(oa);
             project(ube_kernel_gemm_out_k, kEpiResid, oa, Wl.s_o, 0.f);
-            if (kp && kp->x1) UBE_HIP(hipMemcpyAsync(kp->x1 + l * TD, x, TD * 4, hipMemcpyDeviceToDevice, st));
-            if (m->e4m3) norm(Wl.g2);
+            if (m->e4m3) norm(x1_l, Wl.g2);
             GemmArgs ua{};
             ua.w = Wl.wgu, ua.x = h, ua.M = T, ua.N = 2 * F, ua.K = D, ua.out_bf16 = act, ua.ld_out = F;
             folded_norm(ua);
             project(ube_kernel_gemm_gate_up_k, kEpiSwiglu, ua, Wl.s_gate, Wl.s_up);
             if (m->e4m3) quantize(act, F);
             GemmArgs da{};
-            da.w = Wl.wd, da.x = act, da.M = T, da.N = D, da.K = F, da.out_f32 = x, da.ld_f32 = D;
+            da.w = Wl.wd, da.x = act, da.M = T, da.N = D, da.K = F, da.out_f32 = x_next, da.ld_f32 = D;
+            da.res_in = x_next == x1_l ? nullptr : x1_l;
             residual_out(da);
             project(ube_kernel_gemm_down_k, kEpiResid, da, Wl.s_down, 0.f);
-            if (r.trace)
-                UBE_HIP(hipMemcpyAsync(r.trace + (l + 1) * (size_t)T * D, x, (size_t)T * D * 4,
-                                       hipMemcpyDeviceToDevice, st));
+            if (r.trace) UBE_HIP(hipMemcpyAsync(r.trace + (l + 1) * TD, x_next, TD * 4, hipMemcpyDeviceToDevice, st));
         }
-        if (kp) {
-            UBE_HIP(hipMemcpyAsync(kp->x + g.depth * TD, x, TD * 4, hipMemcpyDeviceToDevice, st));
-            xf = kp->xf, s = kp->s;
-        }
+        if (kp) xf = kp->xf, s = kp->s;
         float *states = tok.states_f32 ? (float *)(db + L.st) : nullptr;
         timed(ube_kernel_final_norm_k, st,
-              [&] { return launch_final_norm_scores(x, m->gf, m->u, xf, s, states, T, D, H, eps, st); });
+              [&] { return launch_final_norm_scores(xin(g.depth), m->gf, m->u, xf, s, states, T, D, H, eps, st); });
         if (tok.vectors) {
             // token head (bf16 operands, fp32 rows), then unit rows
             GemmArgs ta{};
@@ -1782,8 +1783,10 @@ void train_backward(ube_trainer_t tr, hipStream_t st, float const *d_embeddings)
             qa.D = Di, qa.sec0 = m->sec0, qa.sec1 = m->sec1;
             UBE_HIP(launch_gemm(kEpiQkv, qa, st));
             UBE_HIP(launch_attention(qk, qk + D, 2 * Di, vt, ldvt, o, Di, cu, tiles, ntiles, Hi, st, lse, ldl));
-            UBE_HIP(hipMemcpyAsync(x1, x_in, TD * 4, hipMemcpyDeviceToDevice, st));
-            gemm(kEpiResid, m->layers[li].wo, o, Ti, Di, Di, nullptr, 0, x1, Di, st);
+            GemmArgs oa{};
+            oa.w = m->layers[li].wo, oa.x = o, oa.M = Ti, oa.N = Di, oa.K = Di;
+            oa.out_f32 = x1, oa.ld_f32 = Di, oa.res_in = x_in, oa.scale = 1.0f;
+            UBE_HIP(launch_gemm(kEpiResid, oa, st));
         }
         // the block's inputs that were not kept
         UBE_HIP(launch_vt_rows(vt, ldvt, v, Ti, Di, st));

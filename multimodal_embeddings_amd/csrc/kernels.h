@@ -31,6 +31,7 @@ struct GemmArgs {
     int ld_out;
     float *out_f32;
     int ld_f32;
+    const float *res_in;  // residual: x read from here (ld_f32) and x + acc written to out_f32; NULL: in place
     uint16_t *vt;
     int ld_vt;
     const int16_t *pos;   // [M_alloc x 4] rotary coordinates per token

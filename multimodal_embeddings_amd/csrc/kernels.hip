@@ -643,7 +643,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs &a, f32x16 (&acc)[T
                         f32x4 *px = (f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n);
                         f32x4 xv;
                         if constexpr (EPI == kEpiResid) {
-                            xv = *px;
+                            xv = a.res_in ? *(const f32x4 *)(a.res_in + (size_t)m * a.ld_f32 + n) : *px;
                             xv = f32x4{xv.x + o[0], xv.y + o[1], xv.z + o[2], xv.w + o[3]};
                         } else {
                             xv = f32x4{o[0] * a.scale, o[1] * a.scale, o[2] * a.scale, o[3] * a.scale};
@@ -1055,7 +1055,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
                 const int m = m0 + s * 64 + wave * 8 + k;
                 dst[k] = f32x4{0.f, 0.f, 0.f, 0.f};
                 if (EPI == kEpiResid && m < a.M)
-                    dst[k] = *(const f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n0 + lane * 4);
+                    dst[k] = *(const f32x4 *)((a.res_in ? a.res_in : a.out_f32) + (size_t)m * a.ld_f32 + n0 + lane * 4);
             }
         };
         load_x(0, xin[0]);
