@@ -40,6 +40,27 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// Sums HP per-lane values over the 64 lanes of a wave at once: each exchange
+// step halves the values a lane keeps (lane bits 5, 4, ... pick the half), the
+// remaining steps finish the sums. Lane L then holds the total of value
+// L / (64 / HP).
+template <int HP>
+__device__ __forceinline__ float lanes_reduce(const float (&p)[HP], int lane) {
+    float cur[HP];
+#pragma unroll
+    for (int j = 0; j < HP; ++j) cur[j] = p[j];
+    int m = 32;
+#pragma unroll
+    for (int n = HP; n > 1; n >>= 1, m >>= 1) {
+        const bool up = lane & m;
+#pragma unroll
+        for (int j = 0; j < n / 2; ++j)
+            cur[j] = (up ? cur[n / 2 + j] : cur[j]) + __shfl_xor(up ? cur[j] : cur[n / 2 + j], m, 64);
+    }
+    for (; m >= 1; m >>= 1) cur[0] += __shfl_xor(cur[0], m, 64);
+    return cur[0];
+}
+
 // Workgroups are dispatched round-robin over the 8 XCDs (block b runs on XCD
 // b % 8). This remap gives every XCD one contiguous range of logical tiles, so
 // tiles that share operands share that XCD's L2.

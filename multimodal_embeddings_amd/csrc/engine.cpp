@@ -1316,7 +1316,7 @@ namespace {
 struct TrainLayout {
     size_t kx, kx1, kqk, kvt, ko, klse, kxf, ks, kcu, ktiles, kpos, tok_off, tok;
     size_t h1, v, h2, gu, dx, dxb, da, dgu, act, dh, dx1, dx1b, dout, dqkv, gpart, gsum, xty, dz, pd, z,
-        du, dxf, delta, total;
+        du, spa, zpart, dupart, dxf, delta, total;
     size_t Tpad, rows_per_block;
 };
 }  // namespace
@@ -1419,6 +1419,10 @@ TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count, size_t 
     L.pd = take(Tp * H * 2 * 4);
     L.z = take(std::max<size_t>(count, 1) * H * D * 4);
     L.du = take(std::max<size_t>(count, 1) * H * D * 4);
+    L.spa = take(std::max<size_t>(count, 1) * H * 4);
+    const size_t pchunks = (size_t)pool_bwd_chunks((int)count);
+    L.zpart = take(std::max<size_t>(count, 1) * pchunks * H * D * 4);
+    L.dupart = take(std::max<size_t>(count, 1) * pchunks * H * D * 4);
     L.dxf = take(Tp * D * 4);
     L.total = total;
     return L;
@@ -1759,7 +1763,7 @@ void train_backward(ube_trainer_t tr, hipStream_t st, float const *d_embeddings)
     pa.dpooled = d_embeddings;
     pa.dxf = F32(L.dxf), pa.z = F32(L.z), pa.du = F32(L.du);
     pa.dwv = TT[tr->t_wv].grad, pa.dwk = TT[tr->t_wk].grad, pa.dquery = TT[tr->t_query].grad;
-    UBE_HIP(launch_pool_bwd(pa, F32(L.dz), F32(L.pd), st));
+    UBE_HIP(launch_pool_bwd(pa, F32(L.dz), F32(L.pd), F32(L.spa), F32(L.zpart), F32(L.dupart), st));
     UBE_HIP(launch_rmsnorm_bwd(F32(L.kx) + N * TD, TT[tr->t_gf].w32, F32(L.dxf), nullptr, F32(L.dx), B16(L.dxb),
                                F32(L.gpart), (int)L.rows_per_block, Ti, Di, eps, st));
     UBE_HIP(launch_sum_rows(F32(L.gpart), blocks, Di, TT[tr->t_gf].grad, F32(L.gsum), st));

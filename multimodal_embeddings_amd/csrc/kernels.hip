@@ -155,27 +155,6 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, co
     }
 }
 
-// Sums HP per-lane values over the 64 lanes of a wave at once: each exchange
-// step halves the values a lane keeps (lane bits 5, 4, ... pick the half), the
-// remaining steps finish the sums. Lane L then holds the total of value
-// L / (64 / HP).
-template <int HP>
-__device__ __forceinline__ float lanes_reduce(const float (&p)[HP], int lane) {
-    float cur[HP];
-#pragma unroll
-    for (int j = 0; j < HP; ++j) cur[j] = p[j];
-    int m = 32;
-#pragma unroll
-    for (int n = HP; n > 1; n >>= 1, m >>= 1) {
-        const bool up = lane & m;
-#pragma unroll
-        for (int j = 0; j < n / 2; ++j)
-            cur[j] = (up ? cur[n / 2 + j] : cur[j]) + __shfl_xor(up ? cur[j] : cur[n / 2 + j], m, 64);
-    }
-    for (; m >= 1; m >>= 1) cur[0] += __shfl_xor(cur[0], m, 64);
-    return cur[0];
-}
-
 template <int V, int C>
 __global__ __launch_bounds__(256) void k_final_norm_scores(const float *__restrict__ x, const float *__restrict__ gain,
                                                            const float *__restrict__ u, uint16_t *__restrict__ xf,
@@ -1562,9 +1541,138 @@ __global__ __launch_bounds__(256) void k_pool(const uint16_t *__restrict__ xf, c
     }
 }
 
+// The same pool for D <= 512 and H <= 8 with the token sum spread over the workgroup: 8 waves, wave w
+// taking tokens t0 + w, t0 + w + 8, ...; lane l holds columns 8 l .. 8 l + 7 (one 16-byte load of xf per
+// token, four tokens in flight) and the partial z of every head; the waves' partials are added in wave
+// order through LDS. Softmax statistics by a fixed tree over the threads. One item's tokens are never
+// read twice and no thread walks the whole item alone.
+__global__ __launch_bounds__(512) void k_pool_wide(const uint16_t *__restrict__ xf, const float *__restrict__ s,
+                                                   const int *__restrict__ cu, const uint16_t *__restrict__ wv,
+                                                   void *__restrict__ out, int out_bf16, size_t out_stride, int D,
+                                                   int H) {
+    __shared__ float z[8 * 512];
+    __shared__ float red[8][8];
+    __shared__ float mh[8], ih[8];
+    const int item = blockIdx.x, t0 = cu[item], t1 = cu[item + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    char *orow = (char *)out + (size_t)item * out_stride;
+    if (t1 == t0) {
+        for (int col = tid; col < D; col += 512) {
+            if (out_bf16) ((uint16_t *)orow)[col] = 0;
+            else ((float *)orow)[col] = 0.f;
+        }
+        return;
+    }
+    // softmax statistics of every head
+    float loc[8];
+#pragma unroll
+    for (int hd = 0; hd < 8; ++hd) loc[hd] = -INFINITY;
+    for (int t = t0 + tid; t < t1; t += 512)
+#pragma unroll
+        for (int hd = 0; hd < 8; ++hd)
+            if (hd < H) loc[hd] = fmaxf(loc[hd], s[(size_t)t * H + hd]);
+#pragma unroll
+    for (int hd = 0; hd < 8; ++hd) {
+        const float v = wave_max(loc[hd]);
+        if (lane == 0) red[wave][hd] = v;
+    }
+    __syncthreads();
+    if (tid < H) {
+        float m = red[0][tid];
+        for (int w = 1; w < 8; ++w) m = fmaxf(m, red[w][tid]);
+        mh[tid] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hd = 0; hd < 8; ++hd) loc[hd] = 0.f;
+    for (int t = t0 + tid; t < t1; t += 512)
+#pragma unroll
+        for (int hd = 0; hd < 8; ++hd)
+            if (hd < H) loc[hd] += __expf(s[(size_t)t * H + hd] - mh[hd]);
+#pragma unroll
+    for (int hd = 0; hd < 8; ++hd) {
+        const float v = wave_sum(loc[hd]);
+        if (lane == 0) red[wave][hd] = v;
+    }
+    __syncthreads();
+    if (tid < H) {
+        float sum = red[0][tid];
+        for (int w = 1; w < 8; ++w) sum += red[w][tid];
+        ih[tid] = 1.0f / sum;
+    }
+    __syncthreads();
+    float m8[8], i8[8];
+#pragma unroll
+    for (int hd = 0; hd < 8; ++hd) m8[hd] = hd < H ? mh[hd] : 0.f, i8[hd] = hd < H ? ih[hd] : 0.f;
+    // z_h partials of this wave's tokens
+    const bool on = 8 * lane < D;
+    float zacc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int hd = 0; hd < 8; ++hd) zacc[i][hd] = 0.f;
+    auto add = [&](int t, u32x4 v) {
+        float p[8];
+#pragma unroll
+        for (int hd = 0; hd < 8; ++hd) p[hd] = hd < H ? __expf(s[(size_t)t * H + hd] - m8[hd]) * i8[hd] : 0.f;
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const float a = bf16_to_f32(w4[q] & 0xffff), b = bf16_to_f32(w4[q] >> 16);
+#pragma unroll
+            for (int hd = 0; hd < 8; ++hd) {
+                zacc[2 * q][hd] += p[hd] * a;
+                zacc[2 * q + 1][hd] += p[hd] * b;
+            }
+        }
+    };
+    int t = t0 + wave;
+    for (; t + 24 < t1; t += 32) {
+        u32x4 v[4] = {};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (on) v[k] = *(const u32x4 *)(xf + (size_t)(t + 8 * k) * D + 8 * lane);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) add(t + 8 * k, v[k]);
+    }
+    for (; t < t1; t += 8) {
+        u32x4 v = {};
+        if (on) v = *(const u32x4 *)(xf + (size_t)t * D + 8 * lane);
+        add(t, v);
+    }
+    // partials added in wave order
+    for (int w = 0; w < 8; ++w) {
+        if (wave == w && on) {
+#pragma unroll
+            for (int hd = 0; hd < 8; ++hd)
+                if (hd < H) {
+                    float *zr = z + hd * D + 8 * lane;
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) zr[i] = w == 0 ? zacc[i][hd] : zr[i] + zacc[i][hd];
+                }
+        }
+        __syncthreads();
+    }
+    // pooled_h = z_h W_v[:, 64 h .. 64 h + 63]
+    for (int col = tid; col < D; col += 512) {
+        const float *zh = z + (col >> 6) * D;
+        float acc8[8] = {};
+        for (int f = 0; f < D; f += 8)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) acc8[k] += zh[f + k] * bf16_to_f32(wv[(size_t)(f + k) * D + col]);
+        const float accv = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
+        if (out_bf16) ((uint16_t *)orow)[col] = (uint16_t)f32_to_bf16(accv);
+        else ((float *)orow)[col] = accv;
+    }
+}
+
 hipError_t launch_pool(const uint16_t *xf, const float *s, const int *cu, int count, const uint16_t *wv, void *out,
                        int out_bf16, size_t out_stride, int D, int H, hipStream_t stream) {
     if (count == 0) return hipSuccess;
+    if (D <= 512 && D % 8 == 0 && H <= 8) {
+        k_pool_wide<<<count, 512, 0, stream>>>(xf, s, cu, wv, out, out_bf16, out_stride, D, H);
+        return hipGetLastError();
+    }
     const size_t lds = ((size_t)H * D + 256 * (size_t)H + 2 * (size_t)H + 4) * sizeof(float);
     const int C = (D + 255) / 256;
     auto go = [&](auto kernel) -> hipError_t {

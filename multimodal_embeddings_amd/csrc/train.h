@@ -76,8 +76,11 @@ struct PoolBwdArgs {
     float *z, *du;        // [count x H x D] work
     float *dwv, *dwk, *dquery;  // [D x D], [D x D], [D]
 };
-// dz [count x H x D] and pd [T x H x 2] are work buffers
-hipError_t launch_pool_bwd(const PoolBwdArgs &a, float *dz, float *pd, hipStream_t stream);
+// Work buffers: dz [count x H x D], pd [T x H x 2], spa [count x H], zpart and dupart [count x chunks x H x D]
+// each with chunks = pool_bwd_chunks(count). D % 8 == 0, D <= 1024, H <= 16.
+int pool_bwd_chunks(int count);
+hipError_t launch_pool_bwd(const PoolBwdArgs &a, float *dz, float *pd, float *spa, float *zpart, float *dupart,
+                           hipStream_t stream);
 
 // Adafactor over every tensor of a model in four launches. One table entry per tensor (device memory,
 // built once): gradient g fp32; master bf16 (w16) or fp32 (w32); state r [rows], c [cols] (matrices) or

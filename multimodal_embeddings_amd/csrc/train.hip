@@ -612,72 +612,156 @@ __global__ __launch_bounds__(256) void k_pool_bwd_dz(PoolBwdArgs a, float *dz) {
     dz[((size_t)item * a.H + h) * a.D + i] = s;
 }
 
-// p and ds of every (token, head) into pd[t][h][2]; one workgroup (4 waves) per (item, head): softmax
-// statistics by a fixed tree, a_t,h by one wave per token, sum p a in token order
-__global__ __launch_bounds__(256) void k_pool_bwd_tokens(PoolBwdArgs a, const float *dz, float *pd) {
-    __shared__ float red[4];
-    __shared__ float stat[3];
-    const int item = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// p and a of every (token, head) into pd[t][h][2] and sum_t p a per (item, head) into spa; one workgroup
+// (8 waves) per item. Softmax statistics per head by a fixed tree over the threads; then wave w takes the
+// item's tokens t0 + w, t0 + w + 8, ...: lane l holds columns 8 l + 512 c .. + 7 (c < CG) of xf_t and of
+// dz_h for 8 heads at a time, a_t,h = xf_t . dz_h comes from a cross-lane tree (head h ends in lanes
+// 8h .. 8h + 7), and those lanes keep p_t,h and the running sum of p a (token order per wave, then the
+// waves in order).
+template <int CG>
+__global__ __launch_bounds__(512) void k_pool_bwd_tokens(PoolBwdArgs a, const float *dz, float *pd, float *spa) {
+    __shared__ float red[8][16];
+    __shared__ float mh[16], ih[16];
+    const int item = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int D = a.D, H = a.H, t0 = a.cu[item], t1 = a.cu[item + 1];
-    if (t1 == t0) return;
-    float mx = -INFINITY;
-    for (int t = t0 + tid; t < t1; t += 256) mx = fmaxf(mx, a.s[(size_t)t * H + h]);
-    mx = wave_max(mx);
-    if (lane == 0) red[wave] = mx;
+    if (t1 == t0) {
+        if (tid < H) spa[(size_t)item * H + tid] = 0.f;
+        return;
+    }
+    // softmax statistics of every head
+    float loc[16];
+#pragma unroll
+    for (int hd = 0; hd < 16; ++hd) loc[hd] = -INFINITY;
+    for (int t = t0 + tid; t < t1; t += 512)
+#pragma unroll
+        for (int hd = 0; hd < 16; ++hd)
+            if (hd < H) loc[hd] = fmaxf(loc[hd], a.s[(size_t)t * H + hd]);
+#pragma unroll
+    for (int hd = 0; hd < 16; ++hd) {
+        const float v = wave_max(loc[hd]);
+        if (lane == 0 && hd < H) red[wave][hd] = v;
+    }
     __syncthreads();
-    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (tid < H) {
+        float m = red[0][tid];
+        for (int w = 1; w < 8; ++w) m = fmaxf(m, red[w][tid]);
+        mh[tid] = m;
+    }
     __syncthreads();
-    float se = 0.f;
-    for (int t = t0 + tid; t < t1; t += 256) se += expf(a.s[(size_t)t * H + h] - mx);
-    se = wave_sum(se);
-    if (lane == 0) red[wave] = se;
+#pragma unroll
+    for (int hd = 0; hd < 16; ++hd) loc[hd] = 0.f;
+    for (int t = t0 + tid; t < t1; t += 512)
+#pragma unroll
+        for (int hd = 0; hd < 16; ++hd)
+            if (hd < H) loc[hd] += __expf(a.s[(size_t)t * H + hd] - mh[hd]);
+#pragma unroll
+    for (int hd = 0; hd < 16; ++hd) {
+        const float v = wave_sum(loc[hd]);
+        if (lane == 0 && hd < H) red[wave][hd] = v;
+    }
     __syncthreads();
-    se = ((red[0] + red[1]) + red[2]) + red[3];
-    const float *dzh = dz + ((size_t)item * H + h) * D;
-    for (int t = t0 + wave; t < t1; t += 4) {
-        float dot = 0.f;
-        for (int i = lane; i < D; i += 64) dot += bf16_to_f32(a.xf[(size_t)t * D + i]) * dzh[i];
-        dot = wave_sum(dot);
-        if (lane == 0) {
-            pd[((size_t)t * H + h) * 2] = expf(a.s[(size_t)t * H + h] - mx) / se;
-            pd[((size_t)t * H + h) * 2 + 1] = dot;
+    if (tid < H) {
+        float sum = red[0][tid];
+        for (int w = 1; w < 8; ++w) sum += red[w][tid];
+        ih[tid] = 1.0f / sum;
+    }
+    __syncthreads();
+    for (int h0 = 0; h0 < H; h0 += 8) {
+        float dzr[CG][8][8];
+#pragma unroll
+        for (int c = 0; c < CG; ++c)
+#pragma unroll
+            for (int hd = 0; hd < 8; ++hd)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int col = 512 * c + 8 * lane + i;
+                    dzr[c][hd][i] = (h0 + hd < H && col < D) ? dz[((size_t)item * H + h0 + hd) * D + col] : 0.f;
+                }
+        const int hl = h0 + (lane >> 3);  // the head whose total this lane receives
+        const bool mine = hl < H;
+        const float mhl = mine ? mh[hl] : 0.f, ihl = mine ? ih[hl] : 0.f;
+        float pa = 0.f;
+        auto tok = [&](int t, const u32x4 (&v)[CG]) {
+            float d[8];
+#pragma unroll
+            for (int hd = 0; hd < 8; ++hd) d[hd] = 0.f;
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+                const uint32_t w4[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float x0 = bf16_to_f32(w4[q] & 0xffff), x1 = bf16_to_f32(w4[q] >> 16);
+#pragma unroll
+                    for (int hd = 0; hd < 8; ++hd) d[hd] += x0 * dzr[c][hd][2 * q] + x1 * dzr[c][hd][2 * q + 1];
+                }
+            }
+            const float av = lanes_reduce<8>(d, lane);
+            if (mine) {
+                const float p = __expf(a.s[(size_t)t * H + hl] - mhl) * ihl;
+                pa += p * av;
+                if ((lane & 7) == 0) *(float2 *)(pd + ((size_t)t * H + hl) * 2) = float2{p, av};
+            }
+        };
+        auto load = [&](int t, u32x4 (&v)[CG]) {
+#pragma unroll
+            for (int c = 0; c < CG; ++c) {
+                const int col = 512 * c + 8 * lane;
+                v[c] = col < D ? *(const u32x4 *)(a.xf + (size_t)t * D + col) : u32x4{0u, 0u, 0u, 0u};
+            }
+        };
+        int t = t0 + wave;
+        for (; t + 24 < t1; t += 32) {
+            u32x4 v[4][CG];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) load(t + 8 * k, v[k]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) tok(t + 8 * k, v[k]);
         }
-    }
-    __syncthreads();
-    if (tid == 0) {
-        float spa = 0.f;
-        for (int t = t0; t < t1; ++t) spa += pd[((size_t)t * H + h) * 2] * pd[((size_t)t * H + h) * 2 + 1];
-        stat[0] = spa;
-    }
-    __syncthreads();
-    for (int t = t0 + tid; t < t1; t += 256) {
-        float *q = pd + ((size_t)t * H + h) * 2;
-        q[1] = q[0] * (q[1] - stat[0]);
+        for (; t < t1; t += 8) {
+            u32x4 v[CG];
+            load(t, v);
+            tok(t, v);
+        }
+        __syncthreads();
+        if ((lane & 7) == 0 && mine) red[wave][hl - h0] = pa;
+        __syncthreads();
+        if (tid < 8 && h0 + tid < H) {
+            float sum = red[0][tid];
+            for (int w = 1; w < 8; ++w) sum += red[w][tid];
+            spa[(size_t)item * H + h0 + tid] = sum;
+        }
     }
 }
 
-// per item, one thread per column: z, du and dxf
-__global__ __launch_bounds__(256) void k_pool_bwd_cols(PoolBwdArgs a, const float *dz, const float *pd) {
-    const int item = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
+// One workgroup per (256 columns, item, range of the item's tokens), one thread per column: per token
+// ds_h = p_h (a_h - spa_h) and dxf_t = sum_h (p_h dz_h + ds_h u_h); the range's partial sums of
+// z_h = sum p x and du_h = sum ds x (token order).
+__global__ __launch_bounds__(256) void k_pool_bwd_cols(PoolBwdArgs a, const float *dz, const float *pd,
+                                                       const float *spa, float *zpart, float *dupart, int chunks) {
+    const int item = blockIdx.y, ch = blockIdx.z, i = blockIdx.x * 256 + threadIdx.x;
     const int D = a.D, H = a.H, t0 = a.cu[item], t1 = a.cu[item + 1];
     if (i >= D) return;
-    float zv[16], duv[16], dzv[16], uv[16];
+    const int len = t1 - t0;
+    const int c0 = t0 + (int)((long long)len * ch / chunks), c1 = t0 + (int)((long long)len * (ch + 1) / chunks);
+    float dzv[16], uv[16], sp[16], zv[16], duv[16];
 #pragma unroll
     for (int h = 0; h < 16; ++h) {
         zv[h] = duv[h] = 0.f;
         dzv[h] = h < H ? dz[((size_t)item * H + h) * D + i] : 0.f;
         uv[h] = h < H ? a.u[(size_t)h * D + i] : 0.f;
+        sp[h] = h < H ? spa[(size_t)item * H + h] : 0.f;
     }
-    for (int t = t0; t < t1; ++t) {
+    for (int t = c0; t < c1; ++t) {
         const float xv = bf16_to_f32(a.xf[(size_t)t * D + i]);
         float g = 0.f;
 #pragma unroll
         for (int h = 0; h < 16; ++h) {
             if (h < H) {
-                const float p = pd[((size_t)t * H + h) * 2], ds = pd[((size_t)t * H + h) * 2 + 1];
-                zv[h] += p * xv;
+                const float2 q = *(const float2 *)(pd + ((size_t)t * H + h) * 2);
+                const float ds = q.x * (q.y - sp[h]);
+                zv[h] += q.x * xv;
                 duv[h] += ds * xv;
-                g += p * dzv[h] + ds * uv[h];
+                g += q.x * dzv[h] + ds * uv[h];
             }
         }
         a.dxf[(size_t)t * D + i] = g;
@@ -685,10 +769,26 @@ __global__ __launch_bounds__(256) void k_pool_bwd_cols(PoolBwdArgs a, const floa
 #pragma unroll
     for (int h = 0; h < 16; ++h) {
         if (h < H) {
-            a.z[((size_t)item * H + h) * D + i] = zv[h];
-            a.du[((size_t)item * H + h) * D + i] = duv[h];
+            const size_t o = (((size_t)item * chunks + ch) * H + h) * D + i;
+            zpart[o] = zv[h];
+            dupart[o] = duv[h];
         }
     }
+}
+
+// per item: z and du from the ranges' partials (ranges ascending), one thread per (h, i)
+__global__ __launch_bounds__(256) void k_pool_bwd_item_sums(PoolBwdArgs a, const float *zpart, const float *dupart,
+                                                            int chunks) {
+    const int item = blockIdx.y, x = blockIdx.x * 256 + threadIdx.x, HD = a.H * a.D;
+    if (x >= HD) return;
+    float zs = 0.f, ds = 0.f;
+    for (int ch = 0; ch < chunks; ++ch) {
+        const size_t o = ((size_t)item * chunks + ch) * HD + x;
+        zs += zpart[o];
+        ds += dupart[o];
+    }
+    a.z[(size_t)item * HD + x] = zs;
+    a.du[(size_t)item * HD + x] = ds;
 }
 
 // du totals over items (items ascending), one thread per (h, i)
@@ -1030,15 +1130,25 @@ hipError_t launch_embed_bwd(const float *dx, const uint32_t *tok_off, const uint
     return hipGetLastError();
 }
 
-hipError_t launch_pool_bwd(const PoolBwdArgs &a, float *dz, float *pd, hipStream_t stream) {
-    if (a.H > 16 || a.D > 1024) return hipErrorInvalidValue;
+int pool_bwd_chunks(int count) { return std::max(1, std::min(16, 512 / std::max(count, 1))); }
+
+hipError_t launch_pool_bwd(const PoolBwdArgs &a, float *dz, float *pd, float *spa, float *zpart, float *dupart,
+                           hipStream_t stream) {
+    if (a.H > 16 || a.D > 1024 || a.D % 8) return hipErrorInvalidValue;
     hipError_t e;
+    const int chunks = pool_bwd_chunks(a.count);
     if (a.count > 0) {
         k_pool_bwd_dz<<<dim3((a.H * a.D + 255) / 256, a.count), 256, 0, stream>>>(a, dz);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_pool_bwd_tokens<<<dim3(a.count, a.H), 256, 0, stream>>>(a, dz, pd);
+        if (a.D <= 512)
+            k_pool_bwd_tokens<1><<<a.count, 512, 0, stream>>>(a, dz, pd, spa);
+        else
+            k_pool_bwd_tokens<2><<<a.count, 512, 0, stream>>>(a, dz, pd, spa);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_pool_bwd_cols<<<dim3((a.D + 255) / 256, a.count), 256, 0, stream>>>(a, dz, pd);
+        k_pool_bwd_cols<<<dim3((a.D + 255) / 256, a.count, chunks), 256, 0, stream>>>(a, dz, pd, spa, zpart, dupart,
+                                                                                        chunks);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        k_pool_bwd_item_sums<<<dim3((a.H * a.D + 255) / 256, a.count), 256, 0, stream>>>(a, zpart, dupart, chunks);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     float *du_tot = dz;  // dz is free once the columns pass ran
