@@ -401,7 +401,7 @@ void ube_contrastive(ube_contrastive_t *arguments);
  * A trainer keeps bf16 master weights (fp32 for the norm gains) in the canonical layout of ube_weights_t,
  * their fp32 gradients and the Adafactor state, and refreshes the model's forward weights after every
  * step (so encodes on the model see the updated weights). Text models in bf16 with 1-axis rotary and
- * hidden <= 1024 (unsupported otherwise). Adafactor: beta1 [0.9], decay_rate [-0.8] (beta2_t = 1 -
+ * hidden a multiple of 128 up to 1024 (unsupported otherwise). Adafactor: beta1 [0.9], decay_rate [-0.8] (beta2_t = 1 -
  * t^decay_rate), epsilon1 [1e-30], clip_threshold [1]; zero fields take the defaults in brackets; the
  * update reads each fp32 gradient cast to bf16 (nearest even). With activation_recomputation the
  * training forward keeps only every block's fp32 input and the backward replays each block's attention

@@ -1456,7 +1456,8 @@ extern "C" void ube_trainer_init(ube_trainer_init_t *a) {
         if (!m->text) throw Failure{ube_status_unsupported_k, "training runs text models"};
         if (m->e4m3) throw Failure{ube_status_unsupported_k, "training runs bf16 models (E4M3 is inference-only)"};
         if (g.rope_axes != 1) throw Failure{ube_status_unsupported_k, "training runs 1-axis rotary"};
-        if (g.hidden > 1024 || g.heads > 16) throw Failure{ube_status_unsupported_k, "training runs hidden <= 1024"};
+        if (g.hidden > 1024 || g.hidden % 128 || g.heads > 16)
+            throw Failure{ube_status_unsupported_k, "training runs hidden <= 1024, a multiple of 128"};
         ube_weights_t const &w = *a->weights;
         if (!w.embed || !w.w_qkv || !w.w_o || !w.w_gate || !w.w_up || !w.w_down || !w.attn_norm || !w.mlp_norm ||
             !w.final_norm || !w.pool_query || !w.pool_wk || !w.pool_wv)

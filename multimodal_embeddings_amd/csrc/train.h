@@ -41,7 +41,7 @@ hipError_t launch_vt_rows(const uint16_t *vt, int ldvt, uint16_t *v, int T, int 
 // and a = SiLU(g) u [T x F]
 hipError_t launch_swiglu_bwd(const uint16_t *gu, const uint16_t *da, uint16_t *dgu, uint16_t *a, int T, int F,
                              hipStream_t stream);
-// RMSNorm backward with residual: dx = dres + d/dx <rmsnorm(x) * g, dh>; dxb = bf16(dx) (optional);
+// RMSNorm backward with residual (D a multiple of 128, at most 1024): dx = dres + d/dx <rmsnorm(x) * g, dh>; dxb = bf16(dx) (optional);
 // gain partials gpart[block][D] = sum over the block's rows of dh * x / rms (rows_per_block rows each)
 hipError_t launch_rmsnorm_bwd(const float *x, const float *gain, const float *dh, const float *dres, float *dx,
                               uint16_t *dxb, float *gpart, int rows_per_block, int T, int D, float eps,

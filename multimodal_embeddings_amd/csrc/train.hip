@@ -339,50 +339,86 @@ __global__ __launch_bounds__(256) void k_swiglu_bwd(const uint16_t *gu, const ui
 }
 
 // One wave per row; workgroup (4 waves) = rows_per_block consecutive rows, so the gain partial of the
-// block is summed in a fixed order.
+// block is summed in a fixed order. Lane l holds columns 64 V c + V l .. + V - 1 (c < D / 64 V) and moves
+// them with V-wide loads and stores; each wave keeps two rows in flight.
+template <int V, int CM>
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const float *x, const float *gain, const float *dh,
                                                      const float *dres, float *dx, uint16_t *dxb, float *gpart,
                                                      int rows_per_block, int T, int D, float eps) {
     __shared__ float sg[4][1024];
+    typedef float fv __attribute__((ext_vector_type(V)));
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int per = D / 64;  // columns per lane (D <= 1024)
-    float gacc[16];
+    constexpr int C = CM;  // column groups: D = 64 V CM
+    float gacc[CM][V], gv[CM][V];
 #pragma unroll
-    for (int c = 0; c < 16; ++c) gacc[c] = 0.f;
+    for (int c = 0; c < CM; ++c)
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+            gacc[c][v] = 0.f;
+            gv[c][v] = c < C ? gain[64 * V * c + V * lane + v] : 0.f;
+        }
     const int r0 = blockIdx.x * rows_per_block, r1 = min(T, r0 + rows_per_block);
-    for (int t = r0 + wave; t < r1; t += 4) {
-        float xv[16], hv[16], gv[16];
+    auto row = [&](int t, const fv (&xv)[CM], const fv (&hv)[CM]) {
         float ss = 0.f, sd = 0.f;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            if (c < per) {
-                const int i = c * 64 + lane;
-                xv[c] = x[(size_t)t * D + i];
-                hv[c] = dh[(size_t)t * D + i];
-                gv[c] = gain[i];
-                ss += xv[c] * xv[c];
-                sd += hv[c] * gv[c] * xv[c];
-            }
-        }
+        for (int c = 0; c < CM; ++c)
+            if (c < C)
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    ss += xv[c][v] * xv[c][v];
+                    sd += hv[c][v] * gv[c][v] * xv[c][v];
+                }
         ss = wave_sum(ss);
         sd = wave_sum(sd);
         const float inv = 1.0f / sqrtf(ss / (float)D + eps);
         const float k = inv * inv * inv * sd / (float)D;
 #pragma unroll
-        for (int c = 0; c < 16; ++c) {
-            if (c < per) {
-                const int i = c * 64 + lane;
-                float v = inv * gv[c] * hv[c] - xv[c] * k;
-                if (dres) v += dres[(size_t)t * D + i];
-                dx[(size_t)t * D + i] = v;
-                if (dxb) dxb[(size_t)t * D + i] = (uint16_t)f32_to_bf16(v);
-                gacc[c] += hv[c] * xv[c] * inv;
+        for (int c = 0; c < CM; ++c)
+            if (c < C) {
+                const size_t i = (size_t)t * D + 64 * V * c + V * lane;
+                fv o;
+#pragma unroll
+                for (int v = 0; v < V; ++v) {
+                    o[v] = inv * gv[c][v] * hv[c][v] - xv[c][v] * k;
+                    gacc[c][v] += hv[c][v] * xv[c][v] * inv;
+                }
+                if (dres) o += *(const fv *)(dres + i);
+                *(fv *)(dx + i) = o;
+                if (dxb) {
+                    if constexpr (V == 4)
+                        *(u32x2 *)(dxb + i) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+                    else
+                        *(uint32_t *)(dxb + i) = pack2(o[0], o[1]);
+                }
             }
-        }
+    };
+    auto load = [&](int t, fv (&xv)[CM], fv (&hv)[CM]) {
+#pragma unroll
+        for (int c = 0; c < CM; ++c)
+            if (c < C) {
+                const size_t i = (size_t)t * D + 64 * V * c + V * lane;
+                xv[c] = *(const fv *)(x + i);
+                hv[c] = *(const fv *)(dh + i);
+            }
+    };
+    int t = r0 + wave;
+    for (; t + 4 < r1; t += 8) {
+        fv xa[CM], ha[CM], xb[CM], hb[CM];
+        load(t, xa, ha);
+        load(t + 4, xb, hb);
+        row(t, xa, ha);
+        row(t + 4, xb, hb);
+    }
+    if (t < r1) {
+        fv xa[CM], ha[CM];
+        load(t, xa, ha);
+        row(t, xa, ha);
     }
 #pragma unroll
-    for (int c = 0; c < 16; ++c)
-        if (c < per) sg[wave][c * 64 + lane] = gacc[c];
+    for (int c = 0; c < CM; ++c)
+        if (c < C)
+#pragma unroll
+            for (int v = 0; v < V; ++v) sg[wave][64 * V * c + V * lane + v] = gacc[c][v];
     __syncthreads();
     for (int i = threadIdx.x; i < D; i += 256) gpart[(size_t)blockIdx.x * D + i] = ((sg[0][i] + sg[1][i]) + sg[2][i]) + sg[3][i];
 }
@@ -1079,10 +1115,22 @@ int rmsnorm_bwd_blocks(int T, int rows_per_block) { return (T + rows_per_block -
 hipError_t launch_rmsnorm_bwd(const float *x, const float *gain, const float *dh, const float *dres, float *dx,
                               uint16_t *dxb, float *gpart, int rows_per_block, int T, int D, float eps,
                               hipStream_t stream) {
-    if (D % 64 || D > 1024) return hipErrorInvalidValue;
     const int blocks = rmsnorm_bwd_blocks(T, rows_per_block);
     if (!blocks) return hipSuccess;
-    k_rmsnorm_bwd<<<blocks, 256, 0, stream>>>(x, gain, dh, dres, dx, dxb, gpart, rows_per_block, T, D, eps);
+#define UBE_RMSNORM_BWD(V, CM) \
+    k_rmsnorm_bwd<V, CM><<<blocks, 256, 0, stream>>>(x, gain, dh, dres, dx, dxb, gpart, rows_per_block, T, D, eps)
+    switch (D) {
+        case 128: UBE_RMSNORM_BWD(2, 1); break;
+        case 256: UBE_RMSNORM_BWD(4, 1); break;
+        case 512: UBE_RMSNORM_BWD(4, 2); break;
+        case 768: UBE_RMSNORM_BWD(4, 3); break;
+        case 1024: UBE_RMSNORM_BWD(4, 4); break;
+        case 384: UBE_RMSNORM_BWD(2, 3); break;
+        case 640: UBE_RMSNORM_BWD(2, 5); break;
+        case 896: UBE_RMSNORM_BWD(2, 7); break;
+        default: return hipErrorInvalidValue;
+    }
+#undef UBE_RMSNORM_BWD
     return hipGetLastError();
 }
 
