@@ -101,7 +101,7 @@ __device__ __forceinline__ void unrotate4(float (&g)[4], f32x4 cs) {
     g[0] = a0, g[1] = a1, g[2] = b0, g[3] = b1;
 }
 
-__global__ __launch_bounds__(512, 1) void k_attn_bwd_dq(AttnBwdArgs a) {
+__global__ __launch_bounds__(512, 4) void k_attn_bwd_dq(AttnBwdArgs a) {
     __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * 1024];  // stage: K tile 512 | V tile 512 chunks
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int head = logical / a.ntiles, ti = logical % a.ntiles;
