@@ -20,6 +20,9 @@ GEOMETRIES = {
     "text512": dict(depth=12, hidden=512, heads=8, ffn=1536, vocab=258, context=1024, token_width=128),
     "text512_4k": dict(depth=12, hidden=512, heads=8, ffn=1536, vocab=258, context=4096, token_width=128),
     "image768": dict(depth=12, hidden=768, heads=12, ffn=2304, rope_axes=2, context=1024, modality="image"),
+    # shallow text encoders at the widths of the pages' wider tiers (training parity cases)
+    "text768_shallow": dict(depth=2, hidden=768, heads=12, ffn=2304, vocab=258, context=1024),
+    "text1024_shallow": dict(depth=2, hidden=1024, heads=16, ffn=3072, vocab=258, context=1024),
     "video1024": dict(depth=24, hidden=1024, heads=16, ffn=3072, rope_axes=3, context=2048, modality="video"),
     "video1024_e4m3": dict(depth=24, hidden=1024, heads=16, ffn=3072, rope_axes=3, context=2048,
                            modality="video", quantization="e4m3"),

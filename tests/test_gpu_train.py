@@ -170,6 +170,25 @@ def test_depth12_backward_matches_oracle(ube, recompute):
     say(f"[text512] worst gradient cosine {worst[0]:.6f}, worst max |diff| {worst[1]:.2e}")
 
 
+@pytest.mark.parametrize("name", ["text768_shallow", "text1024_shallow"])
+def test_wide_backward_matches_oracle(ube, name):
+    """Hidden 768 (12 heads) and 1024 (16 heads), depth 2, a few ragged rows: the wider pool and norm paths
+    and heads beyond one group of 8 (cosine and max-difference bars as above)."""
+    import torch
+    g = configs.geometry(name)
+    w = synth.make_weights(g, gain_jitter=0.2)
+    batch = synth.text_batch(3, 60, 300, 0, 256, seed=12)
+    model, arena = ube.Model(w, 0), ube.Arena(0)
+    trainer = ube.Trainer(model, w)
+    rng = np.random.default_rng(13)
+    d_pooled = rng.standard_normal((batch.count, g["hidden"])).astype(np.float32)
+    trainer.backward(arena, device_bytes(batch.data), batch.offsets, device_bytes(d_pooled))
+    torch.cuda.synchronize()
+    _, want = TR.text_backward(w, batch.data, batch.offsets, d_pooled)
+    worst = _compare_grads(name, _grads_by_name(trainer), want, g["depth"])
+    say(f"[{name}] worst gradient cosine {worst[0]:.6f}, worst max |diff| {worst[1]:.2e}")
+
+
 def test_full_size_linearity_and_zero(ube):
     """The training step's full batch (64 rows x 1024 bytes, depth 12): gradients are linear in the upstream
     gradient (the backward of d1 + d2 equals the sum of the two) and vanish for a zero upstream gradient."""
