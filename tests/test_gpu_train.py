@@ -151,6 +151,75 @@ def test_forward_then_backward(ube):
         trainer.backward(None, None, None, d, after_forward=True)
 
 
+def test_three_adafactor_steps_track_the_oracle(ube):
+    """Three steps in a row: after each, every master equals the oracle's Adafactor run over the same
+    sequence of GPU gradients (its own state carried from step to step: the decayed factored second
+    moment, beta2_t = 1 - t^-0.8, the first moment and its bias correction), within one bf16 step plus
+    the fp32 rounding of the update at the operands' scale."""
+    import torch
+    g, w, batch, model, trainer, arena = _setup(ube, "tiny")
+    data = device_bytes(batch.data)
+    rng = np.random.default_rng(21)
+    states, masters = {}, {}
+    for n, l, m, _ in trainer.tensors():
+        masters[(n, l)] = m.float().cpu().numpy().astype(np.float64)
+        states[(n, l)] = TR.AdafactorState(m.shape)
+    lr = 1e-3
+    worst = 0.0
+    for step in (1, 2, 3):
+        d_pooled = rng.standard_normal((batch.count, g["hidden"])).astype(np.float32)
+        trainer.backward(arena, data, batch.offsets, device_bytes(d_pooled))
+        torch.cuda.synchronize()
+        grads = {(n, l): gr.double().cpu().numpy() for n, l, _, gr in trainer.tensors()}
+        trainer.step(lr)
+        torch.cuda.synchronize()
+        for n, l, m, _ in trainer.tensors():
+            key = (n, l)
+            w0 = masters[key]
+            want = TR.adafactor(w0, grads[key], states[key], lr, step)
+            got = m.float().cpu().numpy().astype(np.float64)
+            if n in ("attn_norm", "mlp_norm", "final_norm"):
+                assert np.allclose(got, want, rtol=1e-5, atol=1e-7), (key, step)
+            else:
+                upd = np.abs(want - w0)
+                want = synth.bf16_bits_to_f32(synth.to_bf16_bits(want.astype(np.float32))).astype(np.float64)
+                bar = np.abs(want) * 2.0 ** -7 + (np.abs(w0) + upd) * 2.0 ** -20 + 1e-30
+                steps = float((np.abs(got - want) / bar).max())
+                worst = max(worst, steps)
+                assert steps <= 1.0, (key, step, steps)
+            masters[key] = got  # the next step starts from the GPU's own masters
+    say(f"[adafactor x3] worst bf16 difference over three steps {worst:.2f} steps")
+
+
+def test_training_lowers_the_contrastive_loss(ube):
+    """End to end on 16 rows of 256 bytes at depth 12: forward, Matryoshka sigmoid loss over pairs
+    (2k, 2k + 1), backward and Adafactor step, five times; the loss of the same batch goes down."""
+    import torch
+    g = configs.geometry("text512")
+    w = synth.make_weights(g)
+    batch = synth.text_batch(16, 256, 257, 0, 256, seed=14)
+    model, arena, arena2 = ube.Model(w, 0), ube.Arena(0), ube.Arena(0)
+    trainer = ube.Trainer(model, w)
+    data = device_bytes(batch.data)
+    n = batch.count
+    pairs = synth.Edges.from_lists([[i ^ 1] for i in range(n)])
+    widths = (64, 128, 256, 512)
+    scalars = torch.zeros(3 + len(widths), device="cuda")
+    gemb = torch.zeros((n, g["hidden"]), device="cuda")
+    losses = []
+    for _ in range(5):
+        rows, _ = trainer.forward(arena, data, batch.offsets)
+        emb = rows.tensor().to(torch.bfloat16)
+        ube.contrastive(arena2, emb, scalars, widths=widths, attract=(pairs.offsets, pairs.ids, None), gradient=gemb)
+        torch.cuda.synchronize()
+        losses.append(float(scalars[0]))
+        trainer.backward(None, None, None, gemb, after_forward=True)
+        trainer.step(2e-3)
+        torch.cuda.synchronize()
+    say(f"[end to end] contrastive loss over five steps: {', '.join(f'{x:.4f}' for x in losses)}")
+    assert all(np.isfinite(losses)) and losses[-1] < losses[0]
+
+
 @pytest.mark.parametrize("recompute", [False, True])
 def test_depth12_backward_matches_oracle(ube, recompute):
     """The depth-12, hidden-512 encoder on a few ragged rows (cosine and max-difference bars as above), with
