@@ -193,7 +193,8 @@ def test_three_adafactor_steps_track_the_oracle(ube):
 
 def test_training_lowers_the_contrastive_loss(ube):
     """End to end on 16 rows of 256 bytes at depth 12: forward, Matryoshka sigmoid loss over pairs
-    (2k, 2k + 1), backward and Adafactor step, five times; the loss of the same batch goes down."""
+    (2k, 2k + 1), backward and Adafactor step (learning rate 2e-4), five times; the loss of the same batch
+    falls after the first step and ends below where it started."""
     import torch
     g = configs.geometry("text512")
     w = synth.make_weights(g)
@@ -214,10 +215,11 @@ def test_training_lowers_the_contrastive_loss(ube):
         torch.cuda.synchronize()
         losses.append(float(scalars[0]))
         trainer.backward(None, None, None, gemb, after_forward=True)
-        trainer.step(2e-3)
+        trainer.step(2e-4)
         torch.cuda.synchronize()
     say(f"[end to end] contrastive loss over five steps: {', '.join(f'{x:.4f}' for x in losses)}")
-    assert all(np.isfinite(losses)) and losses[-1] < losses[0]
+    # a small step along Adafactor's (sign-like, clipped) update lowers the loss to first order
+    assert all(np.isfinite(losses)) and losses[1] < losses[0] and losses[-1] < losses[0]
 
 
 @pytest.mark.parametrize("recompute", [False, True])
