@@ -72,6 +72,27 @@ def test_backward_matches_oracle(ube, name, count, recompute):
     say(f"[{name}] worst gradient cosine {worst[0]:.6f}, worst max |diff| {worst[1]:.2e}")
 
 
+def test_backward_edge_cases(ube):
+    """Empty items among others (their pooled rows are zero and pass no gradient), an item cut at the
+    context (1100 bytes, the first 1024 kept), and an empty tape (every gradient zero)."""
+    import torch
+    g, w, _, model, trainer, arena = _setup(ube, "tiny")
+    rng = np.random.default_rng(15)
+    lengths = [0, 5, 1100, 0, 37]
+    data = rng.integers(0, 256, size=sum(lengths), dtype=np.int64).astype(np.uint8)
+    offsets = np.concatenate([[0], np.cumsum(lengths)]).astype(np.uint64)
+    d_pooled = rng.standard_normal((len(lengths), g["hidden"])).astype(np.float32)
+    truncated, tokens = trainer.backward(arena, device_bytes(data), offsets, device_bytes(d_pooled))
+    torch.cuda.synchronize()
+    assert (truncated, tokens) == (1, 5 + 1024 + 37)
+    _, want = TR.text_backward(w, data, offsets, d_pooled)
+    worst = _compare_grads("edges", _grads_by_name(trainer), want, g["depth"])
+    say(f"[edges] worst gradient cosine {worst[0]:.6f}, worst max |diff| {worst[1]:.2e}")
+    trainer.backward(arena, device_bytes(np.zeros(1, np.uint8)), np.zeros(1, np.uint64), None)
+    torch.cuda.synchronize()
+    assert all(float(gr.abs().max()) == 0.0 for _, _, _, gr in trainer.tensors())
+
+
 def test_adafactor_step_and_refreshed_forward(ube):
     import torch
     g, w, batch, model, trainer, arena = _setup(ube, "tiny")
