@@ -84,3 +84,34 @@ def test_free_calls_are_null_safe():
     ube.lib().ube_model_free(None)
     ube.lib().ube_arena_free(None)
     assert ube.lib().ube_arena_capacity(None) == 0
+
+
+def test_trainer_calls_refuse_null_arguments_before_any_device_work():
+    L = ube.lib()
+    outcome = ube.ube_outcome_t()
+    handle = C.c_void_p(1234)
+    init = ube.ube_trainer_init_t(C.pointer(handle), C.pointer(outcome), None, None, 0.0, 0.0, 0.0, 0.0, 0)
+    L.ube_trainer_init(C.byref(init))
+    assert ube.STATUS[outcome.status] == "invalid_argument" and not handle.value
+    rows = ube.ube_rows_view_t()
+    rows.count = 7
+    fwd = ube.ube_trainer_forward_t(None, None, None, C.pointer(outcome), 0, ube.ube_tape_view_t(), C.pointer(rows),
+                                    None)
+    L.ube_trainer_forward(C.byref(fwd))
+    assert ube.STATUS[outcome.status] == "invalid_argument" and rows.data is None and rows.count == 0
+    bwd = ube.ube_trainer_backward_t(None, None, None, C.pointer(outcome), 0, ube.ube_tape_view_t(), None, 0, None, 1)
+    L.ube_trainer_backward(C.byref(bwd))
+    assert ube.STATUS[outcome.status] == "invalid_argument"
+    step = ube.ube_trainer_step_t(None, None, C.pointer(outcome), 0, 1e-3)
+    L.ube_trainer_step(C.byref(step))
+    assert ube.STATUS[outcome.status] == "invalid_argument"
+    assert L.ube_trainer_tensors(None, None, 0) == 0
+    L.ube_trainer_free(None)
+
+
+def test_contrastive_refuses_null_arena():
+    outcome = ube.ube_outcome_t()
+    args = ube.ube_contrastive_t()
+    args.outcome = C.pointer(outcome)
+    ube.lib().ube_contrastive(C.byref(args))
+    assert ube.STATUS[outcome.status] == "invalid_argument"
