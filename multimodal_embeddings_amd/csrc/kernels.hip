@@ -932,7 +932,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
                     }
                     v = u32x4{w4[0], w4[1], w4[2], w4[3]};
                 }
-                *(u32x4 *)(a.vt + (size_t)(n0 - 2 * a.D + f) * a.ld_vt + m0 + t0) = v;
+                __builtin_nontemporal_store(v, (u32x4 *)(a.vt + (size_t)(n0 - 2 * a.D + f) * a.ld_vt + m0 + t0));
             }
             return;
         }
@@ -988,7 +988,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
         for (int it = 0; it < 16; ++it) {
             const int t = it * 16 + wave * 2 + hh, m = m0 + t;
             const u32x4 v = *(const u32x4 *)(L + t * kQkPitch + l32 * 16);
-            if (m < a.M) *(u32x4 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 + l32 * 8) = v;
+            if (m < a.M) __builtin_nontemporal_store(v, (u32x4 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 + l32 * 8));
         }
     } else if constexpr (EPI == kEpiSwiglu) {
         // ---- gate (tn 0) and up (tn 1) of 32 outputs per wave: output column
@@ -1018,7 +1018,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
         for (int it = 0; it < 8; ++it) {
             const int t = it * 32 + wave * 4 + (lane >> 4), m = m0 + t, ch = lane & 15;
             const u32x4 v = *(const u32x4 *)(L + t * kGluPitch + ch * 16);
-            if (m < a.M) *(u32x4 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 / 2 + ch * 8) = v;
+            if (m < a.M) __builtin_nontemporal_store(v, (u32x4 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 / 2 + ch * 8));
         }
     } else {
         // ---- residual / patch: four slices of 64 tokens (slice s = tile tokens
@@ -1068,10 +1068,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
                 const f32x4 v = EPI == kEpiResid ? xin[s & 1][k] + d : d * a.scale;
                 sq[k] = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
                 if (m < a.M) {
-                    *(f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n0 + lane * 4) = v;
+                    __builtin_nontemporal_store(v, (f32x4 *)(a.out_f32 + (size_t)m * a.ld_f32 + n0 + lane * 4));
                     if (a.ss_out)
-                        *(u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 + lane * 4) =
-                            u32x2{pack2(v.x, v.y), pack2(v.z, v.w)};
+                        __builtin_nontemporal_store(u32x2{pack2(v.x, v.y), pack2(v.z, v.w)},
+                                                    (u32x2 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 + lane * 4));
                 }
             }
             if (a.ss_out) {
