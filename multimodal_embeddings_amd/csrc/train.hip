@@ -1,14 +1,15 @@
 // train.hip -- gfx950 kernels of the text encoder's backward pass and of the Adafactor update.
 //
 // What is computed: "UForm" page, "Precision by Design" (bf16 storage and matrix products with fp32
-// accumulation; gradients accumulated in fp32; every block's backward replays its forward from the
-// block's fp32 input) and "Adafactor Optimizer" (factored second moment, clipped update, first moment
-// with Adam's bias correction; bf16 master weights, fp32 norm gains).
+// accumulation; gradients accumulated in fp32 and cast to bf16 for the update; optionally every block's
+// backward replays its forward from the block's fp32 input) and "Adafactor Optimizer" (factored second
+// moment, clipped update, first moment with Adam's bias correction; bf16 master weights, fp32 norm gains).
 //
 // The products of the backward pass reuse the forward's GEMM kernel (activation gradients: dY W^T reads
 // the canonical [in x out] weights, which are K-contiguous for that product). This file adds the weight
-// gradients X^T Y (both operands token-major: read through the LDS transpose load), attention backward,
-// and the row kernels (RMSNorm, SwiGLU and rotary backward, the pool and the byte embedding).
+// gradients X^T Y (both operands token-major: read through the LDS transpose load), attention backward
+// (with the rotary's transpose in its stores), and the row kernels (RMSNorm and SwiGLU backward, the pool
+// and the byte embedding), the multi-tensor Adafactor and the repacking of derived weight copies.
 #include <hip/hip_runtime.h>
 #include <math.h>
 
