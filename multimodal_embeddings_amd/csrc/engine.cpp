@@ -1315,7 +1315,7 @@ namespace {
 // host-built tables (cu, tiles, positions, byte -> token lists), then the backward's scratch.
 struct TrainLayout {
     size_t kx, kx1, kqk, kvt, ko, klse, kxf, ks, kcu, ktiles, kpos, tok_off, tok;
-    size_t h1, v, h2, gu, dx, dxb, da, dgu, act, dh, dx1, dx1b, dout, dqkv, gpart, gsum, xty, dz, pd, z,
+    size_t h1, h2, gu, dx, dxb, da, dgu, act, dh, dx1, dx1b, dout, dqkv, gpart, gsum, xty, dz, pd, z,
         du, spa, zpart, dupart, dxf, delta, total;
     size_t Tpad, rows_per_block;
 };
@@ -1389,7 +1389,6 @@ TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count, size_t 
     L.tok = take(T1 * 4);
     // backward scratch
     L.h1 = take(Tp * D * 2);
-    L.v = take(Tp * D * 2);
     L.h2 = take(Tp * D * 2);
     L.gu = take(Tp * 2 * F * 2);
     L.dx = take(Tp * D * 4);
@@ -1776,7 +1775,7 @@ void train_backward(ube_trainer_t tr, hipStream_t st, float const *d_embeddings)
         float *x1 = F32(L.kx1) + kb * TD;
         uint16_t *qk = B16(L.kqk) + kb * Tp * 2 * D, *vt = B16(L.kvt) + kb * D * Tp, *o = B16(L.ko) + kb * Tp * D;
         float *lse = F32(L.klse) + kb * H * Tp;
-        uint16_t *h1 = B16(L.h1), *v = B16(L.v), *h2 = B16(L.h2), *gu = B16(L.gu);
+        uint16_t *h1 = B16(L.h1), *h2 = B16(L.h2), *gu = B16(L.gu);
         float *delta = F32(L.delta);
         UBE_HIP(launch_rmsnorm(x_in, TT[b.g1].w32, h1, Ti, Di, eps, st));
         if (tr->recompute) {
@@ -1793,8 +1792,7 @@ void train_backward(ube_trainer_t tr, hipStream_t st, float const *d_embeddings)
             oa.out_f32 = x1, oa.ld_f32 = Di, oa.res_in = x_in, oa.scale = 1.0f;
             UBE_HIP(launch_gemm(kEpiResid, oa, st));
         }
-        // the block's inputs that were not kept
-        UBE_HIP(launch_vt_rows(vt, ldvt, v, Ti, Di, st));
+        // the block's inputs that were not kept (v is read feature-major, as kept)
         UBE_HIP(launch_rmsnorm(x1, TT[b.g2].w32, h2, Ti, Di, eps, st));
         gemm(kEpiStore, b.guT, h2, Ti, 2 * Fi, Di, gu, 2 * Fi, nullptr, 0, st);
         // MLP half
@@ -1812,10 +1810,9 @@ void train_backward(ube_trainer_t tr, hipStream_t st, float const *d_embeddings)
         uint16_t *dout = B16(L.dout), *dqkv = B16(L.dqkv);
         gemm(kEpiStore, TT[b.o].w16, dx1b, Ti, Di, Di, dout, Di, nullptr, 0, st);
         xty(o, Di, dx1b, Di, TT[b.o].grad, nullptr, false);
-        UBE_HIP(launch_attention_delta(dout, o, Di, delta, ldl, Ti, Hi, st));
         AttnBwdArgs ab2{};
-        ab2.q = qk, ab2.k = qk + D, ab2.ldqk = 2 * Di, ab2.v = v, ab2.ldv = Di, ab2.dout = dout, ab2.lddo = Di;
-        ab2.lse = lse, ab2.delta = delta, ab2.ldl = ldl;
+        ab2.q = qk, ab2.k = qk + D, ab2.ldqk = 2 * Di, ab2.vt = vt, ab2.ldvt = ldvt, ab2.dout = dout, ab2.lddo = Di;
+        ab2.lse = lse, ab2.delta = delta, ab2.ldl = ldl, ab2.o = o, ab2.ldo = Di;
         ab2.dq = dqkv, ab2.dk = dqkv + D, ab2.dv = dqkv + 2 * D, ab2.ldd = 3 * Di;  // straight into d[q|k|v]
         ab2.cu = cu, ab2.tiles = tiles, ab2.ntiles = ntiles, ab2.heads = Hi, ab2.pos = pos, ab2.rope = m->rope;
         timed(ube_kernel_attention_bwd_k, st, [&] { return launch_attention_bwd(ab2, st); });

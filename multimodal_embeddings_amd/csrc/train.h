@@ -8,18 +8,23 @@
 
 namespace ube {
 
-// Attention backward for one head width of 64: rows of q, k (after the rotary), v, dO; the softmax log2
-// denominators (lse, head-major, base-2 units of log2(e) q.k / 8) and delta = rowsum(dO * O) per query
-// and head; tiles as the forward's (item, first token) list of 256-token tiles.
+// Attention backward for one head width of 64: rows of q, k (after the rotary), dO and O, feature-major v;
+// the softmax
+// log2 denominators (lse, head-major, base-2 units of log2(e) q.k / 8); delta = rowsum(dO * O) per query
+// and head is formed by the dQ kernel into `delta`; tiles as the forward's (item, first token) list of
+// 256-token tiles.
 struct AttnBwdArgs {
     const uint16_t *q, *k;
     int ldqk;
-    const uint16_t *v;
-    int ldv;
+    const uint16_t *vt;  // v feature-major [D x ldvt] (as the forward's QKV product writes it)
+    int ldvt;
     const uint16_t *dout;
     int lddo;
-    const float *lse, *delta;
+    const float *lse;
+    float *delta;  // written by the dQ kernel: rowsum(dO * O) per (head, query), read by the dK/dV kernel
     int ldl;
+    const uint16_t *o;  // attention output rows (for delta)
+    int ldo;
     uint16_t *dq, *dk, *dv;  // rows of ldd elements (e.g. the three parts of one [T x 3D] buffer)
     int ldd;
     const int *cu;
@@ -32,11 +37,6 @@ struct AttnBwdArgs {
     const float2 *rope;
 };
 hipError_t launch_attention_bwd(const AttnBwdArgs &a, hipStream_t stream);
-// delta[h][t] = sum_e dO[t][64h + e] O[t][64h + e]
-hipError_t launch_attention_delta(const uint16_t *dout, const uint16_t *o, int ld, float *delta, int ldl, int T,
-                                  int heads, hipStream_t stream);
-// v rows [T x D] from the feature-major vt [D x ldvt]
-hipError_t launch_vt_rows(const uint16_t *vt, int ldvt, uint16_t *v, int T, int D, hipStream_t stream);
 // SwiGLU backward: gu [T x 2F] interleaved in blocks of 32 (gate | up), da [T x F] -> dgu (same interleave)
 // and a = SiLU(g) u [T x F]
 hipError_t launch_swiglu_bwd(const uint16_t *gu, const uint16_t *da, uint16_t *dgu, uint16_t *a, int T, int F,

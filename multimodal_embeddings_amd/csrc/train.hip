@@ -119,13 +119,31 @@ __global__ __launch_bounds__(512, 4) void k_attn_bwd_dq(AttnBwdArgs a) {
         qf[ks] = __builtin_bit_cast(bf16x8, load16(a.q + (size_t)t * a.ldqk + head * 64 + ks * 16 + hh * 8));
         dof[ks] = __builtin_bit_cast(bf16x8, load16(a.dout + (size_t)t * a.lddo + head * 64 + ks * 16 + hh * 8));
     }
-    const float lse2 = a.lse[(size_t)head * a.ldl + t], dlt = a.delta[(size_t)head * a.ldl + t];
-    const int prow = tid >> 3, pc = swz(prow, tid & 7);
+    // delta = rowsum(dO * O) of this lane's query over the head's 64 features (lane half hh holds 32 of
+    // them), written for the dK/dV kernel that runs next
+    float dlt = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 ov = load16(a.o + (size_t)t * a.ldo + head * 64 + ks * 16 + hh * 8);
+        const u32x4 dv = __builtin_bit_cast(u32x4, dof[ks]);
+        const uint32_t o4[4] = {ov.x, ov.y, ov.z, ov.w}, d4[4] = {dv.x, dv.y, dv.z, dv.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            dlt += bf16_to_f32(o4[q] & 0xffff) * bf16_to_f32(d4[q] & 0xffff) +
+                   bf16_to_f32(o4[q] >> 16) * bf16_to_f32(d4[q] >> 16);
+    }
+    dlt += __shfl_xor(dlt, 32, 64);
+    if (hh == 0 && qvalid) a.delta[(size_t)head * a.ldl + t] = dlt;
+    const float lse2 = a.lse[(size_t)head * a.ldl + t];
+    const int prow = tid >> 3, pc = swz(prow, tid & 7), pv = (tid & 7) ^ kmajor_swz<128>(prow);
+    // K tile: 64 key rows of the head's 64 features; V^T tile: the head's 64 feature rows of vt over the
+    // tile's 64 keys (k-major for dP^T = V dO^T, read with the transpose load). Keys past the item read
+    // other items' values or the zeroed band after the last token: finite, and weighted 0.
     auto issue = [&](int tt, int buf) {
         const int row = min(k0 + tt * 64 + prow, k1 - 1);
         u32x4 *dst = smem + buf * 1024;
         lds_dma16(a.k + (size_t)row * a.ldqk + head * 64 + pc * 8, dst + wave * 64);
-        lds_dma16(a.v + (size_t)row * a.ldv + head * 64 + pc * 8, dst + 512 + wave * 64);
+        lds_dma16(a.vt + (size_t)(head * 64 + prow) * a.ldvt + k0 + tt * 64 + pv * 8, dst + 512 + wave * 64);
     };
     f32x16 dQ[2] = {f32x16{}, f32x16{}};
     const int ntile = (k1 - k0 + 63) >> 6;
@@ -136,7 +154,7 @@ __global__ __launch_bounds__(512, 4) void k_attn_bwd_dq(AttnBwdArgs a) {
         lds_barrier();  // tile tt landed for every wave; every wave is done with tile tt - 1
         if (tt + 1 < ntile) issue(tt + 1, (tt + 1) & 1);
         if (!active) continue;
-        const u32x4 *sK = smem + (tt & 1) * 1024, *sV = sK + 512;
+        const u32x4 *sK = smem + (tt & 1) * 1024, *sVt = sK + 512;
         const int kt = k0 + tt * 64;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -146,8 +164,8 @@ __global__ __launch_bounds__(512, 4) void k_attn_bwd_dq(AttnBwdArgs a) {
             for (int ks = 0; ks < 4; ++ks) {
                 const int ch = swz(row, ks * 2 + hh);
                 S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sK[row * 8 + ch]), qf[ks], S, 0, 0, 0);
-                dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sV[row * 8 + ch]), dof[ks], dP, 0, 0,
-                                                             0);
+                dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<128>((const uint8_t *)sVt, 16 * ks, 32 * kk, lane),
+                                                             dof[ks], dP, 0, 0, 0);
             }
             f32x16 dS;
 #pragma unroll
@@ -198,7 +216,11 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         kf[ks] = __builtin_bit_cast(bf16x8, load16(a.k + (size_t)u * a.ldqk + head * 64 + ks * 16 + hh * 8));
-        vf[ks] = __builtin_bit_cast(bf16x8, load16(a.v + (size_t)u * a.ldv + head * 64 + ks * 16 + hh * 8));
+        // v of key u, features 16 ks + 8 hh .. + 7, gathered from the feature-major vt
+        uint16_t e8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) e8[e] = a.vt[(size_t)(head * 64 + ks * 16 + hh * 8 + e) * a.ldvt + u];
+        vf[ks] = __builtin_bit_cast(bf16x8, e8);
     }
     const int prow = tid >> 3, pc = swz(prow, tid & 7);
     const float *lse = a.lse + (size_t)head * a.ldl, *dl = a.delta + (size_t)head * a.ldl;
@@ -277,39 +299,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
                 *(u32x2 *)(a.dv + (size_t)u * a.ldd + head * 64 + e) =
                     u32x2{pack2(dV[te][4 * i], dV[te][4 * i + 1]), pack2(dV[te][4 * i + 2], dV[te][4 * i + 3])};
             }
-    }
-}
-
-// one thread per (token, head)
-__global__ __launch_bounds__(256) void k_attn_delta(const uint16_t *dout, const uint16_t *o, int ld, float *delta,
-                                                    int ldl, int T, int heads) {
-    const int idx = blockIdx.x * 256 + threadIdx.x;
-    if (idx >= T * heads) return;
-    const int t = idx / heads, h = idx % heads;
-    float s = 0.f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const u32x4 x = load16(dout + (size_t)t * ld + h * 64 + c * 8), y = load16(o + (size_t)t * ld + h * 64 + c * 8);
-        const uint32_t xs[4] = {x.x, x.y, x.z, x.w}, ys[4] = {y.x, y.y, y.z, y.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-            s += bf16_to_f32(xs[q] & 0xffff) * bf16_to_f32(ys[q] & 0xffff) + bf16_to_f32(xs[q] >> 16) * bf16_to_f32(ys[q] >> 16);
-    }
-    delta[(size_t)h * ldl + t] = s;
-}
-
-// 64 x 64 tiles through LDS
-__global__ __launch_bounds__(256) void k_vt_rows(const uint16_t *vt, int ldvt, uint16_t *v, int T, int D) {
-    __shared__ uint16_t tile[64][66];
-    const int f0 = blockIdx.x * 64, t0 = blockIdx.y * 64;
-    for (int x = threadIdx.x; x < 64 * 64; x += 256) {
-        const int f = x >> 6, t = x & 63;
-        tile[f][t] = (t0 + t < T) ? vt[(size_t)(f0 + f) * ldvt + t0 + t] : 0;
-    }
-    __syncthreads();
-    for (int x = threadIdx.x; x < 64 * 64; x += 256) {
-        const int t = x >> 6, f = x & 63;
-        if (t0 + t < T) v[(size_t)(t0 + t) * D + f0 + f] = tile[f][t];
     }
 }
 
@@ -1087,19 +1076,6 @@ hipError_t launch_attention_bwd(const AttnBwdArgs &a, hipStream_t stream) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_attn_bwd_dkv<<<a.ntiles * a.heads, 512, 0, stream>>>(a);
-    return hipGetLastError();
-}
-
-hipError_t launch_attention_delta(const uint16_t *dout, const uint16_t *o, int ld, float *delta, int ldl, int T,
-                                  int heads, hipStream_t stream) {
-    if (T == 0) return hipSuccess;
-    k_attn_delta<<<(T * heads + 255) / 256, 256, 0, stream>>>(dout, o, ld, delta, ldl, T, heads);
-    return hipGetLastError();
-}
-
-hipError_t launch_vt_rows(const uint16_t *vt, int ldvt, uint16_t *v, int T, int D, hipStream_t stream) {
-    if (T == 0) return hipSuccess;
-    k_vt_rows<<<dim3(D / 64, (T + 63) / 64), 256, 0, stream>>>(vt, ldvt, v, T, D);
     return hipGetLastError();
 }
 
