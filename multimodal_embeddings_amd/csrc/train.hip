@@ -591,20 +591,21 @@ __global__ __launch_bounds__(512, 1) void k_xty256(const uint16_t *x, int ldx, c
     }
 }
 
+// four consecutive outputs per thread (M * N % 4 == 0; a group of four never straddles a 32-column block)
 __global__ __launch_bounds__(256) void k_xty_reduce(const float *partial, int splits, int M, int N, float *out,
                                                     float *out2, int deinterleave) {
-    const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t idx = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
     if (idx >= (size_t)M * N) return;
-    float s = 0.f;
-    for (int sp = 0; sp < splits; ++sp) s += partial[(size_t)sp * M * N + idx];
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int sp = 0; sp < splits; ++sp) s += *(const f32x4 *)(partial + (size_t)sp * M * N + idx);
     if (!deinterleave) {
-        out[idx] = s;
+        *(f32x4 *)(out + idx) = s;
         return;
     }
     const int m = (int)(idx / N), n = (int)(idx % N);
     const int blk = n >> 6, w = n & 63, half = N / 2;
-    if (w < 32) out[(size_t)m * half + blk * 32 + w] = s;
-    else out2[(size_t)m * half + blk * 32 + w - 32] = s;
+    if (w < 32) *(f32x4 *)(out + (size_t)m * half + blk * 32 + w) = s;
+    else *(f32x4 *)(out2 + (size_t)m * half + blk * 32 + w - 32) = s;
 }
 
 // -------------------------------------------------------------------------------- embedding and pool
@@ -1145,7 +1146,8 @@ hipError_t launch_xty(const uint16_t *x, int ldx, const uint16_t *y, int ldy, in
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t n = (size_t)M * N;
-    k_xty_reduce<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(partial, splits, M, N, out, out2, deinterleave ? 1 : 0);
+    k_xty_reduce<<<(unsigned)((n / 4 + 255) / 256), 256, 0, stream>>>(partial, splits, M, N, out, out2,
+                                                                      deinterleave ? 1 : 0);
     return hipGetLastError();
 }
 
