@@ -611,13 +611,34 @@ __global__ __launch_bounds__(256) void k_xty_reduce(const float *partial, int sp
 // -------------------------------------------------------------------------------- embedding and pool
 
 // one workgroup per byte value: its tokens' gradient rows summed in token order
-__global__ __launch_bounds__(256) void k_embed_bwd(const float *dx, const uint32_t *tok_off, const uint32_t *tok, int D,
+// One workgroup (8 waves) per byte value: wave w sums the rows of the w-th eighth of that value's tokens
+// (token order; lane l holds columns 4 l + 256 g .. + 3), then the eight partial rows are added in wave
+// order.
+__global__ __launch_bounds__(512) void k_embed_bwd(const float *dx, const uint32_t *tok_off, const uint32_t *tok, int D,
                                                    float *dE) {
-    const int v = blockIdx.x;
-    for (int i = threadIdx.x; i < D; i += 256) {
-        float s = 0.f;
-        for (uint32_t p = tok_off[v]; p < tok_off[v + 1]; ++p) s += dx[(size_t)tok[p] * D + i];
-        dE[(size_t)v * D + i] = s;
+    __shared__ __attribute__((aligned(16))) float part[8][1024];
+    const int v = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const uint32_t p0 = tok_off[v], n = tok_off[v + 1] - p0;
+    const uint32_t q0 = p0 + (uint32_t)((uint64_t)n * wave / 8), q1 = p0 + (uint32_t)((uint64_t)n * (wave + 1) / 8);
+    f32x4 acc[4] = {};
+    for (uint32_t p = q0; p < q1; ++p) {
+        const float *row = dx + (size_t)tok[p] * D;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const int c = 256 * g + 4 * lane;
+            if (c < D) acc[g] += *(const f32x4 *)(row + c);
+        }
+    }
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int c = 256 * g + 4 * lane;
+        if (c < D) *(f32x4 *)&part[wave][c] = acc[g];
+    }
+    __syncthreads();
+    for (int i = tid; i < D; i += 512) {
+        float sum = part[0][i];
+        for (int w = 1; w < 8; ++w) sum += part[w][i];
+        dE[(size_t)v * D + i] = sum;
     }
 }
 
@@ -838,11 +859,13 @@ __global__ __launch_bounds__(256) void k_pool_bwd_weights(PoolBwdArgs a, const f
             wv += a.z[((size_t)item * H + h) * D + i] * a.dpooled[(size_t)item * D + c];
         a.dwv[x] = wv;
         a.dwk[x] = du_tot[(size_t)h * D + i] * bf16_to_f32(a.query[c]) * 0.125f;
-    } else if (x < (size_t)D * D + D) {
-        const int c = (int)(x - (size_t)D * D), h = c / 64;
+    } else if (x < (size_t)D * D + (size_t)D * 64) {
+        // one wave per query column c: lane l sums rows l, l + 64, ..., then a fixed tree over the lanes
+        const int c = (int)((x - (size_t)D * D) >> 6), l = (int)(x & 63), h = c / 64;
         float dq = 0.f;
-        for (int r = 0; r < D; ++r) dq += bf16_to_f32(a.wk[(size_t)r * D + c]) * du_tot[(size_t)h * D + r];
-        a.dquery[c] = dq * 0.125f;
+        for (int r = l; r < D; r += 64) dq += bf16_to_f32(a.wk[(size_t)r * D + c]) * du_tot[(size_t)h * D + r];
+        dq = wave_sum(dq);
+        if (l == 0) a.dquery[c] = dq * 0.125f;
     }
 }
 
@@ -1153,7 +1176,8 @@ hipError_t launch_xty(const uint16_t *x, int ldx, const uint16_t *y, int ldy, in
 
 hipError_t launch_embed_bwd(const float *dx, const uint32_t *tok_off, const uint32_t *tok, int V, int D, float *dE,
                             hipStream_t stream) {
-    k_embed_bwd<<<V, 256, 0, stream>>>(dx, tok_off, tok, D, dE);
+    if (D > 1024 || D % 4) return hipErrorInvalidValue;
+    k_embed_bwd<<<V, 512, 0, stream>>>(dx, tok_off, tok, D, dE);
     return hipGetLastError();
 }
 
@@ -1181,7 +1205,7 @@ hipError_t launch_pool_bwd(const PoolBwdArgs &a, float *dz, float *pd, float *sp
     float *du_tot = dz;  // dz is free once the columns pass ran
     k_pool_bwd_du<<<(a.H * a.D + 255) / 256, 256, 0, stream>>>(a, du_tot);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const size_t n = (size_t)a.D * a.D + a.D;
+    const size_t n = (size_t)a.D * a.D + (size_t)a.D * 64;
     k_pool_bwd_weights<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a, du_tot);
     return hipGetLastError();
 }
