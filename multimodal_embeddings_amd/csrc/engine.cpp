@@ -1418,7 +1418,7 @@ TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count, size_t 
     L.pd = take(Tp * H * 2 * 4);
     L.z = take(std::max<size_t>(count, 1) * H * D * 4);
     L.du = take(std::max<size_t>(count, 1) * H * D * 4);
-    L.spa = take(std::max<size_t>(count, 1) * H * 4);
+    L.spa = take(std::max<size_t>(count, 1) * (size_t)pool_bwd_token_ranges((int)count) * H * 4);
     const size_t pchunks = (size_t)pool_bwd_chunks((int)count);
     L.zpart = take(std::max<size_t>(count, 1) * pchunks * H * D * 4);
     L.dupart = take(std::max<size_t>(count, 1) * pchunks * H * D * 4);

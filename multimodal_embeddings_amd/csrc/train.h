@@ -76,9 +76,11 @@ struct PoolBwdArgs {
     float *z, *du;        // [count x H x D] work
     float *dwv, *dwk, *dquery;  // [D x D], [D x D], [D]
 };
-// Work buffers: dz [count x H x D], pd [T x H x 2], spa [count x H], zpart and dupart [count x chunks x H x D]
-// each with chunks = pool_bwd_chunks(count). D % 8 == 0, D <= 1024, H <= 16.
+// Work buffers: dz [count x H x D], pd [T x H x 2], spa [count x ranges x H] with ranges =
+// pool_bwd_token_ranges(count), zpart and dupart [count x chunks x H x D] each with chunks =
+// pool_bwd_chunks(count). D % 8 == 0, D <= 1024, H <= 16.
 int pool_bwd_chunks(int count);
+int pool_bwd_token_ranges(int count);
 hipError_t launch_pool_bwd(const PoolBwdArgs &a, float *dz, float *pd, float *spa, float *zpart, float *dupart,
                            hipStream_t stream);
 

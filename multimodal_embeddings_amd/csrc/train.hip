@@ -667,15 +667,20 @@ __global__ __launch_bounds__(256) void k_pool_bwd_dz(PoolBwdArgs a, float *dz) {
 // 8h .. 8h + 7), and those lanes keep p_t,h and the running sum of p a (token order per wave, then the
 // waves in order).
 template <int CG>
-__global__ __launch_bounds__(512) void k_pool_bwd_tokens(PoolBwdArgs a, const float *dz, float *pd, float *spa) {
+__global__ __launch_bounds__(512) void k_pool_bwd_tokens(PoolBwdArgs a, const float *dz, float *pd, float *spa,
+                                                         int tchunks) {
     __shared__ float red[8][16];
     __shared__ float mh[16], ih[16];
-    const int item = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int item = blockIdx.x, ch = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int D = a.D, H = a.H, t0 = a.cu[item], t1 = a.cu[item + 1];
+    float *spa_out = spa + ((size_t)item * tchunks + ch) * H;  // this token range's sums of p a
     if (t1 == t0) {
-        if (tid < H) spa[(size_t)item * H + tid] = 0.f;
+        if (tid < H) spa_out[tid] = 0.f;
         return;
     }
+    // this workgroup's range of the item's tokens (statistics still over the whole item)
+    const int len = t1 - t0;
+    const int r0 = t0 + (int)((long long)len * ch / tchunks), r1 = t0 + (int)((long long)len * (ch + 1) / tchunks);
     // softmax statistics of every head
     float loc[16];
 #pragma unroll
@@ -757,15 +762,15 @@ __global__ __launch_bounds__(512) void k_pool_bwd_tokens(PoolBwdArgs a, const fl
                 v[c] = col < D ? *(const u32x4 *)(a.xf + (size_t)t * D + col) : u32x4{0u, 0u, 0u, 0u};
             }
         };
-        int t = t0 + wave;
-        for (; t + 24 < t1; t += 32) {
+        int t = r0 + wave;
+        for (; t + 24 < r1; t += 32) {
             u32x4 v[4][CG];
 #pragma unroll
             for (int k = 0; k < 4; ++k) load(t + 8 * k, v[k]);
 #pragma unroll
             for (int k = 0; k < 4; ++k) tok(t + 8 * k, v[k]);
         }
-        for (; t < t1; t += 8) {
+        for (; t < r1; t += 8) {
             u32x4 v[CG];
             load(t, v);
             tok(t, v);
@@ -776,7 +781,7 @@ __global__ __launch_bounds__(512) void k_pool_bwd_tokens(PoolBwdArgs a, const fl
         if (tid < 8 && h0 + tid < H) {
             float sum = red[0][tid];
             for (int w = 1; w < 8; ++w) sum += red[w][tid];
-            spa[(size_t)item * H + h0 + tid] = sum;
+            spa_out[h0 + tid] = sum;
         }
     }
 }
@@ -785,7 +790,8 @@ __global__ __launch_bounds__(512) void k_pool_bwd_tokens(PoolBwdArgs a, const fl
 // ds_h = p_h (a_h - spa_h) and dxf_t = sum_h (p_h dz_h + ds_h u_h); the range's partial sums of
 // z_h = sum p x and du_h = sum ds x (token order).
 __global__ __launch_bounds__(256) void k_pool_bwd_cols(PoolBwdArgs a, const float *dz, const float *pd,
-                                                       const float *spa, float *zpart, float *dupart, int chunks) {
+                                                       const float *spa, int tchunks, float *zpart, float *dupart,
+                                                       int chunks) {
     const int item = blockIdx.y, ch = blockIdx.z, i = blockIdx.x * 256 + threadIdx.x;
     const int D = a.D, H = a.H, t0 = a.cu[item], t1 = a.cu[item + 1];
     if (i >= D) return;
@@ -797,7 +803,8 @@ __global__ __launch_bounds__(256) void k_pool_bwd_cols(PoolBwdArgs a, const floa
         zv[h] = duv[h] = 0.f;
         dzv[h] = h < H ? dz[((size_t)item * H + h) * D + i] : 0.f;
         uv[h] = h < H ? a.u[(size_t)h * D + i] : 0.f;
-        sp[h] = h < H ? spa[(size_t)item * H + h] : 0.f;
+        sp[h] = 0.f;
+        for (int c = 0; c < tchunks; ++c) sp[h] += h < H ? spa[((size_t)item * tchunks + c) * H + h] : 0.f;
     }
     for (int t = c0; t < c1; ++t) {
         const float xv = bf16_to_f32(a.xf[(size_t)t * D + i]);
@@ -1182,6 +1189,7 @@ hipError_t launch_embed_bwd(const float *dx, const uint32_t *tok_off, const uint
 }
 
 int pool_bwd_chunks(int count) { return std::max(1, std::min(16, 512 / std::max(count, 1))); }
+int pool_bwd_token_ranges(int count) { return std::max(1, std::min(8, 256 / std::max(count, 1))); }
 
 hipError_t launch_pool_bwd(const PoolBwdArgs &a, float *dz, float *pd, float *spa, float *zpart, float *dupart,
                            hipStream_t stream) {
@@ -1191,13 +1199,14 @@ hipError_t launch_pool_bwd(const PoolBwdArgs &a, float *dz, float *pd, float *sp
     if (a.count > 0) {
         k_pool_bwd_dz<<<dim3((a.H * a.D + 255) / 256, a.count), 256, 0, stream>>>(a, dz);
         if ((e = hipGetLastError()) != hipSuccess) return e;
+        const int tchunks = pool_bwd_token_ranges(a.count);
         if (a.D <= 512)
-            k_pool_bwd_tokens<1><<<a.count, 512, 0, stream>>>(a, dz, pd, spa);
+            k_pool_bwd_tokens<1><<<dim3(a.count, tchunks), 512, 0, stream>>>(a, dz, pd, spa, tchunks);
         else
-            k_pool_bwd_tokens<2><<<a.count, 512, 0, stream>>>(a, dz, pd, spa);
+            k_pool_bwd_tokens<2><<<dim3(a.count, tchunks), 512, 0, stream>>>(a, dz, pd, spa, tchunks);
         if ((e = hipGetLastError()) != hipSuccess) return e;
-        k_pool_bwd_cols<<<dim3((a.D + 255) / 256, a.count, chunks), 256, 0, stream>>>(a, dz, pd, spa, zpart, dupart,
-                                                                                        chunks);
+        k_pool_bwd_cols<<<dim3((a.D + 255) / 256, a.count, chunks), 256, 0, stream>>>(a, dz, pd, spa, tchunks, zpart,
+                                                                                        dupart, chunks);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         k_pool_bwd_item_sums<<<dim3((a.H * a.D + 255) / 256, a.count), 256, 0, stream>>>(a, zpart, dupart, chunks);
         if ((e = hipGetLastError()) != hipSuccess) return e;
