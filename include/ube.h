@@ -99,7 +99,7 @@ typedef struct ube_rows_tape_view_t {
 
 /* Surfaces an encode writes ("Rust" and "Python" pages, "Encoding": Outputs);
  * OR-ed together, 0 meaning embeddings alone. States are the final-norm rows,
- * one per token; token vectors are the token head's unit rows on the same
+ * one per token; token vectors are the unit-normalised outputs of the token head, on the same
  * offsets. A surface left out costs nothing past the final norm. */
 typedef enum ube_outputs_t {
     ube_outputs_embeddings_k = 1,
@@ -191,8 +191,8 @@ void ube_model_describe(ube_model_describe_t *arguments);
 /* NULL-safe; cannot fail. Waits for nothing: the caller finishes its streams first. */
 void ube_model_free(ube_model_t model);
 
-/* An empty arena on GPU `device` ("Arenas" page, `uform_arena_init`): nothing
- * is allocated until a call writes into it. In this build the arena also holds
+/* An empty arena on GPU `device` ("Arenas" page, `uform_arena_init`): it holds
+ * no memory before the first call that writes into it. In this build the arena also holds
  * the call's activations, so an arena is the unit of concurrency. */
 typedef struct ube_arena_init_t {
     ube_arena_t *arena;
@@ -406,7 +406,7 @@ void ube_contrastive(ube_contrastive_t *arguments);
  * update reads each fp32 gradient cast to bf16 (nearest even). With activation_recomputation the
  * training forward keeps only every block's fp32 input and the backward replays each block's attention
  * half from it (the pages' memory plan: 4 * hidden bytes per token and block); without it the forward
- * keeps what the backward reads (about 16 * hidden bytes per token and block, no replay). */
+ * keeps what the backward reads (about 16 * hidden + 4 * ffn bytes per token and block, no replay). */
 typedef struct ube_trainer_handle_t *ube_trainer_t;
 
 typedef struct ube_trainer_init_t {
@@ -421,7 +421,8 @@ void ube_trainer_init(ube_trainer_init_t *arguments);
 
 /* Training forward over a byte tape: the model's forward, with the activations its backward reads kept in
  * the trainer's device memory (per block: the fp32 input; without recomputation also the fp32 rows after
- * the attention half, the rotated q|k rows, v, the attention output and its softmax denominators).
+ * the attention half, the rotated q|k rows, v, the attention output and its softmax denominators, and
+ * the gate/up pre-activations when 2 * ffn is a multiple of 256).
  * *embeddings receives the pooled fp32 rows [count x hidden] in the arena, valid until
  * the arena's next call. The kept activations serve the next ube_trainer_backward with after_forward set,
  * until a step changes the weights. */

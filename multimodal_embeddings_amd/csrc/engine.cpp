@@ -575,10 +575,11 @@ struct ArenaLease {
 struct Keep {
     float *x;         // [(N + 1) x T x D]
     float *x1;        // [N x T x D] or NULL
-    uint16_t *qk;     // [N][Tpad x 2D] or NULL (then vt, o, lse unused)
+    uint16_t *qk;     // [N][Tpad x 2D] or NULL (then vt, o, lse, gu unused)
     uint16_t *vt;     // [N][D x ldvt]
     uint16_t *o;      // [N][Tpad x D]
     float *lse;       // [N][H x ldl]
+    uint16_t *gu;     // [N][Tpad x 2F] gate/up pre-activations (interleaved as the packed weights) or NULL
     uint16_t *xf;     // [Tpad x D]
     float *s;         // [Tpad x H]
     size_t Tpad, ldvt, ldl;
@@ -783,6 +784,7 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
             if (m->e4m3) norm(x1_l, Wl.g2);
             GemmArgs ua{};
             ua.w = Wl.wgu, ua.x = h, ua.M = T, ua.N = 2 * F, ua.K = D, ua.out_bf16 = act, ua.ld_out = F;
+            if (kp && kp->gu) ua.gu_out = kp->gu + l * kp->Tpad * 2 * F, ua.ld_gu = 2 * F;
             folded_norm(ua);
             project(ube_kernel_gemm_gate_up_k, kEpiSwiglu, ua, Wl.s_gate, Wl.s_up);
             if (m->e4m3) quantize(act, F);
@@ -1314,7 +1316,7 @@ namespace {
 // Workspace of one training forward and backward over T tokens: the activations the forward keeps (k*),
 // host-built tables (cu, tiles, positions, byte -> token lists), then the backward's scratch.
 struct TrainLayout {
-    size_t kx, kx1, kqk, kvt, ko, klse, kxf, ks, kcu, ktiles, kpos, tok_off, tok;
+    size_t kx, kx1, kqk, kvt, ko, klse, kgu, kxf, ks, kcu, ktiles, kpos, tok_off, tok;
     size_t h1, h2, gu, dx, dxb, da, dgu, act, dh, dx1, dx1b, dout, dqkv, gpart, gsum, xty, dz, pd, z,
         du, spa, zpart, dupart, dxf, delta, total;
     size_t Tpad, rows_per_block;
@@ -1361,6 +1363,10 @@ struct ube_trainer_handle_t {
 
 namespace {
 
+// The forward keeps each block's gate/up pre-activations unless activations are recomputed or the
+// gate/up product is too narrow for the 256-column tiles whose epilogue can store them.
+bool keeps_gate_up(ube_geometry_t const &g, bool recompute) { return !recompute && (2 * g.ffn) % 256 == 0; }
+
 TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count, size_t ntiles, bool recompute) {
     TrainLayout L{};
     const size_t D = g.hidden, F = g.ffn, H = g.heads, N = g.depth;
@@ -1380,6 +1386,8 @@ TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count, size_t 
     L.kvt = take(NB * D * Tp * 2);
     L.ko = take(NB * Tp * D * 2);
     L.klse = take(NB * H * Tp * 4);
+    const bool kgu = keeps_gate_up(g, recompute);
+    L.kgu = take(kgu ? N * Tp * 2 * F * 2 : 0);
     L.kxf = take(Tp * D * 2);
     L.ks = take(Tp * H * 4);
     L.kcu = take((count + 1) * 4);
@@ -1390,7 +1398,7 @@ TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count, size_t 
     // backward scratch
     L.h1 = take(Tp * D * 2);
     L.h2 = take(Tp * D * 2);
-    L.gu = take(Tp * 2 * F * 2);
+    L.gu = take(kgu ? 0 : Tp * 2 * F * 2);  // rebuilt per block when not kept
     L.dx = take(Tp * D * 4);
     L.dxb = take(Tp * D * 2);
     L.da = take(Tp * F * 2);
@@ -1707,6 +1715,7 @@ void train_forward(ube_trainer_t tr, ube_arena_t arena, hipStream_t st, ube_tape
         k.x1 = (float *)(wb + L.kx1);
         k.qk = (uint16_t *)(wb + L.kqk), k.vt = (uint16_t *)(wb + L.kvt), k.o = (uint16_t *)(wb + L.ko);
         k.lse = (float *)(wb + L.klse);
+        if (keeps_gate_up(g, false)) k.gu = (uint16_t *)(wb + L.kgu);
     }
     k.Tpad = L.Tpad, k.ldvt = L.Tpad, k.ldl = L.Tpad;
     Layout EL{};
@@ -1794,7 +1803,10 @@ void train_backward(ube_trainer_t tr, hipStream_t st, float const *d_embeddings)
         }
         // the block's inputs that were not kept (v is read feature-major, as kept)
         UBE_HIP(launch_rmsnorm(x1, TT[b.g2].w32, h2, Ti, Di, eps, st));
-        gemm(kEpiStore, b.guT, h2, Ti, 2 * Fi, Di, gu, 2 * Fi, nullptr, 0, st);
+        if (!keeps_gate_up(g, tr->recompute))
+            gemm(kEpiStore, b.guT, h2, Ti, 2 * Fi, Di, gu, 2 * Fi, nullptr, 0, st);
+        else
+            gu = B16(L.kgu) + li * Tp * 2 * F;  // kept by the forward's gate/up product
         // MLP half
         float *dx = F32(L.dx), *dh = F32(L.dh), *dx1 = F32(L.dx1);
         uint16_t *dxb = B16(L.dxb), *da = B16(L.da), *dgu = B16(L.dgu), *act = B16(L.act), *dx1b = B16(L.dx1b);

@@ -32,6 +32,8 @@ struct GemmArgs {
     float *out_f32;
     int ld_f32;
     const float *res_in;  // residual: x read from here (ld_f32) and x + acc written to out_f32; NULL: in place
+    uint16_t *gu_out;     // SwiGLU: when set, also the bf16 pre-activations [M x N] (interleaved as the product)
+    int ld_gu;
     uint16_t *vt;
     int ld_vt;
     const int16_t *pos;   // [M_alloc x 4] rotary coordinates per token

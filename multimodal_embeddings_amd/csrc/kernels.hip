@@ -1020,6 +1020,35 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
             const u32x4 v = *(const u32x4 *)(L + t * kGluPitch + ch * 16);
             if (m < a.M) __builtin_nontemporal_store(v, (u32x4 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 / 2 + ch * 8));
         }
+        if (a.gu_out) {
+            // the pre-activations themselves (g, u in the interleaved column order of the product), for
+            // a backward pass: 512-byte rows through LDS like the plain store
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            lds_barrier();
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) {
+                const int t = wm * 128 + tm * 32 + l32;
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn) {
+                    const float k = fac[tm] * (tn ? su : sg);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int c = wn * 64 + tn * 32 + i * 8 + hh * 4;
+                        *(u32x2 *)(L + t * kQkPitch + c * 2) =
+                            u32x2{pack2(acc[tn][tm][i * 4] * k, acc[tn][tm][i * 4 + 1] * k),
+                                  pack2(acc[tn][tm][i * 4 + 2] * k, acc[tn][tm][i * 4 + 3] * k)};
+                    }
+                }
+            }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            lds_barrier();
+#pragma unroll
+            for (int it = 0; it < 16; ++it) {
+                const int t = it * 16 + wave * 2 + hh, m = m0 + t;
+                const u32x4 v = *(const u32x4 *)(L + t * kQkPitch + l32 * 16);
+                if (m < a.M) __builtin_nontemporal_store(v, (u32x4 *)(a.gu_out + (size_t)m * a.ld_gu + n0 + l32 * 8));
+            }
+        }
     } else {
         // ---- residual / patch: four slices of 64 tokens (slice s = tile tokens
         // [64 s, 64 s + 64), held by the waves with wm = s / 2 at tm = 2 (s % 2) +
@@ -1129,6 +1158,7 @@ hipError_t launch_gemm(int epi, const GemmArgs &a, hipStream_t stream) {
     if (a.M == 0) return hipSuccess;
     if (a.N % 128 != 0 || a.K % 64 != 0) return hipErrorInvalidValue;
     if (a.N % 256 == 0) return gemm256_dispatch<false>(epi, a, stream);
+    if (a.gu_out) return hipErrorInvalidValue;  // only the 256-column tiles store pre-activations
     return gemm_dispatch<256, 128>(epi, a, stream);
 }
 

@@ -13,8 +13,8 @@ TEST INFRASTRUCTURE ONLY: imported by the tests, ``__graft_entry__.smoke`` and t
   differences).
 * ``adafactor``: one Adafactor update ("UForm" page, "Adafactor Optimizer" and "Precision by Design")
   of the gradient cast to bf16: factored second moment (row and column means of g^2 + eps1, decayed by beta2_t = 1 - t^decay) for
-  matrices, an unfactored one for vectors; update u = g / sqrt(v) clipped to RMS <= d; first moment of
-  the clipped update with Adam's bias correction; w -= lr * m_hat. Written from Shazeer and Stern's
+  matrices, an unfactored one for vectors; update u = g / sqrt(v) clipped to RMS <= d; a running mean
+  m of the clipped u, bias-corrected as Adam does; w -= lr * m_hat. Written from Shazeer and Stern's
   published algorithm (Adafactor, 2018), with the first moment the pages add.
 """
 from __future__ import annotations
