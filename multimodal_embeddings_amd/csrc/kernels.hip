@@ -155,59 +155,88 @@ __global__ __launch_bounds__(256) void k_rmsnorm(const float *__restrict__ x, co
     }
 }
 
-template <int V, int C>
+// Final RMSNorm and pool scores, R rows per wave at a time: the R rows' loads are
+// in flight together and their reductions interleave, so a wave is not left
+// waiting on one row's load and one row's chain of cross-lane steps at a time.
+// Pool scores s[t][h] = xf_t . u_h for up to HP heads, the per-lane partial dots of
+// all heads reduced across lanes together (lanes_reduce); each u value read from
+// LDS serves all R rows.
+template <int V, int C, int HP>
 __global__ __launch_bounds__(256) void k_final_norm_scores(const float *__restrict__ x, const float *__restrict__ gain,
                                                            const float *__restrict__ u, uint16_t *__restrict__ xf,
                                                            float *__restrict__ s, float *__restrict__ states, int T,
                                                            int D, int H, float eps) {
+    constexpr int R = 4;
     extern __shared__ float su[];  // u [H x D]
     for (int i = threadIdx.x; i < H * D; i += 256) su[i] = u[i];
     __syncthreads();
     const int lane = threadIdx.x & 63;
     const int waves = gridDim.x * 4;
-    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += waves) {
-        float v[C][V];
-        float ss = 0.f;
+    float g[C][V];
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            RowIO<V>::load_f32(x + (size_t)t * D + c * 64 * V + lane * V, v[c]);
+    for (int c = 0; c < C; ++c)
 #pragma unroll
-            for (int i = 0; i < V; ++i) ss += v[c][i] * v[c][i];
+        for (int i = 0; i < V; ++i) g[c][i] = gain[c * 64 * V + lane * V + i];
+    for (int t0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * R; t0 < T; t0 += waves * R) {
+        float v[R][C][V], ss[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            ss[r] = 0.f;
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                if (t0 + r < T) {
+                    RowIO<V>::load_f32(x + (size_t)(t0 + r) * D + c * 64 * V + lane * V, v[r][c]);
+                } else {
+#pragma unroll
+                    for (int i = 0; i < V; ++i) v[r][c][i] = 0.f;
+                }
+#pragma unroll
+                for (int i = 0; i < V; ++i) ss[r] += v[r][c][i] * v[r][c][i];
+            }
         }
-        ss = wave_sum(ss);
-        const float inv = 1.0f / sqrtf(ss / (float)D + eps);
 #pragma unroll
-        for (int c = 0; c < C; ++c) {
-            const int f = c * 64 * V + lane * V;
+        for (int m = 32; m >= 1; m >>= 1)
 #pragma unroll
-            for (int i = 0; i < V; ++i) v[c][i] = v[c][i] * inv * gain[f + i];
-            RowIO<V>::store_bf16(xf + (size_t)t * D + f, v[c]);
-            if (states) RowIO<V>::store_f32(states + (size_t)t * D + f, v[c]);
+            for (int r = 0; r < R; ++r) ss[r] += __shfl_xor(ss[r], m, 64);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const float inv = 1.0f / sqrtf(ss[r] / (float)D + eps);
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const int f = c * 64 * V + lane * V;
+#pragma unroll
+                for (int i = 0; i < V; ++i) v[r][c][i] = v[r][c][i] * inv * g[c][i];
+                if (t0 + r < T) {
+                    RowIO<V>::store_bf16(xf + (size_t)(t0 + r) * D + f, v[r][c]);
+                    if (states) RowIO<V>::store_f32(states + (size_t)(t0 + r) * D + f, v[r][c]);
+                }
+            }
         }
-        // pool scores of up to 16 heads reduced together (lanes_reduce)
-        float dots[16];
+        float dots[R][HP];
 #pragma unroll
-        for (int hd = 0; hd < 16; ++hd) {
-            float dot = 0.f;
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int hd = 0; hd < HP; ++hd) dots[r][hd] = 0.f;
+#pragma unroll
+        for (int hd = 0; hd < HP; ++hd) {
             if (hd < H) {
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
                     const int f = c * 64 * V + lane * V;
 #pragma unroll
-                    for (int i = 0; i < V; ++i) dot += v[c][i] * su[hd * D + f + i];
+                    for (int i = 0; i < V; ++i) {
+                        const float uv = su[hd * D + f + i];
+#pragma unroll
+                        for (int r = 0; r < R; ++r) dots[r][hd] += v[r][c][i] * uv;
+                    }
                 }
             }
-            dots[hd] = dot;
         }
-        if (H <= 8) {
-            float d8[8];
+        constexpr int LPH = 64 / HP;  // lanes per head after the reduction
 #pragma unroll
-            for (int hd = 0; hd < 8; ++hd) d8[hd] = dots[hd];
-            const float tot = lanes_reduce<8>(d8, lane);
-            if ((lane & 7) == 0 && (lane >> 3) < H) s[(size_t)t * H + (lane >> 3)] = tot;
-        } else {
-            const float tot = lanes_reduce<16>(dots, lane);
-            if ((lane & 3) == 0 && (lane >> 2) < H) s[(size_t)t * H + (lane >> 2)] = tot;
+        for (int r = 0; r < R; ++r) {
+            const float tot = lanes_reduce<HP>(dots[r], lane);
+            if (t0 + r < T && lane % LPH == 0 && lane / LPH < H) s[(size_t)(t0 + r) * H + lane / LPH] = tot;
         }
     }
 }
@@ -365,13 +394,19 @@ hipError_t launch_final_norm_scores(const float *x, const float *gain, const flo
                                     float *states, int T, int D, int H, float eps, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const size_t lds = (size_t)H * D * sizeof(float);
-    UBE_ROW_DISPATCH(D, {
+    // four rows per wave: a quarter of the row kernels' grid
+    const int grid = row_grid((T + 3) / 4);
+    auto run = [&](auto kernel) -> hipError_t {
         if (lds > 65536) {
-            hipError_t e = hipFuncSetAttribute((const void *)k_final_norm_scores<V, C>,
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+            hipError_t e = hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
         }
-        k_final_norm_scores<V, C><<<row_grid(T), 256, lds, stream>>>(x, gain, u, xf, s, states, T, D, H, eps);
+        kernel<<<grid, 256, lds, stream>>>(x, gain, u, xf, s, states, T, D, H, eps);
+        return hipSuccess;
+    };
+    UBE_ROW_DISPATCH(D, {
+        const hipError_t e = H <= 8 ? run(k_final_norm_scores<V, C, 8>) : run(k_final_norm_scores<V, C, 16>);
+        if (e != hipSuccess) return e;
     });
     return hipGetLastError();
 }
@@ -1574,13 +1609,17 @@ __global__ __launch_bounds__(256) void k_pool(const uint16_t *__restrict__ xf, c
 // The same pool for D <= 512 and H <= 8 with the token sum spread over the workgroup: 8 waves, wave w
 // taking tokens t0 + w, t0 + w + 8, ...; lane l holds columns 8 l .. 8 l + 7 (one 16-byte load of xf per
 // token, four tokens in flight) and the partial z of every head; the waves' partials are added in wave
-// order through LDS. Softmax statistics by a fixed tree over the threads. One item's tokens are never
-// read twice and no thread walks the whole item alone.
+// order through LDS. Softmax statistics by a fixed tree over the threads; the weights p of every head are
+// then formed once per token, a chunk of tokens at a time, into LDS, where the token loop reads them as
+// broadcasts (no global load and no exponential inside it). One item's tokens are never read twice and
+// no thread walks the whole item alone.
 __global__ __launch_bounds__(512) void k_pool_wide(const uint16_t *__restrict__ xf, const float *__restrict__ s,
                                                    const int *__restrict__ cu, const uint16_t *__restrict__ wv,
                                                    void *__restrict__ out, int out_bf16, size_t out_stride, int D,
                                                    int H) {
+    constexpr int kChunk = 1024;  // tokens whose weights sit in LDS at a time
     __shared__ float z[8 * 512];
+    __shared__ __attribute__((aligned(16))) float pw[kChunk][8];
     __shared__ float red[8][8];
     __shared__ float mh[8], ih[8];
     const int item = blockIdx.x, t0 = cu[item], t1 = cu[item + 1];
@@ -1631,9 +1670,6 @@ __global__ __launch_bounds__(512) void k_pool_wide(const uint16_t *__restrict__ 
         ih[tid] = 1.0f / sum;
     }
     __syncthreads();
-    float m8[8], i8[8];
-#pragma unroll
-    for (int hd = 0; hd < 8; ++hd) m8[hd] = hd < H ? mh[hd] : 0.f, i8[hd] = hd < H ? ih[hd] : 0.f;
     // z_h partials of this wave's tokens
     const bool on = 8 * lane < D;
     float zacc[8][8];
@@ -1641,10 +1677,10 @@ __global__ __launch_bounds__(512) void k_pool_wide(const uint16_t *__restrict__ 
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int hd = 0; hd < 8; ++hd) zacc[i][hd] = 0.f;
+    int c0 = t0;  // first token of the chunk whose weights are in pw
     auto add = [&](int t, u32x4 v) {
-        float p[8];
-#pragma unroll
-        for (int hd = 0; hd < 8; ++hd) p[hd] = hd < H ? __expf(s[(size_t)t * H + hd] - m8[hd]) * i8[hd] : 0.f;
+        const f32x4 pa = *(const f32x4 *)&pw[t - c0][0], pb = *(const f32x4 *)&pw[t - c0][4];
+        const float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1656,19 +1692,28 @@ __global__ __launch_bounds__(512) void k_pool_wide(const uint16_t *__restrict__ 
             }
         }
     };
-    int t = t0 + wave;
-    for (; t + 24 < t1; t += 32) {
-        u32x4 v[4] = {};
+    for (; c0 < t1; c0 += kChunk) {
+        const int c1 = min(t1, c0 + kChunk);
+        if (c0 > t0) __syncthreads();  // every wave is done with the previous chunk's weights
+        for (int i = tid; i < (c1 - c0) * 8; i += 512) {
+            const int tt = i >> 3, hd = i & 7;
+            pw[tt][hd] = hd < H ? __expf(s[(size_t)(c0 + tt) * H + hd] - mh[hd]) * ih[hd] : 0.f;
+        }
+        __syncthreads();
+        int t = c0 + wave;
+        for (; t + 24 < c1; t += 32) {
+            u32x4 v[4] = {};
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-            if (on) v[k] = *(const u32x4 *)(xf + (size_t)(t + 8 * k) * D + 8 * lane);
+            for (int k = 0; k < 4; ++k)
+                if (on) v[k] = *(const u32x4 *)(xf + (size_t)(t + 8 * k) * D + 8 * lane);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) add(t + 8 * k, v[k]);
-    }
-    for (; t < t1; t += 8) {
-        u32x4 v = {};
-        if (on) v = *(const u32x4 *)(xf + (size_t)t * D + 8 * lane);
-        add(t, v);
+            for (int k = 0; k < 4; ++k) add(t + 8 * k, v[k]);
+        }
+        for (; t < c1; t += 8) {
+            u32x4 v = {};
+            if (on) v = *(const u32x4 *)(xf + (size_t)t * D + 8 * lane);
+            add(t, v);
+        }
     }
     // partials added in wave order
     for (int w = 0; w < 8; ++w) {
