@@ -37,8 +37,18 @@ __device__ __forceinline__ bf16x8 join(s16x4 lo, s16x4 hi) {
     return __builtin_bit_cast(bf16x8, v);
 }
 
+// Tiles of 128-byte rows that are read both along their rows (16-byte reads) and down them (transpose
+// reads): the 16-byte chunks of row r are XOR-swizzled by m ^ 4 (m % 2), m = (r / 2) % 8. That is a
+// permutation of 0..7, so 16 consecutive rows read at one logical chunk hit 16 distinct bank groups, and
+// the four rows 4j .. 4j + 3 that one transpose read covers (8 bytes from each of four chunks per row)
+// land in four distinct 64-byte bank ranges: no bank conflicts either way.
+__device__ __forceinline__ int swzb(int row, int ch) {
+    const int m = (row >> 1) & 7;
+    return ch ^ m ^ ((m & 1) << 2);
+}
+
 // MFMA A operand whose k runs down the rows of an LDS tile [rows][64 bf16] (128-byte rows, 16-byte chunks
-// swizzled by swz): lane l receives column c0 + l % 32 at the 8 k slots of half hh = l / 32, slot q being
+// swizzled by swzb): lane l receives column c0 + l % 32 at the 8 k slots of half hh = l / 32, slot q being
 // row kb + 4 hh + (q % 4) + 8 (q / 4) -- the order in which a 32x32 MFMA result holds its rows in
 // registers 8s .. 8s + 7 (kb = 16 s), so such an accumulator, packed to bf16, is the matching B operand.
 // ds_read_b64_tr_b16: lane i = 4a + b of a 16-lane group receives element b of the 8 bytes read by lanes
@@ -48,8 +58,8 @@ __device__ __forceinline__ bf16x8 tr_rows_frag(const uint8_t *tile, int kb, int 
     const int col = c0 + 16 * (g & 1) + 4 * (i & 3);
     const int chunk = col >> 3, half = (col >> 2) & 1;
     const int r0 = kb + 4 * hh + (i >> 2), r1 = r0 + 8;
-    const uint8_t *p0 = tile + r0 * 128 + (swz(r0, chunk) << 4) + (half << 3);
-    const uint8_t *p1 = tile + r1 * 128 + (swz(r1, chunk) << 4) + (half << 3);
+    const uint8_t *p0 = tile + r0 * 128 + (swzb(r0, chunk) << 4) + (half << 3);
+    const uint8_t *p1 = tile + r1 * 128 + (swzb(r1, chunk) << 4) + (half << 3);
     return join(tr16(p0), tr16(p1));
 }
 
@@ -85,7 +95,7 @@ __device__ __forceinline__ u32x4 load16(const uint16_t *p) { return *(const u32x
 // 2^(log2(e) s - lse) from the forward's base-2 log denominators; dP = dO V^T; dS = P (dP - delta) with
 // delta = rowsum(dO O); dQ = dS K / 8, dK = dS^T Q / 8, dV = P^T dO.
 // Two kernels, 8 waves x 32 rows per workgroup (one 256-token tile of one item and head), 64-row tiles of
-// the other side double-buffered in LDS by DMA (16-byte chunks swizzled by swz):
+// the other side double-buffered in LDS by DMA (16-byte chunks swizzled by swzb; V^T by kmajor_swz):
 //   dQ: S^T = K Q^T and dP^T = V dO^T (a lane holds one query and 16 keys), dQ^T += K^T dS^T;
 //   dK, dV: S = Q K^T and dP = dO V^T (a lane holds one key and 16 queries), dV^T += dO^T P,
 //           dK^T += Q^T dS.
@@ -135,7 +145,7 @@ __global__ __launch_bounds__(512, 4) void k_attn_bwd_dq(AttnBwdArgs a) {
     dlt += __shfl_xor(dlt, 32, 64);
     if (hh == 0 && qvalid) a.delta[(size_t)head * a.ldl + t] = dlt;
     const float lse2 = a.lse[(size_t)head * a.ldl + t];
-    const int prow = tid >> 3, pc = swz(prow, tid & 7), pv = (tid & 7) ^ kmajor_swz<128>(prow);
+    const int prow = tid >> 3, pc = swzb(prow, tid & 7), pv = (tid & 7) ^ kmajor_swz<128>(prow);
     // K tile: 64 key rows of the head's 64 features; V^T tile: the head's 64 feature rows of vt over the
     // tile's 64 keys (k-major for dP^T = V dO^T, read with the transpose load). Keys past the item read
     // other items' values or the zeroed band after the last token: finite, and weighted 0.
@@ -162,7 +172,7 @@ __global__ __launch_bounds__(512, 4) void k_attn_bwd_dq(AttnBwdArgs a) {
             const int row = kk * 32 + l32;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const int ch = swz(row, ks * 2 + hh);
+                const int ch = swzb(row, ks * 2 + hh);
                 S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sK[row * 8 + ch]), qf[ks], S, 0, 0, 0);
                 dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<128>((const uint8_t *)sVt, 16 * ks, 32 * kk, lane),
                                                              dof[ks], dP, 0, 0, 0);
@@ -222,7 +232,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
         for (int e = 0; e < 8; ++e) e8[e] = a.vt[(size_t)(head * 64 + ks * 16 + hh * 8 + e) * a.ldvt + u];
         vf[ks] = __builtin_bit_cast(bf16x8, e8);
     }
-    const int prow = tid >> 3, pc = swz(prow, tid & 7);
+    const int prow = tid >> 3, pc = swzb(prow, tid & 7);
     const float *lse = a.lse + (size_t)head * a.ldl, *dl = a.delta + (size_t)head * a.ldl;
     auto issue = [&](int tt, int buf) {
         const int row = min(k0 + tt * 64 + prow, k1 - 1);
@@ -252,7 +262,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
             const int row = qq * 32 + l32;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
-                const int ch = swz(row, ks * 2 + hh);
+                const int ch = swzb(row, ks * 2 + hh);
                 S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sQ[row * 8 + ch]), kf[ks], S, 0, 0, 0);
                 dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sO[row * 8 + ch]), vf[ks], dP, 0, 0,
                                                              0);
