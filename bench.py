@@ -391,7 +391,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported in this build "
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(items are independent; a multi-GPU run would shard the tape by items)", file=sys.stderr)
         sys.exit(2)
 

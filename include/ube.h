@@ -48,7 +48,7 @@ typedef enum ube_status_t {
     ube_status_out_of_memory_k = 3,    /* the GPU could not grow the arena; no host fallback */
     ube_status_device_k = 4,           /* arena and model on different devices, or a HIP runtime failure */
     ube_status_contended_k = 5,        /* the arena is serving another call */
-    ube_status_unsupported_k = 6,      /* a geometry or mode this build does not run */
+    ube_status_unsupported_k = 6,      /* a geometry or mode the library does not run */
     ube_status_internal_k = 7,
 } ube_status_t;
 
@@ -192,7 +192,7 @@ void ube_model_describe(ube_model_describe_t *arguments);
 void ube_model_free(ube_model_t model);
 
 /* An empty arena on GPU `device` ("Arenas" page, `uform_arena_init`): it holds
- * no memory before the first call that writes into it. In this build the arena also holds
+ * no memory before the first call that writes into it. Here the arena also holds
  * the call's activations, so an arena is the unit of concurrency. */
 typedef struct ube_arena_init_t {
     ube_arena_t *arena;
