@@ -21,12 +21,12 @@
  *     ragged inputs are Arrow tapes with count+1 offsets in host memory.
  *   - "Rust" and "Python" pages, "Encoding": `text_encode` takes a tape, a byte per
  *     token; `image_encode_pixels` takes interleaved 8-bit RGB with per-item
- *     heights and widths; outputs are f32 by default or bf16; stats report the
- *     truncated items and the encoded tokens.
+ *     heights and widths; outputs are f32 by default or bf16; stats count the
+ *     items that were cut short and the tokens that were encoded.
  *   - "Python" page, "Errors": the status codes.
  *
- * Threading: calls on different arenas may run concurrently; an arena serves one
- * call at a time (a second concurrent call reports `contended`). All device work
+ * Threading: calls on different arenas may run concurrently; one arena takes a
+ * single call at once (a second, overlapping call reports `contended`). All device work
  * of a call is enqueued on the caller's HIP stream (`stream`, a hipStream_t; NULL
  * is the null stream).
  */
@@ -85,8 +85,8 @@ typedef struct ube_rows_view_t {
     ube_scalar_t scalar;
 } ube_rows_view_t;
 
-/* Ragged output rows ("Arenas" page, "Rows and Tapes": packed rows and one
- * more offset than items): item i owns rows offsets[i] .. offsets[i+1]; row r
+/* Ragged output rows ("Arenas" page, "Rows and Tapes": rows packed back to back,
+ * count + 1 offsets): item i owns rows offsets[i] .. offsets[i+1]; row r
  * starts at (char*)data + r*stride and holds `columns` values of `scalar`;
  * `rows` = offsets[count]. Written by an encode, data and offsets are device
  * memory inside the arena, valid until the next call naming that arena. */
@@ -318,7 +318,7 @@ typedef struct ube_maxsim_t {
 } ube_maxsim_t;
 void ube_maxsim(ube_maxsim_t *arguments);
 
-/* Which pairs the contrastive loss pushes apart ("Training" page, uform_negatives_t): ambient repels
+/* Negative pairs of the contrastive loss ("Training" page, uform_negatives_t): ambient repels
  * every pair no edge names at `ambient_repulsion_weight` (and the named repel edges); named repels the
  * repel edges alone. */
 typedef enum ube_negatives_t {
