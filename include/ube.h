@@ -400,8 +400,8 @@ void ube_contrastive(ube_contrastive_t *arguments);
  *
  * A trainer keeps bf16 master weights (fp32 for the norm gains) in the canonical layout of ube_weights_t,
  * their fp32 gradients and the Adafactor state, and refreshes the model's forward weights after every
- * step (so encodes on the model see the updated weights). Text models in bf16 with 1-axis rotary and
- * hidden a multiple of 128 up to 1024 (unsupported otherwise). Adafactor: beta1 [0.9], decay_rate [-0.8] (beta2_t = 1 -
+ * step (so encodes on the model see the updated weights). Text models in bf16 with 1-axis rotary,
+ * hidden a multiple of 128 up to 1024 and ffn a multiple of 128 (unsupported otherwise). Adafactor: beta1 [0.9], decay_rate [-0.8] (beta2_t = 1 -
  * t^decay_rate), epsilon1 [1e-30], clip_threshold [1]; zero fields take the defaults in brackets; the
  * update reads each fp32 gradient cast to bf16 (nearest even). With activation_recomputation the
  * training forward keeps only every block's fp32 input and the backward replays each block's attention
@@ -422,7 +422,7 @@ void ube_trainer_init(ube_trainer_init_t *arguments);
 /* Training forward over a byte tape: the model's forward, with the activations its backward reads kept in
  * the trainer's device memory (per block: the fp32 input; without recomputation also the fp32 rows after
  * the attention half, the rotated q|k rows, v, the attention output and its softmax denominators, and
- * the gate/up pre-activations when 2 * ffn is a multiple of 256).
+ * the gate/up pre-activations).
  * *embeddings receives the pooled fp32 rows [count x hidden] in the arena, valid until
  * the arena's next call. The kept activations serve the next ube_trainer_backward with after_forward set,
  * until a step changes the weights. */

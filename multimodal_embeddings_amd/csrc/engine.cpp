@@ -1363,8 +1363,8 @@ struct ube_trainer_handle_t {
 
 namespace {
 
-// The forward keeps each block's gate/up pre-activations unless activations are recomputed or the
-// gate/up product is too narrow for the 256-column tiles whose epilogue can store them.
+// The forward keeps each block's gate/up pre-activations unless activations are recomputed (a trainer's
+// ffn is a multiple of 128, so the gate/up product always runs on the 256-column tiles that store them).
 bool keeps_gate_up(ube_geometry_t const &g, bool recompute) { return !recompute && (2 * g.ffn) % 256 == 0; }
 
 TrainLayout train_carve(ube_geometry_t const &g, size_t T, size_t count, size_t ntiles, bool recompute) {
@@ -1463,8 +1463,8 @@ extern "C" void ube_trainer_init(ube_trainer_init_t *a) {
         if (!m->text) throw Failure{ube_status_unsupported_k, "training runs text models"};
         if (m->e4m3) throw Failure{ube_status_unsupported_k, "training runs bf16 models (E4M3 is inference-only)"};
         if (g.rope_axes != 1) throw Failure{ube_status_unsupported_k, "training runs 1-axis rotary"};
-        if (g.hidden > 1024 || g.hidden % 128 || g.heads > 16)
-            throw Failure{ube_status_unsupported_k, "training runs hidden <= 1024, a multiple of 128"};
+        if (g.hidden > 1024 || g.hidden % 128 || g.heads > 16 || g.ffn % 128)
+            throw Failure{ube_status_unsupported_k, "training runs hidden <= 1024 and ffn, multiples of 128"};
         ube_weights_t const &w = *a->weights;
         if (!w.embed || !w.w_qkv || !w.w_o || !w.w_gate || !w.w_up || !w.w_down || !w.attn_norm || !w.mlp_norm ||
             !w.final_norm || !w.pool_query || !w.pool_wk || !w.pool_wv)

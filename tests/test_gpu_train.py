@@ -93,6 +93,18 @@ def test_backward_edge_cases(ube):
     assert all(float(gr.abs().max()) == 0.0 for _, _, _, gr in trainer.tensors())
 
 
+def test_trainer_refuses_unsupported_geometry(ube):
+    """A model the encoder runs (ffn 320, a multiple of 64) but whose activation-gradient products the
+    trainer's 128-column tiles cannot cover: the trainer reports unsupported instead of failing later."""
+    g = dict(configs.geometry("tiny"))
+    g["ffn"] = 320
+    w = synth.make_weights(g)
+    model = ube.Model(w, 0)
+    with pytest.raises(ube.UbeError) as e:
+        ube.Trainer(model, w)
+    assert e.value.status == "unsupported", e.value
+
+
 def test_adafactor_step_and_refreshed_forward(ube):
     import torch
     g, w, batch, model, trainer, arena = _setup(ube, "tiny")
