@@ -26,7 +26,6 @@ namespace {
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 
-constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ s16x4 tr16(const uint8_t *p) {
     return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)p);
@@ -255,7 +254,6 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
         if (tt + 1 < ntile) issue(tt + 1, (tt + 1) & 1);
         if (!active) continue;
         const u32x4 *sQ = smem + (tt & 1) * 1024, *sO = sQ + 512;
-        const int tq = k0 + tt * 64;
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
             f32x16 S = f32x16{}, dP = f32x16{};
