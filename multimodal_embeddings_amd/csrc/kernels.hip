@@ -1207,8 +1207,9 @@ hipError_t launch_gemm_e4m3(int epi, const GemmArgs &a, hipStream_t stream) {
 //
 // Bidirectional attention inside each item (varlen, tiles from the tape's
 // prefix sums). Workgroup = (query tile of 256 tokens of one item, head), 8
-// waves of 32 queries; key tiles of 64 keys staged in LDS by DMA, four stages
-// (three in flight), one barrier per tile. Per key tile:
+// waves of 32 queries; key tiles of 64 keys staged in LDS by DMA in four
+// buffers taken a pair of tiles at a time, one barrier per pair (the next pair
+// loads while this one is computed). Per key tile:
 //   S^T (keys x queries) = K Q^T   -- each lane keeps one query and 32 of its
 //                                      scores; the row max needs one exchange
 //                                      between the two lane halves
@@ -1354,20 +1355,20 @@ __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict
     };
 
     const int ntile = (k1 - k0 + 63) >> 6;
-#pragma unroll
-    for (int s = 0; s < NS - 1; ++s)
-        if (s < ntile) issue(s);
-    for (int t = 0; t < ntile; ++t) {
-        // stage t landed for every wave, and every wave is done with stage t-1,
-        // whose buffer receives stage t + NS - 1
-        const int after = min(ntile - 1, t + NS - 2) - t;  // stages in flight behind t
-        if (after >= 2) asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else if (after == 1) asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
-        else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    // key tiles in pairs, one barrier per pair: the barrier publishes both tiles of the pair and
+    // retires every wave's reads of the previous pair, whose two buffers then receive the next pair
+    if (0 < ntile) issue(0);
+    if (1 < ntile) issue(1);
+    for (int t = 0; t < ntile; t += 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         lds_barrier();
-        if (t + NS - 1 < ntile) issue(t + NS - 1);
-        if (active) compute(smem + (t % NS) * STAGE, k0 + t * 64, t == 0);
+        if (t + 2 < ntile) issue(t + 2);
+        if (t + 3 < ntile) issue(t + 3);
+        if (active) {
+            compute(smem + (t % NS) * STAGE, k0 + t * 64, t == 0);
+            if (t + 1 < ntile) compute(smem + ((t + 1) % NS) * STAGE, k0 + (t + 1) * 64, false);
+        }
     }
 
     const float l_tot = l_run + __shfl_xor(l_run, 32, 64);
