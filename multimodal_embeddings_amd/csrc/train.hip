@@ -112,7 +112,7 @@ __device__ __forceinline__ void unrotate4(float (&g)[4], f32x4 cs) {
 }
 
 __global__ __launch_bounds__(512, 4) void k_attn_bwd_dq(AttnBwdArgs a) {
-    __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * 1024];  // stage: K tile 512 | V tile 512 chunks
+    __shared__ __attribute__((aligned(1024))) u32x4 smem[4 * 1024];  // stage: K tile 512 | V tile 512 chunks
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int head = logical / a.ntiles, ti = logical % a.ntiles;
     const int2 tile = a.tiles[ti];
@@ -156,14 +156,19 @@ __global__ __launch_bounds__(512, 4) void k_attn_bwd_dq(AttnBwdArgs a) {
     };
     f32x16 dQ[2] = {f32x16{}, f32x16{}};
     const int ntile = (k1 - k0 + 63) >> 6;
+    // key tiles in pairs over four buffers: one barrier per pair publishes both tiles and retires every
+    // wave's reads of the previous pair, whose buffers then receive the next pair
     issue(0, 0);
-    for (int tt = 0; tt < ntile; ++tt) {
+    if (1 < ntile) issue(1, 1);
+    for (int tp = 0; tp < ntile; tp += 2) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-        lds_barrier();  // tile tt landed for every wave; every wave is done with tile tt - 1
-        if (tt + 1 < ntile) issue(tt + 1, (tt + 1) & 1);
+        lds_barrier();
+        if (tp + 2 < ntile) issue(tp + 2, (tp + 2) & 3);
+        if (tp + 3 < ntile) issue(tp + 3, (tp + 3) & 3);
         if (!active) continue;
-        const u32x4 *sK = smem + (tt & 1) * 1024, *sVt = sK + 512;
+        for (int tt = tp; tt < min(tp + 2, ntile); ++tt) {
+        const u32x4 *sK = smem + (tt & 3) * 1024, *sVt = sK + 512;
         const int kt = k0 + tt * 64;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -192,6 +197,7 @@ __global__ __launch_bounds__(512, 4) void k_attn_bwd_dq(AttnBwdArgs a) {
                         tr_rows_frag((const uint8_t *)sK, kk * 32 + 16 * s, 32 * te, lane), b, dQ[te], 0, 0, 0);
             }
         }
+        }
     }
     if (active && qvalid) {
         const float2 *rb = a.rope ? a.rope + (int)a.pos[(size_t)t * 4] * 32 : nullptr;
@@ -210,8 +216,8 @@ __global__ __launch_bounds__(512, 4) void k_attn_bwd_dq(AttnBwdArgs a) {
 }
 
 __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
-    __shared__ __attribute__((aligned(1024))) u32x4 smem[2 * 1024];  // stage: Q tile 512 | dO tile 512 chunks
-    __shared__ __attribute__((aligned(16))) float sld[2][2][64];     // stage: lse, delta of the tile's queries
+    __shared__ __attribute__((aligned(1024))) u32x4 smem[4 * 1024];  // stage: Q tile 512 | dO tile 512 chunks
+    __shared__ __attribute__((aligned(16))) float sld[4][2][64];     // stage: lse, delta of the tile's queries
     const int logical = xcd_remap(blockIdx.x, gridDim.x);
     const int head = logical / a.ntiles, ti = logical % a.ntiles;
     const int2 tile = a.tiles[ti];
@@ -246,14 +252,18 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
     };
     f32x16 dK[2] = {f32x16{}, f32x16{}}, dV[2] = {f32x16{}, f32x16{}};
     const int ntile = (k1 - k0 + 63) >> 6;
+    // query tiles in pairs over four buffers, one barrier per pair (as in the dQ kernel)
     issue(0, 0);
-    for (int tt = 0; tt < ntile; ++tt) {
+    if (1 < ntile) issue(1, 1);
+    for (int tp = 0; tp < ntile; tp += 2) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         lds_barrier();
-        if (tt + 1 < ntile) issue(tt + 1, (tt + 1) & 1);
+        if (tp + 2 < ntile) issue(tp + 2, (tp + 2) & 3);
+        if (tp + 3 < ntile) issue(tp + 3, (tp + 3) & 3);
         if (!active) continue;
-        const u32x4 *sQ = smem + (tt & 1) * 1024, *sO = sQ + 512;
+        for (int tt = tp; tt < min(tp + 2, ntile); ++tt) {
+        const u32x4 *sQ = smem + (tt & 3) * 1024, *sO = sQ + 512;
 #pragma unroll
         for (int qq = 0; qq < 2; ++qq) {
             f32x16 S = f32x16{}, dP = f32x16{};
@@ -269,7 +279,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r0 = qq * 32 + 8 * i + 4 * hh;
-                const f32x4 l4 = *(const f32x4 *)&sld[tt & 1][0][r0], d4 = *(const f32x4 *)&sld[tt & 1][1][r0];
+                const f32x4 l4 = *(const f32x4 *)&sld[tt & 3][0][r0], d4 = *(const f32x4 *)&sld[tt & 3][1][r0];
                 const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
                 for (int jj = 0; jj < 4; ++jj) {
@@ -290,6 +300,7 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
                         tr_rows_frag((const uint8_t *)sQ, qq * 32 + 16 * s, 32 * te, lane), bs, dK[te], 0, 0, 0);
                 }
             }
+        }
         }
     }
     if (active && kvalid) {
