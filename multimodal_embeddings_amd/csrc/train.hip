@@ -493,10 +493,17 @@ __global__ __launch_bounds__(256, 2) void k_xty(const uint16_t *x, int ldx, cons
         }
     };
     const int nk = te > tb ? (te - tb + 63) >> 6 : 0;
+    // The next stage's DMA is issued before this stage's wait (its buffer was freed by the previous
+    // iteration's closing barrier), so it has a whole stage of compute and both barriers to land.
     if (nk) issue(tb, 0);
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1, t0 = tb + kt * 64;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (kt + 1 < nk) {
+            issue(t0 + 64, buf ^ 1);
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
         if (t0 + 64 > te) {  // rows past the range read as zero
             u32x4 *st = smem + buf * kXtyStage;
 #pragma unroll
@@ -566,10 +573,17 @@ __global__ __launch_bounds__(512, 1) void k_xty256(const uint16_t *x, int ldx, c
         }
     };
     const int nk = te > tb ? (te - tb + 63) >> 6 : 0;
+    // The next stage's DMA is issued before this stage's wait (its buffer was freed by the previous
+    // iteration's closing barrier), so it has a whole stage of compute and both barriers to land.
     if (nk) issue(tb, 0);
     for (int kt = 0; kt < nk; ++kt) {
         const int buf = kt & 1, t0 = tb + kt * 64;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if (kt + 1 < nk) {
+            issue(t0 + 64, buf ^ 1);
+            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        } else {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
         if (t0 + 64 > te) {  // rows past the range read as zero
             u32x4 *st = smem + buf * kXtyWideStage;
 #pragma unroll
@@ -581,7 +595,6 @@ __global__ __launch_bounds__(512, 1) void k_xty256(const uint16_t *x, int ldx, c
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         lds_barrier();
-        if (kt + 1 < nk) issue(t0 + 64, buf ^ 1);
         const uint8_t *sY = (const uint8_t *)(smem + buf * kXtyWideStage), *sX = sY + 2048 * 16;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
