@@ -76,6 +76,9 @@ def _declare(L):
     L.oracle_forward_states.argtypes = [C.POINTER(Geometry), P, P, P, P, P, SZ, P, P]
     L.oracle_token_vectors.argtypes = [P, SZ, SZ, P, SZ, P]
     L.oracle_maxsim.argtypes = [P, P, SZ, P, P, SZ, SZ, SZ, SZ, P]
+    L.oracle_matmul.argtypes = [P, SZ, SZ, P, SZ, P, C.c_int]
+    L.oracle_e4m3_weights.argtypes = [P, SZ, P]
+    L.oracle_set_tap.argtypes = [P]
 
 
 def _p(a):
@@ -201,6 +204,55 @@ def pool(xf, cu, heads, query, wk, wv):
     out = np.zeros((max(count, 1), D), np.float64)
     lib().oracle_pool(_p(xf), _p(cu), count, D, heads, _p(q), _p(Wk), _p(Wv), _p(out))
     return out[:count]
+
+
+def matmul(x, w, e4m3=False):
+    """One block product y = x W (W used as given); with ``e4m3`` the rows of x are quantised per row
+    (amax / 448 scale each) as the E4M3 blocks do."""
+    x = _f64(x)
+    W = _f64(w)
+    T, K = x.shape
+    N = W.shape[1]
+    y = np.zeros((max(T, 1), N), np.float64)
+    if T:
+        lib().oracle_matmul(_p(x), T, K, _p(W), N, _p(y), 1 if e4m3 else 0)
+    return y[:T]
+
+
+def e4m3_weights(w):
+    """A block matrix as the E4M3 blocks use it: one quantise-dequantise over the whole tensor."""
+    w32 = _f32(w)
+    out = np.empty(w32.shape, np.float64)
+    lib().oracle_e4m3_weights(_p(w32), w32.size, _p(out))
+    return out
+
+
+_TAP_FN = C.CFUNCTYPE(None, C.c_char_p, C.POINTER(C.c_double), C.c_size_t, C.c_size_t)
+
+
+class Taps:
+    """Context manager recording what the blocks observe: ``taps[name]`` is the list (one entry per
+    block, in order) of float64 copies of that value -- GEMM inputs as the products read them
+    (``qkv_in``, ``out_in``, ``mlp_in``, ``up_in``, ``down_in``), weights as used (``w_qkv``, ``w_o``,
+    ``w_gate``, ``w_up``, ``w_down``) and stored activations (``q``, ``k``, ``v``, ``o``, ``a``)."""
+
+    def __init__(self):
+        self.taps = {}
+
+        def record(name, data, rows, cols):
+            a = np.ctypeslib.as_array(data, shape=(rows * cols,)).reshape(rows, cols).copy() if rows * cols else \
+                np.zeros((rows, cols))
+            self.taps.setdefault(name.decode(), []).append(a)
+
+        self._fn = _TAP_FN(record)
+
+    def __enter__(self):
+        lib().oracle_set_tap(C.cast(self._fn, C.c_void_p))
+        return self.taps
+
+    def __exit__(self, *exc):
+        lib().oracle_set_tap(None)
+        return False
 
 
 # ------------------------------------------------------------ whole encoder

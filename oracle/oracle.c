@@ -193,29 +193,56 @@ static void bf16_round_all(double *a, size_t n) {
 
 /* ------------------------------------------------------------- the blocks */
 
+/* Observation points for the pins: when a tap is installed, the blocks hand it
+ * every GEMM input exactly as the product reads it (after its per-row E4M3
+ * quantise-dequantise in E4M3 mode), every weight matrix as the products use it,
+ * and the activations stored between steps (q and k as attention reads them, v,
+ * the attention output o and the SwiGLU output a). A tap only reads; it changes
+ * no value. Not thread-safe: one forward at a time while a tap is installed. */
+typedef void (*oracle_tap_t)(const char *name, const double *data, size_t rows, size_t cols);
+static oracle_tap_t g_tap = NULL;
+
+void oracle_set_tap(oracle_tap_t fn) { g_tap = fn; }
+
+static void tap(const char *name, const double *data, size_t rows, size_t cols) {
+    if (g_tap && name) g_tap(name, data, rows, cols);
+}
+
 /* y[T x N] = x[T x K] W[K x N]. With `e4m3`, every row of x is first
- * replaced by its per-row quantise-dequantise (W is already quantised). */
-static void matmul(const double *x, size_t T, size_t K, const double *W, size_t N, double *y, int e4m3) {
-#pragma omp parallel
-    {
-        double *row = (double *)malloc(K * sizeof(double));
-#pragma omp for schedule(static)
-        for (size_t t = 0; t < T; ++t) {
-            const double *xr = x + t * K;
-            if (e4m3) {
-                e4m3_qdq(xr, row, K);
-                xr = row;
-            }
-            double *yr = y + t * N;
-            for (size_t n = 0; n < N; ++n) yr[n] = 0.0;
-            for (size_t k = 0; k < K; ++k) {
-                double a = xr[k];
-                const double *w = W + k * N;
-                for (size_t n = 0; n < N; ++n) yr[n] += a * w[n];
-            }
-        }
-        free(row);
+ * replaced by its per-row quantise-dequantise (W is already quantised).
+ * `name` labels the product's input for the tap (NULL: not observed). */
+static void matmul_named(const char *name, const double *x, size_t T, size_t K, const double *W, size_t N, double *y,
+                         int e4m3) {
+    double *xq = NULL;
+    if (e4m3) {
+        xq = (double *)malloc((T ? T : 1) * K * sizeof(double));
+#pragma omp parallel for schedule(static)
+        for (size_t t = 0; t < T; ++t) e4m3_qdq(x + t * K, xq + t * K, K);
+        x = xq;
     }
+    tap(name, x, T, K);
+#pragma omp parallel for schedule(static)
+    for (size_t t = 0; t < T; ++t) {
+        const double *xr = x + t * K;
+        double *yr = y + t * N;
+        for (size_t n = 0; n < N; ++n) yr[n] = 0.0;
+        for (size_t k = 0; k < K; ++k) {
+            double a = xr[k];
+            const double *w = W + k * N;
+            for (size_t n = 0; n < N; ++n) yr[n] += a * w[n];
+        }
+    }
+    free(xq);
+}
+
+static void matmul(const double *x, size_t T, size_t K, const double *W, size_t N, double *y, int e4m3) {
+    matmul_named(NULL, x, T, K, W, N, y, e4m3);
+}
+
+/* One block product on its own (exposed for pins): y = x W, W [K x N] used as
+ * given; with `e4m3` the rows of x are quantised per row as in the blocks. */
+void oracle_matmul(const double *x, size_t T, size_t K, const double *W, size_t N, double *y, int e4m3) {
+    matmul(x, T, K, W, N, y, e4m3);
 }
 
 /* RMSNorm ("UForm" page, "Architecture & Goals"; inverse RMS in at least
@@ -336,6 +363,14 @@ static double *widen(const float *w, size_t n, int e4m3) {
     return out;
 }
 
+/* A block matrix as the E4M3 blocks use it (exposed for pins): one
+ * quantise-dequantise over the whole tensor of n values. */
+void oracle_e4m3_weights(const float *w, size_t n, double *out) {
+    double *q = widen(w, n, 1);
+    memcpy(out, q, n * sizeof(double));
+    free(q);
+}
+
 /* One pre-norm block ("UForm" page, "Architecture & Goals"; the residual
  * stream is the block's fp32 input kept across the block, "Precision by
  * Design"). Readings: x += Attn(RMSNorm1(x)); x += MLP(RMSNorm2(x)); fused
@@ -361,9 +396,15 @@ void oracle_block(const oracle_geometry_t *g, const oracle_block_t *w, double *x
     double *Wg = widen(w->w_gate, D * F, g->e4m3), *Wu = widen(w->w_up, D * F, g->e4m3);
     double *Wd = widen(w->w_down, F * D, g->e4m3);
 
+    tap("w_qkv", Wqkv, D, 3 * D);
+    tap("w_o", Wo, D, D);
+    tap("w_gate", Wg, D, F);
+    tap("w_up", Wu, D, F);
+    tap("w_down", Wd, F, D);
+
     /* attention half */
     oracle_rmsnorm(x, w->attn_norm, T, D, g->rms_epsilon, h);
-    matmul(h, T, D, Wqkv, 3 * D, qkv, g->e4m3);
+    matmul_named("qkv_in", h, T, D, Wqkv, 3 * D, qkv, g->e4m3);
     for (size_t t = 0; t < T; ++t)
         for (size_t f = 0; f < D; ++f) {
             q[t * D + f] = qkv[t * 3 * D + f];
@@ -377,18 +418,23 @@ void oracle_block(const oracle_geometry_t *g, const oracle_block_t *w, double *x
         bf16_round_all(k, T * D);
         bf16_round_all(v, T * D);
     }
+    tap("q", q, T, D);
+    tap("k", k, T, D);
+    tap("v", v, T, D);
     oracle_attention(q, k, v, cu, count, H, d, o);
     if (g->e4m3) bf16_round_all(o, T * D);
-    matmul(o, T, D, Wo, D, y, g->e4m3);
+    tap("o", o, T, D);
+    matmul_named("out_in", o, T, D, Wo, D, y, g->e4m3);
     for (size_t i = 0; i < T * D; ++i) x[i] += y[i];
 
     /* MLP half */
     oracle_rmsnorm(x, w->mlp_norm, T, D, g->rms_epsilon, h);
-    matmul(h, T, D, Wg, F, gt, g->e4m3);
-    matmul(h, T, D, Wu, F, up, g->e4m3);
+    matmul_named("mlp_in", h, T, D, Wg, F, gt, g->e4m3);
+    matmul_named("up_in", h, T, D, Wu, F, up, g->e4m3);
     for (size_t i = 0; i < T * F; ++i) gt[i] = silu(gt[i]) * up[i];
     if (g->e4m3) bf16_round_all(gt, T * F);
-    matmul(gt, T, F, Wd, D, y, g->e4m3);
+    tap("a", gt, T, F);
+    matmul_named("down_in", gt, T, F, Wd, D, y, g->e4m3);
     for (size_t i = 0; i < T * D; ++i) x[i] += y[i];
 
     free(h); free(qkv); free(q); free(k); free(v); free(o); free(y); free(gt); free(up);
