@@ -193,11 +193,15 @@ void ube_model_free(ube_model_t model);
 
 /* An empty arena on GPU `device` ("Arenas" page, `uform_arena_init`): it holds
  * no memory before the first call that writes into it. Here the arena also holds
- * the call's activations, so an arena is the unit of concurrency. */
+ * the call's activations, so an arena is the unit of concurrency.
+ * capacity_limit: device bytes the arena may grow to (0: no limit). A call that
+ * would need more fails with out_of_memory and NULL outputs, as when the GPU has
+ * no memory left ("Python" page, "Errors"); the arena keeps what it held. */
 typedef struct ube_arena_init_t {
     ube_arena_t *arena;
     ube_outcome_t *outcome;
     int device;
+    size_t capacity_limit;
 } ube_arena_init_t;
 void ube_arena_init(ube_arena_init_t *arguments);
 

@@ -61,6 +61,28 @@ ube_status_t ube_step_quantize_e4m3(void const *in, void *codes, float *scales, 
 ube_status_t ube_step_gemm_e4m3(void const *w, float w_scale, void const *x, float const *x_scale, void *y, size_t M,
                                 size_t N, size_t K, void *stream);
 
+/* QKV projection with multi-axis rotary ("UForm" page, "Architecture & Goals": QKV
+ * attention with M-RoPE; "One Omni Model": 1-D text, 2-D (row, col) image and 3-D
+ * (frame, row, col) video coordinates), the kernel and epilogue an encode runs:
+ * [q | k | v] = x w^T with w given transposed as [3D x K] (rows 0..D-1 give q,
+ * D..2D-1 give k, 2D..3D-1 give v); accumulation fp32. Within every head of 64
+ * features, pair j (features 2j, 2j+1) of q and k turns by the angle
+ * pos[t][axis(j)] * base^(-2j/64); the 32 pairs form `rope_axes` contiguous sections
+ * as even as possible, leading sections taking the remainder ([32]; [16, 16];
+ * [11, 11, 10]). Outputs: qk bf16 [M x 2D] (row t = rotated q_t | rotated k_t),
+ * vt bf16 feature-major [D x ldvt] (element (f, t) = v_t[f]; columns M ..
+ * round_up(M, 256) - 1 are written as 0).
+ * x: bf16 [M x K] with round_up(M, 256) readable rows (rows past M are read, their
+ * products discarded). pos_host: host int16 [M x 4], entries 0..2 the token's
+ * coordinates on axes 0..2, each in [0, positions); entry 3 unused.
+ * Requirements: D % 128 == 0, K % 64 == 0, 1 <= rope_axes <= 3, positions <= 32767,
+ * ldvt >= round_up(M, 256); invalid_argument otherwise or for a coordinate outside
+ * [0, positions). Synchronous: builds the cos/sin table (double, stored fp32) and
+ * uploads the coordinates into device memory it allocates and frees. */
+ube_status_t ube_step_qkv_rotary(void const *w, void const *x, size_t M, size_t D, size_t K, int16_t const *pos_host,
+                                 size_t rope_axes, float rope_base, size_t positions, void *qk, void *vt, size_t ldvt,
+                                 void *stream);
+
 /* Kernels of an encode, contrastive or trainer call, for timing. */
 typedef enum ube_kernel_t {
     ube_kernel_gather_k = 0,

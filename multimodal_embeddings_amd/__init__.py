@@ -80,7 +80,8 @@ class ube_model_describe_t(C.Structure):
 
 
 class ube_arena_init_t(C.Structure):
-    _fields_ = [("arena", C.POINTER(VP)), ("outcome", C.POINTER(ube_outcome_t)), ("device", C.c_int)]
+    _fields_ = [("arena", C.POINTER(VP)), ("outcome", C.POINTER(ube_outcome_t)), ("device", C.c_int),
+                ("capacity_limit", SZ)]
 
 
 _ENCODE_HEAD = [("model", VP), ("arena", VP), ("stream", VP), ("outcome", C.POINTER(ube_outcome_t)),
@@ -190,6 +191,7 @@ _SIGNATURES = {
     "ube_step_attention": ([VP, VP, SZ, VP, SZ, VP, SZ, VP, SZ, SZ, VP], C.c_int),
     "ube_step_quantize_e4m3": ([VP, VP, VP, SZ, SZ, VP], C.c_int),
     "ube_step_gemm_e4m3": ([VP, C.c_float, VP, VP, VP, SZ, SZ, SZ, VP], C.c_int),
+    "ube_step_qkv_rotary": ([VP, VP, SZ, SZ, SZ, VP, SZ, C.c_float, SZ, VP, VP, SZ, VP], C.c_int),
     "ube_kernel_timer_start": ([C.c_int, SZ], C.c_int),
     "ube_kernel_timer_stop": ([C.POINTER(C.c_double), C.POINTER(SZ)], C.c_int),
     "ube_kernel_name": ([C.c_int], C.c_char_p),
@@ -319,10 +321,11 @@ class Model:
 
 
 class Arena:
-    def __init__(self, device: int = 0):
+    def __init__(self, device: int = 0, capacity_limit: int = 0):
         handle = VP()
         outcome = ube_outcome_t()
-        lib().ube_arena_init(C.byref(ube_arena_init_t(C.pointer(handle), C.pointer(outcome), device)))
+        lib().ube_arena_init(C.byref(ube_arena_init_t(C.pointer(handle), C.pointer(outcome), device,
+                                                      capacity_limit)))
         _check(outcome)
         self.handle = handle
         self.device = device
@@ -684,6 +687,15 @@ def step_attention(q, k, ldqk, vt, ldvt, o, ldo, cu, heads, stream=None):
 
 def step_quantize_e4m3(x, codes, scales, T, W, stream=None):
     _step(lib().ube_step_quantize_e4m3(_ptr(x), _ptr(codes), _ptr(scales), T, W, _stream_handle(stream)))
+
+
+def step_qkv_rotary(w, x, M, D, K, pos, rope_axes, rope_base, positions, qk, vt, ldvt, stream=None):
+    """pos: host int16 [M x 4] (coordinates on axes 0..2); synchronous."""
+    pos = np.ascontiguousarray(pos, dtype=np.int16)
+    if pos.size < 4 * M:
+        raise ValueError("pos must hold M x 4 coordinates")
+    _step(lib().ube_step_qkv_rotary(_ptr(w), _ptr(x), M, D, K, pos.ctypes.data, rope_axes, rope_base, positions,
+                                    _ptr(qk), _ptr(vt), ldvt, _stream_handle(stream)))
 
 
 def step_gemm_e4m3(w, w_scale, x, x_scale, y, M, N, K, stream=None):

@@ -30,20 +30,25 @@ def build(verbose: bool = False) -> str:
     hipcc = _hipcc()
     objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for src in SOURCES:
+    objs, procs = [], []
+    for src in SOURCES:  # the sources compile in parallel
         obj = os.path.join(objdir, src + ".o")
         cmd = [hipcc, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
-        r = subprocess.run(cmd, capture_output=True, text=True)
-        noise = "is not a recognized feature for this target"
-        err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
-        if r.returncode != 0:
-            raise RuntimeError(f"hipcc failed on {src}:\n{err}")
-        if err.strip() and verbose:
-            print(err, file=sys.stderr)
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
         objs.append(obj)
+    noise = "is not a recognized feature for this target"
+    failed = []
+    for src, proc in procs:
+        _, stderr = proc.communicate()
+        err = "\n".join(l for l in stderr.splitlines() if noise not in l)
+        if proc.returncode != 0:
+            failed.append(f"hipcc failed on {src}:\n{err}")
+        elif err.strip() and verbose:
+            print(err, file=sys.stderr)
+    if failed:
+        raise RuntimeError("\n".join(failed))
     tmp = LIB + ".tmp"
     cmd = [hipcc, *DEVICE_FLAGS, "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)

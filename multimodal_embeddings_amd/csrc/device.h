@@ -74,6 +74,14 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, void *lds_base) {
     __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
+// Waits until at most N vector memory operations of this wave are outstanding (loads
+// complete in issue order, so the oldest ones are then done).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 // Workgroup barrier without a memory fence (the DMA of the next stage stays in
 // flight); the empty asm keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() {

@@ -413,6 +413,7 @@ struct ube_arena_handle_t {
     std::atomic<int> busy{0};
     char *dev = nullptr;
     size_t cap = 0;
+    size_t limit = 0;  // device bytes the arena may hold (0: no limit)
     char *pinned = nullptr;
     size_t pinned_cap = 0;
     hipEvent_t staged = nullptr;  // recorded after the last copy out of `pinned`
@@ -437,6 +438,7 @@ extern "C" void ube_arena_init(ube_arena_init_t *a) {
         return;
     }
     ar->device = a->device;
+    ar->limit = a->capacity_limit;
     *a->arena = ar;
     set_outcome(a->outcome, ube_status_success_k, nullptr);
 }
@@ -455,6 +457,26 @@ extern "C" void ube_arena_free(ube_arena_t ar) {
 }
 
 extern "C" size_t ube_arena_capacity(ube_arena_t ar) { return ar ? ar->cap : 0; }
+
+namespace {
+
+// Grows the arena to hold `total` bytes (whole MiB), only when outgrown; the old contents are not kept.
+// Beyond the arena's capacity limit the call fails out_of_memory and the arena keeps what it holds.
+void arena_reserve(ube_arena_t ar, size_t total, hipStream_t st, bool clear) {
+    if (total <= ar->cap) return;
+    const size_t want = align_up(total, (size_t)1 << 20);
+    if (ar->limit && want > ar->limit)
+        throw Failure{ube_status_out_of_memory_k, "the call needs more device memory than the arena's capacity limit"};
+    UBE_HIP(hipStreamSynchronize(st));
+    if (ar->dev) UBE_HIP(hipFree(ar->dev));
+    ar->dev = nullptr;
+    ar->cap = 0;
+    UBE_HIP(hipMalloc((void **)&ar->dev, want));
+    ar->cap = want;
+    if (clear) UBE_HIP(hipMemsetAsync(ar->dev, 0, want, st));
+}
+
+}  // namespace
 
 // ===================================================================== plan
 
@@ -483,22 +505,27 @@ struct Plan {
     size_t count = 0, T = 0, truncated = 0;
     std::vector<int> cu;            // count + 1
     std::vector<int64_t> src;       // count: byte offset of each item in the device input
-    std::vector<int2> tiles;        // (item, first token) per 128-token tile
+    std::vector<int2> tiles;        // (item, first token) per 256-token tile
+    std::vector<int> itile;         // count + 1: first tile of each item
     std::vector<MediaItem> media;   // media items
     size_t input_lo = 0, input_hi = 0;  // tape data range the items read
 };
 
 void make_tiles(Plan &p) {
     p.tiles.clear();
-    for (size_t i = 0; i < p.count; ++i)
+    p.itile.assign(p.count + 1, 0);
+    for (size_t i = 0; i < p.count; ++i) {
+        p.itile[i] = (int)p.tiles.size();
         for (int t = p.cu[i]; t < p.cu[i + 1]; t += kTileTokens) p.tiles.push_back(int2{(int)i, t});
+    }
+    p.itile[p.count] = (int)p.tiles.size();
 }
 
 // Device regions of one call.
 struct Layout {
     size_t Tpad = 0;
-    size_t out, cu, offs, src, tiles, media, input, x, h, a, qk, vt, o, xf, s, pos, patches, q8, qs, ss, st, tvf, tv,
-        total;
+    size_t out, cu, offs, src, tiles, itile, media, input, x, h, a, qk, vt, o, xf, s, pos, patches, q8, qs, ss, st,
+        tvf, tv, zp, zs, total;
 };
 
 // Per-token surfaces of one call: fp32 states (bf16 states are the final-norm
@@ -524,6 +551,7 @@ Layout carve(ube_geometry_t const &g, Plan const &p, bool media, size_t input_by
     L.offs = take((p.count + 1) * 8);  // the token offsets as size_t, for rows tapes
     L.src = take(std::max<size_t>(p.count, 1) * 8);
     L.tiles = take(std::max<size_t>(p.tiles.size(), 1) * 8);
+    L.itile = take((p.count + 1) * 4);
     L.media = take(media ? std::max<size_t>(p.count, 1) * sizeof(MediaItem) : 0);
     L.input = take(input_bytes);
     L.x = take(L.Tpad * D * 4);
@@ -542,6 +570,8 @@ Layout carve(ube_geometry_t const &g, Plan const &p, bool media, size_t input_by
     L.st = take(tok.states_f32 ? L.Tpad * D * 4 : 0);
     L.tvf = take(tok.vectors ? L.Tpad * tok.width * 4 : 0);  // token head output before normalisation
     L.tv = take(tok.vectors ? L.Tpad * tok.width * tok.vector_bytes : 0);
+    L.zp = take(pool_partial_bytes((int)p.tiles.size(), (int)D, (int)H));  // pool: per-tile partial sums
+    L.zs = take(pool_stats_bytes((int)p.tiles.size(), (int)H));
     L.total = total;
     return L;
 }
@@ -634,16 +664,7 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
     if (r.layout) *r.layout = L;
 
     // grow the arena (only when outgrown)
-    if (L.total > ar->cap) {
-        UBE_HIP(hipStreamSynchronize(st));
-        if (ar->dev) UBE_HIP(hipFree(ar->dev));
-        ar->dev = nullptr;
-        ar->cap = 0;
-        size_t want = align_up(L.total, (size_t)1 << 20);
-        UBE_HIP(hipMalloc((void **)&ar->dev, want));
-        ar->cap = want;
-        UBE_HIP(hipMemsetAsync(ar->dev, 0, want, st));
-    }
+    arena_reserve(ar, L.total, st, true);
     char *db = ar->dev;
 
     // host staging: cu, src, tiles, media items (+ tape bytes when host-resident)
@@ -669,6 +690,7 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
     for (size_t i = 0; i < p.count; ++i)
         ((int64_t *)(hp + (L.src - L.cu)))[i] = p.src[i] - (on_device ? 0 : (int64_t)p.input_lo);
     if (!p.tiles.empty()) std::memcpy(hp + (L.tiles - L.cu), p.tiles.data(), p.tiles.size() * 8);
+    std::memcpy(hp + (L.itile - L.cu), p.itile.data(), p.itile.size() * 4);
     if (media && p.count) {
         std::vector<MediaItem> items = p.media;
         for (auto &it : items) it.pixel_offset -= on_device ? 0 : (int64_t)p.input_lo;
@@ -812,7 +834,8 @@ void run_encode(EncodeRequest const &r, Plan &p, bool media) {
     const bool embeddings = wants(r.outputs, ube_outputs_embeddings_k);
     if (p.count && embeddings) {
         timed(ube_kernel_pool_k, st, [&] {
-            return launch_pool(xf, s, cu, (int)p.count, m->wv, db + L.out, bf16_out ? 1 : 0, row_bytes, D, H, st);
+            return launch_pool(xf, s, cu, tiles, ntiles, (const int *)(db + L.itile), (int)p.count, m->wv, db + L.out,
+                               bf16_out ? 1 : 0, row_bytes, D, H, (float *)(db + L.zp), (float2 *)(db + L.zs), st);
         });
     }
     if (r.completion == 0) UBE_HIP(hipStreamSynchronize(st));
@@ -1224,15 +1247,7 @@ extern "C" void ube_contrastive(ube_contrastive_t *a) {
         const size_t o_cole = take(E * 4);
         const size_t o_touch = take(T * 4);
         const size_t total = off;
-        if (total > ar->cap) {
-            UBE_HIP(hipStreamSynchronize(st));
-            if (ar->dev) UBE_HIP(hipFree(ar->dev));
-            ar->dev = nullptr;
-            ar->cap = 0;
-            const size_t want = align_up(total, (size_t)1 << 20);
-            UBE_HIP(hipMalloc((void **)&ar->dev, want));
-            ar->cap = want;
-        }
+        arena_reserve(ar, total, st, false);
         char *db = ar->dev;
         ca.inv = (float *)(db + o_inv);
         ca.H = (uint16_t *)(db + o_h);
@@ -1932,6 +1947,47 @@ extern "C" ube_status_t ube_step_gemm(void const *w, void const *x, void *y, siz
     a.w = (const uint16_t *)w, a.x = (const uint16_t *)x, a.M = (int)M, a.N = (int)N, a.K = (int)K;
     a.out_bf16 = (uint16_t *)y, a.ld_out = (int)N;
     return step_status(launch_gemm(kEpiStore, a, (hipStream_t)stream));
+}
+
+extern "C" ube_status_t ube_step_qkv_rotary(void const *w, void const *x, size_t M, size_t D, size_t K,
+                                           int16_t const *pos_host, size_t rope_axes, float rope_base,
+                                           size_t positions, void *qk, void *vt, size_t ldvt, void *stream) {
+    if (!w || !x || !qk || !vt || (M && !pos_host) || !D || D % 128 || !K || K % 64 || rope_axes < 1 ||
+        rope_axes > 3 || !positions || positions > 32767 || M > 0x7fffff00 || D > 8192 ||
+        ldvt < align_up(M, 256) || ldvt > 0x7fffffff)
+        return ube_status_invalid_argument_k;
+    for (size_t t = 0; t < M; ++t)
+        for (size_t a = 0; a < 3; ++a)
+            if (pos_host[t * 4 + a] < 0 || (size_t)pos_host[t * 4 + a] >= positions) return ube_status_invalid_argument_k;
+    std::vector<float2> table(positions * 32);
+    for (size_t p = 0; p < positions; ++p)
+        for (int j = 0; j < 32; ++j) {
+            const double phi = (double)p * std::pow((double)rope_base, -2.0 * (double)j / 64.0);
+            table[p * 32 + j] = float2{(float)std::cos(phi), (float)std::sin(phi)};
+        }
+    hipStream_t st = (hipStream_t)stream;
+    void *drope = nullptr, *dpos = nullptr;
+    hipError_t e = hipMalloc(&drope, table.size() * sizeof(float2));
+    if (e == hipSuccess) e = hipMalloc(&dpos, std::max<size_t>(M, 1) * 8);
+    if (e == hipSuccess) e = hipMemcpyAsync(drope, table.data(), table.size() * sizeof(float2), hipMemcpyHostToDevice, st);
+    if (e == hipSuccess && M) e = hipMemcpyAsync(dpos, pos_host, M * 8, hipMemcpyHostToDevice, st);
+    if (e == hipSuccess) {
+        GemmArgs a{};
+        a.w = (const uint16_t *)w, a.x = (const uint16_t *)x, a.M = (int)M, a.N = (int)(3 * D), a.K = (int)K;
+        a.out_bf16 = (uint16_t *)qk, a.ld_out = (int)(2 * D), a.vt = (uint16_t *)vt, a.ld_vt = (int)ldvt;
+        a.pos = (const int16_t *)dpos, a.rope = (const float2 *)drope, a.D = (int)D;
+        const int pairs = 32, axes = (int)rope_axes, base = pairs / axes, rem = pairs % axes;
+        a.sec0 = base + (0 < rem ? 1 : 0);
+        a.sec1 = axes >= 2 ? base + (1 < rem ? 1 : 0) : 0;
+        e = launch_gemm(kEpiQkv, a, st);
+    }
+    // the 256-wide kernel writes the columns past M as zeros itself; the narrow one leaves them
+    const size_t Mp = align_up(M, 256);
+    if (e == hipSuccess && Mp > M) e = hipMemset2DAsync((char *)vt + M * 2, ldvt * 2, 0, (Mp - M) * 2, D, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (drope) (void)hipFree(drope);
+    if (dpos) (void)hipFree(dpos);
+    return step_status(e);
 }
 
 extern "C" ube_status_t ube_step_quantize_e4m3(void const *in, void *codes, float *scales, size_t T, size_t W,

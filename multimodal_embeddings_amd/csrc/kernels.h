@@ -97,7 +97,12 @@ hipError_t launch_maxsim(const uint16_t *q, const size_t *qoff, size_t qrows, si
 
 // Per item: softmax of the scores over the item's tokens per head,
 // z_h = sum_t p_t,h xf_t, pooled_h = z_h W_v[:, head h]; empty items -> 0.
-hipError_t launch_pool(const uint16_t *xf, const float *s, const int *cu, int count, const uint16_t *wv, void *out,
-                       int out_bf16, size_t out_stride, int D, int H, hipStream_t stream);
+// tiles: the 256-token tiles (item, first token); itile[count + 1]: first tile of each item.
+// zp, zs: scratch of pool_partial_bytes / pool_stats_bytes.
+size_t pool_partial_bytes(int ntiles, int D, int H);
+size_t pool_stats_bytes(int ntiles, int H);
+hipError_t launch_pool(const uint16_t *xf, const float *s, const int *cu, const int2 *tiles, int ntiles,
+                       const int *itile, int count, const uint16_t *wv, void *out, int out_bf16, size_t out_stride,
+                       int D, int H, float *zp, float2 *zs, hipStream_t stream);
 
 }  // namespace ube

@@ -1519,250 +1519,191 @@ hipError_t launch_maxsim(const uint16_t *q, const size_t *qoff, size_t qrows, si
 
 // =========================================================== pool
 //
-// One workgroup per item. Scores s[t][h] = xf_t . u_h with u_h = W_k,h q_h / 8
-// (the reassociated form of q_h . (xf_t W_k)_h / sqrt(64)) come from the final
-// norm kernel. Here: per head softmax over the item's tokens (written back as
-// probabilities), z_h = sum_t p_t,h xf_t, then pooled_h = z_h W_v[:, h].
+// Scores s[t][h] = xf_t . u_h with u_h = W_k,h q_h / 8 (the reassociated form of
+// q_h . (xf_t W_k)_h / sqrt(64)) come from the final norm kernel. Two launches:
+//  - token-parallel, one workgroup per 256-token tile of an item (the attention
+//    tile list): per head h, m = max over the tile's tokens of s[t][h],
+//    p_t = e^(s[t][h] - m), l = sum_t p_t and the partial z[h][f] = sum_t p_t xf[t][f],
+//    fp32, the tile's tokens in order;
+//  - per (item, head): the item's tile partials combined in tile order, each scaled
+//    by e^(m_tile - m_item), z_h = sum / L, then pooled_h = z_h W_v[:, 64 h .. 64 h + 63].
+// Both orders are fixed, so a row never depends on the rest of the batch; an item
+// with no tokens has no tiles and pools to zero.
 
-__device__ float block_reduce(float v, float *scratch, bool is_max) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    v = is_max ? wave_max(v) : wave_sum(v);
-    __syncthreads();
-    if (lane == 0) scratch[wave] = v;
-    __syncthreads();
-    float r = scratch[0];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) r = is_max ? fmaxf(r, scratch[w]) : r + scratch[w];
-    return r;
-}
+constexpr int kPoolTile = kTileTokens;
 
-template <int HMAX, int CMAX>
-__global__ __launch_bounds__(256) void k_pool(const uint16_t *__restrict__ xf, const float *__restrict__ s,
-                                              const int *__restrict__ cu, const uint16_t *__restrict__ wv,
-                                              void *__restrict__ out, int out_bf16, size_t out_stride, int D, int H) {
-    // LDS: z [H x D] | p chunk [256 x H] | per-head max and 1/sum [2 x H] | 4 floats of reduction scratch
-    extern __shared__ float smem[];
-    float *z = smem, *pc = z + H * D, *mh = pc + 256 * H, *ih = mh + H, *scratch = ih + H;
-    const int item = blockIdx.x, t0 = cu[item], t1 = cu[item + 1];
-    const int tid = threadIdx.x;
-    char *orow = (char *)out + (size_t)item * out_stride;
-    if (t1 == t0) {
-        for (int col = tid; col < D; col += 256) {
-            if (out_bf16) ((uint16_t *)orow)[col] = 0;
-            else ((float *)orow)[col] = 0.f;
-        }
-        return;
-    }
-    for (int hd = 0; hd < H; ++hd) {
-        float m = -INFINITY;
-        for (int t = t0 + tid; t < t1; t += 256) m = fmaxf(m, s[(size_t)t * H + hd]);
-        m = block_reduce(m, scratch, true);
-        float sum = 0.f;
-        for (int t = t0 + tid; t < t1; t += 256) sum += __expf(s[(size_t)t * H + hd] - m);
-        sum = block_reduce(sum, scratch, false);
-        if (tid == 0) mh[hd] = m, ih[hd] = 1.0f / sum;
-    }
-    float zacc[CMAX][HMAX];
-#pragma unroll
-    for (int c = 0; c < CMAX; ++c)
-#pragma unroll
-        for (int hd = 0; hd < HMAX; ++hd) zacc[c][hd] = 0.f;
-    for (int cs = t0; cs < t1; cs += 256) {
-        __syncthreads();
-        if (cs + tid < t1)
-            for (int hd = 0; hd < H; ++hd)
-                pc[tid * H + hd] = __expf(s[(size_t)(cs + tid) * H + hd] - mh[hd]) * ih[hd];
-        __syncthreads();
-        const int n = min(256, t1 - cs);
-        for (int tt = 0; tt < n; ++tt) {
-            float p[HMAX];
-#pragma unroll
-            for (int hd = 0; hd < HMAX; ++hd) p[hd] = hd < H ? pc[tt * H + hd] : 0.f;
-#pragma unroll
-            for (int c = 0; c < CMAX; ++c) {
-                const int f = tid + 256 * c;
-                if (f < D) {
-                    const float xv = bf16_to_f32(xf[(size_t)(cs + tt) * D + f]);
-#pragma unroll
-                    for (int hd = 0; hd < HMAX; ++hd) zacc[c][hd] += p[hd] * xv;
-                }
-            }
-        }
-    }
-#pragma unroll
-    for (int c = 0; c < CMAX; ++c) {
-        const int f = tid + 256 * c;
-        if (f < D)
-#pragma unroll
-            for (int hd = 0; hd < HMAX; ++hd)
-                if (hd < H) z[hd * D + f] = zacc[c][hd];
-    }
-    __syncthreads();
-    for (int col = tid; col < D; col += 256) {
-        const float *zh = z + (col >> 6) * D;
-        float accv = 0.f;
-        for (int f = 0; f < D; ++f) accv += zh[f] * bf16_to_f32(wv[(size_t)f * D + col]);
-        if (out_bf16) ((uint16_t *)orow)[col] = (uint16_t)f32_to_bf16(accv);
-        else ((float *)orow)[col] = accv;
-    }
-}
-
-// The same pool for D <= 512 and H <= 8 with the token sum spread over the workgroup: 8 waves, wave w
-// taking tokens t0 + w, t0 + w + 8, ...; lane l holds columns 8 l .. 8 l + 7 (one 16-byte load of xf per
-// token, four tokens in flight) and the partial z of every head; the waves' partials are added in wave
-// order through LDS. Softmax statistics by a fixed tree over the threads; the weights p of every head are
-// then formed once per token, a chunk of tokens at a time, into LDS, where the token loop reads them as
-// broadcasts (no global load and no exponential inside it). One item's tokens are never read twice and
-// no thread walks the whole item alone.
-__global__ __launch_bounds__(512) void k_pool_wide(const uint16_t *__restrict__ xf, const float *__restrict__ s,
-                                                   const int *__restrict__ cu, const uint16_t *__restrict__ wv,
-                                                   void *__restrict__ out, int out_bf16, size_t out_stride, int D,
-                                                   int H) {
-    constexpr int kChunk = 1024;  // tokens whose weights sit in LDS at a time
-    __shared__ float z[8 * 512];
-    __shared__ __attribute__((aligned(16))) float pw[kChunk][8];
-    __shared__ float red[8][8];
-    __shared__ float mh[8], ih[8];
-    const int item = blockIdx.x, t0 = cu[item], t1 = cu[item + 1];
+template <int HMAX>
+__global__ __launch_bounds__(256) void k_pool_part(const uint16_t *__restrict__ xf, const float *__restrict__ s,
+                                                   const int *__restrict__ cu, const int2 *__restrict__ tiles, int D,
+                                                   int H, float *__restrict__ zp, float2 *__restrict__ zs) {
+    // LDS: weights p [256][HMAX] | z [HMAX][D] | per-wave reductions [4][HMAX]
+    extern __shared__ __attribute__((aligned(16))) float lds[];
+    float *pw = lds, *zl = pw + kPoolTile * HMAX, *red = zl + HMAX * D;
+    const int2 tl = tiles[blockIdx.x];
+    const int c0 = tl.y, n = min(cu[tl.x + 1] - c0, kPoolTile);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    char *orow = (char *)out + (size_t)item * out_stride;
-    if (t1 == t0) {
-        for (int col = tid; col < D; col += 512) {
-            if (out_bf16) ((uint16_t *)orow)[col] = 0;
-            else ((float *)orow)[col] = 0.f;
-        }
-        return;
+
+    // softmax statistics of the tile: thread tid holds token tid's scores
+    float sv[HMAX];
+#pragma unroll
+    for (int h = 0; h < HMAX; ++h) sv[h] = (tid < n && h < H) ? s[(size_t)(c0 + tid) * H + h] : -INFINITY;
+#pragma unroll
+    for (int h = 0; h < HMAX; ++h) {
+        const float v = wave_max(sv[h]);
+        if (lane == 0) red[wave * HMAX + h] = v;
     }
-    // softmax statistics of every head
-    float loc[8];
+    __syncthreads();
+    float m[HMAX];
 #pragma unroll
-    for (int hd = 0; hd < 8; ++hd) loc[hd] = -INFINITY;
-    for (int t = t0 + tid; t < t1; t += 512)
+    for (int h = 0; h < HMAX; ++h)
+        m[h] = fmaxf(fmaxf(red[h], red[HMAX + h]), fmaxf(red[2 * HMAX + h], red[3 * HMAX + h]));
+    __syncthreads();  // every thread has read the maxima before the sums reuse `red`
 #pragma unroll
-        for (int hd = 0; hd < 8; ++hd)
-            if (hd < H) loc[hd] = fmaxf(loc[hd], s[(size_t)t * H + hd]);
-#pragma unroll
-    for (int hd = 0; hd < 8; ++hd) {
-        const float v = wave_max(loc[hd]);
-        if (lane == 0) red[wave][hd] = v;
+    for (int h = 0; h < HMAX; ++h) {
+        const float p = (tid < n && h < H) ? __expf(sv[h] - m[h]) : 0.f;
+        pw[tid * HMAX + h] = p;
+        const float v = wave_sum(p);
+        if (lane == 0) red[wave * HMAX + h] = v;
     }
     __syncthreads();
     if (tid < H) {
-        float m = red[0][tid];
-        for (int w = 1; w < 8; ++w) m = fmaxf(m, red[w][tid]);
-        mh[tid] = m;
-    }
-    __syncthreads();
+        float mt = 0.f;
 #pragma unroll
-    for (int hd = 0; hd < 8; ++hd) loc[hd] = 0.f;
-    for (int t = t0 + tid; t < t1; t += 512)
-#pragma unroll
-        for (int hd = 0; hd < 8; ++hd)
-            if (hd < H) loc[hd] += __expf(s[(size_t)t * H + hd] - mh[hd]);
-#pragma unroll
-    for (int hd = 0; hd < 8; ++hd) {
-        const float v = wave_sum(loc[hd]);
-        if (lane == 0) red[wave][hd] = v;
+        for (int h = 0; h < HMAX; ++h)
+            if (h == tid) mt = m[h];
+        const float l = ((red[tid] + red[HMAX + tid]) + red[2 * HMAX + tid]) + red[3 * HMAX + tid];
+        zs[(size_t)blockIdx.x * H + tid] = float2{mt, l};
     }
-    __syncthreads();
-    if (tid < H) {
-        float sum = red[0][tid];
-        for (int w = 1; w < 8; ++w) sum += red[w][tid];
-        ih[tid] = 1.0f / sum;
-    }
-    __syncthreads();
-    // z_h partials of this wave's tokens
-    const bool on = 8 * lane < D;
-    float zacc[8][8];
+
+    // z partials: thread (slot, g) sums columns 8 g .. 8 g + 7 over tokens slot, slot + slots, ...
+    const int G = D / 8, slots = kPoolTile / G;
+    const int slot = tid / G, g = tid % G;
+    const bool on = slot < slots;
+    float acc[8][HMAX];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int hd = 0; hd < 8; ++hd) zacc[i][hd] = 0.f;
-    int c0 = t0;  // first token of the chunk whose weights are in pw
+        for (int h = 0; h < HMAX; ++h) acc[i][h] = 0.f;
     auto add = [&](int t, u32x4 v) {
-        const f32x4 pa = *(const f32x4 *)&pw[t - c0][0], pb = *(const f32x4 *)&pw[t - c0][4];
-        const float p[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+        float p[HMAX];
+#pragma unroll
+        for (int h = 0; h < HMAX; h += 4) {
+            const f32x4 q = *(const f32x4 *)&pw[t * HMAX + h];
+            p[h] = q.x, p[h + 1] = q.y, p[h + 2] = q.z, p[h + 3] = q.w;
+        }
         const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const float a = bf16_to_f32(w4[q] & 0xffff), b = bf16_to_f32(w4[q] >> 16);
 #pragma unroll
-            for (int hd = 0; hd < 8; ++hd) {
-                zacc[2 * q][hd] += p[hd] * a;
-                zacc[2 * q + 1][hd] += p[hd] * b;
+            for (int h = 0; h < HMAX; ++h) {
+                acc[2 * q][h] += p[h] * a;
+                acc[2 * q + 1][h] += p[h] * b;
             }
         }
     };
-    for (; c0 < t1; c0 += kChunk) {
-        const int c1 = min(t1, c0 + kChunk);
-        if (c0 > t0) __syncthreads();  // every wave is done with the previous chunk's weights
-        for (int i = tid; i < (c1 - c0) * 8; i += 512) {
-            const int tt = i >> 3, hd = i & 7;
-            pw[tt][hd] = hd < H ? __expf(s[(size_t)(c0 + tt) * H + hd] - mh[hd]) * ih[hd] : 0.f;
-        }
-        __syncthreads();
-        int t = c0 + wave;
-        for (; t + 24 < c1; t += 32) {
-            u32x4 v[4] = {};
+    if (on) {
+        const uint16_t *col = xf + (size_t)c0 * D + 8 * g;
+        int t = slot;
+        for (; t + 3 * slots < n; t += 4 * slots) {
+            u32x4 v[4];
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-                if (on) v[k] = *(const u32x4 *)(xf + (size_t)(t + 8 * k) * D + 8 * lane);
+            for (int k = 0; k < 4; ++k) v[k] = *(const u32x4 *)(col + (size_t)(t + k * slots) * D);
 #pragma unroll
-            for (int k = 0; k < 4; ++k) add(t + 8 * k, v[k]);
+            for (int k = 0; k < 4; ++k) add(t + k * slots, v[k]);
         }
-        for (; t < c1; t += 8) {
-            u32x4 v = {};
-            if (on) v = *(const u32x4 *)(xf + (size_t)t * D + 8 * lane);
-            add(t, v);
-        }
+        for (; t < n; t += slots) add(t, *(const u32x4 *)(col + (size_t)t * D));
     }
-    // partials added in wave order
-    for (int w = 0; w < 8; ++w) {
-        if (wave == w && on) {
+    // the slots' partials added in slot order, then stored as whole rows
+    for (int sl = 0; sl < slots; ++sl) {
+        if (on && slot == sl) {
 #pragma unroll
-            for (int hd = 0; hd < 8; ++hd)
-                if (hd < H) {
-                    float *zr = z + hd * D + 8 * lane;
+            for (int h = 0; h < HMAX; ++h)
+                if (h < H) {
+                    float *zr = zl + h * D + 8 * g;
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) zr[i] = w == 0 ? zacc[i][hd] : zr[i] + zacc[i][hd];
+                    for (int i = 0; i < 8; ++i) zr[i] = sl == 0 ? acc[i][h] : zr[i] + acc[i][h];
                 }
         }
         __syncthreads();
     }
-    // pooled_h = z_h W_v[:, 64 h .. 64 h + 63]
-    for (int col = tid; col < D; col += 512) {
-        const float *zh = z + (col >> 6) * D;
-        float acc8[8] = {};
-        for (int f = 0; f < D; f += 8)
+    float *zo = zp + (size_t)blockIdx.x * H * D;
+    for (int i = 4 * tid; i < H * D; i += 4 * 256) *(f32x4 *)(zo + i) = *(const f32x4 *)(zl + i);
+}
+
+constexpr int kPoolMaxTiles = 128;  // tiles of one item at the largest context (32767 tokens)
+
+__global__ __launch_bounds__(256) void k_pool_finish(const float *__restrict__ zp, const float2 *__restrict__ zs,
+                                                     const int *__restrict__ itile, const uint16_t *__restrict__ wv,
+                                                     void *__restrict__ out, int out_bf16, size_t out_stride, int D,
+                                                     int H) {
+    __shared__ float zh[1024];
+    __shared__ float wt[kPoolMaxTiles];
+    __shared__ float red[4][64];
+    const int item = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int k0 = itile[item], nk = itile[item + 1] - k0;
+    char *orow = (char *)out + (size_t)item * out_stride;
+    const int col = 64 * h + lane;
+    if (nk == 0) {
+        if (tid < 64) {
+            if (out_bf16) ((uint16_t *)orow)[col] = 0;
+            else ((float *)orow)[col] = 0.f;
+        }
+        return;
+    }
+    // tile weights e^(m_tile - m_item) / L, L = sum over tiles of e^(m_tile - m_item) l_tile (tile order)
+    float mi = -INFINITY;
+    for (int k = 0; k < nk; ++k) mi = fmaxf(mi, zs[(size_t)(k0 + k) * H + h].x);
+    float L = 0.f;
+    for (int k = 0; k < nk; ++k) {
+        const float2 st = zs[(size_t)(k0 + k) * H + h];
+        L += __expf(st.x - mi) * st.y;
+    }
+    const float inv = 1.0f / L;
+    for (int k = tid; k < nk; k += 256) wt[k] = __expf(zs[(size_t)(k0 + k) * H + h].x - mi) * inv;
+    __syncthreads();
+    for (int f = tid; f < D; f += 256) {
+        float z = 0.f;
+        for (int k = 0; k < nk; ++k) z += wt[k] * zp[((size_t)(k0 + k) * H + h) * D + f];
+        zh[f] = z;
+    }
+    __syncthreads();
+    // pooled_h: lane = output column of the head, the four waves take quarters of the D inputs
+    const int q = D / 4, f0 = wave * q;
+    float acc8[8] = {};
+    for (int f = f0; f < f0 + q; f += 8)
 #pragma unroll
-            for (int k = 0; k < 8; ++k) acc8[k] += zh[f + k] * bf16_to_f32(wv[(size_t)(f + k) * D + col]);
-        const float accv = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
-        if (out_bf16) ((uint16_t *)orow)[col] = (uint16_t)f32_to_bf16(accv);
-        else ((float *)orow)[col] = accv;
+        for (int k = 0; k < 8; ++k) acc8[k] += zh[f + k] * bf16_to_f32(wv[(size_t)(f + k) * D + col]);
+    red[wave][lane] = ((acc8[0] + acc8[1]) + (acc8[2] + acc8[3])) + ((acc8[4] + acc8[5]) + (acc8[6] + acc8[7]));
+    __syncthreads();
+    if (wave == 0) {
+        const float v = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+        if (out_bf16) ((uint16_t *)orow)[col] = (uint16_t)f32_to_bf16(v);
+        else ((float *)orow)[col] = v;
     }
 }
 
-hipError_t launch_pool(const uint16_t *xf, const float *s, const int *cu, int count, const uint16_t *wv, void *out,
-                       int out_bf16, size_t out_stride, int D, int H, hipStream_t stream) {
+size_t pool_partial_bytes(int ntiles, int D, int H) { return (size_t)ntiles * H * D * 4; }
+size_t pool_stats_bytes(int ntiles, int H) { return (size_t)ntiles * H * 8; }
+
+hipError_t launch_pool(const uint16_t *xf, const float *s, const int *cu, const int2 *tiles, int ntiles,
+                       const int *itile, int count, const uint16_t *wv, void *out, int out_bf16, size_t out_stride,
+                       int D, int H, float *zp, float2 *zs, hipStream_t stream) {
     if (count == 0) return hipSuccess;
-    if (D <= 512 && D % 8 == 0 && H <= 8) {
-        k_pool_wide<<<count, 512, 0, stream>>>(xf, s, cu, wv, out, out_bf16, out_stride, D, H);
-        return hipGetLastError();
-    }
-    const size_t lds = ((size_t)H * D + 256 * (size_t)H + 2 * (size_t)H + 4) * sizeof(float);
-    const int C = (D + 255) / 256;
-    auto go = [&](auto kernel) -> hipError_t {
-        if (lds > 65536) {
+    if (D % 128 || D > 1024 || H * 64 != D || H > 16) return hipErrorInvalidValue;
+    if (ntiles > 0) {
+        auto go = [&](auto kernel, int hmax) -> hipError_t {
+            const size_t lds = ((size_t)kPoolTile * hmax + (size_t)hmax * D + 4 * (size_t)hmax) * sizeof(float);
             hipError_t e = hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
             if (e != hipSuccess) return e;
-        }
-        kernel<<<count, 256, lds, stream>>>(xf, s, cu, wv, out, out_bf16, out_stride, D, H);
-        return hipGetLastError();
-    };
-    if (H <= 2 && C <= 1) return go(k_pool<2, 1>);
-    if (H <= 8 && C <= 2) return go(k_pool<8, 2>);
-    if (H <= 16 && C <= 4) return go(k_pool<16, 4>);
-    return hipErrorInvalidValue;
+            kernel<<<ntiles, 256, lds, stream>>>(xf, s, cu, tiles, D, H, zp, zs);
+            return hipGetLastError();
+        };
+        hipError_t e = H <= 4 ? go(k_pool_part<4>, 4) : H <= 8 ? go(k_pool_part<8>, 8) : go(k_pool_part<16>, 16);
+        if (e != hipSuccess) return e;
+    }
+    k_pool_finish<<<dim3(count, H), 256, 0, stream>>>(zp, zs, itile, wv, out, out_bf16, out_stride, D, H);
+    return hipGetLastError();
 }
 
 }  // namespace ube

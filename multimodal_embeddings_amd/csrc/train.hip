@@ -465,6 +465,7 @@ __global__ __launch_bounds__(256) void k_sum_rows(const float *part, int blocks,
 // fp32 partials are stored as rows of out. Split over t into `splits` ranges of `chunk` tokens (a multiple
 // of 64); the last range's rows past T are zeroed in LDS.
 constexpr int kXtyStage = 512 + 1024;  // chunks: Y tile [64 t][64 n] | X tile [64 t][128 m]
+constexpr int kXtyLoads = 2 + 4;       // DMA loads per thread per stage (Y rounds + X rounds)
 
 __global__ __launch_bounds__(256, 2) void k_xty(const uint16_t *x, int ldx, const uint16_t *y, int ldy, int T, int M,
                                                 int N, float *partial, int chunk) {
@@ -500,9 +501,9 @@ __global__ __launch_bounds__(256, 2) void k_xty(const uint16_t *x, int ldx, cons
         const int buf = kt & 1, t0 = tb + kt * 64;
         if (kt + 1 < nk) {
             issue(t0 + 64, buf ^ 1);
-            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            wait_vmcnt<kXtyLoads>();  // this stage's loads are the older ones
         } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            wait_vmcnt<0>();
         }
         if (t0 + 64 > te) {  // rows past the range read as zero
             u32x4 *st = smem + buf * kXtyStage;
@@ -515,7 +516,6 @@ __global__ __launch_bounds__(256, 2) void k_xty(const uint16_t *x, int ldx, cons
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         lds_barrier();
-        if (kt + 1 < nk) issue(t0 + 64, buf ^ 1);
         const uint8_t *sY = (const uint8_t *)(smem + buf * kXtyStage), *sX = sY + 512 * 16;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -542,6 +542,7 @@ __global__ __launch_bounds__(256, 2) void k_xty(const uint16_t *x, int ldx, cons
 // rows (chunks swizzled by 4 (t % 4), which keeps the transpose reads of a 16-lane group on distinct banks);
 // two stages, the next one's DMA in flight during the current one's products.
 constexpr int kXtyWideStage = 2 * 2048;  // 16-byte chunks: Y tile [64 t][256 n] | X tile [64 t][256 m]
+constexpr int kXtyWideLoads = 4 + 4;     // DMA loads per thread per stage (Y rounds + X rounds)
 
 __global__ __launch_bounds__(512, 1) void k_xty256(const uint16_t *x, int ldx, const uint16_t *y, int ldy, int T,
                                                    int M, int N, float *partial, int chunk) {
@@ -580,9 +581,9 @@ __global__ __launch_bounds__(512, 1) void k_xty256(const uint16_t *x, int ldx, c
         const int buf = kt & 1, t0 = tb + kt * 64;
         if (kt + 1 < nk) {
             issue(t0 + 64, buf ^ 1);
-            asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+            wait_vmcnt<kXtyWideLoads>();  // this stage's loads are the older ones
         } else {
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+            wait_vmcnt<0>();
         }
         if (t0 + 64 > te) {  // rows past the range read as zero
             u32x4 *st = smem + buf * kXtyWideStage;

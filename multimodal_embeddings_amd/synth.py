@@ -55,25 +55,30 @@ class Weights:
 
 
 def _bf16_draw(rng, shape, std):
-    raw = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(std)
+    raw = rng.standard_normal(size=shape, dtype=np.float32) * np.asarray(std, np.float32)
     bits = to_bf16_bits(raw)
     return bits, bf16_bits_to_f32(bits)
 
 
 def make_weights(geometry: dict, seed: int = 0, std: float = 0.02,
-                 gain_jitter: float = 0.0, gain_seed: int = 7) -> Weights:
+                 gain_jitter: float = 0.0, gain_seed: int = 7, qk_std: float | None = None,
+                 pool_query_std: float | None = None, pool_wk_std: float | None = None) -> Weights:
     """Draw a model's weights in the canonical order.
 
     ``gain_jitter`` > 0 replaces the unit gains by 1 + jitter * N(0, 1)
     (from a separate stream, so the matrices stay the same).
+    ``qk_std`` (the q and k columns of every ``w_qkv``), ``pool_query_std`` and
+    ``pool_wk_std`` replace ``std`` for those tensors: the same standard-normal
+    draws scaled differently, so that the softmax of the blocks and of the pool
+    is sharp (with std 0.02 both are nearly uniform).
     """
     g = configs.complete(geometry)
     D, F, N = g["hidden"], g["ffn"], g["depth"]
     rng = np.random.default_rng(seed)
     w = Weights(g)
 
-    def put(name, shape, layer_list=False):
-        bits, f32 = _bf16_draw(rng, shape, std)
+    def put(name, shape, layer_list=False, scale=None):
+        bits, f32 = _bf16_draw(rng, shape, std if scale is None else scale)
         if layer_list:
             w.bits.setdefault(name, []).append(bits)
             w.f32.setdefault(name, []).append(f32)
@@ -88,14 +93,18 @@ def make_weights(geometry: dict, seed: int = 0, std: float = 0.02,
     for name in ("w_qkv", "w_o", "w_gate", "w_up", "w_down"):
         w.bits[name] = []
         w.f32[name] = []
+    qkv_scale = None
+    if qk_std is not None:
+        qkv_scale = np.full((1, 3 * D), std, np.float32)
+        qkv_scale[0, :2 * D] = qk_std
     for _ in range(N):
-        put("w_qkv", (D, 3 * D), True)
+        put("w_qkv", (D, 3 * D), True, qkv_scale)
         put("w_o", (D, D), True)
         put("w_gate", (D, F), True)
         put("w_up", (D, F), True)
         put("w_down", (F, D), True)
-    put("pool_query", (D,))
-    put("pool_wk", (D, D))
+    put("pool_query", (D,), scale=pool_query_std)
+    put("pool_wk", (D, D), scale=pool_wk_std)
     put("pool_wv", (D, D))
     if g.get("token_width"):
         put("token_head", (D, g["token_width"]))

@@ -9,6 +9,7 @@ import pytest
 
 import oracle
 from multimodal_embeddings_amd import configs, synth
+from tests import sharp_cases as S
 from tests.gpu_util import check_pooled, device_bytes, say
 
 pytestmark = pytest.mark.gpu
@@ -157,9 +158,17 @@ def test_throughput_batch_sampled_parity_invariance_determinism(ube):
     sub = synth.subset(batch, pick)
     rows_s, _ = ube.text_encode(model, arena, device_bytes(sub.data), sub.offsets)
     np.testing.assert_array_equal(_pooled(rows_s), full[pick])  # batch invariance
-    sample = synth.subset(batch, [0, 517])
+    sample_rows = _sample(1024, 16, seed=3, always=(0, 517, 1023))
+    sample = synth.subset(batch, sample_rows)
     want, _ = oracle.encode_text(w, sample.data, sample.offsets)
-    check_pooled(full[[0, 517]], want, "throughput")
+    check_pooled(full[sample_rows], want, "throughput")
+
+
+def _sample(n, k, seed, always=()):
+    """k seeded distinct item indices out of n, including `always`."""
+    rng = np.random.default_rng(seed)
+    rest = [int(i) for i in rng.permutation(n) if int(i) not in always]
+    return sorted(list(always) + rest[:k - len(always)])
 
 
 # ------------------------------------------------------------------ media
@@ -171,7 +180,7 @@ def test_image_batch_sampled_parity(ube):
     rows, stats = ube.encode(model, arena, _dev(batch))
     assert stats == (0, 128 * 256) and rows.count == 128
     full = _pooled(rows)
-    pick = [0, 77]
+    pick = _sample(128, 8, seed=4, always=(0, 77, 127))
     sub = synth.subset(batch, pick)
     want, _ = oracle.encode_media(w, sub)
     check_pooled(full[pick], want, "image")
@@ -228,23 +237,66 @@ def _video_full(ube, name):
     return w, batch, _pooled(rows)
 
 
+VIDEO_SAMPLE = [0, 11]
+
+
 def test_video_full_batch_sampled_parity(ube):
     w, batch, full = _video_full(ube, "video1024")
-    sub = synth.subset(batch, [0])
+    sub = synth.subset(batch, VIDEO_SAMPLE)
     want, _ = oracle.encode_media(w, sub)
-    check_pooled(full[[0]], want, "video")
+    check_pooled(full[VIDEO_SAMPLE], want, "video")
 
 
 def test_video_e4m3_full_batch_sampled_parity(ube):
     w, batch, full = _video_full(ube, "video1024_e4m3")
-    sub = synth.subset(batch, [0])
+    sub = synth.subset(batch, VIDEO_SAMPLE)
     want, _ = oracle.encode_media(w, sub)
     from tests.gpu_util import row_cos
-    say(f"  e4m3 clip 0: cos {row_cos(full[[0]], want)[0]:.6f}, max |diff| {np.abs(full[0] - want[0]).max():.3e}, "
-        f"pooled rms {np.sqrt((want ** 2).mean()):.3e}")
+    for j, i in enumerate(VIDEO_SAMPLE):
+        say(f"  e4m3 clip {i}: cos {row_cos(full[[i]], want[[j]])[0]:.6f}, max |diff| "
+            f"{np.abs(full[i] - want[j]).max():.3e}, pooled rms {np.sqrt((want[j] ** 2).mean()):.3e}")
     _, _, full_bf16 = _video_full(ube, "video1024")
     say(f"  e4m3 vs bf16 run, all clips: min cos {row_cos(full, full_bf16).min():.5f}")
-    check_pooled(full[[0]], want, "video-e4m3", e4m3=True)
+    check_pooled(full[VIDEO_SAMPLE], want, "video-e4m3", e4m3=True)
+
+
+# ------------------------------------------------------------------ pool and rotary that matter
+#
+# With std-0.02 weights the pool and block softmaxes are nearly uniform; these cases (tests/sharp_cases.py)
+# sharpen them, and tests/test_oracle_sensitivity.py shows on the CPU that a mean pool or wrongly wired
+# rotary coordinates miss these bars by at least ten times.
+
+
+@pytest.mark.parametrize("kind", ["text", "image", "video"])
+def test_sharp_pool_matches_oracle(ube, kind):
+    w, batch = S.pool_case(kind)
+    model, arena = ube.Model(w, 0), ube.Arena(0)
+    rows, _ = ube.encode(model, arena, _dev(batch))
+    x0, pos, cu = S.frontend(w, batch)
+    want = oracle.forward(w, x0, pos, cu)
+    check_pooled(_pooled(rows), want, f"sharp pool {kind}")
+    arena.close()
+    model.close()
+
+
+@pytest.mark.parametrize("kind", ["text", "image", "video"])
+def test_sharp_rotary_residual_trace_matches_oracle(ube, kind):
+    import torch
+    w, batch = S.rotary_case(kind)
+    g = w.geometry
+    model, arena = ube.Model(w, 0), ube.Arena(0)
+    x0, pos, cu = S.frontend(w, batch)
+    T, D = x0.shape
+    trace = torch.zeros(((g["depth"] + 1) * T * D,), dtype=torch.float32, device="cuda:0")
+    ube.encode(model, arena, _dev(batch), trace=trace)
+    tr = trace.cpu().numpy().astype(np.float64).reshape(g["depth"] + 1, T, D)
+    ref = S.residual_trace(w, x0, pos, cu)
+    for d in range(1, g["depth"] + 1):
+        rel = np.linalg.norm(tr[d] - ref[d - 1]) / np.linalg.norm(ref[d - 1])
+        say(f"  {kind}: residual after block {d}: relative error {rel:.2e} (bar {S.TRACE_REL:.1e})")
+        assert rel <= S.TRACE_REL
+    arena.close()
+    model.close()
 
 
 # ------------------------------------------------------------------ 4096-byte rows, packed segments

@@ -177,3 +177,88 @@ def test_gemm_e4m3_matches_float64_matmul_of_decoded_codes(M, N, K):
     # bf16 output rounding plus the fp8 MFMA's own summation, which keeps fewer bits
     # than fp32 (measured <= 0.2% of sum|products|; E4M3 inputs carry 3 mantissa bits)
     assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 4e-3 * scale)
+
+
+def _positions(kind, M, rng):
+    """Coordinates [M x 3] of seeded tokens: text positions restart per item; image (row, col) on a 16 x 16
+    grid; video (frame, row, col) on 8 frames of 14 x 14."""
+    t = np.arange(M)
+    if kind == "text":
+        starts = np.sort(rng.choice(np.arange(1, M), size=3, replace=False))
+        item_start = np.zeros(M, np.int64)
+        for s in starts:
+            item_start[s:] = s
+        return np.stack([t - item_start, 0 * t, 0 * t], 1)
+    if kind == "image":
+        u = t % 256
+        return np.stack([u // 16, u % 16, 0 * t], 1)
+    u = t % 1568
+    return np.stack([u // 196, (u // 14) % 14, u % 14], 1)
+
+
+@pytest.mark.parametrize("M,D,axes,kind", [(300, 128, 1, "text"), (1000, 512, 1, "text"), (700, 768, 2, "image"),
+                                           (1700, 1024, 3, "video"), (1, 1024, 3, "video")])
+def test_qkv_rotary_matches_oracle_rope(M, D, axes, kind):
+    """The QKV product with its rotary epilogue against the oracle's rotation of a float64 product, element by
+    element, at one, two and three rotary axes; a rotation with the axes exchanged (or none) misses the bar."""
+    import multimodal_embeddings_amd as ube
+    torch = _torch()
+    say(f"qkv+rotary M={M} D={D} axes={axes} ({kind})")
+    rng = np.random.default_rng(M + D + axes)
+    Mp = (M + 255) // 256 * 256
+    K = D
+    wb, wf = _bf16(rng, (3 * D, K), 1.0 / np.sqrt(K))
+    xb, xf = _bf16(rng, (Mp, K))
+    pos = _positions(kind, M, rng)
+    pos4 = np.zeros((M, 4), np.int16)
+    pos4[:, :3] = pos
+    positions = int(pos.max()) + 1
+    qk = torch.empty((M, 2 * D), dtype=torch.bfloat16, device="cuda:0")
+    vt = torch.full((D, Mp), float("nan"), dtype=torch.bfloat16, device="cuda:0")
+    ube.step_qkv_rotary(_to_dev_bf16(wb), _to_dev_bf16(xb), M, D, K, pos4, axes, 10000.0, positions, qk, vt, Mp)
+    torch.cuda.synchronize()
+    got = _from_dev_bf16(qk)
+    got_v = _from_dev_bf16(vt)
+    prod = xf[:M] @ wf.T
+    heads = D // 64
+    p32 = pos.astype(np.int32)
+    ref_q = oracle.rope(prod[:, :D], p32, heads, 64, axes, 10000.0)
+    ref_k = oracle.rope(prod[:, D:2 * D], p32, heads, 64, axes, 10000.0)
+    ref = np.concatenate([ref_q, ref_k], 1)
+    rms = np.sqrt((ref ** 2).mean())
+    err = np.abs(got - ref)
+    # one bf16 step of the value (rounding alone reaches half of it) plus fp32 cancellation in the rotation
+    bar = 2.0 ** -7 * np.abs(ref) + 1e-4 * rms
+    say(f"  q|k max |err| {err.max():.3e} (rms {rms:.3f}); worst err / bar {(err / bar).max():.3f}")
+    assert np.all(err <= bar)
+    # v feature-major, zero past M up to the 256-token boundary
+    v_err = np.abs(got_v[:, :M] - prod[:, 2 * D:].T)
+    assert np.all(v_err <= 2.0 ** -7 * np.abs(prod[:, 2 * D:].T) + 1e-4 * rms)
+    assert not got_v[:, M:Mp].any()
+    # teeth: the rotation is not the identity, and exchanging two axes (when there are two) is far off the bar
+    if M > 1:
+        plain = np.concatenate([prod[:, :D], prod[:, D:2 * D]], 1)
+        assert (np.abs(got - plain) > bar).mean() > 0.5
+        if axes > 1:
+            sw = p32[:, [1, 0, 2]]
+            alt = np.concatenate([oracle.rope(prod[:, :D], sw, heads, 64, axes, 10000.0),
+                                  oracle.rope(prod[:, D:2 * D], sw, heads, 64, axes, 10000.0)], 1)
+            assert (np.abs(got - alt) > bar).mean() > 0.3
+
+
+def test_qkv_rotary_refuses_coordinates_outside_the_table():
+    import multimodal_embeddings_amd as ube
+    torch = _torch()
+    D = K = 128
+    w = torch.zeros((3 * D, K), dtype=torch.bfloat16, device="cuda:0")
+    x = torch.zeros((256, K), dtype=torch.bfloat16, device="cuda:0")
+    qk = torch.empty((4, 2 * D), dtype=torch.bfloat16, device="cuda:0")
+    vt = torch.empty((D, 256), dtype=torch.bfloat16, device="cuda:0")
+    pos = np.zeros((4, 4), np.int16)
+    pos[2, 1] = 50
+    with pytest.raises(ube.UbeError) as e:
+        ube.step_qkv_rotary(w, x, 4, D, K, pos, 2, 10000.0, 50, qk, vt, 256)
+    assert e.value.status == "invalid_argument"
+    pos[2, 1] = -1
+    with pytest.raises(ube.UbeError):
+        ube.step_qkv_rotary(w, x, 4, D, K, pos, 2, 10000.0, 64, qk, vt, 256)
