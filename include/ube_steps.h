@@ -49,6 +49,20 @@ ube_status_t ube_step_rmsnorm(float const *x, float const *gain, void *h, size_t
 ube_status_t ube_step_attention(void const *q, void const *k, size_t ldqk, void const *vt, size_t ldvt, void *o,
                                 size_t ldo, uint32_t const *cu_host, size_t count, size_t heads, void *stream);
 
+/* The attention step above for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that must not call hipMalloc): same
+ * arguments, same kernel, same results bit for bit. The item bounds and the
+ * 256-token tile list go to a fixed 1 MiB buffer the library holds on every GPU it
+ * runs on (a static device array, kept until the process ends) instead of memory
+ * allocated per call; it calls no hipMalloc, hipFree or hipHostMalloc. Limits:
+ * count + 2 + 2 * tiles <= 262144 (tiles = sum over items of ceil(length / 256)),
+ * else invalid_argument with nothing launched. Every call on one GPU shares that
+ * buffer: calls that overlap on one GPU race (this call waits for `stream` before
+ * it returns, so calls made one after another are safe). Synchronous. */
+ube_status_t ube_step_attention_static(void const *q, void const *k, size_t ldqk, void const *vt, size_t ldvt,
+                                       void *o, size_t ldo, uint32_t const *cu_host, size_t count, size_t heads,
+                                       void *stream);
+
 /* E4M3 activation rows ("UForm" page, "Precision by Design": an e4m3 model runs
  * its blocks in Float8): in bf16 [T x W] -> codes [T x W] (OCP E4M3FN bytes) and
  * scales[T] = amax_row / 448, code = nearest-even E4M3 of value * (448 / amax_row)

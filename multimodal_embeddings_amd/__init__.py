@@ -191,6 +191,7 @@ _SIGNATURES = {
     "ube_step_attention": ([VP, VP, SZ, VP, SZ, VP, SZ, VP, SZ, SZ, VP], C.c_int),
     "ube_step_quantize_e4m3": ([VP, VP, VP, SZ, SZ, VP], C.c_int),
     "ube_step_gemm_e4m3": ([VP, C.c_float, VP, VP, VP, SZ, SZ, SZ, VP], C.c_int),
+    "ube_step_attention_static": ([VP, VP, SZ, VP, SZ, VP, SZ, VP, SZ, SZ, VP], C.c_int),
     "ube_step_qkv_rotary": ([VP, VP, SZ, SZ, SZ, VP, SZ, C.c_float, SZ, VP, VP, SZ, VP], C.c_int),
     "ube_kernel_timer_start": ([C.c_int, SZ], C.c_int),
     "ube_kernel_timer_stop": ([C.POINTER(C.c_double), C.POINTER(SZ)], C.c_int),
@@ -683,6 +684,13 @@ def step_attention(q, k, ldqk, vt, ldvt, o, ldo, cu, heads, stream=None):
     cu = np.ascontiguousarray(cu, dtype=np.uint32)
     _step(lib().ube_step_attention(_ptr(q), _ptr(k), ldqk, _ptr(vt), ldvt, _ptr(o), ldo, cu.ctypes.data,
                                    len(cu) - 1, heads, _stream_handle(stream)))
+
+
+def step_attention_static(q, k, ldqk, vt, ldvt, o, ldo, cu, heads, stream=None):
+    """ube_step_attention_static: the attention step with its tile list in the library's fixed buffer."""
+    cu = np.ascontiguousarray(cu, dtype=np.uint32)
+    _step(lib().ube_step_attention_static(_ptr(q), _ptr(k), ldqk, _ptr(vt), ldvt, _ptr(o), ldo, cu.ctypes.data,
+                                          len(cu) - 1, heads, _stream_handle(stream)))
 
 
 def step_quantize_e4m3(x, codes, scales, T, W, stream=None):

@@ -10,7 +10,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libube.so")
-SOURCES = ["kernels.hip", "contrastive.hip", "train.hip", "engine.cpp"]
+SOURCES = ["kernels.hip", "contrastive.hip", "train.hip", "static_scratch.hip", "engine.cpp"]
 HEADERS = ["kernels.h", "device.h", "contrastive.h", "train.h"]
 
 # Packed fp32 VALU forms stay off (ordinary fp32 code only); gfx950 only.
