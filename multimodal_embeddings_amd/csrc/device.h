@@ -74,6 +74,11 @@ __device__ __forceinline__ void lds_dma16(const void *gptr, void *lds_base) {
     __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
+// One 4-byte DMA per lane: lane i's dword lands at lds_base + 4 i (lds_base uniform).
+__device__ __forceinline__ void lds_dma4(const void *gptr, void *lds_base) {
+    __builtin_amdgcn_global_load_lds(gptr, (__attribute__((address_space(3))) void *)lds_base, 4, 0, 0);
+}
+
 // Waits until at most N vector memory operations of this wave are outstanding (loads
 // complete in issue order, so the oldest ones are then done).
 template <int N>

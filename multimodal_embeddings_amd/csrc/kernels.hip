@@ -376,10 +376,47 @@ hipError_t launch_rmsnorm_e4m3(const float *x, const float *gain, uint8_t *h8, f
     return hipGetLastError();
 }
 
+// The same for rows of NV * 512 values: the row's loads are all issued before the maximum is taken, and the
+// codes are formed from the registers (one read of the row).
+template <int NV>
+__global__ __launch_bounds__(256) void k_quantize_rows_fixed(const uint16_t *__restrict__ in, uint8_t *__restrict__ out,
+                                                             float *__restrict__ scale, int T) {
+    constexpr int W = NV * 512;
+    const int lane = threadIdx.x & 63;
+    const int waves = gridDim.x * 4;
+    for (int t = blockIdx.x * 4 + (threadIdx.x >> 6); t < T; t += waves) {
+        const uint16_t *row = in + (size_t)t * W;
+        float v[NV][8];
+#pragma unroll
+        for (int c = 0; c < NV; ++c) RowIO<8>::load_bf16(row + c * 512 + lane * 8, v[c]);
+        float amax = 0.f;
+#pragma unroll
+        for (int c = 0; c < NV; ++c)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(v[c][i]));
+        amax = wave_max(amax);
+        const float q = amax > 0.f ? 448.0f / amax : 0.f;
+        if (lane == 0) scale[t] = amax / 448.0f;
+#pragma unroll
+        for (int c = 0; c < NV; ++c)
+            *(u32x2 *)(out + (size_t)t * W + c * 512 + lane * 8) =
+                u32x2{pack4_e4m3(v[c][0] * q, v[c][1] * q, v[c][2] * q, v[c][3] * q),
+                      pack4_e4m3(v[c][4] * q, v[c][5] * q, v[c][6] * q, v[c][7] * q)};
+    }
+}
+
 hipError_t launch_quantize_rows(const uint16_t *in, uint8_t *out, float *scale, int T, int W, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     if (W % 8) return hipErrorInvalidValue;
-    k_quantize_rows<<<row_grid(T), 256, 0, stream>>>(in, out, scale, T, W);
+    switch (W % 512 == 0 ? W / 512 : 0) {
+        case 1: k_quantize_rows_fixed<1><<<row_grid(T), 256, 0, stream>>>(in, out, scale, T); break;
+        case 2: k_quantize_rows_fixed<2><<<row_grid(T), 256, 0, stream>>>(in, out, scale, T); break;
+        case 3: k_quantize_rows_fixed<3><<<row_grid(T), 256, 0, stream>>>(in, out, scale, T); break;
+        case 4: k_quantize_rows_fixed<4><<<row_grid(T), 256, 0, stream>>>(in, out, scale, T); break;
+        case 6: k_quantize_rows_fixed<6><<<row_grid(T), 256, 0, stream>>>(in, out, scale, T); break;
+        case 8: k_quantize_rows_fixed<8><<<row_grid(T), 256, 0, stream>>>(in, out, scale, T); break;
+        default: k_quantize_rows<<<row_grid(T), 256, 0, stream>>>(in, out, scale, T, W); break;
+    }
     return hipGetLastError();
 }
 
@@ -720,6 +757,14 @@ constexpr int kResPitch = 1040;               // fp32 rows of 256 values + 16 B
 constexpr int kResSlice = 64 * kResPitch;     // 64 tokens
 constexpr int kStageBytes = 256 * kQkPitch;   // 135,168 >= 2 * kResSlice
 constexpr int kSmemBytes = kStageBytes + 256 * 4;
+// QKV epilogue: the tile's rotary table rows (256 B of (cos, sin) pairs per token, 16 B
+// of padding so that 16 lanes reading 16 consecutive rows cover all 64 banks), then
+// one staging area per wave of 32 rows of 64 bf16 features.
+constexpr int kRopePitch = 272;
+constexpr int kRopeBytes = 256 * kRopePitch;           // 69,632
+constexpr int kQkStagePitch = 144;                     // 128 B + 16 B
+constexpr int kQkStageBytes = 32 * kQkStagePitch;      // 4,608 per wave
+static_assert(kRopeBytes + 8 * kQkStageBytes <= kStageBytes, "QKV epilogue LDS");
 
 // K loop of one tile. SWAP = false: MFMA A operand = weight rows, B = token
 // rows, so lane (l32, hh) holds features 8 i + 4 hh + j of token l32 in register
@@ -973,22 +1018,66 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
         }
     }
 
-    if constexpr (EPI == kEpiStore || EPI == kEpiQkv) {
-        // ---- token-major bf16 rows of 256 features (q and k rotated)
+    if constexpr (EPI == kEpiQkv) {
+        // ---- rotated q, k rows. The tile's 256 rotary table rows (32 (cos, sin) pairs per token, each pair
+        // from the row of its axis' coordinate) go into LDS once, one 4-byte DMA per lane and token: wave
+        // (wm, wn) fetches tokens 128 wm + 32 wn .. + 31, whose coordinates its lanes loaded before the K
+        // loop (tm = wn). Then every wave rotates its 128 tokens x 64 features from LDS and stores them
+        // through a wave-private staging area, 32 tokens at a time, as whole 128-byte row segments.
+        {
+            const u32x2 mine = wn == 0 ? pw[0] : wn == 1 ? pw[1] : wn == 2 ? pw[2] : pw[3];
+            const int pair = lane >> 1;
+            const int axis = pair < a.sec0 ? 0 : (pair < a.sec0 + a.sec1 ? 1 : 2);
+            const uint8_t *rope = (const uint8_t *)a.rope + lane * 4;
+#pragma unroll
+            for (int r = 0; r < 32; ++r) {
+                const uint32_t px = (uint32_t)__builtin_amdgcn_readlane((int)mine.x, r);
+                const uint32_t py = (uint32_t)__builtin_amdgcn_readlane((int)mine.y, r);
+                const int p = axis == 0 ? (int)(int16_t)(px & 0xffff)
+                                        : (axis == 1 ? (int)(int16_t)(px >> 16) : (int)(int16_t)(py & 0xffff));
+                lds_dma4(rope + (size_t)p * 256, L + (wm * 128 + wn * 32 + r) * kRopePitch);
+            }
+            wait_vmcnt<0>();
+            lds_barrier();
+        }
         const float wsc = FP8 ? a.w_scale : 1.0f;
-        const bool one_axis = a.sec0 >= 32;
+        uint8_t *stage = L + kRopeBytes + wave * kQkStageBytes;
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) {
             const int t = wm * 128 + tm * 32 + l32;
             const float k = fac[tm] * wsc;
-            // rotary table row of each axis for this token, offset by the lane half's
-            // first pair (hh * 2): pair 4 i + 16 tn + q + 2 hh is then rb[axis][4 i + 16 tn + q]
-            const float2 *rb[3] = {a.rope, a.rope, a.rope};
-            if constexpr (EPI == kEpiQkv) {
-                rb[0] = a.rope + (int)(int16_t)(pw[tm].x & 0xffff) * 32 + hh * 2;
-                rb[1] = a.rope + (int)(int16_t)(pw[tm].x >> 16) * 32 + hh * 2;
-                rb[2] = a.rope + (int)(int16_t)(pw[tm].y & 0xffff) * 32 + hh * 2;
+            const uint8_t *row = L + t * kRopePitch + hh * 16;  // pairs 2 hh, 2 hh + 1 of each group of 4
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int cl = tn * 32 + i * 8 + hh * 4;  // feature within the wave's 64
+                    float o[4];
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) o[j] = acc[tn][tm][i * 4 + j] * k;
+                    const f32x4 e = *(const f32x4 *)(row + (tn * 16 + i * 4) * 8);
+                    const float2 cs[2] = {float2{e.x, e.y}, float2{e.z, e.w}};
+                    rotate4(o, cs);
+                    *(u32x2 *)(stage + l32 * kQkStagePitch + cl * 2) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
+                }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int it = 0; it < 4; ++it) {
+                const int chunk = it * 64 + lane, r = chunk >> 3, part = chunk & 7;
+                const int m = m0 + wm * 128 + tm * 32 + r;
+                const u32x4 v = *(const u32x4 *)(stage + r * kQkStagePitch + part * 16);
+                if (m < a.M)
+                    __builtin_nontemporal_store(v, (u32x4 *)(a.out_bf16 + (size_t)m * a.ld_out + n0 + wn * 64 + part * 8));
             }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // staging read back before the next tm writes it
+        }
+    } else if constexpr (EPI == kEpiStore) {
+        // ---- token-major bf16 rows of 256 features
+        const float wsc = FP8 ? a.w_scale : 1.0f;
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) {
+            const int t = wm * 128 + tm * 32 + l32;
+            const float k = fac[tm] * wsc;
 #pragma unroll
             for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
@@ -997,23 +1086,6 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
                     float o[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) o[j] = acc[tn][tm][i * 4 + j] * k;
-                    if constexpr (EPI == kEpiQkv) {
-                        float2 cs[2];
-                        if (one_axis) {
-                            // one rotary axis (text): both (cos, sin) entries in one 16-byte load
-                            const f32x4 e = *(const f32x4 *)(rb[0] + tn * 16 + i * 4);
-                            cs[0] = float2{e.x, e.y};
-                            cs[1] = float2{e.z, e.w};
-                        } else {
-#pragma unroll
-                            for (int q = 0; q < 2; ++q) {
-                                const int jp = tn * 16 + i * 4 + q, pair = jp + hh * 2;
-                                const float2 *b = pair < a.sec0 ? rb[0] : (pair < a.sec0 + a.sec1 ? rb[1] : rb[2]);
-                                cs[q] = b[jp];
-                            }
-                        }
-                        rotate4(o, cs);
-                    }
                     *(u32x2 *)(L + t * kQkPitch + c * 2) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
                 }
         }
