@@ -1303,6 +1303,8 @@ __device__ __forceinline__ int perm32(int r) {  // r = 8 i + 4 h + j
     return (i >> 1) * 16 + h * 8 + (i & 1) * 4 + j;
 }
 
+constexpr float kRescaleLog2 = 8.0f;  // attention: largest weight allowed above the reference, log2 units
+
 __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                       int ldqk, const uint16_t *__restrict__ vt, int ldvt,
                                                       uint16_t *__restrict__ o, int ldo, const int *__restrict__ cu,
@@ -1320,6 +1322,7 @@ __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict
 
     const int qbase = tile.y + wave * 32;
     const bool active = qbase < k1;
+    const bool qvalid = qbase + l32 < k1;
     // queries pre-scaled by c = log2(e) / sqrt(64): scores come out of the MFMAs in
     // base-2 logit units
     const float c = 0.18033688011112042f;
@@ -1377,10 +1380,15 @@ __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kk][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // the first tile sets the running max; later ones move it only where some
-        // score exceeds it (then the output and the row sum are rescaled)
+        // the first tile sets the reference max; later ones move it only when some
+        // score exceeds it by more than 2^8 in weight (then the output and the row sum
+        // are rescaled). Below that the weights may exceed 1 by up to 2^8, which the
+        // bf16 weights and fp32 sums hold exactly as well; the softmax does not depend
+        // on the reference, and most tiles skip the rescale.
+        // (only queries inside the item vote: the lanes past its end hold whatever rows follow it, and
+        // must not change the reference of the others, or a row would depend on its batch)
         const float d = first ? mx : fmaxf(mx, 0.f);
-        if (first || __any(d > 0.f)) {
+        if (first || __any(qvalid && d > kRescaleLog2)) {
             m_run += d;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) S[kk] -= d;
