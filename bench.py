@@ -206,7 +206,7 @@ def bench_maxsim(args):
         t0 = time.perf_counter()
         oracle.maxsim(host, off_h[:nq + 1], host, off_h, prefix=0, span=span)
         dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": nq * n / dt, "unit": "pairs/s", "cores": threads, "kind": "oracle",
+        out["cpu_baseline"] = {"value": nq * n / dt, "unit": "pairs/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": f"queries 0-{nq - 1} against all {n} documents (float64 oracle, {dt:.1f} s)"}
     else:
         out["cpu_baseline"] = None
@@ -298,7 +298,7 @@ def bench_siglip(args):
         S.siglip(batch.emb, batch.anchor_begin, A, widths, configs.SIGLIP_TEMPERATURE, configs.SIGLIP_BIAS,
                  head(batch.attract), head(batch.repel), head(batch.ignore, False))
         dt = time.perf_counter() - t0
-        out["cpu_baseline"] = {"value": A * n / dt, "unit": "pairs/s", "cores": threads, "kind": "oracle",
+        out["cpu_baseline"] = {"value": A * n / dt, "unit": "pairs/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": f"anchors 0-{A - 1} against all {n} items, loss and gradient "
                                          f"(float64 oracle, {dt:.1f} s)"}
     else:
@@ -405,7 +405,7 @@ def bench_train(args):
         TR.text_backward(weights, sub.data, sub.offsets, np.ones((rows_s, D)))
         dt = time.perf_counter() - t0
         toks = int(sub.offsets[-1])
-        out["cpu_baseline"] = {"value": toks / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        out["cpu_baseline"] = {"value": toks / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
                                "sample": f"rows 0-{rows_s - 1} ({toks} bytes): float64 forward and autograd backward "
                                          f"({dt:.1f} s; the Adafactor update not included)"}
     else:
