@@ -35,13 +35,22 @@ def _model(ube, name, **kw):
     return _MODELS[key]
 
 
+# Per-token rows are not averaged over an item as the pooled rows are: besides the pooled-row bar's
+# absolute part, each value may carry one bf16 step of its own magnitude (the blocks store every activation
+# in bf16, and a single token's state keeps the rounding that pooling averages away).
+TOKEN_REL = 2.0 ** -7
+
+
 def _check_rows(got, want, label):
     got = np.asarray(got, np.float64)
     cos = row_cos(got, want)
-    err = np.abs(got - want).max() if want.size else 0.0
-    say(f"[{label}] rows {len(want)}: min cos {cos.min() if len(cos) else 1:.6f}, max |diff| {err:.3e}")
+    diff = np.abs(got - want)
+    err = diff.max() if want.size else 0.0
+    ratio = (diff / (ABS_MAX + TOKEN_REL * np.abs(want))).max() if want.size else 0.0
+    say(f"[{label}] rows {len(want)}: min cos {cos.min() if len(cos) else 1:.6f}, max |diff| {err:.3e}, "
+        f"worst |diff| / bar {ratio:.3f}")
     assert cos.min() >= COS_MIN, (label, cos.min())
-    assert err <= ABS_MAX, (label, err)
+    assert ratio <= 1.0, (label, err, ratio)
 
 
 def _oracle_token_outputs(w, data, offsets):
