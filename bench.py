@@ -73,7 +73,21 @@ def kernel_flops_per_launch(kernel, g, T, lengths):
         return 2.0 * T * D * D
     if kernel == "attention":
         return 4.0 * float(np.sum(np.asarray(lengths, np.float64) ** 2)) * D
-    raise ValueError(kernel)
+    if kernel == "gemm_patch":
+        return 2.0 * T * g["patch_side"] * g["patch_side"] * g["channels"] * D
+    return None  # not a contraction: see kernel_bytes_per_launch
+
+
+def kernel_bytes_per_launch(kernel, g, T, count):
+    """Algorithmic HBM bytes of one launch of a row kernel (what the step must read and write)."""
+    D, H = g["hidden"], g["heads"]
+    if kernel == "gather":  # byte in; fp32 row, its bf16 copy, the row's sum-of-squares parts, positions out
+        return T * (1 + 4 * D + 2 * D + 4 * 16 + 8)
+    if kernel == "final_norm":  # fp32 row in; bf16 normalised row and the H pool scores out
+        return T * (4 * D + 2 * D + 4 * H)
+    if kernel == "pool":  # normalised rows and scores in; pooled fp32 rows out
+        return T * (2 * D + 4 * H) + count * D * 4
+    raise ValueError(f"no roofline for kernel {kernel}")
 
 
 def source_digest(kernel="gemm"):
@@ -514,7 +528,6 @@ def main():
 
     kflops = kernel_flops_per_launch(args.kernel, g, T, lengths)
     avg_s = kms / max(launches, 1) / 1e3
-    achieved = kflops / avg_s / 1e12
     # E4M3 models run the block projections on fp8 MFMA (twice the bf16 rate); attention, the patch
     # projection and the pool stay bf16. Utilisation = the time at each precision's peak / the time taken.
     e4m3 = g["quantization"] == "e4m3"
@@ -543,9 +556,14 @@ def main():
         "mfma_util": ideal_s / (ms / 1e3),
         "flops_per_step": flops,
         "fp8_flops_per_step": fp8_flops,
-        "roofline": {"kernel": args.kernel, "bound": "mfma", "achieved": achieved, "peak": kpeak / 1e12,
-                     "unit": "TFLOP/s", "frac": achieved / (kpeak / 1e12), "traffic": traffic,
-                     "avg_launch_ms": avg_s * 1e3, "launches": launches},
+        "roofline": ({"kernel": args.kernel, "bound": "mfma", "achieved": kflops / avg_s / 1e12,
+                      "peak": kpeak / 1e12, "unit": "TFLOP/s", "frac": kflops / avg_s / kpeak, "traffic": traffic,
+                      "avg_launch_ms": avg_s * 1e3, "launches": launches} if kflops is not None else
+                     {"kernel": args.kernel, "bound": "hbm",
+                      "achieved": kernel_bytes_per_launch(args.kernel, g, T, batch.count) / avg_s / 1e9,
+                      "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                      "frac": kernel_bytes_per_launch(args.kernel, g, T, batch.count) / avg_s / PEAK_HBM,
+                      "traffic": traffic, "avg_launch_ms": avg_s * 1e3, "launches": launches}),
     }
     if per_kernel:
         out["per_kernel_ms"] = per_kernel

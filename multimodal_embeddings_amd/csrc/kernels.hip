@@ -14,6 +14,8 @@
 // sits in lane l, register r = 4i + j at row 8i + 4(l / 32) + j, column l % 32.
 #include <hip/hip_runtime.h>
 #include <math.h>
+
+#include <algorithm>
 #include <stdint.h>
 
 #include "device.h"
@@ -431,8 +433,10 @@ hipError_t launch_final_norm_scores(const float *x, const float *gain, const flo
                                     float *states, int T, int D, int H, float eps, hipStream_t stream) {
     if (T == 0) return hipSuccess;
     const size_t lds = (size_t)H * D * sizeof(float);
-    // four rows per wave: a quarter of the row kernels' grid
-    const int grid = row_grid((T + 3) / 4);
+    // four rows per wave: a quarter of the row kernels' grid, and no more workgroups than fit on the CUs
+    // at once (each first copies u, up to 64 KB, into LDS; the waves then stride over the rows)
+    const int resident = 256 * (int)std::max<size_t>(1, (160 * 1024) / lds);
+    const int grid = std::min(row_grid((T + 3) / 4), resident);
     auto run = [&](auto kernel) -> hipError_t {
         if (lds > 65536) {
             hipError_t e = hipFuncSetAttribute((const void *)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -757,22 +761,24 @@ constexpr int kResPitch = 1040;               // fp32 rows of 256 values + 16 B
 constexpr int kResSlice = 64 * kResPitch;     // 64 tokens
 constexpr int kStageBytes = 256 * kQkPitch;   // 135,168 >= 2 * kResSlice
 constexpr int kSmemBytes = kStageBytes + 256 * 4;
-// QKV epilogue: the tile's rotary table rows (256 B of (cos, sin) pairs per token, 16 B
-// of padding so that 16 lanes reading 16 consecutive rows cover all 64 banks), then
-// one staging area per wave of 32 rows of 64 bf16 features.
-constexpr int kRopePitch = 272;
-constexpr int kRopeBytes = 256 * kRopePitch;           // 69,632
+// QKV epilogue: the tile's rotary table rows (256 B of (cos, sin) pairs per token) fill
+// one 64 KB operand stage buffer; the other holds one staging area per wave of 32 rows
+// of 64 bf16 features.
+constexpr int kStageBytes2 = 65536;                    // one operand stage of the K loop
 constexpr int kQkStagePitch = 144;                     // 128 B + 16 B
 constexpr int kQkStageBytes = 32 * kQkStagePitch;      // 4,608 per wave
-static_assert(kRopeBytes + 8 * kQkStageBytes <= kStageBytes, "QKV epilogue LDS");
+static_assert(256 * 256 <= kStageBytes2 && 8 * kQkStageBytes <= kStageBytes2, "QKV epilogue LDS");
 
 // K loop of one tile. SWAP = false: MFMA A operand = weight rows, B = token
 // rows, so lane (l32, hh) holds features 8 i + 4 hh + j of token l32 in register
 // 4 i + j. SWAP = true (feature-major v tiles): A = token rows, so the lane holds
 // tokens 8 i + 4 hh + j of feature l32.
-template <bool FP8, bool SWAP>
+// `before_last(buffer)` runs right before the last stage's products, once the other stage buffer is free
+// (its last reads retired at the preceding barrier, and no DMA targets it any more); it may start DMA into
+// that buffer, which the epilogue then waits for.
+template <bool FP8, bool SWAP, typename BeforeLast>
 __device__ __forceinline__ void gemm256_kloop(const GemmArgs &a, u32x4 *smem, f32x16 (&acc)[2][4], int m0, int n0,
-                                              int wave, int lane) {
+                                              int wave, int lane, BeforeLast &&before_last) {
     constexpr int BM = 256, BN = 256, ES = FP8 ? 1 : 2, BK = 128 / ES;
     constexpr int STAGE = (BM + BN) * 8;  // 16-byte chunks per stage
     const int wm = wave & 1, wn = wave >> 1, l32 = lane & 31, hh = lane >> 5;
@@ -871,6 +877,7 @@ __device__ __forceinline__ void gemm256_kloop(const GemmArgs &a, u32x4 *smem, f3
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         }
         lds_barrier();
+        if (kt == nk - 1 && nk >= 2) before_last(1);
         compute(smem);
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         lds_barrier();
@@ -882,6 +889,7 @@ __device__ __forceinline__ void gemm256_kloop(const GemmArgs &a, u32x4 *smem, f3
                 asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
             }
             lds_barrier();
+            if (kt + 1 == nk - 1) before_last(0);
             compute(smem + STAGE);
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             lds_barrier();
@@ -926,14 +934,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
     constexpr bool kNorm = EPI == kEpiQkv || EPI == kEpiSwiglu;
     const bool ss_early = kNorm && a.ss_in && a.ss_parts <= 4;
     f32x4 ssv[4] = {};
-    u32x2 pw[4] = {};
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm) {
         const int m = m0 + wm * 128 + tm * 32 + l32;
         if (ss_early) ssv[tm] = *(const f32x4 *)(a.ss_in + (size_t)m * kSsParts);
-        // rows past M hold whatever an earlier call left in the arena: their
-        // positions must not index the rotary table
-        if (EPI == kEpiQkv && m < a.M) pw[tm] = *(const u32x2 *)(a.pos + (size_t)m * 4);
+    }
+    // coordinates of the tokens whose rotary rows this wave fetches (128 wm + 32 wn + l32); rows past M
+    // hold whatever an earlier call left in the arena, so they take coordinate 0 and never index the table
+    u32x2 mine = {};
+    if constexpr (EPI == kEpiQkv) {
+        const int m = m0 + wm * 128 + wn * 32 + l32;
+        if (m < a.M) mine = *(const u32x2 *)(a.pos + (size_t)m * 4);
     }
 
     f32x16 acc[2][4];
@@ -941,10 +952,44 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+    // QKV q/k tiles: the tile's rotary table rows (32 (cos, sin) pairs per token, each pair from the row of
+    // its axis' coordinate, 256 B) enter LDS by DMA during the last K stage, into the stage buffer that stage
+    // does not read: one 4-byte DMA per lane and token; wave (wm, wn) fetches tokens 128 wm + 32 wn .. + 31,
+    // whose coordinates its lanes loaded above (tm = wn). The 16-byte chunk c of token t's row is stored at
+    // chunk c ^ (t % 16), so 16 lanes reading the same chunk of 16 consecutive rows cover all 64 banks.
+    int rope_buf = -1;
+    auto fetch_rope = [&](int buf) {
+        if constexpr (EPI == kEpiQkv) {
+            rope_buf = buf;
+            uint8_t *dst = L + buf * kStageBytes2 + (wm * 128 + wn * 32) * 256;
+            const uint8_t *rope = (const uint8_t *)a.rope;
+            // (rolled loops: unrolled, the compiler keeps every lane offset live through the K loop)
+            if (a.sec0 >= 32) {  // one axis: every pair of a token reads the row of its only coordinate
+#pragma unroll 1
+                for (int r = 0; r < 32; ++r) {
+                    const int gd = (((lane >> 2) ^ (r & 15)) << 2) | (lane & 3);  // dword of the table row
+                    const int p = (int)(int16_t)((uint32_t)__builtin_amdgcn_readlane((int)mine.x, r) & 0xffff);
+                    lds_dma4(rope + p * 256 + gd * 4, dst + r * 256);
+                }
+            } else {
+#pragma unroll 1
+                for (int r = 0; r < 32; ++r) {
+                    const int gd = (((lane >> 2) ^ (r & 15)) << 2) | (lane & 3);
+                    const int pair = gd >> 1;
+                    const uint32_t px = (uint32_t)__builtin_amdgcn_readlane((int)mine.x, r);
+                    const uint32_t py = (uint32_t)__builtin_amdgcn_readlane((int)mine.y, r);
+                    const int p = pair < a.sec0 ? (int)(int16_t)(px & 0xffff)
+                                                : (pair < a.sec0 + a.sec1 ? (int)(int16_t)(px >> 16)
+                                                                          : (int)(int16_t)(py & 0xffff));
+                    lds_dma4(rope + p * 256 + gd * 4, dst + r * 256);
+                }
+            }
+        }
+    };
     if (vtile)
-        gemm256_kloop<FP8, true>(a, smem, acc, m0, n0, wave, lane);
+        gemm256_kloop<FP8, true>(a, smem, acc, m0, n0, wave, lane, [](int) {});
     else
-        gemm256_kloop<FP8, false>(a, smem, acc, m0, n0, wave, lane);
+        gemm256_kloop<FP8, false>(a, smem, acc, m0, n0, wave, lane, fetch_rope);
 
     // per-token row factor of lane token (m0 + 128 wm + 32 tm + l32): folded
     // RMSNorm 1/rms (fixed summation order: part 0, 1, 2, ...) times the E4M3
@@ -1019,34 +1064,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
     }
 
     if constexpr (EPI == kEpiQkv) {
-        // ---- rotated q, k rows. The tile's 256 rotary table rows (32 (cos, sin) pairs per token, each pair
-        // from the row of its axis' coordinate) go into LDS once, one 4-byte DMA per lane and token: wave
-        // (wm, wn) fetches tokens 128 wm + 32 wn .. + 31, whose coordinates its lanes loaded before the K
-        // loop (tm = wn). Then every wave rotates its 128 tokens x 64 features from LDS and stores them
-        // through a wave-private staging area, 32 tokens at a time, as whole 128-byte row segments.
-        {
-            const u32x2 mine = wn == 0 ? pw[0] : wn == 1 ? pw[1] : wn == 2 ? pw[2] : pw[3];
-            const int pair = lane >> 1;
-            const int axis = pair < a.sec0 ? 0 : (pair < a.sec0 + a.sec1 ? 1 : 2);
-            const uint8_t *rope = (const uint8_t *)a.rope + lane * 4;
-#pragma unroll
-            for (int r = 0; r < 32; ++r) {
-                const uint32_t px = (uint32_t)__builtin_amdgcn_readlane((int)mine.x, r);
-                const uint32_t py = (uint32_t)__builtin_amdgcn_readlane((int)mine.y, r);
-                const int p = axis == 0 ? (int)(int16_t)(px & 0xffff)
-                                        : (axis == 1 ? (int)(int16_t)(px >> 16) : (int)(int16_t)(py & 0xffff));
-                lds_dma4(rope + (size_t)p * 256, L + (wm * 128 + wn * 32 + r) * kRopePitch);
-            }
-            wait_vmcnt<0>();
-            lds_barrier();
-        }
+        // ---- rotated q, k rows: every wave rotates its 128 tokens x 64 features with the table rows the K
+        // loop fetched (a K of one stage fetches them here), and stores them through a wave-private staging
+        // area in the other stage buffer, 32 tokens at a time, as whole 128-byte row segments.
+        if (rope_buf < 0) fetch_rope(1);
+        wait_vmcnt<0>();
+        lds_barrier();
         const float wsc = FP8 ? a.w_scale : 1.0f;
-        uint8_t *stage = L + kRopeBytes + wave * kQkStageBytes;
+        const uint8_t *rope_lds = L + rope_buf * kStageBytes2;
+        uint8_t *stage = L + (1 - rope_buf) * kStageBytes2 + wave * kQkStageBytes;
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) {
             const int t = wm * 128 + tm * 32 + l32;
             const float k = fac[tm] * wsc;
-            const uint8_t *row = L + t * kRopePitch + hh * 16;  // pairs 2 hh, 2 hh + 1 of each group of 4
+            const uint8_t *row = rope_lds + t * 256;
 #pragma unroll
             for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
@@ -1055,7 +1086,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
                     float o[4];
 #pragma unroll
                     for (int j = 0; j < 4; ++j) o[j] = acc[tn][tm][i * 4 + j] * k;
-                    const f32x4 e = *(const f32x4 *)(row + (tn * 16 + i * 4) * 8);
+                    // pairs 2 hh, 2 hh + 1 of the group of 4 starting at pair 16 tn + 4 i: chunk 8 tn + 2 i + hh
+                    const f32x4 e = *(const f32x4 *)(row + (((tn * 8 + i * 2 + hh) ^ (t & 15)) << 4));
                     const float2 cs[2] = {float2{e.x, e.y}, float2{e.z, e.w}};
                     rotate4(o, cs);
                     *(u32x2 *)(stage + l32 * kQkStagePitch + cl * 2) = u32x2{pack2(o[0], o[1]), pack2(o[2], o[3])};
