@@ -200,6 +200,35 @@ def test_image_shape_refusals(ube):
     assert e.value.status == "shape_mismatch"
 
 
+def test_image_edge_cases_empty_single_patch_and_mixed_sizes(ube):
+    """An empty batch, a one-patch image (its pooled row is that token's value projection: the pool's
+    one-token case), and images of different sizes in one batch (ragged 256-token tiles: 1, 6, 80 and
+    256 patches) against the oracle, with batch invariance of a sub-batch."""
+    w, model, arena = _model(ube, "image768")
+    rows, stats = ube.image_encode_pixels(model, arena, device_bytes(np.zeros(1, np.uint8)), [0], [], [])
+    assert rows.count == 0 and stats == (0, 0)
+    rng = np.random.default_rng(21)
+    sizes = [(16, 16), (32, 48), (128, 160), (256, 256)]
+    items = [rng.integers(0, 256, size=h * w_ * 3, dtype=np.int64).astype(np.uint8) for h, w_ in sizes]
+    offsets = np.zeros(len(items) + 1, np.uint64)
+    offsets[1:] = np.cumsum([len(x) for x in items])
+    batch = synth.MediaBatch(np.concatenate(items), offsets, [h for h, _ in sizes], [w_ for _, w_ in sizes],
+                             [1] * len(sizes))
+    rows, stats = ube.encode(model, arena, _dev(batch))
+    assert stats == (0, 1 + 6 + 80 + 256)
+    got = _pooled(rows)
+    want, _ = oracle.encode_media(w, batch)
+    check_pooled(got, want, "image mixed sizes")
+    # the one-patch image: the oracle's dense pool of one token returns xf W_v, which the GPU's
+    # reassociated pool must reproduce
+    x0, pos, cu = oracle.media_frontend(w, synth.subset(batch, [0]))
+    _, xf = oracle.forward_states(w, x0, pos, cu)
+    np.testing.assert_allclose(want[0], xf[0] @ w.f32["pool_wv"].astype(np.float64), rtol=1e-9, atol=1e-12)
+    sub = synth.subset(batch, [2, 0])
+    rows_s, _ = ube.encode(model, arena, _dev(sub))
+    np.testing.assert_array_equal(_pooled(rows_s), got[[2, 0]])
+
+
 def test_video_small_clips_match_oracle(ube):
     w, model, arena = _model(ube, "video1024")
     batch = synth.media_batch(3, 2, 64, 48, seed=4)  # 2 x 4 x 3 = 24 tokens per clip
@@ -317,6 +346,32 @@ def test_long_rows_at_depth_2_all_rows(ube):
     want, ostats = oracle.encode_text(w, data, offsets)
     assert stats == ostats == (1, 4096 + 2500 + 4096 + 1)
     check_pooled(_pooled(rows), want, "long depth 2")
+    arena.close()
+    model.close()
+
+
+def test_largest_context_one_block(ube):
+    """The largest context the library takes (32767 tokens: positions fill the int16 coordinates and the
+    rotary table): one full-context item, one truncated past it and one short item, at hidden 128 and
+    depth 1, against the oracle (128 key tiles per query tile in the attention)."""
+    g = dict(configs.geometry("tiny"), depth=1, context=32767, token_width=0)
+    w = synth.make_weights(g, gain_jitter=0.2)
+    model, arena = ube.Model(w, 0), ube.Arena(0)
+    rng = np.random.default_rng(12)
+    lengths = [32767, 33000, 5]
+    data = rng.integers(0, 256, sum(lengths), dtype=np.int64).astype(np.uint8)
+    offsets = np.zeros(len(lengths) + 1, np.uint64)
+    offsets[1:] = np.cumsum(lengths)
+    rows, stats = ube.text_encode(model, arena, device_bytes(data), offsets)
+    assert stats == (1, 32767 + 32767 + 5)
+    sub = synth.subset(synth.TextBatch(data, offsets), [0, 2])
+    want, _ = oracle.encode_text(w, sub.data, sub.offsets)
+    got = _pooled(rows)
+    check_pooled(got[[0, 2]], want, "context 32767")
+    # the truncated item pools exactly like its first 32767 bytes, which is item 0's length
+    prefix = data[int(offsets[1]):int(offsets[1]) + 32767]
+    rows_p, _ = ube.text_encode(model, arena, device_bytes(prefix), np.array([0, 32767], np.uint64))
+    np.testing.assert_array_equal(_pooled(rows_p)[0], got[1])
     arena.close()
     model.close()
 
