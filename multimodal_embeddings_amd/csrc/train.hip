@@ -181,11 +181,13 @@ __global__ __launch_bounds__(512, 4) void k_attn_bwd_dq(AttnBwdArgs a) {
                 dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(tr_frag<128>((const uint8_t *)sVt, 16 * ks, 32 * kk, lane),
                                                              dof[ks], dP, 0, 0, 0);
             }
+            // keys past the item weigh 0; a query past the item (its lane clamped to the last row, so finite)
+            // only feeds its own dQ row, which is not stored
             f32x16 dS;
+            const int ulim = k1 - (kt + kk * 32 + 4 * hh);  // this lane's keys u = ... + 8 (r / 4) + r % 4
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int u = kt + kk * 32 + 8 * (r >> 2) + 4 * hh + (r & 3);
-                const float p = (u < k1 && qvalid) ? __builtin_amdgcn_exp2f(S[r] * kScale2 - lse2) : 0.f;
+                const float p = 8 * (r >> 2) + (r & 3) < ulim ? __builtin_amdgcn_exp2f(S[r] * kScale2 - lse2) : 0.f;
                 dS[r] = p * (dP[r] - dlt);
             }
 #pragma unroll
