@@ -11,6 +11,7 @@ from __future__ import annotations
 
 import ctypes as C
 import os
+import weakref
 
 import numpy as np
 
@@ -497,9 +498,15 @@ def contrastive(arena: Arena, embeddings, scalars, *, anchor_begin=0, anchor_cou
 
 
 class _DeviceArray:
-    """__cuda_array_interface__ over raw device memory (torch.as_tensor turns it into a view)."""
+    """__cuda_array_interface__ over raw device memory (torch.as_tensor turns it into a view).
 
-    def __init__(self, ptr, shape, typestr):
+    ``owner`` is the object whose memory this is: torch keeps this array alive as long as
+    any tensor made from it, and the array keeps the owner alive, so the memory outlives
+    every view unless the owner is closed explicitly (which the owner refuses while
+    views exist)."""
+
+    def __init__(self, ptr, shape, typestr, owner=None):
+        self.owner = owner
         self.__cuda_array_interface__ = {"shape": tuple(shape), "typestr": typestr, "data": (ptr or 0, False),
                                          "version": 2}
 
@@ -519,21 +526,30 @@ class Trainer:
         del keep
         self.handle = handle
         self.model = model
+        self._views = weakref.WeakSet()
 
     def tensors(self):
-        """[(name, layer, master view, gradient view)] as torch tensors over the trainer's device memory."""
+        """[(name, layer, master view, gradient view)] as torch tensors over the trainer's device memory.
+        Each view keeps the trainer alive; ``close()`` refuses while any view exists."""
         import torch
         n = lib().ube_trainer_tensors(self.handle, None, 0)
         arr = (ube_trainer_tensor_t * n)()
         lib().ube_trainer_tensors(self.handle, arr, n)
+        dev = f"cuda:{self.model.device}"
         out = []
+
+        def view(ptr, shape, typestr):
+            a = _DeviceArray(ptr, shape, typestr, owner=self)
+            self._views.add(a)
+            return torch.as_tensor(a, device=dev)
+
         for t in arr:
             shape = (t.rows, t.cols) if t.cols else (t.rows,)
             if t.master_scalar == SCALAR["bf16"]:
-                master = torch.as_tensor(_DeviceArray(t.master, shape, "<i2"), device="cuda").view(torch.bfloat16)
+                master = view(t.master, shape, "<i2").view(torch.bfloat16)
             else:
-                master = torch.as_tensor(_DeviceArray(t.master, shape, "<f4"), device="cuda")
-            grad = torch.as_tensor(_DeviceArray(t.gradient, shape, "<f4"), device="cuda")
+                master = view(t.master, shape, "<f4")
+            grad = view(t.gradient, shape, "<f4")
             out.append((t.name.decode(), t.layer, master, grad))
         return out
 
@@ -573,6 +589,8 @@ class Trainer:
 
     def close(self):
         if getattr(self, "handle", None):
+            if len(getattr(self, "_views", ())):
+                raise RuntimeError("tensors() views of this trainer are still alive; drop them before close()")
             lib().ube_trainer_free(self.handle)
             self.handle = None
 

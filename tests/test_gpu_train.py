@@ -93,6 +93,29 @@ def test_backward_edge_cases(ube):
     assert all(float(gr.abs().max()) == 0.0 for _, _, _, gr in trainer.tensors())
 
 
+def test_tensor_views_keep_the_trainer_alive(ube):
+    import gc
+    import torch
+    g, w, batch, model, trainer, arena = _setup(ube)
+    views = trainer.tensors()
+    assert all(m.device == torch.device("cuda:0") for _, _, m, _ in views)
+    first = views[0][2].float().cpu().clone()
+    with pytest.raises(RuntimeError):
+        trainer.close()  # views alive: the memory must not be freed under them
+    del trainer
+    gc.collect()
+    # the trainer object is gone from this scope, but its memory is not: the views hold it
+    np.testing.assert_array_equal(views[0][2].float().cpu().numpy(), first.numpy())
+    del views
+    gc.collect()
+    t2 = ube.Trainer(model, w)
+    v2 = t2.tensors()
+    del v2
+    gc.collect()
+    t2.close()  # no views left: closes
+    arena.close()
+
+
 def test_trainer_refuses_unsupported_geometry(ube):
     """A model the encoder runs (ffn 320, a multiple of 64) but whose activation-gradient products the
     trainer's 128-column tiles cannot cover: the trainer reports unsupported instead of failing later."""
