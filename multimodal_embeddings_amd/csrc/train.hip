@@ -246,63 +246,94 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
         u32x4 *dst = smem + buf * 1024;
         lds_dma16(a.q + (size_t)row * a.ldqk + head * 64 + pc * 8, dst + wave * 64);
         lds_dma16(a.dout + (size_t)row * a.lddo + head * 64 + pc * 8, dst + 512 + wave * 64);
-        if (tid < 128) {  // queries past the item get lse = +inf (weight 0) and delta 0
+        if (tid < 128) {  // queries past the item get lse = +inf (weight 0) and delta 0; delta is kept negated
             const int r = tid & 63, t = k0 + tt * 64 + r;
             const bool ok = t < k1;
-            sld[buf][tid >> 6][r] = (tid < 64) ? (ok ? lse[t] : INFINITY) : (ok ? dl[t] : 0.f);
+            sld[buf][tid >> 6][r] = (tid < 64) ? (ok ? lse[t] : INFINITY) : (ok ? -dl[t] : 0.f);
         }
     };
     f32x16 dK[2] = {f32x16{}, f32x16{}}, dV[2] = {f32x16{}, f32x16{}};
+    // One 32-query slice (half qq of query tile tt) in two steps. scores: S = Q K^T and dP - delta =
+    // dO V^T - delta, the subtraction done by starting the dP accumulator at -delta of each row.
+    auto scores = [&](int tt, int qq, f32x16 &S, f32x16 &dP) {
+        const u32x4 *sQ = smem + (tt & 3) * 1024, *sO = sQ + 512;
+        const int row = qq * 32 + l32;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 d4 = *(const f32x4 *)&sld[tt & 3][1][qq * 32 + 8 * i + 4 * hh];
+            dP[4 * i] = d4.x, dP[4 * i + 1] = d4.y, dP[4 * i + 2] = d4.z, dP[4 * i + 3] = d4.w;
+        }
+        S = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int ch = swzb(row, ks * 2 + hh);
+            S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sQ[row * 8 + ch]), kf[ks], S, 0, 0, 0);
+            dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sO[row * 8 + ch]), vf[ks], dP, 0, 0,
+                                                         0);
+        }
+    };
+    // grads: P and dS = P (dP - delta), then dV^T += dO^T P and dK^T += Q^T dS
+    auto grads = [&](int tt, int qq, const f32x16 &S, const f32x16 &dP) {
+        const u32x4 *sQ = smem + (tt & 3) * 1024, *sO = sQ + 512;
+        f32x16 P, dS;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 l4 = *(const f32x4 *)&sld[tt & 3][0][qq * 32 + 8 * i + 4 * hh];
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int r = 4 * i + jj;
+                const float p = __builtin_amdgcn_exp2f(S[r] * kScale2 - lv[jj]);
+                P[r] = p;
+                dS[r] = p * dP[r];
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const bf16x8 bp = pack8(P, s), bs = pack8(dS, s);
+#pragma unroll
+            for (int te = 0; te < 2; ++te) {
+                dV[te] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    tr_rows_frag((const uint8_t *)sO, qq * 32 + 16 * s, 32 * te, lane), bp, dV[te], 0, 0, 0);
+                dK[te] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                    tr_rows_frag((const uint8_t *)sQ, qq * 32 + 16 * s, 32 * te, lane), bs, dK[te], 0, 0, 0);
+            }
+        }
+    };
     const int ntile = (k1 - k0 + 63) >> 6;
     // query tiles in pairs over four buffers, one barrier per pair (as in the dQ kernel)
-    issue(0, 0);
-    if (1 < ntile) issue(1, 1);
-    for (int tp = 0; tp < ntile; tp += 2) {
+    auto next_pair = [&](int tp) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         lds_barrier();
         if (tp + 2 < ntile) issue(tp + 2, (tp + 2) & 3);
         if (tp + 3 < ntile) issue(tp + 3, (tp + 3) & 3);
+    };
+    issue(0, 0);
+    if (1 < ntile) issue(1, 1);
+    // the slices of a pair in a pipeline: each slice's products are issued before the previous slice's
+    // exponentials, which then run while the matrix cores work on them
+    f32x16 Sa, dPa, Sb, dPb;
+    int tp = 0;
+    for (; tp + 1 < ntile; tp += 2) {
+        next_pair(tp);
         if (!active) continue;
-        for (int tt = tp; tt < min(tp + 2, ntile); ++tt) {
-        const u32x4 *sQ = smem + (tt & 3) * 1024, *sO = sQ + 512;
-#pragma unroll
-        for (int qq = 0; qq < 2; ++qq) {
-            f32x16 S = f32x16{}, dP = f32x16{};
-            const int row = qq * 32 + l32;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                const int ch = swzb(row, ks * 2 + hh);
-                S = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sQ[row * 8 + ch]), kf[ks], S, 0, 0, 0);
-                dP = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, sO[row * 8 + ch]), vf[ks], dP, 0, 0,
-                                                             0);
-            }
-            f32x16 P, dS;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r0 = qq * 32 + 8 * i + 4 * hh;
-                const f32x4 l4 = *(const f32x4 *)&sld[tt & 3][0][r0], d4 = *(const f32x4 *)&sld[tt & 3][1][r0];
-                const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int r = 4 * i + jj;
-                    const float p = __builtin_amdgcn_exp2f(S[r] * kScale2 - lv[jj]);
-                    P[r] = p;
-                    dS[r] = p * (dP[r] - dv4[jj]);
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const bf16x8 bp = pack8(P, s), bs = pack8(dS, s);
-#pragma unroll
-                for (int te = 0; te < 2; ++te) {
-                    dV[te] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_rows_frag((const uint8_t *)sO, qq * 32 + 16 * s, 32 * te, lane), bp, dV[te], 0, 0, 0);
-                    dK[te] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        tr_rows_frag((const uint8_t *)sQ, qq * 32 + 16 * s, 32 * te, lane), bs, dK[te], 0, 0, 0);
-                }
-            }
-        }
+        scores(tp, 0, Sa, dPa);
+        scores(tp, 1, Sb, dPb);
+        grads(tp, 0, Sa, dPa);
+        scores(tp + 1, 0, Sa, dPa);
+        grads(tp, 1, Sb, dPb);
+        scores(tp + 1, 1, Sb, dPb);
+        grads(tp + 1, 0, Sa, dPa);
+        grads(tp + 1, 1, Sb, dPb);
+    }
+    if (tp < ntile) {  // an odd last tile
+        next_pair(tp);
+        if (active) {
+            scores(tp, 0, Sa, dPa);
+            scores(tp, 1, Sb, dPb);
+            grads(tp, 0, Sa, dPa);
+            grads(tp, 1, Sb, dPb);
         }
     }
     if (active && kvalid) {
