@@ -1318,8 +1318,9 @@ hipError_t launch_gemm_e4m3(int epi, const GemmArgs &a, hipStream_t stream) {
 //                                      scores; the row max needs one exchange
 //                                      between the two lane halves
 //   online softmax in fp32 on exp2 of pre-scaled logits: the score accumulators
-//   start at minus the running max, so a weight costs one exponential; the
-//   output is only rescaled when some query's running max grew
+//   start at minus a per-query reference (the first tile's max), so a weight
+//   costs one exponential; the reference moves up, rescaling the output, only
+//   when a tile's weights of some query sum past 2^8, so most tiles take no max
 //   O^T (d x queries) += V^T P^T   -- P^T comes straight from the S^T registers.
 // Small waves (under 128 registers) let four waves share each SIMD, so the
 // softmax of some waves runs on the vector ALUs while others keep the matrix
@@ -1335,7 +1336,7 @@ __device__ __forceinline__ int perm32(int r) {  // r = 8 i + 4 h + j
     return (i >> 1) * 16 + h * 8 + (i & 1) * 4 + j;
 }
 
-constexpr float kRescaleLog2 = 8.0f;  // attention: largest weight allowed above the reference, log2 units
+constexpr float kRescaleSum = 256.0f;  // attention: largest sum of one query's weights in a tile half
 
 __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict__ q, const uint16_t *__restrict__ k,
                                                       int ldqk, const uint16_t *__restrict__ vt, int ldvt,
@@ -1378,19 +1379,17 @@ __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict
     };
 
     f32x16 O[2] = {f32x16{}, f32x16{}};
-    float m_run = 0.f, l_run = 0.f;  // running max of the scaled scores, sum of weights
+    float m_run = 0.f, l_run = 0.f;  // reference (running max) of the scaled scores, sum of weights
 
     auto compute = [&](const u32x4 *sK, int kt, bool first) {
         const u32x4 *sV = sK + 512;
         // the accumulators start at -m_run: the MFMAs return scores relative to the
-        // running max, ready for the exponential
-        const float init = first ? 0.f : -m_run;
+        // reference, ready for the exponential
         f32x16 S[2];
-        S[0] = init;
-        S[1] = init;
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
             const int row = kk * 32 + l32;
+            S[kk] = -m_run;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const bf16x8 kf = __builtin_bit_cast(bf16x8, sK[row * 8 + swz(row, ks * 2 + hh)]);
@@ -1406,21 +1405,16 @@ __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict
                     if (key >= k1) S[kk][r] = -INFINITY;
                 }
         }
-        float mx = -INFINITY;
+        // moves the reference up by the query's largest relative score (never down; the first tile
+        // sets it) and rescales what was summed so far
+        auto rebase = [&]() {
+            float mx = -INFINITY;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kk][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // the first tile sets the reference max; later ones move it only when some
-        // score exceeds it by more than 2^8 in weight (then the output and the row sum
-        // are rescaled). Below that the weights may exceed 1 by up to 2^8, which the
-        // bf16 weights and fp32 sums hold exactly as well; the softmax does not depend
-        // on the reference, and most tiles skip the rescale.
-        // (only queries inside the item vote: the lanes past its end hold whatever rows follow it, and
-        // must not change the reference of the others, or a row would depend on its batch)
-        const float d = first ? mx : fmaxf(mx, 0.f);
-        if (first || __any(qvalid && d > kRescaleLog2)) {
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kk][r]);
+            mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+            const float d = first ? mx : fmaxf(mx, 0.f);
             m_run += d;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) S[kk] -= d;
@@ -1430,28 +1424,44 @@ __global__ __launch_bounds__(512, 2) void k_attention(const uint16_t *__restrict
                 O[0] *= alpha;
                 O[1] *= alpha;
             }
-        }
+        };
         // p = 2^(relative score) on the raw v_exp_f32 (weights below 2^-126 flush to
         // 0); packed to bf16 at once, and the row sum taken over those same bf16 values
         u32x4 P[2][2];
         float rs = 0.f;
-        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+        auto weights = [&]() {
+            const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+            rs = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+            for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-            for (int ip = 0; ip < 2; ++ip) {
-                uint32_t w[4];
+                for (int ip = 0; ip < 2; ++ip) {
+                    uint32_t w[4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = ip * 4 + e;
-                    const float p0 = __builtin_amdgcn_exp2f(S[kk][2 * r]);
-                    const float p1 = __builtin_amdgcn_exp2f(S[kk][2 * r + 1]);
-                    const bf16x2 pb = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
-                    w[e] = __builtin_bit_cast(uint32_t, pb);
-                    rs = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rs, false);
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = ip * 4 + e;
+                        const float p0 = __builtin_amdgcn_exp2f(S[kk][2 * r]);
+                        const float p1 = __builtin_amdgcn_exp2f(S[kk][2 * r + 1]);
+                        const bf16x2 pb = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+                        w[e] = __builtin_bit_cast(uint32_t, pb);
+                        rs = __builtin_amdgcn_fdot2_f32_bf16(pb, ones, rs, false);
+                    }
+                    P[kk][ip] = u32x4{w[0], w[1], w[2], w[3]};
                 }
-                P[kk][ip] = u32x4{w[0], w[1], w[2], w[3]};
-            }
+        };
+        // Later tiles keep the reference unless some query's weights in the tile sum past 2^8 (so
+        // every weight is at most 2^8, which the bf16 weights and fp32 sums hold as well as weights
+        // up to 1; a sum that overflowed or is NaN fails the test too): then the reference moves
+        // and the weights are taken again. The softmax does not depend on the reference, most
+        // tiles keep it, and they need no maximum. Only queries inside the item vote: the lanes
+        // past its end hold whatever rows follow it, and must not change the reference of the
+        // others, or a row would depend on its batch.
+        if (first) rebase();
+        weights();
+        if (!first && __any(qvalid && !(rs <= kRescaleSum))) {
+            rebase();
+            weights();
+        }
         l_run += rs;
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
