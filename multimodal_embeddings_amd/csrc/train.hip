@@ -354,30 +354,38 @@ __global__ __launch_bounds__(512, 1) void k_attn_bwd_dkv(AttnBwdArgs a) {
     }
 }
 
-// one thread per (token, 2 features)
+// one thread per (token, 8 features): gate and up are interleaved in blocks of 32 features, so the 8
+// gates, the 8 ups, their 8 output gradients and the 8 activations are each one 16-byte access. SiLU as in
+// the forward's epilogue: s = 1 / (1 + 2^(-g log2 e)) on the raw v_exp_f32 and v_rcp_f32.
 __global__ __launch_bounds__(256) void k_swiglu_bwd(const uint16_t *gu, const uint16_t *da, uint16_t *dgu, uint16_t *a,
                                                     int T, int F) {
     const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
-    if (idx >= (size_t)T * (F / 2)) return;
-    const int t = (int)(idx / (F / 2)), f = (int)(idx % (F / 2)) * 2;
+    if (idx >= (size_t)T * (F / 8)) return;
+    const int t = (int)(idx / (F / 8)), f = (int)(idx % (F / 8)) * 8;
     const int blk = f >> 5, w = f & 31;
-    const size_t gi = (size_t)t * 2 * F + blk * 64 + w, ui = gi + 32;
-    const uint32_t gg = *(const uint32_t *)(gu + gi), uu = *(const uint32_t *)(gu + ui);
-    const uint32_t dd = *(const uint32_t *)(da + (size_t)t * F + f);
-    float g[2] = {bf16_to_f32(gg & 0xffff), bf16_to_f32(gg >> 16)}, up[2] = {bf16_to_f32(uu & 0xffff), bf16_to_f32(uu >> 16)};
-    float d[2] = {bf16_to_f32(dd & 0xffff), bf16_to_f32(dd >> 16)};
-    float dg[2], du[2], av[2];
+    const size_t gi = (size_t)t * 2 * F + blk * 64 + w, ui = gi + 32, ai = (size_t)t * F + f;
+    const u32x4 gg = *(const u32x4 *)(gu + gi), uu = *(const u32x4 *)(gu + ui), dd = *(const u32x4 *)(da + ai);
+    const uint32_t g2[4] = {gg.x, gg.y, gg.z, gg.w}, u2[4] = {uu.x, uu.y, uu.z, uu.w}, d2[4] = {dd.x, dd.y, dd.z, dd.w};
+    uint32_t dg[4], du[4], av[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const float sg = 1.f / (1.f + expf(-g[j]));
-        const float silu = g[j] * sg;
-        av[j] = silu * up[j];
-        du[j] = d[j] * silu;
-        dg[j] = d[j] * up[j] * sg * (1.f + g[j] * (1.f - sg));
+    for (int q = 0; q < 4; ++q) {
+        float o[3][2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float g = bf16_to_f32(h ? g2[q] >> 16 : g2[q] & 0xffff);
+            const float up = bf16_to_f32(h ? u2[q] >> 16 : u2[q] & 0xffff);
+            const float d = bf16_to_f32(h ? d2[q] >> 16 : d2[q] & 0xffff);
+            const float sg = __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(g * -1.4426950408889634f));
+            const float silu = g * sg;
+            o[0][h] = d * up * sg * (1.f + g * (1.f - sg));  // d/dg
+            o[1][h] = d * silu;                             // d/du
+            o[2][h] = silu * up;                            // the activation
+        }
+        dg[q] = pack2(o[0][0], o[0][1]), du[q] = pack2(o[1][0], o[1][1]), av[q] = pack2(o[2][0], o[2][1]);
     }
-    *(uint32_t *)(dgu + gi) = pack2(dg[0], dg[1]);
-    *(uint32_t *)(dgu + ui) = pack2(du[0], du[1]);
-    *(uint32_t *)(a + (size_t)t * F + f) = pack2(av[0], av[1]);
+    *(u32x4 *)(dgu + gi) = u32x4{dg[0], dg[1], dg[2], dg[3]};
+    *(u32x4 *)(dgu + ui) = u32x4{du[0], du[1], du[2], du[3]};
+    *(u32x4 *)(a + ai) = u32x4{av[0], av[1], av[2], av[3]};
 }
 
 // One wave per row; workgroup (4 waves) = rows_per_block consecutive rows, so the gain partial of the
@@ -400,7 +408,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const float *x, const float
             gv[c][v] = c < C ? gain[64 * V * c + V * lane + v] : 0.f;
         }
     const int r0 = blockIdx.x * rows_per_block, r1 = min(T, r0 + rows_per_block);
-    auto row = [&](int t, const fv (&xv)[CM], const fv (&hv)[CM]) {
+    auto row = [&](int t, const fv (&xv)[CM], const fv (&hv)[CM], const fv (&rv)[CM]) {
         float ss = 0.f, sd = 0.f;
 #pragma unroll
         for (int c = 0; c < CM; ++c)
@@ -424,7 +432,7 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const float *x, const float
                     o[v] = inv * gv[c][v] * hv[c][v] - xv[c][v] * k;
                     gacc[c][v] += hv[c][v] * xv[c][v] * inv;
                 }
-                if (dres) o += *(const fv *)(dres + i);
+                if (dres) o += rv[c];
                 *(fv *)(dx + i) = o;
                 if (dxb) {
                     if constexpr (V == 4)
@@ -434,27 +442,30 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const float *x, const float
                 }
             }
     };
-    auto load = [&](int t, fv (&xv)[CM], fv (&hv)[CM]) {
+    // x, dh and the residual gradient of a row are loaded together (dres joins them rather than waiting for
+    // the row's reductions)
+    auto load = [&](int t, fv (&xv)[CM], fv (&hv)[CM], fv (&rv)[CM]) {
 #pragma unroll
         for (int c = 0; c < CM; ++c)
             if (c < C) {
                 const size_t i = (size_t)t * D + 64 * V * c + V * lane;
                 xv[c] = *(const fv *)(x + i);
                 hv[c] = *(const fv *)(dh + i);
+                rv[c] = dres ? *(const fv *)(dres + i) : fv{};
             }
     };
     int t = r0 + wave;
     for (; t + 4 < r1; t += 8) {
-        fv xa[CM], ha[CM], xb[CM], hb[CM];
-        load(t, xa, ha);
-        load(t + 4, xb, hb);
-        row(t, xa, ha);
-        row(t + 4, xb, hb);
+        fv xa[CM], ha[CM], ra[CM], xb[CM], hb[CM], rb[CM];
+        load(t, xa, ha, ra);
+        load(t + 4, xb, hb, rb);
+        row(t, xa, ha, ra);
+        row(t + 4, xb, hb, rb);
     }
     if (t < r1) {
-        fv xa[CM], ha[CM];
-        load(t, xa, ha);
-        row(t, xa, ha);
+        fv xa[CM], ha[CM], ra[CM];
+        load(t, xa, ha, ra);
+        row(t, xa, ha, ra);
     }
 #pragma unroll
     for (int c = 0; c < CM; ++c)
@@ -1178,7 +1189,8 @@ hipError_t launch_attention_bwd(const AttnBwdArgs &a, hipStream_t stream) {
 
 hipError_t launch_swiglu_bwd(const uint16_t *gu, const uint16_t *da, uint16_t *dgu, uint16_t *a, int T, int F,
                              hipStream_t stream) {
-    const size_t n = (size_t)T * (F / 2);
+    if (F % 32) return hipErrorInvalidValue;  // gate and up interleave in blocks of 32 features
+    const size_t n = (size_t)T * (F / 8);
     if (!n) return hipSuccess;
     k_swiglu_bwd<<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(gu, da, dgu, a, T, F);
     return hipGetLastError();
