@@ -954,7 +954,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
     // QKV q/k tiles: the tile's rotary table rows (32 (cos, sin) pairs per token, each pair from the row of
     // its axis' coordinate, 256 B) enter LDS by DMA during the last K stage, into the stage buffer that stage
-    // does not read: one 4-byte DMA per lane and token; wave (wm, wn) fetches tokens 128 wm + 32 wn .. + 31,
+    // does not read (16-byte DMAs, or 4-byte ones where an axis section has odd length); wave (wm, wn)
+    // fetches tokens 128 wm + 32 wn .. + 31,
     // whose coordinates its lanes loaded above (tm = wn). The 16-byte chunk c of token t's row is stored at
     // chunk c ^ (t % 16), so 16 lanes reading the same chunk of 16 consecutive rows cover all 64 banks.
     int rope_buf = -1;
@@ -964,14 +965,22 @@ __global__ __launch_bounds__(512, 1) void k_gemm256(GemmArgs a) {
             uint8_t *dst = L + buf * kStageBytes2 + (wm * 128 + wn * 32) * 256;
             const uint8_t *rope = (const uint8_t *)a.rope;
             // (rolled loops: unrolled, the compiler keeps every lane offset live through the K loop)
-            if (a.sec0 >= 32) {  // one axis: every pair of a token reads the row of its only coordinate
+            if (a.sec0 >= 32 || ((a.sec0 | a.sec1) & 1) == 0) {
+                // every 16-byte chunk (two pairs) lies within one axis' section: one 16-byte DMA per lane,
+                // four tokens per instruction; lane l fetches stored chunk l % 16 of token 4 it + l / 16,
+                // whose coordinate sits in lane (token) of the wave
 #pragma unroll 1
-                for (int r = 0; r < 32; ++r) {
-                    const int gd = (((lane >> 2) ^ (r & 15)) << 2) | (lane & 3);  // dword of the table row
-                    const int p = (int)(int16_t)((uint32_t)__builtin_amdgcn_readlane((int)mine.x, r) & 0xffff);
-                    lds_dma4(rope + p * 256 + gd * 4, dst + r * 256);
+                for (int it = 0; it < 8; ++it) {
+                    const int r = it * 4 + (lane >> 4);
+                    const int c = (lane & 15) ^ (r & 15);  // chunk of the table row: pairs 2 c, 2 c + 1
+                    const uint32_t px = (uint32_t)__shfl((int)mine.x, r, 64);
+                    const uint32_t py = (uint32_t)__shfl((int)mine.y, r, 64);
+                    const int p = 2 * c < a.sec0 ? (int)(int16_t)(px & 0xffff)
+                                                 : (2 * c < a.sec0 + a.sec1 ? (int)(int16_t)(px >> 16)
+                                                                            : (int)(int16_t)(py & 0xffff));
+                    lds_dma16(rope + p * 256 + c * 16, dst + it * 1024);
                 }
-            } else {
+            } else {  // a section of odd length: pairs of one chunk may take different rows, one dword each
 #pragma unroll 1
                 for (int r = 0; r < 32; ++r) {
                     const int gd = (((lane >> 2) ^ (r & 15)) << 2) | (lane & 3);
