@@ -90,6 +90,25 @@ def kernel_bytes_per_launch(kernel, g, T, count):
     raise ValueError(f"no roofline for kernel {kernel}")
 
 
+
+def timed_steps(step, steps, stream):
+    """Runs `steps` steps between events on `stream` (one event after each step as well) ->
+    (mean ms per step over the whole timed region, [ms of each step])."""
+    import torch
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        step()
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return ev[0].elapsed_time(ev[-1]) / steps, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def step_stats(per):
+    """Median and minimum of the per-step times (the mean is `ms_per_step`)."""
+    import statistics
+    return {"ms_step_median": statistics.median(per), "ms_step_min": min(per)} if per else {}
+
 def source_digest(kernel="gemm"):
     h = hashlib.sha256()
     files = ("contrastive.hip", "contrastive.h") if kernel.startswith("contrastive") else ("kernels.hip", "kernels.h")
@@ -194,18 +213,13 @@ def bench_maxsim(args):
     for _ in range(args.warmup):
         ube.maxsim(tape, tape, scores, span=span, completion=1, stream=stream)
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        ube.maxsim(tape, tape, scores, span=span, completion=1, stream=stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms, per = timed_steps(lambda: ube.maxsim(tape, tape, scores, span=span, completion=1, stream=stream), args.steps,
+                          stream)
     achieved = flops / (ms / 1e3) / 1e12
     out = {
         "metric": "MaxSim query-document pairs/sec (256 x 256 band, 64 query tokens x 1024 document tokens, width 128)",
         "value": n * n / (ms / 1e3), "unit": "pairs/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "ms_per_step": ms, **step_stats(per), "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (token vectors of the seeded 1024-byte text batch, random-init weights)",
         "config": {"workload": f"maxsim: {WORKLOAD_TEXT['maxsim']}", "pairs": n * n, "parallelism": "1 GPU"},
         "roofline": {"kernel": "maxsim", "bound": "mfma", "achieved": achieved, "peak": PEAK_BF16 / 1e12,
@@ -257,14 +271,8 @@ def bench_siglip(args):
         step()
     torch.cuda.synchronize()
     ube.kernel_timer_start(kernel, args.steps + 4)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
+    ms, per = timed_steps(step, args.steps, stream)
     kms, launches = ube.kernel_timer_stop()
-    ms = start.elapsed_time(end) / args.steps
     per_kernel = {}
     if args.per_kernel:
         for kname in ("contrastive_cells", "contrastive_rows", "contrastive_cols"):
@@ -288,7 +296,7 @@ def bench_siglip(args):
     out = {
         "metric": "contrastive band pairs/sec (Matryoshka sigmoid loss + gradient over pooled embeddings)",
         "value": pairs / (ms / 1e3), "unit": "pairs/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "ms_per_step": ms, **step_stats(per), "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded paired views of shared latents, bf16 rows, seeded edges)",
         "config": {"workload": f"{args.workload}: {WORKLOAD_TEXT[args.workload]}", "anchors": R, "items": n,
                    "columns": D, "widths": list(widths), "parallelism": "1 GPU"},
@@ -364,14 +372,8 @@ def bench_train(args):
     torch.cuda.synchronize()
     kernel = args.kernel
     ube.kernel_timer_start(kernel, args.steps * g["depth"] * 8 + 8)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
+    ms, per = timed_steps(step, args.steps, stream)
     kms, launches = ube.kernel_timer_stop()
-    ms = start.elapsed_time(end) / args.steps
     per_kernel = {}
     if args.per_kernel:
         for kname in ube.KERNELS:
@@ -402,7 +404,7 @@ def bench_train(args):
     out = {
         "metric": "training tokens/sec (one device's step: encode, contrastive loss, backward, Adafactor)",
         "value": T / (ms / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
-        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "ms_per_step": ms, **step_stats(per), "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded bytes, random-init bf16 weights N(0, 0.02))",
         "config": {"workload": f"train: {WORKLOAD_TEXT['train']}", "items": n, "tokens": T, "parallelism": "1 GPU",
                    "activation_recomputation": bool(args.recompute)},
@@ -506,15 +508,9 @@ def main():
     torch.cuda.synchronize()
 
     ube.kernel_timer_start(args.kernel, args.steps * g["depth"] + 8)
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    end.record(stream)
-    torch.cuda.synchronize()
+    ms, per = timed_steps(step, args.steps, stream)
     kms, launches = ube.kernel_timer_stop()
-    ms = start.elapsed_time(end) / args.steps
 
     per_kernel = {}
     if args.per_kernel:
@@ -545,6 +541,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms,
+        **step_stats(per),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
