@@ -96,6 +96,48 @@ def test_attention_matches_oracle(lengths, heads):
     assert err.max() <= 2e-2 and err.mean() <= 2e-3
 
 
+@pytest.mark.parametrize("top", [3.0, 1000.0])
+def test_attention_reference_follows_growing_scores(top):
+    """Keys whose scale grows geometrically along each item (0.1 at its first token, `top` at its last), so
+    later key tiles score far above the first one: up to ~15 log2 units (weights summing past 2^8 against
+    the first tile's reference) or hundreds (2^score overflows against it). The kernel must move its
+    reference when a tile's weights sum past 2^8 or overflow and still give the softmax ("UForm" page, One
+    Omni Model: bidirectional attention inside each item). At these magnitudes the kernel's bf16 rounding
+    of the pre-scaled queries (q log2(e) / 8, rounded once when loaded) moves scores by up to 2^-9 of their
+    size, so the oracle is given those same rounded queries: the comparison isolates the reference
+    handling."""
+    import multimodal_embeddings_amd as ube
+    torch = _torch()
+    lengths, heads = [1024, 333, 64, 65, 1], 2
+    say(f"attention with key scales 0.1 .. {top}, lengths={lengths}")
+    rng = np.random.default_rng(int(top) + 7)
+    T = int(sum(lengths))
+    W = heads * 64
+    Tp = (T + 255) // 256 * 256 + 256
+    qb, _ = _bf16(rng, (Tp, W))
+    pos = np.concatenate([np.arange(n) / max(n - 1, 1) for n in lengths])
+    scale = np.ones((Tp, 1), np.float32)
+    scale[:T, 0] = 0.1 * (top / 0.1) ** pos
+    kb = synth.to_bf16_bits(rng.standard_normal((Tp, W)).astype(np.float32) * scale)
+    kf = synth.bf16_bits_to_f32(kb).astype(np.float64)
+    vb, vf = _bf16(rng, (T, W))
+    vt = np.zeros((W, Tp), np.uint16)
+    vt[:, :T] = vb.T
+    o = torch.zeros((T, W), dtype=torch.bfloat16, device="cuda:0")
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.uint32)
+    ube.step_attention(_to_dev_bf16(qb), _to_dev_bf16(kb), W, _to_dev_bf16(vt), Tp, o, W, cu, heads)
+    torch.cuda.synchronize()
+    got = _from_dev_bf16(o)
+    c32 = np.float32(0.18033688011112042)  # log2(e) / 8 as the kernel holds it
+    qs = synth.bf16_bits_to_f32(synth.to_bf16_bits(synth.bf16_bits_to_f32(qb) * c32)).astype(np.float64)
+    q_eff = qs / (np.log2(np.e) / 8.0)  # the queries whose exact softmax the kernel's weights follow
+    ref = oracle.attention(q_eff[:T], kf[:T], vf, cu.astype(np.uint64), heads, 64)
+    err = np.abs(got - ref)
+    say(f"  max |err| {err.max():.3e}, mean {err.mean():.3e}")
+    assert np.all(np.isfinite(got))
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
+
+
 def test_device_bf16_rounding_is_nearest_even():
     # the kernels' fp32 -> bf16 conversion, checked through the RMSNorm step with
     # unit gain on rows whose normalised values are known exactly in fp32
