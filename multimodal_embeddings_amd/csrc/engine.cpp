@@ -540,8 +540,8 @@ void make_tiles(Plan &p) {
 // Device regions of one call.
 struct Layout {
     size_t Tpad = 0;
-    size_t out, cu, offs, src, tiles, atiles, itile, media, input, x, h, a, qk, vt, o, xf, s, pos, patches, q8, qs, ss, st,
-        tvf, tv, zp, zs, total;
+    size_t out, cu, offs, src, tiles, atiles, itile, media, input, x, h, a, qk, vt, o, xf, s, pos, patches, q8, qs,
+        ss, st, tvf, tv, zp, zs, total;
 };
 
 // Per-token surfaces of one call: fp32 states (bf16 states are the final-norm
