@@ -169,8 +169,14 @@ __global__ __launch_bounds__(256) void k_final_norm_scores(const float *__restri
                                                            float *__restrict__ s, float *__restrict__ states, int T,
                                                            int D, int H, float eps) {
     constexpr int R = 4;
-    extern __shared__ float su[];  // u [H x D]
-    for (int i = threadIdx.x; i < H * D; i += 256) su[i] = u[i];
+    // u [H x D] in LDS with each lane's V consecutive values spread one per bank row: value i of lane l in
+    // column group c sits at 64 V c + 64 i + l, so a wave reading value i of all its lanes touches 64
+    // consecutive dwords (in u's own order, lanes V floats apart, eight lanes would share each bank)
+    extern __shared__ float su[];
+    for (int e = threadIdx.x; e < H * D; e += 256) {
+        const int hd = e / D, f = e % D, c = f / (64 * V), l = (f / V) % 64, i = f % V;
+        su[hd * D + c * 64 * V + i * 64 + l] = u[e];
+    }
     __syncthreads();
     const int lane = threadIdx.x & 63;
     const int waves = gridDim.x * 4;
@@ -224,10 +230,9 @@ __global__ __launch_bounds__(256) void k_final_norm_scores(const float *__restri
             if (hd < H) {
 #pragma unroll
                 for (int c = 0; c < C; ++c) {
-                    const int f = c * 64 * V + lane * V;
 #pragma unroll
                     for (int i = 0; i < V; ++i) {
-                        const float uv = su[hd * D + f + i];
+                        const float uv = su[hd * D + c * 64 * V + i * 64 + lane];
 #pragma unroll
                         for (int r = 0; r < R; ++r) dots[r][hd] += v[r][c][i] * uv;
                     }
