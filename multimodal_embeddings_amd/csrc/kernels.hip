@@ -172,10 +172,11 @@ __global__ __launch_bounds__(256) void k_final_norm_scores(const float *__restri
     // u [H x D] in LDS with each lane's V consecutive values spread one per bank row: value i of lane l in
     // column group c sits at 64 V c + 64 i + l, so a wave reading value i of all its lanes touches 64
     // consecutive dwords (in u's own order, lanes V floats apart, eight lanes would share each bank)
+    // (filled in LDS order, so consecutive threads write consecutive dwords and gather from u, a few KB in L2)
     extern __shared__ float su[];
-    for (int e = threadIdx.x; e < H * D; e += 256) {
-        const int hd = e / D, f = e % D, c = f / (64 * V), l = (f / V) % 64, i = f % V;
-        su[hd * D + c * 64 * V + i * 64 + l] = u[e];
+    for (int d = threadIdx.x; d < H * D; d += 256) {
+        const int hd = d / D, r = d % D, c = r / (64 * V), i = (r / 64) % V, l = r % 64;
+        su[d] = u[hd * D + c * 64 * V + l * V + i];
     }
     __syncthreads();
     const int lane = threadIdx.x & 63;
